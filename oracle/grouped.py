@@ -1,0 +1,118 @@
+"""Grouped (MoE) scaled linear and the per-token scaled SwiGLU.
+
+Test infrastructure (see the package docstring): never used by the product path.
+
+"Activation + GroupedLinear Fusion for MOE and other MOE optimizations"
+(Description; Greptile Summary; Sequence Diagram) describes a grouped MLP:
+fc1 as a GroupedLinear, a scaled SwiGLU whose scales are per-token
+probabilities, fc2 as a GroupedLinear; in the backward the activation
+gradient also returns the gradient of the scales ("grad_scales"). Rows of
+group g are tokens ``base[g] .. base[g+1]-1`` (see ``offsets``).
+
+Readings where the page is silent:
+
+* fc1's output h [T, 2F] holds the SwiGLU gate in its first half and the
+  linear ("up") part in its second half: ``a = h[:, :F]``, ``b = h[:, F:]``.
+* ``y = p[:, None] * silu(a) * b`` with ``silu(a) = a * sigmoid(a)``.
+* The grouped GEMMs take an alpha like the dense ones (1 for the MLP).
+* A group with no token contributes an all-zero weight gradient.
+"""
+
+import numpy as np
+
+
+def _groups(base):
+    base = np.asarray(base, dtype=np.int64)
+    return [(g, int(base[g]), int(base[g + 1])) for g in range(len(base) - 1)]
+
+
+def grouped_linear_fwd(x, w, base, alpha=1.0):
+    """out[t] = alpha * x[t] @ W_g^T for t in group g. x [T, K], W [G, N, K] -> [T, N]."""
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w, np.float64)
+    out = np.zeros((x.shape[0], w.shape[1]), np.float64)
+    for g, lo, hi in _groups(base):
+        out[lo:hi] = alpha * (x[lo:hi] @ w[g].T)
+    return out
+
+
+def grouped_linear_dgrad(dy, w, base, alpha=1.0):
+    """dx[t] = alpha * dy[t] @ W_g. dy [T, N], W [G, N, K] -> [T, K]."""
+    dy = np.asarray(dy, np.float64)
+    w = np.asarray(w, np.float64)
+    out = np.zeros((dy.shape[0], w.shape[2]), np.float64)
+    for g, lo, hi in _groups(base):
+        out[lo:hi] = alpha * (dy[lo:hi] @ w[g])
+    return out
+
+
+def grouped_linear_wgrad(dy, x, base, alpha=1.0):
+    """dW_g = alpha * sum over t in g of dy[t]^T x[t]. -> [G, N, K] (zero for an empty group)."""
+    dy = np.asarray(dy, np.float64)
+    x = np.asarray(x, np.float64)
+    G = len(base) - 1
+    out = np.zeros((G, dy.shape[1], x.shape[1]), np.float64)
+    for g, lo, hi in _groups(base):
+        out[g] = alpha * (dy[lo:hi].T @ x[lo:hi])
+    return out
+
+
+def _sigmoid(a):
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-a))
+
+
+def scaled_swiglu_fwd(h, p):
+    """y = p * silu(a) * b with a, b the two halves of h [T, 2F]; p [T]."""
+    h = np.asarray(h, np.float64)
+    F = h.shape[1] // 2
+    a, b = h[:, :F], h[:, F:]
+    return np.asarray(p, np.float64)[:, None] * (a * _sigmoid(a)) * b
+
+
+def scaled_swiglu_bwd(gy, h, p):
+    """Gradients of y = p * silu(a) * b given dL/dy.
+
+    da = gy * p * b * silu'(a),  silu'(a) = s(a) * (1 + a * (1 - s(a)))
+    db = gy * p * silu(a)
+    dp = sum_j gy_j * silu(a_j) * b_j        (the per-token "grad_scales")
+    Returns (dh [T, 2F] = [da, db], dp [T]).
+    """
+    gy = np.asarray(gy, np.float64)
+    h = np.asarray(h, np.float64)
+    p = np.asarray(p, np.float64)[:, None]
+    F = h.shape[1] // 2
+    a, b = h[:, :F], h[:, F:]
+    s = _sigmoid(a)
+    silu = a * s
+    dsilu = s * (1.0 + a * (1.0 - s))
+    da = gy * p * b * dsilu
+    db = gy * p * silu
+    dp = np.sum(gy * silu * b, axis=1)
+    return np.concatenate([da, db], axis=1), dp
+
+
+def grouped_mlp_fwd(x, w1, w2, p, base):
+    """fc1 -> scaled SwiGLU -> fc2. Returns dict(h, y, out)."""
+    h = grouped_linear_fwd(x, w1, base)
+    y = scaled_swiglu_fwd(h, p)
+    out = grouped_linear_fwd(y, w2, base)
+    return {"h": h, "y": y, "out": out}
+
+
+def grouped_mlp_bwd(dout, x, w1, w2, p, base, h=None, y=None):
+    """Backward of ``grouped_mlp_fwd`` given dL/dout.
+
+    Returns dict(gy = dL/dy, dh, dp, dw2, dx, dw1). ``h`` and ``y`` are
+    recomputed in fp64 when not given.
+    """
+    if h is None:
+        h = grouped_linear_fwd(x, w1, base)
+    if y is None:
+        y = scaled_swiglu_fwd(h, p)
+    gy = grouped_linear_dgrad(dout, w2, base)
+    dh, dp = scaled_swiglu_bwd(gy, h, p)
+    dw2 = grouped_linear_wgrad(dout, y, base)
+    dx = grouped_linear_dgrad(dh, w1, base)
+    dw1 = grouped_linear_wgrad(dh, x, base)
+    return {"gy": gy, "dh": dh, "dp": dp, "dw2": dw2, "dx": dx, "dw1": dw1}

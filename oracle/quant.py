@@ -1,0 +1,136 @@
+"""Quantizers: FP8 E4M3 with per-tensor current scaling, and MXFP8.
+
+Test infrastructure (see the package docstring): never used by the product path.
+
+Per-tensor current scaling follows "NVIDIA TransformerEngine PyTorch Ext
+Normalization", Description: for current scaling the amax of the tensor is
+computed first, then the tensor is quantized with a scale derived from it.
+The scale is 448/amax (448 is the E4M3 maximum). The pages give no formula
+for the inverse scale or for degenerate amax values; the readings taken are:
+
+* ``scale = fp32(448 / amax)`` with IEEE correctly rounded fp32 division;
+  ``amax == 0`` gives ``scale = 1``; a quotient that overflows fp32 is clamped
+  to the largest finite fp32 value.
+* ``scale_inv = fp32(1 / scale)``.
+* ``q = e4m3(fp32(x * scale))``: one fp32 multiply, rounded, then converted.
+
+MXFP8 ("core.tensor_parallel.inference_layers", ``_apply_linear`` with an
+MXFP8Tensor weight) stores E4M3 data with one E8M0 scale per 32 consecutive
+elements along the contraction dimension. The pages give no rule for the
+shared exponent; the plainest published one is OCP MX v1.0 section 6.3:
+``X = floor(log2(max|v|)) - emax_elem`` with ``emax_elem = 8`` for E4M3,
+clamped to the E8M0 range [-127, 127]; elements are ``e4m3(v / 2^X)`` with
+saturation. An all-zero block takes X = -127 (the smallest scale).
+"""
+
+import numpy as np
+
+from .codecs import bf16_to_f32, e4m3_encode, e4m3_decode, e8m0_decode, E4M3_MAX
+
+MX_BLOCK = 32
+E4M3_EMAX = 8          # floor(log2(448))
+_FLT_MAX = np.float32(np.finfo(np.float32).max)
+
+
+# ------------------------------------------------- per-tensor (current) -----
+def amax(x_bits):
+    """max_i |x_i| of a bf16 tensor, as float32 (exact: a max has no rounding)."""
+    x = bf16_to_f32(x_bits)
+    if x.size == 0:
+        return np.float32(0.0)
+    return np.float32(np.max(np.abs(x)))
+
+
+def fp8_scale(amax_f32):
+    """scale = fp32(448 / amax), with the degenerate readings of the module docstring."""
+    a = np.float32(amax_f32)
+    if a == 0:
+        return np.float32(1.0)
+    with np.errstate(over="ignore", divide="ignore"):
+        s = np.float32(E4M3_MAX) / a             # numpy fp32 '/' is IEEE RN division
+    if not np.isfinite(s):
+        s = _FLT_MAX
+    return np.float32(s)
+
+
+def fp8_scale_inv(scale_f32):
+    """scale_inv = fp32(1 / scale)."""
+    return np.float32(np.float32(1.0) / np.float32(scale_f32))
+
+
+def fp8_quantize_with_scale(x_bits, scale_f32):
+    """E4M3 codes of fp32(x * scale) for every element of a bf16 tensor."""
+    with np.errstate(over="ignore"):
+        prod = bf16_to_f32(x_bits) * np.float32(scale_f32)   # fp32 multiply, RN
+    return e4m3_encode(prod)
+
+
+def fp8_current_scaling(x_bits):
+    """Full per-tensor current scaling of a bf16 matrix [R, C].
+
+    Returns a dict with ``amax``, ``scale``, ``scale_inv`` (float32 scalars),
+    ``q`` (uint8 [R, C]) and ``q_t`` (uint8 [C, R], the transpose of ``q``;
+    the scale is per tensor, so orientation changes no byte).
+    """
+    a = amax(x_bits)
+    s = fp8_scale(a)
+    q = fp8_quantize_with_scale(x_bits, s)
+    return {"amax": a, "scale": s, "scale_inv": fp8_scale_inv(s), "q": q,
+            "q_t": np.ascontiguousarray(q.T)}
+
+
+def fp8_dequantize(q, scale_inv_f32):
+    """Exact fp64 value each code stands for: e4m3(q) * scale_inv."""
+    return e4m3_decode(q) * np.float64(np.float32(scale_inv_f32))
+
+
+# ------------------------------------------------------------- MXFP8 --------
+def mx_shared_exponent(block_amax_f32):
+    """OCP MX v1.0 section 6.3 shared exponent of blocks with the given amax.
+
+    X = floor(log2(amax)) - 8, clamped to [-127, 127]; amax == 0 gives -127.
+    floor(log2(a)) of a positive float is read off frexp exactly.
+    """
+    a = np.asarray(block_amax_f32, dtype=np.float32).astype(np.float64)
+    _, e2 = np.frexp(np.where(a > 0, a, 1.0))      # a = f * 2^e2, f in [0.5, 1)
+    x = (e2.astype(np.int64) - 1) - E4M3_EMAX
+    x = np.where(a > 0, x, -127)
+    return np.clip(x, -127, 127)
+
+
+def mxfp8_rowwise(x_bits):
+    """MXFP8 with blocks of 32 along the last dim of a bf16 matrix [R, C].
+
+    Returns (q uint8 [R, C], s uint8 [R, C/32]) with s the E8M0 byte X + 127.
+    C must be a multiple of 32.
+    """
+    x = bf16_to_f32(x_bits)
+    R, C = x.shape
+    if C % MX_BLOCK:
+        raise ValueError("MXFP8 needs the blocked dimension to be a multiple of 32")
+    blocks = x.reshape(R, C // MX_BLOCK, MX_BLOCK)
+    bamax = np.max(np.abs(blocks), axis=2) if x.size else np.zeros((R, 0), np.float32)
+    X = mx_shared_exponent(bamax)                                   # [R, C/32]
+    inv = np.ldexp(np.float32(1.0), -X).astype(np.float32)          # 2^-X, exact in fp32
+    with np.errstate(over="ignore", under="ignore"):
+        scaled = (blocks * inv[:, :, None]).astype(np.float32)      # exact power-of-two scaling
+    q = e4m3_encode(scaled).reshape(R, C)
+    return q, (X + 127).astype(np.uint8)
+
+
+def mxfp8_colwise(x_bits):
+    """MXFP8 with blocks of 32 along the first dim, stored transposed.
+
+    Defined as the rowwise quantization of x^T: returns (q_colT uint8 [C, R],
+    s_colT uint8 [C, R/32]). This is the operand a GEMM contracting over the
+    rows of x consumes.
+    """
+    return mxfp8_rowwise(np.ascontiguousarray(np.asarray(x_bits, dtype=np.uint16).T))
+
+
+def mx_dequantize(q, s):
+    """Exact fp64 value: e4m3(q) * 2^(s-127), the scale repeated over each block of 32."""
+    q = np.asarray(q)
+    R, C = q.shape
+    sc = np.repeat(e8m0_decode(s), MX_BLOCK, axis=1)[:, :C]
+    return e4m3_decode(q) * sc
