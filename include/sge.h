@@ -1,0 +1,255 @@
+/*
+ * sge.h — C ABI of libsge, the fused scaled linear for AMD Instinct MI355X (gfx950).
+ *
+ * Every call validates its arguments on the host before any HIP call, then
+ * enqueues its kernels on the caller's stream and returns without waiting:
+ * no call synchronizes, copies to the host or allocates device memory, so
+ * every call can be captured in a HIP graph. Device faults surface at the
+ * caller's next synchronization.
+ *
+ * Ownership: every pointer is caller-owned. Pointers documented "device" must
+ * point to device memory of the current device; "host" pointers are read
+ * during the call only. Workspaces are sized by the matching *_workspace_size
+ * query and passed in by the caller (query, allocate, execute).
+ *
+ * Errors: a call returns SGE_OK or the first error found, in this order:
+ * NULL pointer, shape, format, alignment, aliasing, workspace, then HIP
+ * launch errors. sge_last_error_message() gives a thread-local description.
+ * On an error before launch nothing was enqueued and no output was touched.
+ *
+ * Matrices are row-major. A bf16 matrix is stored as 16-bit patterns; an E4M3
+ * matrix as bytes (OCP OFP8 E4M3, max 448); an E8M0 scale array as bytes
+ * (2^(s-127)). Leading dimensions are in elements. Base pointers must be
+ * 16-byte aligned and leading dimensions a multiple of 16 bytes.
+ */
+#ifndef SGE_H
+#define SGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SGE_ABI_VERSION 1
+
+typedef enum {
+  SGE_OK = 0,
+  SGE_ERR_NULL = 1,        /* a required pointer is NULL */
+  SGE_ERR_SHAPE = 2,       /* negative or inconsistent sizes, or a size the path does not tile */
+  SGE_ERR_FORMAT = 3,      /* unknown or unsupported operand format / layout combination */
+  SGE_ERR_ALIGN = 4,       /* base pointer or leading dimension not 16-byte aligned */
+  SGE_ERR_ALIAS = 5,       /* an output overlaps an input it may not overlap */
+  SGE_ERR_WORKSPACE = 6,   /* workspace missing or smaller than the query returned */
+  SGE_ERR_ARG = 7,         /* any other invalid argument (flag values, counts) */
+  SGE_ERR_HIP = 8          /* a HIP runtime call failed */
+} sge_status;
+
+/* Operand formats. */
+typedef enum {
+  SGE_FMT_BF16 = 0,        /* bf16 values */
+  SGE_FMT_E4M3 = 1,        /* E4M3 bytes with one per-tensor fp32 scale_inv (current scaling) */
+  SGE_FMT_MXFP8 = 2        /* E4M3 bytes with one E8M0 scale per 32 elements along the contraction dim */
+} sge_format;
+
+/*
+ * One GEMM operand: a logical matrix [outer, inner] where inner is the
+ * dimension the GEMM contracts over.
+ *   inner_contiguous = 1: stored as [outer][inner], element (o, i) at data[o*ld + i]
+ *   inner_contiguous = 0: stored as [inner][outer], element (o, i) at data[i*ld + o]
+ *                          (bf16 only; E4M3/MXFP8 operands are always
+ *                          inner-contiguous: the quantizers write the transposed
+ *                          copies the backward needs)
+ * scale_inv: E4M3 only, device fp32[1] (the value x ~= e4m3(q) * scale_inv).
+ * mx_scale:  MXFP8 only, device E8M0 bytes [outer][inner/32] with leading
+ *            dimension mx_ld (bytes); element (o, i) is e4m3(q) * 2^(s[o][i/32]-127).
+ */
+typedef struct {
+  const void* data;
+  int64_t outer;
+  int64_t inner;
+  int64_t ld;
+  int32_t inner_contiguous;
+  int32_t format;              /* sge_format */
+  const float* scale_inv;
+  const uint8_t* mx_scale;
+  int64_t mx_ld;
+} sge_operand;
+
+/* Epilogues of the grouped linear. */
+typedef enum {
+  SGE_EPI_NONE = 0,            /* out = alpha * acc */
+  SGE_EPI_SCALED_SWIGLU = 1,   /* forward: h = alpha*acc, y = p * silu(h[:, :F]) * h[:, F:] */
+  SGE_EPI_DSCALED_SWIGLU = 2   /* backward: dgrad g of the next layer -> dh = [da, db], dp */
+} sge_epilogue;
+
+int sge_abi_version(void);
+const char* sge_status_string(sge_status s);
+const char* sge_last_error_message(void);
+
+/*
+ * Forward of the fused scaled linear.
+ * ("NVIDIA TransformerEngine Ops Fused Forward Linear Scale Add", Description
+ * and I/O Contract: the scale is the GEMM alpha and the residual buffer is the
+ * GEMM output with accumulation on.)
+ *
+ *   residual[m][n] <- bf16( (accumulate ? fp32(residual[m][n]) : 0) + alpha_eff * sum_k x[m][k] * w[n][k] )
+ *
+ * x: operand [M, K] (outer M); w: operand [N, K] (outer N); both the same format.
+ * alpha_eff = alpha (BF16, MXFP8) or fp32(fp32(x.scale_inv * w.scale_inv) * alpha) (E4M3).
+ * Sums are fp32 (MFMA), rounded once to bf16 (nearest-even).
+ * residual: device bf16 [M, N], leading dimension ld_res; read and written in place.
+ * alpha == 0: nothing is read or written when accumulate != 0 (the residual is
+ * returned bit-exactly); with accumulate == 0 the output is filled with +0.
+ * Shapes: K % 8 == 0 (bf16), % 16 (E4M3), % 32 (MXFP8); N % 8 == 0; M >= 0 any.
+ * Aliasing: residual may not overlap x or w (SGE_ERR_ALIAS).
+ */
+sge_status sge_linear_scale_add_fwd(const sge_operand* x, const sge_operand* w, void* residual,
+                                    int64_t ld_res, float alpha, int32_t accumulate,
+                                    hipStream_t stream);
+
+/*
+ * Backward of the fused scaled linear, alpha folded into both GEMMs.
+ * ("NVIDIA TransformerEngine Ops Fused Backward Linear Scale", Description and
+ * I/O Contract: the scale is passed as grad_input_alpha and grad_weight_alpha.)
+ *
+ *   dgrad[m][k] = bf16( dgrad_alpha_eff * sum_n dy[m][n] * w[n][k] )     [M, K]
+ *   wgrad[n][k] = bf16( wgrad_alpha_eff * sum_m dy[m][n] * x[m][k] )     [N, K]
+ *
+ * Operands are given in GEMM form (outer, inner = contraction):
+ *   dg_a = dy as [M, N]   (bf16: dy itself, inner-contiguous; E4M3/MX: quantized dy)
+ *   dg_b = w  as [K, N]   (bf16: w itself with inner_contiguous = 0; E4M3: the
+ *                          transposed copy q_t(w) [K][N]; MX: w quantized in blocks along N, stored [K][N])
+ *   wg_a = dy as [N, M]   (bf16: dy with inner_contiguous = 0; E4M3/MX: transposed copy [N][M])
+ *   wg_b = x  as [K, M]   (bf16: x with inner_contiguous = 0; E4M3/MX: transposed copy [K][M])
+ * dgrad / wgrad: device bf16 outputs (overwritten, not accumulated); either may
+ * be NULL to skip that GEMM (its operands may then be NULL too).
+ * alpha == 0 fills that output with +0 without reading its operands.
+ */
+sge_status sge_linear_scale_bwd(const sge_operand* dg_a, const sge_operand* dg_b,
+                                const sge_operand* wg_a, const sge_operand* wg_b,
+                                void* dgrad, int64_t ld_dgrad, void* wgrad, int64_t ld_wgrad,
+                                float dgrad_alpha, float wgrad_alpha, hipStream_t stream);
+
+/*
+ * FP8 E4M3 per-tensor current scaling of a bf16 matrix [rows, cols].
+ * ("NVIDIA TransformerEngine PyTorch Ext Normalization", Description: for
+ * current scaling the amax is computed, then the tensor is quantized.)
+ *
+ *   amax = max |x|;  scale = fp32(448 / amax) (1 if amax == 0, FLT_MAX on overflow);
+ *   scale_inv = fp32(1 / scale);  q = e4m3_sat_rne(fp32(x * scale))
+ *
+ * src: device bf16 [rows][cols] (leading dimension cols).
+ * q: device bytes [rows][cols] or NULL; q_t: device bytes [cols][rows] (the
+ * transpose) or NULL. amax, scale, scale_inv: device fp32[1] each (required).
+ * workspace: device, at least sge_quantize_fp8_amax_workspace_size(rows, cols) bytes.
+ * Shapes: rows % 16 == 0 and cols % 16 == 0.
+ * Two kernels: a block-wise amax, then a quantize pass that finishes the amax.
+ * Non-finite inputs are outside the contract.
+ */
+size_t sge_quantize_fp8_amax_workspace_size(int64_t rows, int64_t cols);
+sge_status sge_quantize_fp8_amax(const void* src, int64_t rows, int64_t cols, uint8_t* q,
+                                 uint8_t* q_t, float* amax, float* scale, float* scale_inv,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * MXFP8 quantization of a bf16 matrix [rows, cols], rowwise and/or columnwise.
+ * (MXFP8 operands: "core.tensor_parallel.inference_layers", _apply_linear with an
+ * MXFP8Tensor; the shared exponent follows OCP MX v1.0 section 6.3.)
+ *
+ * Per block of 32: X = clamp(floor(log2(max|v|)) - 8, -127, 127) (-127 for an
+ * all-zero block), scale byte X + 127, q = e4m3_sat_rne(v * 2^-X).
+ * Rowwise: blocks along cols -> q_row [rows][cols], s_row [rows][cols/32].
+ * Columnwise: blocks along rows, stored transposed -> q_colT [cols][rows],
+ * s_colT [cols][rows/32]. Either pair may be NULL (not both).
+ * Shapes: cols % 32 == 0; rows % 32 == 0 when the columnwise copy is requested.
+ */
+sge_status sge_quantize_mxfp8(const void* src, int64_t rows, int64_t cols, uint8_t* q_row,
+                              uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT,
+                              hipStream_t stream);
+
+/*
+ * Per-group split sizes to tensor offsets, computed once and reused by the
+ * forward and the backward.
+ * ("Activation + GroupedLinear Fusion for MOE and other MOE optimizations",
+ * Description, Precomputed Tensor Offsets Optimization.)
+ *
+ *   base[0] = 0, base[g+1] = base[g] + splits[g];  offsets[i][g] = base[g] * multipliers[i]
+ *
+ * splits: device int64 [G]; multipliers: host int64 [n_mult] (1 <= n_mult <= 8);
+ * offsets: device int64 [n_mult][G+1]. 1 <= G <= 4096.
+ * err_flag: device int32[1] or NULL; when given, it is set to 1 if any split is
+ * negative or base[G] != expected_total (pass expected_total < 0 to skip the
+ * total check) and to 0 otherwise.
+ */
+sge_status sge_splits_to_offsets(const int64_t* splits, int32_t G, const int64_t* multipliers,
+                                 int32_t n_mult, int64_t expected_total, int64_t* offsets,
+                                 int32_t* err_flag, hipStream_t stream);
+
+/*
+ * Grouped linear forward over token groups given by device offsets (no host sync).
+ * ("Activation + GroupedLinear Fusion for MOE and other MOE optimizations",
+ * Description and Sequence Diagram.)
+ *
+ * Tokens t in [offsets[g], offsets[g+1]) use weight W_g:
+ *   h[t] = alpha * x[t] @ W_g^T                             x [T, K] bf16, W [G, N, K] bf16
+ * SGE_EPI_NONE:          out [T, N] bf16 = h.
+ * SGE_EPI_SCALED_SWIGLU: F = N/2, a = h[:, :F], b = h[:, F:];
+ *                        out [T, F] bf16 = p[t] * silu(a) * b (from the fp32 h),
+ *                        preact [T, N] bf16 = h (saved for the backward; may be NULL).
+ * offsets: device int64 [G+1] (row 0 of sge_splits_to_offsets with multiplier 1);
+ * values are clamped into [0, T] and made non-decreasing before use.
+ * probs: device fp32 [T] (SWIGLU only). Shapes: K % 8 == 0, N % 8 == 0
+ * (SWIGLU: N % 256 == 0).
+ */
+sge_status sge_grouped_linear_fwd(const void* x, const void* w, int32_t G, int64_t T, int64_t N,
+                                  int64_t K, const int64_t* offsets, float alpha, int32_t epilogue,
+                                  const float* probs, void* out, void* preact, hipStream_t stream);
+
+/*
+ * Grouped linear backward for one layer with the precomputed offsets.
+ * ("Activation + GroupedLinear Fusion for MOE and other MOE optimizations",
+ * Greptile Summary and Sequence Diagram: the backward reuses the forward's
+ * offsets; the activation backward returns the gradient of the scales.)
+ *
+ * dy [T, N] bf16, x [T, K] bf16 (the layer input), W [G, N, K] bf16.
+ *   g[t]  = alpha * dy[t] @ W_g                                      [T, K]
+ *   dW_g  = alpha * sum_{t in g} dy[t]^T x[t]                         [G, N, K] (0 for empty groups)
+ * SGE_EPI_NONE:           dx [T, K] bf16 = g (dx may be NULL to skip).
+ * SGE_EPI_DSCALED_SWIGLU: the layer input x was y = p * silu(a) * b with
+ *                         preact h = [a, b] [T, 2K] bf16; writes
+ *                         dact [T, 2K] bf16 = [g*p*b*silu'(a), g*p*silu(a)] and
+ *                         dprobs [T] fp32 = sum_j g*silu(a)*b (deterministic order).
+ *                         dx is not used.
+ * dw: device bf16 [G, N, K] or NULL to skip the weight gradient.
+ * workspace: device, >= sge_grouped_linear_bwd_workspace_size(T, K, G, epilogue) bytes
+ * (0 is valid for SGE_EPI_NONE).
+ */
+size_t sge_grouped_linear_bwd_workspace_size(int64_t T, int64_t K, int32_t G, int32_t epilogue);
+sge_status sge_grouped_linear_bwd(const void* dy, const void* x, const void* w, int32_t G,
+                                  int64_t T, int64_t N, int64_t K, const int64_t* offsets,
+                                  float alpha, int32_t epilogue, const void* preact,
+                                  const float* probs, void* dact, float* dprobs, void* dx,
+                                  void* dw, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/*
+ * Unfused per-token scaled SwiGLU (the composition the fused epilogues replace).
+ * ("Activation + GroupedLinear Fusion for MOE and other MOE optimizations",
+ * Description: scaled SwiGLU tex API.)
+ * fwd: y [T, F] = p * silu(h[:, :F]) * h[:, F:]           h [T, 2F] bf16, p [T] fp32
+ * bwd: dh [T, 2F] = [gy*p*b*silu'(a), gy*p*silu(a)], dp [T] = sum_j gy*silu(a)*b
+ * Shapes: F % 8 == 0.
+ */
+sge_status sge_scaled_swiglu_fwd(const void* h, const float* probs, void* y, int64_t T, int64_t F,
+                                 hipStream_t stream);
+sge_status sge_scaled_swiglu_bwd(const void* gy, const void* h, const float* probs, void* dh,
+                                 float* dprobs, int64_t T, int64_t F, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGE_H */

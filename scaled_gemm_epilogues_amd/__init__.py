@@ -1,0 +1,218 @@
+"""Python binding of libsge, the fused scaled linear for MI355X (gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of
+``libsge.so``. Tensors are torch tensors on the current HIP device; calls are
+enqueued on ``torch.cuda.current_stream()`` unless a stream is given. The
+library is loaded after torch so both share one HIP runtime. There is no CPU
+fallback: importing this package fails loudly when the library is missing.
+
+Names follow the C ABI in ``include/sge.h``.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsge.so")
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m scaled_gemm_epilogues_amd.build`")
+
+_lib = ctypes.CDLL(_LIB_PATH)
+
+# status codes
+OK, ERR_NULL, ERR_SHAPE, ERR_FORMAT, ERR_ALIGN, ERR_ALIAS, ERR_WORKSPACE, ERR_ARG, ERR_HIP = range(9)
+# operand formats
+FMT_BF16, FMT_E4M3, FMT_MXFP8 = 0, 1, 2
+# grouped epilogues
+EPI_NONE, EPI_SCALED_SWIGLU, EPI_DSCALED_SWIGLU = 0, 1, 2
+
+EXPORTED = (
+    "sge_abi_version", "sge_status_string", "sge_last_error_message",
+    "sge_linear_scale_add_fwd", "sge_linear_scale_bwd",
+    "sge_quantize_fp8_amax_workspace_size", "sge_quantize_fp8_amax", "sge_quantize_mxfp8",
+    "sge_splits_to_offsets", "sge_grouped_linear_fwd",
+    "sge_grouped_linear_bwd_workspace_size", "sge_grouped_linear_bwd",
+    "sge_scaled_swiglu_fwd", "sge_scaled_swiglu_bwd",
+)
+
+
+class SgeOperand(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p), ("outer", ctypes.c_int64), ("inner", ctypes.c_int64),
+        ("ld", ctypes.c_int64), ("inner_contiguous", ctypes.c_int32), ("format", ctypes.c_int32),
+        ("scale_inv", ctypes.c_void_p), ("mx_scale", ctypes.c_void_p), ("mx_ld", ctypes.c_int64),
+    ]
+
+
+class SgeError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{_lib.sge_status_string(status).decode()}: {message}")
+        self.status = status
+
+
+_vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+_OP = ctypes.POINTER(SgeOperand)
+_SIGS = {
+    "sge_abi_version": ([], ctypes.c_int),
+    "sge_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "sge_last_error_message": ([], ctypes.c_char_p),
+    "sge_linear_scale_add_fwd": ([_OP, _OP, _vp, _i64, _f32, _i32, _vp], ctypes.c_int),
+    "sge_linear_scale_bwd": ([_OP, _OP, _OP, _OP, _vp, _i64, _vp, _i64, _f32, _f32, _vp], ctypes.c_int),
+    "sge_quantize_fp8_amax_workspace_size": ([_i64, _i64], _sz),
+    "sge_quantize_fp8_amax": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "sge_quantize_mxfp8": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "sge_splits_to_offsets": ([_vp, _i32, ctypes.POINTER(_i64), _i32, _i64, _vp, _vp, _vp], ctypes.c_int),
+    "sge_grouped_linear_fwd": ([_vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _vp, _vp, _vp, _vp],
+                               ctypes.c_int),
+    "sge_grouped_linear_bwd_workspace_size": ([_i64, _i64, _i32, _i32], _sz),
+    "sge_grouped_linear_bwd": ([_vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _vp, _vp, _vp, _vp,
+                                _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "sge_scaled_swiglu_fwd": ([_vp, _vp, _vp, _i64, _i64, _vp], ctypes.c_int),
+    "sge_scaled_swiglu_bwd": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp], ctypes.c_int),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def abi_version():
+    return _lib.sge_abi_version()
+
+
+def _check(status):
+    if status != OK:
+        raise SgeError(status, _lib.sge_last_error_message().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ----------------------------------------------------------------- operands
+class Operand:
+    """A GEMM operand: logical [outer, inner] with inner the contraction dim.
+
+    Build with ``Operand.bf16``, ``Operand.e4m3`` or ``Operand.mxfp8``; the
+    tensors are kept alive by the object.
+    """
+
+    def __init__(self, data, outer, inner, ld, inner_contiguous, fmt, scale_inv=None, mx_scale=None,
+                 mx_ld=0):
+        self.keep = (data, scale_inv, mx_scale)
+        self.c = SgeOperand(data.data_ptr() if data is not None else None, outer, inner, ld,
+                            1 if inner_contiguous else 0, fmt,
+                            scale_inv.data_ptr() if scale_inv is not None else None,
+                            mx_scale.data_ptr() if mx_scale is not None else None, mx_ld)
+
+    @classmethod
+    def bf16(cls, t, transposed=False):
+        """``t`` stored [outer, inner]; with ``transposed=True`` it is stored [inner, outer]."""
+        assert t.dtype == torch.bfloat16 and t.dim() == 2 and t.stride(1) == 1
+        if transposed:
+            return cls(t, t.shape[1], t.shape[0], t.stride(0), False, FMT_BF16)
+        return cls(t, t.shape[0], t.shape[1], t.stride(0), True, FMT_BF16)
+
+    @classmethod
+    def e4m3(cls, q, scale_inv):
+        """E4M3 bytes ``q`` [outer, inner] (uint8 or float8_e4m3fn) with device fp32[1] scale_inv."""
+        assert q.dim() == 2 and q.stride(1) == 1 and q.element_size() == 1
+        return cls(q, q.shape[0], q.shape[1], q.stride(0), True, FMT_E4M3, scale_inv=scale_inv)
+
+    @classmethod
+    def mxfp8(cls, q, s):
+        """E4M3 bytes ``q`` [outer, inner] with E8M0 scales ``s`` [outer, inner/32] (uint8)."""
+        assert q.dim() == 2 and q.stride(1) == 1 and s.dim() == 2 and s.stride(1) == 1
+        return cls(q, q.shape[0], q.shape[1], q.stride(0), True, FMT_MXFP8, mx_scale=s, mx_ld=s.stride(0))
+
+
+def _op(o):
+    return None if o is None else ctypes.byref(o.c)
+
+
+# -------------------------------------------------------------- dense path
+def linear_scale_add_fwd(x, w, residual, alpha, accumulate=True, stream=None):
+    """residual <- residual + alpha * x @ w^T in place (bf16 [M, N]); x, w are Operands."""
+    _check(_lib.sge_linear_scale_add_fwd(_op(x), _op(w), _ptr(residual), residual.stride(0), float(alpha),
+                                         1 if accumulate else 0, _stream(stream)))
+    return residual
+
+
+def linear_scale_bwd(dg_a, dg_b, wg_a, wg_b, dgrad, wgrad, dgrad_alpha, wgrad_alpha, stream=None):
+    """dgrad = a_d * dy @ W and wgrad = a_w * dy^T @ x (operands in GEMM form, see sge.h)."""
+    _check(_lib.sge_linear_scale_bwd(_op(dg_a), _op(dg_b), _op(wg_a), _op(wg_b), _ptr(dgrad),
+                                     dgrad.stride(0) if dgrad is not None else 0, _ptr(wgrad),
+                                     wgrad.stride(0) if wgrad is not None else 0, float(dgrad_alpha),
+                                     float(wgrad_alpha), _stream(stream)))
+
+
+def quantize_fp8_amax_workspace_size(rows, cols):
+    return int(_lib.sge_quantize_fp8_amax_workspace_size(rows, cols))
+
+
+def quantize_fp8_amax(src, q, q_t, amax, scale, scale_inv, workspace, stream=None):
+    """Per-tensor current scaling of bf16 ``src`` [rows, cols] into E4M3 ``q`` and/or ``q_t``."""
+    rows, cols = src.shape
+    _check(_lib.sge_quantize_fp8_amax(_ptr(src), rows, cols, _ptr(q), _ptr(q_t), _ptr(amax), _ptr(scale),
+                                      _ptr(scale_inv), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def quantize_mxfp8(src, q_row=None, s_row=None, q_colT=None, s_colT=None, stream=None):
+    """MXFP8 rowwise and/or columnwise (transposed) quantization of bf16 ``src`` [rows, cols]."""
+    rows, cols = src.shape
+    _check(_lib.sge_quantize_mxfp8(_ptr(src), rows, cols, _ptr(q_row), _ptr(s_row), _ptr(q_colT), _ptr(s_colT),
+                                   _stream(stream)))
+
+
+# ------------------------------------------------------------ grouped path
+def splits_to_offsets(splits, multipliers, offsets, expected_total=-1, err_flag=None, stream=None):
+    """offsets [n, G+1] int64 = exclusive prefix sum of device ``splits`` [G] times each multiplier."""
+    m = (ctypes.c_int64 * len(multipliers))(*[int(v) for v in multipliers])
+    _check(_lib.sge_splits_to_offsets(_ptr(splits), splits.numel(), m, len(multipliers), int(expected_total),
+                                      _ptr(offsets), _ptr(err_flag), _stream(stream)))
+
+
+def grouped_linear_fwd(x, w, offsets, out, alpha=1.0, epilogue=EPI_NONE, probs=None, preact=None, stream=None):
+    """Grouped forward: x [T, K], w [G, N, K], offsets [G+1] (device) -> out (and preact for SwiGLU)."""
+    G, N, K = w.shape
+    T = x.shape[0]
+    _check(_lib.sge_grouped_linear_fwd(_ptr(x), _ptr(w), G, T, N, K, _ptr(offsets), float(alpha), epilogue,
+                                       _ptr(probs), _ptr(out), _ptr(preact), _stream(stream)))
+
+
+def grouped_linear_bwd_workspace_size(T, K, G, epilogue):
+    return int(_lib.sge_grouped_linear_bwd_workspace_size(T, K, G, epilogue))
+
+
+def grouped_linear_bwd(dy, x, w, offsets, alpha=1.0, epilogue=EPI_NONE, preact=None, probs=None, dact=None,
+                       dprobs=None, dx=None, dw=None, workspace=None, stream=None):
+    """Grouped backward of one layer (see sge.h): dgrad (optionally through dSwiGLU) and wgrad."""
+    G, N, K = w.shape
+    T = dy.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.sge_grouped_linear_bwd(_ptr(dy), _ptr(x), _ptr(w), G, T, N, K, _ptr(offsets), float(alpha),
+                                       epilogue, _ptr(preact), _ptr(probs), _ptr(dact), _ptr(dprobs), _ptr(dx),
+                                       _ptr(dw), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def scaled_swiglu_fwd(h, probs, y, stream=None):
+    T, F2 = h.shape
+    _check(_lib.sge_scaled_swiglu_fwd(_ptr(h), _ptr(probs), _ptr(y), T, F2 // 2, _stream(stream)))
+
+
+def scaled_swiglu_bwd(gy, h, probs, dh, dprobs, stream=None):
+    T, F2 = h.shape
+    _check(_lib.sge_scaled_swiglu_bwd(_ptr(gy), _ptr(h), _ptr(probs), _ptr(dh), _ptr(dprobs), T, F2 // 2,
+                                      _stream(stream)))

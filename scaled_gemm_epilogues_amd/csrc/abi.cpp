@@ -1,0 +1,467 @@
+// C ABI of libsge: argument validation (host only, before any HIP call) and dispatch.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/sge.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_msg;
+
+sge_status fail(sge_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_msg = buf;
+  return s;
+}
+
+sge_status ok() {
+  g_msg.clear();
+  return SGE_OK;
+}
+
+sge_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SGE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_size(int fmt) { return fmt == SGE_FMT_BF16 ? 2 : 1; }
+
+// Byte range [lo, hi) touched by a row-major matrix.
+struct Range {
+  uintptr_t lo, hi;
+};
+Range range_of(const void* p, int64_t rows, int64_t cols, int64_t ld, int es) {
+  const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+  if (rows <= 0 || cols <= 0) return {b, b};
+  return {b, b + (uintptr_t)(((rows - 1) * ld + cols) * es)};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+Range operand_range(const sge_operand& o) {
+  const int64_t rows = o.inner_contiguous ? o.outer : o.inner;
+  const int64_t cols = o.inner_contiguous ? o.inner : o.outer;
+  return range_of(o.data, rows, cols, o.ld, elem_size(o.format));
+}
+
+// Checks one GEMM operand in the order NULL, shape, format, alignment.
+sge_status check_operand(const sge_operand* o, const char* name) {
+  if (!o) return fail(SGE_ERR_NULL, "%s: operand descriptor is NULL", name);
+  if (o->outer < 0 || o->inner < 0) return fail(SGE_ERR_SHAPE, "%s: negative size", name);
+  const bool empty = o->outer == 0 || o->inner == 0;
+  if (!empty && !o->data) return fail(SGE_ERR_NULL, "%s: data is NULL", name);
+  if (o->format == SGE_FMT_E4M3 && !o->scale_inv) return fail(SGE_ERR_NULL, "%s: scale_inv is NULL", name);
+  if (o->format == SGE_FMT_MXFP8 && !empty && !o->mx_scale)
+    return fail(SGE_ERR_NULL, "%s: mx_scale is NULL", name);
+  const int64_t min_ld = o->inner_contiguous ? o->inner : o->outer;
+  if (o->ld < min_ld || o->ld <= 0) return fail(SGE_ERR_SHAPE, "%s: ld %lld < %lld", name, (long long)o->ld,
+                                                (long long)min_ld);
+  switch (o->format) {
+    case SGE_FMT_BF16:
+      if (o->inner_contiguous && o->inner % 8)
+        return fail(SGE_ERR_SHAPE, "%s: bf16 contraction dim %lld not a multiple of 8", name, (long long)o->inner);
+      if (!o->inner_contiguous && o->outer % 8)
+        return fail(SGE_ERR_SHAPE, "%s: bf16 transposed operand needs outer %% 8 == 0 (got %lld)", name,
+                    (long long)o->outer);
+      break;
+    case SGE_FMT_E4M3:
+      if (!o->inner_contiguous) return fail(SGE_ERR_FORMAT, "%s: E4M3 operands must be inner-contiguous", name);
+      if (o->inner % 16)
+        return fail(SGE_ERR_SHAPE, "%s: E4M3 contraction dim %lld not a multiple of 16", name, (long long)o->inner);
+      break;
+    case SGE_FMT_MXFP8:
+      if (!o->inner_contiguous) return fail(SGE_ERR_FORMAT, "%s: MXFP8 operands must be inner-contiguous", name);
+      if (o->inner % 32)
+        return fail(SGE_ERR_SHAPE, "%s: MXFP8 contraction dim %lld not a multiple of 32", name, (long long)o->inner);
+      if (o->mx_ld < o->inner / 32) return fail(SGE_ERR_SHAPE, "%s: mx_ld too small", name);
+      break;
+    default:
+      return fail(SGE_ERR_FORMAT, "%s: unknown format %d", name, o->format);
+  }
+  if (!aligned16(o->data) || (o->ld * elem_size(o->format)) % 16)
+    return fail(SGE_ERR_ALIGN, "%s: data or ld not 16-byte aligned", name);
+  return SGE_OK;
+}
+
+sge::GemmParams gemm_params(const sge_operand& a, const sge_operand& b, void* c, int64_t ldc, float alpha,
+                            int accumulate) {
+  sge::GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.a = static_cast<const uint8_t*>(a.data);
+  p.lda = a.ld;
+  p.b = static_cast<const uint8_t*>(b.data);
+  p.ldb = b.ld;
+  p.M = a.outer;
+  p.N = b.outer;
+  p.K = a.inner;
+  p.a_sinv = a.scale_inv;
+  p.b_sinv = b.scale_inv;
+  p.a_mx = a.mx_scale;
+  p.a_mx_ld = a.mx_ld;
+  p.b_mx = b.mx_scale;
+  p.b_mx_ld = b.mx_ld;
+  p.mx_aligned = (a.inner % 128 == 0) && (a.mx_ld % 4 == 0) && (b.mx_ld % 4 == 0) &&
+                 ((reinterpret_cast<uintptr_t>(a.mx_scale) & 3u) == 0) &&
+                 ((reinterpret_cast<uintptr_t>(b.mx_scale) & 3u) == 0);
+  p.alpha = alpha;
+  p.c = static_cast<uint16_t*>(c);
+  p.ldc = ldc;
+  p.accumulate = accumulate;
+  return p;
+}
+
+// Validates the pair (a, b) of one GEMM producing bf16 C [a.outer, b.outer].
+sge_status check_gemm(const sge_operand* a, const sge_operand* b, const void* c, int64_t ldc, const char* what) {
+  sge_status s = check_operand(a, "A");
+  if (s != SGE_OK) return s;
+  if ((s = check_operand(b, "B")) != SGE_OK) return s;
+  if (a->inner != b->inner)
+    return fail(SGE_ERR_SHAPE, "%s: contraction dims differ (%lld vs %lld)", what, (long long)a->inner,
+                (long long)b->inner);
+  if (a->format != b->format) return fail(SGE_ERR_FORMAT, "%s: operand formats differ", what);
+  if (a->outer > 0 && b->outer > 0 && !c) return fail(SGE_ERR_NULL, "%s: output is NULL", what);
+  if (b->outer % 8) return fail(SGE_ERR_SHAPE, "%s: output columns %lld not a multiple of 8", what,
+                                (long long)b->outer);
+  if (ldc < b->outer) return fail(SGE_ERR_SHAPE, "%s: output ld too small", what);
+  if (c && (!aligned16(c) || (ldc * 2) % 16)) return fail(SGE_ERR_ALIGN, "%s: output not 16-byte aligned", what);
+  const int64_t tiles = ((a->outer + 255) / 256) * ((b->outer + 255) / 256);
+  if (tiles > 0x7FFFFFFF) return fail(SGE_ERR_SHAPE, "%s: too many tiles", what);
+  return SGE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sge_abi_version(void) { return SGE_ABI_VERSION; }
+
+const char* sge_status_string(sge_status s) {
+  switch (s) {
+    case SGE_OK: return "SGE_OK";
+    case SGE_ERR_NULL: return "SGE_ERR_NULL";
+    case SGE_ERR_SHAPE: return "SGE_ERR_SHAPE";
+    case SGE_ERR_FORMAT: return "SGE_ERR_FORMAT";
+    case SGE_ERR_ALIGN: return "SGE_ERR_ALIGN";
+    case SGE_ERR_ALIAS: return "SGE_ERR_ALIAS";
+    case SGE_ERR_WORKSPACE: return "SGE_ERR_WORKSPACE";
+    case SGE_ERR_ARG: return "SGE_ERR_ARG";
+    case SGE_ERR_HIP: return "SGE_ERR_HIP";
+  }
+  return "unknown sge_status";
+}
+
+const char* sge_last_error_message(void) { return g_msg.c_str(); }
+
+sge_status sge_linear_scale_add_fwd(const sge_operand* x, const sge_operand* w, void* residual, int64_t ld_res,
+                                    float alpha, int32_t accumulate, hipStream_t stream) {
+  sge_status s = check_gemm(x, w, residual, ld_res, "linear_scale_add_fwd");
+  if (s != SGE_OK) return s;
+  const Range out = range_of(residual, x->outer, w->outer, ld_res, 2);
+  if (overlap(out, operand_range(*x)) || overlap(out, operand_range(*w)))
+    return fail(SGE_ERR_ALIAS, "linear_scale_add_fwd: residual overlaps x or w");
+  if (x->outer == 0 || w->outer == 0) return ok();
+  if (alpha == 0.0f) {
+    if (accumulate) return ok();   // the residual is the result, bit for bit
+    return hip_status(sge::launch_fill_bf16_zero(static_cast<uint16_t*>(residual), x->outer, w->outer, ld_res,
+                                                 stream),
+                      "fill");
+  }
+  if (x->inner == 0) {
+    if (accumulate) return ok();
+    return hip_status(sge::launch_fill_bf16_zero(static_cast<uint16_t*>(residual), x->outer, w->outer, ld_res,
+                                                 stream),
+                      "fill");
+  }
+  sge::GemmParams p = gemm_params(*x, *w, residual, ld_res, alpha, accumulate ? 1 : 0);
+  return hip_status(sge::launch_gemm(p, x->format, x->inner_contiguous != 0, w->inner_contiguous != 0, stream),
+                    "gemm launch");
+}
+
+sge_status sge_linear_scale_bwd(const sge_operand* dg_a, const sge_operand* dg_b, const sge_operand* wg_a,
+                                const sge_operand* wg_b, void* dgrad, int64_t ld_dgrad, void* wgrad,
+                                int64_t ld_wgrad, float dgrad_alpha, float wgrad_alpha, hipStream_t stream) {
+  sge_status s;
+  if (dgrad) {
+    if ((s = check_gemm(dg_a, dg_b, dgrad, ld_dgrad, "dgrad")) != SGE_OK) return s;
+  }
+  if (wgrad) {
+    if ((s = check_gemm(wg_a, wg_b, wgrad, ld_wgrad, "wgrad")) != SGE_OK) return s;
+  }
+  if (dgrad && wgrad) {
+    if (dg_a->outer != wg_b->inner || dg_b->outer != wg_b->outer || wg_a->outer != dg_a->inner)
+      return fail(SGE_ERR_SHAPE, "backward: dgrad [M,N]x[K,N] and wgrad [N,M]x[K,M] shapes disagree");
+  }
+  if (dgrad) {
+    const Range out = range_of(dgrad, dg_a->outer, dg_b->outer, ld_dgrad, 2);
+    if (overlap(out, operand_range(*dg_a)) || overlap(out, operand_range(*dg_b)) ||
+        (wgrad && (overlap(out, operand_range(*wg_a)) || overlap(out, operand_range(*wg_b)))))
+      return fail(SGE_ERR_ALIAS, "dgrad overlaps an input");
+  }
+  if (wgrad) {
+    const Range out = range_of(wgrad, wg_a->outer, wg_b->outer, ld_wgrad, 2);
+    if (overlap(out, operand_range(*wg_a)) || overlap(out, operand_range(*wg_b)) ||
+        (dgrad && (overlap(out, operand_range(*dg_a)) || overlap(out, operand_range(*dg_b)))))
+      return fail(SGE_ERR_ALIAS, "wgrad overlaps an input");
+    if (dgrad && overlap(out, range_of(dgrad, dg_a->outer, dg_b->outer, ld_dgrad, 2)))
+      return fail(SGE_ERR_ALIAS, "wgrad overlaps dgrad");
+  }
+  if (dgrad && dg_a->outer > 0 && dg_b->outer > 0) {
+    hipError_t e;
+    if (dgrad_alpha == 0.0f || dg_a->inner == 0) {
+      e = sge::launch_fill_bf16_zero(static_cast<uint16_t*>(dgrad), dg_a->outer, dg_b->outer, ld_dgrad, stream);
+    } else {
+      sge::GemmParams p = gemm_params(*dg_a, *dg_b, dgrad, ld_dgrad, dgrad_alpha, 0);
+      e = sge::launch_gemm(p, dg_a->format, dg_a->inner_contiguous != 0, dg_b->inner_contiguous != 0, stream);
+    }
+    if (e != hipSuccess) return hip_status(e, "dgrad launch");
+  }
+  if (wgrad && wg_a->outer > 0 && wg_b->outer > 0) {
+    hipError_t e;
+    if (wgrad_alpha == 0.0f || wg_a->inner == 0) {
+      e = sge::launch_fill_bf16_zero(static_cast<uint16_t*>(wgrad), wg_a->outer, wg_b->outer, ld_wgrad, stream);
+    } else {
+      sge::GemmParams p = gemm_params(*wg_a, *wg_b, wgrad, ld_wgrad, wgrad_alpha, 0);
+      e = sge::launch_gemm(p, wg_a->format, wg_a->inner_contiguous != 0, wg_b->inner_contiguous != 0, stream);
+    }
+    if (e != hipSuccess) return hip_status(e, "wgrad launch");
+  }
+  return ok();
+}
+
+size_t sge_quantize_fp8_amax_workspace_size(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return 0;
+  return (size_t)sge::amax_partial_blocks(rows * cols) * sizeof(uint32_t);
+}
+
+sge_status sge_quantize_fp8_amax(const void* src, int64_t rows, int64_t cols, uint8_t* q, uint8_t* q_t, float* amax,
+                                 float* scale, float* scale_inv, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  if (rows < 0 || cols < 0) return fail(SGE_ERR_SHAPE, "quantize_fp8_amax: negative size");
+  if ((rows * cols > 0 && !src) || !amax || !scale || !scale_inv || !workspace)
+    return fail(SGE_ERR_NULL, "quantize_fp8_amax: NULL pointer");
+  if (rows % 16 || cols % 16) return fail(SGE_ERR_SHAPE, "quantize_fp8_amax: rows and cols must be multiples of 16");
+  if (!aligned16(src) || (q && !aligned16(q)) || (q_t && !aligned16(q_t)))
+    return fail(SGE_ERR_ALIGN, "quantize_fp8_amax: pointers must be 16-byte aligned");
+  const Range in = range_of(src, rows, cols, cols, 2);
+  if ((q && overlap(in, range_of(q, rows, cols, cols, 1))) || (q_t && overlap(in, range_of(q_t, cols, rows, rows, 1))))
+    return fail(SGE_ERR_ALIAS, "quantize_fp8_amax: output overlaps the input");
+  const size_t need = sge_quantize_fp8_amax_workspace_size(rows, cols);
+  if (workspace_bytes < need)
+    return fail(SGE_ERR_WORKSPACE, "quantize_fp8_amax: workspace %zu < %zu bytes", workspace_bytes, need);
+  const int nb = sge::amax_partial_blocks(rows * cols);
+  hipError_t e = sge::launch_amax_partial(static_cast<const uint16_t*>(src), rows * cols,
+                                          static_cast<uint32_t*>(workspace), nb, stream);
+  if (e != hipSuccess) return hip_status(e, "amax launch");
+  e = sge::launch_quantize_fp8(static_cast<const uint16_t*>(src), rows, cols, static_cast<const uint32_t*>(workspace),
+                               nb, q, q_t, amax, scale, scale_inv, stream);
+  return hip_status(e, "quantize launch");
+}
+
+sge_status sge_quantize_mxfp8(const void* src, int64_t rows, int64_t cols, uint8_t* q_row, uint8_t* s_row,
+                              uint8_t* q_colT, uint8_t* s_colT, hipStream_t stream) {
+  if (rows < 0 || cols < 0) return fail(SGE_ERR_SHAPE, "quantize_mxfp8: negative size");
+  const bool want_row = q_row || s_row, want_col = q_colT || s_colT;
+  if (!want_row && !want_col) return fail(SGE_ERR_NULL, "quantize_mxfp8: no output requested");
+  if ((want_row && (!q_row || !s_row)) || (want_col && (!q_colT || !s_colT)))
+    return fail(SGE_ERR_NULL, "quantize_mxfp8: data and scale pointers come in pairs");
+  if (rows * cols > 0 && !src) return fail(SGE_ERR_NULL, "quantize_mxfp8: src is NULL");
+  if (cols % 32 || (want_col && rows % 32))
+    return fail(SGE_ERR_SHAPE, "quantize_mxfp8: cols (and rows, for the columnwise copy) must be multiples of 32");
+  if (!aligned16(src) || (q_row && !aligned16(q_row)) || (q_colT && !aligned16(q_colT)))
+    return fail(SGE_ERR_ALIGN, "quantize_mxfp8: pointers must be 16-byte aligned");
+  const Range in = range_of(src, rows, cols, cols, 2);
+  if ((q_row && overlap(in, range_of(q_row, rows, cols, cols, 1))) ||
+      (q_colT && overlap(in, range_of(q_colT, cols, rows, rows, 1))))
+    return fail(SGE_ERR_ALIAS, "quantize_mxfp8: output overlaps the input");
+  if (rows == 0 || cols == 0) return ok();
+  return hip_status(sge::launch_quantize_mxfp8(static_cast<const uint16_t*>(src), rows, cols, q_row, s_row, q_colT,
+                                               s_colT, stream),
+                    "quantize_mxfp8 launch");
+}
+
+sge_status sge_splits_to_offsets(const int64_t* splits, int32_t G, const int64_t* multipliers, int32_t n_mult,
+                                 int64_t expected_total, int64_t* offsets, int32_t* err_flag, hipStream_t stream) {
+  if (!splits || !multipliers || !offsets) return fail(SGE_ERR_NULL, "splits_to_offsets: NULL pointer");
+  if (G < 1 || G > 4096) return fail(SGE_ERR_ARG, "splits_to_offsets: G=%d outside [1, 4096]", G);
+  if (n_mult < 1 || n_mult > 8) return fail(SGE_ERR_ARG, "splits_to_offsets: n_mult=%d outside [1, 8]", n_mult);
+  return hip_status(sge::launch_splits_to_offsets(splits, G, multipliers, n_mult, expected_total, offsets, err_flag,
+                                                  stream),
+                    "splits_to_offsets launch");
+}
+
+sge_status sge_grouped_linear_fwd(const void* x, const void* w, int32_t G, int64_t T, int64_t N, int64_t K,
+                                  const int64_t* offsets, float alpha, int32_t epilogue, const float* probs, void* out,
+                                  void* preact, hipStream_t stream) {
+  if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd: bad sizes");
+  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_SCALED_SWIGLU)
+    return fail(SGE_ERR_ARG, "grouped_linear_fwd: epilogue %d not allowed", epilogue);
+  if (!x || !w || !offsets || !out) return fail(SGE_ERR_NULL, "grouped_linear_fwd: NULL pointer");
+  if (epilogue == SGE_EPI_SCALED_SWIGLU && !probs) return fail(SGE_ERR_NULL, "grouped_linear_fwd: probs is NULL");
+  if (K % 8 || N % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd: N and K must be multiples of 8");
+  if (epilogue == SGE_EPI_SCALED_SWIGLU && N % 256)
+    return fail(SGE_ERR_SHAPE, "grouped_linear_fwd: SwiGLU needs N %% 256 == 0");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(out) || (preact && !aligned16(preact)))
+    return fail(SGE_ERR_ALIGN, "grouped_linear_fwd: pointers must be 16-byte aligned");
+  const int64_t out_cols = epilogue == SGE_EPI_SCALED_SWIGLU ? N / 2 : N;
+  const Range ro = range_of(out, T, out_cols, out_cols, 2);
+  if (overlap(ro, range_of(x, T, K, K, 2)) || overlap(ro, range_of(w, (int64_t)G * N, K, K, 2)) ||
+      (preact && overlap(range_of(preact, T, N, N, 2), ro)))
+    return fail(SGE_ERR_ALIAS, "grouped_linear_fwd: outputs overlap inputs");
+  if (T == 0 || N == 0) return ok();
+  sge::GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.a = static_cast<const uint8_t*>(x);
+  p.lda = K;
+  p.b = static_cast<const uint8_t*>(w);
+  p.ldb = K;
+  p.M = T;
+  p.N = N;
+  p.K = K;
+  p.b_group_stride = N * K;
+  p.alpha = alpha;
+  p.c = static_cast<uint16_t*>(out);
+  p.ldc = out_cols;
+  p.offsets = offsets;
+  p.G = G;
+  p.T = T;
+  p.probs = probs;
+  p.aux = static_cast<uint16_t*>(preact);
+  p.ld_aux = N;
+  p.F = N / 2;
+  return hip_status(sge::launch_grouped_fwd(p, epilogue, stream), "grouped fwd launch");
+}
+
+size_t sge_grouped_linear_bwd_workspace_size(int64_t T, int64_t K, int32_t G, int32_t epilogue) {
+  (void)G;
+  if (epilogue != SGE_EPI_DSCALED_SWIGLU || T <= 0 || K <= 0) return 0;
+  const int64_t parts = 2 * ((K + sge::gemm_tile_n() - 1) / sge::gemm_tile_n());
+  return (size_t)(parts * T) * sizeof(float);
+}
+
+sge_status sge_grouped_linear_bwd(const void* dy, const void* x, const void* w, int32_t G, int64_t T, int64_t N,
+                                  int64_t K, const int64_t* offsets, float alpha, int32_t epilogue, const void* preact,
+                                  const float* probs, void* dact, float* dprobs, void* dx, void* dw, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_bwd: bad sizes");
+  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_DSCALED_SWIGLU)
+    return fail(SGE_ERR_ARG, "grouped_linear_bwd: epilogue %d not allowed", epilogue);
+  const bool swiglu = epilogue == SGE_EPI_DSCALED_SWIGLU;
+  if (!dy || !w || !offsets) return fail(SGE_ERR_NULL, "grouped_linear_bwd: NULL pointer");
+  if (dw && !x) return fail(SGE_ERR_NULL, "grouped_linear_bwd: x is NULL");
+  if (swiglu && (!preact || !probs || !dact || !dprobs))
+    return fail(SGE_ERR_NULL, "grouped_linear_bwd: SwiGLU backward needs preact, probs, dact and dprobs");
+  if (K % 8 || N % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_bwd: N and K must be multiples of 8");
+  if (!aligned16(dy) || (x && !aligned16(x)) || !aligned16(w) || (dx && !aligned16(dx)) || (dw && !aligned16(dw)) ||
+      (preact && !aligned16(preact)) || (dact && !aligned16(dact)))
+    return fail(SGE_ERR_ALIGN, "grouped_linear_bwd: pointers must be 16-byte aligned");
+  const Range rdy = range_of(dy, T, N, N, 2), rw = range_of(w, (int64_t)G * N, K, K, 2);
+  const Range rx = x ? range_of(x, T, K, K, 2) : Range{0, 0};
+  if ((dx && !swiglu && (overlap(range_of(dx, T, K, K, 2), rdy) || overlap(range_of(dx, T, K, K, 2), rw))) ||
+      (dw && (overlap(range_of(dw, (int64_t)G * N, K, K, 2), rdy) || overlap(range_of(dw, (int64_t)G * N, K, K, 2), rx))) ||
+      (swiglu && (overlap(range_of(dact, T, 2 * K, 2 * K, 2), rdy) ||
+                  overlap(range_of(dact, T, 2 * K, 2 * K, 2), range_of(preact, T, 2 * K, 2 * K, 2)))))
+    return fail(SGE_ERR_ALIAS, "grouped_linear_bwd: outputs overlap inputs");
+  const size_t need = sge_grouped_linear_bwd_workspace_size(T, K, G, epilogue);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(SGE_ERR_WORKSPACE, "grouped_linear_bwd: workspace %zu < %zu bytes", workspace_bytes, need);
+  if (T == 0) {
+    if (dw) return hip_status(sge::launch_fill_bf16_zero(static_cast<uint16_t*>(dw), (int64_t)G * N, K, K, stream), "fill");
+    return ok();
+  }
+  hipError_t e = hipSuccess;
+  if (swiglu || dx) {
+    sge::GemmParams p;
+    memset(&p, 0, sizeof(p));
+    p.a = static_cast<const uint8_t*>(dy);
+    p.lda = N;
+    p.b = static_cast<const uint8_t*>(w);
+    p.ldb = K;
+    p.M = T;
+    p.N = K;
+    p.K = N;
+    p.b_group_stride = N * K;
+    p.alpha = alpha;
+    p.c = static_cast<uint16_t*>(dx);
+    p.ldc = K;
+    p.offsets = offsets;
+    p.G = G;
+    p.T = T;
+    if (swiglu) {
+      p.probs = probs;
+      p.aux = const_cast<uint16_t*>(static_cast<const uint16_t*>(preact));
+      p.ld_aux = 2 * K;
+      p.aux_out = static_cast<uint16_t*>(dact);
+      p.ld_aux_out = 2 * K;
+      p.dp_part = static_cast<float*>(workspace);
+      p.F = K;
+    }
+    e = sge::launch_grouped_dgrad(p, epilogue, stream);
+    if (e != hipSuccess) return hip_status(e, "grouped dgrad launch");
+    if (swiglu) {
+      const int parts = (int)(2 * ((K + sge::gemm_tile_n() - 1) / sge::gemm_tile_n()));
+      e = sge::launch_rowsum_parts(static_cast<const float*>(workspace), parts, offsets, G, T, dprobs, stream);
+      if (e != hipSuccess) return hip_status(e, "dprobs reduction launch");
+    }
+  }
+  if (dw) {
+    sge::GemmParams p;
+    memset(&p, 0, sizeof(p));
+    p.a = static_cast<const uint8_t*>(dy);
+    p.lda = N;
+    p.b = static_cast<const uint8_t*>(x);
+    p.ldb = K;
+    p.M = N;
+    p.N = K;
+    p.K = T;
+    p.alpha = alpha;
+    p.c = static_cast<uint16_t*>(dw);
+    p.ldc = K;
+    p.c_group_stride = N * K;
+    p.offsets = offsets;
+    p.G = G;
+    p.T = T;
+    e = sge::launch_grouped_wgrad(p, stream);
+    if (e != hipSuccess) return hip_status(e, "grouped wgrad launch");
+  }
+  return ok();
+}
+
+sge_status sge_scaled_swiglu_fwd(const void* h, const float* probs, void* y, int64_t T, int64_t F, hipStream_t stream) {
+  if (T < 0 || F < 0) return fail(SGE_ERR_SHAPE, "scaled_swiglu_fwd: negative size");
+  if (T > 0 && (!h || !probs || !y)) return fail(SGE_ERR_NULL, "scaled_swiglu_fwd: NULL pointer");
+  if (F % 8) return fail(SGE_ERR_SHAPE, "scaled_swiglu_fwd: F must be a multiple of 8");
+  if ((h && !aligned16(h)) || (y && !aligned16(y))) return fail(SGE_ERR_ALIGN, "scaled_swiglu_fwd: alignment");
+  if (T == 0 || F == 0) return ok();
+  if (overlap(range_of(y, T, F, F, 2), range_of(h, T, 2 * F, 2 * F, 2)))
+    return fail(SGE_ERR_ALIAS, "scaled_swiglu_fwd: y overlaps h");
+  return hip_status(sge::launch_swiglu_fwd(static_cast<const uint16_t*>(h), probs, static_cast<uint16_t*>(y), T, F,
+                                           stream),
+                    "swiglu fwd launch");
+}
+
+sge_status sge_scaled_swiglu_bwd(const void* gy, const void* h, const float* probs, void* dh, float* dprobs, int64_t T,
+                                 int64_t F, hipStream_t stream) {
+  if (T < 0 || F < 0) return fail(SGE_ERR_SHAPE, "scaled_swiglu_bwd: negative size");
+  if (T > 0 && (!gy || !h || !probs || !dh || !dprobs)) return fail(SGE_ERR_NULL, "scaled_swiglu_bwd: NULL pointer");
+  if (F % 8) return fail(SGE_ERR_SHAPE, "scaled_swiglu_bwd: F must be a multiple of 8");
+  if ((gy && !aligned16(gy)) || (h && !aligned16(h)) || (dh && !aligned16(dh)))
+    return fail(SGE_ERR_ALIGN, "scaled_swiglu_bwd: alignment");
+  if (T == 0) return ok();
+  const Range rdh = range_of(dh, T, 2 * F, 2 * F, 2);
+  if (overlap(rdh, range_of(h, T, 2 * F, 2 * F, 2)) || overlap(rdh, range_of(gy, T, F, F, 2)))
+    return fail(SGE_ERR_ALIAS, "scaled_swiglu_bwd: dh overlaps an input");
+  return hip_status(sge::launch_swiglu_bwd(static_cast<const uint16_t*>(gy), static_cast<const uint16_t*>(h), probs,
+                                           static_cast<uint16_t*>(dh), dprobs, T, F, stream),
+                    "swiglu bwd launch");
+}
+
+}  // extern "C"

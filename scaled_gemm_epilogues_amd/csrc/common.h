@@ -1,0 +1,51 @@
+// Device-side helpers shared by the gfx950 kernels of libsge.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sge {
+
+typedef __attribute__((__ext_vector_type__(8))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+
+constexpr int kWave = 64;
+
+// bf16 bit pattern -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t two) { return __builtin_bit_cast(float, two << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t two) { return __builtin_bit_cast(float, two & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+
+// fp32 -> bf16 with round-to-nearest-even (the compiler's __bf16 conversion; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// fp32 -> OCP E4M3 byte: saturate to +-448 first, then the hardware round-to-nearest-even
+// conversion (which alone turns overflow into NaN). Returns two bytes in the low 16 bits.
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// XOR swizzle of 16-byte chunks inside 128-byte LDS rows: rows r..r+7 (any 8
+// consecutive rows) and rows 8 apart both land on distinct chunks, so the MFMA
+// fragment reads and both tile-fill patterns are free of bank conflicts.
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    T w = __shfl_xor(v, o, kWave);
+    v = v > w ? v : w;
+  }
+  return v;
+}
+
+}  // namespace sge

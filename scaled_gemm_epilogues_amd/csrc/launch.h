@@ -1,0 +1,72 @@
+// Host-side launch interface between the C ABI (abi.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sge {
+
+// Arguments of one GEMM launch: C[m][n] = epilogue(sum_k A[m][k] * B[n][k]).
+// Element strides are in elements of the operand format (2 bytes for bf16,
+// 1 byte for E4M3 / MXFP8).
+struct GemmParams {
+  const uint8_t* a;
+  int64_t lda;
+  const uint8_t* b;
+  int64_t ldb;
+  int64_t M, N, K;            // C is [M, N]; K is the contraction length
+  int64_t b_group_stride;     // grouped rows: elements from W_g to W_{g+1}
+  const float* a_sinv;        // E4M3 per-tensor scale_inv (device fp32[1])
+  const float* b_sinv;
+  const uint8_t* a_mx;        // MXFP8 E8M0 scales [rows][K/32]
+  int64_t a_mx_ld;
+  const uint8_t* b_mx;
+  int64_t b_mx_ld;
+  int mx_aligned;             // K % 128 == 0 and both scale lds % 4 == 0
+  float alpha;
+  uint16_t* c;
+  int64_t ldc;
+  int64_t c_group_stride;     // grouped contraction: elements from dW_g to dW_{g+1}
+  int accumulate;
+  const int64_t* offsets;     // grouped: device int64 [G+1]
+  int G;
+  int64_t T;
+  int mt_count, nt_count;     // filled by the launcher
+  const float* probs;         // SwiGLU: per-token scales
+  uint16_t* aux;              // SwiGLU fwd: preact out; dSwiGLU: preact in
+  int64_t ld_aux;
+  uint16_t* aux_out;          // dSwiGLU: dact out
+  int64_t ld_aux_out;
+  float* dp_part;             // dSwiGLU: per-column-tile partial sums [parts][T]
+  int64_t F;                  // SwiGLU half width
+};
+
+hipError_t launch_gemm(const GemmParams& p, int fmt, bool a_kmaj, bool b_kmaj, hipStream_t s);
+hipError_t launch_grouped_fwd(const GemmParams& p, int epilogue, hipStream_t s);
+hipError_t launch_grouped_dgrad(const GemmParams& p, int epilogue, hipStream_t s);
+hipError_t launch_grouped_wgrad(const GemmParams& p, hipStream_t s);
+int gemm_tile_n();
+
+hipError_t launch_fill_bf16_zero(uint16_t* c, int64_t rows, int64_t cols, int64_t ld, hipStream_t s);
+hipError_t launch_fill_f32_zero(float* c, int64_t n, hipStream_t s);
+
+hipError_t launch_amax_partial(const uint16_t* src, int64_t n, uint32_t* partial, int nblocks,
+                               hipStream_t s);
+int amax_partial_blocks(int64_t n);
+hipError_t launch_quantize_fp8(const uint16_t* src, int64_t rows, int64_t cols, const uint32_t* partial,
+                               int nparts, uint8_t* q, uint8_t* q_t, float* amax, float* scale,
+                               float* scale_inv, hipStream_t s);
+hipError_t launch_quantize_mxfp8(const uint16_t* src, int64_t rows, int64_t cols, uint8_t* q_row,
+                                 uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT, hipStream_t s);
+
+hipError_t launch_splits_to_offsets(const int64_t* splits, int G, const int64_t* mults, int n_mult,
+                                    int64_t expected_total, int64_t* offsets, int32_t* err_flag,
+                                    hipStream_t s);
+hipError_t launch_swiglu_fwd(const uint16_t* h, const float* p, uint16_t* y, int64_t T, int64_t F,
+                             hipStream_t s);
+hipError_t launch_swiglu_bwd(const uint16_t* gy, const uint16_t* h, const float* p, uint16_t* dh,
+                             float* dp, int64_t T, int64_t F, hipStream_t s);
+hipError_t launch_rowsum_parts(const float* part, int nparts, const int64_t* offsets, int G, int64_t T,
+                               float* out, hipStream_t s);
+
+}  // namespace sge

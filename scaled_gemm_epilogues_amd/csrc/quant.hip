@@ -1,0 +1,281 @@
+// Quantizers for gfx950: FP8 E4M3 with per-tensor current scaling, and MXFP8.
+//
+// Current scaling is "amax, then quantize" ("NVIDIA TransformerEngine PyTorch
+// Ext Normalization", Description): an HBM pass reduces max|x| block-wise, a
+// second pass finishes the reduction in every block (a few KB from L2), derives
+// scale = 448/amax and writes the E4M3 bytes (and optionally their transpose,
+// the operand layout the backward GEMMs read).
+//
+// MXFP8 ("core.tensor_parallel.inference_layers", _apply_linear with an MXFP8
+// weight) uses one E8M0 exponent per 32 elements: X = floor(log2(amax)) - 8
+// (OCP MX v1.0 section 6.3), clamped to [-127, 127]. One pass reads each bf16
+// element once and writes both the rowwise and the columnwise (transposed)
+// copy. The per-block amax is an integer max over bf16 bit patterns with the
+// sign cleared, which orders like the magnitudes.
+#include "common.h"
+#include "launch.h"
+
+namespace sge {
+
+constexpr int kAmaxThreads = 256;
+
+__device__ __forceinline__ uint32_t absmax_bits2(uint32_t d) {
+  const uint32_t lo = d & 0x7FFFu, hi = (d >> 16) & 0x7FFFu;
+  return lo > hi ? lo : hi;
+}
+
+__device__ __forceinline__ uint32_t absmax_bits8(const uint4& v) {
+  uint32_t a = absmax_bits2(v.x), b = absmax_bits2(v.y), c = absmax_bits2(v.z), d = absmax_bits2(v.w);
+  a = a > b ? a : b;
+  c = c > d ? c : d;
+  return a > c ? a : c;
+}
+
+// Block-wide max of one uint32 per thread (all threads must call).
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
+  v = wave_max(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  uint32_t m = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) m = red[w] > m ? red[w] : m;
+  __syncthreads();
+  return m;
+}
+
+__global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const uint16_t* __restrict__ src,
+                                                                    int64_t n, uint32_t* __restrict__ partial) {
+  __shared__ uint32_t red[kAmaxThreads / 64];
+  const int64_t nvec = n >> 3;
+  const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
+  const uint4* v = reinterpret_cast<const uint4*>(src);
+  uint32_t m = 0;
+  int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
+  for (; i + 3 * stride < nvec; i += 4 * stride) {
+    const uint4 a = v[i], b = v[i + stride], c = v[i + 2 * stride], d = v[i + 3 * stride];
+    uint32_t x = absmax_bits8(a), y = absmax_bits8(b), z = absmax_bits8(c), w = absmax_bits8(d);
+    x = x > y ? x : y;
+    z = z > w ? z : w;
+    x = x > z ? x : z;
+    m = m > x ? m : x;
+  }
+  for (; i < nvec; i += stride) {
+    const uint32_t x = absmax_bits8(v[i]);
+    m = m > x ? m : x;
+  }
+  for (int64_t t = nvec * 8 + (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; t < n; t += stride) {
+    const uint32_t x = src[t] & 0x7FFFu;
+    m = m > x ? m : x;
+  }
+  m = block_max_u32(m, red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+int amax_partial_blocks(int64_t n) {
+  const int64_t want = (n / 8 + kAmaxThreads * 8 - 1) / (kAmaxThreads * 8);
+  return (int)(want < 1 ? 1 : (want > 1024 ? 1024 : want));
+}
+
+hipError_t launch_amax_partial(const uint16_t* src, int64_t n, uint32_t* partial, int nblocks,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(amax_partial_kernel, dim3(nblocks), dim3(kAmaxThreads), 0, s, src, n, partial);
+  return hipGetLastError();
+}
+
+// Tiles of 64 rows x 64 columns; 256 threads, 8 bf16 (16 B) per thread per pass.
+constexpr int kQT = 64;
+
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(
+    const uint16_t* __restrict__ src, int64_t rows, int64_t cols, const uint32_t* __restrict__ partial,
+    int nparts, uint8_t* __restrict__ q, uint8_t* __restrict__ q_t, float* amax_out, float* scale_out,
+    float* scale_inv_out) {
+  __shared__ uint32_t red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kQT][kQT + 8];
+
+  // Finish the amax: every block reduces the partials itself (no grid barrier).
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = partial[i] > m ? partial[i] : m;
+  m = block_max_u32(m, red);
+  const float amax = __builtin_bit_cast(float, m << 16);
+  float scale = 1.0f;
+  if (amax > 0.0f) {
+    scale = 448.0f / amax;                           // IEEE division (no fast-math)
+    if (scale > 3.402823466e38f) scale = 3.402823466e38f;
+  }
+  const float scale_inv = 1.0f / scale;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *amax_out = amax;
+    *scale_out = scale;
+    *scale_inv_out = scale_inv;
+  }
+
+  const int64_t tr = rows / kQT + (rows % kQT ? 1 : 0);
+  const int64_t tc = cols / kQT + (cols % kQT ? 1 : 0);
+  const int t = threadIdx.x;
+  const int cchunk = t & 7;          // 8 columns each
+  const int rsub = t >> 3;           // 0..31
+  for (int64_t tile_id = blockIdx.x; tile_id < tr * tc; tile_id += gridDim.x) {
+    const int64_t r0 = (tile_id / tc) * kQT, c0 = (tile_id % tc) * kQT;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int lr = rsub + 32 * pass;
+      const int64_t r = r0 + lr, c = c0 + cchunk * 8;
+      uint2 out = make_uint2(0, 0);
+      if (r < rows && c < cols) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src + r * cols + c);
+        const uint32_t b01 = e4m3x2(bf16_lo(v.x) * scale, bf16_hi(v.x) * scale);
+        const uint32_t b23 = e4m3x2(bf16_lo(v.y) * scale, bf16_hi(v.y) * scale);
+        const uint32_t b45 = e4m3x2(bf16_lo(v.z) * scale, bf16_hi(v.z) * scale);
+        const uint32_t b67 = e4m3x2(bf16_lo(v.w) * scale, bf16_hi(v.w) * scale);
+        out = make_uint2(b01 | (b23 << 16), b45 | (b67 << 16));
+        if (q) *reinterpret_cast<uint2*>(q + r * cols + c) = out;
+      }
+      if (q_t) *reinterpret_cast<uint2*>(&tile[lr][cchunk * 8]) = out;
+    }
+    if (q_t) {
+      __syncthreads();
+      // Thread -> one column, 16 consecutive rows of the transposed output.
+      const int lc = t & 63, rb = t >> 6;
+      const int64_t c = c0 + lc, r = r0 + rb * 16;
+      if (c < cols && r < rows) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[e] = (uint32_t)tile[rb * 16 + 4 * e + 0][lc] | ((uint32_t)tile[rb * 16 + 4 * e + 1][lc] << 8) |
+                 ((uint32_t)tile[rb * 16 + 4 * e + 2][lc] << 16) | ((uint32_t)tile[rb * 16 + 4 * e + 3][lc] << 24);
+        }
+        *reinterpret_cast<uint4*>(q_t + c * rows + r) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      __syncthreads();
+    }
+  }
+}
+
+hipError_t launch_quantize_fp8(const uint16_t* src, int64_t rows, int64_t cols, const uint32_t* partial,
+                               int nparts, uint8_t* q, uint8_t* q_t, float* amax, float* scale,
+                               float* scale_inv, hipStream_t s) {
+  const int64_t tiles = ((rows + kQT - 1) / kQT) * ((cols + kQT - 1) / kQT);
+  const int grid = (int)(tiles < 2048 ? (tiles < 1 ? 1 : tiles) : 2048);
+  hipLaunchKernelGGL(quantize_fp8_kernel, dim3(grid), dim3(256), 0, s, src, rows, cols, partial, nparts, q,
+                     q_t, amax, scale, scale_inv);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------- MXFP8
+// E8M0 exponent of a block from its amax bit pattern (bf16 magnitude bits).
+__device__ __forceinline__ int mx_exponent(uint32_t amax_bits) {
+  if (amax_bits == 0) return -127;
+  const uint32_t f = amax_bits << 16;                  // as fp32 bits
+  const int be = (int)(f >> 23);                       // biased exponent (0 for subnormals)
+  int e;
+  if (be > 0) {
+    e = be - 127;
+  } else {
+    // subnormal: value = mant * 2^-149, floor(log2) = msb(mant) - 149
+    e = (31 - __builtin_clz(f & 0x7FFFFFu)) - 149;
+  }
+  int x = e - 8;
+  return x < -127 ? -127 : (x > 127 ? 127 : x);
+}
+
+// 2^-X as fp32 for X in [-127, 119] (always a normal number).
+__device__ __forceinline__ float pow2_neg(int x) {
+  return __builtin_bit_cast(float, (uint32_t)(127 - x) << 23);
+}
+
+constexpr int kMR = 32, kMC = 64;   // MX tile: 32 rows x 64 columns
+
+__global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const uint16_t* __restrict__ src, int64_t rows,
+                                                            int64_t cols, uint8_t* __restrict__ q_row,
+                                                            uint8_t* __restrict__ s_row,
+                                                            uint8_t* __restrict__ q_colT,
+                                                            uint8_t* __restrict__ s_colT) {
+  __shared__ uint32_t colmax[4][kMC];
+  __shared__ __attribute__((aligned(16))) uint8_t qt[kMC][kMR + 8];
+  const int64_t tc = cols / kMC + (cols % kMC ? 1 : 0);
+  const int64_t r0 = (int64_t)(blockIdx.x / tc) * kMR;
+  const int64_t c0 = (int64_t)(blockIdx.x % tc) * kMC;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int lr = t >> 3;                 // 0..31
+  const int cc = t & 7;                  // column chunk of 8
+  const int64_t r = r0 + lr, c = c0 + cc * 8;
+  const bool ok = r < rows && c < cols;  // rows, cols are multiples of 32
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (ok) v = *reinterpret_cast<const uint4*>(src + r * cols + c);
+  float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+  uint32_t ab[8] = {v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu, v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu,
+                    v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu, v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu};
+
+  if (q_row) {
+    // Rowwise: a 32-column block is 4 consecutive threads of one row.
+    uint32_t m = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = ab[e] > m ? ab[e] : m;
+    uint32_t o = __shfl_xor(m, 1, 64);
+    m = o > m ? o : m;
+    o = __shfl_xor(m, 2, 64);
+    m = o > m ? o : m;
+    const int X = mx_exponent(m);
+    const float sc = pow2_neg(X);
+    if (ok) {
+      const uint32_t b01 = e4m3x2(x[0] * sc, x[1] * sc), b23 = e4m3x2(x[2] * sc, x[3] * sc);
+      const uint32_t b45 = e4m3x2(x[4] * sc, x[5] * sc), b67 = e4m3x2(x[6] * sc, x[7] * sc);
+      *reinterpret_cast<uint2*>(q_row + r * cols + c) = make_uint2(b01 | (b23 << 16), b45 | (b67 << 16));
+      if ((cc & 3) == 0) s_row[r * (cols / 32) + (c >> 5)] = (uint8_t)(X + 127);
+    }
+  }
+
+  if (q_colT) {
+    // Columnwise: a block is one column over the tile's 32 rows.
+    uint32_t m[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t a = ab[e];
+#pragma unroll
+      for (int o = 8; o <= 32; o <<= 1) {
+        const uint32_t b = __shfl_xor(a, o, 64);
+        a = b > a ? b : a;
+      }
+      m[e] = a;
+    }
+    if (lane < 8) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) colmax[wave][lane * 8 + e] = m[e];
+    }
+    __syncthreads();
+    uint8_t qb[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int col = cc * 8 + e;
+      uint32_t a = colmax[0][col];
+      a = colmax[1][col] > a ? colmax[1][col] : a;
+      a = colmax[2][col] > a ? colmax[2][col] : a;
+      a = colmax[3][col] > a ? colmax[3][col] : a;
+      const int X = mx_exponent(a);
+      qb[e] = (uint8_t)(e4m3x2(x[e] * pow2_neg(X), 0.0f) & 0xFF);
+      if (lr == 0 && c0 + col < cols) s_colT[(c0 + col) * (rows / 32) + (r0 >> 5)] = (uint8_t)(X + 127);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qt[cc * 8 + e][lr] = qb[e];
+    __syncthreads();
+    // Thread -> one column, 8 consecutive rows of the transposed output.
+    const int col = t >> 2, rs = (t & 3) * 8;
+    if (c0 + col < cols && r0 + rs < rows) {
+      const uint2 w = *reinterpret_cast<const uint2*>(&qt[col][rs]);
+      *reinterpret_cast<uint2*>(q_colT + (c0 + col) * rows + r0 + rs) = w;
+    }
+  }
+}
+
+hipError_t launch_quantize_mxfp8(const uint16_t* src, int64_t rows, int64_t cols, uint8_t* q_row,
+                                 uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT, hipStream_t s) {
+  const int64_t tiles = ((rows + kMR - 1) / kMR) * ((cols + kMC - 1) / kMC);
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_mxfp8_kernel, dim3((unsigned)tiles), dim3(256), 0, s, src, rows, cols, q_row,
+                     s_row, q_colT, s_colT);
+  return hipGetLastError();
+}
+
+}  // namespace sge

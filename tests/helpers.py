@@ -1,0 +1,56 @@
+"""Test helpers: moving seeded inputs to the device and comparing against the oracle."""
+
+import numpy as np
+import torch
+
+# Spec bars: |gpu - ref| <= tau * (|ref| + 1) per element.
+TAU_BF16 = 2e-2
+TAU_FP8 = 6e-2
+
+
+def dev_bf16(bits):
+    """uint16 bf16 bit patterns (numpy) -> torch bf16 tensor on cuda:0."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host_f64(t):
+    """Any device tensor -> numpy float64 (bf16 decoded by torch)."""
+    return t.detach().to("cpu").double().numpy()
+
+
+def host_u8(t):
+    return t.detach().to("cpu").contiguous().view(torch.uint8).numpy()
+
+
+def host_bits(t):
+    """bf16 tensor -> uint16 bit patterns."""
+    return t.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def assert_close(gpu, ref, tau, what="", rel_tight=2.0 ** -8, abs_tight=1e-2):
+    """Both the spec bar and a tighter bar scaled by the output's RMS.
+
+    The tight bar allows one bf16 rounding of the output (2^-8 relative) plus
+    ``abs_tight`` of the RMS for accumulation-order and intermediate roundings;
+    it fails e.g. an all-zero output, which the spec bar alone would
+    accept for outputs much smaller than 1.
+    """
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
+    err = np.abs(gpu - ref)
+    bound = tau * (np.abs(ref) + 1.0)
+    if not np.all(err <= bound):
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: north-star bar broken at {i}: gpu={gpu[i]} ref={ref[i]}")
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    tight = rel_tight * np.abs(ref) + abs_tight * rms
+    if not np.all(err <= tight):
+        i = np.unravel_index(np.argmax(err - tight), err.shape)
+        raise AssertionError(f"{what}: tight bar broken at {i}: gpu={gpu[i]} ref={ref[i]} rms={rms}")
+    return float(np.max(err / (np.abs(ref) + 1.0))) if ref.size else 0.0

@@ -1,0 +1,146 @@
+"""The C ABI on the host: the library loads, exports what include/sge.h declares, and rejects
+bad arguments before touching the GPU (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (loads the HIP runtime libsge links against)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sge.h")
+
+
+@pytest.fixture(scope="module")
+def sge():
+    import scaled_gemm_epilogues_amd as m
+    return m
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(sge_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi(sge):
+    assert set(_declared()) == set(sge.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(sge):
+    lib = ctypes.CDLL(sge.library_path())
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert sge.abi_version() == 1
+
+
+def test_status_strings(sge):
+    lib = sge._lib
+    assert lib.sge_status_string(0) == b"SGE_OK"
+    assert lib.sge_status_string(sge.ERR_ALIAS) == b"SGE_ERR_ALIAS"
+
+
+FAKE = 0x10000            # never dereferenced: every call below fails validation first
+
+
+def _op(sge, outer, inner, ld=None, contig=1, fmt=0, data=FAKE, sinv=None, mx=None, mx_ld=0):
+    return sge.SgeOperand(data, outer, inner, ld if ld is not None else (inner if contig else outer), contig, fmt,
+                          sinv, mx, mx_ld)
+
+
+def _fwd(sge, x, w, res=FAKE * 64, ld_res=None, alpha=0.5):
+    lib = sge._lib
+    st = lib.sge_linear_scale_add_fwd(ctypes.byref(x), ctypes.byref(w), res,
+                                      ld_res if ld_res is not None else w.outer, alpha, 1, None)
+    return st, lib.sge_last_error_message().decode()
+
+
+def test_forward_validation_errors(sge):
+    ok_x, ok_w = _op(sge, 64, 128), _op(sge, 64, 128, data=FAKE * 2)
+    st, msg = _fwd(sge, _op(sge, 64, 128, data=None), ok_w)
+    assert st == sge.ERR_NULL, msg
+    st, msg = _fwd(sge, ok_x, _op(sge, 64, 96, data=FAKE * 2))
+    assert st == sge.ERR_SHAPE and "contraction" in msg
+    st, _ = _fwd(sge, _op(sge, 64, 100), _op(sge, 64, 100, data=FAKE * 2))
+    assert st == sge.ERR_SHAPE                       # bf16 K % 8
+    st, _ = _fwd(sge, ok_x, _op(sge, 60, 128, data=FAKE * 2))
+    assert st == sge.ERR_SHAPE                       # N % 8
+    st, _ = _fwd(sge, _op(sge, 64, 128, data=FAKE + 2), ok_w)
+    assert st == sge.ERR_ALIGN
+    st, _ = _fwd(sge, ok_x, _op(sge, 64, 128, fmt=1, data=FAKE * 2, sinv=FAKE))
+    assert st == sge.ERR_FORMAT                      # mixed formats
+    st, _ = _fwd(sge, _op(sge, 64, 128, fmt=1, sinv=None), _op(sge, 64, 128, fmt=1, data=FAKE * 2, sinv=FAKE))
+    assert st == sge.ERR_NULL                        # E4M3 needs scale_inv
+    st, _ = _fwd(sge, _op(sge, 64, 128, contig=0, fmt=1, sinv=FAKE), _op(sge, 64, 128, fmt=1, data=FAKE * 2,
+                                                                        sinv=FAKE))
+    assert st == sge.ERR_FORMAT                      # E4M3 must be inner-contiguous
+    st, _ = _fwd(sge, _op(sge, 64, 48, fmt=2, mx=FAKE, mx_ld=1), _op(sge, 64, 48, fmt=2, data=FAKE * 2, mx=FAKE,
+                                                                       mx_ld=1))
+    assert st == sge.ERR_SHAPE                       # MX needs K % 32
+    st, _ = _fwd(sge, ok_x, ok_w, res=FAKE)          # residual over x
+    assert st == sge.ERR_ALIAS
+    st, _ = _fwd(sge, ok_x, ok_w, res=FAKE * 64 + 8)
+    assert st == sge.ERR_ALIGN
+
+
+def test_forward_shape_zero_is_a_noop(sge):
+    st, msg = _fwd(sge, _op(sge, 0, 128), _op(sge, 64, 128, data=FAKE * 2))
+    assert st == 0, msg
+
+
+def test_backward_validation_errors(sge):
+    lib = sge._lib
+    M, N, K = 64, 32, 16
+    dy = _op(sge, M, N, data=FAKE)
+    wT = _op(sge, K, N, contig=0, data=FAKE * 4)          # W [N, K] read as [K, N]
+    dyT = _op(sge, N, M, contig=0, data=FAKE)
+    xT = _op(sge, K, M + 8, contig=0, data=FAKE * 8)      # wrong: contraction M+8
+    st = lib.sge_linear_scale_bwd(ctypes.byref(dy), ctypes.byref(wT), ctypes.byref(dyT), ctypes.byref(xT),
+                                  FAKE * 16, K, FAKE * 32, K, 1.0, 1.0, None)
+    assert st == sge.ERR_SHAPE
+    xT = _op(sge, K, M, contig=0, data=FAKE * 8)
+    st = lib.sge_linear_scale_bwd(ctypes.byref(dy), ctypes.byref(wT), ctypes.byref(dyT), ctypes.byref(xT),
+                                  FAKE * 16, K, FAKE, K, 1.0, 1.0, None)          # wgrad over dy
+    assert st == sge.ERR_ALIAS
+
+
+def test_quantizer_validation_errors(sge):
+    lib = sge._lib
+    assert lib.sge_quantize_fp8_amax_workspace_size(1024, 1024) > 0
+    st = lib.sge_quantize_fp8_amax(FAKE, 64, 64, FAKE * 8, None, FAKE * 16, FAKE * 17, FAKE * 18, FAKE * 32, 0, None)
+    assert st == sge.ERR_WORKSPACE
+    st = lib.sge_quantize_fp8_amax(FAKE, 60, 64, FAKE * 8, None, FAKE * 16, FAKE * 17, FAKE * 18, FAKE * 32, 1 << 20,
+                                   None)
+    assert st == sge.ERR_SHAPE
+    st = lib.sge_quantize_fp8_amax(FAKE, 64, 64, FAKE, None, FAKE * 16, FAKE * 17, FAKE * 18, FAKE * 32, 1 << 20, None)
+    assert st == sge.ERR_ALIAS
+    st = lib.sge_quantize_mxfp8(FAKE, 64, 48, FAKE * 8, FAKE * 9, None, None, None)
+    assert st == sge.ERR_SHAPE
+    st = lib.sge_quantize_mxfp8(FAKE, 48, 64, None, None, FAKE * 8, FAKE * 9, None)
+    assert st == sge.ERR_SHAPE                       # columnwise needs rows % 32
+    st = lib.sge_quantize_mxfp8(FAKE, 64, 64, FAKE * 8, None, None, None, None)
+    assert st == sge.ERR_NULL
+    st = lib.sge_quantize_mxfp8(FAKE, 64, 64, None, None, None, None, None)
+    assert st == sge.ERR_NULL
+
+
+def test_grouped_validation_errors(sge):
+    lib = sge._lib
+    m = (ctypes.c_int64 * 1)(1)
+    assert lib.sge_splits_to_offsets(FAKE, 0, m, 1, -1, FAKE * 2, None, None) == sge.ERR_ARG
+    assert lib.sge_splits_to_offsets(FAKE, 8, m, 9, -1, FAKE * 2, None, None) == sge.ERR_ARG
+    assert lib.sge_splits_to_offsets(None, 8, m, 1, -1, FAKE * 2, None, None) == sge.ERR_NULL
+    st = lib.sge_grouped_linear_fwd(FAKE, FAKE * 64, 8, 100, 136, 64, FAKE * 1024, 1.0, 1, FAKE * 4096, FAKE * 8192,
+                                    None, None)
+    assert st == sge.ERR_SHAPE                       # SwiGLU needs N % 256
+    st = lib.sge_grouped_linear_fwd(FAKE, FAKE * 64, 8, 100, 256, 64, FAKE * 1024, 1.0, 1, None, FAKE * 8192, None,
+                                    None)
+    assert st == sge.ERR_NULL                        # SwiGLU needs probs
+    st = lib.sge_grouped_linear_fwd(FAKE, FAKE * 64, 8, 100, 256, 64, FAKE * 1024, 1.0, 7, None, FAKE * 8192, None,
+                                    None)
+    assert st == sge.ERR_ARG
+    ws = lib.sge_grouped_linear_bwd_workspace_size(1000, 2048, 8, 2)
+    assert ws == 2 * 8 * 1000 * 4
+    st = lib.sge_grouped_linear_bwd(FAKE, FAKE * 8, FAKE * 64, 8, 1000, 256, 2048, FAKE * 1024, 1.0, 2,
+                                    FAKE * 2048, FAKE * 4096, FAKE * 8192, FAKE * 9000, None, None, None, 0, None)
+    assert st == sge.ERR_WORKSPACE
