@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused scaled linear on one MI355X.
+
+One step is one pass of the hot path over one batch of seeded synthetic
+inputs already resident in HBM:
+
+* dense workloads: quantize the operands (FP8 / MXFP8 only), forward GEMM with
+  the in-place residual add, dgrad and wgrad with alpha folded in;
+* grouped workload: split offsets, fc1 + scaled SwiGLU, fc2, and the backward
+  of both layers.
+
+Prints ONE JSON line on stdout. The default workload is the bf16 forward +
+backward at M = N = K = 4096 (alpha 0.125). Per-kernel durations come from
+HIP events recorded on the stream the kernels run on; ``roofline`` reports the
+kernel with the largest share of the step. ``cpu_baseline`` times the CPU
+oracle on a bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# published MI355X peaks
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0}
+PEAK_HBM_GBS = 8000.0
+METRIC = "scaled-linear fwd+bwd TFLOP/s & % of MFMA peak (bf16/FP8/MXFP8), 1 MI355X"
+DEFAULT_WORKLOAD = "bf16_fwdbwd_4096"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------- GPU path
+class Timer:
+    """Named HIP-event intervals on the current stream, summed over the timed steps."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.marks = []
+        self.on = False
+
+    def mark(self, name):
+        if self.on:
+            e = self.torch.cuda.Event(enable_timing=True)
+            e.record()
+            self.marks.append((name, e))
+
+    def durations_ms(self):
+        out = {}
+        for (name, a), (_, b) in zip(self.marks[:-1], self.marks[1:]):
+            if name is None:
+                continue
+            out.setdefault(name, []).append(a.elapsed_time(b))
+        return out
+
+
+def build_dense(torch, sge, wl, inp, timer):
+    fmt = wl["fmt"]
+
+    def dev_bf16(bits):
+        import numpy as np
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    bwd = "dgrad" in wl["passes"]
+    X, W = dev_bf16(inp["x"]), dev_bf16(inp["w"])
+    DY = dev_bf16(inp["dy"]) if bwd else torch.zeros(X.shape[0], W.shape[0], dtype=torch.bfloat16,
+                                                       device="cuda")
+    R = dev_bf16(inp["residual"])
+    M, K = X.shape
+    N = W.shape[0]
+    alpha = wl["alpha"]
+    dgrad = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    wgrad = torch.empty(N, K, dtype=torch.bfloat16, device="cuda")
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    flops = {"gemm_fwd": 2 * M * N * K}
+    if bwd:
+        flops.update(gemm_dgrad=2 * M * N * K, gemm_wgrad=2 * M * N * K)
+    hbm = {}
+
+    if fmt == "bf16":
+        fwd = (sge.Operand.bf16(X), sge.Operand.bf16(W))
+        dg = (sge.Operand.bf16(DY), sge.Operand.bf16(W, transposed=True))
+        wg = (sge.Operand.bf16(DY, transposed=True), sge.Operand.bf16(X, transposed=True))
+
+        def quantize():
+            pass
+    elif fmt == "fp8":
+        bufs = {}
+        for name, t in (("x", X), ("w", W), ("dy", DY)):
+            r, c = t.shape
+            bufs[name] = {"q": torch.empty(r, c, **u8), "q_t": torch.empty(c, r, **u8),
+                          "amax": torch.empty(1, **f32), "scale": torch.empty(1, **f32),
+                          "scale_inv": torch.empty(1, **f32),
+                          "ws": torch.empty(sge.quantize_fp8_amax_workspace_size(r, c), **u8), "src": t}
+            hbm[f"quant_{name}"] = r * c * (2 + 2 + 1 + 1)      # amax read, quantize read, q and q_t written
+        bx, bw, bd = bufs["x"], bufs["w"], bufs["dy"]
+        fwd = (sge.Operand.e4m3(bx["q"], bx["scale_inv"]), sge.Operand.e4m3(bw["q"], bw["scale_inv"]))
+        dg = (sge.Operand.e4m3(bd["q"], bd["scale_inv"]), sge.Operand.e4m3(bw["q_t"], bw["scale_inv"]))
+        wg = (sge.Operand.e4m3(bd["q_t"], bd["scale_inv"]), sge.Operand.e4m3(bx["q_t"], bx["scale_inv"]))
+
+        def quantize():
+            for name, b in bufs.items():
+                timer.mark(f"quant_{name}")
+                sge.quantize_fp8_amax(b["src"], b["q"], b["q_t"], b["amax"], b["scale"], b["scale_inv"], b["ws"])
+    else:
+        bufs = {}
+        for name, t in (("x", X), ("w", W), ("dy", DY)):
+            r, c = t.shape
+            bufs[name] = {"q_row": torch.empty(r, c, **u8), "s_row": torch.empty(r, c // 32, **u8),
+                          "q_colT": torch.empty(c, r, **u8), "s_colT": torch.empty(c, r // 32, **u8), "src": t}
+            hbm[f"quant_{name}"] = r * c * (2 + 1 + 1) + 2 * (r * c // 32)
+        bx, bw, bd = bufs["x"], bufs["w"], bufs["dy"]
+        fwd = (sge.Operand.mxfp8(bx["q_row"], bx["s_row"]), sge.Operand.mxfp8(bw["q_row"], bw["s_row"]))
+        dg = (sge.Operand.mxfp8(bd["q_row"], bd["s_row"]), sge.Operand.mxfp8(bw["q_colT"], bw["s_colT"]))
+        wg = (sge.Operand.mxfp8(bd["q_colT"], bd["s_colT"]), sge.Operand.mxfp8(bx["q_colT"], bx["s_colT"]))
+
+        def quantize():
+            for name, b in bufs.items():
+                timer.mark(f"quant_{name}")
+                sge.quantize_mxfp8(b["src"], b["q_row"], b["s_row"], b["q_colT"], b["s_colT"])
+
+    def step():
+        quantize()
+        timer.mark("gemm_fwd")
+        sge.linear_scale_add_fwd(*fwd, R, alpha)
+        if bwd:
+            timer.mark("gemm_dgrad")
+            sge.linear_scale_bwd(*dg, None, None, dgrad, None, alpha, alpha)
+            timer.mark("gemm_wgrad")
+            sge.linear_scale_bwd(None, None, *wg, None, wgrad, alpha, alpha)
+        timer.mark(None)
+
+    return step, flops, hbm, sum(flops.values())
+
+
+def build_grouped(torch, sge, wl, inp, timer):
+    import numpy as np
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    X, W1, W2, DOUT = dev_bf16(inp["x"]), dev_bf16(inp["w1"]), dev_bf16(inp["w2"]), dev_bf16(inp["dout"])
+    P = torch.from_numpy(inp["p"]).cuda()
+    splits = torch.from_numpy(inp["splits"]).cuda()
+    T, H = X.shape
+    G, N1, _ = W1.shape
+    F = N1 // 2
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    offs = torch.empty(2, G + 1, dtype=torch.int64, device="cuda")
+    h, y, out = torch.empty(T, N1, **bf), torch.empty(T, F, **bf), torch.empty(T, H, **bf)
+    dh, dp = torch.empty(T, N1, **bf), torch.empty(T, dtype=torch.float32, device="cuda")
+    dw2, dx, dw1 = torch.empty(G, H, F, **bf), torch.empty(T, H, **bf), torch.empty(G, N1, H, **bf)
+    ws = torch.empty(max(1, sge.grouped_linear_bwd_workspace_size(T, F, G, sge.EPI_DSCALED_SWIGLU)),
+                     dtype=torch.uint8, device="cuda")
+    flops = {"fc1_fwd": 2 * T * N1 * H, "fc2_fwd": 2 * T * H * F, "fc2_dgrad_dswiglu": 2 * T * H * F,
+             "fc2_wgrad": 2 * T * H * F, "fc1_dgrad": 2 * T * N1 * H, "fc1_wgrad": 2 * T * N1 * H}
+
+    def step():
+        timer.mark("offsets")
+        sge.splits_to_offsets(splits, [1, H], offs)
+        base = offs[0]
+        timer.mark("fc1_fwd")
+        sge.grouped_linear_fwd(X, W1, base, y, epilogue=sge.EPI_SCALED_SWIGLU, probs=P, preact=h)
+        timer.mark("fc2_fwd")
+        sge.grouped_linear_fwd(y, W2, base, out)
+        timer.mark("fc2_dgrad_dswiglu")
+        sge.grouped_linear_bwd(DOUT, None, W2, base, epilogue=sge.EPI_DSCALED_SWIGLU, preact=h, probs=P,
+                               dact=dh, dprobs=dp, workspace=ws)
+        timer.mark("fc2_wgrad")
+        sge.grouped_linear_bwd(DOUT, y, W2, base, dw=dw2)
+        timer.mark("fc1_dgrad")
+        sge.grouped_linear_bwd(dh, None, W1, base, dx=dx)
+        timer.mark("fc1_wgrad")
+        sge.grouped_linear_bwd(dh, X, W1, base, dw=dw1)
+        timer.mark(None)
+
+    return step, flops, {}, sum(flops.values())
+
+
+# ----------------------------------------------------------- CPU baseline
+def cpu_baseline(wl, inp, target_s):
+    """The oracle, as it stands, on a bounded sample of the same workload (rows of the token dim)."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:                                          # pragma: no cover
+        cores = os.cpu_count() or 1
+    from oracle import grouped, linear, offsets
+    from oracle.codecs import bf16_to_f64
+
+    if wl["kind"] == "dense":
+        M = inp["x"].shape[0]
+        N, K = inp["w"].shape
+        rows = 64
+        while True:
+            bwd = "dgrad" in wl["passes"]
+            t0 = time.perf_counter()
+            ops = linear.operands(wl["fmt"], inp["x"][:rows], inp["w"], inp["dy"][:rows] if bwd else None)
+            linear.linear_scale_add_fwd(*ops["fwd"], bf16_to_f64(inp["residual"][:rows]), wl["alpha"])
+            if bwd:
+                linear.linear_scale_dgrad(*ops["dgrad"], wl["alpha"])
+                linear.linear_scale_wgrad(*ops["wgrad"], wl["alpha"])
+            dt = time.perf_counter() - t0
+            if dt >= target_s / 4 or rows >= M:
+                break
+            rows = min(M, rows * 4)
+        flops = (3 if "dgrad" in wl["passes"] else 1) * 2 * rows * N * K
+        sample = f"first {rows} of {M} token rows through {'/'.join(wl['passes'])} (quantizers included)"
+    else:
+        T = inp["x"].shape[0]
+        tok = 256
+        while True:
+            t0 = time.perf_counter()
+            G = len(inp["splits"])
+            splits = np.zeros(G, np.int64)
+            splits[0] = tok                                     # first `tok` tokens, all in group 0's weights
+            base = offsets.base_offsets(splits)
+            x = bf16_to_f64(inp["x"][:tok])
+            w1, w2 = bf16_to_f64(inp["w1"]), bf16_to_f64(inp["w2"])
+            p = inp["p"][:tok].astype(np.float64)
+            f = grouped.grouped_mlp_fwd(x, w1, w2, p, base)
+            grouped.grouped_mlp_bwd(bf16_to_f64(inp["dout"][:tok]), x, w1, w2, p, base, h=f["h"], y=f["y"])
+            dt = time.perf_counter() - t0
+            if dt >= target_s / 4 or tok >= T:
+                break
+            tok = min(T, tok * 4)
+        H = inp["x"].shape[1]
+        N1 = inp["w1"].shape[1]
+        flops = 3 * (2 * tok * N1 * H + 2 * tok * H * (N1 // 2))
+        sample = f"first {tok} of {T} tokens through the grouped MLP forward and backward"
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3)}
+
+
+# ---------------------------------------------------------------- traffic
+def traffic_for(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if its kernel source is current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    src = os.path.join(ROOT, "scaled_gemm_epilogues_amd", "csrc", t.get("source", "gemm.hip"))
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != t.get("source_sha256"):
+        return None
+    return t.get("bytes_per_launch", {}).get(kernel_key)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this path has no "
+              "multi-GPU sharding).", file=sys.stderr)
+        return 2
+    import torch
+    import numpy as np  # noqa: F401
+    import scaled_gemm_epilogues_amd as sge
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    inp = synth.workload_inputs(args.workload, seed=0)
+    timer = Timer(torch)
+    builder = build_dense if wl["kind"] == "dense" else build_grouped
+    step, flops, hbm, step_flops = builder(torch, sge, wl, inp, timer)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timer.on = True
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    timer.on = False
+    ms_per_step = total_ms / args.steps
+    per = {k: sum(v) / len(v) for k, v in timer.durations_ms().items()}
+
+    fmt = wl["fmt"]
+    peak = PEAK_TFLOPS[fmt]
+    kernels = {}
+    for k, ms in per.items():
+        if k in flops:
+            kernels[k] = {"ms": round(ms, 4), "tflops": round(flops[k] / ms / 1e9, 1),
+                          "frac_peak": round(flops[k] / ms / 1e9 / peak, 4)}
+        elif k in hbm:
+            kernels[k] = {"ms": round(ms, 4), "gbs": round(hbm[k] / ms / 1e6, 1),
+                          "frac_hbm": round(hbm[k] / ms / 1e6 / PEAK_HBM_GBS, 4)}
+        else:
+            kernels[k] = {"ms": round(ms, 4)}
+    dom = max((k for k in per if k in flops), key=lambda k: per[k])
+    achieved = flops[dom] / per[dom] / 1e9
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic_for(f"{args.workload}:{dom}"),
+                "kernel": dom, "flops_per_launch": flops[dom], "avg_launch_ms": round(per[dom], 4)}
+
+    value = step_flops / (ms_per_step * 1e9)
+    cfg = {"workload": args.workload}
+    cfg.update({k: wl[k] for k in ("M", "N", "K", "T", "G", "hidden", "ffn", "alpha") if k in wl})
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": fmt, "data": "synthetic (seeded; see synth/)",
+        "config": cfg, "frac_of_peak": round(value / peak, 4), "kernels": kernels, "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
