@@ -343,7 +343,7 @@ sge_status sge_grouped_linear_fwd(const void* x, const void* w, int32_t G, int64
 size_t sge_grouped_linear_bwd_workspace_size(int64_t T, int64_t K, int32_t G, int32_t epilogue) {
   (void)G;
   if (epilogue != SGE_EPI_DSCALED_SWIGLU || T <= 0 || K <= 0) return 0;
-  const int64_t parts = 2 * ((K + sge::gemm_tile_n() - 1) / sge::gemm_tile_n());
+  const int64_t parts = sge::gemm_dp_parts_per_tile() * ((K + sge::gemm_tile_n() - 1) / sge::gemm_tile_n());
   return (size_t)(parts * T) * sizeof(float);
 }
 
@@ -407,7 +407,8 @@ sge_status sge_grouped_linear_bwd(const void* dy, const void* x, const void* w, 
     e = sge::launch_grouped_dgrad(p, epilogue, stream);
     if (e != hipSuccess) return hip_status(e, "grouped dgrad launch");
     if (swiglu) {
-      const int parts = (int)(2 * ((K + sge::gemm_tile_n() - 1) / sge::gemm_tile_n()));
+      const int parts =
+          (int)(sge::gemm_dp_parts_per_tile() * ((K + sge::gemm_tile_n() - 1) / sge::gemm_tile_n()));
       e = sge::launch_rowsum_parts(static_cast<const float*>(workspace), parts, offsets, G, T, dprobs, stream);
       if (e != hipSuccess) return hip_status(e, "dprobs reduction launch");
     }

@@ -16,13 +16,15 @@
 // * 256 threads = 4 waves in a 2x2 grid; each wave owns WMF x WNF fragments of
 //   32x32 fp32 accumulators (v_mfma_f32_32x32x16_bf16, or the MX-scaled
 //   v_mfma_scale_f32_32x32x64_f8f6f4 for E4M3 / MXFP8 with E8M0 scales).
-// * Tiles of 128 contraction bytes per row (64 bf16 or 128 fp8) are staged in
-//   LDS, double-buffered, rows 128 B with an XOR swizzle of the 16-B chunks.
-//   Global loads of tile k+1 are in flight while tile k is multiplied.
-// * Operands stored contraction-contiguous are copied 16 B at a time; bf16
-//   operands stored the other way round are loaded as 8x8 blocks and
-//   transposed in registers on the way into LDS, so dgrad and wgrad read the
-//   untransposed tensors directly.
+// * Tiles of 128 contraction bytes per operand row (64 bf16 or 128 fp8) move
+//   from HBM straight into LDS with buffer_load ... lds (no staging registers;
+//   out-of-range lanes read zeros), in two LDS stages: the copy of tile k+1 is
+//   in flight while tile k is multiplied. LDS images are XOR-swizzled per 16-B
+//   chunk so fragment reads are free of bank conflicts.
+// * bf16 operands stored with the contraction dimension outermost (dgrad's W,
+//   wgrad's dy and x) are copied as they are and read with the transposing
+//   ds_read_b64_tr_b16, so dgrad and wgrad read the untransposed tensors.
+// * Fragments of k-step s+1 are read from LDS while the MFMAs of step s run.
 // * The MFMA is issued with B as its first operand, so each lane ends with 4
 //   consecutive output columns per group and stores 8 bytes of bf16 at a time.
 #include "common.h"
@@ -36,106 +38,110 @@ enum { S_DENSE = 0, S_GROUP_M = 1, S_GROUP_K = 2 };
 
 constexpr int kRowBytes = 128;   // contraction bytes per LDS row and per k-tile
 
-__device__ __forceinline__ uint32_t perm(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi_src, lo_src, sel);
-}
-
-// Transpose an 8x8 block of 16-bit values: in[i] holds row i (8 values, two per
-// dword); out[j] receives column j.
-__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-    uint32_t d[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint4& lo = in[2 * e];
-      const uint4& hi = in[2 * e + 1];
-      const uint32_t l = (j >> 1) == 0 ? lo.x : (j >> 1) == 1 ? lo.y : (j >> 1) == 2 ? lo.z : lo.w;
-      const uint32_t h = (j >> 1) == 0 ? hi.x : (j >> 1) == 1 ? hi.y : (j >> 1) == 2 ? hi.z : hi.w;
-      d[e] = perm(h, l, sel);
-    }
-    out[j] = make_uint4(d[0], d[1], d[2], d[3]);
-  }
-}
+// Macro tile: kWavesM x kWavesN waves, each owning kFragsM x kFragsN 32x32 accumulators.
+#ifndef SGE_WAVES_M
+#define SGE_WAVES_M 2
+#define SGE_WAVES_N 4
+#define SGE_FRAGS_M 4
+#define SGE_FRAGS_N 2
+#endif
+constexpr int kWavesM = SGE_WAVES_M, kWavesN = SGE_WAVES_N, kFragsM = SGE_FRAGS_M, kFragsN = SGE_FRAGS_N;
 
 __device__ __forceinline__ float fast_sigmoid(float a) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-a));
 }
 
-// Per-operand tile loader: global -> registers -> LDS.
-template <int ROWS, bool KMAJ, int ES>
-struct Loader {
-  static constexpr int kRegs = KMAJ ? ROWS / 32 : 8;
-  uint4 r[kRegs];
+typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-  // base: element (row, k) of the operand is at base[row*ld + k] (KMAJ) or
-  // base[k*ld + row] (!KMAJ); rows >= row_end and k >= k_end read as zero.
-  // rowmap: logical tile row -> operand row (identity except for SwiGLU).
+constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past num_records: the load returns zeros
+
+// Buffer resource over [base, base + bytes); loads beyond it read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7FFFFF00 ? 0x7FFFFF00 : (bytes < 0 ? 0 : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// Global -> LDS copy of one operand tile with buffer_load ... lds (16 B per lane, the wave's
+// 64 lanes filling 1 KB of LDS contiguously); no staging registers. Lanes fetch permuted
+// sources so that the LDS image is swizzled:
+// * inner-contiguous tile: ROWS rows of 128 contraction bytes; chunk c of row r sits at
+//   chunk c ^ swz(r);
+// * outer-contiguous tile (bf16): 64 contraction rows of ROWS*2 bytes; chunk c of row k sits
+//   at chunk c ^ (2*(k & 3)), so the transposing ds_read_b64_tr_b16 of 4 consecutive rows
+//   hits distinct banks.
+// Chunks outside the operand (rows >= row_end, contraction >= k_end) are fetched from an
+// out-of-range offset and land as zeros.
+template <int ROWS, bool KMAJ, int ES, int NWAVES>
+struct TileCopy {
+  static constexpr int kInstr = ROWS * kRowBytes / 1024 / NWAVES;   // 1-KB pieces per wave
+  static constexpr int kRowsPerInstr = KMAJ ? 8 : 1024 / (ROWS * 2);
+  static constexpr int kChunksPerRow = KMAJ ? 8 : ROWS / 8;
+  uint32_t off[kInstr];      // byte offset of the lane's source at contraction 0 (or kOOB)
+  int32_t kk[kInstr];        // contraction index of the lane's source relative to the tile start
+
   template <class RowMap>
-  __device__ __forceinline__ void load(const uint8_t* __restrict__ base, int64_t ld, int64_t row0,
-                                       int64_t row_end, int64_t k0, int64_t k_end,
-                                       const RowMap& rowmap) {
-    const int t = threadIdx.x;
-    if constexpr (KMAJ) {
-      constexpr int kElemsPerChunk = 16 / ES;
-      const int c = t & 7;
-      const int64_t k = k0 + c * kElemsPerChunk;
+  __device__ __forceinline__ void init(int64_t ld, int64_t row0, int64_t row_end, const RowMap& rowmap) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-      for (int i = 0; i < kRegs; ++i) {
-        const int rr = (t >> 3) + 32 * i;
-        const int64_t row = rowmap(row0, rr);
-        if (row < row_end && k < k_end) {
-          r[i] = *reinterpret_cast<const uint4*>(base + (row * ld + k) * ES);
-        } else {
-          r[i] = make_uint4(0, 0, 0, 0);
-        }
-      }
-    } else {
-      static_assert(ES == 2, "transposed tile loads exist for bf16 only");
-      constexpr int kOuterChunks = ROWS / 8;
-      if (t < ROWS) {
-        const int oc = t % kOuterChunks;
-        const int kc = t / kOuterChunks;
-        const int64_t outer = row0 + oc * 8;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int64_t k = k0 + kc * 8 + i;
-          if (outer < row_end && k < k_end) {
-            r[i] = *reinterpret_cast<const uint4*>(base + (k * ld + outer) * 2);
-          } else {
-            r[i] = make_uint4(0, 0, 0, 0);
-          }
-        }
+    for (int i = 0; i < kInstr; ++i) {
+      const int piece = NWAVES * i + wave;
+      const int r = piece * kRowsPerInstr + lane / kChunksPerRow;   // LDS row
+      const int p = lane % kChunksPerRow;                           // physical chunk
+      if constexpr (KMAJ) {
+        const int c = p ^ swz(r);
+        const int64_t row = rowmap(row0, r);
+        kk[i] = c * (16 / ES);
+        off[i] = row < row_end ? (uint32_t)((row - row0) * ld * ES + c * 16) : kOOB;
+      } else {
+        const int c = p ^ (2 * (r & 3));
+        const int64_t outer = row0 + c * 8;
+        kk[i] = r;
+        off[i] = outer < row_end ? (uint32_t)(r * ld * 2 + c * 16) : kOOB;
       }
     }
   }
 
-  __device__ __forceinline__ void store(uint8_t* lds) const {
-    const int t = threadIdx.x;
-    if constexpr (KMAJ) {
-      const int c = t & 7;
+  // Issue the copy of contraction range [k0, k0 + tile) into lds (base of this operand's tile).
+  // base_row0: address of operand row row0 (inner-contiguous) or of contraction row 0 (outer).
+  __device__ __forceinline__ void issue(uint8_t* lds, const uint8_t* base, int64_t ld, int64_t bytes_from_base,
+                                        int64_t k0, int64_t k_end) const {
+    const int wave = threadIdx.x >> 6;
+    // Resource based at the tile's first contraction element keeps offsets 32-bit.
+    const int64_t shift = KMAJ ? k0 * ES : k0 * ld * 2;
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(base + shift, bytes_from_base - shift);
 #pragma unroll
-      for (int i = 0; i < kRegs; ++i) {
-        const int rr = (t >> 3) + 32 * i;
-        *reinterpret_cast<uint4*>(lds + rr * kRowBytes + ((c ^ swz(rr)) << 4)) = r[i];
-      }
-    } else {
-      constexpr int kOuterChunks = ROWS / 8;
-      if (t < ROWS) {
-        const int oc = t % kOuterChunks;
-        const int kc = t / kOuterChunks;
-        uint4 tr[8];
-        transpose8x8(r, tr);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int rr = oc * 8 + j;
-          *reinterpret_cast<uint4*>(lds + rr * kRowBytes + ((kc ^ swz(rr)) << 4)) = tr[j];
-        }
-      }
+    for (int i = 0; i < kInstr; ++i) {
+      const uint32_t o = (k0 + kk[i] < k_end) ? off[i] : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)(lds + (NWAVES * i + wave) * 1024), 16, (int)o, 0,
+                                               0, 0);
     }
   }
 };
+
+// bf16 MFMA fragment (8 contraction values of one row) from an inner-contiguous tile.
+__device__ __forceinline__ bf16x8 frag_k_bf16(const uint8_t* lds, int r, int ch) {
+  return *reinterpret_cast<const bf16x8*>(lds + r * kRowBytes + ((ch ^ swz(r)) << 4));
+}
+
+// The same fragment from an outer-contiguous tile with two transposing reads. Within each
+// 16-lane group, ds_read_b64_tr_b16 hands output lane 4g+c element c of the 8-byte rows
+// addressed by lanes g, 4+g, 8+g, 12+g; lane s therefore addresses contraction row
+// kb + s/4 at outer offset 4*(s%4), and output lane i receives rows kb..kb+3 of outer i.
+template <int ROWS>
+__device__ __forceinline__ bf16x8 frag_t_bf16(const uint8_t* lds, int mbase, int ks, int lane) {
+  const int q = lane >> 4, s = lane & 15;
+  const int m = mbase + 16 * (q & 1) + 4 * (s & 3);
+  const int k = ks * 16 + 8 * (q >> 1) + (s >> 2);
+  const int k2 = k + 4;
+  const uint8_t* p0 = lds + k * (ROWS * 2) + ((((m >> 3) ^ (2 * (k & 3)))) << 4) + (m & 7) * 2;
+  const uint8_t* p1 = lds + k2 * (ROWS * 2) + ((((m >> 3) ^ (2 * (k2 & 3)))) << 4) + (m & 7) * 2;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p1);
+  typedef short i16x8 __attribute__((__vector_size__(8 * sizeof(short))));
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
 
 struct IdentityRows {
   __device__ __forceinline__ int64_t operator()(int64_t row0, int rr) const { return row0 + rr; }
@@ -156,19 +162,24 @@ struct SwigluRows {
   }
 };
 
-template <int FMT, bool AK, bool BK, int EPI, int SCHED, int WMF, int WNF>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+template <int FMT, bool AK, bool BK, int EPI, int SCHED, int WGM, int WGN, int WMF, int WNF>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM * WGN),
+                          amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
 void gemm_kernel(const GemmParams p) {
+  constexpr int NWAVES = WGM * WGN;
   constexpr int ES = FMT == F_BF16 ? 2 : 1;
   constexpr int WM = 32 * WMF, WN = 32 * WNF;
-  constexpr int BM = 2 * WM, BN = 2 * WN;
+  constexpr int BM = WGM * WM, BN = WGN * WN;
   constexpr int KT_ELEMS = kRowBytes / ES;               // contraction elements per k-tile
   constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (A_BYTES + B_BYTES)];
+  // Two LDS stages as distinct objects, so the compiler can tell the tile being
+  // multiplied from the one the direct-to-LDS loads are filling.
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[A_BYTES + B_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[A_BYTES + B_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
   // ---------------------------------------------------------------- schedule
   int64_t m0, n0, row_end, k_begin = 0, k_end = p.K;
@@ -241,23 +252,32 @@ void gemm_kernel(const GemmParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  Loader<BM, AK, ES> la;
-  Loader<BN, BK, ES> lb;
   IdentityRows idrows;
   SwigluRows<WN> swrows{p.F};
-  // Rows of B beyond the operand: N (dense / group M), or N_out rows for group K.
+  // Rows of B: N (dense / group M, 2F for SwiGLU), or the N_out rows of group K.
   const int64_t b_rows = EPI == E_SWIGLU ? 2 * p.F : p.N;
 
-  auto load_tiles = [&](int64_t k0) {
-    la.load(p.a, p.lda, m0, row_end, k0, k_end, idrows);
-    if constexpr (EPI == E_SWIGLU) lb.load(bptr, p.ldb, n0, b_rows, k0, k_end, swrows);
-    else lb.load(bptr, p.ldb, n0, b_rows, k0, k_end, idrows);
+  // Tile copies. Inner-contiguous operands are addressed from their first tile row,
+  // outer-contiguous ones from the tile's first outer column of contraction row 0.
+  TileCopy<BM, AK, ES, NWAVES> ca;
+  TileCopy<BN, BK, ES, NWAVES> cb;
+  const uint8_t* a_base = AK ? p.a + m0 * p.lda * ES : p.a + m0 * 2;
+  const int64_t a_bytes = AK ? ((SCHED == S_GROUP_M ? p.T : p.M) - m0) * p.lda * ES : p.K * p.lda * 2 - m0 * 2;
+  const uint8_t* b_base = BK ? bptr + n0 * p.ldb * ES : bptr + n0 * 2;
+  const int64_t b_bytes = BK ? (b_rows - n0) * p.ldb * ES : p.K * p.ldb * 2 - n0 * 2;
+  ca.init(p.lda, m0, row_end, idrows);
+  if constexpr (EPI == E_SWIGLU) cb.init(p.ldb, n0, b_rows, swrows);
+  else cb.init(p.ldb, n0, b_rows, idrows);
+
+  auto issue_tile = [&](uint8_t* buf, int64_t k0) {
+    ca.issue(buf, a_base, p.lda, a_bytes, k0, k_end);
+    cb.issue(buf + A_BYTES, b_base, p.ldb, b_bytes, k0, k_end);
   };
 
   // MX scales: one dword per fragment row holds the 4 E8M0 bytes of a k-tile,
   // pre-shifted so byte 2*ks of the register is this lane's 32-block.
-  uint32_t sa[WMF], sb[WNF];
-  auto load_scales = [&](int64_t k0) {
+  uint32_t sa[WMF], sb[WNF], san[WMF], sbn[WNF];
+  auto load_scales = [&](int64_t k0, uint32_t (&da)[WMF], uint32_t (&db)[WNF]) {
     if constexpr (FMT == F_MX) {
       const int64_t blk0 = k0 >> 5;
       const int64_t nblk = (k_end + 31) >> 5;
@@ -276,7 +296,7 @@ void gemm_kernel(const GemmParams p) {
             for (int e = 0; e < 4; ++e) v |= (blk0 + e < nblk ? (uint32_t)s[e] : 127u) << (8 * e);
           }
         }
-        sa[i] = v >> sh;
+        da[i] = v >> sh;
       }
 #pragma unroll
       for (int j = 0; j < WNF; ++j) {
@@ -292,75 +312,84 @@ void gemm_kernel(const GemmParams p) {
             for (int e = 0; e < 4; ++e) v |= (blk0 + e < nblk ? (uint32_t)s[e] : 127u) << (8 * e);
           }
         }
-        sb[j] = v >> sh;
+        db[j] = v >> sh;
       }
     }
   };
 
   const int64_t klen = k_end - k_begin;
   const int KT = klen > 0 ? (int)((klen + KT_ELEMS - 1) / KT_ELEMS) : 0;
-
-  if (KT > 0) {
-    load_tiles(k_begin);
-    la.store(smem);
-    lb.store(smem + A_BYTES);
-    __syncthreads();
-  }
-
   const int lrow = lane & 31;
   const int lhalf = lane >> 5;
-  for (int kt = 0; kt < KT; ++kt) {
-    uint8_t* a_lds = smem + (kt & 1) * (A_BYTES + B_BYTES);
-    uint8_t* b_lds = a_lds + A_BYTES;
-    const bool more = kt + 1 < KT;
-    const int64_t k0 = k_begin + (int64_t)kt * KT_ELEMS;
-    load_scales(k0);
-    if (more) load_tiles(k0 + KT_ELEMS);
 
+  // Multiply one LDS stage into the accumulators. Fragments of k-step ks+1 are
+  // read while the MFMAs of step ks run.
+  auto compute = [&](const uint8_t* buf) {
+    const uint8_t* a_lds = buf;
+    const uint8_t* b_lds = buf + A_BYTES;
     if constexpr (FMT == F_BF16) {
+      bf16x8 af[2][WMF], bfr[2][WNF];
+      auto rd = [&](int ks, bf16x8 (&fa)[WMF], bf16x8 (&fb)[WNF]) {
+#pragma unroll
+        for (int i = 0; i < WMF; ++i)
+          fa[i] = AK ? frag_k_bf16(a_lds, wm * WM + i * 32 + lrow, ks * 2 + lhalf)
+                     : frag_t_bf16<BM>(a_lds, wm * WM + i * 32, ks, lane);
+#pragma unroll
+        for (int j = 0; j < WNF; ++j)
+          fb[j] = BK ? frag_k_bf16(b_lds, wn * WN + j * 32 + lrow, ks * 2 + lhalf)
+                     : frag_t_bf16<BN>(b_lds, wn * WN + j * 32, ks, lane);
+      };
+      constexpr int kReads = (AK ? WMF : 2 * WMF) + (BK ? WNF : 2 * WNF);
+      constexpr int kMfma = WMF * WNF;
+      rd(0, af[0], bfr[0]);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int ch = ks * 2 + lhalf;
-        bf16x8 af[WMF], bfr[WNF];
-#pragma unroll
-        for (int i = 0; i < WMF; ++i) {
-          const int r = wm * WM + i * 32 + lrow;
-          af[i] = *reinterpret_cast<const bf16x8*>(a_lds + r * kRowBytes + ((ch ^ swz(r)) << 4));
-        }
-#pragma unroll
-        for (int j = 0; j < WNF; ++j) {
-          const int r = wn * WN + j * 32 + lrow;
-          bfr[j] = *reinterpret_cast<const bf16x8*>(b_lds + r * kRowBytes + ((ch ^ swz(r)) << 4));
-        }
+        if (ks < 3) rd(ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
 #pragma unroll
         for (int i = 0; i < WMF; ++i)
 #pragma unroll
           for (int j = 0; j < WNF; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks & 1][j], af[ks & 1][i], acc[i][j], 0, 0, 0);
+      }
+      // Issue order: the first fragments, then per k-step one MFMA after each LDS read of
+      // the next step's fragments, then the remaining MFMAs of the step.
+      __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks < 3) {
+#pragma unroll
+          for (int t = 0; t < (kReads < kMfma ? kReads : kMfma); ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          if (kReads < kMfma) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
+        }
       }
     } else {
+      // f8f6f4 32x32x64 lane layout: bytes 0-15 hold k = 16*half .. +15 and
+      // bytes 16-31 hold k = 32 + 16*half .. +15 of the 64-wide step.
+      i32x8 af[2][WMF], bfr[2][WNF];
+      auto rd8 = [&](const uint8_t* base, int r, int ks) {
+        const int c0 = ks * 4 + lhalf, c1 = c0 + 2;
+        const uint8_t* row = base + r * kRowBytes;
+        const int4 lo = *reinterpret_cast<const int4*>(row + ((c0 ^ swz(r)) << 4));
+        const int4 hi = *reinterpret_cast<const int4*>(row + ((c1 ^ swz(r)) << 4));
+        return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      };
+      auto rd = [&](int ks, i32x8 (&fa)[WMF], i32x8 (&fb)[WNF]) {
+#pragma unroll
+        for (int i = 0; i < WMF; ++i) fa[i] = rd8(a_lds, wm * WM + i * 32 + lrow, ks);
+#pragma unroll
+        for (int j = 0; j < WNF; ++j) fb[j] = rd8(b_lds, wn * WN + j * 32 + lrow, ks);
+      };
+      constexpr int kReads = 2 * (WMF + WNF);
+      constexpr int kMfma = WMF * WNF;
+      rd(0, af[0], bfr[0]);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        // f8f6f4 32x32x64 lane layout: bytes 0-15 hold k = 16*half .. +15 and
-        // bytes 16-31 hold k = 32 + 16*half .. +15 of the 64-wide step.
-        const int c0 = ks * 4 + lhalf, c1 = c0 + 2;
-        i32x8 af[WMF], bfr[WNF];
-#pragma unroll
-        for (int i = 0; i < WMF; ++i) {
-          const int r = wm * WM + i * 32 + lrow;
-          const uint8_t* row = a_lds + r * kRowBytes;
-          const int4 lo = *reinterpret_cast<const int4*>(row + ((c0 ^ swz(r)) << 4));
-          const int4 hi = *reinterpret_cast<const int4*>(row + ((c1 ^ swz(r)) << 4));
-          af[i] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        }
-#pragma unroll
-        for (int j = 0; j < WNF; ++j) {
-          const int r = wn * WN + j * 32 + lrow;
-          const uint8_t* row = b_lds + r * kRowBytes;
-          const int4 lo = *reinterpret_cast<const int4*>(row + ((c0 ^ swz(r)) << 4));
-          const int4 hi = *reinterpret_cast<const int4*>(row + ((c1 ^ swz(r)) << 4));
-          bfr[j] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        }
+        if (ks < 1) rd(ks + 1, af[1], bfr[1]);
 #pragma unroll
         for (int i = 0; i < WMF; ++i)
 #pragma unroll
@@ -368,68 +397,127 @@ void gemm_kernel(const GemmParams p) {
             if constexpr (FMT == F_MX) {
               if (ks == 0)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    bfr[j], af[i], acc[i][j], 0, 0, 0, (int)sb[j], 0, (int)sa[i]);
+                    bfr[0][j], af[0][i], acc[i][j], 0, 0, 0, (int)sb[j], 0, (int)sa[i]);
               else
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    bfr[j], af[i], acc[i][j], 0, 0, 2, (int)sb[j], 2, (int)sa[i]);
+                    bfr[1][j], af[1][i], acc[i][j], 0, 0, 2, (int)sb[j], 2, (int)sa[i]);
             } else {
               acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  bfr[j], af[i], acc[i][j], 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
+                  bfr[ks][j], af[ks][i], acc[i][j], 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
             }
           }
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+#pragma unroll
+      for (int t = 0; t < (kReads < kMfma ? kReads : kMfma); ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if (kReads < kMfma) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
     }
+  };
 
-    if (more) {
-      uint8_t* na = smem + ((kt + 1) & 1) * (A_BYTES + B_BYTES);
-      la.store(na);
-      lb.store(na + A_BYTES);
-    }
+  // Each wave waits for its own direct-to-LDS copies, then the barrier makes the
+  // whole stage visible (and frees the other stage for the next copies).
+  auto stage_done = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+
+  if (KT > 0) {
+    issue_tile(lds0, k_begin);
+    load_scales(k_begin, sa, sb);
+    stage_done();
+  }
+  for (int kt = 0; kt < KT; ++kt) {
+    uint8_t* cur = (kt & 1) ? lds1 : lds0;
+    uint8_t* nxt = (kt & 1) ? lds0 : lds1;
+    const bool more = kt + 1 < KT;
+    if (more) {
+      issue_tile(nxt, k_begin + (int64_t)(kt + 1) * KT_ELEMS);
+      load_scales(k_begin + (int64_t)(kt + 1) * KT_ELEMS, san, sbn);
+    }
+    compute(cur);
+    stage_done();
+    if constexpr (FMT == F_MX) {
+#pragma unroll
+      for (int i = 0; i < WMF; ++i) sa[i] = san[i];
+#pragma unroll
+      for (int j = 0; j < WNF; ++j) sb[j] = sbn[j];
+    }
   }
 
   // ---------------------------------------------------------------- epilogue
+  // Branch-free: every global access is a buffer op over the output tile whose
+  // out-of-range lanes read zeros / drop their writes, so all loads of a row block
+  // are in flight together (and the next block's loads overlap this block's math).
   float alpha = p.alpha;
   if constexpr (FMT == F_E4M3) alpha = (p.a_sinv[0] * p.b_sinv[0]) * p.alpha;
+  typedef int v2i __attribute__((__vector_size__(2 * sizeof(int))));
+  const int64_t c_rows = SCHED == S_GROUP_M ? p.T : p.M;
+  const int64_t rows_left = c_rows - m0;
+  auto row_in_tile = [&](int i) { return wm * WM + i * 32 + lrow; };
+  auto row_ok = [&](int i) { return m0 + row_in_tile(i) < row_end; };
 
   if constexpr (EPI == E_STORE) {
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(cptr + m0 * p.ldc, rows_left * p.ldc * 2);
+    auto off = [&](int i, int j, int q) -> int {
+      const int64_t n = n0 + wn * WN + j * 32 + 8 * q + 4 * lhalf;
+      return (row_ok(i) && n < n_end) ? (int)(((int64_t)row_in_tile(i) * p.ldc + n) * 2) : (int)kOOB;
+    };
+    auto store = [&](int i, int j, int q, float v0, float v1, float v2, float v3) {
+      const v2i w = {(int)pack_bf16x2(v0, v1), (int)pack_bf16x2(v2, v3)};
+      __builtin_amdgcn_raw_buffer_store_b64(w, rc, off(i, j, q), 0, 0);
+    };
+    if (p.accumulate) {
+      v2i res[2][WNF][4];
+      auto load = [&](int i, v2i (&r)[WNF][4]) {
 #pragma unroll
-    for (int i = 0; i < WMF; ++i) {
-      const int64_t m = m0 + wm * WM + i * 32 + lrow;
-      if (m >= row_end) continue;
+        for (int j = 0; j < WNF; ++j)
 #pragma unroll
-      for (int j = 0; j < WNF; ++j) {
+          for (int q = 0; q < 4; ++q) r[j][q] = __builtin_amdgcn_raw_buffer_load_b64(rc, off(i, j, q), 0, 0);
+      };
+      load(0, res[0]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t n = n0 + wn * WN + j * 32 + 8 * q + 4 * lhalf;
-          if (n >= n_end) continue;
-          float v0 = alpha * acc[i][j][4 * q + 0], v1 = alpha * acc[i][j][4 * q + 1];
-          float v2 = alpha * acc[i][j][4 * q + 2], v3 = alpha * acc[i][j][4 * q + 3];
-          uint16_t* cp = cptr + m * p.ldc + n;
-          if (p.accumulate) {
-            const uint2 r = *reinterpret_cast<const uint2*>(cp);
-            v0 = bf16_lo(r.x) + v0;
-            v1 = bf16_hi(r.x) + v1;
-            v2 = bf16_lo(r.y) + v2;
-            v3 = bf16_hi(r.y) + v3;
+      for (int i = 0; i < WMF; ++i) {
+        if (i + 1 < WMF) load(i + 1, res[(i + 1) & 1]);
+#pragma unroll
+        for (int j = 0; j < WNF; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const v2i r = res[i & 1][j][q];
+            store(i, j, q, bf16_lo((uint32_t)r[0]) + alpha * acc[i][j][4 * q + 0],
+                  bf16_hi((uint32_t)r[0]) + alpha * acc[i][j][4 * q + 1],
+                  bf16_lo((uint32_t)r[1]) + alpha * acc[i][j][4 * q + 2],
+                  bf16_hi((uint32_t)r[1]) + alpha * acc[i][j][4 * q + 3]);
           }
-          *reinterpret_cast<uint2*>(cp) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
-        }
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < WMF; ++i)
+#pragma unroll
+        for (int j = 0; j < WNF; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            store(i, j, q, alpha * acc[i][j][4 * q + 0], alpha * acc[i][j][4 * q + 1], alpha * acc[i][j][4 * q + 2],
+                  alpha * acc[i][j][4 * q + 3]);
     }
   } else if constexpr (EPI == E_SWIGLU) {
     constexpr int HJ = WNF / 2;
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(cptr + m0 * p.ldc, rows_left * p.ldc * 2);
+    const __amdgpu_buffer_rsrc_t rh = make_rsrc(p.aux ? p.aux + m0 * p.ld_aux : p.aux, p.aux ? rows_left * p.ld_aux * 2 : 0);
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.probs + m0, rows_left * 4);
 #pragma unroll
     for (int i = 0; i < WMF; ++i) {
-      const int64_t m = m0 + wm * WM + i * 32 + lrow;
-      if (m >= row_end) continue;
-      const float pm = p.probs[m];
+      const float pm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                     rp, row_ok(i) ? row_in_tile(i) * 4 : (int)kOOB, 0, 0));
 #pragma unroll
       for (int j = 0; j < HJ; ++j) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int64_t col = n0 + wn * (WN / 2) + j * 32 + 8 * q + 4 * lhalf;
-          if (col >= n_end) continue;
+          const bool ok = row_ok(i) && col < n_end;
           float a[4], b[4], y[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -437,70 +525,92 @@ void gemm_kernel(const GemmParams p) {
             b[e] = alpha * acc[i][j + HJ][4 * q + e];
             y[e] = pm * (a[e] * fast_sigmoid(a[e])) * b[e];
           }
-          if (p.aux) {
-            uint16_t* hp = p.aux + m * p.ld_aux + col;
-            *reinterpret_cast<uint2*>(hp) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
-            *reinterpret_cast<uint2*>(hp + p.F) =
-                make_uint2(pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]));
-          }
-          *reinterpret_cast<uint2*>(cptr + m * p.ldc + col) =
-              make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+          const int oh = ok ? (int)(((int64_t)row_in_tile(i) * p.ld_aux + col) * 2) : (int)kOOB;
+          const int ohb = ok ? (int)(((int64_t)row_in_tile(i) * p.ld_aux + p.F + col) * 2) : (int)kOOB;
+          const int oy = ok ? (int)(((int64_t)row_in_tile(i) * p.ldc + col) * 2) : (int)kOOB;
+          const v2i hv = {(int)pack_bf16x2(a[0], a[1]), (int)pack_bf16x2(a[2], a[3])};
+          const v2i bv = {(int)pack_bf16x2(b[0], b[1]), (int)pack_bf16x2(b[2], b[3])};
+          const v2i yv = {(int)pack_bf16x2(y[0], y[1]), (int)pack_bf16x2(y[2], y[3])};
+          __builtin_amdgcn_raw_buffer_store_b64(hv, rh, oh, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(bv, rh, ohb, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(yv, ry, oy, 0, 0);
         }
       }
     }
   } else {  // E_DSWIGLU
+    const __amdgpu_buffer_rsrc_t rh = make_rsrc(p.aux + m0 * p.ld_aux, rows_left * p.ld_aux * 2);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.aux_out + m0 * p.ld_aux_out, rows_left * p.ld_aux_out * 2);
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.probs + m0, rows_left * 4);
+    const __amdgpu_buffer_rsrc_t rpart = make_rsrc(p.dp_part + (int64_t)(nt * WGN + wn) * p.T + m0, rows_left * 4);
+    auto hoff = [&](int i, int j, int q, int half) -> int {
+      const int64_t n = n0 + wn * WN + j * 32 + 8 * q + 4 * lhalf;
+      return (row_ok(i) && n < n_end) ? (int)(((int64_t)row_in_tile(i) * p.ld_aux + half * p.F + n) * 2) : (int)kOOB;
+    };
+    v2i hab[1][WNF][4][2];
+    auto load = [&](int i, v2i (&h)[WNF][4][2]) {
+#pragma unroll
+      for (int j = 0; j < WNF; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int half = 0; half < 2; ++half)
+            h[j][q][half] = __builtin_amdgcn_raw_buffer_load_b64(rh, hoff(i, j, q, half), 0, 0);
+    };
 #pragma unroll
     for (int i = 0; i < WMF; ++i) {
-      const int64_t m = m0 + wm * WM + i * 32 + lrow;
-      const bool mok = m < row_end;
-      const float pm = mok ? p.probs[m] : 0.0f;
+      load(i, hab[0]);
+      const float pm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                     rp, row_ok(i) ? row_in_tile(i) * 4 : (int)kOOB, 0, 0));
       float part = 0.0f;
 #pragma unroll
       for (int j = 0; j < WNF; ++j) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int64_t n = n0 + wn * WN + j * 32 + 8 * q + 4 * lhalf;
-          if (!mok || n >= n_end) continue;
-          const uint16_t* hp = p.aux + m * p.ld_aux + n;
-          const uint2 ha = *reinterpret_cast<const uint2*>(hp);
-          const uint2 hb = *reinterpret_cast<const uint2*>(hp + p.F);
-          const float a[4] = {bf16_lo(ha.x), bf16_hi(ha.x), bf16_lo(ha.y), bf16_hi(ha.y)};
-          const float b[4] = {bf16_lo(hb.x), bf16_hi(hb.x), bf16_lo(hb.y), bf16_hi(hb.y)};
+          const v2i ha = hab[0][j][q][0], hb = hab[0][j][q][1];
+          const float a[4] = {bf16_lo((uint32_t)ha[0]), bf16_hi((uint32_t)ha[0]), bf16_lo((uint32_t)ha[1]),
+                              bf16_hi((uint32_t)ha[1])};
+          const float b[4] = {bf16_lo((uint32_t)hb[0]), bf16_hi((uint32_t)hb[0]), bf16_lo((uint32_t)hb[1]),
+                              bf16_hi((uint32_t)hb[1])};
           float da[4], db[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float g = alpha * acc[i][j][4 * q + e];
-            const float s = fast_sigmoid(a[e]);
-            const float silu = a[e] * s;
-            const float dsilu = s * (1.0f + a[e] * (1.0f - s));
+            const float sg = fast_sigmoid(a[e]);
+            const float silu = a[e] * sg;
+            const float dsilu = sg * (1.0f + a[e] * (1.0f - sg));
             da[e] = g * pm * b[e] * dsilu;
             db[e] = g * pm * silu;
             part += g * silu * b[e];
           }
-          uint16_t* dp = p.aux_out + m * p.ld_aux_out + n;
-          *reinterpret_cast<uint2*>(dp) = make_uint2(pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3]));
-          *reinterpret_cast<uint2*>(dp + p.F) =
-              make_uint2(pack_bf16x2(db[0], db[1]), pack_bf16x2(db[2], db[3]));
+          const v2i dav = {(int)pack_bf16x2(da[0], da[1]), (int)pack_bf16x2(da[2], da[3])};
+          const v2i dbv = {(int)pack_bf16x2(db[0], db[1]), (int)pack_bf16x2(db[2], db[3])};
+          __builtin_amdgcn_raw_buffer_store_b64(dav, rd, hoff(i, j, q, 0) == (int)kOOB ? (int)kOOB
+                                                    : (int)(((int64_t)row_in_tile(i) * p.ld_aux_out + n0 + wn * WN + j * 32 + 8 * q + 4 * lhalf) * 2), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(dbv, rd, hoff(i, j, q, 1) == (int)kOOB ? (int)kOOB
+                                                    : (int)(((int64_t)row_in_tile(i) * p.ld_aux_out + p.F + n0 + wn * WN + j * 32 + 8 * q + 4 * lhalf) * 2), 0, 0);
         }
       }
+      // Lanes l and l+32 hold the same row: combine, then one lane writes the row's partial.
       part += __shfl_xor(part, 32, 64);
-      if (mok && lhalf == 0) p.dp_part[(int64_t)(nt * 2 + wn) * p.T + m] = part;
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, part), rpart,
+                                            (row_ok(i) && lhalf == 0) ? row_in_tile(i) * 4 : (int)kOOB, 0, 0);
     }
   }
 }
 
 // ------------------------------------------------------------------ launchers
-template <int FMT, bool AK, bool BK, int EPI, int SCHED, int WMF, int WNF>
+template <int FMT, bool AK, bool BK, int EPI, int SCHED, int WGM, int WGN, int WMF, int WNF>
 static hipError_t launch_cfg(GemmParams p, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<FMT, AK, BK, EPI, SCHED, WMF, WNF>), dim3(grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_kernel<FMT, AK, BK, EPI, SCHED, WGM, WGN, WMF, WNF>), dim3(grid), dim3(64 * WGM * WGN), 0,
+                     s, p);
   return hipGetLastError();
 }
 
 template <int FMT, bool AK, bool BK, int EPI, int SCHED>
 static hipError_t launch_tile(GemmParams p, hipStream_t s) {
-  constexpr int WMF = 4, WNF = 4;
-  constexpr int BM = 64 * WMF, BN = 64 * WNF;
+  constexpr int WGM = kWavesM, WGN = kWavesN, WMF = kFragsM, WNF = kFragsN;
+  constexpr int BM = WGM * 32 * WMF, BN = WGN * 32 * WNF;
   int grid = 0;
   if constexpr (SCHED == S_DENSE) {
     p.mt_count = (int)((p.M + BM - 1) / BM);
@@ -517,7 +627,7 @@ static hipError_t launch_tile(GemmParams p, hipStream_t s) {
     p.nt_count = (int)((p.N + BN - 1) / BN);
     grid = p.mt_count * p.nt_count * p.G;
   }
-  return launch_cfg<FMT, AK, BK, EPI, SCHED, WMF, WNF>(p, grid, s);
+  return launch_cfg<FMT, AK, BK, EPI, SCHED, WGM, WGN, WMF, WNF>(p, grid, s);
 }
 
 hipError_t launch_gemm(const GemmParams& p, int fmt, bool a_kmaj, bool b_kmaj, hipStream_t s) {
@@ -545,6 +655,7 @@ hipError_t launch_grouped_wgrad(const GemmParams& p, hipStream_t s) {
   return launch_tile<F_BF16, false, false, E_STORE, S_GROUP_K>(p, s);
 }
 
-int gemm_tile_n() { return 256; }
+int gemm_tile_n() { return kWavesN * 32 * kFragsN; }
+int gemm_dp_parts_per_tile() { return kWavesN; }
 
 }  // namespace sge

@@ -46,6 +46,7 @@ hipError_t launch_grouped_fwd(const GemmParams& p, int epilogue, hipStream_t s);
 hipError_t launch_grouped_dgrad(const GemmParams& p, int epilogue, hipStream_t s);
 hipError_t launch_grouped_wgrad(const GemmParams& p, hipStream_t s);
 int gemm_tile_n();
+int gemm_dp_parts_per_tile();
 
 hipError_t launch_fill_bf16_zero(uint16_t* c, int64_t rows, int64_t cols, int64_t ld, hipStream_t s);
 hipError_t launch_fill_f32_zero(float* c, int64_t n, hipStream_t s);
