@@ -10,10 +10,15 @@ inputs already resident in HBM:
   of both layers.
 
 Prints ONE JSON line on stdout. The default workload is the bf16 forward +
-backward at M = N = K = 4096 (alpha 0.125). Per-kernel durations come from
-HIP events recorded on the stream the kernels run on; ``roofline`` reports the
-kernel with the largest share of the step. ``cpu_baseline`` times the CPU
-oracle on a bounded sample of the same workload.
+backward at M = N = K = 4096 (alpha 0.125). The timed region is ``--steps``
+eager steps between HIP events; ``ms_per_step_graph`` replays the same step
+captured as one HIP graph (every libsge call is capture-safe), for
+comparison. Per-kernel durations come from a graph of repeated
+launches of that one call, timed with HIP events on the stream they run on;
+``roofline`` reports the kernel with the largest share of the step, and its
+``traffic`` comes from the committed rocprofv3 counter summary when that was
+taken on the current kernel source. ``cpu_baseline`` times the CPU oracle on a
+bounded sample of the same workload.
 """
 
 import argparse
@@ -45,30 +50,36 @@ def parse():
 
 
 # --------------------------------------------------------------- GPU path
-class Timer:
-    """Named HIP-event intervals on the current stream, summed over the timed steps."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.marks = []
-        self.on = False
-
-    def mark(self, name):
-        if self.on:
-            e = self.torch.cuda.Event(enable_timing=True)
-            e.record()
-            self.marks.append((name, e))
-
-    def durations_ms(self):
-        out = {}
-        for (name, a), (_, b) in zip(self.marks[:-1], self.marks[1:]):
-            if name is None:
-                continue
-            out.setdefault(name, []).append(a.elapsed_time(b))
-        return out
+def capture(torch, fns):
+    """A HIP graph of the given launches (every libsge call is capture-safe: no allocation, no sync)."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return g
 
 
-def build_dense(torch, sge, wl, inp, timer):
+def time_ms(torch, fn, reps):
+    """HIP events on the current stream around `reps` calls of fn; returns ms per call."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def build_dense(torch, sge, wl, inp):
     fmt = wl["fmt"]
 
     def dev_bf16(bits):
@@ -97,8 +108,8 @@ def build_dense(torch, sge, wl, inp, timer):
         dg = (sge.Operand.bf16(DY), sge.Operand.bf16(W, transposed=True))
         wg = (sge.Operand.bf16(DY, transposed=True), sge.Operand.bf16(X, transposed=True))
 
-        def quantize():
-            pass
+        def quantize_launches():
+            return []
     elif fmt == "fp8":
         bufs = {}
         for name, t in (("x", X), ("w", W), ("dy", DY)):
@@ -113,10 +124,10 @@ def build_dense(torch, sge, wl, inp, timer):
         dg = (sge.Operand.e4m3(bd["q"], bd["scale_inv"]), sge.Operand.e4m3(bw["q_t"], bw["scale_inv"]))
         wg = (sge.Operand.e4m3(bd["q_t"], bd["scale_inv"]), sge.Operand.e4m3(bx["q_t"], bx["scale_inv"]))
 
-        def quantize():
-            for name, b in bufs.items():
-                timer.mark(f"quant_{name}")
-                sge.quantize_fp8_amax(b["src"], b["q"], b["q_t"], b["amax"], b["scale"], b["scale_inv"], b["ws"])
+        def quantize_launches():
+            return [(f"quant_{name}", (lambda b=b: sge.quantize_fp8_amax(b["src"], b["q"], b["q_t"], b["amax"],
+                                                                          b["scale"], b["scale_inv"], b["ws"])))
+                    for name, b in bufs.items()]
     else:
         bufs = {}
         for name, t in (("x", X), ("w", W), ("dy", DY)):
@@ -129,26 +140,20 @@ def build_dense(torch, sge, wl, inp, timer):
         dg = (sge.Operand.mxfp8(bd["q_row"], bd["s_row"]), sge.Operand.mxfp8(bw["q_colT"], bw["s_colT"]))
         wg = (sge.Operand.mxfp8(bd["q_colT"], bd["s_colT"]), sge.Operand.mxfp8(bx["q_colT"], bx["s_colT"]))
 
-        def quantize():
-            for name, b in bufs.items():
-                timer.mark(f"quant_{name}")
-                sge.quantize_mxfp8(b["src"], b["q_row"], b["s_row"], b["q_colT"], b["s_colT"])
+        def quantize_launches():
+            return [(f"quant_{name}", (lambda b=b: sge.quantize_mxfp8(b["src"], b["q_row"], b["s_row"], b["q_colT"],
+                                                                       b["s_colT"])))
+                    for name, b in bufs.items()]
 
-    def step():
-        quantize()
-        timer.mark("gemm_fwd")
-        sge.linear_scale_add_fwd(*fwd, R, alpha)
-        if bwd:
-            timer.mark("gemm_dgrad")
-            sge.linear_scale_bwd(*dg, None, None, dgrad, None, alpha, alpha)
-            timer.mark("gemm_wgrad")
-            sge.linear_scale_bwd(None, None, *wg, None, wgrad, alpha, alpha)
-        timer.mark(None)
-
-    return step, flops, hbm, sum(flops.values())
+    launches = list(quantize_launches())
+    launches.append(("gemm_fwd", lambda: sge.linear_scale_add_fwd(*fwd, R, alpha)))
+    if bwd:
+        launches.append(("gemm_dgrad", lambda: sge.linear_scale_bwd(*dg, None, None, dgrad, None, alpha, alpha)))
+        launches.append(("gemm_wgrad", lambda: sge.linear_scale_bwd(None, None, *wg, None, wgrad, alpha, alpha)))
+    return launches, flops, hbm
 
 
-def build_grouped(torch, sge, wl, inp, timer):
+def build_grouped(torch, sge, wl, inp):
     import numpy as np
 
     def dev_bf16(bits):
@@ -170,26 +175,19 @@ def build_grouped(torch, sge, wl, inp, timer):
     flops = {"fc1_fwd": 2 * T * N1 * H, "fc2_fwd": 2 * T * H * F, "fc2_dgrad_dswiglu": 2 * T * H * F,
              "fc2_wgrad": 2 * T * H * F, "fc1_dgrad": 2 * T * N1 * H, "fc1_wgrad": 2 * T * N1 * H}
 
-    def step():
-        timer.mark("offsets")
-        sge.splits_to_offsets(splits, [1, H], offs)
-        base = offs[0]
-        timer.mark("fc1_fwd")
-        sge.grouped_linear_fwd(X, W1, base, y, epilogue=sge.EPI_SCALED_SWIGLU, probs=P, preact=h)
-        timer.mark("fc2_fwd")
-        sge.grouped_linear_fwd(y, W2, base, out)
-        timer.mark("fc2_dgrad_dswiglu")
-        sge.grouped_linear_bwd(DOUT, None, W2, base, epilogue=sge.EPI_DSCALED_SWIGLU, preact=h, probs=P,
-                               dact=dh, dprobs=dp, workspace=ws)
-        timer.mark("fc2_wgrad")
-        sge.grouped_linear_bwd(DOUT, y, W2, base, dw=dw2)
-        timer.mark("fc1_dgrad")
-        sge.grouped_linear_bwd(dh, None, W1, base, dx=dx)
-        timer.mark("fc1_wgrad")
-        sge.grouped_linear_bwd(dh, X, W1, base, dw=dw1)
-        timer.mark(None)
-
-    return step, flops, {}, sum(flops.values())
+    base = offs[0]
+    launches = [
+        ("offsets", lambda: sge.splits_to_offsets(splits, [1, H], offs)),
+        ("fc1_fwd", lambda: sge.grouped_linear_fwd(X, W1, base, y, epilogue=sge.EPI_SCALED_SWIGLU, probs=P,
+                                                   preact=h)),
+        ("fc2_fwd", lambda: sge.grouped_linear_fwd(y, W2, base, out)),
+        ("fc2_dgrad_dswiglu", lambda: sge.grouped_linear_bwd(DOUT, None, W2, base, epilogue=sge.EPI_DSCALED_SWIGLU,
+                                                             preact=h, probs=P, dact=dh, dprobs=dp, workspace=ws)),
+        ("fc2_wgrad", lambda: sge.grouped_linear_bwd(DOUT, y, W2, base, dw=dw2)),
+        ("fc1_dgrad", lambda: sge.grouped_linear_bwd(dh, None, W1, base, dx=dx)),
+        ("fc1_wgrad", lambda: sge.grouped_linear_bwd(dh, X, W1, base, dw=dw1)),
+    ]
+    return launches, flops, {}
 
 
 # ----------------------------------------------------------- CPU baseline
@@ -275,25 +273,32 @@ def main():
 
     wl = synth.WORKLOADS[args.workload]
     inp = synth.workload_inputs(args.workload, seed=0)
-    timer = Timer(torch)
     builder = build_dense if wl["kind"] == "dense" else build_grouped
-    step, flops, hbm, step_flops = builder(torch, sge, wl, inp, timer)
+    launches, flops, hbm = builder(torch, sge, wl, inp)
+    step_flops = sum(flops.values())
+
+    def eager_step():
+        for _, f in launches:
+            f()
 
     for _ in range(args.warmup):
-        step()
+        eager_step()
     torch.cuda.synchronize()
-    timer.on = True
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        step()
-    stop.record()
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    timer.on = False
-    ms_per_step = total_ms / args.steps
-    per = {k: sum(v) / len(v) for k, v in timer.durations_ms().items()}
+    # The timed region: exactly `steps` eager steps between HIP events, synchronized on both sides.
+    ms_per_step = time_ms(torch, eager_step, args.steps)
+    # The same step as one HIP graph (reported for comparison; not the timed value).
+    graph = capture(torch, [f for _, f in launches])
+    ms_graph = time_ms(torch, graph.replay, max(1, min(args.steps, 10)))
+    del graph
+    # Per-kernel durations: a graph of `reps` back-to-back launches of one call, timed with
+    # HIP events around its replays (the kernels run on the replay stream the events mark).
+    per = {}
+    reps = 8
+    for name, f in launches:
+        g = capture(torch, [f] * reps)
+        g.replay()
+        per[name] = time_ms(torch, g.replay, 3) / reps
+        del g
 
     fmt = wl["fmt"]
     peak = PEAK_TFLOPS[fmt]
@@ -318,7 +323,8 @@ def main():
     cfg.update({k: wl[k] for k in ("M", "N", "K", "T", "G", "hidden", "ffn", "alpha") if k in wl})
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "ms_per_step_graph": round(ms_graph, 4),
+        "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": fmt, "data": "synthetic (seeded; see synth/)",
         "config": cfg, "frac_of_peak": round(value / peak, 4), "kernels": kernels, "roofline": roofline,
     }
