@@ -27,12 +27,14 @@
 // * Fragments of k-step s+1 are read from LDS while the MFMAs of step s run.
 // * The MFMA is issued with B as its first operand, so each lane ends with 4
 //   consecutive output columns per group and stores 8 bytes of bf16 at a time.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace sge {
 
-enum { F_BF16 = 0, F_E4M3 = 1, F_MX = 2 };
+enum { F_BF16 = 0, F_E4M3 = 1, F_MX = 2, F_MXU = 3 };   // F_MXU: MXFP8 with unaligned scale rows
 enum { E_STORE = 0, E_SWIGLU = 1, E_DSWIGLU = 2 };
 enum { S_DENSE = 0, S_GROUP_M = 1, S_GROUP_K = 2 };
 
@@ -68,8 +70,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // * inner-contiguous tile: ROWS rows of 128 contraction bytes; chunk c of row r sits at
 //   chunk c ^ swz(r);
 // * outer-contiguous tile (bf16): 64 contraction rows of ROWS*2 bytes; chunk c of row k sits
-//   at chunk c ^ (2*(k & 3)), so the transposing ds_read_b64_tr_b16 of 4 consecutive rows
-//   hits distinct banks.
+//   at chunk c ^ (4*(k & 3)), so the 32 lanes the LDS serves per cycle for a transposing
+//   ds_read_b64_tr_b16 (4 consecutive rows x 64 bytes) hit distinct banks.
 // Chunks outside the operand (rows >= row_end, contraction >= k_end) are fetched from an
 // out-of-range offset and land as zeros.
 template <int ROWS, bool KMAJ, int ES, int NWAVES>
@@ -94,7 +96,7 @@ struct TileCopy {
         kk[i] = c * (16 / ES);
         off[i] = row < row_end ? (uint32_t)((row - row0) * ld * ES + c * 16) : kOOB;
       } else {
-        const int c = p ^ (2 * (r & 3));
+        const int c = p ^ (4 * (r & 3));
         const int64_t outer = row0 + c * 8;
         kk[i] = r;
         off[i] = outer < row_end ? (uint32_t)(r * ld * 2 + c * 16) : kOOB;
@@ -134,8 +136,8 @@ __device__ __forceinline__ bf16x8 frag_t_bf16(const uint8_t* lds, int mbase, int
   const int m = mbase + 16 * (q & 1) + 4 * (s & 3);
   const int k = ks * 16 + 8 * (q >> 1) + (s >> 2);
   const int k2 = k + 4;
-  const uint8_t* p0 = lds + k * (ROWS * 2) + ((((m >> 3) ^ (2 * (k & 3)))) << 4) + (m & 7) * 2;
-  const uint8_t* p1 = lds + k2 * (ROWS * 2) + ((((m >> 3) ^ (2 * (k2 & 3)))) << 4) + (m & 7) * 2;
+  const uint8_t* p0 = lds + k * (ROWS * 2) + ((((m >> 3) ^ (4 * (k & 3)))) << 4) + (m & 7) * 2;
+  const uint8_t* p1 = lds + k2 * (ROWS * 2) + ((((m >> 3) ^ (4 * (k2 & 3)))) << 4) + (m & 7) * 2;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p1);
   typedef short i16x8 __attribute__((__vector_size__(8 * sizeof(short))));
@@ -167,6 +169,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM *
                           amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
 void gemm_kernel(const GemmParams p) {
   constexpr int NWAVES = WGM * WGN;
+  constexpr bool kMX = FMT == F_MX || FMT == F_MXU;
   constexpr int ES = FMT == F_BF16 ? 2 : 1;
   constexpr int WM = 32 * WMF, WN = 32 * WNF;
   constexpr int BM = WGM * WM, BN = WGN * WN;
@@ -176,6 +179,10 @@ void gemm_kernel(const GemmParams p) {
   // multiplied from the one the direct-to-LDS loads are filling.
   __shared__ __attribute__((aligned(16))) uint8_t lds0[A_BYTES + B_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t lds1[A_BYTES + B_BYTES];
+  // MXFP8: E8M0 scales of 4 k-tiles (16 blocks of 32) per operand row, double-buffered.
+  constexpr int kScaleTiles = 4;
+  constexpr int SC_BYTES = FMT == F_MX ? (BM + BN) * 4 * kScaleTiles : 16;
+  __shared__ __attribute__((aligned(16))) uint8_t sc_lds[2][SC_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -275,26 +282,58 @@ void gemm_kernel(const GemmParams p) {
   };
 
   // MX scales: one dword per fragment row holds the 4 E8M0 bytes of a k-tile,
-  // pre-shifted so byte 2*ks of the register is this lane's 32-block.
+  // pre-shifted so byte 2*ks of the register is this lane's 32-block. When the scale
+  // rows are dword-aligned, 16 bytes per row (4 k-tiles) move to LDS by DMA and each
+  // k-tile reads its dword from there; otherwise bytes are read from global memory.
   uint32_t sa[WMF], sb[WNF], san[WMF], sbn[WNF];
-  auto load_scales = [&](int64_t k0, uint32_t (&da)[WMF], uint32_t (&db)[WNF]) {
+  constexpr bool mx_lds = FMT == F_MX;
+  auto issue_scales = [&](int group, int buf) {
     if constexpr (FMT == F_MX) {
+      // 1-KB pieces: 64 rows x 16 bytes; A rows then B rows.
+      constexpr int kPieces = (BM + BN) / 64;
+      const int64_t blk0 = (k_begin >> 5) + (int64_t)group * 4 * kScaleTiles;
+      const int64_t nblk = (k_end + 31) >> 5;
+      static_assert(kPieces <= NWAVES, "one scale piece per wave");
+      if (wave < kPieces) {
+        const int piece = wave;
+        const bool is_a = piece < BM / 64;
+        const int r = (is_a ? piece : piece - BM / 64) * 64 + lane;
+        const int64_t row = (is_a ? m0 : n0) + r;
+        const bool ok = row < (is_a ? row_end : b_rows) && blk0 < nblk;
+        const uint8_t* base = is_a ? p.a_mx : p.b_mx;
+        const int64_t ld = is_a ? p.a_mx_ld : p.b_mx_ld;
+        const int64_t rows_total = is_a ? (SCHED == S_GROUP_M ? p.T : p.M) : b_rows;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + blk0, rows_total * ld - blk0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(sc_lds[buf] + piece * 1024), 16,
+                                                 ok ? (int)(row * ld) : (int)kOOB, 0, 0, 0);
+      }
+    }
+  };
+  auto load_scales = [&](int64_t k0, uint32_t (&da)[WMF], uint32_t (&db)[WNF]) {
+    if constexpr (kMX) {
+      const int sh = 8 * (lane >> 5);
+      if constexpr (mx_lds) {
+        const int t = (int)((k0 - k_begin) / KT_ELEMS);
+        const uint8_t* sl = sc_lds[(t / kScaleTiles) & 1] + (t % kScaleTiles) * 4;
+#pragma unroll
+        for (int i = 0; i < WMF; ++i)
+          da[i] = *reinterpret_cast<const uint32_t*>(sl + (wm * WM + i * 32 + (lane & 31)) * 16) >> sh;
+#pragma unroll
+        for (int j = 0; j < WNF; ++j)
+          db[j] = *reinterpret_cast<const uint32_t*>(sl + (BM + wn * WN + j * 32 + (lane & 31)) * 16) >> sh;
+        return;
+      }
       const int64_t blk0 = k0 >> 5;
       const int64_t nblk = (k_end + 31) >> 5;
-      const int sh = 8 * (lane >> 5);
 #pragma unroll
       for (int i = 0; i < WMF; ++i) {
         const int64_t row = m0 + wm * WM + i * 32 + (lane & 31);
         uint32_t v = 0x7F7F7F7Fu;
         if (row < row_end) {
           const uint8_t* s = p.a_mx + row * p.a_mx_ld + blk0;
-          if (p.mx_aligned) {
-            v = *reinterpret_cast<const uint32_t*>(s);
-          } else {
-            v = 0;
+          v = 0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v |= (blk0 + e < nblk ? (uint32_t)s[e] : 127u) << (8 * e);
-          }
+          for (int e = 0; e < 4; ++e) v |= (blk0 + e < nblk ? (uint32_t)s[e] : 127u) << (8 * e);
         }
         da[i] = v >> sh;
       }
@@ -304,13 +343,9 @@ void gemm_kernel(const GemmParams p) {
         uint32_t v = 0x7F7F7F7Fu;
         if (row < b_rows) {
           const uint8_t* s = p.b_mx + row * p.b_mx_ld + blk0;
-          if (p.mx_aligned) {
-            v = *reinterpret_cast<const uint32_t*>(s);
-          } else {
-            v = 0;
+          v = 0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v |= (blk0 + e < nblk ? (uint32_t)s[e] : 127u) << (8 * e);
-          }
+          for (int e = 0; e < 4; ++e) v |= (blk0 + e < nblk ? (uint32_t)s[e] : 127u) << (8 * e);
         }
         db[j] = v >> sh;
       }
@@ -322,99 +357,73 @@ void gemm_kernel(const GemmParams p) {
   const int lrow = lane & 31;
   const int lhalf = lane >> 5;
 
-  // Multiply one LDS stage into the accumulators. Fragments of k-step ks+1 are
-  // read while the MFMAs of step ks run.
-  auto compute = [&](const uint8_t* buf) {
+  // Fragments: 8 bf16 (32x32x16) or 32 fp8 (32x32x64) contraction values per lane.
+  using Frag = typename std::conditional<FMT == F_BF16, bf16x8, i32x8>::type;
+  constexpr int KS = FMT == F_BF16 ? 4 : 2;                         // MFMA k-steps per tile
+  constexpr int kReads = FMT == F_BF16 ? (AK ? WMF : 2 * WMF) + (BK ? WNF : 2 * WNF) : 2 * (WMF + WNF);
+  constexpr int kMfma = WMF * WNF;
+
+  auto rd = [&](const uint8_t* buf, int ks, Frag (&fa)[WMF], Frag (&fb)[WNF]) {
     const uint8_t* a_lds = buf;
     const uint8_t* b_lds = buf + A_BYTES;
     if constexpr (FMT == F_BF16) {
-      bf16x8 af[2][WMF], bfr[2][WNF];
-      auto rd = [&](int ks, bf16x8 (&fa)[WMF], bf16x8 (&fb)[WNF]) {
 #pragma unroll
-        for (int i = 0; i < WMF; ++i)
-          fa[i] = AK ? frag_k_bf16(a_lds, wm * WM + i * 32 + lrow, ks * 2 + lhalf)
-                     : frag_t_bf16<BM>(a_lds, wm * WM + i * 32, ks, lane);
+      for (int i = 0; i < WMF; ++i)
+        fa[i] = AK ? frag_k_bf16(a_lds, wm * WM + i * 32 + lrow, ks * 2 + lhalf)
+                   : frag_t_bf16<BM>(a_lds, wm * WM + i * 32, ks, lane);
 #pragma unroll
-        for (int j = 0; j < WNF; ++j)
-          fb[j] = BK ? frag_k_bf16(b_lds, wn * WN + j * 32 + lrow, ks * 2 + lhalf)
-                     : frag_t_bf16<BN>(b_lds, wn * WN + j * 32, ks, lane);
-      };
-      constexpr int kReads = (AK ? WMF : 2 * WMF) + (BK ? WNF : 2 * WNF);
-      constexpr int kMfma = WMF * WNF;
-      rd(0, af[0], bfr[0]);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if (ks < 3) rd(ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
-#pragma unroll
-        for (int i = 0; i < WMF; ++i)
-#pragma unroll
-          for (int j = 0; j < WNF; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks & 1][j], af[ks & 1][i], acc[i][j], 0, 0, 0);
-      }
-      // Issue order: the first fragments, then per k-step one MFMA after each LDS read of
-      // the next step's fragments, then the remaining MFMAs of the step.
-      __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if (ks < 3) {
-#pragma unroll
-          for (int t = 0; t < (kReads < kMfma ? kReads : kMfma); ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-          if (kReads < kMfma) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
-        } else {
-          __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
-        }
-      }
+      for (int j = 0; j < WNF; ++j)
+        fb[j] = BK ? frag_k_bf16(b_lds, wn * WN + j * 32 + lrow, ks * 2 + lhalf)
+                   : frag_t_bf16<BN>(b_lds, wn * WN + j * 32, ks, lane);
     } else {
       // f8f6f4 32x32x64 lane layout: bytes 0-15 hold k = 16*half .. +15 and
       // bytes 16-31 hold k = 32 + 16*half .. +15 of the 64-wide step.
-      i32x8 af[2][WMF], bfr[2][WNF];
-      auto rd8 = [&](const uint8_t* base, int r, int ks) {
+      auto rd8 = [&](const uint8_t* base, int r) {
         const int c0 = ks * 4 + lhalf, c1 = c0 + 2;
         const uint8_t* row = base + r * kRowBytes;
         const int4 lo = *reinterpret_cast<const int4*>(row + ((c0 ^ swz(r)) << 4));
         const int4 hi = *reinterpret_cast<const int4*>(row + ((c1 ^ swz(r)) << 4));
         return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       };
-      auto rd = [&](int ks, i32x8 (&fa)[WMF], i32x8 (&fb)[WNF]) {
 #pragma unroll
-        for (int i = 0; i < WMF; ++i) fa[i] = rd8(a_lds, wm * WM + i * 32 + lrow, ks);
+      for (int i = 0; i < WMF; ++i) fa[i] = rd8(a_lds, wm * WM + i * 32 + lrow);
 #pragma unroll
-        for (int j = 0; j < WNF; ++j) fb[j] = rd8(b_lds, wn * WN + j * 32 + lrow, ks);
-      };
-      constexpr int kReads = 2 * (WMF + WNF);
-      constexpr int kMfma = WMF * WNF;
-      rd(0, af[0], bfr[0]);
+      for (int j = 0; j < WNF; ++j) fb[j] = rd8(b_lds, wn * WN + j * 32 + lrow);
+    }
+  };
+
+  auto mma = [&](int ks, const Frag (&fa)[WMF], const Frag (&fb)[WNF]) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (ks < 1) rd(ks + 1, af[1], bfr[1]);
+    for (int i = 0; i < WMF; ++i)
 #pragma unroll
-        for (int i = 0; i < WMF; ++i)
-#pragma unroll
-          for (int j = 0; j < WNF; ++j) {
-            if constexpr (FMT == F_MX) {
-              if (ks == 0)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    bfr[0][j], af[0][i], acc[i][j], 0, 0, 0, (int)sb[j], 0, (int)sa[i]);
-              else
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    bfr[1][j], af[1][i], acc[i][j], 0, 0, 2, (int)sb[j], 2, (int)sa[i]);
-            } else {
-              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  bfr[ks][j], af[ks][i], acc[i][j], 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
-            }
-          }
+      for (int j = 0; j < WNF; ++j) {
+        if constexpr (FMT == F_BF16) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+        } else if constexpr (kMX) {
+          // byte 2*ks of the pre-shifted scale registers is this lane's 32-block
+          if (ks == 0)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0,
+                                                                        (int)sb[j], 0, (int)sa[i]);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 2,
+                                                                        (int)sb[j], 2, (int)sa[i]);
+        } else {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0, 0x7F7F7F7F,
+                                                                      0, 0x7F7F7F7F);
+        }
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+  };
+
+  // Issue order inside a scheduling region: one MFMA after each LDS fragment read.
+  auto interleave = [&](int steps) {
+    for (int s = 0; s < steps; ++s) {
 #pragma unroll
       for (int t = 0; t < (kReads < kMfma ? kReads : kMfma); ++t) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       if (kReads < kMfma) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
+      if (kReads > kMfma) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kMfma, 0);
     }
   };
 
@@ -425,26 +434,52 @@ void gemm_kernel(const GemmParams p) {
     __syncthreads();
   };
 
+  // Software pipeline: fragments of k-step s+1 are read while the MFMAs of step s
+  // run; the barrier sits before the tile's last k-step, whose MFMAs cover the
+  // reads of the next tile's first fragments (the fragments of that last step
+  // are already in registers, so the other stage may be refilled).
+  Frag fa[2][WMF], fb[2][WNF];
   if (KT > 0) {
     issue_tile(lds0, k_begin);
-    load_scales(k_begin, sa, sb);
+    if constexpr (mx_lds) issue_scales(0, 0);
     stage_done();
+    load_scales(k_begin, sa, sb);
+    rd(lds0, 0, fa[0], fb[0]);
   }
   for (int kt = 0; kt < KT; ++kt) {
-    uint8_t* cur = (kt & 1) ? lds1 : lds0;
+    const uint8_t* cur = (kt & 1) ? lds1 : lds0;
     uint8_t* nxt = (kt & 1) ? lds0 : lds1;
-    const bool more = kt + 1 < KT;
-    if (more) {
+    if (kt + 1 < KT) {
       issue_tile(nxt, k_begin + (int64_t)(kt + 1) * KT_ELEMS);
-      load_scales(k_begin + (int64_t)(kt + 1) * KT_ELEMS, san, sbn);
+      // Scales of the next group of k-tiles: the buffer they fill was last read before
+      // the previous barrier; they land (vmcnt 0) at least one barrier before use.
+      if constexpr (mx_lds) {
+        if (kt % kScaleTiles == 0 && (kt / kScaleTiles + 1) * kScaleTiles < KT)
+          issue_scales(kt / kScaleTiles + 1, (kt / kScaleTiles + 1) & 1);
+      } else if constexpr (kMX) {
+        load_scales(k_begin + (int64_t)(kt + 1) * KT_ELEMS, san, sbn);
+      }
     }
-    compute(cur);
+#pragma unroll
+    for (int ks = 0; ks < KS - 1; ++ks) {
+      rd(cur, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      mma(ks, fa[ks & 1], fb[ks & 1]);
+    }
+    interleave(KS - 1);
     stage_done();
-    if constexpr (FMT == F_MX) {
+    // On the last tile this reads a stale stage: in bounds, never used.
+    rd(nxt, 0, fa[0], fb[0]);
+    mma(KS - 1, fa[1], fb[1]);
+    interleave(1);
+    if constexpr (kMX) {
+      if constexpr (mx_lds) {
+        load_scales(k_begin + (int64_t)(kt + 1) * KT_ELEMS, sa, sb);
+      } else {
 #pragma unroll
-      for (int i = 0; i < WMF; ++i) sa[i] = san[i];
+        for (int i = 0; i < WMF; ++i) sa[i] = san[i];
 #pragma unroll
-      for (int j = 0; j < WNF; ++j) sb[j] = sbn[j];
+        for (int j = 0; j < WNF; ++j) sb[j] = sbn[j];
+      }
     }
   }
 
@@ -638,7 +673,8 @@ hipError_t launch_gemm(const GemmParams& p, int fmt, bool a_kmaj, bool b_kmaj, h
     return launch_tile<F_BF16, false, true, E_STORE, S_DENSE>(p, s);
   }
   if (fmt == F_E4M3) return launch_tile<F_E4M3, true, true, E_STORE, S_DENSE>(p, s);
-  return launch_tile<F_MX, true, true, E_STORE, S_DENSE>(p, s);
+  if (p.mx_aligned) return launch_tile<F_MX, true, true, E_STORE, S_DENSE>(p, s);
+  return launch_tile<F_MXU, true, true, E_STORE, S_DENSE>(p, s);
 }
 
 hipError_t launch_grouped_fwd(const GemmParams& p, int epilogue, hipStream_t s) {
