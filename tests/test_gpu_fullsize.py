@@ -1,0 +1,145 @@
+"""Full-size parity: each workload at its own size, run through the same calls as bench.py, checked
+on sampled outputs that the oracle computes row by row / column by column.
+
+Per-tensor FP8 scales come from the oracle's amax over the whole tensor; MXFP8 blocks are local to
+a row (rowwise) or a column (columnwise), so sampled rows and columns quantize on their own."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import grouped, linear, offsets, quant
+from oracle.codecs import bf16_to_f64
+
+from .gpu_paths import run_dense, run_grouped_mlp
+from .helpers import TAU_BF16, TAU_FP8, assert_close, host_f64, host_u8
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def _pick(n, k, rng):
+    idx = set(rng.choice(n, size=min(k, n), replace=False).tolist()) | {0, n - 1}
+    return np.array(sorted(idx))
+
+
+def _fp8_rows(bits, rows, scale):
+    """Oracle E4M3 codes of the given rows with the whole tensor's scale, and their values."""
+    q = quant.fp8_quantize_with_scale(bits[rows], scale)
+    return q, quant.fp8_dequantize(q, quant.fp8_scale_inv(scale))
+
+
+@pytest.mark.parametrize("name", ["bf16_fwdbwd_4096", "fp8_tensor_fwdbwd_8192x14336x4096",
+                                  "mxfp8_fwdbwd_16384x8192x8192"])
+def test_dense_workload_full_size_sampled(name):
+    w = synth.WORKLOADS[name]
+    print(f"case full-size {name}", flush=True)
+    d = synth.workload_inputs(name, seed=0)
+    fmt, alpha = w["fmt"], w["alpha"]
+    got = run_dense(fmt, d, alpha)
+    M, N, K = w["M"], w["N"], w["K"]
+    rng = np.random.default_rng(123)
+    R, C = _pick(M, 24, rng), _pick(N, 48, rng)          # sampled rows of x/dy, rows of W (= out columns)
+    Ck = _pick(K, 48, rng)                               # sampled contraction columns (dgrad/wgrad columns)
+    tau = TAU_BF16 if fmt == "bf16" else TAU_FP8
+    x, W, dy = d["x"], d["w"], d["dy"]
+    xT, WT, dyT = (np.ascontiguousarray(a.T) for a in (x, W, dy))
+
+    if fmt == "bf16":
+        xr, Wc, dyr = bf16_to_f64(x[R]), bf16_to_f64(W[C]), bf16_to_f64(dy[R])
+        Wk, dyn_, xk = bf16_to_f64(WT[Ck]), bf16_to_f64(dyT[C]), bf16_to_f64(xT[Ck])
+    elif fmt == "fp8":
+        sx, sw, sd = (quant.fp8_scale(quant.amax(a)) for a in (x, W, dy))
+        qg = got["quant"]
+        for src, g, s in ((x, qg["x"], sx), (W, qg["w"], sw), (dy, qg["dy"], sd)):
+            assert float(g["scale"].item()) == float(s)
+            assert float(g["amax"].item()) == float(quant.amax(src))
+        qx, xr = _fp8_rows(x, R, sx)
+        qw, Wc = _fp8_rows(W, C, sw)
+        qd, dyr = _fp8_rows(dy, R, sd)
+        assert np.array_equal(host_u8(qg["x"]["q"][torch.from_numpy(R).cuda()]), qx)
+        assert np.array_equal(host_u8(qg["w"]["q"][torch.from_numpy(C).cuda()]), qw)
+        qwt, Wk = _fp8_rows(WT, Ck, sw)                  # rows of W^T = columns of W
+        qdt, dyn_ = _fp8_rows(dyT, C, sd)
+        qxt, xk = _fp8_rows(xT, Ck, sx)
+        assert np.array_equal(host_u8(qg["x"]["q_t"][torch.from_numpy(Ck).cuda()]), qxt)
+        assert np.array_equal(host_u8(qg["dy"]["q_t"][torch.from_numpy(C).cuda()]), qdt)
+    else:
+        qg = got["quant"]
+        qxr, sxr = quant.mxfp8_rowwise(x[R])
+        qwr, swr = quant.mxfp8_rowwise(W[C])
+        qdr, sdr = quant.mxfp8_rowwise(dy[R])
+        rr, cc = torch.from_numpy(R).cuda(), torch.from_numpy(C).cuda()
+        assert np.array_equal(host_u8(qg["x"]["q_row"][rr]), qxr) and np.array_equal(host_u8(qg["x"]["s_row"][rr]), sxr)
+        assert np.array_equal(host_u8(qg["w"]["q_row"][cc]), qwr) and np.array_equal(host_u8(qg["w"]["s_row"][cc]), swr)
+        xr, Wc, dyr = quant.mx_dequantize(qxr, sxr), quant.mx_dequantize(qwr, swr), quant.mx_dequantize(qdr, sdr)
+        # columnwise copies: blocks run down a column, so a column quantizes on its own
+        qwc, swc = quant.mxfp8_rowwise(WT[Ck])
+        qdc, sdc = quant.mxfp8_rowwise(dyT[C])
+        qxc, sxc = quant.mxfp8_rowwise(xT[Ck])
+        kk = torch.from_numpy(Ck).cuda()
+        assert np.array_equal(host_u8(qg["x"]["q_colT"][kk]), qxc) and np.array_equal(host_u8(qg["x"]["s_colT"][kk]), sxc)
+        assert np.array_equal(host_u8(qg["dy"]["q_colT"][cc]), qdc)
+        Wk, dyn_, xk = quant.mx_dequantize(qwc, swc), quant.mx_dequantize(qdc, sdc), quant.mx_dequantize(qxc, sxc)
+
+    # forward: sampled rows x sampled output columns
+    ref_f = linear.linear_scale_add_fwd(xr, Wc, bf16_to_f64(d["residual"][np.ix_(R, C)]), alpha)
+    assert_close(host_f64(got["fwd"][torch.from_numpy(R).cuda()][:, torch.from_numpy(C).cuda()]), ref_f, tau,
+                 what=f"{name} fwd")
+    # dgrad[R, Ck] = alpha * dy[R, :] @ W[:, Ck]  (W columns Ck as rows of W^T)
+    ref_d = linear.linear_scale_dgrad(dyr, Wk.T, alpha)
+    assert_close(host_f64(got["dgrad"][torch.from_numpy(R).cuda()][:, torch.from_numpy(Ck).cuda()]), ref_d, tau,
+                 what=f"{name} dgrad")
+    # wgrad[C, Ck] = alpha * dy[:, C]^T @ x[:, Ck]
+    ref_w = linear.linear_scale_wgrad(dyn_.T, xk.T, alpha)
+    assert_close(host_f64(got["wgrad"][torch.from_numpy(C).cuda()][:, torch.from_numpy(Ck).cuda()]), ref_w, tau,
+                 what=f"{name} wgrad")
+
+
+def test_grouped_workload_full_size_sampled():
+    name = "grouped_swiglu_mlp_T65536_G8"
+    w = synth.WORKLOADS[name]
+    print(f"case full-size {name}", flush=True)
+    inp = synth.workload_inputs(name, seed=0)
+    got = run_grouped_mlp(inp)
+    assert int(got["err"].item()) == 0
+    base = offsets.base_offsets(inp["splits"])
+    assert np.array_equal(got["offsets"][0].cpu().numpy(), base)
+    T, F, G = w["T"], w["ffn"], w["G"]
+    rng = np.random.default_rng(7)
+    x = inp["x"]
+    W1, W2 = bf16_to_f64(inp["w1"]), bf16_to_f64(inp["w2"])
+    p = inp["p"].astype(np.float64)
+    dout = inp["dout"]
+    cols = _pick(F, 6, rng)
+    for g in range(G):
+        lo, hi = int(base[g]), int(base[g + 1])
+        if hi == lo:
+            continue
+        toks = np.array(sorted({lo, hi - 1} | set(rng.integers(lo, hi, size=min(6, hi - lo)).tolist())))
+        one = np.array([0, len(toks)])
+        xs = bf16_to_f64(x[toks])
+        f = grouped.grouped_mlp_fwd(xs, W1[g:g + 1], W2[g:g + 1], p[toks], one)
+        b = grouped.grouped_mlp_bwd(bf16_to_f64(dout[toks]), xs, W1[g:g + 1], W2[g:g + 1], p[toks], one,
+                                    h=f["h"], y=f["y"])
+        tt = torch.from_numpy(toks).cuda()
+        kw = dict(rel_tight=2.0 ** -7, abs_tight=5e-2)
+        assert_close(host_f64(got["out"][tt]), f["out"], TAU_BF16, what=f"out g{g}", **kw)
+        assert_close(host_f64(got["h"][tt]), f["h"], TAU_BF16, what=f"h g{g}", **kw)
+        assert_close(host_f64(got["dh"][tt]), b["dh"], TAU_BF16, what=f"dh g{g}", **kw)
+        assert_close(host_f64(got["dp"][tt]), b["dp"], TAU_BF16, what=f"dp g{g}", **kw)
+        assert_close(host_f64(got["dx"][tt]), b["dx"], TAU_BF16, what=f"dx g{g}", **kw)
+        # weight gradients at sampled columns: every token of the group, column-local quantities
+        xg = bf16_to_f64(x[lo:hi])
+        hk = xg @ W1[g][np.concatenate([cols, F + cols])].T          # h[:, k] and h[:, F+k]
+        yk = grouped.scaled_swiglu_fwd(hk, p[lo:hi])                  # y[:, cols]
+        dg = bf16_to_f64(dout[lo:hi])
+        ref_dw2 = dg.T @ yk                                           # dW2_g[:, cols]
+        assert_close(host_f64(got["dw2"][g][:, torch.from_numpy(cols).cuda()]), ref_dw2, TAU_BF16,
+                     what=f"dw2 g{g}", **kw)
+        gk = dg @ W2[g][:, cols]                                      # g[:, cols]
+        dhk, _ = grouped.scaled_swiglu_bwd(gk, hk, p[lo:hi])          # dh[:, cols] and dh[:, F+cols]
+        rows1 = np.concatenate([cols, F + cols])
+        ref_dw1 = dhk.T @ xg                                          # dW1_g[rows1, :]
+        assert_close(host_f64(got["dw1"][g][torch.from_numpy(rows1).cuda()]), ref_dw1, TAU_BF16,
+                     what=f"dw1 g{g}", **kw)
