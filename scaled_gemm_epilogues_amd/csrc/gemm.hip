@@ -293,9 +293,10 @@ void gemm_kernel(const GemmParams p) {
       constexpr int kPieces = (BM + BN) / 64;
       const int64_t blk0 = (k_begin >> 5) + (int64_t)group * 4 * kScaleTiles;
       const int64_t nblk = (k_end + 31) >> 5;
-      static_assert(kPieces <= NWAVES, "one scale piece per wave");
-      if (wave < kPieces) {
-        const int piece = wave;
+#pragma unroll
+      for (int it = 0; it < (kPieces + NWAVES - 1) / NWAVES; ++it) {
+        const int piece = it * NWAVES + wave;
+        if (piece >= kPieces) break;
         const bool is_a = piece < BM / 64;
         const int r = (is_a ? piece : piece - BM / 64) * 64 + lane;
         const int64_t row = (is_a ? m0 : n0) + r;
