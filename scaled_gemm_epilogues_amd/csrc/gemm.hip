@@ -40,7 +40,9 @@ enum { S_DENSE = 0, S_GROUP_M = 1, S_GROUP_K = 2 };
 
 constexpr int kRowBytes = 128;   // contraction bytes per LDS row and per k-tile
 
-// Macro tile: kWavesM x kWavesN waves, each owning kFragsM x kFragsN 32x32 accumulators.
+// Macro tile 256x256. bf16 and E4M3: 2x4 waves (two per SIMD), each owning 4x2 32x32
+// accumulators, so one wave's LDS and barrier waits are covered by the other's MFMAs.
+// MXFP8 (more live registers for the E8M0 scales): 2x2 waves, each 4x4 accumulators.
 #ifndef SGE_WAVES_M
 #define SGE_WAVES_M 2
 #define SGE_WAVES_N 4
@@ -48,6 +50,22 @@ constexpr int kRowBytes = 128;   // contraction bytes per LDS row and per k-tile
 #define SGE_FRAGS_N 2
 #endif
 constexpr int kWavesM = SGE_WAVES_M, kWavesN = SGE_WAVES_N, kFragsM = SGE_FRAGS_M, kFragsN = SGE_FRAGS_N;
+#ifndef SGE_XCD_GROUP_M
+#define SGE_XCD_GROUP_M 4
+#endif
+
+template <int FMT>
+struct TileShape {
+  static constexpr int WGM = kWavesM, WGN = kWavesN, WMF = kFragsM, WNF = kFragsN;
+};
+template <>
+struct TileShape<2> {
+  static constexpr int WGM = 2, WGN = 2, WMF = 4, WNF = 4;
+};
+template <>
+struct TileShape<3> {
+  static constexpr int WGM = 2, WGN = 2, WMF = 4, WNF = 4;
+};
 
 __device__ __forceinline__ float fast_sigmoid(float a) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-a));
@@ -198,7 +216,7 @@ void gemm_kernel(const GemmParams p) {
     const int nblk = gridDim.x;
     if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);   // tiles of one XCD adjacent
     const int MT = p.mt_count, NT = p.nt_count;
-    const int GM = 8;
+    const int GM = SGE_XCD_GROUP_M;
     const int group = bid / (GM * NT);
     const int first_m = group * GM;
     const int gsz = min(MT - first_m, GM);
@@ -497,47 +515,67 @@ void gemm_kernel(const GemmParams p) {
   auto row_ok = [&](int i) { return m0 + row_in_tile(i) < row_end; };
 
   if constexpr (EPI == E_STORE) {
+    // Two passes over half of each wave's rows: alpha*acc (fp32) goes to LDS in row-major
+    // order (16-byte granule g of row r at g ^ (r & 15), conflict-free from the fragment
+    // layout), then every thread takes 8 consecutive columns of a row: one 16-byte residual
+    // load and one 16-byte store, so each wave moves whole 128-byte lines.
+    static_assert(BM == 2 * WM && A_BYTES + B_BYTES == 64 * BN * 4, "epilogue staging assumes 2 wave rows");
+    typedef int v4i __attribute__((__vector_size__(4 * sizeof(int))));
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(cptr + m0 * p.ldc, rows_left * p.ldc * 2);
-    auto off = [&](int i, int j, int q) -> int {
-      const int64_t n = n0 + wn * WN + j * 32 + 8 * q + 4 * lhalf;
-      return (row_ok(i) && n < n_end) ? (int)(((int64_t)row_in_tile(i) * p.ldc + n) * 2) : (int)kOOB;
-    };
-    auto store = [&](int i, int j, int q, float v0, float v1, float v2, float v3) {
-      const v2i w = {(int)pack_bf16x2(v0, v1), (int)pack_bf16x2(v2, v3)};
-      __builtin_amdgcn_raw_buffer_store_b64(w, rc, off(i, j, q), 0, 0);
-    };
-    if (p.accumulate) {
-      v2i res[2][WNF][4];
-      auto load = [&](int i, v2i (&r)[WNF][4]) {
+    constexpr int kChunks = BN / 8;                        // 8-column chunks per row
+    constexpr int kIters = 128 * kChunks / (NWAVES * 64);  // chunks per thread per pass
+    float* stage = reinterpret_cast<float*>(wm ? lds1 : lds0);
+    __syncthreads();                                       // every wave is done with the LDS stages
 #pragma unroll
-        for (int j = 0; j < WNF; ++j)
+    for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) r[j][q] = __builtin_amdgcn_raw_buffer_load_b64(rc, off(i, j, q), 0, 0);
-      };
-      load(0, res[0]);
-#pragma unroll
-      for (int i = 0; i < WMF; ++i) {
-        if (i + 1 < WMF) load(i + 1, res[(i + 1) & 1]);
+      for (int il = 0; il < WMF / 2; ++il) {
+        const int i = pass * (WMF / 2) + il;
+        const int r = il * 32 + lrow;                      // row within this wave row's half
 #pragma unroll
         for (int j = 0; j < WNF; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const v2i r = res[i & 1][j][q];
-            store(i, j, q, bf16_lo((uint32_t)r[0]) + alpha * acc[i][j][4 * q + 0],
-                  bf16_hi((uint32_t)r[0]) + alpha * acc[i][j][4 * q + 1],
-                  bf16_lo((uint32_t)r[1]) + alpha * acc[i][j][4 * q + 2],
-                  bf16_hi((uint32_t)r[1]) + alpha * acc[i][j][4 * q + 3]);
+            const int g = (wn * WN + j * 32 + 8 * q + 4 * lhalf) >> 2;
+            const float4 v = make_float4(alpha * acc[i][j][4 * q + 0], alpha * acc[i][j][4 * q + 1],
+                                         alpha * acc[i][j][4 * q + 2], alpha * acc[i][j][4 * q + 3]);
+            *reinterpret_cast<float4*>(stage + r * BN + ((g ^ (r & 15)) << 2)) = v;
           }
       }
-    } else {
+      __syncthreads();
+      v4i res[kIters];
+      int offs[kIters];
 #pragma unroll
-      for (int i = 0; i < WMF; ++i)
+      for (int it = 0; it < kIters; ++it) {
+        const int id = it * NWAVES * 64 + threadIdx.x;
+        const int rp = id / kChunks, c = id % kChunks;     // row of the pass (0..127), chunk
+        const int brow = (rp >> 6) * WM + pass * (WM / 2) + (rp & 63);
+        const int64_t n = n0 + c * 8;
+        offs[it] = (m0 + brow < row_end && n < n_end) ? (int)(((int64_t)brow * p.ldc + n) * 2) : (int)kOOB;
+        if (p.accumulate) res[it] = __builtin_amdgcn_raw_buffer_load_b128(rc, offs[it], 0, 0);
+      }
 #pragma unroll
-        for (int j = 0; j < WNF; ++j)
+      for (int it = 0; it < kIters; ++it) {
+        const int id = it * NWAVES * 64 + threadIdx.x;
+        const int rp = id / kChunks, c = id % kChunks;
+        const float* row = reinterpret_cast<const float*>(rp >= 64 ? lds1 : lds0) + (rp & 63) * BN;
+        const int sw = (rp & 63) & 15;
+        const float4 lo = *reinterpret_cast<const float4*>(row + (((2 * c) ^ sw) << 2));
+        const float4 hi = *reinterpret_cast<const float4*>(row + (((2 * c + 1) ^ sw) << 2));
+        float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        if (p.accumulate) {
+          const v4i r4 = res[it];
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            store(i, j, q, alpha * acc[i][j][4 * q + 0], alpha * acc[i][j][4 * q + 1], alpha * acc[i][j][4 * q + 2],
-                  alpha * acc[i][j][4 * q + 3]);
+          for (int e = 0; e < 4; ++e) {
+            v[2 * e] = bf16_lo((uint32_t)r4[e]) + v[2 * e];
+            v[2 * e + 1] = bf16_hi((uint32_t)r4[e]) + v[2 * e + 1];
+          }
+        }
+        const v4i w = {(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3]), (int)pack_bf16x2(v[4], v[5]),
+                       (int)pack_bf16x2(v[6], v[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(w, rc, offs[it], 0, 0);
+      }
+      if (pass == 0) __syncthreads();                      // stage reused by the second pass
     }
   } else if constexpr (EPI == E_SWIGLU) {
     constexpr int HJ = WNF / 2;
@@ -645,7 +683,8 @@ static hipError_t launch_cfg(GemmParams p, int grid, hipStream_t s) {
 
 template <int FMT, bool AK, bool BK, int EPI, int SCHED>
 static hipError_t launch_tile(GemmParams p, hipStream_t s) {
-  constexpr int WGM = kWavesM, WGN = kWavesN, WMF = kFragsM, WNF = kFragsN;
+  constexpr int WGM = TileShape<FMT>::WGM, WGN = TileShape<FMT>::WGN;
+  constexpr int WMF = TileShape<FMT>::WMF, WNF = TileShape<FMT>::WNF;
   constexpr int BM = WGM * 32 * WMF, BN = WGN * 32 * WNF;
   int grid = 0;
   if constexpr (SCHED == S_DENSE) {
