@@ -82,15 +82,18 @@ hipError_t launch_amax_partial(const uint16_t* src, int64_t n, uint32_t* partial
   return hipGetLastError();
 }
 
-// Tiles of 64 rows x 64 columns; 256 threads, 8 bf16 (16 B) per thread per pass.
-constexpr int kQT = 64;
+// Tiles of 128 rows x 64 columns; 256 threads, 8 bf16 (16 B) per thread per pass. The
+// transposed copy is written through LDS so each column's 128 rows leave as one 128-byte
+// line. Tiles are visited in the reverse order of the amax pass, which left the most
+// recently read part of the tensor in the last-level cache.
+constexpr int kQR = 128, kQC = 64;
 
 __global__ __launch_bounds__(256) void quantize_fp8_kernel(
     const uint16_t* __restrict__ src, int64_t rows, int64_t cols, const uint32_t* __restrict__ partial,
     int nparts, uint8_t* __restrict__ q, uint8_t* __restrict__ q_t, float* amax_out, float* scale_out,
     float* scale_inv_out) {
   __shared__ uint32_t red[4];
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kQT][kQT + 8];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kQC][kQR + 16];   // [column][row]
 
   // Finish the amax: every block reduces the partials itself (no grid barrier).
   uint32_t m = 0;
@@ -109,42 +112,46 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(
     *scale_inv_out = scale_inv;
   }
 
-  const int64_t tr = rows / kQT + (rows % kQT ? 1 : 0);
-  const int64_t tc = cols / kQT + (cols % kQT ? 1 : 0);
+  const int64_t tr = (rows + kQR - 1) / kQR;
+  const int64_t tc = (cols + kQC - 1) / kQC;
+  const int64_t ntiles = tr * tc;
   const int t = threadIdx.x;
   const int cchunk = t & 7;          // 8 columns each
   const int rsub = t >> 3;           // 0..31
-  for (int64_t tile_id = blockIdx.x; tile_id < tr * tc; tile_id += gridDim.x) {
-    const int64_t r0 = (tile_id / tc) * kQT, c0 = (tile_id % tc) * kQT;
+  for (int64_t it = blockIdx.x; it < ntiles; it += gridDim.x) {
+    const int64_t tile_id = ntiles - 1 - it;
+    const int64_t r0 = (tile_id / tc) * kQR, c0 = (tile_id % tc) * kQC;
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
+    for (int pass = 0; pass < kQR / 32; ++pass) {
       const int lr = rsub + 32 * pass;
       const int64_t r = r0 + lr, c = c0 + cchunk * 8;
-      uint2 out = make_uint2(0, 0);
+      uint32_t b[4] = {0, 0, 0, 0};
       if (r < rows && c < cols) {
         const uint4 v = *reinterpret_cast<const uint4*>(src + r * cols + c);
-        const uint32_t b01 = e4m3x2(bf16_lo(v.x) * scale, bf16_hi(v.x) * scale);
-        const uint32_t b23 = e4m3x2(bf16_lo(v.y) * scale, bf16_hi(v.y) * scale);
-        const uint32_t b45 = e4m3x2(bf16_lo(v.z) * scale, bf16_hi(v.z) * scale);
-        const uint32_t b67 = e4m3x2(bf16_lo(v.w) * scale, bf16_hi(v.w) * scale);
-        out = make_uint2(b01 | (b23 << 16), b45 | (b67 << 16));
-        if (q) *reinterpret_cast<uint2*>(q + r * cols + c) = out;
+        b[0] = e4m3x2(bf16_lo(v.x) * scale, bf16_hi(v.x) * scale);
+        b[1] = e4m3x2(bf16_lo(v.y) * scale, bf16_hi(v.y) * scale);
+        b[2] = e4m3x2(bf16_lo(v.z) * scale, bf16_hi(v.z) * scale);
+        b[3] = e4m3x2(bf16_lo(v.w) * scale, bf16_hi(v.w) * scale);
+        if (q) *reinterpret_cast<uint2*>(q + r * cols + c) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
       }
-      if (q_t) *reinterpret_cast<uint2*>(&tile[lr][cchunk * 8]) = out;
+      if (q_t) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          tile[cchunk * 8 + 2 * e][lr] = (uint8_t)(b[e] & 0xFF);
+          tile[cchunk * 8 + 2 * e + 1][lr] = (uint8_t)(b[e] >> 8);
+        }
+      }
     }
     if (q_t) {
       __syncthreads();
-      // Thread -> one column, 16 consecutive rows of the transposed output.
-      const int lc = t & 63, rb = t >> 6;
-      const int64_t c = c0 + lc, r = r0 + rb * 16;
+      // Thread -> one column, 32 consecutive rows (2 x 16 bytes) of the transposed output.
+      const int lc = t >> 2, seg = (t & 3) * 32;
+      const int64_t c = c0 + lc, r = r0 + seg;
       if (c < cols && r < rows) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w[e] = (uint32_t)tile[rb * 16 + 4 * e + 0][lc] | ((uint32_t)tile[rb * 16 + 4 * e + 1][lc] << 8) |
-                 ((uint32_t)tile[rb * 16 + 4 * e + 2][lc] << 16) | ((uint32_t)tile[rb * 16 + 4 * e + 3][lc] << 24);
-        }
-        *reinterpret_cast<uint4*>(q_t + c * rows + r) = make_uint4(w[0], w[1], w[2], w[3]);
+        const uint4 lo = *reinterpret_cast<const uint4*>(&tile[lc][seg]);
+        const uint4 hi = *reinterpret_cast<const uint4*>(&tile[lc][seg + 16]);
+        *reinterpret_cast<uint4*>(q_t + c * rows + r) = lo;
+        if (r + 16 < rows) *reinterpret_cast<uint4*>(q_t + c * rows + r + 16) = hi;
       }
       __syncthreads();
     }
@@ -154,7 +161,7 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(
 hipError_t launch_quantize_fp8(const uint16_t* src, int64_t rows, int64_t cols, const uint32_t* partial,
                                int nparts, uint8_t* q, uint8_t* q_t, float* amax, float* scale,
                                float* scale_inv, hipStream_t s) {
-  const int64_t tiles = ((rows + kQT - 1) / kQT) * ((cols + kQT - 1) / kQT);
+  const int64_t tiles = ((rows + kQR - 1) / kQR) * ((cols + kQC - 1) / kQC);
   const int grid = (int)(tiles < 2048 ? (tiles < 1 ? 1 : tiles) : 2048);
   hipLaunchKernelGGL(quantize_fp8_kernel, dim3(grid), dim3(256), 0, s, src, rows, cols, partial, nparts, q,
                      q_t, amax, scale, scale_inv);
@@ -183,88 +190,107 @@ __device__ __forceinline__ float pow2_neg(int x) {
   return __builtin_bit_cast(float, (uint32_t)(127 - x) << 23);
 }
 
-constexpr int kMR = 32, kMC = 64;   // MX tile: 32 rows x 64 columns
+// MX tile: 128 rows x 64 columns (16 KB of bf16 read once). 256 threads; thread t owns
+// columns 8*(t%8)..+7 of rows t/8 + 32k, k = 0..3. Rowwise blocks are 4 consecutive threads
+// of a row; columnwise blocks are the 32 rows of one k, reduced across lanes and waves. The
+// columnwise copy goes through LDS so each column's 128 rows leave as one 128-byte line.
+constexpr int kMR = 128, kMC = 64;
 
 __global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const uint16_t* __restrict__ src, int64_t rows,
                                                             int64_t cols, uint8_t* __restrict__ q_row,
                                                             uint8_t* __restrict__ s_row,
                                                             uint8_t* __restrict__ q_colT,
                                                             uint8_t* __restrict__ s_colT) {
-  __shared__ uint32_t colmax[4][kMC];
-  __shared__ __attribute__((aligned(16))) uint8_t qt[kMC][kMR + 8];
-  const int64_t tc = cols / kMC + (cols % kMC ? 1 : 0);
+  __shared__ __attribute__((aligned(16))) uint16_t xt[kMC][kMR + 8];    // [column][row] bf16 bits
+  const int64_t tc = (cols + kMC - 1) / kMC;
   const int64_t r0 = (int64_t)(blockIdx.x / tc) * kMR;
   const int64_t c0 = (int64_t)(blockIdx.x % tc) * kMC;
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
   const int lr = t >> 3;                 // 0..31
   const int cc = t & 7;                  // column chunk of 8
-  const int64_t r = r0 + lr, c = c0 + cc * 8;
-  const bool ok = r < rows && c < cols;  // rows, cols are multiples of 32
-  uint4 v = make_uint4(0, 0, 0, 0);
-  if (ok) v = *reinterpret_cast<const uint4*>(src + r * cols + c);
-  float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-  uint32_t ab[8] = {v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu, v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu,
-                    v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu, v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu};
+  const int64_t c = c0 + cc * 8;
+  float x[4][8];
+  uint32_t ab[4][8];
+  uint32_t x_sign[4];    // bit e: sign of element e
+  bool ok[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t r = r0 + lr + 32 * k;
+    ok[k] = r < rows && c < cols;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (ok[k]) v = *reinterpret_cast<const uint4*>(src + r * cols + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    x_sign[k] = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x_sign[k] |= ((w[e] >> 15) & 1u) << (2 * e) | ((w[e] >> 31) & 1u) << (2 * e + 1);
+      x[k][2 * e] = bf16_lo(w[e]);
+      x[k][2 * e + 1] = bf16_hi(w[e]);
+      ab[k][2 * e] = w[e] & 0x7FFFu;
+      ab[k][2 * e + 1] = (w[e] >> 16) & 0x7FFFu;
+    }
+  }
 
   if (q_row) {
-    // Rowwise: a 32-column block is 4 consecutive threads of one row.
-    uint32_t m = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) m = ab[e] > m ? ab[e] : m;
-    uint32_t o = __shfl_xor(m, 1, 64);
-    m = o > m ? o : m;
-    o = __shfl_xor(m, 2, 64);
-    m = o > m ? o : m;
-    const int X = mx_exponent(m);
-    const float sc = pow2_neg(X);
-    if (ok) {
-      const uint32_t b01 = e4m3x2(x[0] * sc, x[1] * sc), b23 = e4m3x2(x[2] * sc, x[3] * sc);
-      const uint32_t b45 = e4m3x2(x[4] * sc, x[5] * sc), b67 = e4m3x2(x[6] * sc, x[7] * sc);
-      *reinterpret_cast<uint2*>(q_row + r * cols + c) = make_uint2(b01 | (b23 << 16), b45 | (b67 << 16));
-      if ((cc & 3) == 0) s_row[r * (cols / 32) + (c >> 5)] = (uint8_t)(X + 127);
+    for (int k = 0; k < 4; ++k) {
+      // Rowwise: a 32-column block is 4 consecutive threads of one row.
+      uint32_t m = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = ab[k][e] > m ? ab[k][e] : m;
+      uint32_t o = __shfl_xor(m, 1, 64);
+      m = o > m ? o : m;
+      o = __shfl_xor(m, 2, 64);
+      m = o > m ? o : m;
+      const int X = mx_exponent(m);
+      const float sc = pow2_neg(X);
+      if (ok[k]) {
+        const int64_t r = r0 + lr + 32 * k;
+        const uint32_t b01 = e4m3x2(x[k][0] * sc, x[k][1] * sc), b23 = e4m3x2(x[k][2] * sc, x[k][3] * sc);
+        const uint32_t b45 = e4m3x2(x[k][4] * sc, x[k][5] * sc), b67 = e4m3x2(x[k][6] * sc, x[k][7] * sc);
+        *reinterpret_cast<uint2*>(q_row + r * cols + c) = make_uint2(b01 | (b23 << 16), b45 | (b67 << 16));
+        if ((cc & 3) == 0) s_row[r * (cols / 32) + (c >> 5)] = (uint8_t)(X + 127);
+      }
     }
   }
 
   if (q_colT) {
-    // Columnwise: a block is one column over the tile's 32 rows.
-    uint32_t m[8];
+    // Columnwise: the tile goes to LDS transposed ([column][row] bf16), then thread t owns
+    // the block of rows 32k..32k+31 (k = t % 4) of column t / 4: local amax, 32 codes,
+    // written as 32 contiguous bytes (each column's 128 rows leave as one line).
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint32_t a = ab[e];
+    for (int k = 0; k < 4; ++k)
 #pragma unroll
-      for (int o = 8; o <= 32; o <<= 1) {
-        const uint32_t b = __shfl_xor(a, o, 64);
-        a = b > a ? b : a;
-      }
-      m[e] = a;
-    }
-    if (lane < 8) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) colmax[wave][lane * 8 + e] = m[e];
-    }
+      for (int e = 0; e < 8; ++e) xt[cc * 8 + e][lr + 32 * k] = (uint16_t)(ab[k][e] | (x_sign[k] >> e & 1) << 15);
     __syncthreads();
-    uint8_t qb[8];
+    const int col = t >> 2, k = t & 3;
+    const uint4* seg = reinterpret_cast<const uint4*>(&xt[col][32 * k]);
+    uint32_t w[16];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int col = cc * 8 + e;
-      uint32_t a = colmax[0][col];
-      a = colmax[1][col] > a ? colmax[1][col] : a;
-      a = colmax[2][col] > a ? colmax[2][col] : a;
-      a = colmax[3][col] > a ? colmax[3][col] : a;
-      const int X = mx_exponent(a);
-      qb[e] = (uint8_t)(e4m3x2(x[e] * pow2_neg(X), 0.0f) & 0xFF);
-      if (lr == 0 && c0 + col < cols) s_colT[(c0 + col) * (rows / 32) + (r0 >> 5)] = (uint8_t)(X + 127);
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = seg[i];
+      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
     }
+    uint32_t m = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qt[cc * 8 + e][lr] = qb[e];
-    __syncthreads();
-    // Thread -> one column, 8 consecutive rows of the transposed output.
-    const int col = t >> 2, rs = (t & 3) * 8;
-    if (c0 + col < cols && r0 + rs < rows) {
-      const uint2 w = *reinterpret_cast<const uint2*>(&qt[col][rs]);
-      *reinterpret_cast<uint2*>(q_colT + (c0 + col) * rows + r0 + rs) = w;
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t v = absmax_bits2(w[i]);
+      m = v > m ? v : m;
+    }
+    const int X = mx_exponent(m);
+    const float sc = pow2_neg(X);
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t lo = e4m3x2(bf16_lo(w[2 * i]) * sc, bf16_hi(w[2 * i]) * sc);
+      const uint32_t hi = e4m3x2(bf16_lo(w[2 * i + 1]) * sc, bf16_hi(w[2 * i + 1]) * sc);
+      o[i] = lo | (hi << 16);
+    }
+    if (c0 + col < cols && r0 + 32 * k < rows) {
+      uint8_t* dst = q_colT + (c0 + col) * rows + r0 + 32 * k;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4*>(dst + 16) = make_uint4(o[4], o[5], o[6], o[7]);
+      s_colT[(c0 + col) * (rows / 32) + (r0 >> 5) + k] = (uint8_t)(X + 127);
     }
   }
 }
