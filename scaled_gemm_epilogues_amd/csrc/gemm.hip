@@ -53,6 +53,9 @@ constexpr int kWavesM = SGE_WAVES_M, kWavesN = SGE_WAVES_N, kFragsM = SGE_FRAGS_
 #ifndef SGE_XCD_GROUP_M
 #define SGE_XCD_GROUP_M 4
 #endif
+#ifndef SGE_RD_PER_MFMA
+#define SGE_RD_PER_MFMA 2
+#endif
 
 template <int FMT>
 struct TileShape {
@@ -72,7 +75,6 @@ __device__ __forceinline__ float fast_sigmoid(float a) {
 }
 
 typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past num_records: the load returns zeros
 
@@ -81,6 +83,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   const int n = bytes > 0x7FFFFF00 ? 0x7FFFFF00 : (bytes < 0 ? 0 : (int)bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
+
+// The same resource as four dwords, for the direct-to-LDS copies issued from inline asm.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_rsrc4(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7FFFFF00 ? 0x7FFFFF00 : (bytes < 0 ? 0 : (int)bytes);
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xFFFFu), n, 0x00020000};
+}
+
+// buffer_load_dwordx4 ... lds: lane i's 16 bytes at voff land at LDS byte lds_addr + 16*i
+// (lds_addr wave-uniform). Issued from asm so that the compiler tracks no LDS writes in
+// flight: it would otherwise make reads of the stage being multiplied wait for the copy
+// into the other stage (it cannot always tell the two apart). Completion is the caller's
+// explicit s_waitcnt vmcnt plus the workgroup barrier before a stage is read.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(const i32x4& rsrc, const void* lds, uint32_t voff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
+  // wave-uniform by construction; readfirstlane states it so the descriptor sits in SGPRs
+  const i32x4 r = {__builtin_amdgcn_readfirstlane(rsrc.x), __builtin_amdgcn_readfirstlane(rsrc.y),
+                   __builtin_amdgcn_readfirstlane(rsrc.z), __builtin_amdgcn_readfirstlane(rsrc.w)};
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // Global -> LDS copy of one operand tile with buffer_load ... lds (16 B per lane, the wave's
 // 64 lanes filling 1 KB of LDS contiguously); no staging registers. Lanes fetch permuted
@@ -129,12 +156,11 @@ struct TileCopy {
     const int wave = threadIdx.x >> 6;
     // Resource based at the tile's first contraction element keeps offsets 32-bit.
     const int64_t shift = KMAJ ? k0 * ES : k0 * ld * 2;
-    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(base + shift, bytes_from_base - shift);
+    const i32x4 rsrc = make_rsrc4(base + shift, bytes_from_base - shift);
 #pragma unroll
     for (int i = 0; i < kInstr; ++i) {
       const uint32_t o = (k0 + kk[i] < k_end) ? off[i] : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)(lds + (NWAVES * i + wave) * 1024), 16, (int)o, 0,
-                                               0, 0);
+      lds_copy16(rsrc, lds + (NWAVES * i + wave) * 1024, o);
     }
   }
 };
@@ -322,9 +348,8 @@ void gemm_kernel(const GemmParams p) {
         const uint8_t* base = is_a ? p.a_mx : p.b_mx;
         const int64_t ld = is_a ? p.a_mx_ld : p.b_mx_ld;
         const int64_t rows_total = is_a ? (SCHED == S_GROUP_M ? p.T : p.M) : b_rows;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + blk0, rows_total * ld - blk0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(sc_lds[buf] + piece * 1024), 16,
-                                                 ok ? (int)(row * ld) : (int)kOOB, 0, 0, 0);
+        const i32x4 rs = make_rsrc4(base + blk0, rows_total * ld - blk0);
+        lds_copy16(rs, sc_lds[buf] + piece * 1024, ok ? (uint32_t)(row * ld) : kOOB);
       }
     }
   };
@@ -385,15 +410,19 @@ void gemm_kernel(const GemmParams p) {
   auto rd = [&](const uint8_t* buf, int ks, Frag (&fa)[WMF], Frag (&fb)[WNF]) {
     const uint8_t* a_lds = buf;
     const uint8_t* b_lds = buf + A_BYTES;
+    // Reads go out in the order the MFMAs consume them: A0, B0..B(WNF-1), A1, A2, ...
     if constexpr (FMT == F_BF16) {
-#pragma unroll
-      for (int i = 0; i < WMF; ++i)
+      auto ra = [&](int i) {
         fa[i] = AK ? frag_k_bf16(a_lds, wm * WM + i * 32 + lrow, ks * 2 + lhalf)
                    : frag_t_bf16<BM>(a_lds, wm * WM + i * 32, ks, lane);
+      };
+      ra(0);
 #pragma unroll
       for (int j = 0; j < WNF; ++j)
         fb[j] = BK ? frag_k_bf16(b_lds, wn * WN + j * 32 + lrow, ks * 2 + lhalf)
                    : frag_t_bf16<BN>(b_lds, wn * WN + j * 32, ks, lane);
+#pragma unroll
+      for (int i = 1; i < WMF; ++i) ra(i);
     } else {
       // f8f6f4 32x32x64 lane layout: bytes 0-15 hold k = 16*half .. +15 and
       // bytes 16-31 hold k = 32 + 16*half .. +15 of the 64-wide step.
@@ -404,10 +433,11 @@ void gemm_kernel(const GemmParams p) {
         const int4 hi = *reinterpret_cast<const int4*>(row + ((c1 ^ swz(r)) << 4));
         return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       };
-#pragma unroll
-      for (int i = 0; i < WMF; ++i) fa[i] = rd8(a_lds, wm * WM + i * 32 + lrow);
+      fa[0] = rd8(a_lds, wm * WM + lrow);
 #pragma unroll
       for (int j = 0; j < WNF; ++j) fb[j] = rd8(b_lds, wn * WN + j * 32 + lrow);
+#pragma unroll
+      for (int i = 1; i < WMF; ++i) fa[i] = rd8(a_lds, wm * WM + i * 32 + lrow);
     }
   };
 
@@ -433,16 +463,24 @@ void gemm_kernel(const GemmParams p) {
       }
   };
 
-  // Issue order inside a scheduling region: one MFMA after each LDS fragment read.
+  // Issue order inside a scheduling region: the next step's fragment reads go out early,
+  // kRdPer after each of the first MFMAs, and the remaining MFMAs cover their latency.
+  constexpr int kRdPer0 = SGE_RD_PER_MFMA;
+  constexpr int kRdPer = kRdPer0 * kMfma >= kReads ? kRdPer0 : (kReads + kMfma - 1) / kMfma;
+  constexpr int kRdFull = kReads / kRdPer, kRdRem = kReads % kRdPer;
+  constexpr int kRdUsed = kRdFull + (kRdRem ? 1 : 0);
   auto interleave = [&](int steps) {
     for (int s = 0; s < steps; ++s) {
 #pragma unroll
-      for (int t = 0; t < (kReads < kMfma ? kReads : kMfma); ++t) {
+      for (int t = 0; t < kRdFull; ++t) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, kRdPer, 0);
       }
-      if (kReads < kMfma) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
-      if (kReads > kMfma) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kMfma, 0);
+      if constexpr (kRdRem > 0) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, kRdRem, 0);
+      }
+      if constexpr (kMfma > kRdUsed) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kRdUsed, 0);
     }
   };
 
@@ -470,15 +508,15 @@ void gemm_kernel(const GemmParams p) {
     uint8_t* nxt = (kt & 1) ? lds0 : lds1;
     if (kt + 1 < KT) {
       issue_tile(nxt, k_begin + (int64_t)(kt + 1) * KT_ELEMS);
-      // Scales of the next group of k-tiles: the buffer they fill was last read before
-      // the previous barrier; they land (vmcnt 0) at least one barrier before use.
-      if constexpr (mx_lds) {
-        if (kt % kScaleTiles == 0 && (kt / kScaleTiles + 1) * kScaleTiles < KT)
-          issue_scales(kt / kScaleTiles + 1, (kt / kScaleTiles + 1) & 1);
-      } else if constexpr (kMX) {
-        load_scales(k_begin + (int64_t)(kt + 1) * KT_ELEMS, san, sbn);
-      }
+      if constexpr (kMX && !mx_lds) load_scales(k_begin + (int64_t)(kt + 1) * KT_ELEMS, san, sbn);
     }
+    // Scales of the next group of k-tiles: the buffer they fill was last read before the
+    // previous barrier; they land at least one barrier before use.
+    if constexpr (mx_lds) {
+      if (kt % kScaleTiles == 0 && (kt / kScaleTiles + 1) * kScaleTiles < KT)
+        issue_scales(kt / kScaleTiles + 1, (kt / kScaleTiles + 1) & 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // the copies leave first: their latency spans the tile
 #pragma unroll
     for (int ks = 0; ks < KS - 1; ++ks) {
       rd(cur, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
