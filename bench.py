@@ -46,6 +46,16 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    # measurement helpers (rocprofv3 targets and summaries); none of them prints the bench line
+    ap.add_argument("--profile-launch", metavar="KEY",
+                    help="one warm-up step, then --profile-reps launches of this call only (a --pmc target)")
+    ap.add_argument("--profile-reps", type=int, default=5, help="keep the default for --summarize-traffic")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="one 1 GiB device-to-device copy (calibrates FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--summarize-traffic", metavar="PMC_DIR",
+                    help="write profiles/traffic.json and its summary from rocprofv3 --pmc CSV output")
+    ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "BENCH_JSON", "OUT_MD", "COMMAND"),
+                    help="write a kernel-trace summary from rocprofv3 --kernel-trace --stats CSV output")
     return ap.parse_args()
 
 
@@ -260,8 +270,130 @@ def traffic_for(kernel_key):
     return t.get("bytes_per_launch", {}).get(kernel_key)
 
 
+# ------------------------------------------------------ profile summaries
+COPY_BYTES = 1 << 30
+PROFILE_REPS_KEY = "profile_reps"
+PROFILE_REPS = 5
+
+
+def copy_calibration():
+    import torch
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES}), flush=True)
+
+
+def _pmc_rows(path):
+    """Counter value summed over the rows of each dispatch: {dispatch_id: (kernel, value)}."""
+    import csv
+    out = {}
+    for r in csv.DictReader(open(path)):
+        d = int(r["Dispatch_Id"])
+        k, v = out.get(d, (r["Kernel_Name"], 0.0))
+        out[d] = (k, v + float(r["Counter_Value"]))
+    return out
+
+
+def summarize_traffic(pmc_dir):
+    """profiles/traffic.json: HBM bytes per launch of each profiled kernel.
+
+    Expects rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs named ``copy_<COUNTER>`` (of
+    ``bench.py --copy-calibration``) and ``<workload>__<key>_<COUNTER>`` (of ``bench.py
+    --workload <workload> --profile-launch <key>``). A launch's traffic is the mean over its
+    last profile-reps dispatches (all of one kernel), each counter scaled by the bytes a plain
+    copy moves per unit of that counter."""
+    import glob
+    cal = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        rows = _pmc_rows(os.path.join(pmc_dir, f"copy_{c}_counter_collection.csv"))
+        copies = [v for k, v in rows.values() if "copyBuffer" in k]
+        cal[c] = COPY_BYTES / (copies[-1] * 1024.0)            # counters count KiB
+    src = os.path.join(ROOT, "scaled_gemm_epilogues_amd", "csrc", "gemm.hip")
+    out = {"source": "gemm.hip", "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+           "calibration": {"copy_bytes": COPY_BYTES, "fetch_factor": cal["FETCH_SIZE"],
+                           "write_factor": cal["WRITE_SIZE"]},
+           "bytes_per_launch": {}, "raw_kib_per_launch": {}}
+    md = ["# HBM traffic per launch of the dominant kernels", "",
+          "Two rocprofv3 counter runs per launch (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each",
+          "scaled by what the same counter reads for a 1 GiB device-to-device copy",
+          f"(fetch factor {cal['FETCH_SIZE']:.3f}, write factor {cal['WRITE_SIZE']:.3f}). Commands, from /tmp:", "",
+          "```",
+          "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o copy_FETCH_SIZE -- python3 bench.py --copy-calibration",
+          "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o <workload>__<key>_FETCH_SIZE -- \\",
+          "    python3 bench.py --workload <workload> --profile-launch <key> --no-cpu-baseline",
+          "(the same with WRITE_SIZE), then: python3 bench.py --summarize-traffic <dir>",
+          "```", "",
+          "| workload | launch | kernel | FETCH_SIZE MiB | WRITE_SIZE MiB | HBM MB (scaled) |", "|---|---|---|---|---|---|"]
+    for f in sorted(glob.glob(os.path.join(pmc_dir, "*__*_FETCH_SIZE_counter_collection.csv"))):
+        tag = os.path.basename(f)[: -len("_FETCH_SIZE_counter_collection.csv")]
+        wl, key = tag.split("__", 1)
+        vals, kern = {}, None
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            rows = _pmc_rows(os.path.join(pmc_dir, f"{tag}_{c}_counter_collection.csv"))
+            seq = [rows[d] for d in sorted(rows)]
+            # a launch may run more than one kernel: its main one moves the most bytes
+            tail = seq[-4 * PROFILE_REPS:]
+            names = sorted({k for k, _ in tail}, key=lambda n: -sum(v for k, v in tail if k == n))
+            kern = kern or names[0]
+            last = [v for k, v in seq if k == kern][-PROFILE_REPS:]
+            vals[c] = sum(last) / len(last) * 1024.0
+        t = vals["FETCH_SIZE"] * cal["FETCH_SIZE"] + vals["WRITE_SIZE"] * cal["WRITE_SIZE"]
+        out["bytes_per_launch"][f"{wl}:{key}"] = int(t)
+        out["raw_kib_per_launch"][f"{wl}:{key}"] = {c: vals[c] / 1024.0 for c in vals}
+        short = kern.split("(")[0].replace("void ", "")[:60]
+        md.append(f"| {wl} | {key} | `{short}` | {vals['FETCH_SIZE'] / 2**20:.1f} | "
+                  f"{vals['WRITE_SIZE'] / 2**20:.1f} | {t / 1e6:.1f} |")
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+    with open(os.path.join(ROOT, "profiles", "traffic_dominant_gemms.md"), "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
+def summarize_trace(trace_dir, bench_json, out_md, command):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats CSV run of bench.py."""
+    import csv
+    import collections
+    rows = list(csv.DictReader(open(os.path.join(trace_dir, "trace_kernel_trace.csv"))))
+    stats = list(csv.DictReader(open(os.path.join(trace_dir, "trace_kernel_stats.csv"))))
+    with open(bench_json) as fh:
+        b = json.loads([ln for ln in fh.read().splitlines() if ln.startswith("{")][-1])
+    per = collections.defaultdict(list)
+    for r in rows:
+        per[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    L = [f"# Kernel trace: {b['config']['workload']}", "", "Produced by (from /tmp):", "", "```", command, "```", "",
+         "## rocprofv3 kernel statistics (every dispatch of the run)", "",
+         "| kernel | calls | avg us | median us | min us | max us | % time |", "|---|---|---|---|---|---|---|"]
+    for st in stats:
+        d = sorted(per.get(st["Name"], []))
+        med = d[len(d) // 2] if d else 0.0
+        L.append(f"| `{st['Name'][:110]}` | {st['Calls']} | {float(st['AverageNs']) / 1e3:.1f} | {med:.1f} | "
+                 f"{float(st['MinNs']) / 1e3:.1f} | {float(st['MaxNs']) / 1e3:.1f} | {float(st['Percentage']):.1f} |")
+    L += ["", "## bench.py line of the same run", "",
+          f"value {b['value']} {b['unit']}, ms_per_step {b['ms_per_step']} (graph {b.get('ms_per_step_graph')})", "",
+          "| launch | ms | rate |", "|---|---|---|"]
+    for k, v in b["kernels"].items():
+        rate = f"{v['tflops']} TFLOP/s" if "tflops" in v else (f"{v['gbs']} GB/s" if "gbs" in v else "")
+        L.append(f"| {k} | {v['ms']} | {rate} |")
+    L += ["", f"roofline: `{json.dumps(b['roofline'])}`", ""]
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(L) + "\n")
+
+
 def main():
     args = parse()
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic)
+        return 0
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return 0
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this path has no "
               "multi-GPU sharding).", file=sys.stderr)
@@ -280,6 +412,19 @@ def main():
     def eager_step():
         for _, f in launches:
             f()
+
+    if args.profile_launch:
+        fns = dict(launches)
+        if args.profile_launch not in fns:
+            print(f"unknown launch {args.profile_launch}; this workload has {list(fns)}", file=sys.stderr)
+            return 2
+        eager_step()
+        torch.cuda.synchronize()
+        for _ in range(args.profile_reps):
+            fns[args.profile_launch]()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_launch": args.profile_launch, PROFILE_REPS_KEY: args.profile_reps}), flush=True)
+        return 0
 
     for _ in range(args.warmup):
         eager_step()

@@ -13,9 +13,11 @@
 // optimizations" (Description, Sequence Diagram).
 //
 // Design (CDNA4):
-// * 256 threads = 4 waves in a 2x2 grid; each wave owns WMF x WNF fragments of
-//   32x32 fp32 accumulators (v_mfma_f32_32x32x16_bf16, or the MX-scaled
-//   v_mfma_scale_f32_32x32x64_f8f6f4 for E4M3 / MXFP8 with E8M0 scales).
+// * 256x256 macro tiles: 8 waves in a 2x4 grid (bf16, E4M3) or 4 waves in a 2x2 grid
+//   (MXFP8); each wave owns WMF x WNF fragments of 32x32 fp32 accumulators
+//   (v_mfma_f32_32x32x16_bf16, or the MX-scaled v_mfma_scale_f32_32x32x64_f8f6f4 for
+//   E4M3 / MXFP8 with E8M0 scales).
+// * Tiles are renumbered so each XCD runs a contiguous block of them (its own L2).
 // * Tiles of 128 contraction bytes per operand row (64 bf16 or 128 fp8) move
 //   from HBM straight into LDS with buffer_load ... lds (no staging registers;
 //   out-of-range lanes read zeros), in two LDS stages: the copy of tile k+1 is
@@ -69,6 +71,16 @@ template <>
 struct TileShape<3> {
   static constexpr int WGM = 2, WGN = 2, WMF = 4, WNF = 4;
 };
+
+// The dispatcher hands workgroups to the 8 XCDs round-robin (workgroup b runs on XCD b % 8),
+// and each XCD has its own L2. Renumbering so that XCD x receives one contiguous range of
+// tile indices makes the tiles an XCD runs at the same time neighbours, sharing operand
+// panels in its L2. Bijective on [0, total) for any total.
+__device__ __forceinline__ int xcd_tile(int bid, int total) {
+  const int x = bid & 7, i = bid >> 3;
+  const int q = total >> 3, r = total & 7;
+  return x * q + (x < r ? x : r) + i;
+}
 
 __device__ __forceinline__ float fast_sigmoid(float a) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-a));
@@ -238,10 +250,8 @@ void gemm_kernel(const GemmParams p) {
   uint16_t* cptr = p.c;
   int nt;
   if constexpr (SCHED == S_DENSE) {
-    int bid = blockIdx.x;
-    const int nblk = gridDim.x;
-    if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);   // tiles of one XCD adjacent
     const int MT = p.mt_count, NT = p.nt_count;
+    const int bid = xcd_tile(blockIdx.x, MT * NT);                      // grid is exactly MT * NT
     const int GM = SGE_XCD_GROUP_M;
     const int group = bid / (GM * NT);
     const int first_m = group * GM;
@@ -253,8 +263,23 @@ void gemm_kernel(const GemmParams p) {
     n0 = (int64_t)nt * BN;
     row_end = p.M;
   } else if constexpr (SCHED == S_GROUP_M) {
-    nt = blockIdx.x % p.nt_count;
-    int lin = blockIdx.x / p.nt_count;
+    // Row tiles of all groups, counted from the clamped offsets; the grid is an upper bound.
+    int total = 0;
+    {
+      int64_t prev = 0;
+      for (int gg = 0; gg < p.G; ++gg) {
+        int64_t a = p.offsets[gg], b = p.offsets[gg + 1];
+        a = a < prev ? prev : (a > p.T ? p.T : a);
+        b = b < a ? a : (b > p.T ? p.T : b);
+        prev = b;
+        total += (int)((b - a + BM - 1) / BM);
+      }
+    }
+    total *= p.nt_count;
+    if ((int)blockIdx.x >= total) return;                // beyond the last real tile
+    const int t = xcd_tile(blockIdx.x, total);
+    nt = t % p.nt_count;
+    int lin = t / p.nt_count;
     int g = -1;
     int64_t lo = 0, hi = 0, prev = 0;
     for (int gg = 0; gg < p.G; ++gg) {
@@ -272,9 +297,17 @@ void gemm_kernel(const GemmParams p) {
     n0 = (int64_t)nt * (EPI == E_SWIGLU ? BN / 2 : BN);
     bptr += (int64_t)g * p.b_group_stride * ES;
   } else {
+    // Groups differ in length (their contraction), so every XCD takes an equal contiguous
+    // slice of each group's tiles: balanced XCDs, and an XCD's concurrent tiles still share
+    // panels. (Identity when the tiles of a group do not split evenly over 8 XCDs.)
     const int per = p.mt_count * p.nt_count;
-    const int g = blockIdx.x / per;
-    const int rem = blockIdx.x % per;
+    int t = blockIdx.x;
+    if ((per & 7) == 0) {
+      const int per8 = per >> 3, x = t & 7, i = t >> 3;
+      t = (i / per8) * per + x * per8 + i % per8;
+    }
+    const int g = t / per;
+    const int rem = t % per;
     const int mt = rem / p.nt_count;
     nt = rem % p.nt_count;
     int64_t prev = 0, a = 0, b = 0;
