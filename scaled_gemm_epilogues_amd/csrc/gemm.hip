@@ -683,62 +683,96 @@ void gemm_kernel(const GemmParams p) {
       }
     }
   } else {  // E_DSWIGLU
-    const __amdgpu_buffer_rsrc_t rh = make_rsrc(p.aux + m0 * p.ld_aux, rows_left * p.ld_aux * 2);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.aux_out + m0 * p.ld_aux_out, rows_left * p.ld_aux_out * 2);
+    // Staged like E_STORE: g = alpha*acc for half of each wave's rows goes to LDS, then each
+    // thread takes 8 consecutive columns of one row: 16-byte loads of a and b (the two halves
+    // of the saved pre-activation), 16-byte stores of da and db. A row's BN/8 chunks are 32
+    // consecutive lanes, which reduce the row's dprobs partial in a fixed order; one partial
+    // per row and column tile goes to the workspace.
+    static_assert(BM == 2 * WM && A_BYTES + B_BYTES == 64 * BN * 4, "epilogue staging assumes 2 wave rows");
+    static_assert(BN / 8 == 32, "a row's chunks fill half a wave");
+    typedef int v4i __attribute__((__vector_size__(4 * sizeof(int))));
+    const int64_t hbytes = rows_left * p.ld_aux * 2, dbytes = rows_left * p.ld_aux_out * 2;
+    const __amdgpu_buffer_rsrc_t rha = make_rsrc(p.aux + m0 * p.ld_aux, hbytes);
+    const __amdgpu_buffer_rsrc_t rhb = make_rsrc(p.aux + m0 * p.ld_aux + p.F, hbytes - p.F * 2);
+    const __amdgpu_buffer_rsrc_t rda = make_rsrc(p.aux_out + m0 * p.ld_aux_out, dbytes);
+    const __amdgpu_buffer_rsrc_t rdb = make_rsrc(p.aux_out + m0 * p.ld_aux_out + p.F, dbytes - p.F * 2);
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.probs + m0, rows_left * 4);
-    const __amdgpu_buffer_rsrc_t rpart = make_rsrc(p.dp_part + (int64_t)(nt * WGN + wn) * p.T + m0, rows_left * 4);
-    auto hoff = [&](int i, int j, int q, int half) -> int {
-      const int64_t n = n0 + wn * WN + j * 32 + 8 * q + 4 * lhalf;
-      return (row_ok(i) && n < n_end) ? (int)(((int64_t)row_in_tile(i) * p.ld_aux + half * p.F + n) * 2) : (int)kOOB;
-    };
-    v2i hab[1][WNF][4][2];
-    auto load = [&](int i, v2i (&h)[WNF][4][2]) {
+    const __amdgpu_buffer_rsrc_t rpart = make_rsrc(p.dp_part + (int64_t)nt * p.T + m0, rows_left * 4);
+    constexpr int kChunks = BN / 8;
+    constexpr int kIters = 128 * kChunks / (NWAVES * 64);
+    float* stage = reinterpret_cast<float*>(wm ? lds1 : lds0);
+    __syncthreads();                                       // every wave is done with the LDS stages
 #pragma unroll
-      for (int j = 0; j < WNF; ++j)
+    for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+      for (int il = 0; il < WMF / 2; ++il) {
+        const int i = pass * (WMF / 2) + il;
+        const int r = il * 32 + lrow;
 #pragma unroll
-          for (int half = 0; half < 2; ++half)
-            h[j][q][half] = __builtin_amdgcn_raw_buffer_load_b64(rh, hoff(i, j, q, half), 0, 0);
-    };
+        for (int j = 0; j < WNF; ++j)
 #pragma unroll
-    for (int i = 0; i < WMF; ++i) {
-      load(i, hab[0]);
-      const float pm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                     rp, row_ok(i) ? row_in_tile(i) * 4 : (int)kOOB, 0, 0));
-      float part = 0.0f;
-#pragma unroll
-      for (int j = 0; j < WNF; ++j) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const v2i ha = hab[0][j][q][0], hb = hab[0][j][q][1];
-          const float a[4] = {bf16_lo((uint32_t)ha[0]), bf16_hi((uint32_t)ha[0]), bf16_lo((uint32_t)ha[1]),
-                              bf16_hi((uint32_t)ha[1])};
-          const float b[4] = {bf16_lo((uint32_t)hb[0]), bf16_hi((uint32_t)hb[0]), bf16_lo((uint32_t)hb[1]),
-                              bf16_hi((uint32_t)hb[1])};
-          float da[4], db[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float g = alpha * acc[i][j][4 * q + e];
-            const float sg = fast_sigmoid(a[e]);
-            const float silu = a[e] * sg;
-            const float dsilu = sg * (1.0f + a[e] * (1.0f - sg));
-            da[e] = g * pm * b[e] * dsilu;
-            db[e] = g * pm * silu;
-            part += g * silu * b[e];
+          for (int q = 0; q < 4; ++q) {
+            const int g = (wn * WN + j * 32 + 8 * q + 4 * lhalf) >> 2;
+            const float4 v = make_float4(alpha * acc[i][j][4 * q + 0], alpha * acc[i][j][4 * q + 1],
+                                         alpha * acc[i][j][4 * q + 2], alpha * acc[i][j][4 * q + 3]);
+            *reinterpret_cast<float4*>(stage + r * BN + ((g ^ (r & 15)) << 2)) = v;
           }
-          const v2i dav = {(int)pack_bf16x2(da[0], da[1]), (int)pack_bf16x2(da[2], da[3])};
-          const v2i dbv = {(int)pack_bf16x2(db[0], db[1]), (int)pack_bf16x2(db[2], db[3])};
-          __builtin_amdgcn_raw_buffer_store_b64(dav, rd, hoff(i, j, q, 0) == (int)kOOB ? (int)kOOB
-                                                    : (int)(((int64_t)row_in_tile(i) * p.ld_aux_out + n0 + wn * WN + j * 32 + 8 * q + 4 * lhalf) * 2), 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b64(dbv, rd, hoff(i, j, q, 1) == (int)kOOB ? (int)kOOB
-                                                    : (int)(((int64_t)row_in_tile(i) * p.ld_aux_out + p.F + n0 + wn * WN + j * 32 + 8 * q + 4 * lhalf) * 2), 0, 0);
-        }
       }
-      // Lanes l and l+32 hold the same row: combine, then one lane writes the row's partial.
-      part += __shfl_xor(part, 32, 64);
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, part), rpart,
-                                            (row_ok(i) && lhalf == 0) ? row_in_tile(i) * 4 : (int)kOOB, 0, 0);
+      __syncthreads();
+      v4i ha[kIters], hb[kIters];
+      float pr[kIters];
+      int oh[kIters], od[kIters], orow[kIters];
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) {
+        const int id = it * NWAVES * 64 + threadIdx.x;
+        const int rp_ = id / kChunks, c = id % kChunks;
+        const int brow = (rp_ >> 6) * WM + pass * (WM / 2) + (rp_ & 63);
+        const int64_t n = n0 + c * 8;
+        const bool rok = m0 + brow < row_end;
+        const bool ok = rok && n < n_end;
+        oh[it] = ok ? (int)(((int64_t)brow * p.ld_aux + n) * 2) : (int)kOOB;
+        od[it] = ok ? (int)(((int64_t)brow * p.ld_aux_out + n) * 2) : (int)kOOB;
+        orow[it] = rok ? brow * 4 : (int)kOOB;
+        ha[it] = __builtin_amdgcn_raw_buffer_load_b128(rha, oh[it], 0, 0);
+        hb[it] = __builtin_amdgcn_raw_buffer_load_b128(rhb, oh[it], 0, 0);
+        pr[it] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, orow[it], 0, 0));
+      }
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) {
+        const int id = it * NWAVES * 64 + threadIdx.x;
+        const int rp_ = id / kChunks, c = id % kChunks;
+        const float* row = reinterpret_cast<const float*>(rp_ >= 64 ? lds1 : lds0) + (rp_ & 63) * BN;
+        const int sw = (rp_ & 63) & 15;
+        const float4 lo = *reinterpret_cast<const float4*>(row + (((2 * c) ^ sw) << 2));
+        const float4 hi = *reinterpret_cast<const float4*>(row + (((2 * c + 1) ^ sw) << 2));
+        const float g[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        const float pm = pr[it];
+        float da[8], db[8], part = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t wa = (uint32_t)ha[it][e >> 1], wb = (uint32_t)hb[it][e >> 1];
+          const float a = (e & 1) ? bf16_hi(wa) : bf16_lo(wa);
+          const float b = (e & 1) ? bf16_hi(wb) : bf16_lo(wb);
+          const float sg = fast_sigmoid(a);
+          const float silu = a * sg;
+          const float dsilu = sg * (1.0f + a * (1.0f - sg));
+          da[e] = g[e] * pm * b * dsilu;
+          db[e] = g[e] * pm * silu;
+          part += g[e] * silu * b;
+        }
+        const v4i va = {(int)pack_bf16x2(da[0], da[1]), (int)pack_bf16x2(da[2], da[3]),
+                        (int)pack_bf16x2(da[4], da[5]), (int)pack_bf16x2(da[6], da[7])};
+        const v4i vb = {(int)pack_bf16x2(db[0], db[1]), (int)pack_bf16x2(db[2], db[3]),
+                        (int)pack_bf16x2(db[4], db[5]), (int)pack_bf16x2(db[6], db[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(va, rda, od[it], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(vb, rdb, od[it], 0, 0);
+        // the row's 32 chunks are lanes c = 0..31 of one half-wave: fixed-order tree sum
+#pragma unroll
+        for (int d = 1; d < 32; d <<= 1) part += __shfl_xor(part, d, 64);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, part), rpart, c == 0 ? orow[it] : (int)kOOB,
+                                              0, 0);
+      }
+      if (pass == 0) __syncthreads();                      // stage reused by the second pass
     }
   }
 }
@@ -803,6 +837,6 @@ hipError_t launch_grouped_wgrad(const GemmParams& p, hipStream_t s) {
 }
 
 int gemm_tile_n() { return kWavesN * 32 * kFragsN; }
-int gemm_dp_parts_per_tile() { return kWavesN; }
+int gemm_dp_parts_per_tile() { return 1; }
 
 }  // namespace sge
