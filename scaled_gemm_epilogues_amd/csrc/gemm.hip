@@ -649,38 +649,84 @@ void gemm_kernel(const GemmParams p) {
       if (pass == 0) __syncthreads();                      // stage reused by the second pass
     }
   } else if constexpr (EPI == E_SWIGLU) {
-    constexpr int HJ = WNF / 2;
+    // Staged like E_STORE: alpha*acc (each wave column holds WN/2 gate columns a, then the
+    // matching WN/2 up columns b) goes to LDS, then each thread takes 8 consecutive output
+    // columns of one row: y = p * silu(a) * b, and 16-byte stores of y and of the two
+    // halves of the saved pre-activation. The granule XOR includes the wave column, so the
+    // 16 chunks of a row (4 per wave column) read 16 distinct bank groups.
+    static_assert(BM == 2 * WM && A_BYTES + B_BYTES == 64 * BN * 4, "epilogue staging assumes 2 wave rows");
+    static_assert(WNF == 2 && WN == 64, "one gate and one up fragment per wave column");
+    typedef int v4i __attribute__((__vector_size__(4 * sizeof(int))));
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(cptr + m0 * p.ldc, rows_left * p.ldc * 2);
-    const __amdgpu_buffer_rsrc_t rh = make_rsrc(p.aux ? p.aux + m0 * p.ld_aux : p.aux, p.aux ? rows_left * p.ld_aux * 2 : 0);
+    const int64_t hbytes = p.aux ? rows_left * p.ld_aux * 2 : 0;
+    const __amdgpu_buffer_rsrc_t rha = make_rsrc(p.aux ? p.aux + m0 * p.ld_aux : p.aux, hbytes);
+    const __amdgpu_buffer_rsrc_t rhb = make_rsrc(p.aux ? p.aux + m0 * p.ld_aux + p.F : p.aux, hbytes - p.F * 2);
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.probs + m0, rows_left * 4);
+    constexpr int kChunks = BN / 16;                       // 8-column output chunks per row
+    constexpr int kIters = 128 * kChunks / (NWAVES * 64);
+    auto wsw = [](int w) { return (w & 1) | ((w & 2) << 2); };
+    float* stage = reinterpret_cast<float*>(wm ? lds1 : lds0);
+    __syncthreads();                                       // every wave is done with the LDS stages
 #pragma unroll
-    for (int i = 0; i < WMF; ++i) {
-      const float pm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                     rp, row_ok(i) ? row_in_tile(i) * 4 : (int)kOOB, 0, 0));
+    for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-      for (int j = 0; j < HJ; ++j) {
+      for (int il = 0; il < WMF / 2; ++il) {
+        const int i = pass * (WMF / 2) + il;
+        const int r = il * 32 + lrow;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t col = n0 + wn * (WN / 2) + j * 32 + 8 * q + 4 * lhalf;
-          const bool ok = row_ok(i) && col < n_end;
-          float a[4], b[4], y[4];
+        for (int j = 0; j < WNF; ++j)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            a[e] = alpha * acc[i][j][4 * q + e];
-            b[e] = alpha * acc[i][j + HJ][4 * q + e];
-            y[e] = pm * (a[e] * fast_sigmoid(a[e])) * b[e];
+          for (int q = 0; q < 4; ++q) {
+            const int g = (wn * WN + j * 32 + 8 * q + 4 * lhalf) >> 2;
+            const float4 v = make_float4(alpha * acc[i][j][4 * q + 0], alpha * acc[i][j][4 * q + 1],
+                                         alpha * acc[i][j][4 * q + 2], alpha * acc[i][j][4 * q + 3]);
+            *reinterpret_cast<float4*>(stage + r * BN + ((g ^ (r & 15) ^ wsw(wn)) << 2)) = v;
           }
-          const int oh = ok ? (int)(((int64_t)row_in_tile(i) * p.ld_aux + col) * 2) : (int)kOOB;
-          const int ohb = ok ? (int)(((int64_t)row_in_tile(i) * p.ld_aux + p.F + col) * 2) : (int)kOOB;
-          const int oy = ok ? (int)(((int64_t)row_in_tile(i) * p.ldc + col) * 2) : (int)kOOB;
-          const v2i hv = {(int)pack_bf16x2(a[0], a[1]), (int)pack_bf16x2(a[2], a[3])};
-          const v2i bv = {(int)pack_bf16x2(b[0], b[1]), (int)pack_bf16x2(b[2], b[3])};
-          const v2i yv = {(int)pack_bf16x2(y[0], y[1]), (int)pack_bf16x2(y[2], y[3])};
-          __builtin_amdgcn_raw_buffer_store_b64(hv, rh, oh, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b64(bv, rh, ohb, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b64(yv, ry, oy, 0, 0);
-        }
       }
+      __syncthreads();
+      float pr[kIters];
+      int oy[kIters], oh[kIters];
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) {
+        const int id = it * NWAVES * 64 + threadIdx.x;
+        const int rp_ = id / kChunks, c = id % kChunks;
+        const int brow = (rp_ >> 6) * WM + pass * (WM / 2) + (rp_ & 63);
+        const int64_t n = n0 + c * 8;
+        const bool rok = m0 + brow < row_end;
+        const bool ok = rok && n < n_end;
+        oy[it] = ok ? (int)(((int64_t)brow * p.ldc + n) * 2) : (int)kOOB;
+        oh[it] = ok ? (int)(((int64_t)brow * p.ld_aux + n) * 2) : (int)kOOB;
+        pr[it] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, rok ? brow * 4 : (int)kOOB, 0, 0));
+      }
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) {
+        const int id = it * NWAVES * 64 + threadIdx.x;
+        const int rp_ = id / kChunks, c = id % kChunks;
+        const int rr = rp_ & 63, wc = c >> 2, cc = c & 3;
+        const float* row = reinterpret_cast<const float*>(rp_ >= 64 ? lds1 : lds0) + rr * BN;
+        const int x = (rr & 15) ^ wsw(wc);
+        const int ga = wc * 16 + 2 * cc, gb = ga + 8;      // gate and up granules of this chunk
+        const float4 a0 = *reinterpret_cast<const float4*>(row + ((ga ^ x) << 2));
+        const float4 a1 = *reinterpret_cast<const float4*>(row + (((ga + 1) ^ x) << 2));
+        const float4 b0 = *reinterpret_cast<const float4*>(row + ((gb ^ x) << 2));
+        const float4 b1 = *reinterpret_cast<const float4*>(row + (((gb + 1) ^ x) << 2));
+        const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        const float pm = pr[it];
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = pm * (a[e] * fast_sigmoid(a[e])) * b[e];
+        const v4i va = {(int)pack_bf16x2(a[0], a[1]), (int)pack_bf16x2(a[2], a[3]), (int)pack_bf16x2(a[4], a[5]),
+                        (int)pack_bf16x2(a[6], a[7])};
+        const v4i vb = {(int)pack_bf16x2(b[0], b[1]), (int)pack_bf16x2(b[2], b[3]), (int)pack_bf16x2(b[4], b[5]),
+                        (int)pack_bf16x2(b[6], b[7])};
+        const v4i vy = {(int)pack_bf16x2(y[0], y[1]), (int)pack_bf16x2(y[2], y[3]), (int)pack_bf16x2(y[4], y[5]),
+                        (int)pack_bf16x2(y[6], y[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(va, rha, oh[it], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(vb, rhb, oh[it], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(vy, ry, oy[it], 0, 0);
+      }
+      if (pass == 0) __syncthreads();                      // stage reused by the second pass
     }
   } else {  // E_DSWIGLU
     // Staged like E_STORE: g = alpha*acc for half of each wave's rows goes to LDS, then each
