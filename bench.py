@@ -316,7 +316,7 @@ def summarize_traffic(pmc_dir):
            "calibration": {"copy_bytes": COPY_BYTES, "fetch_factor": cal["FETCH_SIZE"],
                            "write_factor": cal["WRITE_SIZE"]},
            "bytes_per_launch": {}, "raw_kib_per_launch": {}}
-    md = ["# HBM traffic per launch of the dominant kernels", "",
+    md = ["# HBM-side traffic per launch (GEMMs and quantizers)", "",
           "Two rocprofv3 counter runs per launch (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each",
           "scaled by what the same counter reads for a 1 GiB device-to-device copy",
           f"(fetch factor {cal['FETCH_SIZE']:.3f}, write factor {cal['WRITE_SIZE']:.3f}). Commands, from /tmp:", "",
@@ -326,29 +326,34 @@ def summarize_traffic(pmc_dir):
           "    python3 bench.py --workload <workload> --profile-launch <key> --no-cpu-baseline",
           "(the same with WRITE_SIZE), then: python3 bench.py --summarize-traffic <dir>",
           "```", "",
-          "| workload | launch | kernel | FETCH_SIZE MiB | WRITE_SIZE MiB | HBM MB (scaled) |", "|---|---|---|---|---|---|"]
+          "FETCH_SIZE counts L2 misses, so operand panels that several XCDs' L2s each fetch count once",
+          "per XCD (the repeats are served by the Infinity Cache).", "",
+          "| workload | launch | kernels | FETCH_SIZE MiB | WRITE_SIZE MiB | traffic MB (scaled) |", "|---|---|---|---|---|---|"]
     for f in sorted(glob.glob(os.path.join(pmc_dir, "*__*_FETCH_SIZE_counter_collection.csv"))):
         tag = os.path.basename(f)[: -len("_FETCH_SIZE_counter_collection.csv")]
         wl, key = tag.split("__", 1)
-        vals, kern = {}, None
+        per_kernel = {}
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             rows = _pmc_rows(os.path.join(pmc_dir, f"{tag}_{c}_counter_collection.csv"))
             seq = [rows[d] for d in sorted(rows)]
-            # a launch may run more than one kernel: its main one moves the most bytes
-            tail = seq[-4 * PROFILE_REPS:]
-            names = sorted({k for k, _ in tail}, key=lambda n: -sum(v for k, v in tail if k == n))
-            kern = kern or names[0]
-            last = [v for k, v in seq if k == kern][-PROFILE_REPS:]
-            vals[c] = sum(last) / len(last) * 1024.0
-        t = vals["FETCH_SIZE"] * cal["FETCH_SIZE"] + vals["WRITE_SIZE"] * cal["WRITE_SIZE"]
+            # the repeated launch is the last k * profile-reps dispatches, k its kernel count:
+            # the smallest period of the kernel-name sequence there
+            k = next(k for k in range(1, 9) if all(seq[-k * PROFILE_REPS + i][0] == seq[-k * PROFILE_REPS + i + k][0]
+                                                  for i in range(k * PROFILE_REPS - k)))
+            for name, v in seq[-k * PROFILE_REPS:]:
+                per_kernel.setdefault(name, {}).setdefault(c, 0.0)
+                per_kernel[name][c] += v * 1024.0 / PROFILE_REPS
+        per_kernel = {k: v for k, v in per_kernel.items() if len(v) == 2}
+        fetch = sum(v["FETCH_SIZE"] for v in per_kernel.values())
+        write = sum(v["WRITE_SIZE"] for v in per_kernel.values())
+        t = fetch * cal["FETCH_SIZE"] + write * cal["WRITE_SIZE"]
         out["bytes_per_launch"][f"{wl}:{key}"] = int(t)
-        out["raw_kib_per_launch"][f"{wl}:{key}"] = {c: vals[c] / 1024.0 for c in vals}
-        short = kern.split("(")[0].replace("void ", "")[:60]
-        md.append(f"| {wl} | {key} | `{short}` | {vals['FETCH_SIZE'] / 2**20:.1f} | "
-                  f"{vals['WRITE_SIZE'] / 2**20:.1f} | {t / 1e6:.1f} |")
+        out["raw_kib_per_launch"][f"{wl}:{key}"] = {"FETCH_SIZE": fetch / 1024.0, "WRITE_SIZE": write / 1024.0}
+        kern = " + ".join(f"`{k.split('(')[0].replace('void ', '')[:60]}`" for k in per_kernel)
+        md.append(f"| {wl} | {key} | {kern} | {fetch / 2**20:.1f} | {write / 2**20:.1f} | {t / 1e6:.1f} |")
     with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
         json.dump(out, fh, indent=1)
-    with open(os.path.join(ROOT, "profiles", "traffic_dominant_gemms.md"), "w") as fh:
+    with open(os.path.join(ROOT, "profiles", "traffic_per_launch.md"), "w") as fh:
         fh.write("\n".join(md) + "\n")
     print("\n".join(md))
 
