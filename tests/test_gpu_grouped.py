@@ -48,19 +48,22 @@ def _oracle_mlp(inp):
     return f, b
 
 
+# splits (None: Dirichlet over T=520, G=5), hidden, ffn. The mid-size case gives the weight
+# gradients 16 and 8 output tiles per group, so each XCD takes a slice of every group.
 SPLIT_CASES = {
-    "empty_and_single": [0, 1, 300, 0, 211, 8],
-    "dirichlet": None,
+    "empty_and_single": ([0, 1, 300, 0, 211, 8], 256, 256),
+    "dirichlet": (None, 256, 256),
+    "mid_xcd_slices": ([700, 0, 333, 41, 210], 1024, 512),
 }
 
 
 @pytest.mark.parametrize("case", list(SPLIT_CASES))
 def test_grouped_mlp_parity(case):
-    splits = SPLIT_CASES[case]
+    splits, hidden, ffn = SPLIT_CASES[case]
     T = 520 if splits is None else sum(splits)
     G = 5 if splits is None else len(splits)
-    print(f"case grouped mlp {case} T={T} G={G}", flush=True)
-    inp = synth.grouped(T, G, 256, 256, seed=21, splits=splits)
+    print(f"case grouped mlp {case} T={T} G={G} hidden={hidden} ffn={ffn}", flush=True)
+    inp = synth.grouped(T, G, hidden, ffn, seed=21, splits=splits)
     got = run_grouped_mlp(inp)
     f, b = _oracle_mlp(inp)
     assert int(got["err"].item()) == 0
