@@ -216,20 +216,32 @@ def cpu_baseline(wl, inp, target_s):
         M = inp["x"].shape[0]
         N, K = inp["w"].shape
         rows = 64
-        while True:
-            bwd = "dgrad" in wl["passes"]
-            t0 = time.perf_counter()
+        bwd = "dgrad" in wl["passes"]
+
+        def run(rows):
             ops = linear.operands(wl["fmt"], inp["x"][:rows], inp["w"], inp["dy"][:rows] if bwd else None)
             linear.linear_scale_add_fwd(*ops["fwd"], bf16_to_f64(inp["residual"][:rows]), wl["alpha"])
             if bwd:
                 linear.linear_scale_dgrad(*ops["dgrad"], wl["alpha"])
                 linear.linear_scale_wgrad(*ops["wgrad"], wl["alpha"])
+
+        while True:
+            t0 = time.perf_counter()
+            run(rows)
             dt = time.perf_counter() - t0
             if dt >= target_s / 4 or rows >= M:
                 break
             rows = min(M, rows * 4)
-        flops = (3 if "dgrad" in wl["passes"] else 1) * 2 * rows * N * K
-        sample = f"first {rows} of {M} token rows through {'/'.join(wl['passes'])} (quantizers included)"
+        reps = 1
+        if dt < target_s / 4:                                   # the whole workload is quick: repeat it
+            reps = max(1, int(target_s / 4 / max(dt, 1e-3)))
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                run(rows)
+            dt = (time.perf_counter() - t0) / reps
+        flops = (3 if bwd else 1) * 2 * rows * N * K
+        sample = (f"first {rows} of {M} token rows through {'/'.join(wl['passes'])} (quantizers included)"
+                  + (f", mean of {reps} runs" if reps > 1 else ""))
     else:
         T = inp["x"].shape[0]
         tok = 256
