@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define SGE_ABI_VERSION 1
+#define SGE_ABI_VERSION 2
 
 typedef enum {
   SGE_OK = 0,
@@ -207,6 +207,31 @@ sge_status sge_splits_to_offsets(const int64_t* splits, int32_t G, const int64_t
 sge_status sge_grouped_linear_fwd(const void* x, const void* w, int32_t G, int64_t T, int64_t N,
                                   int64_t K, const int64_t* offsets, float alpha, int32_t epilogue,
                                   const float* probs, void* out, void* preact, hipStream_t stream);
+
+/*
+ * Grouped linear forward with MXFP8 operands, and the fused activation + group quantize.
+ * ("Activation + GroupedLinear Fusion for MOE and other MOE optimizations", Description:
+ * Activation + GroupQuantize Fusion, and the forward of the Sequence Diagram, where the
+ * scaled activation's output reaches FC2 quantized.)
+ *
+ * The same computation as sge_grouped_linear_fwd with x and every W_g given as MXFP8
+ * quantized rowwise (E4M3 bytes, one E8M0 exponent per 32 elements along K):
+ *   x_q [T, K] u8, x_s [T, K/32] u8;  w_q [G, N, K] u8, w_s [G, N, K/32] u8
+ *   (exactly what sge_quantize_mxfp8 writes as q_row / s_row).
+ * SGE_EPI_NONE: out [T, N] bf16.
+ * SGE_EPI_SCALED_SWIGLU: out [T, N/2] bf16 (may be NULL when out_q is given), preact
+ *   [T, N] bf16 (may be NULL), and optionally out_q [T, N/2] u8 + out_s [T, N/64] u8: the
+ *   MXFP8 rowwise quantization of the bf16 output, i.e. the bytes sge_quantize_mxfp8 would
+ *   write for `out` (the operand layout of the next grouped GEMM's forward). out_q and
+ *   out_s are given together or not at all.
+ * Shapes: K % 128 == 0; N % 8 == 0 (SWIGLU: N % 256 == 0). All pointers 16-byte aligned;
+ * outputs must not overlap the inputs or each other (SGE_ERR_ALIAS). offsets and probs
+ * as in sge_grouped_linear_fwd.
+ */
+sge_status sge_grouped_linear_fwd_mxfp8(const void* x_q, const void* x_s, const void* w_q, const void* w_s,
+                                        int32_t G, int64_t T, int64_t N, int64_t K, const int64_t* offsets,
+                                        float alpha, int32_t epilogue, const float* probs, void* out,
+                                        void* preact, void* out_q, void* out_s, hipStream_t stream);
 
 /*
  * Grouped linear backward for one layer with the precomputed offsets.

@@ -30,6 +30,29 @@ def bf16_to_f32(bits):
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def f64_to_bf16(v):
+    """Round finite fp64 values to the nearest bf16, ties to even (IEEE round-to-nearest-even),
+    returned as uint16 bit patterns.
+
+    bf16 keeps 8 significand bits (7 stored) and fp32's exponent range: a value of magnitude
+    in [2^e, 2^(e+1)) sits on a grid of spacing 2^(e-7), subnormals (e < -126) on the grid
+    2^-133. The value is divided by its grid spacing (exact: a power of two), rounded to the
+    nearest integer with ties to even (numpy rint), and multiplied back (exact); the result
+    is a bf16 value, read off as the top half of its fp32 bits. Magnitudes at or above
+    2^128 - 2^119 round to infinity; zeros keep their sign.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, e2 = np.frexp(np.where(a > 0, a, 1.0))           # a = f * 2^e2, f in [0.5, 1)
+    e = np.maximum(e2.astype(np.int64) - 1, -126)       # floor(log2 a), subnormals share -126
+    ulp = np.ldexp(1.0, e - 7)
+    r = np.rint(v / ulp) * ulp                          # exact: |v/ulp| < 2^9
+    r = np.where(a > 0, r, v)                           # keep signed zeros
+    with np.errstate(over="ignore"):
+        f = r.astype(np.float32)                        # exact (r is a bf16 value) or +-inf
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
 # ---------------------------------------------------------------- E4M3 -----
 def e4m3_decode(codes):
     """Value of each E4M3 byte (OCP OFP8: sign, 4-bit exponent bias 7, 3-bit mantissa).

@@ -20,6 +20,9 @@ Readings where the page is silent:
 
 import numpy as np
 
+from .codecs import bf16_to_f64, f64_to_bf16
+from .quant import mx_dequantize, mxfp8_rowwise
+
 
 def _groups(base):
     base = np.asarray(base, dtype=np.int64)
@@ -116,3 +119,38 @@ def grouped_mlp_bwd(dout, x, w1, w2, p, base, h=None, y=None):
     dx = grouped_linear_dgrad(dh, w1, base)
     dw1 = grouped_linear_wgrad(dh, x, base)
     return {"gy": gy, "dh": dh, "dp": dp, "dw2": dw2, "dx": dx, "dw1": dw1}
+
+
+def grouped_mlp_fwd_mxfp8(x_bits, w1_bits, w2_bits, p, base):
+    """Grouped MLP forward on MXFP8 operands, with the activation quantized for fc2.
+
+    "Activation + GroupedLinear Fusion for MOE and other MOE optimizations" (Description:
+    Activation + GroupQuantize Fusion; Sequence Diagram, forward): the scaled activation's
+    output is group-quantized and reaches FC2 quantized. Every GEMM operand here is MXFP8
+    with blocks of 32 along that GEMM's contraction dim (rowwise for the forward), and:
+
+    1. x and each W1_g, W2_g are quantized rowwise (``mxfp8_rowwise``) and dequantized;
+    2. h = x_hat @ W1_g^T per group, y = p * silu(a) * b (``scaled_swiglu_fwd``), in fp64;
+    3. the activation is rounded to bf16 (the dtype the activation has when it is not
+       quantized) and that bf16 tensor is quantized rowwise: (y_q, y_s);
+    4. out = y_hat @ W2_g^T per group, y_hat the dequantized (y_q, y_s).
+
+    x_bits [T, H], w1_bits [G, 2F, H], w2_bits [G, H, F] (bf16 bit patterns); p [T]; base [G+1].
+    Returns h, y (fp64), y_bits (bf16), y_q, y_s and out (fp64).
+    """
+    x_bits = np.asarray(x_bits, np.uint16)
+    w1_bits = np.asarray(w1_bits, np.uint16)
+    w2_bits = np.asarray(w2_bits, np.uint16)
+    G, N1, H = w1_bits.shape
+    F = w2_bits.shape[2]
+    x_hat = mx_dequantize(*mxfp8_rowwise(x_bits))
+    w1_hat = mx_dequantize(*mxfp8_rowwise(w1_bits.reshape(G * N1, H))).reshape(G, N1, H)
+    w2_hat = mx_dequantize(*mxfp8_rowwise(w2_bits.reshape(G * H, F))).reshape(G, H, F)
+    h = grouped_linear_fwd(x_hat, w1_hat, base)
+    y = scaled_swiglu_fwd(h, p)
+    y_bits = f64_to_bf16(y)
+    y_q, y_s = mxfp8_rowwise(y_bits)
+    out = grouped_linear_fwd(mx_dequantize(y_q, y_s), w2_hat, base)
+    return {"h": h, "y": y, "y_bits": y_bits, "y_q": y_q, "y_s": y_s, "out": out,
+            "y_value": bf16_to_f64(y_bits)}
+

@@ -32,7 +32,7 @@ EXPORTED = (
     "sge_abi_version", "sge_status_string", "sge_last_error_message",
     "sge_linear_scale_add_fwd", "sge_linear_scale_bwd",
     "sge_quantize_fp8_amax_workspace_size", "sge_quantize_fp8_amax", "sge_quantize_mxfp8",
-    "sge_splits_to_offsets", "sge_grouped_linear_fwd",
+    "sge_splits_to_offsets", "sge_grouped_linear_fwd", "sge_grouped_linear_fwd_mxfp8",
     "sge_grouped_linear_bwd_workspace_size", "sge_grouped_linear_bwd",
     "sge_scaled_swiglu_fwd", "sge_scaled_swiglu_bwd",
 )
@@ -66,6 +66,8 @@ _SIGS = {
     "sge_splits_to_offsets": ([_vp, _i32, ctypes.POINTER(_i64), _i32, _i64, _vp, _vp, _vp], ctypes.c_int),
     "sge_grouped_linear_fwd": ([_vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _vp, _vp, _vp, _vp],
                                ctypes.c_int),
+    "sge_grouped_linear_fwd_mxfp8": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _vp, _vp, _vp,
+                                      _vp, _vp, _vp], ctypes.c_int),
     "sge_grouped_linear_bwd_workspace_size": ([_i64, _i64, _i32, _i32], _sz),
     "sge_grouped_linear_bwd": ([_vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
@@ -190,6 +192,17 @@ def grouped_linear_fwd(x, w, offsets, out, alpha=1.0, epilogue=EPI_NONE, probs=N
     T = x.shape[0]
     _check(_lib.sge_grouped_linear_fwd(_ptr(x), _ptr(w), G, T, N, K, _ptr(offsets), float(alpha), epilogue,
                                        _ptr(probs), _ptr(out), _ptr(preact), _stream(stream)))
+
+
+def grouped_linear_fwd_mxfp8(x_q, x_s, w_q, w_s, offsets, out=None, alpha=1.0, epilogue=EPI_NONE, probs=None,
+                             preact=None, out_q=None, out_s=None, stream=None):
+    """Grouped forward with MXFP8 operands: x_q [T, K] u8 + x_s [T, K/32] u8, w_q [G, N, K] u8 +
+    w_s [G, N, K/32] u8 (rowwise). SwiGLU may also emit out_q [T, N/2] + out_s [T, N/64]."""
+    G, N, K = w_q.shape
+    T = x_q.shape[0]
+    _check(_lib.sge_grouped_linear_fwd_mxfp8(_ptr(x_q), _ptr(x_s), _ptr(w_q), _ptr(w_s), G, T, N, K, _ptr(offsets),
+                                             float(alpha), epilogue, _ptr(probs), _ptr(out), _ptr(preact),
+                                             _ptr(out_q), _ptr(out_s), _stream(stream)))
 
 
 def grouped_linear_bwd_workspace_size(T, K, G, epilogue):

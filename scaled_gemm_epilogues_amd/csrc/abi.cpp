@@ -340,6 +340,73 @@ sge_status sge_grouped_linear_fwd(const void* x, const void* w, int32_t G, int64
   return hip_status(sge::launch_grouped_fwd(p, epilogue, stream), "grouped fwd launch");
 }
 
+sge_status sge_grouped_linear_fwd_mxfp8(const void* x_q, const void* x_s, const void* w_q, const void* w_s, int32_t G,
+                                        int64_t T, int64_t N, int64_t K, const int64_t* offsets, float alpha,
+                                        int32_t epilogue, const float* probs, void* out, void* preact, void* out_q,
+                                        void* out_s, hipStream_t stream) {
+  if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_mxfp8: bad sizes");
+  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_SCALED_SWIGLU)
+    return fail(SGE_ERR_ARG, "grouped_linear_fwd_mxfp8: epilogue %d not allowed", epilogue);
+  const bool swiglu = epilogue == SGE_EPI_SCALED_SWIGLU;
+  if (!x_q || !x_s || !w_q || !w_s || !offsets) return fail(SGE_ERR_NULL, "grouped_linear_fwd_mxfp8: NULL pointer");
+  if ((out_q == nullptr) != (out_s == nullptr))
+    return fail(SGE_ERR_NULL, "grouped_linear_fwd_mxfp8: out_q and out_s go together");
+  if (out_q && !swiglu) return fail(SGE_ERR_ARG, "grouped_linear_fwd_mxfp8: a quantized output needs the SwiGLU epilogue");
+  if (!out && !out_q) return fail(SGE_ERR_NULL, "grouped_linear_fwd_mxfp8: no output");
+  if (swiglu && !probs) return fail(SGE_ERR_NULL, "grouped_linear_fwd_mxfp8: probs is NULL");
+  if (K % 128) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_mxfp8: K must be a multiple of 128 (got %lld)", (long long)K);
+  if (N % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_mxfp8: N must be a multiple of 8");
+  if (swiglu && N % 256) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_mxfp8: SwiGLU needs N %% 256 == 0");
+  if (!aligned16(x_q) || !aligned16(x_s) || !aligned16(w_q) || !aligned16(w_s) || (out && !aligned16(out)) ||
+      (preact && !aligned16(preact)) || (out_q && !aligned16(out_q)))
+    return fail(SGE_ERR_ALIGN, "grouped_linear_fwd_mxfp8: pointers must be 16-byte aligned");
+  const int64_t out_cols = swiglu ? N / 2 : N;
+  const Range in[4] = {range_of(x_q, T, K, K, 1), range_of(x_s, T, K / 32, K / 32, 1),
+                       range_of(w_q, (int64_t)G * N, K, K, 1), range_of(w_s, (int64_t)G * N, K / 32, K / 32, 1)};
+  const Range outs[4] = {out ? range_of(out, T, out_cols, out_cols, 2) : Range{0, 0},
+                         preact ? range_of(preact, T, N, N, 2) : Range{0, 0},
+                         out_q ? range_of(out_q, T, out_cols, out_cols, 1) : Range{0, 0},
+                         out_s ? range_of(out_s, T, out_cols / 32, out_cols / 32, 1) : Range{0, 0}};
+  for (const Range& o : outs) {
+    for (const Range& i : in)
+      if (overlap(o, i)) return fail(SGE_ERR_ALIAS, "grouped_linear_fwd_mxfp8: outputs overlap inputs");
+  }
+  for (int a = 0; a < 4; ++a)
+    for (int b = a + 1; b < 4; ++b)
+      if (overlap(outs[a], outs[b])) return fail(SGE_ERR_ALIAS, "grouped_linear_fwd_mxfp8: outputs overlap");
+  if (T == 0 || N == 0) return ok();
+  sge::GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.a = static_cast<const uint8_t*>(x_q);
+  p.lda = K;
+  p.b = static_cast<const uint8_t*>(w_q);
+  p.ldb = K;
+  p.M = T;
+  p.N = N;
+  p.K = K;
+  p.b_group_stride = N * K;
+  p.a_mx = static_cast<const uint8_t*>(x_s);
+  p.a_mx_ld = K / 32;
+  p.b_mx = static_cast<const uint8_t*>(w_s);
+  p.b_mx_ld = K / 32;
+  p.b_mx_group_stride = N * (K / 32);
+  p.mx_aligned = 1;
+  p.alpha = alpha;
+  p.c = static_cast<uint16_t*>(out);
+  p.ldc = out_cols;
+  p.offsets = offsets;
+  p.G = G;
+  p.T = T;
+  p.probs = probs;
+  p.aux = static_cast<uint16_t*>(preact);
+  p.ld_aux = N;
+  p.F = N / 2;
+  p.q_out = static_cast<uint8_t*>(out_q);
+  p.s_out = static_cast<uint8_t*>(out_s);
+  p.ld_q = out_cols;
+  return hip_status(sge::launch_grouped_fwd_mx(p, epilogue, stream), "grouped fwd mxfp8 launch");
+}
+
 size_t sge_grouped_linear_bwd_workspace_size(int64_t T, int64_t K, int32_t G, int32_t epilogue) {
   (void)G;
   if (epilogue != SGE_EPI_DSCALED_SWIGLU || T <= 0 || K <= 0) return 0;

@@ -33,6 +33,28 @@ __device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
+// ------------------------------------------------------------------- MXFP8
+// E8M0 exponent of a block from its amax bit pattern (bf16 magnitude bits).
+__device__ __forceinline__ int mx_exponent(uint32_t amax_bits) {
+  if (amax_bits == 0) return -127;
+  const uint32_t f = amax_bits << 16;                  // as fp32 bits
+  const int be = (int)(f >> 23);                       // biased exponent (0 for subnormals)
+  int e;
+  if (be > 0) {
+    e = be - 127;
+  } else {
+    // subnormal: value = mant * 2^-149, floor(log2) = msb(mant) - 149
+    e = (31 - __builtin_clz(f & 0x7FFFFFu)) - 149;
+  }
+  int x = e - 8;
+  return x < -127 ? -127 : (x > 127 ? 127 : x);
+}
+
+// 2^-X as fp32 for X in [-127, 119] (always a normal number).
+__device__ __forceinline__ float pow2_neg(int x) {
+  return __builtin_bit_cast(float, (uint32_t)(127 - x) << 23);
+}
+
 // XOR swizzle of 16-byte chunks inside 128-byte LDS rows: rows r..r+7 (any 8
 // consecutive rows) and rows 8 apart both land on distinct chunks, so the MFMA
 // fragment reads and both tile-fill patterns are free of bank conflicts.

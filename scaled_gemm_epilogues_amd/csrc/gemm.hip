@@ -247,6 +247,7 @@ void gemm_kernel(const GemmParams p) {
   // ---------------------------------------------------------------- schedule
   int64_t m0, n0, row_end, k_begin = 0, k_end = p.K;
   const uint8_t* bptr = p.b;
+  const uint8_t* bmx = p.b_mx;                           // MXFP8: E8M0 scales of B (this group's)
   uint16_t* cptr = p.c;
   int nt;
   if constexpr (SCHED == S_DENSE) {
@@ -296,6 +297,7 @@ void gemm_kernel(const GemmParams p) {
     row_end = hi;
     n0 = (int64_t)nt * (EPI == E_SWIGLU ? BN / 2 : BN);
     bptr += (int64_t)g * p.b_group_stride * ES;
+    if constexpr (FMT == F_MX || FMT == F_MXU) bmx += (int64_t)g * p.b_mx_group_stride;
   } else {
     // Groups differ in length (their contraction), so every XCD takes an equal contiguous
     // slice of each group's tiles: balanced XCDs, and an XCD's concurrent tiles still share
@@ -376,9 +378,10 @@ void gemm_kernel(const GemmParams p) {
         if (piece >= kPieces) break;
         const bool is_a = piece < BM / 64;
         const int r = (is_a ? piece : piece - BM / 64) * 64 + lane;
-        const int64_t row = (is_a ? m0 : n0) + r;
+        // B rows follow the tile's row map (the SwiGLU gate/up interleave)
+        const int64_t row = is_a ? m0 + r : (EPI == E_SWIGLU ? swrows(n0, r) : n0 + r);
         const bool ok = row < (is_a ? row_end : b_rows) && blk0 < nblk;
-        const uint8_t* base = is_a ? p.a_mx : p.b_mx;
+        const uint8_t* base = is_a ? p.a_mx : bmx;
         const int64_t ld = is_a ? p.a_mx_ld : p.b_mx_ld;
         const int64_t rows_total = is_a ? (SCHED == S_GROUP_M ? p.T : p.M) : b_rows;
         const i32x4 rs = make_rsrc4(base + blk0, rows_total * ld - blk0);
@@ -416,10 +419,11 @@ void gemm_kernel(const GemmParams p) {
       }
 #pragma unroll
       for (int j = 0; j < WNF; ++j) {
-        const int64_t row = n0 + wn * WN + j * 32 + (lane & 31);
+        const int rr = wn * WN + j * 32 + (lane & 31);
+        const int64_t row = EPI == E_SWIGLU ? swrows(n0, rr) : n0 + rr;
         uint32_t v = 0x7F7F7F7Fu;
         if (row < b_rows) {
-          const uint8_t* s = p.b_mx + row * p.b_mx_ld + blk0;
+          const uint8_t* s = bmx + row * p.b_mx_ld + blk0;
           v = 0;
 #pragma unroll
           for (int e = 0; e < 4; ++e) v |= (blk0 + e < nblk ? (uint32_t)s[e] : 127u) << (8 * e);
@@ -651,18 +655,27 @@ void gemm_kernel(const GemmParams p) {
   } else if constexpr (EPI == E_SWIGLU) {
     // Staged like E_STORE: alpha*acc (each wave column holds WN/2 gate columns a, then the
     // matching WN/2 up columns b) goes to LDS, then each thread takes 8 consecutive output
-    // columns of one row: y = p * silu(a) * b, and 16-byte stores of y and of the two
+    // columns of one row: y = p * silu(a) * b, and 16-byte stores of bf16 y and of the two
     // halves of the saved pre-activation. The granule XOR includes the wave column, so the
-    // 16 chunks of a row (4 per wave column) read 16 distinct bank groups.
+    // 16 chunks of a row read 16 distinct bank groups.
+    // With q_out, y is also emitted as MXFP8 rowwise (E4M3 bytes plus one E8M0 exponent per
+    // 32 columns): the MX quantization of bf16(y), exactly as the standalone quantizer would
+    // produce it from the bf16 output (four adjacent lanes hold one 32-column block).
     static_assert(BM == 2 * WM && A_BYTES + B_BYTES == 64 * BN * 4, "epilogue staging assumes 2 wave rows");
-    static_assert(WNF == 2 && WN == 64, "one gate and one up fragment per wave column");
+    static_assert(WNF % 2 == 0 && BN / 16 == 16, "gate and up fragments per wave column; 16 chunks per row");
     typedef int v4i __attribute__((__vector_size__(4 * sizeof(int))));
-    const __amdgpu_buffer_rsrc_t ry = make_rsrc(cptr + m0 * p.ldc, rows_left * p.ldc * 2);
+    const int64_t ybytes = cptr ? rows_left * p.ldc * 2 : 0;
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(cptr ? cptr + m0 * p.ldc : cptr, ybytes);
     const int64_t hbytes = p.aux ? rows_left * p.ld_aux * 2 : 0;
     const __amdgpu_buffer_rsrc_t rha = make_rsrc(p.aux ? p.aux + m0 * p.ld_aux : p.aux, hbytes);
     const __amdgpu_buffer_rsrc_t rhb = make_rsrc(p.aux ? p.aux + m0 * p.ld_aux + p.F : p.aux, hbytes - p.F * 2);
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.probs + m0, rows_left * 4);
+    const bool mxq = p.q_out != nullptr;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(mxq ? p.q_out + m0 * p.ld_q : p.q_out, mxq ? rows_left * p.ld_q : 0);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(mxq ? p.s_out + m0 * (p.ld_q / 32) : p.s_out,
+                                                mxq ? rows_left * (p.ld_q / 32) : 0);
     constexpr int kChunks = BN / 16;                       // 8-column output chunks per row
+    constexpr int kCpw = WN / 16, kGpw = WN / 4;           // chunks, granules per wave column
     constexpr int kIters = 128 * kChunks / (NWAVES * 64);
     auto wsw = [](int w) { return (w & 1) | ((w & 2) << 2); };
     float* stage = reinterpret_cast<float*>(wm ? lds1 : lds0);
@@ -685,7 +698,7 @@ void gemm_kernel(const GemmParams p) {
       }
       __syncthreads();
       float pr[kIters];
-      int oy[kIters], oh[kIters];
+      int oy[kIters], oh[kIters], oq[kIters], os[kIters];
 #pragma unroll
       for (int it = 0; it < kIters; ++it) {
         const int id = it * NWAVES * 64 + threadIdx.x;
@@ -696,16 +709,18 @@ void gemm_kernel(const GemmParams p) {
         const bool ok = rok && n < n_end;
         oy[it] = ok ? (int)(((int64_t)brow * p.ldc + n) * 2) : (int)kOOB;
         oh[it] = ok ? (int)(((int64_t)brow * p.ld_aux + n) * 2) : (int)kOOB;
+        oq[it] = ok ? (int)((int64_t)brow * p.ld_q + n) : (int)kOOB;
+        os[it] = (ok && (c & 3) == 0) ? (int)((int64_t)brow * (p.ld_q / 32) + (n >> 5)) : (int)kOOB;
         pr[it] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, rok ? brow * 4 : (int)kOOB, 0, 0));
       }
 #pragma unroll
       for (int it = 0; it < kIters; ++it) {
         const int id = it * NWAVES * 64 + threadIdx.x;
         const int rp_ = id / kChunks, c = id % kChunks;
-        const int rr = rp_ & 63, wc = c >> 2, cc = c & 3;
+        const int rr = rp_ & 63, wc = c / kCpw, cc = c % kCpw;
         const float* row = reinterpret_cast<const float*>(rp_ >= 64 ? lds1 : lds0) + rr * BN;
         const int x = (rr & 15) ^ wsw(wc);
-        const int ga = wc * 16 + 2 * cc, gb = ga + 8;      // gate and up granules of this chunk
+        const int ga = wc * kGpw + 2 * cc, gb = ga + kGpw / 2;   // gate and up granules of this chunk
         const float4 a0 = *reinterpret_cast<const float4*>(row + ((ga ^ x) << 2));
         const float4 a1 = *reinterpret_cast<const float4*>(row + (((ga + 1) ^ x) << 2));
         const float4 b0 = *reinterpret_cast<const float4*>(row + ((gb ^ x) << 2));
@@ -725,6 +740,30 @@ void gemm_kernel(const GemmParams p) {
         __builtin_amdgcn_raw_buffer_store_b128(va, rha, oh[it], 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(vb, rhb, oh[it], 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(vy, ry, oy[it], 0, 0);
+        if (mxq) {
+          // block amax over the bf16 magnitudes of 4 adjacent lanes (one 32-column block)
+          uint32_t m = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t w = (uint32_t)vy[e], lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
+            m = lo > m ? lo : m;
+            m = hi > m ? hi : m;
+          }
+          uint32_t o = __shfl_xor(m, 1, 64);
+          m = o > m ? o : m;
+          o = __shfl_xor(m, 2, 64);
+          m = o > m ? o : m;
+          const int X = mx_exponent(m);
+          const float sc = pow2_neg(X);
+          uint32_t qb[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            qb[e] = e4m3x2(bf16_lo((uint32_t)vy[e]) * sc, bf16_hi((uint32_t)vy[e]) * sc);
+          typedef int v2i_ __attribute__((__vector_size__(2 * sizeof(int))));
+          const v2i_ qv = {(int)(qb[0] | (qb[1] << 16)), (int)(qb[2] | (qb[3] << 16))};
+          __builtin_amdgcn_raw_buffer_store_b64(qv, rq, oq[it], 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b8((char)(X + 127), rs, os[it], 0, 0);
+        }
       }
       if (pass == 0) __syncthreads();                      // stage reused by the second pass
     }
@@ -871,6 +910,11 @@ hipError_t launch_gemm(const GemmParams& p, int fmt, bool a_kmaj, bool b_kmaj, h
 hipError_t launch_grouped_fwd(const GemmParams& p, int epilogue, hipStream_t s) {
   if (epilogue == E_SWIGLU) return launch_tile<F_BF16, true, true, E_SWIGLU, S_GROUP_M>(p, s);
   return launch_tile<F_BF16, true, true, E_STORE, S_GROUP_M>(p, s);
+}
+
+hipError_t launch_grouped_fwd_mx(const GemmParams& p, int epilogue, hipStream_t s) {
+  if (epilogue == E_SWIGLU) return launch_tile<F_MX, true, true, E_SWIGLU, S_GROUP_M>(p, s);
+  return launch_tile<F_MX, true, true, E_STORE, S_GROUP_M>(p, s);
 }
 
 hipError_t launch_grouped_dgrad(const GemmParams& p, int epilogue, hipStream_t s) {

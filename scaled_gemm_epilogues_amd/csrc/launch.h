@@ -39,10 +39,16 @@ struct GemmParams {
   int64_t ld_aux_out;
   float* dp_part;             // dSwiGLU: per-column-tile partial sums [parts][T]
   int64_t F;                  // SwiGLU half width
+  int64_t b_mx_group_stride;  // grouped MXFP8: bytes from W_g's scales to W_{g+1}'s
+  uint8_t* q_out;             // SwiGLU with MXFP8 output: E4M3 [T][ld_q] (or NULL)
+  uint8_t* s_out;             //   and its E8M0 scales [T][ld_q / 32]
+  int64_t ld_q;
 };
 
 hipError_t launch_gemm(const GemmParams& p, int fmt, bool a_kmaj, bool b_kmaj, hipStream_t s);
 hipError_t launch_grouped_fwd(const GemmParams& p, int epilogue, hipStream_t s);
+// The same with MXFP8 operands (scale rows dword-aligned: K % 128 == 0).
+hipError_t launch_grouped_fwd_mx(const GemmParams& p, int epilogue, hipStream_t s);
 hipError_t launch_grouped_dgrad(const GemmParams& p, int epilogue, hipStream_t s);
 hipError_t launch_grouped_wgrad(const GemmParams& p, hipStream_t s);
 int gemm_tile_n();

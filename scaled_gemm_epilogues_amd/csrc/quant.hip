@@ -168,27 +168,6 @@ hipError_t launch_quantize_fp8(const uint16_t* src, int64_t rows, int64_t cols, 
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------------- MXFP8
-// E8M0 exponent of a block from its amax bit pattern (bf16 magnitude bits).
-__device__ __forceinline__ int mx_exponent(uint32_t amax_bits) {
-  if (amax_bits == 0) return -127;
-  const uint32_t f = amax_bits << 16;                  // as fp32 bits
-  const int be = (int)(f >> 23);                       // biased exponent (0 for subnormals)
-  int e;
-  if (be > 0) {
-    e = be - 127;
-  } else {
-    // subnormal: value = mant * 2^-149, floor(log2) = msb(mant) - 149
-    e = (31 - __builtin_clz(f & 0x7FFFFFu)) - 149;
-  }
-  int x = e - 8;
-  return x < -127 ? -127 : (x > 127 ? 127 : x);
-}
-
-// 2^-X as fp32 for X in [-127, 119] (always a normal number).
-__device__ __forceinline__ float pow2_neg(int x) {
-  return __builtin_bit_cast(float, (uint32_t)(127 - x) << 23);
-}
 
 // MX tile: 128 rows x 64 columns (16 KB of bf16 read once). 256 threads; thread t owns
 // columns 8*(t%8)..+7 of rows t/8 + 32k, k = 0..3. Rowwise blocks are 4 consecutive threads

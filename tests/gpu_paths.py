@@ -125,3 +125,34 @@ def run_grouped_mlp(inp, with_backward=True):
         res.update(dh=dh, dp=dp, dw2=dw2, dx=dx, dw1=dw1)
     torch.cuda.synchronize()
     return res
+
+
+def run_grouped_mlp_fwd_mx(inp):
+    """MXFP8 grouped MLP forward: quantize x, W1, W2 rowwise; fc1 + scaled SwiGLU emitting y as
+    bf16 and as MXFP8 rowwise; fc2 on the MXFP8 y."""
+    X, W1, W2 = dev_bf16(inp["x"]), dev_bf16(inp["w1"]), dev_bf16(inp["w2"])
+    P = torch.from_numpy(inp["p"]).cuda()
+    T, H = X.shape
+    G, N1, _ = W1.shape
+    F = N1 // 2
+    offs = torch.empty(1, G + 1, dtype=torch.int64, device="cuda")
+    err = torch.empty(1, dtype=torch.int32, device="cuda")
+    sge.splits_to_offsets(torch.from_numpy(inp["splits"]).cuda(), [1], offs, expected_total=T, err_flag=err)
+    base = offs[0]
+    qx = quant_mx(X, col=False)
+    qw1 = quant_mx(W1.reshape(G * N1, H), col=False)
+    qw2 = quant_mx(W2.reshape(G * H, F), col=False)
+    h = torch.empty(T, N1, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty(T, F, dtype=torch.bfloat16, device="cuda")
+    yq = torch.empty(T, F, dtype=torch.uint8, device="cuda")
+    ys = torch.empty(T, F // 32, dtype=torch.uint8, device="cuda")
+    out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    sge.grouped_linear_fwd_mxfp8(qx["q_row"], qx["s_row"], qw1["q_row"].reshape(G, N1, H),
+                                 qw1["s_row"].reshape(G, N1, H // 32), base, out=y, epilogue=sge.EPI_SCALED_SWIGLU,
+                                 probs=P, preact=h, out_q=yq, out_s=ys)
+    sge.grouped_linear_fwd_mxfp8(yq, ys, qw2["q_row"].reshape(G, H, F), qw2["s_row"].reshape(G, H, F // 32), base,
+                                 out=out)
+    y_unfused = quant_mx(y, col=False)                    # the standalone quantizer on the bf16 y
+    torch.cuda.synchronize()
+    return {"err": err, "qx": qx, "qw1": qw1, "qw2": qw2, "h": h, "y": y, "yq": yq, "ys": ys, "out": out,
+            "y_unfused": y_unfused}

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol(sge):
     lib = ctypes.CDLL(sge.library_path())
     for name in _declared():
         assert hasattr(lib, name), name
-    assert sge.abi_version() == 1
+    assert sge.abi_version() == 2
 
 
 def test_status_strings(sge):
@@ -144,3 +144,32 @@ def test_grouped_validation_errors(sge):
     st = lib.sge_grouped_linear_bwd(FAKE, FAKE * 8, FAKE * 64, 8, 1000, 256, 2048, FAKE * 1024, 1.0, 2,
                                     FAKE * 2048, FAKE * 4096, FAKE * 8192, FAKE * 9000, None, None, None, 0, None)
     assert st == sge.ERR_WORKSPACE
+
+
+def test_grouped_mxfp8_validation_errors(sge):
+    f = sge._lib.sge_grouped_linear_fwd_mxfp8
+    G, T, N, K = 4, 100, 512, 256
+    x_q, x_s, w_q, w_s, offs, probs = FAKE, FAKE * 64, FAKE * 128, FAKE * 4096, FAKE * 8192, FAKE * 8300
+    y, h, yq, ys = FAKE * 10000, FAKE * 20000, FAKE * 30000, FAKE * 40000
+    swiglu = sge.EPI_SCALED_SWIGLU
+    ok_args = (x_q, x_s, w_q, w_s, G, T, N, K, offs, 1.0, swiglu, probs, y, h, yq, ys, None)
+    assert f(*((None,) + ok_args[1:])) == sge.ERR_NULL                  # x_q
+    args = list(ok_args); args[14] = None
+    assert f(*args) == sge.ERR_NULL                                       # out_q without out_s
+    args = list(ok_args); args[12] = None; args[14] = None; args[15] = None
+    assert f(*args) == sge.ERR_NULL                                       # no output at all
+    args = list(ok_args); args[11] = None
+    assert f(*args) == sge.ERR_NULL                                       # SwiGLU needs probs
+    args = list(ok_args); args[7] = 160
+    assert f(*args) == sge.ERR_SHAPE                                      # K % 128
+    args = list(ok_args); args[6] = 136
+    assert f(*args) == sge.ERR_SHAPE                                      # SwiGLU needs N % 256
+    args = list(ok_args); args[10] = sge.EPI_NONE
+    assert f(*args) == sge.ERR_ARG                                        # quantized output needs SwiGLU
+    args = list(ok_args); args[12] = FAKE + 8
+    assert f(*args) == sge.ERR_ALIGN
+    args = list(ok_args); args[14] = x_q
+    assert f(*args) == sge.ERR_ALIAS                                      # out_q over x_q
+    args = list(ok_args); args[15] = y
+    assert f(*args) == sge.ERR_ALIAS                                      # out_s over out
+
