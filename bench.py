@@ -186,6 +186,30 @@ def build_grouped(torch, sge, wl, inp):
              "fc2_wgrad": 2 * T * H * F, "fc1_dgrad": 2 * T * N1 * H, "fc1_wgrad": 2 * T * N1 * H}
 
     base = offs[0]
+    if wl["fmt"] == "mxfp8":
+        # forward on MXFP8 operands: x and both weights quantized rowwise each step, fc1's
+        # scaled SwiGLU emits its output as MXFP8 for fc2 (and the bf16 pre-activation)
+        u8 = dict(dtype=torch.uint8, device="cuda")
+        qx, sx = torch.empty(T, H, **u8), torch.empty(T, H // 32, **u8)
+        qw1, sw1 = torch.empty(G * N1, H, **u8), torch.empty(G * N1, H // 32, **u8)
+        qw2, sw2 = torch.empty(G * H, F, **u8), torch.empty(G * H, F // 32, **u8)
+        qy, sy = torch.empty(T, F, **u8), torch.empty(T, F // 32, **u8)
+        W1f, W2f = W1.reshape(G * N1, H), W2.reshape(G * H, F)
+        flops = {"fc1_fwd": 2 * T * N1 * H, "fc2_fwd": 2 * T * H * F}
+        hbm = {"quant_x": T * H * 3 + T * H // 32, "quant_w1": G * N1 * H * 3 + G * N1 * H // 32,
+               "quant_w2": G * H * F * 3 + G * H * F // 32}
+        launches = [
+            ("offsets", lambda: sge.splits_to_offsets(splits, [1, H], offs)),
+            ("quant_x", lambda: sge.quantize_mxfp8(X, q_row=qx, s_row=sx)),
+            ("quant_w1", lambda: sge.quantize_mxfp8(W1f, q_row=qw1, s_row=sw1)),
+            ("quant_w2", lambda: sge.quantize_mxfp8(W2f, q_row=qw2, s_row=sw2)),
+            ("fc1_fwd", lambda: sge.grouped_linear_fwd_mxfp8(
+                qx, sx, qw1.view(G, N1, H), sw1.view(G, N1, H // 32), base, out=None,
+                epilogue=sge.EPI_SCALED_SWIGLU, probs=P, preact=h, out_q=qy, out_s=sy)),
+            ("fc2_fwd", lambda: sge.grouped_linear_fwd_mxfp8(qy, sy, qw2.view(G, H, F), sw2.view(G, H, F // 32),
+                                                             base, out=out)),
+        ]
+        return launches, flops, hbm
     launches = [
         ("offsets", lambda: sge.splits_to_offsets(splits, [1, H], offs)),
         ("fc1_fwd", lambda: sge.grouped_linear_fwd(X, W1, base, y, epilogue=sge.EPI_SCALED_SWIGLU, probs=P,
@@ -242,6 +266,23 @@ def cpu_baseline(wl, inp, target_s):
         flops = (3 if bwd else 1) * 2 * rows * N * K
         sample = (f"first {rows} of {M} token rows through {'/'.join(wl['passes'])} (quantizers included)"
                   + (f", mean of {reps} runs" if reps > 1 else ""))
+    elif wl["fmt"] == "mxfp8":
+        T = inp["x"].shape[0]
+        tok = 256
+        while True:
+            t0 = time.perf_counter()
+            # first `tok` tokens, all routed to expert 0 (its weights only are quantized)
+            grouped.grouped_mlp_fwd_mxfp8(inp["x"][:tok], inp["w1"][:1], inp["w2"][:1], inp["p"][:tok],
+                                          np.array([0, tok], np.int64))
+            dt = time.perf_counter() - t0
+            if dt >= target_s / 4 or tok >= T:
+                break
+            tok = min(T, tok * 4)
+        H = inp["x"].shape[1]
+        N1 = inp["w1"].shape[1]
+        flops = 2 * tok * N1 * H + 2 * tok * H * (N1 // 2)
+        sample = (f"first {tok} of {T} tokens through the MXFP8 grouped MLP forward with one expert "
+                  "(quantization of that expert's weights included)")
     else:
         T = inp["x"].shape[0]
         tok = 256

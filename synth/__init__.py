@@ -94,7 +94,7 @@ def grouped(T, G, hidden, ffn, *, seed=0, x_std=1.0, w_std=0.02, dout_std=1e-2, 
     }
 
 
-# The five workloads (sizes, distributions, alpha) of the fused scaled linear.
+# The workloads (sizes, distributions, alpha) of the fused scaled linear.
 WORKLOADS = {
     "bf16_fwd_256x512x512": dict(kind="dense", fmt="bf16", M=256, N=512, K=512, alpha=0.5,
                                  passes=("fwd",)),
@@ -107,6 +107,9 @@ WORKLOADS = {
                                          passes=("fwd", "dgrad", "wgrad")),
     "grouped_swiglu_mlp_T65536_G8": dict(kind="grouped", fmt="bf16", T=65536, G=8, hidden=2048,
                                          ffn=2048, alpha=1.0),
+    # the same grouped MLP forward on MXFP8 operands, fc1's activation quantized for fc2
+    "mxfp8_grouped_swiglu_mlp_fwd_T65536_G8": dict(kind="grouped", fmt="mxfp8", T=65536, G=8, hidden=2048,
+                                                   ffn=2048, alpha=1.0, passes=("fwd",)),
 }
 
 

@@ -12,8 +12,8 @@ import synth
 from oracle import grouped, linear, offsets, quant
 from oracle.codecs import bf16_to_f64
 
-from .gpu_paths import run_dense, run_grouped_mlp
-from .helpers import TAU_BF16, TAU_FP8, assert_close, host_f64, host_u8
+from .gpu_paths import run_dense, run_grouped_mlp, run_grouped_mlp_fwd_mx
+from .helpers import TAU_BF16, TAU_FP8, assert_close, assert_mx_dequant_close, host_f64, host_u8
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -143,3 +143,32 @@ def test_grouped_workload_full_size_sampled():
         ref_dw1 = dhk.T @ xg                                          # dW1_g[rows1, :]
         assert_close(host_f64(got["dw1"][g][torch.from_numpy(rows1).cuda()]), ref_dw1, TAU_BF16,
                      what=f"dw1 g{g}", **kw)
+
+
+def test_grouped_mxfp8_forward_full_size_sampled():
+    name = "mxfp8_grouped_swiglu_mlp_fwd_T65536_G8"
+    print(f"case full-size {name}", flush=True)
+    inp = synth.workload_inputs(name, seed=0)
+    got = run_grouped_mlp_fwd_mx(inp)
+    assert int(got["err"].item()) == 0
+    # the fused activation + group quantize equals the standalone quantizer, over the whole tensor
+    assert np.array_equal(host_u8(got["yq"]), host_u8(got["y_unfused"]["q_row"]))
+    assert np.array_equal(host_u8(got["ys"]), host_u8(got["y_unfused"]["s_row"]))
+    base = offsets.base_offsets(inp["splits"])
+    sizes = np.diff(base)
+    nonempty = [g for g in range(len(sizes)) if sizes[g] > 0]
+    rng = np.random.default_rng(11)
+    # the oracle quantizes a group's whole weights; three groups keep it to seconds
+    for g in sorted({nonempty[0], int(np.argmax(sizes)), nonempty[-1]}):
+        lo, hi = int(base[g]), int(base[g + 1])
+        toks = np.array(sorted({lo, hi - 1} | set(rng.integers(lo, hi, size=min(6, hi - lo)).tolist())))
+        ref = grouped.grouped_mlp_fwd_mxfp8(inp["x"][toks], inp["w1"][g:g + 1], inp["w2"][g:g + 1], inp["p"][toks],
+                                            np.array([0, len(toks)]))
+        tt = torch.from_numpy(toks).cuda()
+        kw = dict(rel_tight=2.0 ** -3, abs_tight=0.1)
+        assert_close(host_f64(got["h"][tt]), ref["h"], TAU_FP8, what=f"h g{g}", **kw)
+        assert_close(host_f64(got["y"][tt]), ref["y"], TAU_FP8, what=f"y g{g}", **kw)
+        y_deq = quant.mx_dequantize(host_u8(got["yq"][tt]), host_u8(got["ys"][tt]))
+        assert_mx_dequant_close(y_deq, quant.mx_dequantize(ref["y_q"], ref["y_s"]), what=f"y (MXFP8) g{g}")
+        assert_close(host_f64(got["out"][tt]), ref["out"], TAU_FP8, what=f"out g{g}", **kw)
+
