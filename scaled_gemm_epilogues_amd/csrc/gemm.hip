@@ -600,6 +600,20 @@ void gemm_kernel(const GemmParams p) {
     constexpr int kChunks = BN / 8;                        // 8-column chunks per row
     constexpr int kIters = 128 * kChunks / (NWAVES * 64);  // chunks per thread per pass
     float* stage = reinterpret_cast<float*>(wm ? lds1 : lds0);
+    // The residual of both passes is requested first: its HBM latency overlaps the staging.
+    v4i res[2][kIters];
+    int offs[2][kIters];
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass)
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) {
+        const int id = it * NWAVES * 64 + threadIdx.x;
+        const int rp = id / kChunks, c = id % kChunks;     // row of the pass (0..127), chunk
+        const int brow = (rp >> 6) * WM + pass * (WM / 2) + (rp & 63);
+        const int64_t n = n0 + c * 8;
+        offs[pass][it] = (m0 + brow < row_end && n < n_end) ? (int)(((int64_t)brow * p.ldc + n) * 2) : (int)kOOB;
+        if (p.accumulate) res[pass][it] = __builtin_amdgcn_raw_buffer_load_b128(rc, offs[pass][it], 0, 0);
+      }
     __syncthreads();                                       // every wave is done with the LDS stages
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
@@ -618,17 +632,6 @@ void gemm_kernel(const GemmParams p) {
           }
       }
       __syncthreads();
-      v4i res[kIters];
-      int offs[kIters];
-#pragma unroll
-      for (int it = 0; it < kIters; ++it) {
-        const int id = it * NWAVES * 64 + threadIdx.x;
-        const int rp = id / kChunks, c = id % kChunks;     // row of the pass (0..127), chunk
-        const int brow = (rp >> 6) * WM + pass * (WM / 2) + (rp & 63);
-        const int64_t n = n0 + c * 8;
-        offs[it] = (m0 + brow < row_end && n < n_end) ? (int)(((int64_t)brow * p.ldc + n) * 2) : (int)kOOB;
-        if (p.accumulate) res[it] = __builtin_amdgcn_raw_buffer_load_b128(rc, offs[it], 0, 0);
-      }
 #pragma unroll
       for (int it = 0; it < kIters; ++it) {
         const int id = it * NWAVES * 64 + threadIdx.x;
@@ -639,7 +642,7 @@ void gemm_kernel(const GemmParams p) {
         const float4 hi = *reinterpret_cast<const float4*>(row + (((2 * c + 1) ^ sw) << 2));
         float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         if (p.accumulate) {
-          const v4i r4 = res[it];
+          const v4i r4 = res[pass][it];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             v[2 * e] = bf16_lo((uint32_t)r4[e]) + v[2 * e];
@@ -648,7 +651,7 @@ void gemm_kernel(const GemmParams p) {
         }
         const v4i w = {(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3]), (int)pack_bf16x2(v[4], v[5]),
                        (int)pack_bf16x2(v[6], v[7])};
-        __builtin_amdgcn_raw_buffer_store_b128(w, rc, offs[it], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(w, rc, offs[pass][it], 0, 0);
       }
       if (pass == 0) __syncthreads();                      // stage reused by the second pass
     }
