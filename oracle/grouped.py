@@ -21,7 +21,8 @@ Readings where the page is silent:
 import numpy as np
 
 from .codecs import bf16_to_f64, f64_to_bf16
-from .quant import mx_dequantize, mxfp8_rowwise
+from .quant import (MX_TOKEN_ALIGN, mx_dequantize, mx_group_layout, mxfp8_colwise,
+                    mxfp8_colwise_grouped, mxfp8_rowwise)
 
 
 def _groups(base):
@@ -154,3 +155,70 @@ def grouped_mlp_fwd_mxfp8(x_bits, w1_bits, w2_bits, p, base):
     return {"h": h, "y": y, "y_bits": y_bits, "y_q": y_q, "y_s": y_s, "out": out,
             "y_value": bf16_to_f64(y_bits)}
 
+
+
+def grouped_linear_dgrad_mxfp8(dy_bits, w_bits, base, alpha=1.0):
+    """dgrad of a grouped linear on MXFP8 operands: g[t] = alpha * dy_hat[t] @ W_hat_g.
+
+    The contraction runs over the layer's output features N, so both operands carry blocks
+    of 32 along N: dy [T, N] is quantized rowwise, every W_g [N, K] columnwise (its copy
+    blocked along N, ``mxfp8_colwise``). Blocks never cross experts (N % 32 == 0).
+    dy_bits [T, N], w_bits [G, N, K] (bf16 bit patterns) -> [T, K] fp64.
+    """
+    w_bits = np.asarray(w_bits, np.uint16)
+    dy_hat = mx_dequantize(*mxfp8_rowwise(dy_bits))
+    w_hat = np.stack([mx_dequantize(*mxfp8_colwise(w_bits[g])).T for g in range(w_bits.shape[0])])
+    return grouped_linear_dgrad(dy_hat, w_hat, base, alpha)
+
+
+def grouped_linear_wgrad_mxfp8(dy_bits, x_bits, base, alpha=1.0, align=MX_TOKEN_ALIGN):
+    """wgrad of a grouped linear on MXFP8 operands: dW_g = alpha * sum_{t in g} dy_hat[t]^T x_hat[t].
+
+    The contraction runs over the tokens of each group, so dy [T, N] and x [T, K] are both
+    quantized in blocks of 32 along the tokens of each group (``mxfp8_colwise_grouped``);
+    the zero padding between groups adds nothing. Returns [G, N, K] fp64 (zero for an
+    empty group).
+    """
+    dy_bits = np.asarray(dy_bits, np.uint16)
+    T = dy_bits.shape[0]
+    c, pad = mx_group_layout(base, T, align)
+    ld = max(int(pad[-1]), align)
+    a = mx_dequantize(*mxfp8_colwise_grouped(dy_bits, c, pad, ld))      # [N, ld]
+    b = mx_dequantize(*mxfp8_colwise_grouped(x_bits, c, pad, ld))       # [K, ld]
+    G = len(c) - 1
+    out = np.zeros((G, a.shape[0], b.shape[0]), np.float64)
+    for g in range(G):
+        lo, hi = int(pad[g]), int(pad[g + 1])
+        out[g] = alpha * (a[:, lo:hi] @ b[:, lo:hi].T)
+    return out
+
+
+def grouped_mlp_bwd_mxfp8(x_bits, w1_bits, w2_bits, p, base, dout_bits, fwd=None):
+    """Backward of ``grouped_mlp_fwd_mxfp8`` on MXFP8 operands, given dL/dout (bf16 bits).
+
+    "Activation + GroupedLinear Fusion for MOE and other MOE optimizations" (Sequence
+    Diagram, backward): the activation backward returns the quantized activation gradient
+    for FC1's dgrad, the same gradient unquantized for FC1's wgrad, and the gradient of the
+    scales. Every GEMM operand is MXFP8 blocked along that GEMM's contraction dim:
+
+    1. fc2 dgrad: gy = dout_hat @ W2_hat_g (``grouped_linear_dgrad_mxfp8``);
+    2. dh, dp = ``scaled_swiglu_bwd(gy, h, p)`` with h the pre-activation as the forward
+       saved it (bf16); dh is rounded to bf16, the dtype the gradient has unquantized;
+    3. fc2 wgrad: dW2 from dout and the forward's bf16 activation y, token-blocked;
+    4. fc1 dgrad: dx from the bf16 dh (rowwise) and W1 blocked along 2F;
+    5. fc1 wgrad: dW1 from the bf16 dh and x, token-blocked.
+
+    Returns gy, dh (fp64), dh_bits, dh_q, dh_s (the rowwise MXFP8 of dh_bits), dp, dw2, dx, dw1.
+    """
+    if fwd is None:
+        fwd = grouped_mlp_fwd_mxfp8(x_bits, w1_bits, w2_bits, p, base)
+    h_saved = bf16_to_f64(f64_to_bf16(fwd["h"]))
+    gy = grouped_linear_dgrad_mxfp8(dout_bits, w2_bits, base)
+    dh, dp = scaled_swiglu_bwd(gy, h_saved, p)
+    dh_bits = f64_to_bf16(dh)
+    dh_q, dh_s = mxfp8_rowwise(dh_bits)
+    dw2 = grouped_linear_wgrad_mxfp8(dout_bits, fwd["y_bits"], base)
+    dx = grouped_linear_dgrad_mxfp8(dh_bits, w1_bits, base)
+    dw1 = grouped_linear_wgrad_mxfp8(dh_bits, x_bits, base)
+    return {"gy": gy, "dh": dh, "dh_bits": dh_bits, "dh_q": dh_q, "dh_s": dh_s, "dp": dp,
+            "dw2": dw2, "dx": dx, "dw1": dw1}

@@ -134,3 +134,65 @@ def mx_dequantize(q, s):
     R, C = q.shape
     sc = np.repeat(e8m0_decode(s), MX_BLOCK, axis=1)[:, :C]
     return e4m3_decode(q) * sc
+
+
+# ------------------------------------------- MXFP8 blocked along grouped tokens -----
+# A wgrad contracts over the tokens of one group, so its MXFP8 operands carry blocks of 32
+# along tokens. The pages quantize each group's slice of the grouped tensor as a tensor of
+# its own ("Activation + GroupedLinear Fusion for MOE and other MOE optimizations",
+# Description: the activation is followed by a group quantize; the split sizes travel with
+# it). The reading taken here: a group's first block starts at the group's first token, a
+# group whose length is not a multiple of 32 ends in a short block (its missing elements
+# count as zeros, which leave the block's amax unchanged), and in the stored operand each
+# group starts at a multiple of MX_TOKEN_ALIGN tokens, the space up to the next group
+# holding zero codes under all-zero blocks (scale byte 0).
+MX_TOKEN_ALIGN = 128
+
+
+def mx_group_layout(offsets, T, align=MX_TOKEN_ALIGN):
+    """Token ranges and aligned positions of the groups of a token-blocked MXFP8 operand.
+
+    offsets [G+1] are first made a non-decreasing sequence inside [0, T], the way every
+    grouped call reads them: ``c[0] = clip(offsets[0], 0, T)`` and
+    ``c[g] = max(c[g-1], min(offsets[g], T))``. Group g owns tokens ``c[g] .. c[g+1]-1``.
+    Its position in the stored operand is ``pad[g]``, with ``pad[0] = 0`` and
+    ``pad[g+1] = pad[g] + ceil((c[g+1] - c[g]) / align) * align``.
+    Returns (c, pad), int64 [G+1] each.
+    """
+    off = [int(v) for v in np.asarray(offsets, np.int64)]
+    c, pad = [], [0]
+    prev = 0
+    for v in off:
+        v = min(v, int(T))
+        prev = max(prev, v)
+        c.append(prev)
+    for g in range(len(off) - 1):
+        n = c[g + 1] - c[g]
+        pad.append(pad[g] + -(-n // align) * align)
+    return np.asarray(c, np.int64), np.asarray(pad, np.int64)
+
+
+def mxfp8_colwise_grouped(x_bits, c, pad, ld):
+    """MXFP8 of a bf16 matrix [T, C] with blocks of 32 along the tokens of each group.
+
+    Each group's rows ``c[g] .. c[g+1]-1``, followed by zero rows up to its aligned length
+    ``pad[g+1] - pad[g]``, are quantized columnwise on their own (``mxfp8_colwise``) and stored
+    at columns ``pad[g] ..`` of the transposed operand. Returns (q [C, ld] uint8,
+    s [C, ld/32] uint8); columns from pad[G] to ld are left zero.
+    """
+    x = np.asarray(x_bits, np.uint16)
+    C = x.shape[1]
+    if ld % MX_BLOCK or ld < pad[-1]:
+        raise ValueError("ld must be a multiple of 32 and hold every group")
+    q = np.zeros((C, ld), np.uint8)
+    s = np.zeros((C, ld // MX_BLOCK), np.uint8)
+    for g in range(len(c) - 1):
+        n, L = int(c[g + 1] - c[g]), int(pad[g + 1] - pad[g])
+        if L == 0:
+            continue
+        rows = np.zeros((L, C), np.uint16)                  # bf16 +0 beyond the group's tokens
+        rows[:n] = x[c[g]:c[g + 1]]
+        qg, sg = mxfp8_colwise(rows)
+        q[:, pad[g]:pad[g] + L] = qg
+        s[:, pad[g] // MX_BLOCK:(pad[g] + L) // MX_BLOCK] = sg
+    return q, s

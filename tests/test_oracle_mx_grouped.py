@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import synth
-from oracle import grouped
+from oracle import grouped, quant
 from oracle.codecs import bf16_to_f64, f64_to_bf16
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
@@ -152,3 +152,173 @@ def test_mxfp8_grouped_forward_matches_brute_force():
     assert np.array_equal(got["y_q"], np.array(yq_ref, np.uint8))
     assert np.array_equal(got["y_s"], np.array(ys_ref, np.uint8))
     np.testing.assert_allclose(got["out"], np.array(out_ref), rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------ MXFP8 grouped backward (token-blocked) ------
+def test_mx_group_layout_hand_worked():
+    # splits 300, 0, 211, 9, 0, 40: aligned lengths 384, 0, 256, 128, 0, 128
+    base = [0, 300, 300, 511, 520, 520, 560]
+    c, pad = quant.mx_group_layout(base, 560)
+    assert c.tolist() == base
+    assert pad.tolist() == [0, 384, 384, 640, 768, 768, 896]
+    # out-of-order / out-of-range offsets are read as the grouped kernels read them
+    c, pad = quant.mx_group_layout([5, -3, 10, 7, 100], 20)
+    assert c.tolist() == [5, 5, 10, 10, 20]
+    assert pad.tolist() == [0, 0, 128, 128, 256]
+    c, pad = quant.mx_group_layout([0, 128, 256], 256)
+    assert pad.tolist() == [0, 128, 256]                      # aligned groups are not padded
+
+
+def _bf16_col(bits, j):
+    return [_bf16_value(b) for b in bits[:, j]]
+
+
+def _brute_token_blocks(bits, base, j):
+    """{(g, b): (X, codes)} of column j: blocks of 32 from each group's first token."""
+    col = _bf16_col(bits, j)
+    out = {}
+    for g in range(len(base) - 1):
+        lo, hi = base[g], base[g + 1]
+        for b, t0 in enumerate(range(lo, hi, 32)):
+            out[(g, b)] = _mx_block(col[t0:min(t0 + 32, hi)])
+    return out
+
+
+def test_mxfp8_colwise_grouped_vs_brute_force():
+    splits = [20, 0, 64, 7]
+    base = [0, 20, 20, 84, 91]
+    T, C = 91, 3
+    r = synth.streams(8)
+    x = synth.normal_bf16(r["x"], (T, C), 1.0, r["outliers_x"], outlier_rate=0.05)
+    c, pad = quant.mx_group_layout(base, T)
+    assert pad.tolist() == [0, 128, 128, 256, 384]
+    q, s = quant.mxfp8_colwise_grouped(x, c, pad, 512)
+    for j in range(C):
+        blocks = _brute_token_blocks(x, base, j)
+        want_q = np.zeros(512, np.uint8)
+        want_s = np.zeros(16, np.uint8)                        # all-zero blocks: X = -127
+        for (g, b), (X, codes) in blocks.items():
+            p0 = pad[g] + 32 * b
+            want_q[p0:p0 + len(codes)] = codes
+            want_s[p0 // 32] = X + 127
+        assert np.array_equal(q[j], want_q), j
+        assert np.array_equal(s[j], want_s), j
+    assert sum(splits) == T
+
+
+def _deq(X, codes):
+    table = dict(E4M3)
+    return [float(table[cd] * Fraction(2) ** X) if (cd & 0x7F) else 0.0 for cd in codes]
+
+
+def _token_blocked_values(bits, base, j):
+    """Dequantized column j, token by token, from the brute-force token blocks."""
+    vals = [0.0] * bits.shape[0]
+    for (g, b), (X, codes) in _brute_token_blocks(bits, base, j).items():
+        t0 = base[g] + 32 * b
+        for i, v in enumerate(_deq(X, codes)):
+            vals[t0 + i] = v
+    return vals
+
+
+def test_grouped_wgrad_mxfp8_vs_brute_force():
+    base = [0, 40, 40, 75]
+    T, N, K = 75, 2, 3
+    r = synth.streams(9)
+    dy = synth.normal_bf16(r["dy"], (T, N), 1e-2, r["outliers_dy"], outlier_rate=0.05)
+    x = synth.normal_bf16(r["x"], (T, K), 1.0)
+    got = grouped.grouped_linear_wgrad_mxfp8(dy, x, base, alpha=0.25)
+    dyv = [_token_blocked_values(dy, base, n) for n in range(N)]
+    xv = [_token_blocked_values(x, base, k) for k in range(K)]
+    for g in range(3):
+        for n in range(N):
+            for k in range(K):
+                ref = 0.25 * math.fsum(dyv[n][t] * xv[k][t] for t in range(base[g], base[g + 1]))
+                assert got[g, n, k] == pytest.approx(ref, rel=1e-12, abs=1e-300), (g, n, k)
+    assert not got[1].any()                                   # the empty group
+
+
+def test_grouped_dgrad_mxfp8_vs_brute_force():
+    base = [0, 3, 5]
+    T, G, N, K = 5, 2, 64, 3
+    r = synth.streams(10)
+    dy = synth.normal_bf16(r["dy"], (T, N), 1.0, r["outliers_dy"], outlier_rate=0.05)
+    w = synth.normal_bf16(r["w"], (G, N, K), 0.02, r["outliers_w"], outlier_rate=0.05)
+    got = grouped.grouped_linear_dgrad_mxfp8(dy, w, base, alpha=-0.5)
+    dyd, _, _ = _mx_rows([[_bf16_value(b) for b in row] for row in dy])
+    for g in range(G):
+        # W_g blocked along N: the rowwise blocks of its transpose
+        wtd, _, _ = _mx_rows([[_bf16_value(b) for b in w[g][:, k]] for k in range(K)])
+        for t in range(base[g], base[g + 1]):
+            for k in range(K):
+                ref = -0.5 * math.fsum(dyd[t][n] * wtd[k][n] for n in range(N))
+                assert got[t, k] == pytest.approx(ref, rel=1e-12, abs=1e-300), (t, k)
+
+
+def test_single_aligned_group_wgrad_equals_dense_mx_wgrad():
+    T, N, K = 256, 64, 96
+    r = synth.streams(11)
+    dy = synth.normal_bf16(r["dy"], (T, N), 1.0)
+    x = synth.normal_bf16(r["x"], (T, K), 1.0)
+    got = grouped.grouped_linear_wgrad_mxfp8(dy, x, [0, T])[0]
+    ref = quant.mx_dequantize(*quant.mxfp8_colwise(dy)) @ quant.mx_dequantize(*quant.mxfp8_colwise(x)).T
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-15)
+
+
+def test_mxfp8_grouped_backward_matches_brute_force():
+    T, G, H, F = 6, 2, 32, 32
+    splits = [4, 2]
+    base = [0, 4, 6]
+    inp = synth.grouped(T, G, H, F, seed=6, splits=splits)
+    got = grouped.grouped_mlp_bwd_mxfp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base, inp["dout"])
+
+    bits = lambda m: [[_bf16_value(b) for b in r] for r in m]   # noqa: E731
+    xd, _, _ = _mx_rows(bits(inp["x"]))
+    doutd, _, _ = _mx_rows(bits(inp["dout"]))
+    grp = [0, 0, 0, 0, 1, 1]
+    h_bits, y_bits, dh_bits, dh_q, dh_s, dp = [], [], [], [], [], []
+    for t in range(T):
+        g = grp[t]
+        w1d, _, _ = _mx_rows(bits(inp["w1"][g]))
+        h = [math.fsum(xd[t][k] * w1d[n][k] for k in range(H)) for n in range(2 * F)]
+        hb = [_bf16_nearest_bits(v) for v in h]
+        pt = float(inp["p"][t])
+        y = [pt * (h[j] / (1 + math.exp(-h[j]))) * h[F + j] for j in range(F)]
+        y_bits.append([_bf16_nearest_bits(v) for v in y])
+        # fc2 dgrad: W2_g [H, F] blocked along H (rowwise blocks of its transpose)
+        w2t, _, _ = _mx_rows([[_bf16_value(b) for b in inp["w2"][g][:, f]] for f in range(F)])
+        gy = [math.fsum(doutd[t][n] * w2t[f][n] for n in range(H)) for f in range(F)]
+        a = [_bf16_value(b) for b in hb[:F]]
+        bb = [_bf16_value(b) for b in hb[F:]]
+        sg = [1 / (1 + math.exp(-v)) for v in a]
+        da = [gy[j] * pt * bb[j] * sg[j] * (1 + a[j] * (1 - sg[j])) for j in range(F)]
+        db = [gy[j] * pt * a[j] * sg[j] for j in range(F)]
+        dp.append(math.fsum(gy[j] * a[j] * sg[j] * bb[j] for j in range(F)))
+        row = [_bf16_nearest_bits(v) for v in da + db]
+        dh_bits.append(row)
+        _, cq, ce = _mx_rows([[_bf16_value(b) for b in row]])
+        dh_q.append(cq[0]), dh_s.append(ce[0])
+    dh_bits = np.array(dh_bits, np.uint16)
+    assert np.array_equal(got["dh_bits"], dh_bits)
+    assert np.array_equal(got["dh_q"], np.array(dh_q, np.uint8))
+    assert np.array_equal(got["dh_s"], np.array(dh_s, np.uint8))
+    np.testing.assert_allclose(got["dp"], dp, rtol=1e-12, atol=1e-15)
+
+    # fc1 dgrad: dh rowwise, W1_g [2F, H] blocked along 2F
+    dhd, _, _ = _mx_rows(bits(dh_bits))
+    for t in range(T):
+        w1t, _, _ = _mx_rows([[_bf16_value(b) for b in inp["w1"][grp[t]][:, k]] for k in range(H)])
+        ref = [math.fsum(dhd[t][n] * w1t[k][n] for n in range(2 * F)) for k in range(H)]
+        np.testing.assert_allclose(got["dx"][t], ref, rtol=1e-12, atol=1e-15)
+    # wgrads: token-blocked per group
+    y_bits = np.array(y_bits, np.uint16)
+    dov = [_token_blocked_values(inp["dout"], base, n) for n in range(H)]
+    yv = [_token_blocked_values(y_bits, base, f) for f in range(F)]
+    dhv = [_token_blocked_values(dh_bits, base, n) for n in range(2 * F)]
+    xv = [_token_blocked_values(inp["x"], base, k) for k in range(H)]
+    for g in range(G):
+        ts = range(base[g], base[g + 1])
+        dw2 = [[math.fsum(dov[n][t] * yv[f][t] for t in ts) for f in range(F)] for n in range(H)]
+        dw1 = [[math.fsum(dhv[n][t] * xv[k][t] for t in ts) for k in range(H)] for n in range(2 * F)]
+        np.testing.assert_allclose(got["dw2"][g], dw2, rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(got["dw1"][g], dw1, rtol=1e-12, atol=1e-15)
