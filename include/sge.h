@@ -33,7 +33,10 @@
 extern "C" {
 #endif
 
-#define SGE_ABI_VERSION 2
+#define SGE_ABI_VERSION 3
+
+/* Alignment, in tokens, of each group's start in a token-blocked MXFP8 operand. */
+#define SGE_MX_TOKEN_ALIGN 128
 
 typedef enum {
   SGE_OK = 0,
@@ -259,6 +262,81 @@ sge_status sge_grouped_linear_bwd(const void* dy, const void* x, const void* w, 
                                   const float* probs, void* dact, float* dprobs, void* dx,
                                   void* dw, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream);
+
+/*
+ * Token-blocked MXFP8 operands of the grouped weight gradient.
+ * ("Activation + GroupedLinear Fusion for MOE and other MOE optimizations", Description:
+ * the activation is followed by a group quantize, so each group's slice of a grouped tensor
+ * is quantized as a tensor of its own; the split offsets are computed once and reused by
+ * the backward.)
+ *
+ * A wgrad contracts over the tokens of one group, so its MXFP8 operands have blocks of 32
+ * along tokens, starting at each group's first token; a group whose length is not a
+ * multiple of 32 ends in a short block (as if padded with zeros). They are stored
+ * transposed, [features][ld], group g from column pad[g], a multiple of SGE_MX_TOKEN_ALIGN:
+ *
+ *   sge_mx_group_layout: layout [2][G+1] device int64 from offsets [G+1] (device):
+ *     layout[0][g] = c[g], the offsets as every grouped call reads them: clamped into [0, T]
+ *                    and made non-decreasing (c[g] = max(c[g-1], min(offsets[g], T)), from 0);
+ *     layout[1][g] = pad[g]: pad[0] = 0, pad[g+1] = pad[g] + roundup(c[g+1] - c[g], 128).
+ *     1 <= G <= 4096. One single-block kernel; computed once, reused by every call below.
+ *   sge_mx_token_capacity(T, G): the smallest ld every such operand accepts (an upper
+ *     bound of pad[G] known on the host): roundup(T, 128) + 128 * G; -1 for bad sizes.
+ *   sge_quantize_mxfp8_grouped: src bf16 [T, cols] (cols % 32 == 0) ->
+ *     q_colT [cols][ld] u8 and s_colT [cols][ld/32] u8 (required): token t of group g at
+ *     column pad[g] + t - c[g]; columns pad[g] + (c[g+1]-c[g]) .. pad[g+1]-1 hold code 0
+ *     under all-zero blocks (E8M0 byte 0); columns from pad[G] on are not written.
+ *     Optionally q_row [T, cols] / s_row [T, cols/32] (given together): the rowwise
+ *     quantization of sge_quantize_mxfp8, for the tokens inside [c[0], c[G]).
+ *     ld % 128 == 0 and ld >= sge_mx_token_capacity(T, G); layout from sge_mx_group_layout
+ *     with the same T and G.
+ */
+int64_t sge_mx_token_capacity(int64_t T, int32_t G);
+sge_status sge_mx_group_layout(const int64_t* offsets, int32_t G, int64_t T, int64_t* layout,
+                               hipStream_t stream);
+sge_status sge_quantize_mxfp8_grouped(const void* src, int64_t T, int64_t cols, int32_t G,
+                                      const int64_t* layout, int64_t ld, uint8_t* q_row,
+                                      uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT,
+                                      hipStream_t stream);
+
+/*
+ * Grouped linear backward on MXFP8 operands: the dgrad (with the fused activation backward
+ * and group quantize) and the weight gradient.
+ * ("Activation + GroupedLinear Fusion for MOE and other MOE optimizations", Sequence
+ * Diagram, backward: the activation backward hands FC1's dgrad the quantized gradient,
+ * FC1's wgrad the same gradient unquantized, and returns the gradient of the scales.)
+ *
+ * dgrad, for the layer  out[t] = alpha * x[t] @ W_g^T,  W [G, N, K]:
+ *   g[t] = alpha * dy[t] @ W_g  (contraction over N, all operands MXFP8 blocked along N)
+ *   dy_q [T, N] u8, dy_s [T, N/32] u8: dy quantized rowwise (sge_quantize_mxfp8 q_row/s_row);
+ *   w_q [K][G*N] u8, w_s [K][G*N/32] u8: W viewed as [G*N, K] quantized columnwise
+ *     (sge_quantize_mxfp8 q_colT/s_colT); blocks never cross experts as N % 32 == 0.
+ *   SGE_EPI_NONE: dx [T, K] bf16 = g.
+ *   SGE_EPI_DSCALED_SWIGLU (x was y = p * silu(a) * b, preact h = [a, b] [T, 2K] bf16):
+ *     dact [T, 2K] bf16 = [g*p*b*silu'(a), g*p*silu(a)] (may be NULL when dact_q is given),
+ *     dprobs [T] fp32 = sum_j g*silu(a)*b (deterministic order), and optionally
+ *     dact_q [T, 2K] u8 + dact_s [T, 2K/32] u8: the rowwise MXFP8 of the bf16 dact, the bytes
+ *     sge_quantize_mxfp8 writes for it (the operand of the next layer's dgrad).
+ *     workspace: >= sge_grouped_linear_bwd_workspace_size(T, K, G, epilogue) bytes.
+ *   Shapes: N % 128 == 0, K % 8 == 0 (SwiGLU: K % 32 == 0). offsets as in
+ *   sge_grouped_linear_fwd. Outputs may not overlap inputs or each other.
+ *
+ * wgrad: dW_g [N, K] bf16 = alpha * sum_{t in g} dy[t]^T x[t], zero for an empty group,
+ *   from the token-blocked operands of sge_quantize_mxfp8_grouped:
+ *   dyT_q [N][ld], dyT_s [N][ld/32] (of dy [T, N]); xT_q [K][ld], xT_s [K][ld/32] (of the
+ *   layer input x [T, K]); layout and ld as given to the quantizer. dw [G, N, K] bf16.
+ *   Shapes: ld % 128 == 0, K % 8 == 0, 1 <= G <= 4096.
+ */
+sge_status sge_grouped_linear_dgrad_mxfp8(const void* dy_q, const void* dy_s, const void* w_q,
+                                          const void* w_s, int32_t G, int64_t T, int64_t N, int64_t K,
+                                          const int64_t* offsets, float alpha, int32_t epilogue,
+                                          const void* preact, const float* probs, void* dx, void* dact,
+                                          float* dprobs, void* dact_q, void* dact_s, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream);
+sge_status sge_grouped_linear_wgrad_mxfp8(const void* dyT_q, const void* dyT_s, const void* xT_q,
+                                          const void* xT_s, int32_t G, int64_t N, int64_t K,
+                                          const int64_t* layout, int64_t ld, float alpha, void* dw,
+                                          hipStream_t stream);
 
 /*
  * Unfused per-token scaled SwiGLU (the composition the fused epilogues replace).

@@ -35,6 +35,8 @@ EXPORTED = (
     "sge_splits_to_offsets", "sge_grouped_linear_fwd", "sge_grouped_linear_fwd_mxfp8",
     "sge_grouped_linear_bwd_workspace_size", "sge_grouped_linear_bwd",
     "sge_scaled_swiglu_fwd", "sge_scaled_swiglu_bwd",
+    "sge_mx_token_capacity", "sge_mx_group_layout", "sge_quantize_mxfp8_grouped",
+    "sge_grouped_linear_dgrad_mxfp8", "sge_grouped_linear_wgrad_mxfp8",
 )
 
 
@@ -73,6 +75,13 @@ _SIGS = {
                                 _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "sge_scaled_swiglu_fwd": ([_vp, _vp, _vp, _i64, _i64, _vp], ctypes.c_int),
     "sge_scaled_swiglu_bwd": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp], ctypes.c_int),
+    "sge_mx_token_capacity": ([_i64, _i32], _i64),
+    "sge_mx_group_layout": ([_vp, _i32, _i64, _vp, _vp], ctypes.c_int),
+    "sge_quantize_mxfp8_grouped": ([_vp, _i64, _i64, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "sge_grouped_linear_dgrad_mxfp8": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _vp, _vp,
+                                        _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "sge_grouped_linear_wgrad_mxfp8": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _f32, _vp, _vp],
+                                       ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -218,6 +227,54 @@ def grouped_linear_bwd(dy, x, w, offsets, alpha=1.0, epilogue=EPI_NONE, preact=N
     _check(_lib.sge_grouped_linear_bwd(_ptr(dy), _ptr(x), _ptr(w), G, T, N, K, _ptr(offsets), float(alpha),
                                        epilogue, _ptr(preact), _ptr(probs), _ptr(dact), _ptr(dprobs), _ptr(dx),
                                        _ptr(dw), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+# ------------------------------------------------ MXFP8 grouped backward
+MX_TOKEN_ALIGN = 128
+
+
+def mx_token_capacity(T, G):
+    """Smallest leading dimension of a token-blocked MXFP8 operand of T tokens in G groups."""
+    return int(_lib.sge_mx_token_capacity(int(T), int(G)))
+
+
+def mx_group_layout(offsets, T, layout, stream=None):
+    """layout [2, G+1] int64 (device): clamped offsets and 128-aligned group starts."""
+    G = offsets.numel() - 1
+    _check(_lib.sge_mx_group_layout(_ptr(offsets), G, int(T), _ptr(layout), _stream(stream)))
+
+
+def quantize_mxfp8_grouped(src, layout, q_colT, s_colT, q_row=None, s_row=None, stream=None):
+    """Token-blocked MXFP8 of bf16 ``src`` [T, cols]: q_colT [cols, ld] + s_colT [cols, ld/32],
+    optionally the rowwise copy q_row [T, cols] + s_row [T, cols/32]."""
+    T, cols = src.shape
+    G = layout.numel() // 2 - 1
+    _check(_lib.sge_quantize_mxfp8_grouped(_ptr(src), T, cols, G, _ptr(layout), q_colT.shape[1], _ptr(q_row),
+                                           _ptr(s_row), _ptr(q_colT), _ptr(s_colT), _stream(stream)))
+
+
+def grouped_linear_dgrad_mxfp8(dy_q, dy_s, w_q, w_s, offsets, alpha=1.0, epilogue=EPI_NONE, preact=None,
+                               probs=None, dx=None, dact=None, dprobs=None, dact_q=None, dact_s=None,
+                               workspace=None, stream=None):
+    """MXFP8 grouped dgrad: dy_q [T, N] + dy_s [T, N/32] (rowwise), w_q [K, G*N] + w_s [K, G*N/32]
+    (W viewed [G*N, K], quantized columnwise). SwiGLU backward writes dact / dact_q+dact_s and dprobs."""
+    T, N = dy_q.shape
+    K = w_q.shape[0]
+    G = offsets.numel() - 1
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.sge_grouped_linear_dgrad_mxfp8(_ptr(dy_q), _ptr(dy_s), _ptr(w_q), _ptr(w_s), G, T, N, K,
+                                               _ptr(offsets), float(alpha), epilogue, _ptr(preact), _ptr(probs),
+                                               _ptr(dx), _ptr(dact), _ptr(dprobs), _ptr(dact_q), _ptr(dact_s),
+                                               _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def grouped_linear_wgrad_mxfp8(dyT_q, dyT_s, xT_q, xT_s, layout, dw, alpha=1.0, stream=None):
+    """MXFP8 grouped wgrad from token-blocked operands: dyT [N, ld], xT [K, ld] -> dw [G, N, K] bf16."""
+    N, ld = dyT_q.shape
+    K = xT_q.shape[0]
+    G = layout.numel() // 2 - 1
+    _check(_lib.sge_grouped_linear_wgrad_mxfp8(_ptr(dyT_q), _ptr(dyT_s), _ptr(xT_q), _ptr(xT_s), G, N, K,
+                                               _ptr(layout), ld, float(alpha), _ptr(dw), _stream(stream)))
 
 
 def scaled_swiglu_fwd(h, probs, y, stream=None):

@@ -503,6 +503,180 @@ sge_status sge_grouped_linear_bwd(const void* dy, const void* x, const void* w, 
   return ok();
 }
 
+int64_t sge_mx_token_capacity(int64_t T, int32_t G) {
+  if (T < 0 || G < 1) return -1;
+  return (T + SGE_MX_TOKEN_ALIGN - 1) / SGE_MX_TOKEN_ALIGN * SGE_MX_TOKEN_ALIGN + (int64_t)G * SGE_MX_TOKEN_ALIGN;
+}
+
+sge_status sge_mx_group_layout(const int64_t* offsets, int32_t G, int64_t T, int64_t* layout, hipStream_t stream) {
+  if (!offsets || !layout) return fail(SGE_ERR_NULL, "mx_group_layout: NULL pointer");
+  if (G < 1 || G > 4096) return fail(SGE_ERR_ARG, "mx_group_layout: G=%d outside [1, 4096]", G);
+  if (T < 0) return fail(SGE_ERR_SHAPE, "mx_group_layout: negative T");
+  if (overlap(Range{(uintptr_t)offsets, (uintptr_t)(offsets + G + 1)}, Range{(uintptr_t)layout, (uintptr_t)(layout + 2 * (G + 1))}))
+    return fail(SGE_ERR_ALIAS, "mx_group_layout: layout overlaps offsets");
+  return hip_status(sge::launch_mx_group_layout(offsets, G, T, SGE_MX_TOKEN_ALIGN, layout, stream),
+                    "mx_group_layout launch");
+}
+
+sge_status sge_quantize_mxfp8_grouped(const void* src, int64_t T, int64_t cols, int32_t G, const int64_t* layout,
+                                      int64_t ld, uint8_t* q_row, uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT,
+                                      hipStream_t stream) {
+  if (T < 0 || cols < 0) return fail(SGE_ERR_SHAPE, "quantize_mxfp8_grouped: negative size");
+  if (G < 1 || G > 4096) return fail(SGE_ERR_ARG, "quantize_mxfp8_grouped: G=%d outside [1, 4096]", G);
+  if (!layout || !q_colT || !s_colT) return fail(SGE_ERR_NULL, "quantize_mxfp8_grouped: layout, q_colT and s_colT are required");
+  if ((q_row == nullptr) != (s_row == nullptr))
+    return fail(SGE_ERR_NULL, "quantize_mxfp8_grouped: q_row and s_row go together");
+  if (T * cols > 0 && !src) return fail(SGE_ERR_NULL, "quantize_mxfp8_grouped: src is NULL");
+  if (cols % 32) return fail(SGE_ERR_SHAPE, "quantize_mxfp8_grouped: cols must be a multiple of 32");
+  if (ld % SGE_MX_TOKEN_ALIGN || ld < sge_mx_token_capacity(T, G))
+    return fail(SGE_ERR_SHAPE, "quantize_mxfp8_grouped: ld=%lld must be a multiple of %d and >= sge_mx_token_capacity(T, G)=%lld",
+                (long long)ld, SGE_MX_TOKEN_ALIGN, (long long)sge_mx_token_capacity(T, G));
+  if ((src && !aligned16(src)) || (q_row && !aligned16(q_row)) || !aligned16(q_colT) || !aligned16(s_colT))
+    return fail(SGE_ERR_ALIGN, "quantize_mxfp8_grouped: pointers must be 16-byte aligned");
+  const Range in = range_of(src, T, cols, cols, 2);
+  const Range outs[4] = {q_row ? range_of(q_row, T, cols, cols, 1) : Range{0, 0},
+                         s_row ? range_of(s_row, T, cols / 32, cols / 32, 1) : Range{0, 0},
+                         range_of(q_colT, cols, ld, ld, 1), range_of(s_colT, cols, ld / 32, ld / 32, 1)};
+  const Range lay{(uintptr_t)layout, (uintptr_t)(layout + 2 * (G + 1))};
+  for (int a = 0; a < 4; ++a) {
+    if (overlap(outs[a], in) || overlap(outs[a], lay)) return fail(SGE_ERR_ALIAS, "quantize_mxfp8_grouped: output overlaps an input");
+    for (int b = a + 1; b < 4; ++b)
+      if (overlap(outs[a], outs[b])) return fail(SGE_ERR_ALIAS, "quantize_mxfp8_grouped: outputs overlap");
+  }
+  if (cols == 0) return ok();
+  return hip_status(sge::launch_quantize_mxfp8_grouped(static_cast<const uint16_t*>(src), T, cols, G, layout, ld,
+                                                       q_row, s_row, q_colT, s_colT, stream),
+                    "quantize_mxfp8_grouped launch");
+}
+
+sge_status sge_grouped_linear_dgrad_mxfp8(const void* dy_q, const void* dy_s, const void* w_q, const void* w_s,
+                                          int32_t G, int64_t T, int64_t N, int64_t K, const int64_t* offsets,
+                                          float alpha, int32_t epilogue, const void* preact, const float* probs,
+                                          void* dx, void* dact, float* dprobs, void* dact_q, void* dact_s,
+                                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_mxfp8: bad sizes");
+  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_DSCALED_SWIGLU)
+    return fail(SGE_ERR_ARG, "grouped_linear_dgrad_mxfp8: epilogue %d not allowed", epilogue);
+  const bool swiglu = epilogue == SGE_EPI_DSCALED_SWIGLU;
+  if (!dy_q || !dy_s || !w_q || !w_s || !offsets) return fail(SGE_ERR_NULL, "grouped_linear_dgrad_mxfp8: NULL pointer");
+  if ((dact_q == nullptr) != (dact_s == nullptr))
+    return fail(SGE_ERR_NULL, "grouped_linear_dgrad_mxfp8: dact_q and dact_s go together");
+  if (swiglu) {
+    if (!preact || !probs || !dprobs) return fail(SGE_ERR_NULL, "grouped_linear_dgrad_mxfp8: SwiGLU backward needs preact, probs and dprobs");
+    if (!dact && !dact_q) return fail(SGE_ERR_NULL, "grouped_linear_dgrad_mxfp8: no output");
+  } else {
+    if (!dx) return fail(SGE_ERR_NULL, "grouped_linear_dgrad_mxfp8: dx is NULL");
+    if (dact_q) return fail(SGE_ERR_ARG, "grouped_linear_dgrad_mxfp8: a quantized output needs the SwiGLU backward");
+  }
+  if (N % 128) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_mxfp8: N must be a multiple of 128 (got %lld)", (long long)N);
+  if (K % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_mxfp8: K must be a multiple of 8");
+  if (swiglu && K % 32) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_mxfp8: SwiGLU backward needs K %% 32 == 0");
+  if (!aligned16(dy_q) || !aligned16(dy_s) || !aligned16(w_q) || !aligned16(w_s) || (dx && !aligned16(dx)) ||
+      (preact && !aligned16(preact)) || (dact && !aligned16(dact)) || (dact_q && !aligned16(dact_q)))
+    return fail(SGE_ERR_ALIGN, "grouped_linear_dgrad_mxfp8: pointers must be 16-byte aligned");
+  const int64_t GN = (int64_t)G * N;
+  const Range in[5] = {range_of(dy_q, T, N, N, 1), range_of(dy_s, T, N / 32, N / 32, 1), range_of(w_q, K, GN, GN, 1),
+                       range_of(w_s, K, GN / 32, GN / 32, 1),
+                       swiglu ? range_of(preact, T, 2 * K, 2 * K, 2) : Range{0, 0}};
+  const Range outs[4] = {(dx && !swiglu) ? range_of(dx, T, K, K, 2) : Range{0, 0},
+                         (swiglu && dact) ? range_of(dact, T, 2 * K, 2 * K, 2) : Range{0, 0},
+                         dact_q ? range_of(dact_q, T, 2 * K, 2 * K, 1) : Range{0, 0},
+                         dact_s ? range_of(dact_s, T, 2 * K / 32, 2 * K / 32, 1) : Range{0, 0}};
+  for (int a = 0; a < 4; ++a) {
+    for (const Range& i : in)
+      if (overlap(outs[a], i)) return fail(SGE_ERR_ALIAS, "grouped_linear_dgrad_mxfp8: outputs overlap inputs");
+    for (int b = a + 1; b < 4; ++b)
+      if (overlap(outs[a], outs[b])) return fail(SGE_ERR_ALIAS, "grouped_linear_dgrad_mxfp8: outputs overlap");
+  }
+  const size_t need = sge_grouped_linear_bwd_workspace_size(T, K, G, epilogue);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(SGE_ERR_WORKSPACE, "grouped_linear_dgrad_mxfp8: workspace %zu < %zu bytes", workspace_bytes, need);
+  if (T == 0 || K == 0) return ok();
+  sge::GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.a = static_cast<const uint8_t*>(dy_q);
+  p.lda = N;
+  p.b = static_cast<const uint8_t*>(w_q);       // W blocked along N: [K][G*N], group g at column g*N
+  p.ldb = GN;
+  p.M = T;
+  p.N = K;
+  p.K = N;
+  p.b_group_stride = N;
+  p.a_mx = static_cast<const uint8_t*>(dy_s);
+  p.a_mx_ld = N / 32;
+  p.b_mx = static_cast<const uint8_t*>(w_s);
+  p.b_mx_ld = GN / 32;
+  p.b_mx_group_stride = N / 32;
+  p.b_mx_bytes = K * (GN / 32);
+  p.mx_aligned = 1;
+  p.alpha = alpha;
+  p.c = static_cast<uint16_t*>(swiglu ? nullptr : dx);
+  p.ldc = K;
+  p.offsets = offsets;
+  p.G = G;
+  p.T = T;
+  if (swiglu) {
+    p.probs = probs;
+    p.aux = const_cast<uint16_t*>(static_cast<const uint16_t*>(preact));
+    p.ld_aux = 2 * K;
+    p.aux_out = static_cast<uint16_t*>(dact);
+    p.ld_aux_out = 2 * K;
+    p.dp_part = static_cast<float*>(workspace);
+    p.F = K;
+    p.q_out = static_cast<uint8_t*>(dact_q);
+    p.s_out = static_cast<uint8_t*>(dact_s);
+    p.ld_q = 2 * K;
+  }
+  hipError_t e = sge::launch_grouped_dgrad_mx(p, epilogue, stream);
+  if (e != hipSuccess) return hip_status(e, "grouped dgrad mxfp8 launch");
+  if (swiglu) {
+    const int parts = (int)(sge::gemm_dp_parts_per_tile() * ((K + sge::gemm_tile_n() - 1) / sge::gemm_tile_n()));
+    e = sge::launch_rowsum_parts(static_cast<const float*>(workspace), parts, offsets, G, T, dprobs, stream);
+    if (e != hipSuccess) return hip_status(e, "dprobs reduction launch");
+  }
+  return ok();
+}
+
+sge_status sge_grouped_linear_wgrad_mxfp8(const void* dyT_q, const void* dyT_s, const void* xT_q, const void* xT_s,
+                                          int32_t G, int64_t N, int64_t K, const int64_t* layout, int64_t ld,
+                                          float alpha, void* dw, hipStream_t stream) {
+  if (G < 1 || G > 4096 || N < 0 || K < 0 || ld < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_wgrad_mxfp8: bad sizes");
+  if (!dyT_q || !dyT_s || !xT_q || !xT_s || !layout || !dw) return fail(SGE_ERR_NULL, "grouped_linear_wgrad_mxfp8: NULL pointer");
+  if (ld % SGE_MX_TOKEN_ALIGN) return fail(SGE_ERR_SHAPE, "grouped_linear_wgrad_mxfp8: ld must be a multiple of %d", SGE_MX_TOKEN_ALIGN);
+  if (K % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_wgrad_mxfp8: K must be a multiple of 8");
+  if (!aligned16(dyT_q) || !aligned16(dyT_s) || !aligned16(xT_q) || !aligned16(xT_s) || !aligned16(dw))
+    return fail(SGE_ERR_ALIGN, "grouped_linear_wgrad_mxfp8: pointers must be 16-byte aligned");
+  const Range rdw = range_of(dw, (int64_t)G * N, K, K, 2);
+  const Range in[5] = {range_of(dyT_q, N, ld, ld, 1), range_of(dyT_s, N, ld / 32, ld / 32, 1), range_of(xT_q, K, ld, ld, 1),
+                       range_of(xT_s, K, ld / 32, ld / 32, 1),
+                       Range{(uintptr_t)layout, (uintptr_t)(layout + 2 * (G + 1))}};
+  for (const Range& i : in)
+    if (overlap(rdw, i)) return fail(SGE_ERR_ALIAS, "grouped_linear_wgrad_mxfp8: dw overlaps an input");
+  if (N == 0 || K == 0) return ok();
+  sge::GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.a = static_cast<const uint8_t*>(dyT_q);
+  p.lda = ld;
+  p.b = static_cast<const uint8_t*>(xT_q);
+  p.ldb = ld;
+  p.M = N;
+  p.N = K;
+  p.K = ld;
+  p.a_mx = static_cast<const uint8_t*>(dyT_s);
+  p.a_mx_ld = ld / 32;
+  p.b_mx = static_cast<const uint8_t*>(xT_s);
+  p.b_mx_ld = ld / 32;
+  p.mx_aligned = 1;
+  p.alpha = alpha;
+  p.c = static_cast<uint16_t*>(dw);
+  p.ldc = K;
+  p.c_group_stride = N * K;
+  p.offsets = layout + G + 1;                    // the aligned group starts: each group's contraction range
+  p.G = G;
+  p.T = ld;
+  return hip_status(sge::launch_grouped_wgrad_mx(p, stream), "grouped wgrad mxfp8 launch");
+}
+
 sge_status sge_scaled_swiglu_fwd(const void* h, const float* probs, void* y, int64_t T, int64_t F, hipStream_t stream) {
   if (T < 0 || F < 0) return fail(SGE_ERR_SHAPE, "scaled_swiglu_fwd: negative size");
   if (T > 0 && (!h || !probs || !y)) return fail(SGE_ERR_NULL, "scaled_swiglu_fwd: NULL pointer");

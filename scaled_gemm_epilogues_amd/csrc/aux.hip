@@ -100,6 +100,71 @@ hipError_t launch_splits_to_offsets(const int64_t* splits, int G, const int64_t*
   return hipGetLastError();
 }
 
+// ------------------------------------- token-blocked MXFP8 group layout
+// Operands of a grouped wgrad are quantized in blocks of 32 along the tokens of each group,
+// each group stored from a position aligned to `align` tokens. One block computes
+//   c[g]   = the offsets as every grouped call reads them (clamped into [0, T], non-decreasing)
+//   pad[g] = pad[g-1] + roundup(c[g] - c[g-1], align), pad[0] = 0
+// into layout[0][..] and layout[1][..] ([2][G+1] int64), G + 1 <= kLayoutMax.
+constexpr int kLayoutMax = 4097;
+
+__global__ __launch_bounds__(kScanThreads) void mx_group_layout_kernel(const int64_t* __restrict__ offsets, int G,
+                                                                       int64_t T, int64_t align,
+                                                                       int64_t* __restrict__ layout) {
+  __shared__ int64_t part[kScanThreads];
+  __shared__ int64_t cs[kLayoutMax];
+  const int t = threadIdx.x;
+  const int n = G + 1;
+  const int per = (n + kScanThreads - 1) / kScanThreads;
+  const int i0 = t * per, i1 = i0 + per < n ? i0 + per : n;
+  // clamped offsets: running max of min(offsets[i], T), from 0
+  int64_t m = 0;
+  for (int i = i0; i < i1; ++i) {
+    const int64_t v = offsets[i] < T ? offsets[i] : T;
+    m = v > m ? v : m;
+  }
+  part[t] = m;
+  __syncthreads();
+  for (int o = 1; o < kScanThreads; o <<= 1) {
+    const int64_t other = t >= o ? part[t - o] : 0;
+    __syncthreads();
+    part[t] = other > part[t] ? other : part[t];
+    __syncthreads();
+  }
+  int64_t run = t > 0 ? part[t - 1] : 0;
+  for (int i = i0; i < i1; ++i) {
+    const int64_t v = offsets[i] < T ? offsets[i] : T;
+    run = v > run ? v : run;
+    cs[i] = run;
+    layout[i] = run;
+  }
+  __syncthreads();
+  // aligned starts: exclusive prefix sum of the rounded-up group lengths
+  int64_t sum = 0;
+  for (int g = i0; g < i1 && g < G; ++g) sum += (cs[g + 1] - cs[g] + align - 1) / align * align;
+  part[t] = sum;
+  __syncthreads();
+  for (int o = 1; o < kScanThreads; o <<= 1) {
+    const int64_t add = t >= o ? part[t - o] : 0;
+    __syncthreads();
+    part[t] += add;
+    __syncthreads();
+  }
+  int64_t pos = t > 0 ? part[t - 1] : 0;
+  for (int g = i0; g < i1 && g < G; ++g) {
+    layout[n + g] = pos;
+    pos += (cs[g + 1] - cs[g] + align - 1) / align * align;
+  }
+  if (t == kScanThreads - 1) layout[n + G] = part[kScanThreads - 1];
+}
+
+hipError_t launch_mx_group_layout(const int64_t* offsets, int G, int64_t T, int64_t align, int64_t* layout,
+                                  hipStream_t s) {
+  if (G + 1 > kLayoutMax) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mx_group_layout_kernel, dim3(1), dim3(kScanThreads), 0, s, offsets, G, T, align, layout);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------ unfused scaled SwiGLU
 __device__ __forceinline__ float sigmoid_f(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
 

@@ -58,6 +58,9 @@ constexpr int kWavesM = SGE_WAVES_M, kWavesN = SGE_WAVES_N, kFragsM = SGE_FRAGS_
 #ifndef SGE_RD_PER_MFMA
 #define SGE_RD_PER_MFMA 2
 #endif
+#ifndef SGE_DSWIGLU_BATCH
+#define SGE_DSWIGLU_BATCH 8      // dSwiGLU epilogue chunks whose loads are in flight together
+#endif
 
 template <int FMT>
 struct TileShape {
@@ -84,6 +87,33 @@ __device__ __forceinline__ int xcd_tile(int bid, int total) {
 
 __device__ __forceinline__ float fast_sigmoid(float a) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+}
+
+typedef int v4i __attribute__((__vector_size__(4 * sizeof(int))));
+typedef int v2i __attribute__((__vector_size__(2 * sizeof(int))));
+
+// MXFP8 of 8 bf16 values (one lane's 16 bytes, packed pairs) inside a block of 32 that four
+// adjacent lanes (lane ^ 1, lane ^ 2) hold together: the block amax of the bf16 magnitudes,
+// the E8M0 exponent, and this lane's 8 E4M3 codes. Every lane of the wave must take part.
+__device__ __forceinline__ v2i mx_quant_lane8(const v4i& v, int& e8m0) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t w = (uint32_t)v[e], lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
+    m = lo > m ? lo : m;
+    m = hi > m ? hi : m;
+  }
+  uint32_t o = __shfl_xor(m, 1, 64);
+  m = o > m ? o : m;
+  o = __shfl_xor(m, 2, 64);
+  m = o > m ? o : m;
+  const int X = mx_exponent(m);
+  const float sc = pow2_neg(X);
+  uint32_t qb[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) qb[e] = e4m3x2(bf16_lo((uint32_t)v[e]) * sc, bf16_hi((uint32_t)v[e]) * sc);
+  e8m0 = X + 127;
+  return v2i{(int)(qb[0] | (qb[1] << 16)), (int)(qb[2] | (qb[3] << 16))};
 }
 
 typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
@@ -384,7 +414,11 @@ void gemm_kernel(const GemmParams p) {
         const uint8_t* base = is_a ? p.a_mx : bmx;
         const int64_t ld = is_a ? p.a_mx_ld : p.b_mx_ld;
         const int64_t rows_total = is_a ? (SCHED == S_GROUP_M ? p.T : p.M) : b_rows;
-        const i32x4 rs = make_rsrc4(base + blk0, rows_total * ld - blk0);
+        // B's scales of one group can sit inside wider rows (b_mx_bytes: the whole array), so the
+        // resource ends where the array ends, not rows_total rows after this group's start.
+        const int64_t avail = (!is_a && p.b_mx_bytes) ? (int64_t)((p.b_mx + p.b_mx_bytes) - (bmx + blk0))
+                                                      : rows_total * ld - blk0;
+        const i32x4 rs = make_rsrc4(base + blk0, avail);
         lds_copy16(rs, sc_lds[buf] + piece * 1024, ok ? (uint32_t)(row * ld) : kOOB);
       }
     }
@@ -583,7 +617,6 @@ void gemm_kernel(const GemmParams p) {
   // are in flight together (and the next block's loads overlap this block's math).
   float alpha = p.alpha;
   if constexpr (FMT == F_E4M3) alpha = (p.a_sinv[0] * p.b_sinv[0]) * p.alpha;
-  typedef int v2i __attribute__((__vector_size__(2 * sizeof(int))));
   const int64_t c_rows = SCHED == S_GROUP_M ? p.T : p.M;
   const int64_t rows_left = c_rows - m0;
   auto row_in_tile = [&](int i) { return wm * WM + i * 32 + lrow; };
@@ -595,7 +628,6 @@ void gemm_kernel(const GemmParams p) {
     // layout), then every thread takes 8 consecutive columns of a row: one 16-byte residual
     // load and one 16-byte store, so each wave moves whole 128-byte lines.
     static_assert(BM == 2 * WM && A_BYTES + B_BYTES == 64 * BN * 4, "epilogue staging assumes 2 wave rows");
-    typedef int v4i __attribute__((__vector_size__(4 * sizeof(int))));
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(cptr + m0 * p.ldc, rows_left * p.ldc * 2);
     constexpr int kChunks = BN / 8;                        // 8-column chunks per row
     constexpr int kIters = 128 * kChunks / (NWAVES * 64);  // chunks per thread per pass
@@ -666,7 +698,6 @@ void gemm_kernel(const GemmParams p) {
     // produce it from the bf16 output (four adjacent lanes hold one 32-column block).
     static_assert(BM == 2 * WM && A_BYTES + B_BYTES == 64 * BN * 4, "epilogue staging assumes 2 wave rows");
     static_assert(WNF % 2 == 0 && BN / 16 == 16, "gate and up fragments per wave column; 16 chunks per row");
-    typedef int v4i __attribute__((__vector_size__(4 * sizeof(int))));
     const int64_t ybytes = cptr ? rows_left * p.ldc * 2 : 0;
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(cptr ? cptr + m0 * p.ldc : cptr, ybytes);
     const int64_t hbytes = p.aux ? rows_left * p.ld_aux * 2 : 0;
@@ -744,28 +775,10 @@ void gemm_kernel(const GemmParams p) {
         __builtin_amdgcn_raw_buffer_store_b128(vb, rhb, oh[it], 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(vy, ry, oy[it], 0, 0);
         if (mxq) {
-          // block amax over the bf16 magnitudes of 4 adjacent lanes (one 32-column block)
-          uint32_t m = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t w = (uint32_t)vy[e], lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
-            m = lo > m ? lo : m;
-            m = hi > m ? hi : m;
-          }
-          uint32_t o = __shfl_xor(m, 1, 64);
-          m = o > m ? o : m;
-          o = __shfl_xor(m, 2, 64);
-          m = o > m ? o : m;
-          const int X = mx_exponent(m);
-          const float sc = pow2_neg(X);
-          uint32_t qb[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            qb[e] = e4m3x2(bf16_lo((uint32_t)vy[e]) * sc, bf16_hi((uint32_t)vy[e]) * sc);
-          typedef int v2i_ __attribute__((__vector_size__(2 * sizeof(int))));
-          const v2i_ qv = {(int)(qb[0] | (qb[1] << 16)), (int)(qb[2] | (qb[3] << 16))};
+          int e8;
+          const v2i qv = mx_quant_lane8(vy, e8);
           __builtin_amdgcn_raw_buffer_store_b64(qv, rq, oq[it], 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b8((char)(X + 127), rs, os[it], 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b8((char)e8, rs, os[it], 0, 0);
         }
       }
       if (pass == 0) __syncthreads();                      // stage reused by the second pass
@@ -778,12 +791,20 @@ void gemm_kernel(const GemmParams p) {
     // per row and column tile goes to the workspace.
     static_assert(BM == 2 * WM && A_BYTES + B_BYTES == 64 * BN * 4, "epilogue staging assumes 2 wave rows");
     static_assert(BN / 8 == 32, "a row's chunks fill half a wave");
-    typedef int v4i __attribute__((__vector_size__(4 * sizeof(int))));
-    const int64_t hbytes = rows_left * p.ld_aux * 2, dbytes = rows_left * p.ld_aux_out * 2;
-    const __amdgpu_buffer_rsrc_t rha = make_rsrc(p.aux + m0 * p.ld_aux, hbytes);
-    const __amdgpu_buffer_rsrc_t rhb = make_rsrc(p.aux + m0 * p.ld_aux + p.F, hbytes - p.F * 2);
-    const __amdgpu_buffer_rsrc_t rda = make_rsrc(p.aux_out + m0 * p.ld_aux_out, dbytes);
-    const __amdgpu_buffer_rsrc_t rdb = make_rsrc(p.aux_out + m0 * p.ld_aux_out + p.F, dbytes - p.F * 2);
+    const int64_t hbytes = rows_left * p.ld_aux * 2;
+    const int64_t dbytes = p.aux_out ? rows_left * p.ld_aux_out * 2 : 0;
+    // One resource per tensor; the b half sits F columns further (an out-of-range offset
+    // stays out of range when that is added).
+    const __amdgpu_buffer_rsrc_t rh = make_rsrc(p.aux + m0 * p.ld_aux, hbytes);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.aux_out ? p.aux_out + m0 * p.ld_aux_out : p.aux_out, dbytes);
+    const int fb = (int)(p.F * 2);                         // byte distance of the b half (bf16)
+    // With q_out, dact is also emitted as MXFP8 rowwise (blocks of 32 along 2F, which never
+    // straddle the da / db halves as F % 32 == 0), the bytes the standalone quantizer writes
+    // for the bf16 dact. Its row stride ld_q equals ld_aux_out, so byte offsets are od / 2.
+    const bool mxq = p.q_out != nullptr;
+    const int64_t qbytes = mxq ? rows_left * p.ld_q : 0, sbytes = mxq ? rows_left * (p.ld_q / 32) : 0;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(mxq ? p.q_out + m0 * p.ld_q : p.q_out, qbytes);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(mxq ? p.s_out + m0 * (p.ld_q / 32) : p.s_out, sbytes);
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.probs + m0, rows_left * 4);
     const __amdgpu_buffer_rsrc_t rpart = make_rsrc(p.dp_part + (int64_t)nt * p.T + m0, rows_left * 4);
     constexpr int kChunks = BN / 8;
@@ -807,26 +828,34 @@ void gemm_kernel(const GemmParams p) {
           }
       }
       __syncthreads();
-      v4i ha[kIters], hb[kIters];
-      float pr[kIters];
-      int oh[kIters], od[kIters], orow[kIters];
+      // Chunks go in batches of at most 8 (all loads of a batch in flight together), which
+      // bounds the live registers when one thread owns 16 chunks (4-wave tiles).
+      constexpr int kBatch = kIters < SGE_DSWIGLU_BATCH ? kIters : SGE_DSWIGLU_BATCH;
+      static_assert(kIters % kBatch == 0, "whole batches");
 #pragma unroll
-      for (int it = 0; it < kIters; ++it) {
+      for (int it0 = 0; it0 < kIters; it0 += kBatch) {
+      v4i ha[kBatch], hb[kBatch];
+      float pr[kBatch];
+      int oh[kBatch], od[kBatch], orow[kBatch];
+#pragma unroll
+      for (int ib = 0; ib < kBatch; ++ib) {
+        const int it = it0 + ib;
         const int id = it * NWAVES * 64 + threadIdx.x;
         const int rp_ = id / kChunks, c = id % kChunks;
         const int brow = (rp_ >> 6) * WM + pass * (WM / 2) + (rp_ & 63);
         const int64_t n = n0 + c * 8;
         const bool rok = m0 + brow < row_end;
         const bool ok = rok && n < n_end;
-        oh[it] = ok ? (int)(((int64_t)brow * p.ld_aux + n) * 2) : (int)kOOB;
-        od[it] = ok ? (int)(((int64_t)brow * p.ld_aux_out + n) * 2) : (int)kOOB;
-        orow[it] = rok ? brow * 4 : (int)kOOB;
-        ha[it] = __builtin_amdgcn_raw_buffer_load_b128(rha, oh[it], 0, 0);
-        hb[it] = __builtin_amdgcn_raw_buffer_load_b128(rhb, oh[it], 0, 0);
-        pr[it] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, orow[it], 0, 0));
+        oh[ib] = ok ? (int)(((int64_t)brow * p.ld_aux + n) * 2) : (int)kOOB;
+        od[ib] = ok ? (int)(((int64_t)brow * p.ld_aux_out + n) * 2) : (int)kOOB;
+        orow[ib] = rok ? brow * 4 : (int)kOOB;
+        ha[ib] = __builtin_amdgcn_raw_buffer_load_b128(rh, oh[ib], 0, 0);
+        hb[ib] = __builtin_amdgcn_raw_buffer_load_b128(rh, oh[ib] + fb, 0, 0);
+        pr[ib] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, orow[ib], 0, 0));
       }
 #pragma unroll
-      for (int it = 0; it < kIters; ++it) {
+      for (int ib = 0; ib < kBatch; ++ib) {
+        const int it = it0 + ib;
         const int id = it * NWAVES * 64 + threadIdx.x;
         const int rp_ = id / kChunks, c = id % kChunks;
         const float* row = reinterpret_cast<const float*>(rp_ >= 64 ? lds1 : lds0) + (rp_ & 63) * BN;
@@ -834,11 +863,11 @@ void gemm_kernel(const GemmParams p) {
         const float4 lo = *reinterpret_cast<const float4*>(row + (((2 * c) ^ sw) << 2));
         const float4 hi = *reinterpret_cast<const float4*>(row + (((2 * c + 1) ^ sw) << 2));
         const float g[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        const float pm = pr[it];
+        const float pm = pr[ib];
         float da[8], db[8], part = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const uint32_t wa = (uint32_t)ha[it][e >> 1], wb = (uint32_t)hb[it][e >> 1];
+          const uint32_t wa = (uint32_t)ha[ib][e >> 1], wb = (uint32_t)hb[ib][e >> 1];
           const float a = (e & 1) ? bf16_hi(wa) : bf16_lo(wa);
           const float b = (e & 1) ? bf16_hi(wb) : bf16_lo(wb);
           const float sg = fast_sigmoid(a);
@@ -852,13 +881,24 @@ void gemm_kernel(const GemmParams p) {
                         (int)pack_bf16x2(da[4], da[5]), (int)pack_bf16x2(da[6], da[7])};
         const v4i vb = {(int)pack_bf16x2(db[0], db[1]), (int)pack_bf16x2(db[2], db[3]),
                         (int)pack_bf16x2(db[4], db[5]), (int)pack_bf16x2(db[6], db[7])};
-        __builtin_amdgcn_raw_buffer_store_b128(va, rda, od[it], 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(vb, rdb, od[it], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(va, rd, od[ib], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(vb, rd, od[ib] + fb, 0, 0);
+        if (mxq) {
+          int ea, eb;
+          const v2i qa = mx_quant_lane8(va, ea), qb = mx_quant_lane8(vb, eb);
+          const int oq = od[ib] == (int)kOOB ? (int)kOOB : od[ib] >> 1;
+          const int os = (od[ib] == (int)kOOB || (c & 3)) ? (int)kOOB : od[ib] >> 6;
+          __builtin_amdgcn_raw_buffer_store_b64(qa, rq, oq, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(qb, rq, oq + fb / 2, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b8((char)ea, rs, os, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b8((char)eb, rs, os + fb / 64, 0, 0);
+        }
         // the row's 32 chunks are lanes c = 0..31 of one half-wave: fixed-order tree sum
 #pragma unroll
         for (int d = 1; d < 32; d <<= 1) part += __shfl_xor(part, d, 64);
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, part), rpart, c == 0 ? orow[it] : (int)kOOB,
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, part), rpart, c == 0 ? orow[ib] : (int)kOOB,
                                               0, 0);
+      }
       }
       if (pass == 0) __syncthreads();                      // stage reused by the second pass
     }
@@ -927,6 +967,15 @@ hipError_t launch_grouped_dgrad(const GemmParams& p, int epilogue, hipStream_t s
 
 hipError_t launch_grouped_wgrad(const GemmParams& p, hipStream_t s) {
   return launch_tile<F_BF16, false, false, E_STORE, S_GROUP_K>(p, s);
+}
+
+hipError_t launch_grouped_dgrad_mx(const GemmParams& p, int epilogue, hipStream_t s) {
+  if (epilogue == E_DSWIGLU) return launch_tile<F_MX, true, true, E_DSWIGLU, S_GROUP_M>(p, s);
+  return launch_tile<F_MX, true, true, E_STORE, S_GROUP_M>(p, s);
+}
+
+hipError_t launch_grouped_wgrad_mx(const GemmParams& p, hipStream_t s) {
+  return launch_tile<F_MX, true, true, E_STORE, S_GROUP_K>(p, s);
 }
 
 int gemm_tile_n() { return kWavesN * 32 * kFragsN; }

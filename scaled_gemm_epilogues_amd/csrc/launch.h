@@ -43,6 +43,7 @@ struct GemmParams {
   uint8_t* q_out;             // SwiGLU with MXFP8 output: E4M3 [T][ld_q] (or NULL)
   uint8_t* s_out;             //   and its E8M0 scales [T][ld_q / 32]
   int64_t ld_q;
+  int64_t b_mx_bytes;         // MXFP8: bytes of B's whole scale array from b_mx (0: rows x ld)
 };
 
 hipError_t launch_gemm(const GemmParams& p, int fmt, bool a_kmaj, bool b_kmaj, hipStream_t s);
@@ -51,6 +52,9 @@ hipError_t launch_grouped_fwd(const GemmParams& p, int epilogue, hipStream_t s);
 hipError_t launch_grouped_fwd_mx(const GemmParams& p, int epilogue, hipStream_t s);
 hipError_t launch_grouped_dgrad(const GemmParams& p, int epilogue, hipStream_t s);
 hipError_t launch_grouped_wgrad(const GemmParams& p, hipStream_t s);
+// MXFP8 operands, both inner-contiguous (scale rows dword-aligned: contraction % 128 == 0).
+hipError_t launch_grouped_dgrad_mx(const GemmParams& p, int epilogue, hipStream_t s);
+hipError_t launch_grouped_wgrad_mx(const GemmParams& p, hipStream_t s);
 int gemm_tile_n();
 int gemm_dp_parts_per_tile();
 
@@ -65,6 +69,12 @@ hipError_t launch_quantize_fp8(const uint16_t* src, int64_t rows, int64_t cols, 
                                float* scale_inv, hipStream_t s);
 hipError_t launch_quantize_mxfp8(const uint16_t* src, int64_t rows, int64_t cols, uint8_t* q_row,
                                  uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT, hipStream_t s);
+// Token-blocked (per group) MXFP8: layout = [clamped offsets; aligned starts], [2][G+1].
+hipError_t launch_quantize_mxfp8_grouped(const uint16_t* src, int64_t rows, int64_t cols, int G,
+                                         const int64_t* layout, int64_t ld_t, uint8_t* q_row, uint8_t* s_row,
+                                         uint8_t* q_colT, uint8_t* s_colT, hipStream_t s);
+hipError_t launch_mx_group_layout(const int64_t* offsets, int G, int64_t T, int64_t align, int64_t* layout,
+                                  hipStream_t s);
 
 hipError_t launch_splits_to_offsets(const int64_t* splits, int G, const int64_t* mults, int n_mult,
                                     int64_t expected_total, int64_t* offsets, int32_t* err_flag,

@@ -173,17 +173,44 @@ hipError_t launch_quantize_fp8(const uint16_t* src, int64_t rows, int64_t cols, 
 // columns 8*(t%8)..+7 of rows t/8 + 32k, k = 0..3. Rowwise blocks are 4 consecutive threads
 // of a row; columnwise blocks are the 32 rows of one k, reduced across lanes and waves. The
 // columnwise copy goes through LDS so each column's 128 rows leave as one 128-byte line.
+//
+// GROUPED: the columnwise copy is blocked along the tokens of each group. Tiles then walk the
+// stored (aligned) token positions: a tile of 128 positions lies inside one group's aligned
+// range, reads that group's tokens (zeros past its end) and writes all 128 positions, so the
+// padding between groups comes out as zero codes under all-zero blocks (E8M0 byte 0).
 constexpr int kMR = 128, kMC = 64;
 
+template <bool GROUPED>
 __global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const uint16_t* __restrict__ src, int64_t rows,
                                                             int64_t cols, uint8_t* __restrict__ q_row,
                                                             uint8_t* __restrict__ s_row,
                                                             uint8_t* __restrict__ q_colT,
-                                                            uint8_t* __restrict__ s_colT) {
+                                                            uint8_t* __restrict__ s_colT, int G,
+                                                            const int64_t* __restrict__ layout, int64_t ld_t) {
   __shared__ __attribute__((aligned(16))) uint16_t xt[kMC][kMR + 8];    // [column][row] bf16 bits
   const int64_t tc = (cols + kMC - 1) / kMC;
-  const int64_t r0 = (int64_t)(blockIdx.x / tc) * kMR;
+  const int64_t p0 = (int64_t)(blockIdx.x / tc) * kMR;     // first row (dense) or stored position
   const int64_t c0 = (int64_t)(blockIdx.x % tc) * kMC;
+  int64_t r0 = p0;               // first source row of the tile
+  int64_t nrows = rows - p0;     // source rows of the tile that exist
+  int64_t npos = rows - p0;      // columnwise positions the tile writes
+  if constexpr (GROUPED) {
+    const int64_t* c = layout;
+    const int64_t* pad = layout + G + 1;
+    if (p0 >= pad[G]) return;                             // past the last group (block-uniform)
+    int lo = 0, hi = G - 1;                               // last g with pad[g] <= p0
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pad[mid] <= p0) lo = mid;
+      else hi = mid - 1;
+    }
+    r0 = c[lo] + (p0 - pad[lo]);
+    nrows = c[lo + 1] - r0;                               // >= 1: aligned lengths round up
+    npos = kMR;                                           // pad[lo + 1] - p0 >= 128
+    // a layout not made for these rows reads nothing out of range
+    r0 = r0 < 0 ? 0 : (r0 > rows ? rows : r0);
+    nrows = nrows > rows - r0 ? rows - r0 : nrows;
+  }
   const int t = threadIdx.x;
   const int lr = t >> 3;                 // 0..31
   const int cc = t & 7;                  // column chunk of 8
@@ -195,7 +222,7 @@ __global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const uint16_t* __r
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int64_t r = r0 + lr + 32 * k;
-    ok[k] = r < rows && c < cols;
+    ok[k] = lr + 32 * k < nrows && c < cols;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (ok[k]) v = *reinterpret_cast<const uint4*>(src + r * cols + c);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -265,11 +292,12 @@ __global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const uint16_t* __r
       const uint32_t hi = e4m3x2(bf16_lo(w[2 * i + 1]) * sc, bf16_hi(w[2 * i + 1]) * sc);
       o[i] = lo | (hi << 16);
     }
-    if (c0 + col < cols && r0 + 32 * k < rows) {
-      uint8_t* dst = q_colT + (c0 + col) * rows + r0 + 32 * k;
+    const int64_t ldc = GROUPED ? ld_t : rows;
+    if (c0 + col < cols && 32 * k < npos) {
+      uint8_t* dst = q_colT + (c0 + col) * ldc + p0 + 32 * k;
       *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
       *reinterpret_cast<uint4*>(dst + 16) = make_uint4(o[4], o[5], o[6], o[7]);
-      s_colT[(c0 + col) * (rows / 32) + (r0 >> 5) + k] = (uint8_t)(X + 127);
+      s_colT[(c0 + col) * (ldc / 32) + (p0 >> 5) + k] = (uint8_t)(X + 127);
     }
   }
 }
@@ -278,8 +306,19 @@ hipError_t launch_quantize_mxfp8(const uint16_t* src, int64_t rows, int64_t cols
                                  uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT, hipStream_t s) {
   const int64_t tiles = ((rows + kMR - 1) / kMR) * ((cols + kMC - 1) / kMC);
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(quantize_mxfp8_kernel, dim3((unsigned)tiles), dim3(256), 0, s, src, rows, cols, q_row,
-                     s_row, q_colT, s_colT);
+  hipLaunchKernelGGL(quantize_mxfp8_kernel<false>, dim3((unsigned)tiles), dim3(256), 0, s, src, rows, cols, q_row,
+                     s_row, q_colT, s_colT, 0, nullptr, (int64_t)0);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mxfp8_grouped(const uint16_t* src, int64_t rows, int64_t cols, int G,
+                                         const int64_t* layout, int64_t ld_t, uint8_t* q_row, uint8_t* s_row,
+                                         uint8_t* q_colT, uint8_t* s_colT, hipStream_t s) {
+  // one tile per 128 stored positions (ld_t bounds every group's aligned end) x 64 columns
+  const int64_t tiles = (ld_t / kMR) * ((cols + kMC - 1) / kMC);
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_mxfp8_kernel<true>, dim3((unsigned)tiles), dim3(256), 0, s, src, rows, cols, q_row,
+                     s_row, q_colT, s_colT, G, layout, ld_t);
   return hipGetLastError();
 }
 

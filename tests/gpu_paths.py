@@ -155,4 +155,94 @@ def run_grouped_mlp_fwd_mx(inp):
     y_unfused = quant_mx(y, col=False)                    # the standalone quantizer on the bf16 y
     torch.cuda.synchronize()
     return {"err": err, "qx": qx, "qw1": qw1, "qw2": qw2, "h": h, "y": y, "yq": yq, "ys": ys, "out": out,
-            "y_unfused": y_unfused}
+            "y_unfused": y_unfused, "base": base}
+
+
+# ------------------------------------------------------- MXFP8 grouped backward
+def mx_layout(base, T):
+    """[2, G+1] device layout (clamped offsets, 128-aligned starts) of device offsets ``base``."""
+    lay = torch.empty(2, base.numel(), dtype=torch.int64, device="cuda")
+    sge.mx_group_layout(base, T, lay)
+    return lay
+
+
+def quant_mx_grouped(t, lay, row=False, fill=None):
+    """Token-blocked MXFP8 of device bf16 ``t`` [T, C] (+ the rowwise copy when ``row``).
+    ``fill``: byte value the transposed outputs start with (to see what is left unwritten)."""
+    T, C = t.shape
+    G = lay.shape[1] - 1
+    ld = sge.mx_token_capacity(T, G)
+    mk = (lambda *s: torch.full(s, fill, dtype=torch.uint8, device="cuda")) if fill is not None else \
+        (lambda *s: torch.empty(*s, dtype=torch.uint8, device="cuda"))
+    out = {"q_colT": mk(C, ld), "s_colT": mk(C, ld // 32), "ld": ld}
+    kw = {}
+    if row:
+        out["q_row"] = torch.empty(T, C, dtype=torch.uint8, device="cuda")
+        out["s_row"] = torch.empty(T, C // 32, dtype=torch.uint8, device="cuda")
+        kw.update(q_row=out["q_row"], s_row=out["s_row"])
+    sge.quantize_mxfp8_grouped(t, lay, out["q_colT"], out["s_colT"], **kw)
+    return out
+
+
+def grouped_dgrad_mx(q_dy, w_colT, base, alpha=1.0, preact=None, probs=None, want_q=False):
+    """MXFP8 grouped dgrad from a rowwise-quantized dy and W's columnwise copy [K, G*N].
+    With ``preact`` the scaled-SwiGLU backward runs in the epilogue (dact, dprobs, and the
+    MXFP8 dact when ``want_q``); otherwise dx [T, K] is returned."""
+    T, N = q_dy["q_row"].shape
+    K = w_colT["q_colT"].shape[0]
+    G = base.numel() - 1
+    out = {}
+    if preact is None:
+        out["dx"] = torch.empty(T, K, dtype=torch.bfloat16, device="cuda")
+        sge.grouped_linear_dgrad_mxfp8(q_dy["q_row"], q_dy["s_row"], w_colT["q_colT"], w_colT["s_colT"], base,
+                                       alpha=alpha, dx=out["dx"])
+        return out
+    ws = torch.empty(max(1, sge.grouped_linear_bwd_workspace_size(T, K, G, sge.EPI_DSCALED_SWIGLU)),
+                     dtype=torch.uint8, device="cuda")
+    out["dact"] = torch.empty(T, 2 * K, dtype=torch.bfloat16, device="cuda")
+    out["dprobs"] = torch.empty(T, dtype=torch.float32, device="cuda")
+    if want_q:
+        out["dact_q"] = torch.empty(T, 2 * K, dtype=torch.uint8, device="cuda")
+        out["dact_s"] = torch.empty(T, 2 * K // 32, dtype=torch.uint8, device="cuda")
+    sge.grouped_linear_dgrad_mxfp8(q_dy["q_row"], q_dy["s_row"], w_colT["q_colT"], w_colT["s_colT"], base,
+                                   alpha=alpha, epilogue=sge.EPI_DSCALED_SWIGLU, preact=preact, probs=probs,
+                                   dact=out["dact"], dprobs=out["dprobs"], dact_q=out.get("dact_q"),
+                                   dact_s=out.get("dact_s"), workspace=ws)
+    return out
+
+
+def grouped_wgrad_mx(qa, qb, lay, G, alpha=1.0):
+    """dW [G, N, K] from the token-blocked operands of dy (qa) and x (qb)."""
+    N, K = qa["q_colT"].shape[0], qb["q_colT"].shape[0]
+    dw = torch.empty(G, N, K, dtype=torch.bfloat16, device="cuda")
+    sge.grouped_linear_wgrad_mxfp8(qa["q_colT"], qa["s_colT"], qb["q_colT"], qb["s_colT"], lay, dw, alpha=alpha)
+    return dw
+
+
+def run_grouped_mlp_bwd_mx(inp, fwd):
+    """MXFP8 grouped MLP backward after ``run_grouped_mlp_fwd_mx``: fc2 dgrad with the fused
+    scaled-SwiGLU backward and group quantize of dh, fc2 wgrad, fc1 dgrad on the MXFP8 dh,
+    fc1 wgrad; every wgrad operand token-blocked per group."""
+    X, W1, W2 = dev_bf16(inp["x"]), dev_bf16(inp["w1"]), dev_bf16(inp["w2"])
+    DOUT = dev_bf16(inp["dout"])
+    P = torch.from_numpy(inp["p"]).cuda()
+    T, H = X.shape
+    G, N1, _ = W1.shape
+    F = N1 // 2
+    base = fwd["base"]
+    lay = mx_layout(base, T)
+    q_dout = quant_mx_grouped(DOUT, lay, row=True)
+    w2c = quant_mx(W2.reshape(G * H, F), row=False, col=True)        # [F, G*H]
+    w1c = quant_mx(W1.reshape(G * N1, H), row=False, col=True)       # [H, G*2F]
+    d2 = grouped_dgrad_mx(q_dout, w2c, base, preact=fwd["h"], probs=P, want_q=True)
+    q_y = quant_mx_grouped(fwd["y"], lay)
+    dw2 = grouped_wgrad_mx(q_dout, q_y, lay, G)
+    d1 = grouped_dgrad_mx({"q_row": d2["dact_q"], "s_row": d2["dact_s"]}, w1c, base)
+    q_dh = quant_mx_grouped(d2["dact"], lay)
+    q_x = quant_mx_grouped(X, lay)
+    dw1 = grouped_wgrad_mx(q_dh, q_x, lay, G)
+    dh_unfused = quant_mx(d2["dact"], col=False)                     # the standalone quantizer on dh
+    torch.cuda.synchronize()
+    return {"lay": lay, "q_dout": q_dout, "w2c": w2c, "w1c": w1c, "dh": d2["dact"], "dp": d2["dprobs"],
+            "dhq": d2["dact_q"], "dhs": d2["dact_s"], "dh_unfused": dh_unfused, "dw2": dw2, "dx": d1["dx"],
+            "dw1": dw1, "q_y": q_y, "q_dh": q_dh, "q_x": q_x}

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol(sge):
     lib = ctypes.CDLL(sge.library_path())
     for name in _declared():
         assert hasattr(lib, name), name
-    assert sge.abi_version() == 2
+    assert sge.abi_version() == 3
 
 
 def test_status_strings(sge):
@@ -173,3 +173,83 @@ def test_grouped_mxfp8_validation_errors(sge):
     args = list(ok_args); args[15] = y
     assert f(*args) == sge.ERR_ALIAS                                      # out_s over out
 
+
+
+def test_mx_token_capacity(sge):
+    assert sge.mx_token_capacity(65536, 8) == 65536 + 8 * 128
+    assert sge.mx_token_capacity(560, 6) == 640 + 6 * 128
+    assert sge.mx_token_capacity(0, 1) == 128
+    assert sge.mx_token_capacity(-1, 1) == -1 and sge.mx_token_capacity(10, 0) == -1
+
+
+def test_mxfp8_grouped_backward_validation_errors(sge):
+    def B(k):                      # far-apart fake addresses (no accidental overlaps)
+        return FAKE * 8 * k
+
+    lay = sge._lib.sge_mx_group_layout
+    assert lay(None, 4, 100, FAKE, None) == sge.ERR_NULL
+    assert lay(FAKE, 0, 100, B(2), None) == sge.ERR_ARG
+    assert lay(FAKE, 4097, 100, B(2), None) == sge.ERR_ARG
+    assert lay(FAKE, 4, -1, B(2), None) == sge.ERR_SHAPE
+    assert lay(FAKE, 4, 100, FAKE + 16, None) == sge.ERR_ALIAS           # layout over offsets
+
+    q = sge._lib.sge_quantize_mxfp8_grouped
+    T, C, G = 100, 64, 4
+    ld = sge.mx_token_capacity(T, G)
+    ok = [B(1), T, C, G, B(3), ld, B(5), B(7), B(9), B(11), None]
+    a = list(ok); a[8] = None
+    assert q(*a) == sge.ERR_NULL                                          # q_colT required
+    a = list(ok); a[7] = None
+    assert q(*a) == sge.ERR_NULL                                          # q_row without s_row
+    a = list(ok); a[2] = 48
+    assert q(*a) == sge.ERR_SHAPE                                         # cols % 32
+    a = list(ok); a[5] = ld - 128
+    assert q(*a) == sge.ERR_SHAPE                                         # ld below capacity
+    a = list(ok); a[5] = ld + 64
+    assert q(*a) == sge.ERR_SHAPE                                         # ld % 128
+    a = list(ok); a[8] = B(9) + 8
+    assert q(*a) == sge.ERR_ALIGN
+    a = list(ok); a[8] = B(1)
+    assert q(*a) == sge.ERR_ALIAS                                         # q_colT over src
+    a = list(ok); a[9] = B(3)
+    assert q(*a) == sge.ERR_ALIAS                                         # s_colT over layout
+
+    d = sge._lib.sge_grouped_linear_dgrad_mxfp8
+    G, T, N, K = 4, 100, 256, 512
+    sw = sge.EPI_DSCALED_SWIGLU
+    ws = sge.grouped_linear_bwd_workspace_size(T, K, G, sw)
+    ok = [B(1), B(2), B(3), B(4), G, T, N, K, B(5), 1.0, sw, B(6), B(7), None,
+          B(8), B(9), B(10), B(11), B(12), ws, None]
+    a = list(ok); a[11] = None
+    assert d(*a) == sge.ERR_NULL                                          # SwiGLU needs preact
+    a = list(ok); a[14] = None; a[16] = None; a[17] = None
+    assert d(*a) == sge.ERR_NULL                                          # no output
+    a = list(ok); a[17] = None
+    assert d(*a) == sge.ERR_NULL                                          # dact_q without dact_s
+    a = list(ok); a[10] = sge.EPI_NONE; a[13] = B(13)
+    assert d(*a) == sge.ERR_ARG                                           # quantized output needs SwiGLU
+    a = list(ok); a[6] = 96
+    assert d(*a) == sge.ERR_SHAPE                                         # N % 128
+    a = list(ok); a[7] = 520
+    assert d(*a) == sge.ERR_SHAPE                                         # SwiGLU K % 32
+    a = list(ok); a[16] = B(10) + 4
+    assert d(*a) == sge.ERR_ALIGN
+    a = list(ok); a[14] = B(6)
+    assert d(*a) == sge.ERR_ALIAS                                         # dact over preact
+    a = list(ok); a[16] = B(8)
+    assert d(*a) == sge.ERR_ALIAS                                         # dact_q over dact
+    a = list(ok); a[19] = ws - 4
+    assert d(*a) == sge.ERR_WORKSPACE
+
+    w = sge._lib.sge_grouped_linear_wgrad_mxfp8
+    ok = [B(1), B(2), B(3), B(4), G, N, K, B(5), 640, 1.0, B(6), None]
+    a = list(ok); a[10] = None
+    assert w(*a) == sge.ERR_NULL
+    a = list(ok); a[8] = 600
+    assert w(*a) == sge.ERR_SHAPE                                         # ld % 128
+    a = list(ok); a[4] = 0
+    assert w(*a) == sge.ERR_SHAPE
+    a = list(ok); a[10] = B(6) + 2
+    assert w(*a) == sge.ERR_ALIGN
+    a = list(ok); a[10] = B(3)
+    assert w(*a) == sge.ERR_ALIAS                                         # dw over xT_q
