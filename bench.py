@@ -187,29 +187,7 @@ def build_grouped(torch, sge, wl, inp):
 
     base = offs[0]
     if wl["fmt"] == "mxfp8":
-        # forward on MXFP8 operands: x and both weights quantized rowwise each step, fc1's
-        # scaled SwiGLU emits its output as MXFP8 for fc2 (and the bf16 pre-activation)
-        u8 = dict(dtype=torch.uint8, device="cuda")
-        qx, sx = torch.empty(T, H, **u8), torch.empty(T, H // 32, **u8)
-        qw1, sw1 = torch.empty(G * N1, H, **u8), torch.empty(G * N1, H // 32, **u8)
-        qw2, sw2 = torch.empty(G * H, F, **u8), torch.empty(G * H, F // 32, **u8)
-        qy, sy = torch.empty(T, F, **u8), torch.empty(T, F // 32, **u8)
-        W1f, W2f = W1.reshape(G * N1, H), W2.reshape(G * H, F)
-        flops = {"fc1_fwd": 2 * T * N1 * H, "fc2_fwd": 2 * T * H * F}
-        hbm = {"quant_x": T * H * 3 + T * H // 32, "quant_w1": G * N1 * H * 3 + G * N1 * H // 32,
-               "quant_w2": G * H * F * 3 + G * H * F // 32}
-        launches = [
-            ("offsets", lambda: sge.splits_to_offsets(splits, [1, H], offs)),
-            ("quant_x", lambda: sge.quantize_mxfp8(X, q_row=qx, s_row=sx)),
-            ("quant_w1", lambda: sge.quantize_mxfp8(W1f, q_row=qw1, s_row=sw1)),
-            ("quant_w2", lambda: sge.quantize_mxfp8(W2f, q_row=qw2, s_row=sw2)),
-            ("fc1_fwd", lambda: sge.grouped_linear_fwd_mxfp8(
-                qx, sx, qw1.view(G, N1, H), sw1.view(G, N1, H // 32), base, out=None,
-                epilogue=sge.EPI_SCALED_SWIGLU, probs=P, preact=h, out_q=qy, out_s=sy)),
-            ("fc2_fwd", lambda: sge.grouped_linear_fwd_mxfp8(qy, sy, qw2.view(G, H, F), sw2.view(G, H, F // 32),
-                                                             base, out=out)),
-        ]
-        return launches, flops, hbm
+        return build_grouped_mx(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, dh, dp, dw2, dx, dw1, ws)
     launches = [
         ("offsets", lambda: sge.splits_to_offsets(splits, [1, H], offs)),
         ("fc1_fwd", lambda: sge.grouped_linear_fwd(X, W1, base, y, epilogue=sge.EPI_SCALED_SWIGLU, probs=P,
@@ -222,6 +200,79 @@ def build_grouped(torch, sge, wl, inp):
         ("fc1_wgrad", lambda: sge.grouped_linear_bwd(dh, X, W1, base, dw=dw1)),
     ]
     return launches, flops, {}
+
+
+def build_grouped_mx(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, dh, dp, dw2, dx, dw1, ws):
+    """The grouped MLP on MXFP8 operands: every GEMM operand quantized each step, blocked along
+    that GEMM's contraction (rowwise for the forward and the dgrads, W's columnwise copy for
+    the dgrads, per-group token blocks for the wgrads). fc1's scaled SwiGLU emits its output
+    as MXFP8 for fc2, and fc2's dgrad emits dh as MXFP8 for fc1's dgrad."""
+    T, H = X.shape
+    G, N1, _ = W1.shape
+    F = N1 // 2
+    bwd = "bwd" in wl["passes"]
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    base = offs[0]
+    qx, sx = torch.empty(T, H, **u8), torch.empty(T, H // 32, **u8)
+    qw1, sw1 = torch.empty(G * N1, H, **u8), torch.empty(G * N1, H // 32, **u8)
+    qw2, sw2 = torch.empty(G * H, F, **u8), torch.empty(G * H, F // 32, **u8)
+    qy, sy = torch.empty(T, F, **u8), torch.empty(T, F // 32, **u8)
+    W1f, W2f = W1.reshape(G * N1, H), W2.reshape(G * H, F)
+    flops = {"fc1_fwd": 2 * T * N1 * H, "fc2_fwd": 2 * T * H * F}
+    if not bwd:
+        hbm = {"quant_x": T * H * 3 + T * H // 32, "quant_w1": G * N1 * H * 3 + G * N1 * H // 32,
+               "quant_w2": G * H * F * 3 + G * H * F // 32}
+        return [
+            ("offsets", lambda: sge.splits_to_offsets(splits, [1, H], offs)),
+            ("quant_x", lambda: sge.quantize_mxfp8(X, q_row=qx, s_row=sx)),
+            ("quant_w1", lambda: sge.quantize_mxfp8(W1f, q_row=qw1, s_row=sw1)),
+            ("quant_w2", lambda: sge.quantize_mxfp8(W2f, q_row=qw2, s_row=sw2)),
+            ("fc1_fwd", lambda: sge.grouped_linear_fwd_mxfp8(
+                qx, sx, qw1.view(G, N1, H), sw1.view(G, N1, H // 32), base, out=None,
+                epilogue=sge.EPI_SCALED_SWIGLU, probs=P, preact=h, out_q=qy, out_s=sy)),
+            ("fc2_fwd", lambda: sge.grouped_linear_fwd_mxfp8(qy, sy, qw2.view(G, H, F), sw2.view(G, H, F // 32),
+                                                             base, out=out)),
+        ], flops, hbm
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    ld = sge.mx_token_capacity(T, G)
+    lay = torch.empty(2, G + 1, dtype=torch.int64, device="cuda")
+    y = torch.empty(T, F, **bf)
+    qxT, sxT = torch.empty(H, ld, **u8), torch.empty(H, ld // 32, **u8)
+    qw1T, sw1T = torch.empty(H, G * N1, **u8), torch.empty(H, G * N1 // 32, **u8)
+    qw2T, sw2T = torch.empty(F, G * H, **u8), torch.empty(F, G * H // 32, **u8)
+    qyT, syT = torch.empty(F, ld, **u8), torch.empty(F, ld // 32, **u8)
+    qd, sd = torch.empty(T, H, **u8), torch.empty(T, H // 32, **u8)
+    qdT, sdT = torch.empty(H, ld, **u8), torch.empty(H, ld // 32, **u8)
+    qdh, sdh = torch.empty(T, N1, **u8), torch.empty(T, N1 // 32, **u8)
+    qdhT, sdhT = torch.empty(N1, ld, **u8), torch.empty(N1, ld // 32, **u8)
+    flops.update({"fc2_dgrad_dswiglu": 2 * T * H * F, "fc2_wgrad": 2 * T * H * F, "fc1_dgrad": 2 * T * N1 * H,
+                  "fc1_wgrad": 2 * T * N1 * H})
+    # algorithmic bytes: bf16 read, E4M3 written per copy, one E8M0 byte per 32 (padding not counted)
+    hbm = {"quant_x": T * H * 4 + T * H // 16, "quant_w1": G * N1 * H * 4 + G * N1 * H // 16,
+           "quant_w2": G * H * F * 4 + G * H * F // 16, "quant_y": T * F * 3 + T * F // 32,
+           "quant_dout": T * H * 4 + T * H // 16, "quant_dh": T * N1 * 3 + T * N1 // 32}
+    launches = [
+        ("offsets", lambda: sge.splits_to_offsets(splits, [1, H], offs)),
+        ("mx_layout", lambda: sge.mx_group_layout(base, T, lay)),
+        ("quant_x", lambda: sge.quantize_mxfp8_grouped(X, lay, qxT, sxT, q_row=qx, s_row=sx)),
+        ("quant_w1", lambda: sge.quantize_mxfp8(W1f, q_row=qw1, s_row=sw1, q_colT=qw1T, s_colT=sw1T)),
+        ("quant_w2", lambda: sge.quantize_mxfp8(W2f, q_row=qw2, s_row=sw2, q_colT=qw2T, s_colT=sw2T)),
+        ("fc1_fwd", lambda: sge.grouped_linear_fwd_mxfp8(
+            qx, sx, qw1.view(G, N1, H), sw1.view(G, N1, H // 32), base, out=y,
+            epilogue=sge.EPI_SCALED_SWIGLU, probs=P, preact=h, out_q=qy, out_s=sy)),
+        ("quant_y", lambda: sge.quantize_mxfp8_grouped(y, lay, qyT, syT)),
+        ("fc2_fwd", lambda: sge.grouped_linear_fwd_mxfp8(qy, sy, qw2.view(G, H, F), sw2.view(G, H, F // 32),
+                                                         base, out=out)),
+        ("quant_dout", lambda: sge.quantize_mxfp8_grouped(DOUT, lay, qdT, sdT, q_row=qd, s_row=sd)),
+        ("fc2_dgrad_dswiglu", lambda: sge.grouped_linear_dgrad_mxfp8(
+            qd, sd, qw2T, sw2T, base, epilogue=sge.EPI_DSCALED_SWIGLU, preact=h, probs=P, dact=dh, dprobs=dp,
+            dact_q=qdh, dact_s=sdh, workspace=ws)),
+        ("fc2_wgrad", lambda: sge.grouped_linear_wgrad_mxfp8(qdT, sdT, qyT, syT, lay, dw2)),
+        ("quant_dh", lambda: sge.quantize_mxfp8_grouped(dh, lay, qdhT, sdhT)),
+        ("fc1_dgrad", lambda: sge.grouped_linear_dgrad_mxfp8(qdh, sdh, qw1T, sw1T, base, dx=dx)),
+        ("fc1_wgrad", lambda: sge.grouped_linear_wgrad_mxfp8(qdhT, sdhT, qxT, sxT, lay, dw1)),
+    ]
+    return launches, flops, hbm
 
 
 # ----------------------------------------------------------- CPU baseline
@@ -269,20 +320,24 @@ def cpu_baseline(wl, inp, target_s):
     elif wl["fmt"] == "mxfp8":
         T = inp["x"].shape[0]
         tok = 256
+        bwd = "bwd" in wl["passes"]
         while True:
             t0 = time.perf_counter()
             # first `tok` tokens, all routed to expert 0 (its weights only are quantized)
-            grouped.grouped_mlp_fwd_mxfp8(inp["x"][:tok], inp["w1"][:1], inp["w2"][:1], inp["p"][:tok],
-                                          np.array([0, tok], np.int64))
+            b1 = np.array([0, tok], np.int64)
+            f = grouped.grouped_mlp_fwd_mxfp8(inp["x"][:tok], inp["w1"][:1], inp["w2"][:1], inp["p"][:tok], b1)
+            if bwd:
+                grouped.grouped_mlp_bwd_mxfp8(inp["x"][:tok], inp["w1"][:1], inp["w2"][:1], inp["p"][:tok], b1,
+                                              inp["dout"][:tok], fwd=f)
             dt = time.perf_counter() - t0
             if dt >= target_s / 4 or tok >= T:
                 break
             tok = min(T, tok * 4)
         H = inp["x"].shape[1]
         N1 = inp["w1"].shape[1]
-        flops = 2 * tok * N1 * H + 2 * tok * H * (N1 // 2)
-        sample = (f"first {tok} of {T} tokens through the MXFP8 grouped MLP forward with one expert "
-                  "(quantization of that expert's weights included)")
+        flops = (3 if bwd else 1) * (2 * tok * N1 * H + 2 * tok * H * (N1 // 2))
+        sample = (f"first {tok} of {T} tokens through the MXFP8 grouped MLP {'forward + backward' if bwd else 'forward'}"
+                  " with one expert (quantization of that expert's weights included)")
     else:
         T = inp["x"].shape[0]
         tok = 256

@@ -107,9 +107,12 @@ WORKLOADS = {
                                          passes=("fwd", "dgrad", "wgrad")),
     "grouped_swiglu_mlp_T65536_G8": dict(kind="grouped", fmt="bf16", T=65536, G=8, hidden=2048,
                                          ffn=2048, alpha=1.0),
-    # the same grouped MLP forward on MXFP8 operands, fc1's activation quantized for fc2
+    # the same grouped MLP on MXFP8 operands, fc1's activation quantized for fc2 (forward only,
+    # and forward + backward)
     "mxfp8_grouped_swiglu_mlp_fwd_T65536_G8": dict(kind="grouped", fmt="mxfp8", T=65536, G=8, hidden=2048,
                                                    ffn=2048, alpha=1.0, passes=("fwd",)),
+    "mxfp8_grouped_swiglu_mlp_T65536_G8": dict(kind="grouped", fmt="mxfp8", T=65536, G=8, hidden=2048,
+                                               ffn=2048, alpha=1.0, passes=("fwd", "bwd")),
 }
 
 

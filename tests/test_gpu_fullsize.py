@@ -10,9 +10,9 @@ import torch
 
 import synth
 from oracle import grouped, linear, offsets, quant
-from oracle.codecs import bf16_to_f64
+from oracle.codecs import bf16_to_f64, f64_to_bf16
 
-from .gpu_paths import run_dense, run_grouped_mlp, run_grouped_mlp_fwd_mx
+from .gpu_paths import run_dense, run_grouped_mlp, run_grouped_mlp_bwd_mx, run_grouped_mlp_fwd_mx
 from .helpers import TAU_BF16, TAU_FP8, assert_close, assert_mx_dequant_close, host_f64, host_u8
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -172,3 +172,52 @@ def test_grouped_mxfp8_forward_full_size_sampled():
         assert_mx_dequant_close(y_deq, quant.mx_dequantize(ref["y_q"], ref["y_s"]), what=f"y (MXFP8) g{g}")
         assert_close(host_f64(got["out"][tt]), ref["out"], TAU_FP8, what=f"out g{g}", **kw)
 
+
+
+def test_grouped_mxfp8_backward_full_size_sampled():
+    name = "mxfp8_grouped_swiglu_mlp_T65536_G8"
+    print(f"case full-size {name}", flush=True)
+    inp = synth.workload_inputs(name, seed=0)
+    fwd = run_grouped_mlp_fwd_mx(inp)
+    assert int(fwd["err"].item()) == 0
+    got = run_grouped_mlp_bwd_mx(inp, fwd)
+    # the fused activation backward + group quantize equals the standalone quantizer, whole tensor
+    assert np.array_equal(host_u8(got["dhq"]), host_u8(got["dh_unfused"]["q_row"]))
+    assert np.array_equal(host_u8(got["dhs"]), host_u8(got["dh_unfused"]["s_row"]))
+    base = offsets.base_offsets(inp["splits"])
+    sizes = np.diff(base)
+    F = inp["w2"].shape[2]
+    rng = np.random.default_rng(12)
+    kw = dict(rel_tight=2.0 ** -3, abs_tight=0.1)
+    # the two smallest non-empty groups: the wgrad samples need the oracle over a whole group
+    for g in [int(v) for v in np.argsort(np.where(sizes > 0, sizes, 1 << 62))[:2]]:
+        lo, hi = int(base[g]), int(base[g + 1])
+        Tg = hi - lo
+        # per-token outputs at sampled tokens (the per-token oracle on those tokens alone)
+        toks = np.array(sorted({lo, hi - 1} | set(rng.integers(lo, hi, size=6).tolist())))
+        ref = grouped.grouped_mlp_bwd_mxfp8(inp["x"][toks], inp["w1"][g:g + 1], inp["w2"][g:g + 1],
+                                            inp["p"][toks], np.array([0, len(toks)]), inp["dout"][toks])
+        tt = torch.from_numpy(toks).cuda()
+        assert_close(host_f64(got["dh"][tt]), ref["dh"], TAU_FP8, what=f"dh g{g}", **kw)
+        assert_close(host_f64(got["dp"][tt]), ref["dp"], TAU_FP8, what=f"dprobs g{g}", **kw)
+        assert_close(host_f64(got["dx"][tt]), ref["dx"], TAU_FP8, what=f"dx g{g}", **kw)
+        # weight-gradient entries: sampled columns of the group's activations, over all its tokens
+        fs = _pick(F, 6, rng)
+        hs = _pick(inp["x"].shape[1], 6, rng)
+        xg, doutg, pg = inp["x"][lo:hi], inp["dout"][lo:hi], inp["p"][lo:hi]
+        x_hat = quant.mx_dequantize(*quant.mxfp8_rowwise(xg))
+        rows1 = np.concatenate([fs, F + fs])                          # gate rows fs and up rows F + fs
+        w1_hat = quant.mx_dequantize(*quant.mxfp8_rowwise(inp["w1"][g][rows1]))
+        h_sub = x_hat @ w1_hat.T                                      # [Tg, 2k]: a | b of the sampled columns
+        y_bits = f64_to_bf16(grouped.scaled_swiglu_fwd(h_sub, pg))
+        one = np.array([0, Tg])
+        ref_dw2 = grouped.grouped_linear_wgrad_mxfp8(doutg[:, hs], y_bits, one)[0]
+        assert_close(host_f64(got["dw2"][g][torch.from_numpy(hs).cuda()][:, torch.from_numpy(fs).cuda()]),
+                     ref_dw2, TAU_FP8, what=f"dw2 g{g}", **kw)
+        dout_hat = quant.mx_dequantize(*quant.mxfp8_rowwise(doutg))
+        w2c_hat = quant.mx_dequantize(*quant.mxfp8_colwise(inp["w2"][g][:, fs]))    # [k, H] blocked along H
+        gy = dout_hat @ w2c_hat.T                                     # [Tg, k]
+        dh_sub, _ = grouped.scaled_swiglu_bwd(gy, bf16_to_f64(f64_to_bf16(h_sub)), pg)
+        ref_dw1 = grouped.grouped_linear_wgrad_mxfp8(f64_to_bf16(dh_sub), xg[:, hs], one)[0]
+        assert_close(host_f64(got["dw1"][g][torch.from_numpy(rows1).cuda()][:, torch.from_numpy(hs).cuda()]),
+                     ref_dw1, TAU_FP8, what=f"dw1 g{g}", **kw)
