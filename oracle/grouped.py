@@ -21,8 +21,8 @@ Readings where the page is silent:
 import numpy as np
 
 from .codecs import bf16_to_f64, f64_to_bf16
-from .quant import (MX_TOKEN_ALIGN, mx_dequantize, mx_group_layout, mxfp8_colwise,
-                    mxfp8_colwise_grouped, mxfp8_rowwise)
+from .quant import (MX_TOKEN_ALIGN, fp8_current_scaling_grouped, fp8_dequantize, mx_dequantize,
+                    mx_group_layout, mxfp8_colwise, mxfp8_colwise_grouped, mxfp8_rowwise)
 
 
 def _groups(base):
@@ -222,3 +222,61 @@ def grouped_mlp_bwd_mxfp8(x_bits, w1_bits, w2_bits, p, base, dout_bits, fwd=None
     dw1 = grouped_linear_wgrad_mxfp8(dh_bits, x_bits, base)
     return {"gy": gy, "dh": dh, "dh_bits": dh_bits, "dh_q": dh_q, "dh_s": dh_s, "dp": dp,
             "dw2": dw2, "dx": dx, "dw1": dw1}
+
+
+# ------------------------------------------------ FP8 current scaling, grouped -----
+def _fp8_groups_hat(bits, c):
+    """Exact values of a per-group current-scaled tensor (rows c[g] .. c[g+1]-1 share a scale)."""
+    r = fp8_current_scaling_grouped(bits, c, c)
+    out = np.zeros(np.asarray(bits).shape, np.float64)
+    for g in range(len(c) - 1):
+        lo, hi = int(c[g]), int(c[g + 1])
+        out[lo:hi] = fp8_dequantize(r["q"][lo:hi], r["scale_inv"][g])
+    return out
+
+
+def _fp8_experts_hat(w_bits):
+    """Exact values of each expert's weight W_g [N, K] quantized as its own tensor."""
+    w_bits = np.asarray(w_bits, np.uint16)
+    G, N, K = w_bits.shape
+    c = np.arange(G + 1, dtype=np.int64) * N
+    return _fp8_groups_hat(w_bits.reshape(G * N, K), c).reshape(G, N, K)
+
+
+def grouped_mlp_fwd_fp8(x_bits, w1_bits, w2_bits, p, base):
+    """Grouped MLP forward on FP8 operands with per-group current scaling.
+
+    Every GEMM operand is E4M3 with one scale per group ("Activation + GroupedLinear Fusion for
+    MOE and other MOE optimizations", Description: group quantize; fp8_current_scaling in the
+    grouped-MLP test matrix): x's slice of each group, each W1_g and W2_g, and fc1's
+    activation, which is rounded to bf16 and then quantized per group for fc2. Per-tensor
+    scales are orientation-free, so the same codes serve every GEMM of the backward.
+    Returns h, y (fp64), y_bits (bf16) and out (fp64).
+    """
+    T = np.asarray(x_bits).shape[0]
+    c, _ = mx_group_layout(base, T)
+    h = grouped_linear_fwd(_fp8_groups_hat(x_bits, c), _fp8_experts_hat(w1_bits), base)
+    y = scaled_swiglu_fwd(h, p)
+    y_bits = f64_to_bf16(y)
+    out = grouped_linear_fwd(_fp8_groups_hat(y_bits, c), _fp8_experts_hat(w2_bits), base)
+    return {"h": h, "y": y, "y_bits": y_bits, "out": out}
+
+
+def grouped_mlp_bwd_fp8(x_bits, w1_bits, w2_bits, p, base, dout_bits, fwd=None):
+    """Backward of ``grouped_mlp_fwd_fp8``: dout, dh, x, y and every W_g are E4M3 with one
+    current-scaling scale per group; h is the forward's bf16 pre-activation and dh is rounded
+    to bf16 before it is quantized. Returns gy, dh (fp64), dh_bits, dp, dw2, dx, dw1."""
+    if fwd is None:
+        fwd = grouped_mlp_fwd_fp8(x_bits, w1_bits, w2_bits, p, base)
+    T = np.asarray(x_bits).shape[0]
+    c, _ = mx_group_layout(base, T)
+    dout_hat = _fp8_groups_hat(dout_bits, c)
+    w1_hat, w2_hat = _fp8_experts_hat(w1_bits), _fp8_experts_hat(w2_bits)
+    gy = grouped_linear_dgrad(dout_hat, w2_hat, base)
+    dh, dp = scaled_swiglu_bwd(gy, bf16_to_f64(f64_to_bf16(fwd["h"])), p)
+    dh_bits = f64_to_bf16(dh)
+    dh_hat = _fp8_groups_hat(dh_bits, c)
+    dw2 = grouped_linear_wgrad(dout_hat, _fp8_groups_hat(fwd["y_bits"], c), base)
+    dx = grouped_linear_dgrad(dh_hat, w1_hat, base)
+    dw1 = grouped_linear_wgrad(dh_hat, _fp8_groups_hat(x_bits, c), base)
+    return {"gy": gy, "dh": dh, "dh_bits": dh_bits, "dp": dp, "dw2": dw2, "dx": dx, "dw1": dw1}

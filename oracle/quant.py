@@ -196,3 +196,37 @@ def mxfp8_colwise_grouped(x_bits, c, pad, ld):
         q[:, pad[g]:pad[g] + L] = qg
         s[:, pad[g] // MX_BLOCK:(pad[g] + L) // MX_BLOCK] = sg
     return q, s
+
+
+# ---------------------------------------- FP8 current scaling per group ------
+# A group quantize hands each group's slice of a grouped tensor (and each expert's weight) a
+# quantizer of its own ("Activation + GroupedLinear Fusion for MOE and other MOE
+# optimizations", Description: grouped scaled activations followed by a group quantize; Greptile
+# Summary: fp8_current_scaling in the grouped-MLP test matrix). With current scaling that
+# means one amax, scale and scale_inv per group. The transposed copy a grouped wgrad reads uses
+# the aligned layout of ``mx_group_layout`` (zero codes between groups).
+def fp8_current_scaling_grouped(x_bits, c, pad, ld=None):
+    """Per-group FP8 current scaling of a bf16 matrix [T, C] with group rows c[g] .. c[g+1]-1.
+
+    Returns amax, scale, scale_inv (float32 [G]), q (uint8 [T, C]; rows outside every group
+    are left 0) and, when ``ld`` is given, q_t (uint8 [C, ld]): group g's row t at column
+    pad[g] + t - c[g], zeros elsewhere.
+    """
+    x = np.asarray(x_bits, np.uint16)
+    T, C = x.shape
+    G = len(c) - 1
+    amax_g = np.zeros(G, np.float32)
+    scale_g = np.zeros(G, np.float32)
+    sinv_g = np.zeros(G, np.float32)
+    q = np.zeros((T, C), np.uint8)
+    q_t = None if ld is None else np.zeros((C, ld), np.uint8)
+    for g in range(G):
+        lo, hi = int(c[g]), int(c[g + 1])
+        a = amax(x[lo:hi])
+        s = fp8_scale(a)
+        amax_g[g], scale_g[g], sinv_g[g] = a, s, fp8_scale_inv(s)
+        qg = fp8_quantize_with_scale(x[lo:hi], s)
+        q[lo:hi] = qg
+        if q_t is not None:
+            q_t[:, int(pad[g]):int(pad[g]) + (hi - lo)] = qg.T
+    return {"amax": amax_g, "scale": scale_g, "scale_inv": sinv_g, "q": q, "q_t": q_t}

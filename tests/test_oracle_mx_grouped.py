@@ -1,9 +1,11 @@
-"""Pins of the oracle's MXFP8 grouped forward and its bf16 encoder.
+"""Pins of the oracle's quantized grouped path: MXFP8 forward and backward, FP8 current
+scaling per group, and the bf16 encoder they round through.
 
 The encoder is pinned against every bf16 pattern, exact midpoints (ties to even) and torch's
-float32 -> bfloat16 conversion. The composed MXFP8 grouped MLP forward is pinned against a
-brute-force pure-Python evaluation on tiny shapes: exact rationals for the roundings, a scan
-over all 256 E4M3 codes for the nearest code, and math.fsum for the dot products.
+float32 -> bfloat16 conversion. The group layout is pinned on hand-worked offsets. Everything
+else is pinned against brute-force pure-Python evaluations on tiny shapes: exact rationals for
+the roundings, a scan over all 256 E4M3 codes for the nearest code, blocks and scales rebuilt
+group by group, and math.fsum for the dot products.
 """
 
 import math
@@ -320,5 +322,103 @@ def test_mxfp8_grouped_backward_matches_brute_force():
         ts = range(base[g], base[g + 1])
         dw2 = [[math.fsum(dov[n][t] * yv[f][t] for t in ts) for f in range(F)] for n in range(H)]
         dw1 = [[math.fsum(dhv[n][t] * xv[k][t] for t in ts) for k in range(H)] for n in range(2 * F)]
+        np.testing.assert_allclose(got["dw2"][g], dw2, rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(got["dw1"][g], dw1, rtol=1e-12, atol=1e-15)
+
+
+# ------------------------------------------ FP8 current scaling per group (grouped path) ------
+def _f32(v):
+    return float(np.float32(v))
+
+
+def _fp8_tensor(vals):
+    """Brute-force current scaling of a list of rows sharing one scale: (codes, dequantized rows,
+    scale_inv). amax by Python max; scale = fp32(448 / amax); codes by a scan of fp32(v * scale)."""
+    flat = [v for r in vals for v in r]
+    a = max((abs(v) for v in flat), default=0.0)
+    s = np.float32(1.0) if a == 0 else np.float32(448.0) / np.float32(a)
+    sinv = _f32(np.float32(1.0) / s)
+    codes = [[_e4m3_nearest(_f32(np.float32(v) * s)) for v in r] for r in vals]
+    table = dict(E4M3)
+    deq = [[float(table[cd]) * sinv if (cd & 0x7F) else 0.0 for cd in r] for r in codes]
+    return codes, deq, sinv
+
+
+def test_fp8_current_scaling_grouped_vs_brute_force():
+    base = [0, 20, 20, 57, 60]
+    T, C = 60, 5
+    r = synth.streams(16)
+    x = synth.normal_bf16(r["x"], (T, C), 1.0, r["outliers_x"], outlier_rate=0.05)
+    c, pad = quant.mx_group_layout(base, T)
+    got = quant.fp8_current_scaling_grouped(x, c, pad, 512)
+    want_t = np.zeros((C, 512), np.uint8)
+    for g in range(4):
+        lo, hi = base[g], base[g + 1]
+        codes, _, sinv = _fp8_tensor([[_bf16_value(b) for b in row] for row in x[lo:hi]])
+        if hi > lo:
+            assert np.array_equal(got["q"][lo:hi], np.array(codes, np.uint8)), g
+            want_t[:, pad[g]:pad[g] + hi - lo] = np.array(codes, np.uint8).T
+        assert got["scale_inv"][g] == np.float32(sinv), g
+    assert got["scale"][1] == 1.0 and got["amax"][1] == 0.0               # the empty group
+    assert np.array_equal(got["q_t"], want_t)
+
+
+def test_fp8_grouped_mlp_fwd_bwd_match_brute_force():
+    T, G, H, F = 5, 2, 32, 32
+    splits = [3, 2]
+    base = [0, 3, 5]
+    grp = [0, 0, 0, 1, 1]
+    inp = synth.grouped(T, G, H, F, seed=7, splits=splits)
+    fwd = grouped.grouped_mlp_fwd_fp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base)
+    got = grouped.grouped_mlp_bwd_fp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base, inp["dout"], fwd=fwd)
+
+    vals = lambda m: [[_bf16_value(b) for b in r] for r in m]   # noqa: E731
+    xd = [None] * T
+    dod = [None] * T
+    for g in range(G):
+        lo, hi = base[g], base[g + 1]
+        _, d, _ = _fp8_tensor(vals(inp["x"][lo:hi]))
+        xd[lo:hi] = d
+        _, d, _ = _fp8_tensor(vals(inp["dout"][lo:hi]))
+        dod[lo:hi] = d
+    w1d = [_fp8_tensor(vals(inp["w1"][g]))[1] for g in range(G)]
+    w2d = [_fp8_tensor(vals(inp["w2"][g]))[1] for g in range(G)]
+    h = [[math.fsum(xd[t][k] * w1d[grp[t]][n][k] for k in range(H)) for n in range(2 * F)] for t in range(T)]
+    y_bits = [[_bf16_nearest_bits(float(inp["p"][t]) * (h[t][j] / (1 + math.exp(-h[t][j]))) * h[t][F + j])
+               for j in range(F)] for t in range(T)]
+    assert np.array_equal(fwd["y_bits"], np.array(y_bits, np.uint16))
+    yd = [None] * T
+    for g in range(G):
+        lo, hi = base[g], base[g + 1]
+        yd[lo:hi] = _fp8_tensor(vals(np.array(y_bits[lo:hi], np.uint16)))[1]
+    out = [[math.fsum(yd[t][k] * w2d[grp[t]][n][k] for k in range(F)) for n in range(H)] for t in range(T)]
+    np.testing.assert_allclose(fwd["out"], out, rtol=1e-12, atol=1e-15)
+
+    dh_bits, dp = [], []
+    for t in range(T):
+        g = grp[t]
+        gy = [math.fsum(dod[t][n] * w2d[g][n][f] for n in range(H)) for f in range(F)]
+        hb = [_bf16_value(_bf16_nearest_bits(v)) for v in h[t]]
+        a, b = hb[:F], hb[F:]
+        pt = float(inp["p"][t])
+        sg = [1 / (1 + math.exp(-v)) for v in a]
+        da = [gy[j] * pt * b[j] * sg[j] * (1 + a[j] * (1 - sg[j])) for j in range(F)]
+        db = [gy[j] * pt * a[j] * sg[j] for j in range(F)]
+        dp.append(math.fsum(gy[j] * a[j] * sg[j] * b[j] for j in range(F)))
+        dh_bits.append([_bf16_nearest_bits(v) for v in da + db])
+    assert np.array_equal(got["dh_bits"], np.array(dh_bits, np.uint16))
+    np.testing.assert_allclose(got["dp"], dp, rtol=1e-12, atol=1e-15)
+    dhd = [None] * T
+    for g in range(G):
+        lo, hi = base[g], base[g + 1]
+        dhd[lo:hi] = _fp8_tensor(vals(np.array(dh_bits[lo:hi], np.uint16)))[1]
+    for t in range(T):
+        w1 = w1d[grp[t]]
+        ref = [math.fsum(dhd[t][n] * w1[n][k] for n in range(2 * F)) for k in range(H)]
+        np.testing.assert_allclose(got["dx"][t], ref, rtol=1e-12, atol=1e-15)
+    for g in range(G):
+        ts = range(base[g], base[g + 1])
+        dw2 = [[math.fsum(dod[t][n] * yd[t][f] for t in ts) for f in range(F)] for n in range(H)]
+        dw1 = [[math.fsum(dhd[t][n] * xd[t][k] for t in ts) for k in range(H)] for n in range(2 * F)]
         np.testing.assert_allclose(got["dw2"][g], dw2, rtol=1e-12, atol=1e-15)
         np.testing.assert_allclose(got["dw1"][g], dw1, rtol=1e-12, atol=1e-15)
