@@ -677,6 +677,206 @@ sge_status sge_grouped_linear_wgrad_mxfp8(const void* dyT_q, const void* dyT_s, 
   return hip_status(sge::launch_grouped_wgrad_mx(p, stream), "grouped wgrad mxfp8 launch");
 }
 
+size_t sge_quantize_fp8_grouped_workspace_size(int32_t G) {
+  return G < 1 ? 0 : (size_t)(((int64_t)G * 4 + 15) / 16 * 16);
+}
+
+sge_status sge_quantize_fp8_grouped(const void* src, int64_t rows, int64_t cols, int32_t G, const int64_t* layout,
+                                    int64_t ld_t, uint8_t* q, uint8_t* q_t, float* amax, float* scale,
+                                    float* scale_inv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (rows < 0 || cols < 0) return fail(SGE_ERR_SHAPE, "quantize_fp8_grouped: negative size");
+  if (G < 1 || G > 4096) return fail(SGE_ERR_ARG, "quantize_fp8_grouped: G=%d outside [1, 4096]", G);
+  if (!amax || !scale || !scale_inv) return fail(SGE_ERR_NULL, "quantize_fp8_grouped: amax, scale and scale_inv are required");
+  if (!q && !q_t) return fail(SGE_ERR_NULL, "quantize_fp8_grouped: no output requested");
+  if (rows * cols > 0 && !src) return fail(SGE_ERR_NULL, "quantize_fp8_grouped: src is NULL");
+  if (cols % 16) return fail(SGE_ERR_SHAPE, "quantize_fp8_grouped: cols must be a multiple of 16");
+  if (!layout && (rows % G || (rows / G) % 128))
+    return fail(SGE_ERR_SHAPE, "quantize_fp8_grouped: without a layout, rows / G must be a whole multiple of 128");
+  int64_t npos = rows;
+  if (layout) {
+    const int64_t cap = sge_mx_token_capacity(rows, G);
+    if (q_t && (ld_t % SGE_MX_TOKEN_ALIGN || ld_t < cap))
+      return fail(SGE_ERR_SHAPE, "quantize_fp8_grouped: ld_t=%lld must be a multiple of %d and >= sge_mx_token_capacity=%lld",
+                  (long long)ld_t, SGE_MX_TOKEN_ALIGN, (long long)cap);
+    npos = q_t ? ld_t : cap;
+  } else if (q_t && (ld_t < rows || ld_t % 16)) {
+    return fail(SGE_ERR_SHAPE, "quantize_fp8_grouped: ld_t must be >= rows and a multiple of 16");
+  }
+  if ((src && !aligned16(src)) || (q && !aligned16(q)) || (q_t && !aligned16(q_t)))
+    return fail(SGE_ERR_ALIGN, "quantize_fp8_grouped: pointers must be 16-byte aligned");
+  const size_t need = sge_quantize_fp8_grouped_workspace_size(G);
+  if (!workspace || workspace_bytes < need)
+    return fail(SGE_ERR_WORKSPACE, "quantize_fp8_grouped: workspace %zu < %zu bytes", workspace_bytes, need);
+  const Range in[2] = {range_of(src, rows, cols, cols, 2),
+                       layout ? Range{(uintptr_t)layout, (uintptr_t)(layout + 2 * (G + 1))} : Range{0, 0}};
+  const Range outs[6] = {q ? range_of(q, rows, cols, cols, 1) : Range{0, 0},
+                         q_t ? range_of(q_t, cols, ld_t, ld_t, 1) : Range{0, 0},
+                         range_of(amax, 1, G, G, 4), range_of(scale, 1, G, G, 4), range_of(scale_inv, 1, G, G, 4),
+                         range_of(workspace, 1, G, G, 4)};
+  for (int a = 0; a < 6; ++a) {
+    for (const Range& i : in)
+      if (overlap(outs[a], i)) return fail(SGE_ERR_ALIAS, "quantize_fp8_grouped: an output overlaps an input");
+    for (int b = a + 1; b < 6; ++b)
+      if (overlap(outs[a], outs[b])) return fail(SGE_ERR_ALIAS, "quantize_fp8_grouped: outputs overlap");
+  }
+  return hip_status(sge::launch_quantize_fp8_grouped(static_cast<const uint16_t*>(src), rows, cols, G, layout, npos,
+                                                     static_cast<uint32_t*>(workspace), q, q_t, amax, scale,
+                                                     scale_inv, stream),
+                    "quantize_fp8_grouped launch");
+}
+
+sge_status sge_grouped_linear_fwd_fp8(const void* x_q, const float* x_sinv, const void* w_q, const float* w_sinv,
+                                      int32_t G, int64_t T, int64_t N, int64_t K, const int64_t* offsets, float alpha,
+                                      int32_t epilogue, const float* probs, void* out, void* preact,
+                                      hipStream_t stream) {
+  if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_fp8: bad sizes");
+  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_SCALED_SWIGLU)
+    return fail(SGE_ERR_ARG, "grouped_linear_fwd_fp8: epilogue %d not allowed", epilogue);
+  const bool swiglu = epilogue == SGE_EPI_SCALED_SWIGLU;
+  if (!x_q || !x_sinv || !w_q || !w_sinv || !offsets || !out) return fail(SGE_ERR_NULL, "grouped_linear_fwd_fp8: NULL pointer");
+  if (swiglu && !probs) return fail(SGE_ERR_NULL, "grouped_linear_fwd_fp8: probs is NULL");
+  if (K % 16) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_fp8: K must be a multiple of 16");
+  if (N % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_fp8: N must be a multiple of 8");
+  if (swiglu && N % 256) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_fp8: SwiGLU needs N %% 256 == 0");
+  if (!aligned16(x_q) || !aligned16(w_q) || !aligned16(out) || (preact && !aligned16(preact)))
+    return fail(SGE_ERR_ALIGN, "grouped_linear_fwd_fp8: pointers must be 16-byte aligned");
+  const int64_t out_cols = swiglu ? N / 2 : N;
+  const Range in[2] = {range_of(x_q, T, K, K, 1), range_of(w_q, (int64_t)G * N, K, K, 1)};
+  const Range outs[2] = {range_of(out, T, out_cols, out_cols, 2), preact ? range_of(preact, T, N, N, 2) : Range{0, 0}};
+  for (const Range& o : outs)
+    for (const Range& i : in)
+      if (overlap(o, i)) return fail(SGE_ERR_ALIAS, "grouped_linear_fwd_fp8: outputs overlap inputs");
+  if (overlap(outs[0], outs[1])) return fail(SGE_ERR_ALIAS, "grouped_linear_fwd_fp8: outputs overlap");
+  if (T == 0 || N == 0) return ok();
+  sge::GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.a = static_cast<const uint8_t*>(x_q);
+  p.lda = K;
+  p.b = static_cast<const uint8_t*>(w_q);
+  p.ldb = K;
+  p.M = T;
+  p.N = N;
+  p.K = K;
+  p.b_group_stride = N * K;
+  p.a_sinv = x_sinv;
+  p.b_sinv = w_sinv;
+  p.sinv_per_group = 1;
+  p.alpha = alpha;
+  p.c = static_cast<uint16_t*>(out);
+  p.ldc = out_cols;
+  p.offsets = offsets;
+  p.G = G;
+  p.T = T;
+  p.probs = probs;
+  p.aux = static_cast<uint16_t*>(preact);
+  p.ld_aux = N;
+  p.F = N / 2;
+  return hip_status(sge::launch_grouped_fwd_fp8(p, epilogue, stream), "grouped fwd fp8 launch");
+}
+
+sge_status sge_grouped_linear_dgrad_fp8(const void* dy_q, const float* dy_sinv, const void* w_qT, const float* w_sinv,
+                                        int32_t G, int64_t T, int64_t N, int64_t K, const int64_t* offsets,
+                                        float alpha, int32_t epilogue, const void* preact, const float* probs,
+                                        void* dx, void* dact, float* dprobs, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+  if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_fp8: bad sizes");
+  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_DSCALED_SWIGLU)
+    return fail(SGE_ERR_ARG, "grouped_linear_dgrad_fp8: epilogue %d not allowed", epilogue);
+  const bool swiglu = epilogue == SGE_EPI_DSCALED_SWIGLU;
+  if (!dy_q || !dy_sinv || !w_qT || !w_sinv || !offsets) return fail(SGE_ERR_NULL, "grouped_linear_dgrad_fp8: NULL pointer");
+  if (swiglu && (!preact || !probs || !dact || !dprobs))
+    return fail(SGE_ERR_NULL, "grouped_linear_dgrad_fp8: SwiGLU backward needs preact, probs, dact and dprobs");
+  if (!swiglu && !dx) return fail(SGE_ERR_NULL, "grouped_linear_dgrad_fp8: dx is NULL");
+  if (N % 16) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_fp8: N must be a multiple of 16");
+  if (K % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_fp8: K must be a multiple of 8");
+  if (!aligned16(dy_q) || !aligned16(w_qT) || (dx && !aligned16(dx)) || (preact && !aligned16(preact)) ||
+      (dact && !aligned16(dact)))
+    return fail(SGE_ERR_ALIGN, "grouped_linear_dgrad_fp8: pointers must be 16-byte aligned");
+  const int64_t GN = (int64_t)G * N;
+  const Range in[3] = {range_of(dy_q, T, N, N, 1), range_of(w_qT, K, GN, GN, 1),
+                       swiglu ? range_of(preact, T, 2 * K, 2 * K, 2) : Range{0, 0}};
+  const Range out = swiglu ? range_of(dact, T, 2 * K, 2 * K, 2) : range_of(dx, T, K, K, 2);
+  for (const Range& i : in)
+    if (overlap(out, i)) return fail(SGE_ERR_ALIAS, "grouped_linear_dgrad_fp8: output overlaps an input");
+  const size_t need = sge_grouped_linear_bwd_workspace_size(T, K, G, epilogue);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(SGE_ERR_WORKSPACE, "grouped_linear_dgrad_fp8: workspace %zu < %zu bytes", workspace_bytes, need);
+  if (T == 0 || K == 0) return ok();
+  sge::GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.a = static_cast<const uint8_t*>(dy_q);
+  p.lda = N;
+  p.b = static_cast<const uint8_t*>(w_qT);       // the transposed copy [K][G*N], group g at column g*N
+  p.ldb = GN;
+  p.M = T;
+  p.N = K;
+  p.K = N;
+  p.b_group_stride = N;
+  p.a_sinv = dy_sinv;
+  p.b_sinv = w_sinv;
+  p.sinv_per_group = 1;
+  p.alpha = alpha;
+  p.c = static_cast<uint16_t*>(swiglu ? nullptr : dx);
+  p.ldc = K;
+  p.offsets = offsets;
+  p.G = G;
+  p.T = T;
+  if (swiglu) {
+    p.probs = probs;
+    p.aux = const_cast<uint16_t*>(static_cast<const uint16_t*>(preact));
+    p.ld_aux = 2 * K;
+    p.aux_out = static_cast<uint16_t*>(dact);
+    p.ld_aux_out = 2 * K;
+    p.dp_part = static_cast<float*>(workspace);
+    p.F = K;
+  }
+  hipError_t e = sge::launch_grouped_dgrad_fp8(p, epilogue, stream);
+  if (e != hipSuccess) return hip_status(e, "grouped dgrad fp8 launch");
+  if (swiglu) {
+    const int parts = (int)(sge::gemm_dp_parts_per_tile() * ((K + sge::gemm_tile_n() - 1) / sge::gemm_tile_n()));
+    e = sge::launch_rowsum_parts(static_cast<const float*>(workspace), parts, offsets, G, T, dprobs, stream);
+    if (e != hipSuccess) return hip_status(e, "dprobs reduction launch");
+  }
+  return ok();
+}
+
+sge_status sge_grouped_linear_wgrad_fp8(const void* dyT_q, const float* dy_sinv, const void* xT_q, const float* x_sinv,
+                                        int32_t G, int64_t N, int64_t K, const int64_t* layout, int64_t ld,
+                                        float alpha, void* dw, hipStream_t stream) {
+  if (G < 1 || G > 4096 || N < 0 || K < 0 || ld < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_wgrad_fp8: bad sizes");
+  if (!dyT_q || !dy_sinv || !xT_q || !x_sinv || !layout || !dw) return fail(SGE_ERR_NULL, "grouped_linear_wgrad_fp8: NULL pointer");
+  if (ld % SGE_MX_TOKEN_ALIGN) return fail(SGE_ERR_SHAPE, "grouped_linear_wgrad_fp8: ld must be a multiple of %d", SGE_MX_TOKEN_ALIGN);
+  if (K % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_wgrad_fp8: K must be a multiple of 8");
+  if (!aligned16(dyT_q) || !aligned16(xT_q) || !aligned16(dw))
+    return fail(SGE_ERR_ALIGN, "grouped_linear_wgrad_fp8: pointers must be 16-byte aligned");
+  const Range rdw = range_of(dw, (int64_t)G * N, K, K, 2);
+  const Range in[3] = {range_of(dyT_q, N, ld, ld, 1), range_of(xT_q, K, ld, ld, 1),
+                       Range{(uintptr_t)layout, (uintptr_t)(layout + 2 * (G + 1))}};
+  for (const Range& i : in)
+    if (overlap(rdw, i)) return fail(SGE_ERR_ALIAS, "grouped_linear_wgrad_fp8: dw overlaps an input");
+  if (N == 0 || K == 0) return ok();
+  sge::GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.a = static_cast<const uint8_t*>(dyT_q);
+  p.lda = ld;
+  p.b = static_cast<const uint8_t*>(xT_q);
+  p.ldb = ld;
+  p.M = N;
+  p.N = K;
+  p.K = ld;
+  p.a_sinv = dy_sinv;
+  p.b_sinv = x_sinv;
+  p.sinv_per_group = 1;
+  p.alpha = alpha;
+  p.c = static_cast<uint16_t*>(dw);
+  p.ldc = K;
+  p.c_group_stride = N * K;
+  p.offsets = layout + G + 1;                    // the aligned group starts: each group's contraction range
+  p.G = G;
+  p.T = ld;
+  return hip_status(sge::launch_grouped_wgrad_fp8(p, stream), "grouped wgrad fp8 launch");
+}
+
 sge_status sge_scaled_swiglu_fwd(const void* h, const float* probs, void* y, int64_t T, int64_t F, hipStream_t stream) {
   if (T < 0 || F < 0) return fail(SGE_ERR_SHAPE, "scaled_swiglu_fwd: negative size");
   if (T > 0 && (!h || !probs || !y)) return fail(SGE_ERR_NULL, "scaled_swiglu_fwd: NULL pointer");

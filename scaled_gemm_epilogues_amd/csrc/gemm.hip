@@ -280,6 +280,7 @@ void gemm_kernel(const GemmParams p) {
   const uint8_t* bmx = p.b_mx;                           // MXFP8: E8M0 scales of B (this group's)
   uint16_t* cptr = p.c;
   int nt;
+  int grp = 0;                                           // the group (E4M3 per-group scales)
   if constexpr (SCHED == S_DENSE) {
     const int MT = p.mt_count, NT = p.nt_count;
     const int bid = xcd_tile(blockIdx.x, MT * NT);                      // grid is exactly MT * NT
@@ -323,6 +324,7 @@ void gemm_kernel(const GemmParams p) {
       lin -= tiles;
     }
     if (g < 0) return;                                   // beyond the last real tile
+    grp = g;
     m0 = lo + (int64_t)lin * BM;
     row_end = hi;
     n0 = (int64_t)nt * (EPI == E_SWIGLU ? BN / 2 : BN);
@@ -339,6 +341,7 @@ void gemm_kernel(const GemmParams p) {
       t = (i / per8) * per + x * per8 + i % per8;
     }
     const int g = t / per;
+    grp = g;
     const int rem = t % per;
     const int mt = rem / p.nt_count;
     nt = rem % p.nt_count;
@@ -616,7 +619,10 @@ void gemm_kernel(const GemmParams p) {
   // out-of-range lanes read zeros / drop their writes, so all loads of a row block
   // are in flight together (and the next block's loads overlap this block's math).
   float alpha = p.alpha;
-  if constexpr (FMT == F_E4M3) alpha = (p.a_sinv[0] * p.b_sinv[0]) * p.alpha;
+  if constexpr (FMT == F_E4M3) {
+    const int gs = p.sinv_per_group ? grp : 0;           // grouped: one scale per group on both sides
+    alpha = (p.a_sinv[gs] * p.b_sinv[gs]) * p.alpha;
+  }
   const int64_t c_rows = SCHED == S_GROUP_M ? p.T : p.M;
   const int64_t rows_left = c_rows - m0;
   auto row_in_tile = [&](int i) { return wm * WM + i * 32 + lrow; };
@@ -967,6 +973,20 @@ hipError_t launch_grouped_dgrad(const GemmParams& p, int epilogue, hipStream_t s
 
 hipError_t launch_grouped_wgrad(const GemmParams& p, hipStream_t s) {
   return launch_tile<F_BF16, false, false, E_STORE, S_GROUP_K>(p, s);
+}
+
+hipError_t launch_grouped_fwd_fp8(const GemmParams& p, int epilogue, hipStream_t s) {
+  if (epilogue == E_SWIGLU) return launch_tile<F_E4M3, true, true, E_SWIGLU, S_GROUP_M>(p, s);
+  return launch_tile<F_E4M3, true, true, E_STORE, S_GROUP_M>(p, s);
+}
+
+hipError_t launch_grouped_dgrad_fp8(const GemmParams& p, int epilogue, hipStream_t s) {
+  if (epilogue == E_DSWIGLU) return launch_tile<F_E4M3, true, true, E_DSWIGLU, S_GROUP_M>(p, s);
+  return launch_tile<F_E4M3, true, true, E_STORE, S_GROUP_M>(p, s);
+}
+
+hipError_t launch_grouped_wgrad_fp8(const GemmParams& p, hipStream_t s) {
+  return launch_tile<F_E4M3, true, true, E_STORE, S_GROUP_K>(p, s);
 }
 
 hipError_t launch_grouped_dgrad_mx(const GemmParams& p, int epilogue, hipStream_t s) {

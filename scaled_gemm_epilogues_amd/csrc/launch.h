@@ -44,6 +44,7 @@ struct GemmParams {
   uint8_t* s_out;             //   and its E8M0 scales [T][ld_q / 32]
   int64_t ld_q;
   int64_t b_mx_bytes;         // MXFP8: bytes of B's whole scale array from b_mx (0: rows x ld)
+  int sinv_per_group;         // E4M3 grouped: a_sinv / b_sinv are [G], indexed by the group
 };
 
 hipError_t launch_gemm(const GemmParams& p, int fmt, bool a_kmaj, bool b_kmaj, hipStream_t s);
@@ -54,6 +55,10 @@ hipError_t launch_grouped_dgrad(const GemmParams& p, int epilogue, hipStream_t s
 hipError_t launch_grouped_wgrad(const GemmParams& p, hipStream_t s);
 // MXFP8 operands, both inner-contiguous (scale rows dword-aligned: contraction % 128 == 0).
 hipError_t launch_grouped_dgrad_mx(const GemmParams& p, int epilogue, hipStream_t s);
+// E4M3 operands with one scale per group (sinv_per_group), both inner-contiguous.
+hipError_t launch_grouped_fwd_fp8(const GemmParams& p, int epilogue, hipStream_t s);
+hipError_t launch_grouped_dgrad_fp8(const GemmParams& p, int epilogue, hipStream_t s);
+hipError_t launch_grouped_wgrad_fp8(const GemmParams& p, hipStream_t s);
 hipError_t launch_grouped_wgrad_mx(const GemmParams& p, hipStream_t s);
 int gemm_tile_n();
 int gemm_dp_parts_per_tile();
@@ -73,6 +78,10 @@ hipError_t launch_quantize_mxfp8(const uint16_t* src, int64_t rows, int64_t cols
 hipError_t launch_quantize_mxfp8_grouped(const uint16_t* src, int64_t rows, int64_t cols, int G,
                                          const int64_t* layout, int64_t ld_t, uint8_t* q_row, uint8_t* s_row,
                                          uint8_t* q_colT, uint8_t* s_colT, hipStream_t s);
+// FP8 current scaling with one scale per group (layout NULL: G equal runs of rows / G rows).
+hipError_t launch_quantize_fp8_grouped(const uint16_t* src, int64_t rows, int64_t cols, int G,
+                                       const int64_t* layout, int64_t ld_t, uint32_t* amax_bits, uint8_t* q,
+                                       uint8_t* q_t, float* amax, float* scale, float* scale_inv, hipStream_t s);
 hipError_t launch_mx_group_layout(const int64_t* offsets, int G, int64_t T, int64_t align, int64_t* layout,
                                   hipStream_t s);
 

@@ -82,6 +82,50 @@ hipError_t launch_amax_partial(const uint16_t* src, int64_t n, uint32_t* partial
   return hipGetLastError();
 }
 
+// Current scaling from an amax: scale = 448 / amax (IEEE division, no fast-math; 1 for an
+// all-zero tensor; clamped to the largest finite fp32), scale_inv = 1 / scale.
+__device__ __forceinline__ void fp8_scales(float amax, float& scale, float& scale_inv) {
+  scale = 1.0f;
+  if (amax > 0.0f) {
+    scale = 448.0f / amax;
+    if (scale > 3.402823466e38f) scale = 3.402823466e38f;
+  }
+  scale_inv = 1.0f / scale;
+}
+
+// Tiles of a grouped tensor walk the stored positions of a group layout ([2][G+1]: token
+// ranges c[], aligned starts pad[]): a tile of 128 positions lies inside one group's aligned
+// range. Returns false past the last group; else the group, the tile's first source row and
+// how many of its rows exist (the rest of the 128 positions are padding). With no layout the
+// G groups are equal runs of rows / G rows (a multiple of 128) and positions are rows.
+__device__ __forceinline__ bool group_tile(const int64_t* __restrict__ layout, int G, int64_t rows, int64_t p0,
+                                           int& g, int64_t& r0, int64_t& nrows) {
+  if (!layout) {
+    if (p0 >= rows) return false;
+    const int64_t per = rows / G;
+    g = (int)(p0 / per);
+    r0 = p0;
+    nrows = (int64_t)(g + 1) * per - p0;
+    return true;
+  }
+  const int64_t* c = layout;
+  const int64_t* pad = layout + G + 1;
+  if (p0 >= pad[G]) return false;
+  int lo = 0, hi = G - 1;                               // last g with pad[g] <= p0
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pad[mid] <= p0) lo = mid;
+    else hi = mid - 1;
+  }
+  g = lo;
+  r0 = c[lo] + (p0 - pad[lo]);
+  nrows = c[lo + 1] - r0;                               // >= 1: aligned lengths round up
+  // a layout not made for these rows reads nothing out of range
+  r0 = r0 < 0 ? 0 : (r0 > rows ? rows : r0);
+  nrows = nrows > rows - r0 ? rows - r0 : nrows;
+  return true;
+}
+
 // Tiles of 128 rows x 64 columns; 256 threads, 8 bf16 (16 B) per thread per pass. The
 // transposed copy is written through LDS so each column's 128 rows leave as one 128-byte
 // line. Tiles are visited in the reverse order of the amax pass, which left the most
@@ -100,12 +144,8 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(
   for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = partial[i] > m ? partial[i] : m;
   m = block_max_u32(m, red);
   const float amax = __builtin_bit_cast(float, m << 16);
-  float scale = 1.0f;
-  if (amax > 0.0f) {
-    scale = 448.0f / amax;                           // IEEE division (no fast-math)
-    if (scale > 3.402823466e38f) scale = 3.402823466e38f;
-  }
-  const float scale_inv = 1.0f / scale;
+  float scale, scale_inv;
+  fp8_scales(amax, scale, scale_inv);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     *amax_out = amax;
     *scale_out = scale;
@@ -195,21 +235,9 @@ __global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const uint16_t* __r
   int64_t nrows = rows - p0;     // source rows of the tile that exist
   int64_t npos = rows - p0;      // columnwise positions the tile writes
   if constexpr (GROUPED) {
-    const int64_t* c = layout;
-    const int64_t* pad = layout + G + 1;
-    if (p0 >= pad[G]) return;                             // past the last group (block-uniform)
-    int lo = 0, hi = G - 1;                               // last g with pad[g] <= p0
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (pad[mid] <= p0) lo = mid;
-      else hi = mid - 1;
-    }
-    r0 = c[lo] + (p0 - pad[lo]);
-    nrows = c[lo + 1] - r0;                               // >= 1: aligned lengths round up
-    npos = kMR;                                           // pad[lo + 1] - p0 >= 128
-    // a layout not made for these rows reads nothing out of range
-    r0 = r0 < 0 ? 0 : (r0 > rows ? rows : r0);
-    nrows = nrows > rows - r0 ? rows - r0 : nrows;
+    int g;
+    if (!group_tile(layout, G, rows, p0, g, r0, nrows)) return;   // past the last group (block-uniform)
+    npos = kMR;                                           // pad[g + 1] - p0 >= 128
   }
   const int t = threadIdx.x;
   const int lr = t >> 3;                 // 0..31
@@ -319,6 +347,121 @@ hipError_t launch_quantize_mxfp8_grouped(const uint16_t* src, int64_t rows, int6
   if (tiles == 0) return hipSuccess;
   hipLaunchKernelGGL(quantize_mxfp8_kernel<true>, dim3((unsigned)tiles), dim3(256), 0, s, src, rows, cols, q_row,
                      s_row, q_colT, s_colT, G, layout, ld_t);
+  return hipGetLastError();
+}
+
+// ------------------------------------------- FP8 current scaling per group
+// One amax and scale per group (a group quantize with one quantizer per group). Pass 1: each
+// block takes 128 stored positions x 512 columns of one group and folds its amax into the
+// group's slot with an atomic max over bf16 magnitude bits (order-free, so deterministic).
+// Pass 2 quantizes tiles of 128 positions x 64 columns with their group's scale, writing the
+// rowwise bytes and the transposed copy (all 128 positions: padding comes out as zero codes).
+constexpr int kGAC = 512;
+
+__global__ __launch_bounds__(256) void amax_grouped_kernel(const uint16_t* __restrict__ src, int64_t rows,
+                                                          int64_t cols, int G, const int64_t* __restrict__ layout,
+                                                          uint32_t* __restrict__ amax_bits) {
+  __shared__ uint32_t red[4];
+  const int64_t tc = (cols + kGAC - 1) / kGAC;
+  const int64_t p0 = (int64_t)(blockIdx.x / tc) * kQR;
+  const int64_t c0 = (int64_t)(blockIdx.x % tc) * kGAC;
+  int g;
+  int64_t r0, nrows;
+  if (!group_tile(layout, G, rows, p0, g, r0, nrows)) return;   // block-uniform
+  const int t = threadIdx.x;
+  const int64_t c = c0 + (t & 63) * 8;
+  uint32_t m = 0;
+  if (c < cols) {
+#pragma unroll 8
+    for (int lr = t >> 6; lr < kQR; lr += 4) {
+      if (lr < nrows) {
+        const uint32_t x = absmax_bits8(*reinterpret_cast<const uint4*>(src + (r0 + lr) * cols + c));
+        m = m > x ? m : x;
+      }
+    }
+  }
+  m = block_max_u32(m, red);
+  if (t == 0 && m) atomicMax(amax_bits + g, m);
+}
+
+__global__ __launch_bounds__(256) void quantize_fp8_grouped_kernel(
+    const uint16_t* __restrict__ src, int64_t rows, int64_t cols, int G, const int64_t* __restrict__ layout,
+    int64_t ld_t, const uint32_t* __restrict__ amax_bits, uint8_t* __restrict__ q, uint8_t* __restrict__ q_t,
+    float* amax_out, float* scale_out, float* scale_inv_out) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kQC][kQR + 16];   // [column][position]
+  const int t = threadIdx.x;
+  if (blockIdx.x == 0) {
+    for (int gg = t; gg < G; gg += blockDim.x) {
+      const float a = __builtin_bit_cast(float, amax_bits[gg] << 16);
+      float sc, si;
+      fp8_scales(a, sc, si);
+      amax_out[gg] = a;
+      scale_out[gg] = sc;
+      scale_inv_out[gg] = si;
+    }
+  }
+  const int64_t tc = (cols + kQC - 1) / kQC;
+  const int64_t p0 = (int64_t)(blockIdx.x / tc) * kQR;
+  const int64_t c0 = (int64_t)(blockIdx.x % tc) * kQC;
+  int g;
+  int64_t r0, nrows;
+  if (!group_tile(layout, G, rows, p0, g, r0, nrows)) return;   // block-uniform
+  float scale, scale_inv;
+  fp8_scales(__builtin_bit_cast(float, amax_bits[g] << 16), scale, scale_inv);
+  const int cchunk = t & 7;
+  const int rsub = t >> 3;
+#pragma unroll
+  for (int pass = 0; pass < kQR / 32; ++pass) {
+    const int lr = rsub + 32 * pass;
+    const int64_t r = r0 + lr, c = c0 + cchunk * 8;
+    uint32_t b[4] = {0, 0, 0, 0};
+    if (lr < nrows && c < cols) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src + r * cols + c);
+      b[0] = e4m3x2(bf16_lo(v.x) * scale, bf16_hi(v.x) * scale);
+      b[1] = e4m3x2(bf16_lo(v.y) * scale, bf16_hi(v.y) * scale);
+      b[2] = e4m3x2(bf16_lo(v.z) * scale, bf16_hi(v.z) * scale);
+      b[3] = e4m3x2(bf16_lo(v.w) * scale, bf16_hi(v.w) * scale);
+      if (q) *reinterpret_cast<uint2*>(q + r * cols + c) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+    }
+    if (q_t) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        tile[cchunk * 8 + 2 * e][lr] = (uint8_t)(b[e] & 0xFF);
+        tile[cchunk * 8 + 2 * e + 1][lr] = (uint8_t)(b[e] >> 8);
+      }
+    }
+  }
+  if (q_t) {
+    __syncthreads();
+    // thread -> one column, 32 consecutive positions (2 x 16 bytes) of the transposed copy
+    const int lc = t >> 2, seg = (t & 3) * 32;
+    const int64_t c = c0 + lc;
+    if (c < cols) {
+      const uint4 lo = *reinterpret_cast<const uint4*>(&tile[lc][seg]);
+      const uint4 hi = *reinterpret_cast<const uint4*>(&tile[lc][seg + 16]);
+      uint8_t* dst = q_t + c * ld_t + p0 + seg;
+      *reinterpret_cast<uint4*>(dst) = lo;
+      *reinterpret_cast<uint4*>(dst + 16) = hi;
+    }
+  }
+}
+
+hipError_t launch_quantize_fp8_grouped(const uint16_t* src, int64_t rows, int64_t cols, int G,
+                                       const int64_t* layout, int64_t ld_t, uint32_t* amax_bits, uint8_t* q,
+                                       uint8_t* q_t, float* amax, float* scale, float* scale_inv, hipStream_t s) {
+  hipError_t e = launch_fill_f32_zero(reinterpret_cast<float*>(amax_bits), G, s);   // +0.0f is all-zero bits
+  if (e != hipSuccess) return e;
+  const int64_t npos = layout ? ld_t : rows;            // positions the tiles walk (a bound of the last group's end)
+  const int64_t ta = (npos / kQR) * ((cols + kGAC - 1) / kGAC);
+  if (ta > 0) {
+    hipLaunchKernelGGL(amax_grouped_kernel, dim3((unsigned)ta), dim3(256), 0, s, src, rows, cols, G, layout,
+                       amax_bits);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  int64_t tq = (npos / kQR) * ((cols + kQC - 1) / kQC);
+  if (tq < 1) tq = 1;                                   // block 0 still writes every group's scales
+  hipLaunchKernelGGL(quantize_fp8_grouped_kernel, dim3((unsigned)tq), dim3(256), 0, s, src, rows, cols, G, layout,
+                     ld_t, amax_bits, q, q_t, amax, scale, scale_inv);
   return hipGetLastError();
 }
 

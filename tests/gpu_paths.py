@@ -246,3 +246,61 @@ def run_grouped_mlp_bwd_mx(inp, fwd):
     return {"lay": lay, "q_dout": q_dout, "w2c": w2c, "w1c": w1c, "dh": d2["dact"], "dp": d2["dprobs"],
             "dhq": d2["dact_q"], "dhs": d2["dact_s"], "dh_unfused": dh_unfused, "dw2": dw2, "dx": d1["dx"],
             "dw1": dw1, "q_y": q_y, "q_dh": q_dh, "q_x": q_x}
+
+
+# ------------------------------------------- FP8 current scaling per group
+def quant_fp8_grouped(t, G, lay=None, row=True, col=True, fill=None):
+    """Per-group FP8 current scaling of device bf16 ``t`` [rows, C]: groups from ``lay`` or G
+    equal runs of rows. Returns q [rows, C], q_t [C, ld] and the per-group amax / scale / scale_inv."""
+    rows, C = t.shape
+    ld = sge.mx_token_capacity(rows, G) if lay is not None else rows
+    f32 = dict(dtype=torch.float32, device="cuda")
+    out = {"amax": torch.empty(G, **f32), "scale": torch.empty(G, **f32), "scale_inv": torch.empty(G, **f32),
+           "ld": ld}
+    mk = (lambda *s: torch.full(s, fill, dtype=torch.uint8, device="cuda")) if fill is not None else \
+        (lambda *s: torch.empty(*s, dtype=torch.uint8, device="cuda"))
+    out["q"] = mk(rows, C) if row else None
+    out["q_t"] = mk(C, ld) if col else None
+    ws = torch.empty(max(16, sge.quantize_fp8_grouped_workspace_size(G)), dtype=torch.uint8, device="cuda")
+    sge.quantize_fp8_grouped(t, G, out["amax"], out["scale"], out["scale_inv"], ws, layout=lay, q=out["q"],
+                             q_t=out["q_t"])
+    return out
+
+
+def run_grouped_mlp_fp8(inp):
+    """Grouped MLP forward + backward on E4M3 operands with current scaling per group: every
+    operand quantized per group (x, y, dout, dh per token group; W1, W2 per expert), rowwise for
+    the forward and the dgrads, transposed for the dgrads' weights and the wgrads' operands."""
+    X, W1, W2, DOUT = dev_bf16(inp["x"]), dev_bf16(inp["w1"]), dev_bf16(inp["w2"]), dev_bf16(inp["dout"])
+    P = torch.from_numpy(inp["p"]).cuda()
+    T, H = X.shape
+    G, N1, _ = W1.shape
+    F = N1 // 2
+    offs = torch.empty(1, G + 1, dtype=torch.int64, device="cuda")
+    sge.splits_to_offsets(torch.from_numpy(inp["splits"]).cuda(), [1], offs)
+    base = offs[0]
+    lay = mx_layout(base, T)
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    qx = quant_fp8_grouped(X, G, lay)
+    qw1 = quant_fp8_grouped(W1.reshape(G * N1, H), G)
+    qw2 = quant_fp8_grouped(W2.reshape(G * H, F), G)
+    h, y, out = torch.empty(T, N1, **bf), torch.empty(T, F, **bf), torch.empty(T, H, **bf)
+    sge.grouped_linear_fwd_fp8(qx["q"], qx["scale_inv"], qw1["q"].view(G, N1, H), qw1["scale_inv"], base, y,
+                               epilogue=sge.EPI_SCALED_SWIGLU, probs=P, preact=h)
+    qy = quant_fp8_grouped(y, G, lay)
+    sge.grouped_linear_fwd_fp8(qy["q"], qy["scale_inv"], qw2["q"].view(G, H, F), qw2["scale_inv"], base, out)
+    qd = quant_fp8_grouped(DOUT, G, lay)
+    dh, dp = torch.empty(T, N1, **bf), torch.empty(T, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, sge.grouped_linear_bwd_workspace_size(T, F, G, sge.EPI_DSCALED_SWIGLU)),
+                     dtype=torch.uint8, device="cuda")
+    sge.grouped_linear_dgrad_fp8(qd["q"], qd["scale_inv"], qw2["q_t"], qw2["scale_inv"], base,
+                                 epilogue=sge.EPI_DSCALED_SWIGLU, preact=h, probs=P, dact=dh, dprobs=dp, workspace=ws)
+    dw2 = torch.empty(G, H, F, **bf)
+    sge.grouped_linear_wgrad_fp8(qd["q_t"], qd["scale_inv"], qy["q_t"], qy["scale_inv"], lay, dw2)
+    qdh = quant_fp8_grouped(dh, G, lay)
+    dx, dw1 = torch.empty(T, H, **bf), torch.empty(G, N1, H, **bf)
+    sge.grouped_linear_dgrad_fp8(qdh["q"], qdh["scale_inv"], qw1["q_t"], qw1["scale_inv"], base, dx=dx)
+    sge.grouped_linear_wgrad_fp8(qdh["q_t"], qdh["scale_inv"], qx["q_t"], qx["scale_inv"], lay, dw1)
+    torch.cuda.synchronize()
+    return {"base": base, "lay": lay, "qx": qx, "qw1": qw1, "qw2": qw2, "qy": qy, "qd": qd, "qdh": qdh, "h": h,
+            "y": y, "out": out, "dh": dh, "dp": dp, "dw2": dw2, "dx": dx, "dw1": dw1}

@@ -253,3 +253,73 @@ def test_mxfp8_grouped_backward_validation_errors(sge):
     assert w(*a) == sge.ERR_ALIGN
     a = list(ok); a[10] = B(3)
     assert w(*a) == sge.ERR_ALIAS                                         # dw over xT_q
+
+
+def test_fp8_grouped_validation_errors(sge):
+    def B(k):                      # far-apart fake addresses (no accidental overlaps)
+        return FAKE * 8 * k
+
+    assert sge.quantize_fp8_grouped_workspace_size(8) == 32
+    q = sge._lib.sge_quantize_fp8_grouped
+    rows, C, G = 100, 64, 4
+    ld = sge.mx_token_capacity(rows, G)
+    ws = sge.quantize_fp8_grouped_workspace_size(G)
+    ok = [B(1), rows, C, G, B(2), ld, B(3), B(4), B(5), B(6), B(7), B(8), ws, None]
+    a = list(ok); a[8] = None
+    assert q(*a) == sge.ERR_NULL                                          # amax required
+    a = list(ok); a[6] = None; a[7] = None
+    assert q(*a) == sge.ERR_NULL                                          # no output
+    a = list(ok); a[2] = 40
+    assert q(*a) == sge.ERR_SHAPE                                         # cols % 16
+    a = list(ok); a[5] = ld - 128
+    assert q(*a) == sge.ERR_SHAPE                                         # ld below capacity
+    a = list(ok); a[4] = None
+    assert q(*a) == sge.ERR_SHAPE                                         # equal runs need rows/G % 128
+    a = list(ok); a[4] = None; a[1] = 4 * 256; a[5] = 1000
+    assert q(*a) == sge.ERR_SHAPE                                         # ld_t % 16 without a layout
+    a = list(ok); a[6] = B(6) + 4
+    assert q(*a) == sge.ERR_ALIGN
+    a = list(ok); a[12] = ws - 1
+    assert q(*a) == sge.ERR_WORKSPACE
+    a = list(ok); a[7] = B(1)
+    assert q(*a) == sge.ERR_ALIAS                                         # q_t over src
+    a = list(ok); a[10] = B(8)
+    assert q(*a) == sge.ERR_ALIAS                                         # scale_inv over scale
+
+    f = sge._lib.sge_grouped_linear_fwd_fp8
+    G, T, N, K = 4, 100, 512, 256
+    ok = [B(1), B(2), B(3), B(4), G, T, N, K, B(5), 1.0, sge.EPI_SCALED_SWIGLU, B(6), B(7), B(8), None]
+    a = list(ok); a[1] = None
+    assert f(*a) == sge.ERR_NULL                                          # x_sinv
+    a = list(ok); a[11] = None
+    assert f(*a) == sge.ERR_NULL                                          # SwiGLU needs probs
+    a = list(ok); a[7] = 200
+    assert f(*a) == sge.ERR_SHAPE                                         # K % 16
+    a = list(ok); a[6] = 264
+    assert f(*a) == sge.ERR_SHAPE                                         # SwiGLU N % 256
+    a = list(ok); a[12] = B(1)
+    assert f(*a) == sge.ERR_ALIAS                                         # out over x_q
+
+    d = sge._lib.sge_grouped_linear_dgrad_fp8
+    sw = sge.EPI_DSCALED_SWIGLU
+    wsb = sge.grouped_linear_bwd_workspace_size(T, K, G, sw)
+    ok = [B(1), B(2), B(3), B(4), G, T, N, K, B(5), 1.0, sw, B(6), B(7), None, B(8), B(9), B(10), wsb, None]
+    a = list(ok); a[14] = None
+    assert d(*a) == sge.ERR_NULL                                          # SwiGLU needs dact
+    a = list(ok); a[10] = sge.EPI_NONE
+    assert d(*a) == sge.ERR_NULL                                          # dx required without SwiGLU
+    a = list(ok); a[6] = 200
+    assert d(*a) == sge.ERR_SHAPE                                         # N % 16
+    a = list(ok); a[14] = B(6)
+    assert d(*a) == sge.ERR_ALIAS                                         # dact over preact
+    a = list(ok); a[17] = wsb - 4
+    assert d(*a) == sge.ERR_WORKSPACE
+
+    w = sge._lib.sge_grouped_linear_wgrad_fp8
+    ok = [B(1), B(2), B(3), B(4), G, N, K, B(5), 640, 1.0, B(6), None]
+    a = list(ok); a[1] = None
+    assert w(*a) == sge.ERR_NULL
+    a = list(ok); a[8] = 600
+    assert w(*a) == sge.ERR_SHAPE
+    a = list(ok); a[10] = B(3)
+    assert w(*a) == sge.ERR_ALIAS
