@@ -188,6 +188,9 @@ def build_grouped(torch, sge, wl, inp):
     base = offs[0]
     if wl["fmt"] == "mxfp8":
         return build_grouped_mx(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, dh, dp, dw2, dx, dw1, ws)
+    if wl["fmt"] == "fp8":
+        return build_grouped_fp8(torch, sge, X, W1, W2, DOUT, P, splits, offs, h, out, dh, dp, dw2, dx, dw1, ws,
+                                 flops)
     launches = [
         ("offsets", lambda: sge.splits_to_offsets(splits, [1, H], offs)),
         ("fc1_fwd", lambda: sge.grouped_linear_fwd(X, W1, base, y, epilogue=sge.EPI_SCALED_SWIGLU, probs=P,
@@ -275,6 +278,58 @@ def build_grouped_mx(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, d
     return launches, flops, hbm
 
 
+def build_grouped_fp8(torch, sge, X, W1, W2, DOUT, P, splits, offs, h, out, dh, dp, dw2, dx, dw1, ws, flops):
+    """The grouped MLP on E4M3 operands with current scaling per group: each step quantizes x,
+    y, dout and dh per token group and W1, W2 per expert (an amax pass, then one pass writing
+    the rowwise bytes and the transposed copy), and runs the six grouped GEMMs with per-group
+    scales."""
+    T, H = X.shape
+    G, N1, _ = W1.shape
+    F = N1 // 2
+    base = offs[0]
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    ld = sge.mx_token_capacity(T, G)
+    lay = torch.empty(2, G + 1, dtype=torch.int64, device="cuda")
+    y = torch.empty(T, F, dtype=torch.bfloat16, device="cuda")
+    qws = torch.empty(max(16, sge.quantize_fp8_grouped_workspace_size(G)), **u8)
+
+    def qbuf(rows, cols, lcols):
+        return {"q": torch.empty(rows, cols, **u8), "q_t": torch.empty(cols, lcols, **u8),
+                "s": [torch.empty(G, dtype=torch.float32, device="cuda") for _ in range(3)]}
+
+    qx, qy, qd, qdh = qbuf(T, H, ld), qbuf(T, F, ld), qbuf(T, H, ld), qbuf(T, N1, ld)
+    qw1, qw2 = qbuf(G * N1, H, G * N1), qbuf(G * H, F, G * H)
+    W1f, W2f = W1.reshape(G * N1, H), W2.reshape(G * H, F)
+
+    def quant(src, b, layout):
+        return lambda: sge.quantize_fp8_grouped(src, G, *b["s"], qws, layout=layout, q=b["q"], q_t=b["q_t"])
+
+    sinv = lambda b: b["s"][2]   # noqa: E731
+    hbm = {"quant_x": T * H * 6, "quant_w1": G * N1 * H * 6, "quant_w2": G * H * F * 6, "quant_y": T * F * 6,
+           "quant_dout": T * H * 6, "quant_dh": T * N1 * 6}
+    launches = [
+        ("offsets", lambda: sge.splits_to_offsets(splits, [1, H], offs)),
+        ("layout", lambda: sge.mx_group_layout(base, T, lay)),
+        ("quant_x", quant(X, qx, lay)),
+        ("quant_w1", quant(W1f, qw1, None)),
+        ("quant_w2", quant(W2f, qw2, None)),
+        ("fc1_fwd", lambda: sge.grouped_linear_fwd_fp8(qx["q"], sinv(qx), qw1["q"].view(G, N1, H), sinv(qw1), base,
+                                                       y, epilogue=sge.EPI_SCALED_SWIGLU, probs=P, preact=h)),
+        ("quant_y", quant(y, qy, lay)),
+        ("fc2_fwd", lambda: sge.grouped_linear_fwd_fp8(qy["q"], sinv(qy), qw2["q"].view(G, H, F), sinv(qw2), base,
+                                                       out)),
+        ("quant_dout", quant(DOUT, qd, lay)),
+        ("fc2_dgrad_dswiglu", lambda: sge.grouped_linear_dgrad_fp8(
+            qd["q"], sinv(qd), qw2["q_t"], sinv(qw2), base, epilogue=sge.EPI_DSCALED_SWIGLU, preact=h, probs=P,
+            dact=dh, dprobs=dp, workspace=ws)),
+        ("fc2_wgrad", lambda: sge.grouped_linear_wgrad_fp8(qd["q_t"], sinv(qd), qy["q_t"], sinv(qy), lay, dw2)),
+        ("quant_dh", quant(dh, qdh, lay)),
+        ("fc1_dgrad", lambda: sge.grouped_linear_dgrad_fp8(qdh["q"], sinv(qdh), qw1["q_t"], sinv(qw1), base, dx=dx)),
+        ("fc1_wgrad", lambda: sge.grouped_linear_wgrad_fp8(qdh["q_t"], sinv(qdh), qx["q_t"], sinv(qx), lay, dw1)),
+    ]
+    return launches, flops, hbm
+
+
 # ----------------------------------------------------------- CPU baseline
 def cpu_baseline(wl, inp, target_s):
     """The oracle, as it stands, on a bounded sample of the same workload (rows of the token dim)."""
@@ -317,6 +372,25 @@ def cpu_baseline(wl, inp, target_s):
         flops = (3 if bwd else 1) * 2 * rows * N * K
         sample = (f"first {rows} of {M} token rows through {'/'.join(wl['passes'])} (quantizers included)"
                   + (f", mean of {reps} runs" if reps > 1 else ""))
+    elif wl["fmt"] == "fp8":
+        T = inp["x"].shape[0]
+        tok = 256
+        while True:
+            t0 = time.perf_counter()
+            # first `tok` tokens, all routed to expert 0 (its weights only are quantized)
+            b1 = np.array([0, tok], np.int64)
+            f = grouped.grouped_mlp_fwd_fp8(inp["x"][:tok], inp["w1"][:1], inp["w2"][:1], inp["p"][:tok], b1)
+            grouped.grouped_mlp_bwd_fp8(inp["x"][:tok], inp["w1"][:1], inp["w2"][:1], inp["p"][:tok], b1,
+                                        inp["dout"][:tok], fwd=f)
+            dt = time.perf_counter() - t0
+            if dt >= target_s / 4 or tok >= T:
+                break
+            tok = min(T, tok * 4)
+        H = inp["x"].shape[1]
+        N1 = inp["w1"].shape[1]
+        flops = 3 * (2 * tok * N1 * H + 2 * tok * H * (N1 // 2))
+        sample = (f"first {tok} of {T} tokens through the FP8 (per-group current scaling) grouped MLP forward + "
+                  "backward with one expert (quantization of that expert's weights included)")
     elif wl["fmt"] == "mxfp8":
         T = inp["x"].shape[0]
         tok = 256

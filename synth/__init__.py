@@ -113,6 +113,9 @@ WORKLOADS = {
                                                    ffn=2048, alpha=1.0, passes=("fwd",)),
     "mxfp8_grouped_swiglu_mlp_T65536_G8": dict(kind="grouped", fmt="mxfp8", T=65536, G=8, hidden=2048,
                                                ffn=2048, alpha=1.0, passes=("fwd", "bwd")),
+    # and on FP8 E4M3 operands with current scaling per group (forward + backward)
+    "fp8_grouped_swiglu_mlp_T65536_G8": dict(kind="grouped", fmt="fp8", T=65536, G=8, hidden=2048, ffn=2048,
+                                             alpha=1.0, passes=("fwd", "bwd")),
 }
 
 

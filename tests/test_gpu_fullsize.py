@@ -12,7 +12,7 @@ import synth
 from oracle import grouped, linear, offsets, quant
 from oracle.codecs import bf16_to_f64, f64_to_bf16
 
-from .gpu_paths import run_dense, run_grouped_mlp, run_grouped_mlp_bwd_mx, run_grouped_mlp_fwd_mx
+from .gpu_paths import run_dense, run_grouped_mlp, run_grouped_mlp_bwd_mx, run_grouped_mlp_fp8, run_grouped_mlp_fwd_mx
 from .helpers import TAU_BF16, TAU_FP8, assert_close, assert_mx_dequant_close, host_f64, host_u8
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -221,3 +221,31 @@ def test_grouped_mxfp8_backward_full_size_sampled():
         ref_dw1 = grouped.grouped_linear_wgrad_mxfp8(f64_to_bf16(dh_sub), xg[:, hs], one)[0]
         assert_close(host_f64(got["dw1"][g][torch.from_numpy(rows1).cuda()][:, torch.from_numpy(hs).cuda()]),
                      ref_dw1, TAU_FP8, what=f"dw1 g{g}", **kw)
+
+
+def test_grouped_fp8_full_size_sampled():
+    name = "fp8_grouped_swiglu_mlp_T65536_G8"
+    print(f"case full-size {name}", flush=True)
+    inp = synth.workload_inputs(name, seed=0)
+    got = run_grouped_mlp_fp8(inp)
+    base = offsets.base_offsets(inp["splits"])
+    sizes = np.diff(base)
+    rng = np.random.default_rng(13)
+    kw = dict(rel_tight=2.0 ** -3, abs_tight=0.1)
+    # per-group scales depend on a whole group: the oracle reruns the two smallest groups whole
+    for g in [int(v) for v in np.argsort(np.where(sizes > 0, sizes, 1 << 62))[:2]]:
+        lo, hi = int(base[g]), int(base[g + 1])
+        one = np.array([0, hi - lo])
+        args = (inp["x"][lo:hi], inp["w1"][g:g + 1], inp["w2"][g:g + 1], inp["p"][lo:hi], one)
+        fwd = grouped.grouped_mlp_fwd_fp8(*args)
+        bwd = grouped.grouped_mlp_bwd_fp8(*args, inp["dout"][lo:hi], fwd=fwd)
+        rows = _pick(hi - lo, 8, rng)
+        tt = torch.from_numpy(rows + lo).cuda()
+        for key, ref in (("h", fwd["h"]), ("y", fwd["y"]), ("out", fwd["out"]), ("dh", bwd["dh"]),
+                         ("dx", bwd["dx"])):
+            assert_close(host_f64(got[key][tt]), ref[rows], TAU_FP8, what=f"{key} g{g}", **kw)
+        assert_close(host_f64(got["dp"][tt]), bwd["dp"][rows], TAU_FP8, what=f"dprobs g{g}", **kw)
+        for key in ("dw1", "dw2"):
+            r_, c_ = _pick(bwd[key].shape[1], 8, rng), _pick(bwd[key].shape[2], 8, rng)
+            sub = got[key][g][torch.from_numpy(r_).cuda()][:, torch.from_numpy(c_).cuda()]
+            assert_close(host_f64(sub), bwd[key][0][np.ix_(r_, c_)], TAU_FP8, what=f"{key} g{g}", **kw)
