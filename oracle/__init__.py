@@ -22,6 +22,8 @@ Sources (web pages, cited by title and section):
 * "Activation + GroupedLinear Fusion for MOE and other MOE optimizations"
   (TransformerEngine PR 3238): scaled SwiGLU, grouped linear, precomputed
   split offsets (Description; Greptile Summary; Sequence Diagram).
+* "NVIDIA TransformerEngine PyTorch Ext Normalization" (leeroopedia), Description and I/O
+  Contract: LayerNorm / RMSNorm forward and backward with fused quantized outputs.
 
 Number formats the pages name but do not define are taken from their public
 specifications: OCP 8-bit Floating Point Specification (OFP8) rev. 1.0 for
@@ -33,4 +35,4 @@ other than itself (brute force, closed forms, exhaustive tables, library
 routines, invariants). No function is "parity unpinned".
 """
 
-from . import codecs, quant, linear, offsets, grouped  # noqa: F401
+from . import codecs, quant, linear, offsets, grouped, norm  # noqa: F401
