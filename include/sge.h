@@ -389,6 +389,45 @@ sge_status sge_grouped_linear_wgrad_fp8(const void* dyT_q, const float* dy_sinv,
                                         hipStream_t stream);
 
 /*
+ * RMSNorm / LayerNorm with the quantized outputs that feed a linear.
+ * ("NVIDIA TransformerEngine PyTorch Ext Normalization", Description and I/O Contract: the
+ * forward returns the normalized, optionally quantized, output with the statistics saved
+ * for the backward; current scaling computes the norm and its amax, then quantizes; MXFP8
+ * is written by the norm kernel; the backward returns dx, dgamma and dbeta; gamma may be
+ * zero-centered.)
+ *
+ * x, dz, y, dx: bf16 [rows, cols]; gamma, beta, dgamma, dbeta: bf16 [cols]; mu, rsigma: fp32
+ * [rows] (mu LayerNorm only). g = gamma, or 1 + gamma when zero_centered != 0.
+ *   RMSNorm:   rsigma = 1/sqrt(mean(x^2) + eps),        y = x * rsigma * g
+ *   LayerNorm: mu = mean(x), rsigma = 1/sqrt(mean((x-mu)^2) + eps), y = (x-mu) * rsigma * g + beta
+ * Statistics in fp32, y rounded once to bf16 (always written). Optional quantized outputs of
+ * the bf16 y, byte-identical to the standalone quantizers run on it:
+ *   FP8 current scaling (q [rows, cols] and/or q_t [cols, rows], with amax, scale, scale_inv
+ *   as in sge_quantize_fp8_amax): the norm kernel reduces y's amax, a quantize pass follows;
+ *   rows % 16 == 0, cols % 16 == 0; workspace >= sge_norm_fwd_workspace_size.
+ *   MXFP8 rowwise (q_row [rows, cols] + s_row [rows, cols/32], written by the norm kernel)
+ *   and/or columnwise (q_colT [cols, rows] + s_colT [cols, rows/32], a pass over y;
+ *   rows % 32 == 0); cols % 32 == 0.
+ * Backward (xhat = (x - mu) * rsigma, mu = 0 for RMSNorm, d = dz * g):
+ *   dx = rsigma * (d - mean(d) - xhat * mean(d * xhat))   (RMSNorm: without mean(d))
+ *   dgamma = sum_rows dz * xhat, dbeta = sum_rows dz (fixed-order sums, deterministic);
+ *   mu and rsigma as the forward saved them; workspace >= sge_norm_bwd_workspace_size.
+ * cols % 8 == 0 and 8 <= cols <= 16384.
+ */
+typedef enum { SGE_NORM_RMS = 0, SGE_NORM_LAYER = 1 } sge_norm_kind;
+size_t sge_norm_fwd_workspace_size(int64_t rows, int64_t cols);
+sge_status sge_norm_fwd(int32_t kind, const void* x, const void* gamma, const void* beta, int64_t rows,
+                        int64_t cols, float eps, int32_t zero_centered, void* y, float* mu, float* rsigma,
+                        uint8_t* q, uint8_t* q_t, float* amax, float* scale, float* scale_inv,
+                        uint8_t* q_row, uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+size_t sge_norm_bwd_workspace_size(int64_t rows, int64_t cols);
+sge_status sge_norm_bwd(int32_t kind, const void* dz, const void* x, const float* mu, const float* rsigma,
+                        const void* gamma, int64_t rows, int64_t cols, int32_t zero_centered, void* dx,
+                        void* dgamma, void* dbeta, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
  * Unfused per-token scaled SwiGLU (the composition the fused epilogues replace).
  * ("Activation + GroupedLinear Fusion for MOE and other MOE optimizations",
  * Description: scaled SwiGLU tex API.)

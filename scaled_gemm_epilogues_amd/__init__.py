@@ -27,6 +27,8 @@ OK, ERR_NULL, ERR_SHAPE, ERR_FORMAT, ERR_ALIGN, ERR_ALIAS, ERR_WORKSPACE, ERR_AR
 FMT_BF16, FMT_E4M3, FMT_MXFP8 = 0, 1, 2
 # grouped epilogues
 EPI_NONE, EPI_SCALED_SWIGLU, EPI_DSCALED_SWIGLU = 0, 1, 2
+# normalizations
+NORM_RMS, NORM_LAYER = 0, 1
 
 EXPORTED = (
     "sge_abi_version", "sge_status_string", "sge_last_error_message",
@@ -39,6 +41,7 @@ EXPORTED = (
     "sge_grouped_linear_dgrad_mxfp8", "sge_grouped_linear_wgrad_mxfp8",
     "sge_quantize_fp8_grouped_workspace_size", "sge_quantize_fp8_grouped", "sge_grouped_linear_fwd_fp8",
     "sge_grouped_linear_dgrad_fp8", "sge_grouped_linear_wgrad_fp8",
+    "sge_norm_fwd_workspace_size", "sge_norm_fwd", "sge_norm_bwd_workspace_size", "sge_norm_bwd",
 )
 
 
@@ -93,6 +96,11 @@ _SIGS = {
                                       _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "sge_grouped_linear_wgrad_fp8": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _f32, _vp, _vp],
                                      ctypes.c_int),
+    "sge_norm_fwd_workspace_size": ([_i64, _i64], _sz),
+    "sge_norm_fwd": ([_i32, _vp, _vp, _vp, _i64, _i64, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                      _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "sge_norm_bwd_workspace_size": ([_i64, _i64], _sz),
+    "sge_norm_bwd": ([_i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -333,6 +341,39 @@ def grouped_linear_wgrad_fp8(dyT_q, dy_sinv, xT_q, x_sinv, layout, dw, alpha=1.0
     G = layout.numel() // 2 - 1
     _check(_lib.sge_grouped_linear_wgrad_fp8(_ptr(dyT_q), _ptr(dy_sinv), _ptr(xT_q), _ptr(x_sinv), G, N, K,
                                              _ptr(layout), ld, float(alpha), _ptr(dw), _stream(stream)))
+
+
+# ---------------------------------------------------------- normalization
+def norm_fwd_workspace_size(rows, cols):
+    return int(_lib.sge_norm_fwd_workspace_size(int(rows), int(cols)))
+
+
+def norm_fwd(kind, x, gamma, y, rsigma, beta=None, mu=None, eps=1e-5, zero_centered=False, fp8=None, mx_row=None,
+             mx_col=None, workspace=None, stream=None):
+    """RMSNorm / LayerNorm of bf16 ``x`` [rows, cols] into bf16 ``y`` (+ mu, rsigma). ``fp8``: dict of q, q_t,
+    amax, scale, scale_inv; ``mx_row`` / ``mx_col``: (q, s) pairs of the MXFP8 copies of y."""
+    rows, cols = x.shape
+    f = fp8 or {}
+    qr, sr = mx_row if mx_row is not None else (None, None)
+    qc, sc = mx_col if mx_col is not None else (None, None)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.sge_norm_fwd(int(kind), _ptr(x), _ptr(gamma), _ptr(beta), rows, cols, float(eps), int(zero_centered),
+                             _ptr(y), _ptr(mu), _ptr(rsigma), _ptr(f.get("q")), _ptr(f.get("q_t")), _ptr(f.get("amax")),
+                             _ptr(f.get("scale")), _ptr(f.get("scale_inv")), _ptr(qr), _ptr(sr), _ptr(qc), _ptr(sc),
+                             _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def norm_bwd_workspace_size(rows, cols):
+    return int(_lib.sge_norm_bwd_workspace_size(int(rows), int(cols)))
+
+
+def norm_bwd(kind, dz, x, rsigma, gamma, dx, dgamma, workspace, mu=None, dbeta=None, zero_centered=False,
+             stream=None):
+    """Backward of ``norm_fwd``: dx [rows, cols], dgamma (and LayerNorm dbeta) [cols], all bf16."""
+    rows, cols = x.shape
+    _check(_lib.sge_norm_bwd(int(kind), _ptr(dz), _ptr(x), _ptr(mu), _ptr(rsigma), _ptr(gamma), rows, cols,
+                             int(zero_centered), _ptr(dx), _ptr(dgamma), _ptr(dbeta), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def scaled_swiglu_fwd(h, probs, y, stream=None):

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsge.so")
-SOURCES = ["gemm.hip", "quant.hip", "aux.hip", "abi.cpp"]
+SOURCES = ["gemm.hip", "quant.hip", "aux.hip", "norm.hip", "abi.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [

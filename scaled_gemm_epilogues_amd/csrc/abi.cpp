@@ -877,6 +877,108 @@ sge_status sge_grouped_linear_wgrad_fp8(const void* dyT_q, const float* dy_sinv,
   return hip_status(sge::launch_grouped_wgrad_fp8(p, stream), "grouped wgrad fp8 launch");
 }
 
+size_t sge_norm_fwd_workspace_size(int64_t rows, int64_t cols) {
+  (void)cols;
+  return rows < 0 ? 0 : (size_t)sge::norm_blocks(rows) * 4;
+}
+
+sge_status sge_norm_fwd(int32_t kind, const void* x, const void* gamma, const void* beta, int64_t rows, int64_t cols,
+                        float eps, int32_t zero_centered, void* y, float* mu, float* rsigma, uint8_t* q, uint8_t* q_t,
+                        float* amax, float* scale, float* scale_inv, uint8_t* q_row, uint8_t* s_row, uint8_t* q_colT,
+                        uint8_t* s_colT, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (kind != SGE_NORM_RMS && kind != SGE_NORM_LAYER) return fail(SGE_ERR_ARG, "norm_fwd: kind %d unknown", kind);
+  const bool ln = kind == SGE_NORM_LAYER;
+  if (rows < 0 || cols < 0) return fail(SGE_ERR_SHAPE, "norm_fwd: negative size");
+  // per-row pointers may be NULL when there are no rows
+  if (!gamma || (ln && !beta) || (rows > 0 && (!x || !y || !rsigma || (ln && !mu))))
+    return fail(SGE_ERR_NULL, "norm_fwd: NULL pointer");
+  const bool fp8 = q || q_t, mxr = q_row || s_row, mxc = q_colT || s_colT;
+  if (fp8 && (!amax || !scale || !scale_inv))
+    return fail(SGE_ERR_NULL, "norm_fwd: the FP8 output needs amax, scale and scale_inv");
+  if ((mxr && (!q_row || !s_row)) || (mxc && (!q_colT || !s_colT)))
+    return fail(SGE_ERR_NULL, "norm_fwd: MXFP8 data and scale pointers come in pairs");
+  if (cols == 0 || cols % 8 || cols > 16384) return fail(SGE_ERR_SHAPE, "norm_fwd: cols must be a multiple of 8 in [8, 16384]");
+  if ((mxr || mxc) && cols % 32) return fail(SGE_ERR_SHAPE, "norm_fwd: MXFP8 output needs cols %% 32 == 0");
+  if (mxc && rows % 32) return fail(SGE_ERR_SHAPE, "norm_fwd: the columnwise MXFP8 copy needs rows %% 32 == 0");
+  if (fp8 && (rows % 16 || cols % 16)) return fail(SGE_ERR_SHAPE, "norm_fwd: FP8 output needs rows and cols %% 16 == 0");
+  if ((x && !aligned16(x)) || !aligned16(gamma) || (beta && !aligned16(beta)) || (y && !aligned16(y)) || (q && !aligned16(q)) ||
+      (q_t && !aligned16(q_t)) || (q_row && !aligned16(q_row)) || (q_colT && !aligned16(q_colT)))
+    return fail(SGE_ERR_ALIGN, "norm_fwd: pointers must be 16-byte aligned");
+  const Range in[3] = {range_of(x, rows, cols, cols, 2), range_of(gamma, 1, cols, cols, 2),
+                       ln ? range_of(beta, 1, cols, cols, 2) : Range{0, 0}};
+  const Range outs[9] = {range_of(y, rows, cols, cols, 2), ln ? range_of(mu, 1, rows, rows, 4) : Range{0, 0},
+                         range_of(rsigma, 1, rows, rows, 4), q ? range_of(q, rows, cols, cols, 1) : Range{0, 0},
+                         q_t ? range_of(q_t, cols, rows, rows, 1) : Range{0, 0},
+                         q_row ? range_of(q_row, rows, cols, cols, 1) : Range{0, 0},
+                         s_row ? range_of(s_row, rows, cols / 32, cols / 32, 1) : Range{0, 0},
+                         q_colT ? range_of(q_colT, cols, rows, rows, 1) : Range{0, 0},
+                         s_colT ? range_of(s_colT, cols, rows / 32, rows / 32, 1) : Range{0, 0}};
+  for (int a = 0; a < 9; ++a) {
+    for (const Range& i : in)
+      if (overlap(outs[a], i)) return fail(SGE_ERR_ALIAS, "norm_fwd: an output overlaps an input");
+    for (int b = a + 1; b < 9; ++b)
+      if (overlap(outs[a], outs[b])) return fail(SGE_ERR_ALIAS, "norm_fwd: outputs overlap");
+  }
+  const size_t need = fp8 ? sge_norm_fwd_workspace_size(rows, cols) : 0;
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(SGE_ERR_WORKSPACE, "norm_fwd: workspace %zu < %zu bytes", workspace_bytes, need);
+  if (rows == 0) return ok();
+  uint32_t* part = fp8 ? static_cast<uint32_t*>(workspace) : nullptr;
+  hipError_t e = sge::launch_norm_fwd(ln, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(gamma),
+                                      static_cast<const uint16_t*>(beta), rows, cols, eps, zero_centered ? 1 : 0,
+                                      static_cast<uint16_t*>(y), ln ? mu : nullptr, rsigma, part, q_row, s_row, stream);
+  if (e != hipSuccess) return hip_status(e, "norm_fwd launch");
+  if (fp8) {
+    e = sge::launch_quantize_fp8(static_cast<const uint16_t*>(y), rows, cols, part, sge::norm_blocks(rows), q, q_t,
+                                 amax, scale, scale_inv, stream);
+    if (e != hipSuccess) return hip_status(e, "norm_fwd quantize launch");
+  }
+  if (mxc) {
+    e = sge::launch_quantize_mxfp8(static_cast<const uint16_t*>(y), rows, cols, nullptr, nullptr, q_colT, s_colT,
+                                   stream);
+    if (e != hipSuccess) return hip_status(e, "norm_fwd columnwise MXFP8 launch");
+  }
+  return ok();
+}
+
+size_t sge_norm_bwd_workspace_size(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols <= 0) return 0;
+  return (size_t)sge::norm_bwd_blocks(rows) * (size_t)cols * 2 * sizeof(float);
+}
+
+sge_status sge_norm_bwd(int32_t kind, const void* dz, const void* x, const float* mu, const float* rsigma,
+                        const void* gamma, int64_t rows, int64_t cols, int32_t zero_centered, void* dx, void* dgamma,
+                        void* dbeta, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (kind != SGE_NORM_RMS && kind != SGE_NORM_LAYER) return fail(SGE_ERR_ARG, "norm_bwd: kind %d unknown", kind);
+  const bool ln = kind == SGE_NORM_LAYER;
+  if (rows < 0 || cols < 0) return fail(SGE_ERR_SHAPE, "norm_bwd: negative size");
+  // per-row pointers may be NULL when there are no rows
+  if (!gamma || !dgamma || (ln && !dbeta) || (rows > 0 && (!dz || !x || !rsigma || !dx || (ln && !mu))))
+    return fail(SGE_ERR_NULL, "norm_bwd: NULL pointer");
+  if (cols == 0 || cols % 8 || cols > 16384) return fail(SGE_ERR_SHAPE, "norm_bwd: cols must be a multiple of 8 in [8, 16384]");
+  if ((dz && !aligned16(dz)) || (x && !aligned16(x)) || !aligned16(gamma) || (dx && !aligned16(dx)))
+    return fail(SGE_ERR_ALIGN, "norm_bwd: pointers must be 16-byte aligned");
+  const Range in[5] = {range_of(dz, rows, cols, cols, 2), range_of(x, rows, cols, cols, 2),
+                       range_of(gamma, 1, cols, cols, 2), range_of(rsigma, 1, rows, rows, 4),
+                       ln ? range_of(mu, 1, rows, rows, 4) : Range{0, 0}};
+  const Range outs[3] = {range_of(dx, rows, cols, cols, 2), range_of(dgamma, 1, cols, cols, 2),
+                         ln ? range_of(dbeta, 1, cols, cols, 2) : Range{0, 0}};
+  for (int a = 0; a < 3; ++a) {
+    for (const Range& i : in)
+      if (overlap(outs[a], i)) return fail(SGE_ERR_ALIAS, "norm_bwd: an output overlaps an input");
+    for (int b = a + 1; b < 3; ++b)
+      if (overlap(outs[a], outs[b])) return fail(SGE_ERR_ALIAS, "norm_bwd: outputs overlap");
+  }
+  const size_t need = sge_norm_bwd_workspace_size(rows, cols);
+  if (!workspace || workspace_bytes < need)
+    return fail(SGE_ERR_WORKSPACE, "norm_bwd: workspace %zu < %zu bytes", workspace_bytes, need);
+  return hip_status(sge::launch_norm_bwd(ln, static_cast<const uint16_t*>(dz), static_cast<const uint16_t*>(x), mu,
+                                         rsigma, static_cast<const uint16_t*>(gamma), rows, cols, zero_centered ? 1 : 0,
+                                         static_cast<uint16_t*>(dx), static_cast<uint16_t*>(dgamma),
+                                         static_cast<uint16_t*>(dbeta), static_cast<float*>(workspace), stream),
+                    "norm_bwd launch");
+}
+
 sge_status sge_scaled_swiglu_fwd(const void* h, const float* probs, void* y, int64_t T, int64_t F, hipStream_t stream) {
   if (T < 0 || F < 0) return fail(SGE_ERR_SHAPE, "scaled_swiglu_fwd: negative size");
   if (T > 0 && (!h || !probs || !y)) return fail(SGE_ERR_NULL, "scaled_swiglu_fwd: NULL pointer");

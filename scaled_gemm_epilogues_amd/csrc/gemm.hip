@@ -89,32 +89,6 @@ __device__ __forceinline__ float fast_sigmoid(float a) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-a));
 }
 
-typedef int v4i __attribute__((__vector_size__(4 * sizeof(int))));
-typedef int v2i __attribute__((__vector_size__(2 * sizeof(int))));
-
-// MXFP8 of 8 bf16 values (one lane's 16 bytes, packed pairs) inside a block of 32 that four
-// adjacent lanes (lane ^ 1, lane ^ 2) hold together: the block amax of the bf16 magnitudes,
-// the E8M0 exponent, and this lane's 8 E4M3 codes. Every lane of the wave must take part.
-__device__ __forceinline__ v2i mx_quant_lane8(const v4i& v, int& e8m0) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t w = (uint32_t)v[e], lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
-    m = lo > m ? lo : m;
-    m = hi > m ? hi : m;
-  }
-  uint32_t o = __shfl_xor(m, 1, 64);
-  m = o > m ? o : m;
-  o = __shfl_xor(m, 2, 64);
-  m = o > m ? o : m;
-  const int X = mx_exponent(m);
-  const float sc = pow2_neg(X);
-  uint32_t qb[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) qb[e] = e4m3x2(bf16_lo((uint32_t)v[e]) * sc, bf16_hi((uint32_t)v[e]) * sc);
-  e8m0 = X + 127;
-  return v2i{(int)(qb[0] | (qb[1] << 16)), (int)(qb[2] | (qb[3] << 16))};
-}
 
 typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 

@@ -85,6 +85,19 @@ hipError_t launch_quantize_fp8_grouped(const uint16_t* src, int64_t rows, int64_
 hipError_t launch_mx_group_layout(const int64_t* offsets, int G, int64_t T, int64_t align, int64_t* layout,
                                   hipStream_t s);
 
+// RMSNorm (ln false) / LayerNorm forward: bf16 y, fp32 mu (LayerNorm; may be NULL) and rsigma
+// per row; optionally one amax partial per block (norm_blocks(rows) of them) and the rowwise
+// MXFP8 copy of y. cols % 32 == 0 (8 for no MXFP8), cols <= 16384.
+int norm_blocks(int64_t rows);
+int norm_bwd_blocks(int64_t rows);
+hipError_t launch_norm_fwd(bool ln, const uint16_t* x, const uint16_t* gamma, const uint16_t* beta, int64_t rows,
+                           int64_t cols, float eps, int zc, uint16_t* y, float* mu, float* rsigma,
+                           uint32_t* amax_part, uint8_t* q_row, uint8_t* s_row, hipStream_t s);
+// Backward: dx bf16, dgamma (and LayerNorm dbeta) bf16 [cols] via fp32 partials
+// [2][norm_bwd_blocks(rows)][cols] in `part`.
+hipError_t launch_norm_bwd(bool ln, const uint16_t* dz, const uint16_t* x, const float* mu, const float* rsigma,
+                           const uint16_t* gamma, int64_t rows, int64_t cols, int zc, uint16_t* dx, uint16_t* dgamma,
+                           uint16_t* dbeta, float* part, hipStream_t s);
 hipError_t launch_splits_to_offsets(const int64_t* splits, int G, const int64_t* mults, int n_mult,
                                     int64_t expected_total, int64_t* offsets, int32_t* err_flag,
                                     hipStream_t s);

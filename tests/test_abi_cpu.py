@@ -323,3 +323,47 @@ def test_fp8_grouped_validation_errors(sge):
     assert w(*a) == sge.ERR_SHAPE
     a = list(ok); a[10] = B(3)
     assert w(*a) == sge.ERR_ALIAS
+
+
+def test_norm_validation_errors(sge):
+    def B(k):
+        return FAKE * 8 * k
+
+    f = sge._lib.sge_norm_fwd
+    R, C = 64, 96
+    ws = sge.norm_fwd_workspace_size(R, C)
+    ok = [sge.NORM_LAYER, B(1), B(2), B(3), R, C, 1e-5, 0, B(4), B(5), B(6), B(7), B(8), B(9), B(10), B(11),
+          B(12), B(13), B(14), B(15), B(16), ws, None]
+    a = list(ok); a[0] = 5
+    assert f(*a) == sge.ERR_ARG
+    a = list(ok); a[3] = None
+    assert f(*a) == sge.ERR_NULL                                          # LayerNorm needs beta
+    a = list(ok); a[13] = None
+    assert f(*a) == sge.ERR_NULL                                          # FP8 output needs amax
+    a = list(ok); a[17] = None
+    assert f(*a) == sge.ERR_NULL                                          # q_row without s_row
+    a = list(ok); a[5] = 16392
+    assert f(*a) == sge.ERR_SHAPE                                         # cols <= 16384
+    a = list(ok); a[5] = 72
+    assert f(*a) == sge.ERR_SHAPE                                         # MXFP8 needs cols % 32
+    a = list(ok); a[4] = 48
+    assert f(*a) == sge.ERR_SHAPE                                         # MXFP8 columnwise needs rows % 32
+    a = list(ok); a[8] = B(4) + 2
+    assert f(*a) == sge.ERR_ALIGN
+    a = list(ok); a[8] = B(1)
+    assert f(*a) == sge.ERR_ALIAS                                         # y over x
+    a = list(ok); a[21] = 0
+    assert f(*a) == sge.ERR_WORKSPACE
+    b = sge._lib.sge_norm_bwd
+    wsb = sge.norm_bwd_workspace_size(R, C)
+    ok = [sge.NORM_RMS, B(1), B(2), None, B(3), B(4), R, C, 0, B(5), B(6), None, B(7), wsb, None]
+    a = list(ok); a[10] = None
+    assert b(*a) == sge.ERR_NULL                                          # dgamma
+    a = list(ok); a[0] = sge.NORM_LAYER
+    assert b(*a) == sge.ERR_NULL                                          # LayerNorm needs mu and dbeta
+    a = list(ok); a[7] = 100
+    assert b(*a) == sge.ERR_SHAPE
+    a = list(ok); a[9] = B(2)
+    assert b(*a) == sge.ERR_ALIAS                                         # dx over x
+    a = list(ok); a[13] = wsb - 4
+    assert b(*a) == sge.ERR_WORKSPACE
