@@ -156,10 +156,31 @@ def build_dense(torch, sge, wl, inp):
                     for name, b in bufs.items()]
 
     launches = list(quantize_launches())
+    if wl.get("norm"):
+        # the linear's input is RMSNorm(x): the norm kernel writes the MXFP8 operands (rowwise
+        # from registers, columnwise by a pass over its bf16 output) in place of quant_x, and
+        # the norm's backward takes the dgrad as its incoming gradient
+        assert fmt == "mxfp8" and wl["norm"] == "rms"
+        gam = dev_bf16(inp["gamma"])
+        Y = torch.empty_like(X)
+        RS = torch.empty(M, **f32)
+        DX = torch.empty_like(X)
+        DG = torch.empty(K, dtype=torch.bfloat16, device="cuda")
+        nws = torch.empty(sge.norm_bwd_workspace_size(M, K), **u8)
+        launches = [(n, f) for n, f in launches if n != "quant_x"]
+        launches.insert(0, ("norm_fwd", lambda: sge.norm_fwd(sge.NORM_RMS, X, gam, Y, RS, eps=wl["eps"],
+                                                              mx_row=(bx["q_row"], bx["s_row"]),
+                                                              mx_col=(bx["q_colT"], bx["s_colT"]))))
+        hbm.pop("quant_x")
+        # x read, y written, its two MXFP8 copies written, y read back for the columnwise copy
+        hbm["norm_fwd"] = M * K * (2 + 2 + 1 + 2 + 1) + 2 * (M * K // 32)
+        hbm["norm_bwd"] = M * K * (2 + 2 + 2)                    # dz and x read, dx written
     launches.append(("gemm_fwd", lambda: sge.linear_scale_add_fwd(*fwd, R, alpha)))
     if bwd:
         launches.append(("gemm_dgrad", lambda: sge.linear_scale_bwd(*dg, None, None, dgrad, None, alpha, alpha)))
         launches.append(("gemm_wgrad", lambda: sge.linear_scale_bwd(None, None, *wg, None, wgrad, alpha, alpha)))
+    if wl.get("norm"):
+        launches.append(("norm_bwd", lambda: sge.norm_bwd(sge.NORM_RMS, dgrad, X, RS, gam, DX, DG, nws)))
     return launches, flops, hbm
 
 
@@ -339,8 +360,8 @@ def cpu_baseline(wl, inp, target_s):
         cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:                                          # pragma: no cover
         cores = os.cpu_count() or 1
-    from oracle import grouped, linear, offsets
-    from oracle.codecs import bf16_to_f64
+    from oracle import grouped, linear, norm, offsets
+    from oracle.codecs import bf16_to_f64, f64_to_bf16
 
     if wl["kind"] == "dense":
         M = inp["x"].shape[0]
@@ -349,11 +370,18 @@ def cpu_baseline(wl, inp, target_s):
         bwd = "dgrad" in wl["passes"]
 
         def run(rows):
-            ops = linear.operands(wl["fmt"], inp["x"][:rows], inp["w"], inp["dy"][:rows] if bwd else None)
+            xin = inp["x"][:rows]
+            if wl.get("norm"):
+                nf = norm.norm_fwd(wl["norm"], xin, inp["gamma"], None, wl["eps"])
+                xin = nf["y_bits"]
+            ops = linear.operands(wl["fmt"], xin, inp["w"], inp["dy"][:rows] if bwd else None)
             linear.linear_scale_add_fwd(*ops["fwd"], bf16_to_f64(inp["residual"][:rows]), wl["alpha"])
             if bwd:
-                linear.linear_scale_dgrad(*ops["dgrad"], wl["alpha"])
+                dz = linear.linear_scale_dgrad(*ops["dgrad"], wl["alpha"])
                 linear.linear_scale_wgrad(*ops["wgrad"], wl["alpha"])
+                if wl.get("norm"):
+                    norm.norm_bwd(wl["norm"], f64_to_bf16(dz), inp["x"][:rows], nf["mu"], nf["rsigma"],
+                                  inp["gamma"])
 
         while True:
             t0 = time.perf_counter()

@@ -34,18 +34,21 @@ def _g(gamma_bits, zero_centered):
     return g + 1.0 if zero_centered else g
 
 
+def norm_stats(kind, x_bits, eps):
+    """Per-row statistics in fp64: mu (zeros for RMS) and rsigma."""
+    x = bf16_to_f64(x_bits)
+    mu = np.mean(x, axis=1) if kind == "ln" else np.zeros(x.shape[0])
+    xc = x - mu[:, None]
+    return mu, 1.0 / np.sqrt(np.mean(xc * xc, axis=1) + eps)
+
+
 def norm_fwd(kind, x_bits, gamma_bits, beta_bits, eps, zero_centered=False):
     """kind 'rms' or 'ln'. Returns y (fp64), y_bits (bf16), mu (fp32 [R]; zeros for RMS),
     rsigma (fp32 [R])."""
     x = bf16_to_f64(x_bits)
     g = _g(gamma_bits, zero_centered)
-    if kind == "ln":
-        mu = np.mean(x, axis=1)
-        xc = x - mu[:, None]
-    else:
-        mu = np.zeros(x.shape[0])
-        xc = x
-    rsigma = 1.0 / np.sqrt(np.mean(xc * xc, axis=1) + eps)
+    mu, rsigma = norm_stats(kind, x_bits, eps)
+    xc = x - mu[:, None]
     y = xc * rsigma[:, None] * g
     if kind == "ln":
         y = y + bf16_to_f64(beta_bits)

@@ -26,7 +26,7 @@ import torch
 
 # Stream order within a workload; fixed so every consumer sees the same values.
 STREAMS = ("x", "w", "residual", "dy", "p", "splits", "outliers_x", "outliers_w",
-           "outliers_dy", "w2", "dout")
+           "outliers_dy", "w2", "dout", "gamma")
 
 
 def streams(seed):
@@ -78,6 +78,12 @@ def dense(M, N, K, *, x_std=1.0, w_std=0.02, res_std=1.0, dy_std=1e-2, outliers=
     return out
 
 
+def norm_gamma(C, seed=0, std=0.1):
+    """bf16 bits of a normalization weight gamma [C] = 1 + std * N(0, 1) (drawn in float32)."""
+    a = streams(seed)["gamma"].standard_normal(size=C, dtype=np.float32) * np.float32(std) + np.float32(1.0)
+    return f32_to_bf16_bits(a)
+
+
 def grouped(T, G, hidden, ffn, *, seed=0, x_std=1.0, w_std=0.02, dout_std=1e-2, splits=None):
     """Inputs of the grouped MLP: x [T, hidden], W1 [G, 2*ffn, hidden], W2 [G, hidden, ffn],
     p [T] float32 U(0,1), dout [T, hidden], splits [G] int64."""
@@ -116,6 +122,11 @@ WORKLOADS = {
     # and on FP8 E4M3 operands with current scaling per group (forward + backward)
     "fp8_grouped_swiglu_mlp_T65536_G8": dict(kind="grouped", fmt="fp8", T=65536, G=8, hidden=2048, ffn=2048,
                                              alpha=1.0, passes=("fwd", "bwd")),
+    # the MXFP8 linear fed by an RMSNorm whose kernel writes the MXFP8 operand (forward + backward,
+    # the norm's backward included); x, W, dy as in the MXFP8 linear above, gamma = 1 + 0.1 N(0,1)
+    "rmsnorm_mxfp8_linear_fwdbwd_16384x8192x8192": dict(kind="dense", fmt="mxfp8", M=16384, N=8192, K=8192,
+                                                        alpha=0.25, outliers=True, w_std=1.0, dy_std=1.0,
+                                                        norm="rms", eps=1e-5, passes=("fwd", "dgrad", "wgrad")),
 }
 
 
@@ -123,7 +134,10 @@ def workload_inputs(name, seed=0):
     """Inputs of one named workload at its full size."""
     w = WORKLOADS[name]
     if w["kind"] == "dense":
-        return dense(w["M"], w["N"], w["K"], w_std=w.get("w_std", 0.02),
-                     dy_std=w.get("dy_std", 1e-2), outliers=w.get("outliers", False), seed=seed,
-                     with_dy="dgrad" in w["passes"])
+        d = dense(w["M"], w["N"], w["K"], w_std=w.get("w_std", 0.02),
+                  dy_std=w.get("dy_std", 1e-2), outliers=w.get("outliers", False), seed=seed,
+                  with_dy="dgrad" in w["passes"])
+        if w.get("norm"):
+            d["gamma"] = norm_gamma(w["K"], seed=seed)
+        return d
     return grouped(w["T"], w["G"], w["hidden"], w["ffn"], seed=seed)

@@ -249,3 +249,43 @@ def test_grouped_fp8_full_size_sampled():
             r_, c_ = _pick(bwd[key].shape[1], 8, rng), _pick(bwd[key].shape[2], 8, rng)
             sub = got[key][g][torch.from_numpy(r_).cuda()][:, torch.from_numpy(c_).cuda()]
             assert_close(host_f64(sub), bwd[key][0][np.ix_(r_, c_)], TAU_FP8, what=f"{key} g{g}", **kw)
+
+
+def test_rmsnorm_full_size_sampled():
+    name = "rmsnorm_mxfp8_linear_fwdbwd_16384x8192x8192"
+    w = synth.WORKLOADS[name]
+    print(f"case full-size {name} (norm)", flush=True)
+    import scaled_gemm_epilogues_amd as sge
+    from oracle import norm
+    from .gpu_paths import quant_mx
+    from .helpers import dev_bf16
+    d = synth.workload_inputs(name, seed=0)
+    M, K = w["M"], w["K"]
+    X, gam, DZ = dev_bf16(d["x"]), dev_bf16(d["gamma"]), dev_bf16(d["dy"][:, :K])
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    Y, RS = torch.empty_like(X), torch.empty(M, dtype=torch.float32, device="cuda")
+    mx_row = (torch.empty(M, K, **u8), torch.empty(M, K // 32, **u8))
+    mx_col = (torch.empty(K, M, **u8), torch.empty(K, M // 32, **u8))
+    sge.norm_fwd(sge.NORM_RMS, X, gam, Y, RS, eps=w["eps"], mx_row=mx_row, mx_col=mx_col)
+    DX, DG = torch.empty_like(X), torch.empty(K, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(sge.norm_bwd_workspace_size(M, K), **u8)
+    sge.norm_bwd(sge.NORM_RMS, DZ, X, RS, gam, DX, DG, ws)
+    alone = quant_mx(Y)
+    torch.cuda.synchronize()
+    # the fused MXFP8 copies equal the standalone quantizer on the same bf16 output, whole tensor
+    assert np.array_equal(host_u8(mx_row[0]), host_u8(alone["q_row"]))
+    assert np.array_equal(host_u8(mx_col[1]), host_u8(alone["s_colT"]))
+    rows = _pick(M, 8, np.random.default_rng(14))
+    ref = norm.norm_fwd("rms", d["x"][rows], d["gamma"], None, w["eps"])
+    tt = torch.from_numpy(rows).cuda()
+    kw = dict(rel_tight=2.0 ** -7, abs_tight=1e-3)
+    assert_close(host_f64(Y[tt]), ref["y"], TAU_BF16, what="y", **kw)
+    refb = norm.norm_bwd("rms", d["dy"][rows, :K], d["x"][rows], ref["mu"], ref["rsigma"], d["gamma"])
+    assert_close(host_f64(DX[tt]), refb["dx"], TAU_BF16, what="dx", **kw)
+    # dgamma sums every row: the oracle's statistics of all rows, and (dgamma of a column needs
+    # only that column given the statistics) the sampled columns over all rows
+    mu, rs = norm.norm_stats("rms", d["x"], w["eps"])
+    cs = _pick(K, 16, np.random.default_rng(15))
+    refg = norm.norm_bwd("rms", d["dy"][:, cs], d["x"][:, cs], mu.astype(np.float32), rs.astype(np.float32),
+                         d["gamma"][cs])
+    assert_close(host_f64(DG)[cs], refg["dgamma"], TAU_BF16, what="dgamma", **kw)
