@@ -12,17 +12,17 @@
 // rowwise MXFP8 copy of the bf16 output is written from registers (four adjacent lanes hold a
 // 32-column block), the bytes the standalone quantizer writes for the same bf16 output.
 //
-// Backward: the same row walk; per row the two means (of d*xhat, and of d for LayerNorm) are
-// block-reduced, dx is written in bf16, and each block keeps its own column sums of dz*xhat
-// and dz in registers, stored once as fp32 partials; a second kernel adds the partials of all
-// blocks in a fixed order (deterministic dgamma / dbeta).
+// Backward: the same row walk with the row's dz and x held in registers (one HBM read each);
+// per row the two means (of d*xhat, and of d for LayerNorm) are block-reduced, dx is written
+// in bf16, and each block keeps its own column sums of dz*xhat and dz in registers, stored
+// once as fp32 partials; a second kernel adds the partials of all blocks in a fixed order
+// (deterministic dgamma / dbeta).
 #include "common.h"
 #include "launch.h"
 
 namespace sge {
 
 constexpr int kNormThreads = 256;
-constexpr int kNormMaxChunks = 8;        // 8 chunks of 8 columns per thread: cols <= 16384
 constexpr int kNormBlocks = 1024;        // forward grid cap (= amax partials the quantize pass reduces)
 constexpr int kNormBwdBlocks = 512;      // backward grid cap (= dgamma / dbeta partial rows)
 
@@ -146,60 +146,74 @@ __global__ __launch_bounds__(kNormThreads) void norm_fwd_kernel(
   }
 }
 
-template <bool LN>
+template <bool LN, int NCH>
 __global__ __launch_bounds__(kNormThreads) void norm_bwd_kernel(
     const uint16_t* __restrict__ dz, const uint16_t* __restrict__ x, const float* __restrict__ mu_in,
     const float* __restrict__ rsigma_in, const uint16_t* __restrict__ gamma, int64_t rows, int64_t cols,
     int zero_centered, uint16_t* __restrict__ dx, float* __restrict__ dg_part, float* __restrict__ db_part) {
+  // NCH: chunks of 8 columns per thread (cols <= 2048 * NCH); the row's dz and x stay in
+  // registers (as loaded bf16) between the reduction pass and the dx pass.
   __shared__ float red[kNormThreads / 64];
   const int t = threadIdx.x;
-  const int nch = (int)((cols / 8 + kNormThreads - 1) / kNormThreads);
   const float gofs = zero_centered ? 1.0f : 0.0f;
   const float inv_cols = 1.0f / (float)cols;
-  float pg[kNormMaxChunks][8], pb[kNormMaxChunks][8];
+  float pg[NCH][8], pb[NCH][8], g[NCH][8];
 #pragma unroll
-  for (int i = 0; i < kNormMaxChunks; ++i)
+  for (int i = 0; i < NCH; ++i) {
+    const int64_t c = 8 * (int64_t)t + 2048 * (int64_t)i;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pg[i][e] = pb[i][e] = 0.0f;
+    for (int e = 0; e < 8; ++e) pg[i][e] = pb[i][e] = g[i][e] = 0.0f;
+    if (c < cols) {
+      load8(gamma + c, g[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g[i][e] += gofs;
+    }
+  }
   for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
     const float rs = rsigma_in[r];
     const float m = LN ? mu_in[r] : 0.0f;
     const uint16_t* dzr = dz + r * cols;
     const uint16_t* xr = x + r * cols;
+    uint4 ud[NCH], ux[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int64_t c = 8 * (int64_t)t + 2048 * (int64_t)i;
+      ud[i] = ux[i] = make_uint4(0, 0, 0, 0);
+      if (c < cols) {
+        ud[i] = *reinterpret_cast<const uint4*>(dzr + c);
+        ux[i] = *reinterpret_cast<const uint4*>(xr + c);
+      }
+    }
     float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kNormMaxChunks; ++i) {
-      const int64_t c = 8 * (int64_t)t + 2048 * (int64_t)i;
-      if (i < nch && c < cols) {
-        float d[8], v[8], g[8];
-        load8(dzr + c, d);
-        load8(xr + c, v);
-        load8(gamma + c, g);
+    for (int i = 0; i < NCH; ++i) {
+      const uint32_t wd[4] = {ud[i].x, ud[i].y, ud[i].z, ud[i].w}, wx[4] = {ux[i].x, ux[i].y, ux[i].z, ux[i].w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float xh = (v[e] - m) * rs;
-          const float dg = d[e] * (g[e] + gofs);
-          s1 += dg * xh;
-          if constexpr (LN) s2 += dg;
-          pg[i][e] += d[e] * xh;
-          if constexpr (LN) pb[i][e] += d[e];
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float d = (e & 1) ? bf16_hi(wd[e >> 1]) : bf16_lo(wd[e >> 1]);
+        const float v = (e & 1) ? bf16_hi(wx[e >> 1]) : bf16_lo(wx[e >> 1]);
+        const float xh = (v - m) * rs;
+        const float dg = d * g[i][e];
+        s1 += dg * xh;
+        if constexpr (LN) s2 += dg;
+        pg[i][e] += d * xh;                              // zero for columns past the row (d = 0)
+        if constexpr (LN) pb[i][e] += d;
       }
     }
     const float m1 = block_sum_f32(s1, red) * inv_cols;
     const float m2 = LN ? block_sum_f32(s2, red) * inv_cols : 0.0f;
 #pragma unroll
-    for (int i = 0; i < kNormMaxChunks; ++i) {
+    for (int i = 0; i < NCH; ++i) {
       const int64_t c = 8 * (int64_t)t + 2048 * (int64_t)i;
-      if (i < nch && c < cols) {
-        float d[8], v[8], g[8], o[8];
-        load8(dzr + c, d);
-        load8(xr + c, v);
-        load8(gamma + c, g);
+      if (c < cols) {
+        const uint32_t wd[4] = {ud[i].x, ud[i].y, ud[i].z, ud[i].w}, wx[4] = {ux[i].x, ux[i].y, ux[i].z, ux[i].w};
+        float o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float xh = (v[e] - m) * rs;
-          o[e] = rs * (d[e] * (g[e] + gofs) - m2 - xh * m1);
+          const float d = (e & 1) ? bf16_hi(wd[e >> 1]) : bf16_lo(wd[e >> 1]);
+          const float v = (e & 1) ? bf16_hi(wx[e >> 1]) : bf16_lo(wx[e >> 1]);
+          const float xh = (v - m) * rs;
+          o[e] = rs * (d * g[i][e] - m2 - xh * m1);
         }
         *reinterpret_cast<v4i*>(dx + r * cols + c) =
             v4i{(int)pack_bf16x2(o[0], o[1]), (int)pack_bf16x2(o[2], o[3]), (int)pack_bf16x2(o[4], o[5]),
@@ -208,9 +222,9 @@ __global__ __launch_bounds__(kNormThreads) void norm_bwd_kernel(
     }
   }
 #pragma unroll
-  for (int i = 0; i < kNormMaxChunks; ++i) {
+  for (int i = 0; i < NCH; ++i) {
     const int64_t c = 8 * (int64_t)t + 2048 * (int64_t)i;
-    if (i < nch && c < cols) {
+    if (c < cols) {
       float* dg = dg_part + (int64_t)blockIdx.x * cols + c;
 #pragma unroll
       for (int e = 0; e < 8; ++e) dg[e] = pg[i][e];
@@ -267,12 +281,15 @@ hipError_t launch_norm_bwd(bool ln, const uint16_t* dz, const uint16_t* x, const
   float* dg_part = part;
   float* db_part = part + (int64_t)nb * cols;
   if (rows > 0) {
-    if (ln)
-      hipLaunchKernelGGL(norm_bwd_kernel<true>, dim3(nb), dim3(kNormThreads), 0, s, dz, x, mu, rsigma, gamma, rows,
-                         cols, zc, dx, dg_part, db_part);
-    else
-      hipLaunchKernelGGL(norm_bwd_kernel<false>, dim3(nb), dim3(kNormThreads), 0, s, dz, x, mu, rsigma, gamma, rows,
-                         cols, zc, dx, dg_part, db_part);
+#define SGE_NORM_BWD(L, C)                                                                                      \
+  hipLaunchKernelGGL((norm_bwd_kernel<L, C>), dim3(nb), dim3(kNormThreads), 0, s, dz, x, mu, rsigma, gamma, rows, \
+                     cols, zc, dx, dg_part, db_part)
+    const int64_t nch = (cols / 8 + kNormThreads - 1) / kNormThreads;
+    if (nch <= 1) { if (ln) SGE_NORM_BWD(true, 1); else SGE_NORM_BWD(false, 1); }
+    else if (nch <= 2) { if (ln) SGE_NORM_BWD(true, 2); else SGE_NORM_BWD(false, 2); }
+    else if (nch <= 4) { if (ln) SGE_NORM_BWD(true, 4); else SGE_NORM_BWD(false, 4); }
+    else { if (ln) SGE_NORM_BWD(true, 8); else SGE_NORM_BWD(false, 8); }
+#undef SGE_NORM_BWD
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   } else {
