@@ -322,12 +322,18 @@ def build_grouped_fp8(torch, sge, X, W1, W2, DOUT, P, splits, offs, h, out, dh, 
     qw1, qw2 = qbuf(G * N1, H, G * N1), qbuf(G * H, F, G * H)
     W1f, W2f = W1.reshape(G * N1, H), W2.reshape(G * H, F)
 
-    def quant(src, b, layout):
-        return lambda: sge.quantize_fp8_grouped(src, G, *b["s"], qws, layout=layout, q=b["q"], q_t=b["q_t"])
+    amax_y = torch.empty(G, dtype=torch.float32, device="cuda")
+    amax_dh = torch.empty(G, dtype=torch.float32, device="cuda")
+
+    def quant(src, b, layout, amax_in=None):
+        return lambda: sge.quantize_fp8_grouped(src, G, *b["s"], qws, layout=layout, q=b["q"], q_t=b["q_t"],
+                                                amax_in=amax_in)
 
     sinv = lambda b: b["s"][2]   # noqa: E731
-    hbm = {"quant_x": T * H * 6, "quant_w1": G * N1 * H * 6, "quant_w2": G * H * F * 6, "quant_y": T * F * 6,
-           "quant_dout": T * H * 6, "quant_dh": T * N1 * 6}
+    # amax pass 2 B + quantize pass 2 B read, q and q_t 1 + 1 B written; y's and dh's amax come
+    # from fc1's and fc2's epilogues, so their quantize pass alone (4 B)
+    hbm = {"quant_x": T * H * 6, "quant_w1": G * N1 * H * 6, "quant_w2": G * H * F * 6, "quant_y": T * F * 4,
+           "quant_dout": T * H * 6, "quant_dh": T * N1 * 4}
     launches = [
         ("offsets", lambda: sge.splits_to_offsets(splits, [1, H], offs)),
         ("layout", lambda: sge.mx_group_layout(base, T, lay)),
@@ -335,16 +341,17 @@ def build_grouped_fp8(torch, sge, X, W1, W2, DOUT, P, splits, offs, h, out, dh, 
         ("quant_w1", quant(W1f, qw1, None)),
         ("quant_w2", quant(W2f, qw2, None)),
         ("fc1_fwd", lambda: sge.grouped_linear_fwd_fp8(qx["q"], sinv(qx), qw1["q"].view(G, N1, H), sinv(qw1), base,
-                                                       y, epilogue=sge.EPI_SCALED_SWIGLU, probs=P, preact=h)),
-        ("quant_y", quant(y, qy, lay)),
+                                                       y, epilogue=sge.EPI_SCALED_SWIGLU, probs=P, preact=h,
+                                                       out_amax=amax_y)),
+        ("quant_y", quant(y, qy, lay, amax_y)),
         ("fc2_fwd", lambda: sge.grouped_linear_fwd_fp8(qy["q"], sinv(qy), qw2["q"].view(G, H, F), sinv(qw2), base,
                                                        out)),
         ("quant_dout", quant(DOUT, qd, lay)),
         ("fc2_dgrad_dswiglu", lambda: sge.grouped_linear_dgrad_fp8(
             qd["q"], sinv(qd), qw2["q_t"], sinv(qw2), base, epilogue=sge.EPI_DSCALED_SWIGLU, preact=h, probs=P,
-            dact=dh, dprobs=dp, workspace=ws)),
+            dact=dh, dprobs=dp, dact_amax=amax_dh, workspace=ws)),
         ("fc2_wgrad", lambda: sge.grouped_linear_wgrad_fp8(qd["q_t"], sinv(qd), qy["q_t"], sinv(qy), lay, dw2)),
-        ("quant_dh", quant(dh, qdh, lay)),
+        ("quant_dh", quant(dh, qdh, lay, amax_dh)),
         ("fc1_dgrad", lambda: sge.grouped_linear_dgrad_fp8(qdh["q"], sinv(qdh), qw1["q_t"], sinv(qw1), base, dx=dx)),
         ("fc1_wgrad", lambda: sge.grouped_linear_wgrad_fp8(qdh["q_t"], sinv(qdh), qx["q_t"], sinv(qx), lay, dw1)),
     ]

@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define SGE_ABI_VERSION 3
+#define SGE_ABI_VERSION 4
 
 /* Alignment, in tokens, of each group's start in a token-blocked MXFP8 operand. */
 #define SGE_MX_TOKEN_ALIGN 128
@@ -357,32 +357,38 @@ sge_status sge_grouped_linear_wgrad_mxfp8(const void* dyT_q, const void* dyT_s, 
  *         pad[g] + t - c[g] and zeros up to pad[g+1] (ld_t % 128 == 0 and
  *         ld_t >= sge_mx_token_capacity(rows, G)); without, column r (ld_t >= rows, ld_t % 16 == 0).
  *   workspace: >= sge_quantize_fp8_grouped_workspace_size(G) bytes. Two kernels: a per-group
- *   amax (atomic max, order-free), then the quantize pass.
+ *   amax (atomic max, order-free), then the quantize pass. amax_in (device fp32 [G] or NULL):
+ *   the groups' amax already reduced by the producing epilogue (out_amax / dact_amax below);
+ *   then only the quantize pass runs (and the workspace may be NULL).
  * sge_grouped_linear_fwd_fp8: as sge_grouped_linear_fwd with x_q [T, K] u8 (x_sinv [G]: the
  *   scale_inv of each group's tokens) and w_q [G, N, K] u8 (w_sinv [G]: each expert's);
  *   h = fp32(x_sinv[g] * w_sinv[g]) * alpha * acc. K % 16 == 0, N % 8 == 0 (SwiGLU N % 256).
+ *   out_amax (SwiGLU only; device fp32 [G] or NULL): each group's amax of the bf16 output,
+ *   reduced in the epilogue (the amax a current-scaling quantize of it needs).
  * sge_grouped_linear_dgrad_fp8: as sge_grouped_linear_dgrad_mxfp8 with dy_q [T, N] u8
  *   (dy_sinv [G]) and w_qT [K][G*N] u8, the transpose of W viewed [G*N, K] (the q_t of
  *   sge_quantize_fp8_grouped without a layout; w_sinv [G]). N % 16 == 0, K % 8 == 0; the
- *   SwiGLU backward writes dact [T, 2K] and dprobs [T] (workspace as for sge_grouped_linear_bwd).
+ *   SwiGLU backward writes dact [T, 2K] and dprobs [T] (workspace as for sge_grouped_linear_bwd),
+ *   and, given dact_amax (device fp32 [G]), each group's amax of the bf16 dact.
  * sge_grouped_linear_wgrad_fp8: dW_g = fp32(dy_sinv[g] * x_sinv[g]) * alpha * sum_{t in g}
  *   dy[t]^T x[t] from dyT_q [N][ld] and xT_q [K][ld] (q_t with the layout), dw [G, N, K] bf16.
  */
 size_t sge_quantize_fp8_grouped_workspace_size(int32_t G);
 sge_status sge_quantize_fp8_grouped(const void* src, int64_t rows, int64_t cols, int32_t G,
                                     const int64_t* layout, int64_t ld_t, uint8_t* q, uint8_t* q_t,
-                                    float* amax, float* scale, float* scale_inv, void* workspace,
-                                    size_t workspace_bytes, hipStream_t stream);
+                                    float* amax, float* scale, float* scale_inv, const float* amax_in,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 sge_status sge_grouped_linear_fwd_fp8(const void* x_q, const float* x_sinv, const void* w_q,
                                       const float* w_sinv, int32_t G, int64_t T, int64_t N, int64_t K,
                                       const int64_t* offsets, float alpha, int32_t epilogue,
-                                      const float* probs, void* out, void* preact, hipStream_t stream);
+                                      const float* probs, void* out, void* preact, float* out_amax,
+                                      hipStream_t stream);
 sge_status sge_grouped_linear_dgrad_fp8(const void* dy_q, const float* dy_sinv, const void* w_qT,
                                         const float* w_sinv, int32_t G, int64_t T, int64_t N, int64_t K,
                                         const int64_t* offsets, float alpha, int32_t epilogue,
                                         const void* preact, const float* probs, void* dx, void* dact,
-                                        float* dprobs, void* workspace, size_t workspace_bytes,
-                                        hipStream_t stream);
+                                        float* dprobs, float* dact_amax, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
 sge_status sge_grouped_linear_wgrad_fp8(const void* dyT_q, const float* dy_sinv, const void* xT_q,
                                         const float* x_sinv, int32_t G, int64_t N, int64_t K,
                                         const int64_t* layout, int64_t ld, float alpha, void* dw,

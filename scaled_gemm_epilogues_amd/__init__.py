@@ -88,12 +88,12 @@ _SIGS = {
     "sge_grouped_linear_wgrad_mxfp8": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _f32, _vp, _vp],
                                        ctypes.c_int),
     "sge_quantize_fp8_grouped_workspace_size": ([_i32], _sz),
-    "sge_quantize_fp8_grouped": ([_vp, _i64, _i64, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "sge_quantize_fp8_grouped": ([_vp, _i64, _i64, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                                  ctypes.c_int),
     "sge_grouped_linear_fwd_fp8": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _vp, _vp, _vp,
-                                    _vp], ctypes.c_int),
+                                    _vp, _vp], ctypes.c_int),
     "sge_grouped_linear_dgrad_fp8": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _vp, _vp, _vp,
-                                      _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+                                      _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "sge_grouped_linear_wgrad_fp8": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _f32, _vp, _vp],
                                      ctypes.c_int),
     "sge_norm_fwd_workspace_size": ([_i64, _i64], _sz),
@@ -301,28 +301,32 @@ def quantize_fp8_grouped_workspace_size(G):
     return int(_lib.sge_quantize_fp8_grouped_workspace_size(int(G)))
 
 
-def quantize_fp8_grouped(src, G, amax, scale, scale_inv, workspace, layout=None, q=None, q_t=None, stream=None):
+def quantize_fp8_grouped(src, G, amax, scale, scale_inv, workspace=None, layout=None, q=None, q_t=None,
+                         amax_in=None, stream=None):
     """Per-group FP8 current scaling of bf16 ``src`` [rows, cols]: groups from ``layout`` [2, G+1]
-    or, without one, G equal runs of rows. q [rows, cols] and/or q_t [cols, ld_t]."""
+    or, without one, G equal runs of rows. q [rows, cols] and/or q_t [cols, ld_t]. ``amax_in``: the
+    groups' amax reduced by the producing epilogue (skips the amax pass)."""
     rows, cols = src.shape
     ld_t = 0 if q_t is None else q_t.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.sge_quantize_fp8_grouped(_ptr(src), rows, cols, int(G), _ptr(layout), ld_t, _ptr(q), _ptr(q_t),
-                                         _ptr(amax), _ptr(scale), _ptr(scale_inv), _ptr(workspace),
-                                         workspace.numel() * workspace.element_size(), _stream(stream)))
+                                         _ptr(amax), _ptr(scale), _ptr(scale_inv), _ptr(amax_in), _ptr(workspace),
+                                         ws_bytes, _stream(stream)))
 
 
 def grouped_linear_fwd_fp8(x_q, x_sinv, w_q, w_sinv, offsets, out, alpha=1.0, epilogue=EPI_NONE, probs=None,
-                           preact=None, stream=None):
+                           preact=None, out_amax=None, stream=None):
     """Grouped forward on E4M3 operands with one scale_inv per group: x_q [T, K], w_q [G, N, K]."""
     G, N, K = w_q.shape
     T = x_q.shape[0]
     _check(_lib.sge_grouped_linear_fwd_fp8(_ptr(x_q), _ptr(x_sinv), _ptr(w_q), _ptr(w_sinv), G, T, N, K,
                                            _ptr(offsets), float(alpha), epilogue, _ptr(probs), _ptr(out),
-                                           _ptr(preact), _stream(stream)))
+                                           _ptr(preact), _ptr(out_amax), _stream(stream)))
 
 
 def grouped_linear_dgrad_fp8(dy_q, dy_sinv, w_qT, w_sinv, offsets, alpha=1.0, epilogue=EPI_NONE, preact=None,
-                             probs=None, dx=None, dact=None, dprobs=None, workspace=None, stream=None):
+                             probs=None, dx=None, dact=None, dprobs=None, dact_amax=None, workspace=None,
+                             stream=None):
     """E4M3 grouped dgrad: dy_q [T, N], w_qT [K, G*N] (transpose of W viewed [G*N, K])."""
     T, N = dy_q.shape
     K = w_qT.shape[0]
@@ -330,8 +334,8 @@ def grouped_linear_dgrad_fp8(dy_q, dy_sinv, w_qT, w_sinv, offsets, alpha=1.0, ep
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.sge_grouped_linear_dgrad_fp8(_ptr(dy_q), _ptr(dy_sinv), _ptr(w_qT), _ptr(w_sinv), G, T, N, K,
                                              _ptr(offsets), float(alpha), epilogue, _ptr(preact), _ptr(probs),
-                                             _ptr(dx), _ptr(dact), _ptr(dprobs), _ptr(workspace), ws_bytes,
-                                             _stream(stream)))
+                                             _ptr(dx), _ptr(dact), _ptr(dprobs), _ptr(dact_amax), _ptr(workspace),
+                                             ws_bytes, _stream(stream)))
 
 
 def grouped_linear_wgrad_fp8(dyT_q, dy_sinv, xT_q, x_sinv, layout, dw, alpha=1.0, stream=None):

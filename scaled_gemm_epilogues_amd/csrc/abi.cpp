@@ -683,7 +683,8 @@ size_t sge_quantize_fp8_grouped_workspace_size(int32_t G) {
 
 sge_status sge_quantize_fp8_grouped(const void* src, int64_t rows, int64_t cols, int32_t G, const int64_t* layout,
                                     int64_t ld_t, uint8_t* q, uint8_t* q_t, float* amax, float* scale,
-                                    float* scale_inv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                                    float* scale_inv, const float* amax_in, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
   if (rows < 0 || cols < 0) return fail(SGE_ERR_SHAPE, "quantize_fp8_grouped: negative size");
   if (G < 1 || G > 4096) return fail(SGE_ERR_ARG, "quantize_fp8_grouped: G=%d outside [1, 4096]", G);
   if (!amax || !scale || !scale_inv) return fail(SGE_ERR_NULL, "quantize_fp8_grouped: amax, scale and scale_inv are required");
@@ -704,15 +705,16 @@ sge_status sge_quantize_fp8_grouped(const void* src, int64_t rows, int64_t cols,
   }
   if ((src && !aligned16(src)) || (q && !aligned16(q)) || (q_t && !aligned16(q_t)))
     return fail(SGE_ERR_ALIGN, "quantize_fp8_grouped: pointers must be 16-byte aligned");
-  const size_t need = sge_quantize_fp8_grouped_workspace_size(G);
-  if (!workspace || workspace_bytes < need)
+  const size_t need = amax_in ? 0 : sge_quantize_fp8_grouped_workspace_size(G);
+  if (need && (!workspace || workspace_bytes < need))
     return fail(SGE_ERR_WORKSPACE, "quantize_fp8_grouped: workspace %zu < %zu bytes", workspace_bytes, need);
-  const Range in[2] = {range_of(src, rows, cols, cols, 2),
-                       layout ? Range{(uintptr_t)layout, (uintptr_t)(layout + 2 * (G + 1))} : Range{0, 0}};
+  const Range in[3] = {range_of(src, rows, cols, cols, 2),
+                       layout ? Range{(uintptr_t)layout, (uintptr_t)(layout + 2 * (G + 1))} : Range{0, 0},
+                       amax_in ? range_of(amax_in, 1, G, G, 4) : Range{0, 0}};
   const Range outs[6] = {q ? range_of(q, rows, cols, cols, 1) : Range{0, 0},
                          q_t ? range_of(q_t, cols, ld_t, ld_t, 1) : Range{0, 0},
                          range_of(amax, 1, G, G, 4), range_of(scale, 1, G, G, 4), range_of(scale_inv, 1, G, G, 4),
-                         range_of(workspace, 1, G, G, 4)};
+                         need ? range_of(workspace, 1, G, G, 4) : Range{0, 0}};
   for (int a = 0; a < 6; ++a) {
     for (const Range& i : in)
       if (overlap(outs[a], i)) return fail(SGE_ERR_ALIAS, "quantize_fp8_grouped: an output overlaps an input");
@@ -720,14 +722,14 @@ sge_status sge_quantize_fp8_grouped(const void* src, int64_t rows, int64_t cols,
       if (overlap(outs[a], outs[b])) return fail(SGE_ERR_ALIAS, "quantize_fp8_grouped: outputs overlap");
   }
   return hip_status(sge::launch_quantize_fp8_grouped(static_cast<const uint16_t*>(src), rows, cols, G, layout, npos,
-                                                     static_cast<uint32_t*>(workspace), q, q_t, amax, scale,
+                                                     static_cast<float*>(workspace), amax_in, q, q_t, amax, scale,
                                                      scale_inv, stream),
                     "quantize_fp8_grouped launch");
 }
 
 sge_status sge_grouped_linear_fwd_fp8(const void* x_q, const float* x_sinv, const void* w_q, const float* w_sinv,
                                       int32_t G, int64_t T, int64_t N, int64_t K, const int64_t* offsets, float alpha,
-                                      int32_t epilogue, const float* probs, void* out, void* preact,
+                                      int32_t epilogue, const float* probs, void* out, void* preact, float* out_amax,
                                       hipStream_t stream) {
   if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_fp8: bad sizes");
   if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_SCALED_SWIGLU)
@@ -735,6 +737,7 @@ sge_status sge_grouped_linear_fwd_fp8(const void* x_q, const float* x_sinv, cons
   const bool swiglu = epilogue == SGE_EPI_SCALED_SWIGLU;
   if (!x_q || !x_sinv || !w_q || !w_sinv || !offsets || !out) return fail(SGE_ERR_NULL, "grouped_linear_fwd_fp8: NULL pointer");
   if (swiglu && !probs) return fail(SGE_ERR_NULL, "grouped_linear_fwd_fp8: probs is NULL");
+  if (out_amax && !swiglu) return fail(SGE_ERR_ARG, "grouped_linear_fwd_fp8: out_amax needs the SwiGLU epilogue");
   if (K % 16) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_fp8: K must be a multiple of 16");
   if (N % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_fp8: N must be a multiple of 8");
   if (swiglu && N % 256) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_fp8: SwiGLU needs N %% 256 == 0");
@@ -742,11 +745,17 @@ sge_status sge_grouped_linear_fwd_fp8(const void* x_q, const float* x_sinv, cons
     return fail(SGE_ERR_ALIGN, "grouped_linear_fwd_fp8: pointers must be 16-byte aligned");
   const int64_t out_cols = swiglu ? N / 2 : N;
   const Range in[2] = {range_of(x_q, T, K, K, 1), range_of(w_q, (int64_t)G * N, K, K, 1)};
-  const Range outs[2] = {range_of(out, T, out_cols, out_cols, 2), preact ? range_of(preact, T, N, N, 2) : Range{0, 0}};
+  const Range outs[3] = {range_of(out, T, out_cols, out_cols, 2), preact ? range_of(preact, T, N, N, 2) : Range{0, 0},
+                         out_amax ? range_of(out_amax, 1, G, G, 4) : Range{0, 0}};
   for (const Range& o : outs)
     for (const Range& i : in)
       if (overlap(o, i)) return fail(SGE_ERR_ALIAS, "grouped_linear_fwd_fp8: outputs overlap inputs");
-  if (overlap(outs[0], outs[1])) return fail(SGE_ERR_ALIAS, "grouped_linear_fwd_fp8: outputs overlap");
+  if (overlap(outs[0], outs[1]) || overlap(outs[0], outs[2]) || overlap(outs[1], outs[2]))
+    return fail(SGE_ERR_ALIAS, "grouped_linear_fwd_fp8: outputs overlap");
+  if (out_amax) {
+    const hipError_t z = sge::launch_fill_f32_zero(out_amax, G, stream);
+    if (z != hipSuccess) return hip_status(z, "amax fill");
+  }
   if (T == 0 || N == 0) return ok();
   sge::GemmParams p;
   memset(&p, 0, sizeof(p));
@@ -771,14 +780,15 @@ sge_status sge_grouped_linear_fwd_fp8(const void* x_q, const float* x_sinv, cons
   p.aux = static_cast<uint16_t*>(preact);
   p.ld_aux = N;
   p.F = N / 2;
+  p.amax_out = out_amax;
   return hip_status(sge::launch_grouped_fwd_fp8(p, epilogue, stream), "grouped fwd fp8 launch");
 }
 
 sge_status sge_grouped_linear_dgrad_fp8(const void* dy_q, const float* dy_sinv, const void* w_qT, const float* w_sinv,
                                         int32_t G, int64_t T, int64_t N, int64_t K, const int64_t* offsets,
                                         float alpha, int32_t epilogue, const void* preact, const float* probs,
-                                        void* dx, void* dact, float* dprobs, void* workspace, size_t workspace_bytes,
-                                        hipStream_t stream) {
+                                        void* dx, void* dact, float* dprobs, float* dact_amax, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
   if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_fp8: bad sizes");
   if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_DSCALED_SWIGLU)
     return fail(SGE_ERR_ARG, "grouped_linear_dgrad_fp8: epilogue %d not allowed", epilogue);
@@ -787,6 +797,7 @@ sge_status sge_grouped_linear_dgrad_fp8(const void* dy_q, const float* dy_sinv, 
   if (swiglu && (!preact || !probs || !dact || !dprobs))
     return fail(SGE_ERR_NULL, "grouped_linear_dgrad_fp8: SwiGLU backward needs preact, probs, dact and dprobs");
   if (!swiglu && !dx) return fail(SGE_ERR_NULL, "grouped_linear_dgrad_fp8: dx is NULL");
+  if (dact_amax && !swiglu) return fail(SGE_ERR_ARG, "grouped_linear_dgrad_fp8: dact_amax needs the SwiGLU backward");
   if (N % 16) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_fp8: N must be a multiple of 16");
   if (K % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_fp8: K must be a multiple of 8");
   if (!aligned16(dy_q) || !aligned16(w_qT) || (dx && !aligned16(dx)) || (preact && !aligned16(preact)) ||
@@ -796,11 +807,17 @@ sge_status sge_grouped_linear_dgrad_fp8(const void* dy_q, const float* dy_sinv, 
   const Range in[3] = {range_of(dy_q, T, N, N, 1), range_of(w_qT, K, GN, GN, 1),
                        swiglu ? range_of(preact, T, 2 * K, 2 * K, 2) : Range{0, 0}};
   const Range out = swiglu ? range_of(dact, T, 2 * K, 2 * K, 2) : range_of(dx, T, K, K, 2);
+  const Range ram = dact_amax ? range_of(dact_amax, 1, G, G, 4) : Range{0, 0};
   for (const Range& i : in)
-    if (overlap(out, i)) return fail(SGE_ERR_ALIAS, "grouped_linear_dgrad_fp8: output overlaps an input");
+    if (overlap(out, i) || overlap(ram, i)) return fail(SGE_ERR_ALIAS, "grouped_linear_dgrad_fp8: output overlaps an input");
+  if (overlap(out, ram)) return fail(SGE_ERR_ALIAS, "grouped_linear_dgrad_fp8: outputs overlap");
   const size_t need = sge_grouped_linear_bwd_workspace_size(T, K, G, epilogue);
   if (need && (!workspace || workspace_bytes < need))
     return fail(SGE_ERR_WORKSPACE, "grouped_linear_dgrad_fp8: workspace %zu < %zu bytes", workspace_bytes, need);
+  if (dact_amax) {
+    const hipError_t z = sge::launch_fill_f32_zero(dact_amax, G, stream);
+    if (z != hipSuccess) return hip_status(z, "amax fill");
+  }
   if (T == 0 || K == 0) return ok();
   sge::GemmParams p;
   memset(&p, 0, sizeof(p));
@@ -829,6 +846,7 @@ sge_status sge_grouped_linear_dgrad_fp8(const void* dy_q, const float* dy_sinv, 
     p.ld_aux_out = 2 * K;
     p.dp_part = static_cast<float*>(workspace);
     p.F = K;
+    p.amax_out = dact_amax;
   }
   hipError_t e = sge::launch_grouped_dgrad_fp8(p, epilogue, stream);
   if (e != hipSuccess) return hip_status(e, "grouped dgrad fp8 launch");

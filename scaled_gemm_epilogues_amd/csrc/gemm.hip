@@ -89,6 +89,20 @@ __device__ __forceinline__ float fast_sigmoid(float a) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-a));
 }
 
+// Per-group amax of an epilogue's bf16 output: each wave folds the max of its fp32 values
+// (before their bf16 rounding: rounding is monotone, so the rounded max is the max of the
+// stored values) into a workgroup LDS slot, as bf16 bits << 16, i.e. the value as fp32;
+// non-negative floats order like their bit patterns. One global atomic per workgroup.
+__device__ __forceinline__ void amax_to_slot(uint32_t* slot, float m) {
+  uint32_t b = (uint32_t)f32_to_bf16(m) << 16;
+  b = wave_max(b);
+  if ((threadIdx.x & 63) == 0 && b) atomicMax(slot, b);
+}
+__device__ __forceinline__ void slot_to_group(uint32_t* slot, float* amax, int g) {
+  __syncthreads();
+  if (threadIdx.x == 0 && *slot) atomicMax(reinterpret_cast<uint32_t*>(amax) + g, *slot);
+}
+
 
 typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 
@@ -243,6 +257,7 @@ void gemm_kernel(const GemmParams p) {
   constexpr int kScaleTiles = 4;
   constexpr int SC_BYTES = FMT == F_MX ? (BM + BN) * 4 * kScaleTiles : 16;
   __shared__ __attribute__((aligned(16))) uint8_t sc_lds[2][SC_BYTES];
+  __shared__ uint32_t amax_slot;                         // FP8 (d)SwiGLU epilogues: the tile's amax
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -693,6 +708,9 @@ void gemm_kernel(const GemmParams p) {
     constexpr int kIters = 128 * kChunks / (NWAVES * 64);
     auto wsw = [](int w) { return (w & 1) | ((w & 2) << 2); };
     float* stage = reinterpret_cast<float*>(wm ? lds1 : lds0);
+    constexpr bool kAmax = FMT == F_E4M3;                  // per-group amax of y (FP8 current scaling)
+    float amax_acc = 0.0f;                                 // max |y| (masked lanes hold 0)
+    if (kAmax && threadIdx.x == 0) amax_slot = 0;
     __syncthreads();                                       // every wave is done with the LDS stages
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
@@ -754,6 +772,10 @@ void gemm_kernel(const GemmParams p) {
         __builtin_amdgcn_raw_buffer_store_b128(va, rha, oh[it], 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(vb, rhb, oh[it], 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(vy, ry, oy[it], 0, 0);
+        if constexpr (kAmax) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) amax_acc = fmaxf(amax_acc, fabsf(y[e]));
+        }
         if (mxq) {
           int e8;
           const v2i qv = mx_quant_lane8(vy, e8);
@@ -762,6 +784,12 @@ void gemm_kernel(const GemmParams p) {
         }
       }
       if (pass == 0) __syncthreads();                      // stage reused by the second pass
+    }
+    if constexpr (kAmax) {
+      if (p.amax_out) {
+        amax_to_slot(&amax_slot, amax_acc);
+        slot_to_group(&amax_slot, p.amax_out, grp);
+      }
     }
   } else {  // E_DSWIGLU
     // Staged like E_STORE: g = alpha*acc for half of each wave's rows goes to LDS, then each
@@ -782,6 +810,9 @@ void gemm_kernel(const GemmParams p) {
     // straddle the da / db halves as F % 32 == 0), the bytes the standalone quantizer writes
     // for the bf16 dact. Its row stride ld_q equals ld_aux_out, so byte offsets are od / 2.
     const bool mxq = p.q_out != nullptr;
+    constexpr bool kAmax = FMT == F_E4M3;                  // per-group amax of dh (FP8 current scaling)
+    const bool want_amax = kAmax && p.amax_out != nullptr;
+    if (want_amax && threadIdx.x == 0) amax_slot = 0;       // before the epilogue's first barrier
     const int64_t qbytes = mxq ? rows_left * p.ld_q : 0, sbytes = mxq ? rows_left * (p.ld_q / 32) : 0;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(mxq ? p.q_out + m0 * p.ld_q : p.q_out, qbytes);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(mxq ? p.s_out + m0 * (p.ld_q / 32) : p.s_out, sbytes);
@@ -863,6 +894,14 @@ void gemm_kernel(const GemmParams p) {
                         (int)pack_bf16x2(db[4], db[5]), (int)pack_bf16x2(db[6], db[7])};
         __builtin_amdgcn_raw_buffer_store_b128(va, rd, od[ib], 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(vb, rd, od[ib] + fb, 0, 0);
+        if constexpr (kAmax) {
+          if (want_amax) {                                 // per item: no register lives across items
+            float mi = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mi = fmaxf(mi, fmaxf(fabsf(da[e]), fabsf(db[e])));
+            amax_to_slot(&amax_slot, mi);
+          }
+        }
         if (mxq) {
           int ea, eb;
           const v2i qa = mx_quant_lane8(va, ea), qb = mx_quant_lane8(vb, eb);
@@ -881,6 +920,9 @@ void gemm_kernel(const GemmParams p) {
       }
       }
       if (pass == 0) __syncthreads();                      // stage reused by the second pass
+    }
+    if constexpr (kAmax) {
+      if (want_amax) slot_to_group(&amax_slot, p.amax_out, grp);
     }
   }
 }

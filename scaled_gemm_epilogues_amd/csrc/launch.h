@@ -45,6 +45,7 @@ struct GemmParams {
   int64_t ld_q;
   int64_t b_mx_bytes;         // MXFP8: bytes of B's whole scale array from b_mx (0: rows x ld)
   int sinv_per_group;         // E4M3 grouped: a_sinv / b_sinv are [G], indexed by the group
+  float* amax_out;            // (d)SwiGLU: per-group amax of the bf16 output, atomic max (zeroed by the caller)
 };
 
 hipError_t launch_gemm(const GemmParams& p, int fmt, bool a_kmaj, bool b_kmaj, hipStream_t s);
@@ -80,8 +81,9 @@ hipError_t launch_quantize_mxfp8_grouped(const uint16_t* src, int64_t rows, int6
                                          uint8_t* q_colT, uint8_t* s_colT, hipStream_t s);
 // FP8 current scaling with one scale per group (layout NULL: G equal runs of rows / G rows).
 hipError_t launch_quantize_fp8_grouped(const uint16_t* src, int64_t rows, int64_t cols, int G,
-                                       const int64_t* layout, int64_t ld_t, uint32_t* amax_bits, uint8_t* q,
-                                       uint8_t* q_t, float* amax, float* scale, float* scale_inv, hipStream_t s);
+                                       const int64_t* layout, int64_t ld_t, float* amax_ws, const float* amax_in,
+                                       uint8_t* q, uint8_t* q_t, float* amax, float* scale, float* scale_inv,
+                                       hipStream_t s);
 hipError_t launch_mx_group_layout(const int64_t* offsets, int G, int64_t T, int64_t align, int64_t* layout,
                                   hipStream_t s);
 

@@ -360,7 +360,7 @@ constexpr int kGAC = 512;
 
 __global__ __launch_bounds__(256) void amax_grouped_kernel(const uint16_t* __restrict__ src, int64_t rows,
                                                           int64_t cols, int G, const int64_t* __restrict__ layout,
-                                                          uint32_t* __restrict__ amax_bits) {
+                                                          float* __restrict__ amax_g) {
   __shared__ uint32_t red[4];
   const int64_t tc = (cols + kGAC - 1) / kGAC;
   const int64_t p0 = (int64_t)(blockIdx.x / tc) * kQR;
@@ -381,18 +381,19 @@ __global__ __launch_bounds__(256) void amax_grouped_kernel(const uint16_t* __res
     }
   }
   m = block_max_u32(m, red);
-  if (t == 0 && m) atomicMax(amax_bits + g, m);
+  // non-negative floats order like their bit patterns: an integer max of (bf16 bits << 16)
+  if (t == 0 && m) atomicMax(reinterpret_cast<uint32_t*>(amax_g) + g, m << 16);
 }
 
 __global__ __launch_bounds__(256) void quantize_fp8_grouped_kernel(
     const uint16_t* __restrict__ src, int64_t rows, int64_t cols, int G, const int64_t* __restrict__ layout,
-    int64_t ld_t, const uint32_t* __restrict__ amax_bits, uint8_t* __restrict__ q, uint8_t* __restrict__ q_t,
+    int64_t ld_t, const float* __restrict__ amax_g, uint8_t* __restrict__ q, uint8_t* __restrict__ q_t,
     float* amax_out, float* scale_out, float* scale_inv_out) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kQC][kQR + 16];   // [column][position]
   const int t = threadIdx.x;
   if (blockIdx.x == 0) {
     for (int gg = t; gg < G; gg += blockDim.x) {
-      const float a = __builtin_bit_cast(float, amax_bits[gg] << 16);
+      const float a = amax_g[gg];
       float sc, si;
       fp8_scales(a, sc, si);
       amax_out[gg] = a;
@@ -407,7 +408,7 @@ __global__ __launch_bounds__(256) void quantize_fp8_grouped_kernel(
   int64_t r0, nrows;
   if (!group_tile(layout, G, rows, p0, g, r0, nrows)) return;   // block-uniform
   float scale, scale_inv;
-  fp8_scales(__builtin_bit_cast(float, amax_bits[g] << 16), scale, scale_inv);
+  fp8_scales(amax_g[g], scale, scale_inv);
   const int cchunk = t & 7;
   const int rsub = t >> 3;
 #pragma unroll
@@ -447,21 +448,26 @@ __global__ __launch_bounds__(256) void quantize_fp8_grouped_kernel(
 }
 
 hipError_t launch_quantize_fp8_grouped(const uint16_t* src, int64_t rows, int64_t cols, int G,
-                                       const int64_t* layout, int64_t ld_t, uint32_t* amax_bits, uint8_t* q,
-                                       uint8_t* q_t, float* amax, float* scale, float* scale_inv, hipStream_t s) {
-  hipError_t e = launch_fill_f32_zero(reinterpret_cast<float*>(amax_bits), G, s);   // +0.0f is all-zero bits
-  if (e != hipSuccess) return e;
+                                       const int64_t* layout, int64_t ld_t, float* amax_ws, const float* amax_in,
+                                       uint8_t* q, uint8_t* q_t, float* amax, float* scale, float* scale_inv,
+                                       hipStream_t s) {
   const int64_t npos = layout ? ld_t : rows;            // positions the tiles walk (a bound of the last group's end)
-  const int64_t ta = (npos / kQR) * ((cols + kGAC - 1) / kGAC);
-  if (ta > 0) {
-    hipLaunchKernelGGL(amax_grouped_kernel, dim3((unsigned)ta), dim3(256), 0, s, src, rows, cols, G, layout,
-                       amax_bits);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  const float* amax_g = amax_in;
+  if (!amax_in) {                                       // the amax pass (skipped when the producer reduced it)
+    if ((e = launch_fill_f32_zero(amax_ws, G, s)) != hipSuccess) return e;
+    const int64_t ta = (npos / kQR) * ((cols + kGAC - 1) / kGAC);
+    if (ta > 0) {
+      hipLaunchKernelGGL(amax_grouped_kernel, dim3((unsigned)ta), dim3(256), 0, s, src, rows, cols, G, layout,
+                         amax_ws);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    amax_g = amax_ws;
   }
   int64_t tq = (npos / kQR) * ((cols + kQC - 1) / kQC);
   if (tq < 1) tq = 1;                                   // block 0 still writes every group's scales
   hipLaunchKernelGGL(quantize_fp8_grouped_kernel, dim3((unsigned)tq), dim3(256), 0, s, src, rows, cols, G, layout,
-                     ld_t, amax_bits, q, q_t, amax, scale, scale_inv);
+                     ld_t, amax_g, q, q_t, amax, scale, scale_inv);
   return hipGetLastError();
 }
 

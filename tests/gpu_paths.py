@@ -249,9 +249,10 @@ def run_grouped_mlp_bwd_mx(inp, fwd):
 
 
 # ------------------------------------------- FP8 current scaling per group
-def quant_fp8_grouped(t, G, lay=None, row=True, col=True, fill=None):
+def quant_fp8_grouped(t, G, lay=None, row=True, col=True, fill=None, amax_in=None):
     """Per-group FP8 current scaling of device bf16 ``t`` [rows, C]: groups from ``lay`` or G
-    equal runs of rows. Returns q [rows, C], q_t [C, ld] and the per-group amax / scale / scale_inv."""
+    equal runs of rows (``amax_in``: the groups' amax from the producing epilogue). Returns
+    q [rows, C], q_t [C, ld] and the per-group amax / scale / scale_inv."""
     rows, C = t.shape
     ld = sge.mx_token_capacity(rows, G) if lay is not None else rows
     f32 = dict(dtype=torch.float32, device="cuda")
@@ -263,7 +264,7 @@ def quant_fp8_grouped(t, G, lay=None, row=True, col=True, fill=None):
     out["q_t"] = mk(C, ld) if col else None
     ws = torch.empty(max(16, sge.quantize_fp8_grouped_workspace_size(G)), dtype=torch.uint8, device="cuda")
     sge.quantize_fp8_grouped(t, G, out["amax"], out["scale"], out["scale_inv"], ws, layout=lay, q=out["q"],
-                             q_t=out["q_t"])
+                             q_t=out["q_t"], amax_in=amax_in)
     return out
 
 
@@ -285,22 +286,28 @@ def run_grouped_mlp_fp8(inp):
     qw1 = quant_fp8_grouped(W1.reshape(G * N1, H), G)
     qw2 = quant_fp8_grouped(W2.reshape(G * H, F), G)
     h, y, out = torch.empty(T, N1, **bf), torch.empty(T, F, **bf), torch.empty(T, H, **bf)
+    amax_y = torch.empty(G, dtype=torch.float32, device="cuda")
     sge.grouped_linear_fwd_fp8(qx["q"], qx["scale_inv"], qw1["q"].view(G, N1, H), qw1["scale_inv"], base, y,
-                               epilogue=sge.EPI_SCALED_SWIGLU, probs=P, preact=h)
-    qy = quant_fp8_grouped(y, G, lay)
+                               epilogue=sge.EPI_SCALED_SWIGLU, probs=P, preact=h, out_amax=amax_y)
+    qy = quant_fp8_grouped(y, G, lay, amax_in=amax_y)            # the amax fused into fc1's epilogue
     sge.grouped_linear_fwd_fp8(qy["q"], qy["scale_inv"], qw2["q"].view(G, H, F), qw2["scale_inv"], base, out)
     qd = quant_fp8_grouped(DOUT, G, lay)
     dh, dp = torch.empty(T, N1, **bf), torch.empty(T, dtype=torch.float32, device="cuda")
+    amax_dh = torch.empty(G, dtype=torch.float32, device="cuda")
     ws = torch.empty(max(1, sge.grouped_linear_bwd_workspace_size(T, F, G, sge.EPI_DSCALED_SWIGLU)),
                      dtype=torch.uint8, device="cuda")
     sge.grouped_linear_dgrad_fp8(qd["q"], qd["scale_inv"], qw2["q_t"], qw2["scale_inv"], base,
-                                 epilogue=sge.EPI_DSCALED_SWIGLU, preact=h, probs=P, dact=dh, dprobs=dp, workspace=ws)
+                                 epilogue=sge.EPI_DSCALED_SWIGLU, preact=h, probs=P, dact=dh, dprobs=dp,
+                                 dact_amax=amax_dh, workspace=ws)
     dw2 = torch.empty(G, H, F, **bf)
     sge.grouped_linear_wgrad_fp8(qd["q_t"], qd["scale_inv"], qy["q_t"], qy["scale_inv"], lay, dw2)
-    qdh = quant_fp8_grouped(dh, G, lay)
+    qdh = quant_fp8_grouped(dh, G, lay, amax_in=amax_dh)        # the amax fused into fc2's dgrad epilogue
     dx, dw1 = torch.empty(T, H, **bf), torch.empty(G, N1, H, **bf)
     sge.grouped_linear_dgrad_fp8(qdh["q"], qdh["scale_inv"], qw1["q_t"], qw1["scale_inv"], base, dx=dx)
     sge.grouped_linear_wgrad_fp8(qdh["q_t"], qdh["scale_inv"], qx["q_t"], qx["scale_inv"], lay, dw1)
+    # the standalone quantizer (its own amax pass) on the same bf16 y and dh
+    qy_alone, qdh_alone = quant_fp8_grouped(y, G, lay), quant_fp8_grouped(dh, G, lay)
     torch.cuda.synchronize()
     return {"base": base, "lay": lay, "qx": qx, "qw1": qw1, "qw2": qw2, "qy": qy, "qd": qd, "qdh": qdh, "h": h,
-            "y": y, "out": out, "dh": dh, "dp": dp, "dw2": dw2, "dx": dx, "dw1": dw1}
+            "y": y, "out": out, "dh": dh, "dp": dp, "dw2": dw2, "dx": dx, "dw1": dw1, "qy_alone": qy_alone,
+            "qdh_alone": qdh_alone}

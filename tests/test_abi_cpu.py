@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol(sge):
     lib = ctypes.CDLL(sge.library_path())
     for name in _declared():
         assert hasattr(lib, name), name
-    assert sge.abi_version() == 3
+    assert sge.abi_version() == 4
 
 
 def test_status_strings(sge):
@@ -264,7 +264,7 @@ def test_fp8_grouped_validation_errors(sge):
     rows, C, G = 100, 64, 4
     ld = sge.mx_token_capacity(rows, G)
     ws = sge.quantize_fp8_grouped_workspace_size(G)
-    ok = [B(1), rows, C, G, B(2), ld, B(3), B(4), B(5), B(6), B(7), B(8), ws, None]
+    ok = [B(1), rows, C, G, B(2), ld, B(3), B(4), B(5), B(6), B(7), None, B(8), ws, None]
     a = list(ok); a[8] = None
     assert q(*a) == sge.ERR_NULL                                          # amax required
     a = list(ok); a[6] = None; a[7] = None
@@ -279,16 +279,20 @@ def test_fp8_grouped_validation_errors(sge):
     assert q(*a) == sge.ERR_SHAPE                                         # ld_t % 16 without a layout
     a = list(ok); a[6] = B(6) + 4
     assert q(*a) == sge.ERR_ALIGN
-    a = list(ok); a[12] = ws - 1
+    a = list(ok); a[13] = ws - 1
     assert q(*a) == sge.ERR_WORKSPACE
+    a = list(ok); a[11] = B(9); a[12] = None; a[13] = 0; a[2] = 40
+    assert q(*a) == sge.ERR_SHAPE                                         # no workspace needed with amax_in
     a = list(ok); a[7] = B(1)
     assert q(*a) == sge.ERR_ALIAS                                         # q_t over src
-    a = list(ok); a[10] = B(8)
+    a = list(ok); a[10] = B(6)
     assert q(*a) == sge.ERR_ALIAS                                         # scale_inv over scale
+    a = list(ok); a[11] = B(9); a[8] = B(9)
+    assert q(*a) == sge.ERR_ALIAS                                         # amax output over amax_in
 
     f = sge._lib.sge_grouped_linear_fwd_fp8
     G, T, N, K = 4, 100, 512, 256
-    ok = [B(1), B(2), B(3), B(4), G, T, N, K, B(5), 1.0, sge.EPI_SCALED_SWIGLU, B(6), B(7), B(8), None]
+    ok = [B(1), B(2), B(3), B(4), G, T, N, K, B(5), 1.0, sge.EPI_SCALED_SWIGLU, B(6), B(7), B(8), None, None]
     a = list(ok); a[1] = None
     assert f(*a) == sge.ERR_NULL                                          # x_sinv
     a = list(ok); a[11] = None
@@ -299,11 +303,15 @@ def test_fp8_grouped_validation_errors(sge):
     assert f(*a) == sge.ERR_SHAPE                                         # SwiGLU N % 256
     a = list(ok); a[12] = B(1)
     assert f(*a) == sge.ERR_ALIAS                                         # out over x_q
+    a = list(ok); a[10] = sge.EPI_NONE; a[14] = B(9)
+    assert f(*a) == sge.ERR_ARG                                           # out_amax needs SwiGLU
+    a = list(ok); a[14] = B(7)
+    assert f(*a) == sge.ERR_ALIAS                                         # out_amax over out
 
     d = sge._lib.sge_grouped_linear_dgrad_fp8
     sw = sge.EPI_DSCALED_SWIGLU
     wsb = sge.grouped_linear_bwd_workspace_size(T, K, G, sw)
-    ok = [B(1), B(2), B(3), B(4), G, T, N, K, B(5), 1.0, sw, B(6), B(7), None, B(8), B(9), B(10), wsb, None]
+    ok = [B(1), B(2), B(3), B(4), G, T, N, K, B(5), 1.0, sw, B(6), B(7), None, B(8), B(9), None, B(10), wsb, None]
     a = list(ok); a[14] = None
     assert d(*a) == sge.ERR_NULL                                          # SwiGLU needs dact
     a = list(ok); a[10] = sge.EPI_NONE
@@ -312,8 +320,10 @@ def test_fp8_grouped_validation_errors(sge):
     assert d(*a) == sge.ERR_SHAPE                                         # N % 16
     a = list(ok); a[14] = B(6)
     assert d(*a) == sge.ERR_ALIAS                                         # dact over preact
-    a = list(ok); a[17] = wsb - 4
+    a = list(ok); a[18] = wsb - 4
     assert d(*a) == sge.ERR_WORKSPACE
+    a = list(ok); a[10] = sge.EPI_NONE; a[13] = B(11); a[16] = B(12)
+    assert d(*a) == sge.ERR_ARG                                           # dact_amax needs the SwiGLU backward
 
     w = sge._lib.sge_grouped_linear_wgrad_fp8
     ok = [B(1), B(2), B(3), B(4), G, N, K, B(5), 640, 1.0, B(6), None]

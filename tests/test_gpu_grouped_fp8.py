@@ -126,6 +126,13 @@ def test_fp8_grouped_mlp_fwd_bwd(case):
     base = offsets.base_offsets(inp["splits"])
     fwd = grouped.grouped_mlp_fwd_fp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base)
     bwd = grouped.grouped_mlp_bwd_fp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base, inp["dout"], fwd=fwd)
+    # the amax fused into the epilogues == the quantizer's own amax pass: identical bytes
+    for fused, alone in (("qy", "qy_alone"), ("qdh", "qdh_alone")):
+        for k in ("amax", "scale", "scale_inv"):
+            assert np.array_equal(_host_f32(got[fused][k]), _host_f32(got[alone][k])), (fused, k)
+        assert np.array_equal(host_u8(got[fused]["q"]), host_u8(got[alone]["q"])), fused
+        P = int(quant.mx_group_layout(base, T)[1][-1])
+        assert np.array_equal(host_u8(got[fused]["q_t"])[:, :P], host_u8(got[alone]["q_t"])[:, :P]), fused
     assert_close(host_f64(got["h"]), fwd["h"], TAU_FP8, what="h", **KW)
     assert_close(host_f64(got["y"]), fwd["y"], TAU_FP8, what="y", **KW)
     assert_close(host_f64(got["out"]), fwd["out"], TAU_FP8, what="out", **KW)
