@@ -111,3 +111,101 @@ def test_grouped_step_graph_replays_match_eager():
         torch.cuda.synchronize()
         for t, w in zip(outs, want):
             assert np.array_equal(_bits(t), w)
+
+
+def _replays_match(step, outs):
+    """Run ``step`` eagerly, capture it, replay three times (poisoning the outputs, with eager
+    work between) and compare every output bitwise with the eager run. Outputs are poisoned
+    before the eager run too: regions a call leaves unwritten (past the last group of a
+    token-blocked copy) must stay as they were."""
+    for t in outs:
+        t.fill_(float("nan") if t.is_floating_point() else 0xAB)
+    step()
+    torch.cuda.synchronize()
+    want = [_bits(t) for t in outs]
+    g = _capture(step)
+    for _ in range(3):
+        for t in outs:
+            t.fill_(float("nan") if t.is_floating_point() else 0xAB)
+        torch.cuda.synchronize()
+        _ = torch.randn(64, 64, device="cuda") @ torch.randn(64, 64, device="cuda")
+        g.replay()
+        torch.cuda.synchronize()
+        for t, w in zip(outs, want):
+            assert np.array_equal(_bits(t), w)
+
+
+def test_quantized_grouped_steps_graph_replays_match_eager():
+    inp = synth.grouped(700, 4, 256, 256, seed=33)
+    X, W1, DOUT = dev_bf16(inp["x"]), dev_bf16(inp["w1"]), dev_bf16(inp["dout"])
+    P = torch.from_numpy(inp["p"]).cuda()
+    T, H = X.shape
+    G, N1, _ = W1.shape
+    F = N1 // 2
+    u8, f32, bf = (dict(dtype=d, device="cuda") for d in (torch.uint8, torch.float32, torch.bfloat16))
+    offs = torch.empty(1, G + 1, dtype=torch.int64, device="cuda")
+    splits = torch.from_numpy(inp["splits"]).cuda()
+    lay = torch.empty(2, G + 1, dtype=torch.int64, device="cuda")
+    ld = sge.mx_token_capacity(T, G)
+    # FP8 per group: quantize x and W1 (with fused amax downstream), fc1 + SwiGLU, quantize y
+    qws = torch.empty(16, **u8)
+    fx = [torch.empty(T, H, **u8), torch.empty(H, ld, **u8)] + [torch.empty(G, **f32) for _ in range(3)]
+    fw = [torch.empty(G * N1, H, **u8), torch.empty(H, G * N1, **u8)] + [torch.empty(G, **f32) for _ in range(3)]
+    fy = [torch.empty(T, F, **u8), torch.empty(F, ld, **u8)] + [torch.empty(G, **f32) for _ in range(3)]
+    h, y, amax_y = torch.empty(T, N1, **bf), torch.empty(T, F, **bf), torch.empty(G, **f32)
+    # MXFP8: token-blocked dout, W2 columnwise, dgrad with dSwiGLU + MXFP8 dh, wgrad
+    W2 = dev_bf16(inp["w2"])
+    mdT, msT = torch.empty(H, ld, **u8), torch.empty(H, ld // 32, **u8)
+    md, ms = torch.empty(T, H, **u8), torch.empty(T, H // 32, **u8)
+    w2c, w2s = torch.empty(F, G * H, **u8), torch.empty(F, G * H // 32, **u8)
+    myT, mysT = torch.empty(F, ld, **u8), torch.empty(F, ld // 32, **u8)
+    dh, dp = torch.empty(T, N1, **bf), torch.empty(T, **f32)
+    dhq, dhs = torch.empty(T, N1, **u8), torch.empty(T, N1 // 32, **u8)
+    dw2 = torch.empty(G, H, F, **bf)
+    ws = torch.empty(max(1, sge.grouped_linear_bwd_workspace_size(T, F, G, sge.EPI_DSCALED_SWIGLU)), **u8)
+
+    def step():
+        sge.splits_to_offsets(splits, [1], offs)
+        base = offs[0]
+        sge.mx_group_layout(base, T, lay)
+        sge.quantize_fp8_grouped(X, G, *fx[2:], qws, layout=lay, q=fx[0], q_t=fx[1])
+        sge.quantize_fp8_grouped(W1.reshape(G * N1, H), G, *fw[2:], qws, q=fw[0], q_t=fw[1])
+        sge.grouped_linear_fwd_fp8(fx[0], fx[4], fw[0].view(G, N1, H), fw[4], base, y,
+                                   epilogue=sge.EPI_SCALED_SWIGLU, probs=P, preact=h, out_amax=amax_y)
+        sge.quantize_fp8_grouped(y, G, *fy[2:], layout=lay, q=fy[0], q_t=fy[1], amax_in=amax_y)
+        sge.quantize_mxfp8_grouped(DOUT, lay, mdT, msT, q_row=md, s_row=ms)
+        sge.quantize_mxfp8(W2.reshape(G * H, F), q_colT=w2c, s_colT=w2s)
+        sge.quantize_mxfp8_grouped(y, lay, myT, mysT)
+        sge.grouped_linear_dgrad_mxfp8(md, ms, w2c, w2s, base, epilogue=sge.EPI_DSCALED_SWIGLU, preact=h, probs=P,
+                                       dact=dh, dprobs=dp, dact_q=dhq, dact_s=dhs, workspace=ws)
+        sge.grouped_linear_wgrad_mxfp8(mdT, msT, myT, mysT, lay, dw2)
+
+    _replays_match(step, [lay, fx[0], fx[1], fx[4], fw[1], y, amax_y, fy[0], fy[4], md, mdT, w2c, dh, dp, dhq,
+                          dhs, dw2])
+
+
+@pytest.mark.parametrize("kind", [sge.NORM_RMS, sge.NORM_LAYER])
+def test_norm_steps_graph_replays_match_eager(kind):
+    R, C = 256, 1024
+    r = synth.streams(34)
+    X = dev_bf16(synth.normal_bf16(r["x"], (R, C), 1.0))
+    DZ = dev_bf16(synth.normal_bf16(r["dy"], (R, C), 1.0))
+    gam, bet = dev_bf16(synth.norm_gamma(C, seed=34)), dev_bf16(synth.normal_bf16(r["residual"], (C,), 0.1))
+    u8, f32, bf = (dict(dtype=d, device="cuda") for d in (torch.uint8, torch.float32, torch.bfloat16))
+    Y, RS, MU = torch.empty(R, C, **bf), torch.empty(R, **f32), torch.empty(R, **f32)
+    f8 = {"q": torch.empty(R, C, **u8), "q_t": torch.empty(C, R, **u8), "amax": torch.empty(1, **f32),
+          "scale": torch.empty(1, **f32), "scale_inv": torch.empty(1, **f32)}
+    mr = (torch.empty(R, C, **u8), torch.empty(R, C // 32, **u8))
+    mc = (torch.empty(C, R, **u8), torch.empty(C, R // 32, **u8))
+    wsf = torch.empty(sge.norm_fwd_workspace_size(R, C), **u8)
+    DX, DG, DB = torch.empty(R, C, **bf), torch.empty(C, **bf), torch.empty(C, **bf)
+    wsb = torch.empty(sge.norm_bwd_workspace_size(R, C), **u8)
+    ln = kind == sge.NORM_LAYER
+
+    def step():
+        sge.norm_fwd(kind, X, gam, Y, RS, beta=bet if ln else None, mu=MU if ln else None, fp8=f8, mx_row=mr,
+                     mx_col=mc, workspace=wsf)
+        sge.norm_bwd(kind, DZ, X, RS, gam, DX, DG, wsb, mu=MU if ln else None, dbeta=DB if ln else None)
+
+    _replays_match(step, [Y, RS, f8["q"], f8["q_t"], f8["scale_inv"], mr[0], mr[1], mc[0], mc[1], DX, DG] +
+                   ([MU, DB] if ln else []))
