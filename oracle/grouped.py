@@ -11,6 +11,10 @@ group g are tokens ``base[g] .. base[g+1]-1`` (see ``offsets``).
 
 Readings where the page is silent:
 
+* The page names scaled SReLU beside scaled SwiGLU and clamped SwiGLU without formulas; SReLU
+  is read as the squared ReLU, ``max(h, 0)^2``, applied elementwise (fc1 has F outputs, no
+  gate half), scaled per token like SwiGLU: ``y = p * max(h, 0)^2``.
+
 * fc1's output h [T, 2F] holds the SwiGLU gate in its first half and the
   linear ("up") part in its second half: ``a = h[:, :F]``, ``b = h[:, F:]``.
 * ``y = p[:, None] * silu(a) * b`` with ``silu(a) = a * sigmoid(a)``.
@@ -96,15 +100,33 @@ def scaled_swiglu_bwd(gy, h, p):
     return np.concatenate([da, db], axis=1), dp
 
 
-def grouped_mlp_fwd(x, w1, w2, p, base):
-    """fc1 -> scaled SwiGLU -> fc2. Returns dict(h, y, out)."""
+def scaled_srelu_fwd(h, p):
+    """y = p * srelu(h), srelu(h) = max(h, 0)^2 (squared ReLU, elementwise: no gate half)."""
+    h = np.asarray(h, np.float64)
+    r = np.maximum(h, 0.0)
+    return np.asarray(p, np.float64)[:, None] * r * r
+
+
+def scaled_srelu_bwd(gy, h, p):
+    """Gradients of y = p * max(h, 0)^2 given dL/dy: dh = gy * p * 2 max(h, 0), dp = sum_j gy_j * max(h_j, 0)^2."""
+    gy = np.asarray(gy, np.float64)
+    r = np.maximum(np.asarray(h, np.float64), 0.0)
+    p = np.asarray(p, np.float64)[:, None]
+    return gy * p * 2.0 * r, np.sum(gy * r * r, axis=1)
+
+
+_ACTS = {"swiglu": (scaled_swiglu_fwd, scaled_swiglu_bwd), "srelu": (scaled_srelu_fwd, scaled_srelu_bwd)}
+
+
+def grouped_mlp_fwd(x, w1, w2, p, base, act="swiglu"):
+    """fc1 -> scaled activation (SwiGLU, or SReLU) -> fc2. Returns dict(h, y, out)."""
     h = grouped_linear_fwd(x, w1, base)
-    y = scaled_swiglu_fwd(h, p)
+    y = _ACTS[act][0](h, p)
     out = grouped_linear_fwd(y, w2, base)
     return {"h": h, "y": y, "out": out}
 
 
-def grouped_mlp_bwd(dout, x, w1, w2, p, base, h=None, y=None):
+def grouped_mlp_bwd(dout, x, w1, w2, p, base, h=None, y=None, act="swiglu"):
     """Backward of ``grouped_mlp_fwd`` given dL/dout.
 
     Returns dict(gy = dL/dy, dh, dp, dw2, dx, dw1). ``h`` and ``y`` are
@@ -113,9 +135,9 @@ def grouped_mlp_bwd(dout, x, w1, w2, p, base, h=None, y=None):
     if h is None:
         h = grouped_linear_fwd(x, w1, base)
     if y is None:
-        y = scaled_swiglu_fwd(h, p)
+        y = _ACTS[act][0](h, p)
     gy = grouped_linear_dgrad(dout, w2, base)
-    dh, dp = scaled_swiglu_bwd(gy, h, p)
+    dh, dp = _ACTS[act][1](gy, h, p)
     dw2 = grouped_linear_wgrad(dout, y, base)
     dx = grouped_linear_dgrad(dh, w1, base)
     dw1 = grouped_linear_wgrad(dh, x, base)

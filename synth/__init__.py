@@ -84,15 +84,15 @@ def norm_gamma(C, seed=0, std=0.1):
     return f32_to_bf16_bits(a)
 
 
-def grouped(T, G, hidden, ffn, *, seed=0, x_std=1.0, w_std=0.02, dout_std=1e-2, splits=None):
-    """Inputs of the grouped MLP: x [T, hidden], W1 [G, 2*ffn, hidden], W2 [G, hidden, ffn],
-    p [T] float32 U(0,1), dout [T, hidden], splits [G] int64."""
+def grouped(T, G, hidden, ffn, *, seed=0, x_std=1.0, w_std=0.02, dout_std=1e-2, splits=None, gated=True):
+    """Inputs of the grouped MLP: x [T, hidden], W1 [G, 2*ffn, hidden] (gated activation; [G, ffn,
+    hidden] otherwise), W2 [G, hidden, ffn], p [T] float32 U(0,1), dout [T, hidden], splits [G] int64."""
     r = streams(seed)
     if splits is None:
         splits = dirichlet_splits(r["splits"], G, T)
     return {
         "x": normal_bf16(r["x"], (T, hidden), x_std),
-        "w1": normal_bf16(r["w"], (G, 2 * ffn, hidden), w_std),
+        "w1": normal_bf16(r["w"], (G, (2 if gated else 1) * ffn, hidden), w_std),
         "w2": normal_bf16(r["w2"], (G, hidden, ffn), w_std),
         "p": r["p"].random(size=T, dtype=np.float32),
         "dout": normal_bf16(r["dout"], (T, hidden), dout_std),

@@ -149,3 +149,38 @@ def test_grouped_inputs_recipe():
     assert d["p"].dtype == np.float32 and np.all((d["p"] >= 0) & (d["p"] < 1))
     again = synth.grouped(1000, 8, 64, 32, seed=0)
     assert all(np.array_equal(d[k], again[k]) for k in d)
+
+
+def test_srelu_closed_forms():
+    h = np.array([[-2.0, -0.0, 0.0, 0.5, 3.0]])
+    p = np.array([0.25])
+    y = grouped.scaled_srelu_fwd(h, p)
+    assert y.tolist() == [[0.0, 0.0, 0.0, 0.0625, 2.25]]                   # 0.25 * max(h, 0)^2
+    dh, dp = grouped.scaled_srelu_bwd(np.ones_like(h), h, p)
+    assert dh.tolist() == [[0.0, 0.0, 0.0, 0.25, 1.5]]                    # 0.25 * 2 * max(h, 0)
+    assert dp.tolist() == [0.25 + 9.0]
+
+
+def test_grouped_srelu_mlp_backward_vs_torch_autograd():
+    splits = [2, 0, 3, 1]
+    T, H, F, G = 6, 4, 3, 4
+    base = offsets.base_offsets(splits)
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((T, H))
+    w1 = rng.standard_normal((G, F, H)) * 0.5
+    w2 = rng.standard_normal((G, H, F)) * 0.5
+    p = rng.random(T)
+    dout = rng.standard_normal((T, H))
+    ours_f = grouped.grouped_mlp_fwd(x, w1, w2, p, base, act="srelu")
+    ours_b = grouped.grouped_mlp_bwd(dout, x, w1, w2, p, base, act="srelu")
+    tx, tw1, tw2, tp = (torch.tensor(a, requires_grad=True) for a in (x, w1, w2, p))
+    outs = []
+    for g in range(G):
+        lo, hi = base[g], base[g + 1]
+        y = tp[lo:hi, None] * torch.relu(tx[lo:hi] @ tw1[g].T) ** 2
+        outs.append(y @ tw2[g].T)
+    out = torch.cat(outs)
+    out.backward(torch.tensor(dout))
+    assert np.allclose(ours_f["out"], out.detach().numpy(), rtol=1e-12, atol=1e-13)
+    for k, t in (("dx", tx), ("dw1", tw1), ("dw2", tw2), ("dp", tp)):
+        assert np.allclose(ours_b[k], t.grad.numpy(), rtol=1e-12, atol=1e-13), k
