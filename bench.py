@@ -195,15 +195,19 @@ def build_grouped(torch, sge, wl, inp):
     splits = torch.from_numpy(inp["splits"]).cuda()
     T, H = X.shape
     G, N1, _ = W1.shape
-    F = N1 // 2
+    act = wl.get("act", "swiglu")
+    F = N1 // 2 if act == "swiglu" else N1
+    fwd_epi = sge.EPI_SCALED_SWIGLU if act == "swiglu" else sge.EPI_SCALED_SRELU
+    bwd_epi = sge.EPI_DSCALED_SWIGLU if act == "swiglu" else sge.EPI_DSCALED_SRELU
     bf = dict(dtype=torch.bfloat16, device="cuda")
     offs = torch.empty(2, G + 1, dtype=torch.int64, device="cuda")
     h, y, out = torch.empty(T, N1, **bf), torch.empty(T, F, **bf), torch.empty(T, H, **bf)
     dh, dp = torch.empty(T, N1, **bf), torch.empty(T, dtype=torch.float32, device="cuda")
     dw2, dx, dw1 = torch.empty(G, H, F, **bf), torch.empty(T, H, **bf), torch.empty(G, N1, H, **bf)
-    ws = torch.empty(max(1, sge.grouped_linear_bwd_workspace_size(T, F, G, sge.EPI_DSCALED_SWIGLU)),
+    ws = torch.empty(max(1, sge.grouped_linear_bwd_workspace_size(T, F, G, bwd_epi)),
                      dtype=torch.uint8, device="cuda")
-    flops = {"fc1_fwd": 2 * T * N1 * H, "fc2_fwd": 2 * T * H * F, "fc2_dgrad_dswiglu": 2 * T * H * F,
+    dact = "fc2_dgrad_dswiglu" if act == "swiglu" else "fc2_dgrad_dsrelu"
+    flops = {"fc1_fwd": 2 * T * N1 * H, "fc2_fwd": 2 * T * H * F, dact: 2 * T * H * F,
              "fc2_wgrad": 2 * T * H * F, "fc1_dgrad": 2 * T * N1 * H, "fc1_wgrad": 2 * T * N1 * H}
 
     base = offs[0]
@@ -214,10 +218,9 @@ def build_grouped(torch, sge, wl, inp):
                                  flops)
     launches = [
         ("offsets", lambda: sge.splits_to_offsets(splits, [1, H], offs)),
-        ("fc1_fwd", lambda: sge.grouped_linear_fwd(X, W1, base, y, epilogue=sge.EPI_SCALED_SWIGLU, probs=P,
-                                                   preact=h)),
+        ("fc1_fwd", lambda: sge.grouped_linear_fwd(X, W1, base, y, epilogue=fwd_epi, probs=P, preact=h)),
         ("fc2_fwd", lambda: sge.grouped_linear_fwd(y, W2, base, out)),
-        ("fc2_dgrad_dswiglu", lambda: sge.grouped_linear_bwd(DOUT, None, W2, base, epilogue=sge.EPI_DSCALED_SWIGLU,
+        (dact, lambda: sge.grouped_linear_bwd(DOUT, None, W2, base, epilogue=bwd_epi,
                                                              preact=h, probs=P, dact=dh, dprobs=dp, workspace=ws)),
         ("fc2_wgrad", lambda: sge.grouped_linear_bwd(DOUT, y, W2, base, dw=dw2)),
         ("fc1_dgrad", lambda: sge.grouped_linear_bwd(dh, None, W1, base, dx=dx)),
@@ -459,15 +462,17 @@ def cpu_baseline(wl, inp, target_s):
             x = bf16_to_f64(inp["x"][:tok])
             w1, w2 = bf16_to_f64(inp["w1"]), bf16_to_f64(inp["w2"])
             p = inp["p"][:tok].astype(np.float64)
-            f = grouped.grouped_mlp_fwd(x, w1, w2, p, base)
-            grouped.grouped_mlp_bwd(bf16_to_f64(inp["dout"][:tok]), x, w1, w2, p, base, h=f["h"], y=f["y"])
+            act = wl.get("act", "swiglu")
+            f = grouped.grouped_mlp_fwd(x, w1, w2, p, base, act=act)
+            grouped.grouped_mlp_bwd(bf16_to_f64(inp["dout"][:tok]), x, w1, w2, p, base, h=f["h"], y=f["y"], act=act)
             dt = time.perf_counter() - t0
             if dt >= target_s / 4 or tok >= T:
                 break
             tok = min(T, tok * 4)
         H = inp["x"].shape[1]
         N1 = inp["w1"].shape[1]
-        flops = 3 * (2 * tok * N1 * H + 2 * tok * H * (N1 // 2))
+        F = N1 // 2 if wl.get("act", "swiglu") == "swiglu" else N1
+        flops = 3 * (2 * tok * N1 * H + 2 * tok * H * F)
         sample = f"first {tok} of {T} tokens through the grouped MLP forward and backward"
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": sample, "seconds": round(dt, 3)}

@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define SGE_ABI_VERSION 4
+#define SGE_ABI_VERSION 5
 
 /* Alignment, in tokens, of each group's start in a token-blocked MXFP8 operand. */
 #define SGE_MX_TOKEN_ALIGN 128
@@ -85,7 +85,9 @@ typedef struct {
 typedef enum {
   SGE_EPI_NONE = 0,            /* out = alpha * acc */
   SGE_EPI_SCALED_SWIGLU = 1,   /* forward: h = alpha*acc, y = p * silu(h[:, :F]) * h[:, F:] */
-  SGE_EPI_DSCALED_SWIGLU = 2   /* backward: dgrad g of the next layer -> dh = [da, db], dp */
+  SGE_EPI_DSCALED_SWIGLU = 2,  /* backward: dgrad g of the next layer -> dh = [da, db], dp */
+  SGE_EPI_SCALED_SRELU = 3,    /* forward: h = alpha*acc, y = p * max(h, 0)^2 (elementwise, no gate half) */
+  SGE_EPI_DSCALED_SRELU = 4    /* backward: dh = g * p * 2 max(h, 0), dp = sum_j g * max(h, 0)^2 */
 } sge_epilogue;
 
 int sge_abi_version(void);
@@ -202,6 +204,8 @@ sge_status sge_splits_to_offsets(const int64_t* splits, int32_t G, const int64_t
  * SGE_EPI_SCALED_SWIGLU: F = N/2, a = h[:, :F], b = h[:, F:];
  *                        out [T, F] bf16 = p[t] * silu(a) * b (from the fp32 h),
  *                        preact [T, N] bf16 = h (saved for the backward; may be NULL).
+ * SGE_EPI_SCALED_SRELU:  out [T, N] bf16 = p[t] * max(h, 0)^2 (scaled squared ReLU; the page
+ *                        names scaled SReLU beside scaled SwiGLU), preact [T, N] = h (or NULL).
  * offsets: device int64 [G+1] (row 0 of sge_splits_to_offsets with multiplier 1);
  * values are clamped into [0, T] and made non-decreasing before use.
  * probs: device fp32 [T] (SWIGLU only). Shapes: K % 8 == 0, N % 8 == 0
@@ -251,6 +255,8 @@ sge_status sge_grouped_linear_fwd_mxfp8(const void* x_q, const void* x_s, const 
  *                         dact [T, 2K] bf16 = [g*p*b*silu'(a), g*p*silu(a)] and
  *                         dprobs [T] fp32 = sum_j g*silu(a)*b (deterministic order).
  *                         dx is not used.
+ * SGE_EPI_DSCALED_SRELU:  x was y = p * max(h, 0)^2 with preact h [T, K] bf16; writes
+ *                         dact [T, K] = g*p*2*max(h, 0) and dprobs [T] = sum_j g*max(h, 0)^2.
  * dw: device bf16 [G, N, K] or NULL to skip the weight gradient.
  * workspace: device, >= sge_grouped_linear_bwd_workspace_size(T, K, G, epilogue) bytes
  * (0 is valid for SGE_EPI_NONE).

@@ -26,7 +26,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_FORMAT, ERR_ALIGN, ERR_ALIAS, ERR_WORKSPACE, ERR_AR
 # operand formats
 FMT_BF16, FMT_E4M3, FMT_MXFP8 = 0, 1, 2
 # grouped epilogues
-EPI_NONE, EPI_SCALED_SWIGLU, EPI_DSCALED_SWIGLU = 0, 1, 2
+EPI_NONE, EPI_SCALED_SWIGLU, EPI_DSCALED_SWIGLU, EPI_SCALED_SRELU, EPI_DSCALED_SRELU = 0, 1, 2, 3, 4
 # normalizations
 NORM_RMS, NORM_LAYER = 0, 1
 

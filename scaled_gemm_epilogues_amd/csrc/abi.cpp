@@ -302,10 +302,10 @@ sge_status sge_grouped_linear_fwd(const void* x, const void* w, int32_t G, int64
                                   const int64_t* offsets, float alpha, int32_t epilogue, const float* probs, void* out,
                                   void* preact, hipStream_t stream) {
   if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd: bad sizes");
-  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_SCALED_SWIGLU)
+  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_SCALED_SWIGLU && epilogue != SGE_EPI_SCALED_SRELU)
     return fail(SGE_ERR_ARG, "grouped_linear_fwd: epilogue %d not allowed", epilogue);
   if (!x || !w || !offsets || !out) return fail(SGE_ERR_NULL, "grouped_linear_fwd: NULL pointer");
-  if (epilogue == SGE_EPI_SCALED_SWIGLU && !probs) return fail(SGE_ERR_NULL, "grouped_linear_fwd: probs is NULL");
+  if (epilogue != SGE_EPI_NONE && !probs) return fail(SGE_ERR_NULL, "grouped_linear_fwd: probs is NULL");
   if (K % 8 || N % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd: N and K must be multiples of 8");
   if (epilogue == SGE_EPI_SCALED_SWIGLU && N % 256)
     return fail(SGE_ERR_SHAPE, "grouped_linear_fwd: SwiGLU needs N %% 256 == 0");
@@ -409,7 +409,7 @@ sge_status sge_grouped_linear_fwd_mxfp8(const void* x_q, const void* x_s, const 
 
 size_t sge_grouped_linear_bwd_workspace_size(int64_t T, int64_t K, int32_t G, int32_t epilogue) {
   (void)G;
-  if (epilogue != SGE_EPI_DSCALED_SWIGLU || T <= 0 || K <= 0) return 0;
+  if ((epilogue != SGE_EPI_DSCALED_SWIGLU && epilogue != SGE_EPI_DSCALED_SRELU) || T <= 0 || K <= 0) return 0;
   const int64_t parts = sge::gemm_dp_parts_per_tile() * ((K + sge::gemm_tile_n() - 1) / sge::gemm_tile_n());
   return (size_t)(parts * T) * sizeof(float);
 }
@@ -419,13 +419,14 @@ sge_status sge_grouped_linear_bwd(const void* dy, const void* x, const void* w, 
                                   const float* probs, void* dact, float* dprobs, void* dx, void* dw, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream) {
   if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_bwd: bad sizes");
-  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_DSCALED_SWIGLU)
+  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_DSCALED_SWIGLU && epilogue != SGE_EPI_DSCALED_SRELU)
     return fail(SGE_ERR_ARG, "grouped_linear_bwd: epilogue %d not allowed", epilogue);
-  const bool swiglu = epilogue == SGE_EPI_DSCALED_SWIGLU;
+  const bool swiglu = epilogue != SGE_EPI_NONE;                  // an activation backward in the epilogue
+  const int64_t hw = epilogue == SGE_EPI_DSCALED_SWIGLU ? 2 * K : K;   // pre-activation / dact width
   if (!dy || !w || !offsets) return fail(SGE_ERR_NULL, "grouped_linear_bwd: NULL pointer");
   if (dw && !x) return fail(SGE_ERR_NULL, "grouped_linear_bwd: x is NULL");
   if (swiglu && (!preact || !probs || !dact || !dprobs))
-    return fail(SGE_ERR_NULL, "grouped_linear_bwd: SwiGLU backward needs preact, probs, dact and dprobs");
+    return fail(SGE_ERR_NULL, "grouped_linear_bwd: the activation backward needs preact, probs, dact and dprobs");
   if (K % 8 || N % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_bwd: N and K must be multiples of 8");
   if (!aligned16(dy) || (x && !aligned16(x)) || !aligned16(w) || (dx && !aligned16(dx)) || (dw && !aligned16(dw)) ||
       (preact && !aligned16(preact)) || (dact && !aligned16(dact)))
@@ -434,8 +435,8 @@ sge_status sge_grouped_linear_bwd(const void* dy, const void* x, const void* w, 
   const Range rx = x ? range_of(x, T, K, K, 2) : Range{0, 0};
   if ((dx && !swiglu && (overlap(range_of(dx, T, K, K, 2), rdy) || overlap(range_of(dx, T, K, K, 2), rw))) ||
       (dw && (overlap(range_of(dw, (int64_t)G * N, K, K, 2), rdy) || overlap(range_of(dw, (int64_t)G * N, K, K, 2), rx))) ||
-      (swiglu && (overlap(range_of(dact, T, 2 * K, 2 * K, 2), rdy) ||
-                  overlap(range_of(dact, T, 2 * K, 2 * K, 2), range_of(preact, T, 2 * K, 2 * K, 2)))))
+      (swiglu && (overlap(range_of(dact, T, hw, hw, 2), rdy) ||
+                  overlap(range_of(dact, T, hw, hw, 2), range_of(preact, T, hw, hw, 2)))))
     return fail(SGE_ERR_ALIAS, "grouped_linear_bwd: outputs overlap inputs");
   const size_t need = sge_grouped_linear_bwd_workspace_size(T, K, G, epilogue);
   if (need && (!workspace || workspace_bytes < need))
@@ -465,9 +466,9 @@ sge_status sge_grouped_linear_bwd(const void* dy, const void* x, const void* w, 
     if (swiglu) {
       p.probs = probs;
       p.aux = const_cast<uint16_t*>(static_cast<const uint16_t*>(preact));
-      p.ld_aux = 2 * K;
+      p.ld_aux = hw;
       p.aux_out = static_cast<uint16_t*>(dact);
-      p.ld_aux_out = 2 * K;
+      p.ld_aux_out = hw;
       p.dp_part = static_cast<float*>(workspace);
       p.F = K;
     }

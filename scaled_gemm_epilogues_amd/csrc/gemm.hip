@@ -37,7 +37,7 @@
 namespace sge {
 
 enum { F_BF16 = 0, F_E4M3 = 1, F_MX = 2, F_MXU = 3 };   // F_MXU: MXFP8 with unaligned scale rows
-enum { E_STORE = 0, E_SWIGLU = 1, E_DSWIGLU = 2 };
+enum { E_STORE = 0, E_SWIGLU = 1, E_DSWIGLU = 2, E_SRELU = 3, E_DSRELU = 4 };
 enum { S_DENSE = 0, S_GROUP_M = 1, S_GROUP_K = 2 };
 
 constexpr int kRowBytes = 128;   // contraction bytes per LDS row and per k-tile
@@ -617,11 +617,14 @@ void gemm_kernel(const GemmParams p) {
   auto row_in_tile = [&](int i) { return wm * WM + i * 32 + lrow; };
   auto row_ok = [&](int i) { return m0 + row_in_tile(i) < row_end; };
 
-  if constexpr (EPI == E_STORE) {
+  if constexpr (EPI == E_STORE || EPI == E_SRELU) {
     // Two passes over half of each wave's rows: alpha*acc (fp32) goes to LDS in row-major
     // order (16-byte granule g of row r at g ^ (r & 15), conflict-free from the fragment
     // layout), then every thread takes 8 consecutive columns of a row: one 16-byte residual
     // load and one 16-byte store, so each wave moves whole 128-byte lines.
+    // E_SRELU (scaled squared ReLU, elementwise): y = p * max(v, 0)^2 goes to c and the
+    // pre-activation v (bf16) to aux, at the same offsets (ld_aux == ldc).
+    constexpr bool kSR = EPI == E_SRELU;
     static_assert(BM == 2 * WM && A_BYTES + B_BYTES == 64 * BN * 4, "epilogue staging assumes 2 wave rows");
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(cptr + m0 * p.ldc, rows_left * p.ldc * 2);
     constexpr int kChunks = BN / 8;                        // 8-column chunks per row
@@ -639,7 +642,10 @@ void gemm_kernel(const GemmParams p) {
         const int brow = (rp >> 6) * WM + pass * (WM / 2) + (rp & 63);
         const int64_t n = n0 + c * 8;
         offs[pass][it] = (m0 + brow < row_end && n < n_end) ? (int)(((int64_t)brow * p.ldc + n) * 2) : (int)kOOB;
-        if (p.accumulate) res[pass][it] = __builtin_amdgcn_raw_buffer_load_b128(rc, offs[pass][it], 0, 0);
+        if (!kSR && p.accumulate) res[pass][it] = __builtin_amdgcn_raw_buffer_load_b128(rc, offs[pass][it], 0, 0);
+        if constexpr (kSR)                                 // the row's scale p (res[.][.][0] carries it)
+          res[pass][it][0] = __builtin_amdgcn_raw_buffer_load_b32(
+              make_rsrc(p.probs + m0, rows_left * 4), m0 + brow < row_end ? brow * 4 : (int)kOOB, 0, 0);
       }
     __syncthreads();                                       // every wave is done with the LDS stages
 #pragma unroll
@@ -668,7 +674,19 @@ void gemm_kernel(const GemmParams p) {
         const float4 lo = *reinterpret_cast<const float4*>(row + (((2 * c) ^ sw) << 2));
         const float4 hi = *reinterpret_cast<const float4*>(row + (((2 * c + 1) ^ sw) << 2));
         float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        if (p.accumulate) {
+        if constexpr (kSR) {
+          const float pm = __builtin_bit_cast(float, res[pass][it][0]);
+          const v4i vh = {(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3]), (int)pack_bf16x2(v[4], v[5]),
+                          (int)pack_bf16x2(v[6], v[7])};
+          __builtin_amdgcn_raw_buffer_store_b128(       // no pre-activation buffer: a zero-size resource
+              vh, make_rsrc(p.aux ? p.aux + m0 * p.ld_aux : p.aux, p.aux ? rows_left * p.ld_aux * 2 : 0),
+              offs[pass][it], 0, 0);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float rl = fmaxf(v[e], 0.0f);
+            v[e] = pm * rl * rl;
+          }
+        } else if (p.accumulate) {
           const v4i r4 = res[pass][it];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -791,7 +809,7 @@ void gemm_kernel(const GemmParams p) {
         slot_to_group(&amax_slot, p.amax_out, grp);
       }
     }
-  } else {  // E_DSWIGLU
+  } else {  // E_DSWIGLU, E_DSRELU
     // Staged like E_STORE: g = alpha*acc for half of each wave's rows goes to LDS, then each
     // thread takes 8 consecutive columns of one row: 16-byte loads of a and b (the two halves
     // of the saved pre-activation), 16-byte stores of da and db. A row's BN/8 chunks are 32
@@ -799,6 +817,9 @@ void gemm_kernel(const GemmParams p) {
     // per row and column tile goes to the workspace.
     static_assert(BM == 2 * WM && A_BYTES + B_BYTES == 64 * BN * 4, "epilogue staging assumes 2 wave rows");
     static_assert(BN / 8 == 32, "a row's chunks fill half a wave");
+    // E_DSRELU (scaled squared ReLU): one pre-activation h [T, F]; dh = g * p * 2 max(h, 0),
+    // dprobs partial sum of g * max(h, 0)^2.
+    constexpr bool kSR = EPI == E_DSRELU;
     const int64_t hbytes = rows_left * p.ld_aux * 2;
     const int64_t dbytes = p.aux_out ? rows_left * p.ld_aux_out * 2 : 0;
     // One resource per tensor; the b half sits F columns further (an out-of-range offset
@@ -861,7 +882,7 @@ void gemm_kernel(const GemmParams p) {
         od[ib] = ok ? (int)(((int64_t)brow * p.ld_aux_out + n) * 2) : (int)kOOB;
         orow[ib] = rok ? brow * 4 : (int)kOOB;
         ha[ib] = __builtin_amdgcn_raw_buffer_load_b128(rh, oh[ib], 0, 0);
-        hb[ib] = __builtin_amdgcn_raw_buffer_load_b128(rh, oh[ib] + fb, 0, 0);
+        if constexpr (!kSR) hb[ib] = __builtin_amdgcn_raw_buffer_load_b128(rh, oh[ib] + fb, 0, 0);
         pr[ib] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, orow[ib], 0, 0));
       }
 #pragma unroll
@@ -878,22 +899,30 @@ void gemm_kernel(const GemmParams p) {
         float da[8], db[8], part = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const uint32_t wa = (uint32_t)ha[ib][e >> 1], wb = (uint32_t)hb[ib][e >> 1];
+          const uint32_t wa = (uint32_t)ha[ib][e >> 1];
           const float a = (e & 1) ? bf16_hi(wa) : bf16_lo(wa);
-          const float b = (e & 1) ? bf16_hi(wb) : bf16_lo(wb);
-          const float sg = fast_sigmoid(a);
-          const float silu = a * sg;
-          const float dsilu = sg * (1.0f + a * (1.0f - sg));
-          da[e] = g[e] * pm * b * dsilu;
-          db[e] = g[e] * pm * silu;
-          part += g[e] * silu * b;
+          if constexpr (kSR) {
+            const float rl = fmaxf(a, 0.0f);
+            da[e] = g[e] * pm * 2.0f * rl;
+            db[e] = 0.0f;
+            part += g[e] * rl * rl;
+          } else {
+            const uint32_t wb = (uint32_t)hb[ib][e >> 1];
+            const float b = (e & 1) ? bf16_hi(wb) : bf16_lo(wb);
+            const float sg = fast_sigmoid(a);
+            const float silu = a * sg;
+            const float dsilu = sg * (1.0f + a * (1.0f - sg));
+            da[e] = g[e] * pm * b * dsilu;
+            db[e] = g[e] * pm * silu;
+            part += g[e] * silu * b;
+          }
         }
         const v4i va = {(int)pack_bf16x2(da[0], da[1]), (int)pack_bf16x2(da[2], da[3]),
                         (int)pack_bf16x2(da[4], da[5]), (int)pack_bf16x2(da[6], da[7])};
         const v4i vb = {(int)pack_bf16x2(db[0], db[1]), (int)pack_bf16x2(db[2], db[3]),
                         (int)pack_bf16x2(db[4], db[5]), (int)pack_bf16x2(db[6], db[7])};
         __builtin_amdgcn_raw_buffer_store_b128(va, rd, od[ib], 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(vb, rd, od[ib] + fb, 0, 0);
+        if constexpr (!kSR) __builtin_amdgcn_raw_buffer_store_b128(vb, rd, od[ib] + fb, 0, 0);
         if constexpr (kAmax) {
           if (want_amax) {                                 // per item: no register lives across items
             float mi = 0.0f;
@@ -974,6 +1003,7 @@ hipError_t launch_gemm(const GemmParams& p, int fmt, bool a_kmaj, bool b_kmaj, h
 
 hipError_t launch_grouped_fwd(const GemmParams& p, int epilogue, hipStream_t s) {
   if (epilogue == E_SWIGLU) return launch_tile<F_BF16, true, true, E_SWIGLU, S_GROUP_M>(p, s);
+  if (epilogue == E_SRELU) return launch_tile<F_BF16, true, true, E_SRELU, S_GROUP_M>(p, s);
   return launch_tile<F_BF16, true, true, E_STORE, S_GROUP_M>(p, s);
 }
 
@@ -984,6 +1014,7 @@ hipError_t launch_grouped_fwd_mx(const GemmParams& p, int epilogue, hipStream_t 
 
 hipError_t launch_grouped_dgrad(const GemmParams& p, int epilogue, hipStream_t s) {
   if (epilogue == E_DSWIGLU) return launch_tile<F_BF16, true, false, E_DSWIGLU, S_GROUP_M>(p, s);
+  if (epilogue == E_DSRELU) return launch_tile<F_BF16, true, false, E_DSRELU, S_GROUP_M>(p, s);
   return launch_tile<F_BF16, true, false, E_STORE, S_GROUP_M>(p, s);
 }
 

@@ -92,14 +92,17 @@ def run_dense(fmt, inputs, alpha, passes=("fwd", "dgrad", "wgrad")):
     return out
 
 
-def run_grouped_mlp(inp, with_backward=True):
-    """Grouped MLP on device: offsets, fc1 + scaled SwiGLU, fc2, and the backward of both layers."""
+def run_grouped_mlp(inp, with_backward=True, act="swiglu"):
+    """Grouped MLP on device: offsets, fc1 + scaled SwiGLU (or scaled SReLU), fc2, and the
+    backward of both layers."""
     X, W1, W2 = dev_bf16(inp["x"]), dev_bf16(inp["w1"]), dev_bf16(inp["w2"])
     P = torch.from_numpy(inp["p"]).cuda()
     splits = torch.from_numpy(inp["splits"]).cuda()
     T, H = X.shape
     G, N1, _ = W1.shape
-    F = N1 // 2
+    F = N1 // 2 if act == "swiglu" else N1
+    fwd_epi = sge.EPI_SCALED_SWIGLU if act == "swiglu" else sge.EPI_SCALED_SRELU
+    bwd_epi = sge.EPI_DSCALED_SWIGLU if act == "swiglu" else sge.EPI_DSCALED_SRELU
     offs = torch.empty(1, G + 1, dtype=torch.int64, device="cuda")
     err = torch.empty(1, dtype=torch.int32, device="cuda")
     sge.splits_to_offsets(splits, [1], offs, expected_total=T, err_flag=err)
@@ -107,7 +110,7 @@ def run_grouped_mlp(inp, with_backward=True):
     h = torch.empty(T, N1, dtype=torch.bfloat16, device="cuda")
     y = torch.empty(T, F, dtype=torch.bfloat16, device="cuda")
     out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
-    sge.grouped_linear_fwd(X, W1, base, y, epilogue=sge.EPI_SCALED_SWIGLU, probs=P, preact=h)
+    sge.grouped_linear_fwd(X, W1, base, y, epilogue=fwd_epi, probs=P, preact=h)
     sge.grouped_linear_fwd(y, W2, base, out)
     res = {"offsets": offs, "err": err, "h": h, "y": y, "out": out}
     if with_backward:
@@ -115,9 +118,9 @@ def run_grouped_mlp(inp, with_backward=True):
         dh = torch.empty(T, N1, dtype=torch.bfloat16, device="cuda")
         dp = torch.empty(T, dtype=torch.float32, device="cuda")
         dw2 = torch.empty(G, H, F, dtype=torch.bfloat16, device="cuda")
-        ws = torch.empty(max(1, sge.grouped_linear_bwd_workspace_size(T, F, G, sge.EPI_DSCALED_SWIGLU)),
+        ws = torch.empty(max(1, sge.grouped_linear_bwd_workspace_size(T, F, G, bwd_epi)),
                          dtype=torch.uint8, device="cuda")
-        sge.grouped_linear_bwd(DOUT, y, W2, base, epilogue=sge.EPI_DSCALED_SWIGLU, preact=h, probs=P, dact=dh,
+        sge.grouped_linear_bwd(DOUT, y, W2, base, epilogue=bwd_epi, preact=h, probs=P, dact=dh,
                                dprobs=dp, dw=dw2, workspace=ws)
         dx = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
         dw1 = torch.empty(G, N1, H, dtype=torch.bfloat16, device="cuda")

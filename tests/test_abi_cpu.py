@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol(sge):
     lib = ctypes.CDLL(sge.library_path())
     for name in _declared():
         assert hasattr(lib, name), name
-    assert sge.abi_version() == 4
+    assert sge.abi_version() == 5
 
 
 def test_status_strings(sge):
@@ -377,3 +377,19 @@ def test_norm_validation_errors(sge):
     assert b(*a) == sge.ERR_ALIAS                                         # dx over x
     a = list(ok); a[13] = wsb - 4
     assert b(*a) == sge.ERR_WORKSPACE
+
+
+def test_srelu_epilogue_validation(sge):
+    def B(k):
+        return FAKE * 8 * k
+
+    f = sge._lib.sge_grouped_linear_fwd
+    # bf16 grouped forward: SReLU needs probs
+    assert f(B(1), B(2), 4, 100, 264, 256, B(3), 1.0, sge.EPI_SCALED_SRELU, None, B(4), B(5), None) == sge.ERR_NULL
+    fm = sge._lib.sge_grouped_linear_fwd_mxfp8
+    assert fm(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, sge.EPI_SCALED_SRELU, B(6), B(7), B(8),
+              None, None, None) == sge.ERR_ARG                             # the MXFP8 path has no SReLU
+    b = sge._lib.sge_grouped_linear_bwd
+    assert b(B(1), None, B(2), 4, 100, 256, 264, B(3), 1.0, sge.EPI_DSCALED_SRELU, B(4), B(5), None, B(6), None,
+              None, B(7), 0, None) == sge.ERR_NULL                        # SReLU backward needs dact
+    assert sge.grouped_linear_bwd_workspace_size(100, 264, 4, sge.EPI_DSCALED_SRELU) == 2 * 100 * 4

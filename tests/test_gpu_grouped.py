@@ -132,3 +132,29 @@ def test_unfused_swiglu_parity():
     rdh, rdp = grouped.scaled_swiglu_bwd(bf16_to_f64(gy), hf, pf)
     assert_close(host_f64(dh), rdh, TAU_BF16, what="dh")
     assert_close(host_f64(dp), rdp, TAU_BF16, what="dp", rel_tight=1e-5, abs_tight=1e-5)
+
+
+SRELU_CASES = {
+    "empty_and_single": ([0, 1, 300, 0, 211, 8], 256, 256),
+    "ragged_ffn": (None, 256, 264),                  # F not a multiple of the 256-column tile
+}
+
+
+@pytest.mark.parametrize("case", list(SRELU_CASES))
+def test_grouped_srelu_mlp_parity(case):
+    splits, hidden, ffn = SRELU_CASES[case]
+    T = 520 if splits is None else sum(splits)
+    G = 5 if splits is None else len(splits)
+    print(f"case grouped srelu mlp {case} T={T} G={G} hidden={hidden} ffn={ffn}", flush=True)
+    inp = synth.grouped(T, G, hidden, ffn, seed=23, splits=splits, gated=False)
+    got = run_grouped_mlp(inp, act="srelu")
+    base = offsets.base_offsets(inp["splits"])
+    x, w1, w2 = bf16_to_f64(inp["x"]), bf16_to_f64(inp["w1"]), bf16_to_f64(inp["w2"])
+    p = inp["p"].astype(np.float64)
+    f = grouped.grouped_mlp_fwd(x, w1, w2, p, base, act="srelu")
+    b = grouped.grouped_mlp_bwd(bf16_to_f64(inp["dout"]), x, w1, w2, p, base, h=f["h"], y=f["y"], act="srelu")
+    kw = dict(rel_tight=2.0 ** -7, abs_tight=5e-2)
+    assert_close(host_f64(got["h"]), f["h"], TAU_BF16, what="h")
+    for k, ref in (("y", f["y"]), ("out", f["out"]), ("dh", b["dh"]), ("dp", b["dp"]), ("dw2", b["dw2"]),
+                   ("dx", b["dx"]), ("dw1", b["dw1"])):
+        assert_close(host_f64(got[k]), ref, TAU_BF16, what=k, **kw)
