@@ -158,3 +158,48 @@ def test_grouped_srelu_mlp_parity(case):
     for k, ref in (("y", f["y"]), ("out", f["out"]), ("dh", b["dh"]), ("dp", b["dp"]), ("dw2", b["dw2"]),
                    ("dx", b["dx"]), ("dw1", b["dw1"])):
         assert_close(host_f64(got[k]), ref, TAU_BF16, what=k, **kw)
+
+
+def test_single_group_quantized_equals_dense_bitwise():
+    """One group spanning every token: the MXFP8 and FP8 (per-group current scaling) grouped
+    forward, dgrad and wgrad equal the dense MXFP8 / FP8 linear bit for bit (same operands, same
+    per-tile accumulation order)."""
+    from .gpu_paths import mx_layout, quant_fp8, quant_fp8_grouped, quant_mx, quant_mx_grouped
+    T, N, K = 384, 256, 256                                 # T a multiple of 128: no token padding
+    d = synth.dense(T, N, K, seed=24, outliers=True, w_std=1.0, dy_std=1.0)
+    X, W, DY = dev_bf16(d["x"]), dev_bf16(d["w"]), dev_bf16(d["dy"])
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    offs = torch.tensor([0, T], dtype=torch.int64, device="cuda")
+    lay = mx_layout(offs, T)
+    # MXFP8
+    qx, qw, qd = quant_mx(X), quant_mx(W), quant_mx(DY)
+    ref_f, ref_d, ref_w = torch.empty(T, N, **bf), torch.empty(T, K, **bf), torch.empty(N, K, **bf)
+    sge.linear_scale_add_fwd(sge.Operand.mxfp8(qx["q_row"], qx["s_row"]), sge.Operand.mxfp8(qw["q_row"], qw["s_row"]),
+                             ref_f, 0.5, accumulate=False)
+    sge.linear_scale_bwd(sge.Operand.mxfp8(qd["q_row"], qd["s_row"]), sge.Operand.mxfp8(qw["q_colT"], qw["s_colT"]),
+                         sge.Operand.mxfp8(qd["q_colT"], qd["s_colT"]), sge.Operand.mxfp8(qx["q_colT"], qx["s_colT"]),
+                         ref_d, ref_w, 0.5, 0.5)
+    out, dx, dw = torch.empty(T, N, **bf), torch.empty(T, K, **bf), torch.empty(1, N, K, **bf)
+    sge.grouped_linear_fwd_mxfp8(qx["q_row"], qx["s_row"], qw["q_row"][None], qw["s_row"][None], offs, out=out,
+                                 alpha=0.5)
+    sge.grouped_linear_dgrad_mxfp8(qd["q_row"], qd["s_row"], qw["q_colT"], qw["s_colT"], offs, alpha=0.5, dx=dx)
+    tx, td = quant_mx_grouped(X, lay), quant_mx_grouped(DY, lay)
+    sge.grouped_linear_wgrad_mxfp8(td["q_colT"], td["s_colT"], tx["q_colT"], tx["s_colT"], lay, dw, alpha=0.5)
+    torch.cuda.synchronize()
+    for a, b in ((out, ref_f), (dx, ref_d), (dw[0], ref_w)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # FP8 current scaling: one group's scale is the tensor's scale
+    fx, fw, fd = quant_fp8(X), quant_fp8(W), quant_fp8(DY)
+    gx, gw, gd = quant_fp8_grouped(X, 1, lay), quant_fp8_grouped(W, 1), quant_fp8_grouped(DY, 1, lay)
+    sge.linear_scale_add_fwd(sge.Operand.e4m3(fx["q"], fx["scale_inv"]), sge.Operand.e4m3(fw["q"], fw["scale_inv"]),
+                             ref_f, 0.5, accumulate=False)
+    sge.linear_scale_bwd(sge.Operand.e4m3(fd["q"], fd["scale_inv"]), sge.Operand.e4m3(fw["q_t"], fw["scale_inv"]),
+                         sge.Operand.e4m3(fd["q_t"], fd["scale_inv"]), sge.Operand.e4m3(fx["q_t"], fx["scale_inv"]),
+                         ref_d, ref_w, 0.5, 0.5)
+    sge.grouped_linear_fwd_fp8(gx["q"], gx["scale_inv"], gw["q"][None], gw["scale_inv"], offs, out, alpha=0.5)
+    sge.grouped_linear_dgrad_fp8(gd["q"], gd["scale_inv"], gw["q_t"], gw["scale_inv"], offs, alpha=0.5, dx=dx)
+    sge.grouped_linear_wgrad_fp8(gd["q_t"], gd["scale_inv"], gx["q_t"], gx["scale_inv"], lay, dw, alpha=0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(gx["scale_inv"], fx["scale_inv"]) and torch.equal(gx["q"], fx["q"])
+    for a, b in ((out, ref_f), (dx, ref_d), (dw[0], ref_w)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
