@@ -214,8 +214,8 @@ def build_grouped(torch, sge, wl, inp):
     if wl["fmt"] == "mxfp8":
         return build_grouped_mx(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, dh, dp, dw2, dx, dw1, ws)
     if wl["fmt"] == "fp8":
-        return build_grouped_fp8(torch, sge, X, W1, W2, DOUT, P, splits, offs, h, out, dh, dp, dw2, dx, dw1, ws,
-                                 flops)
+        return build_grouped_fp8(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, dh, dp, dw2, dx, dw1,
+                                 ws, flops)
     launches = [
         ("offsets", lambda: sge.splits_to_offsets(splits, [1, H], offs)),
         ("fc1_fwd", lambda: sge.grouped_linear_fwd(X, W1, base, y, epilogue=fwd_epi, probs=P, preact=h)),
@@ -232,11 +232,15 @@ def build_grouped(torch, sge, wl, inp):
 def build_grouped_mx(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, dh, dp, dw2, dx, dw1, ws):
     """The grouped MLP on MXFP8 operands: every GEMM operand quantized each step, blocked along
     that GEMM's contraction (rowwise for the forward and the dgrads, W's columnwise copy for
-    the dgrads, per-group token blocks for the wgrads). fc1's scaled SwiGLU emits its output
+    the dgrads, per-group token blocks for the wgrads). fc1's scaled activation emits its output
     as MXFP8 for fc2, and fc2's dgrad emits dh as MXFP8 for fc1's dgrad."""
     T, H = X.shape
     G, N1, _ = W1.shape
-    F = N1 // 2
+    swiglu = wl.get("act", "swiglu") == "swiglu"
+    F = N1 // 2 if swiglu else N1
+    fwd_epi = sge.EPI_SCALED_SWIGLU if swiglu else sge.EPI_SCALED_SRELU
+    bwd_epi = sge.EPI_DSCALED_SWIGLU if swiglu else sge.EPI_DSCALED_SRELU
+    dact = "fc2_dgrad_dswiglu" if swiglu else "fc2_dgrad_dsrelu"
     bwd = "bwd" in wl["passes"]
     u8 = dict(dtype=torch.uint8, device="cuda")
     base = offs[0]
@@ -256,7 +260,7 @@ def build_grouped_mx(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, d
             ("quant_w2", lambda: sge.quantize_mxfp8(W2f, q_row=qw2, s_row=sw2)),
             ("fc1_fwd", lambda: sge.grouped_linear_fwd_mxfp8(
                 qx, sx, qw1.view(G, N1, H), sw1.view(G, N1, H // 32), base, out=None,
-                epilogue=sge.EPI_SCALED_SWIGLU, probs=P, preact=h, out_q=qy, out_s=sy)),
+                epilogue=fwd_epi, probs=P, preact=h, out_q=qy, out_s=sy)),
             ("fc2_fwd", lambda: sge.grouped_linear_fwd_mxfp8(qy, sy, qw2.view(G, H, F), sw2.view(G, H, F // 32),
                                                              base, out=out)),
         ], flops, hbm
@@ -272,7 +276,7 @@ def build_grouped_mx(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, d
     qdT, sdT = torch.empty(H, ld, **u8), torch.empty(H, ld // 32, **u8)
     qdh, sdh = torch.empty(T, N1, **u8), torch.empty(T, N1 // 32, **u8)
     qdhT, sdhT = torch.empty(N1, ld, **u8), torch.empty(N1, ld // 32, **u8)
-    flops.update({"fc2_dgrad_dswiglu": 2 * T * H * F, "fc2_wgrad": 2 * T * H * F, "fc1_dgrad": 2 * T * N1 * H,
+    flops.update({dact: 2 * T * H * F, "fc2_wgrad": 2 * T * H * F, "fc1_dgrad": 2 * T * N1 * H,
                   "fc1_wgrad": 2 * T * N1 * H})
     # algorithmic bytes: bf16 read, E4M3 written per copy, one E8M0 byte per 32 (padding not counted)
     hbm = {"quant_x": T * H * 4 + T * H // 16, "quant_w1": G * N1 * H * 4 + G * N1 * H // 16,
@@ -286,13 +290,13 @@ def build_grouped_mx(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, d
         ("quant_w2", lambda: sge.quantize_mxfp8(W2f, q_row=qw2, s_row=sw2, q_colT=qw2T, s_colT=sw2T)),
         ("fc1_fwd", lambda: sge.grouped_linear_fwd_mxfp8(
             qx, sx, qw1.view(G, N1, H), sw1.view(G, N1, H // 32), base, out=y,
-            epilogue=sge.EPI_SCALED_SWIGLU, probs=P, preact=h, out_q=qy, out_s=sy)),
+            epilogue=fwd_epi, probs=P, preact=h, out_q=qy, out_s=sy)),
         ("quant_y", lambda: sge.quantize_mxfp8_grouped(y, lay, qyT, syT)),
         ("fc2_fwd", lambda: sge.grouped_linear_fwd_mxfp8(qy, sy, qw2.view(G, H, F), sw2.view(G, H, F // 32),
                                                          base, out=out)),
         ("quant_dout", lambda: sge.quantize_mxfp8_grouped(DOUT, lay, qdT, sdT, q_row=qd, s_row=sd)),
-        ("fc2_dgrad_dswiglu", lambda: sge.grouped_linear_dgrad_mxfp8(
-            qd, sd, qw2T, sw2T, base, epilogue=sge.EPI_DSCALED_SWIGLU, preact=h, probs=P, dact=dh, dprobs=dp,
+        (dact, lambda: sge.grouped_linear_dgrad_mxfp8(
+            qd, sd, qw2T, sw2T, base, epilogue=bwd_epi, preact=h, probs=P, dact=dh, dprobs=dp,
             dact_q=qdh, dact_s=sdh, workspace=ws)),
         ("fc2_wgrad", lambda: sge.grouped_linear_wgrad_mxfp8(qdT, sdT, qyT, syT, lay, dw2)),
         ("quant_dh", lambda: sge.quantize_mxfp8_grouped(dh, lay, qdhT, sdhT)),
@@ -302,14 +306,18 @@ def build_grouped_mx(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, d
     return launches, flops, hbm
 
 
-def build_grouped_fp8(torch, sge, X, W1, W2, DOUT, P, splits, offs, h, out, dh, dp, dw2, dx, dw1, ws, flops):
+def build_grouped_fp8(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, dh, dp, dw2, dx, dw1, ws, flops):
     """The grouped MLP on E4M3 operands with current scaling per group: each step quantizes x,
     y, dout and dh per token group and W1, W2 per expert (an amax pass, then one pass writing
     the rowwise bytes and the transposed copy), and runs the six grouped GEMMs with per-group
     scales."""
     T, H = X.shape
     G, N1, _ = W1.shape
-    F = N1 // 2
+    swiglu = wl.get("act", "swiglu") == "swiglu"
+    F = N1 // 2 if swiglu else N1
+    fwd_epi = sge.EPI_SCALED_SWIGLU if swiglu else sge.EPI_SCALED_SRELU
+    bwd_epi = sge.EPI_DSCALED_SWIGLU if swiglu else sge.EPI_DSCALED_SRELU
+    dact = "fc2_dgrad_dswiglu" if swiglu else "fc2_dgrad_dsrelu"
     base = offs[0]
     u8 = dict(dtype=torch.uint8, device="cuda")
     ld = sge.mx_token_capacity(T, G)
@@ -344,14 +352,14 @@ def build_grouped_fp8(torch, sge, X, W1, W2, DOUT, P, splits, offs, h, out, dh, 
         ("quant_w1", quant(W1f, qw1, None)),
         ("quant_w2", quant(W2f, qw2, None)),
         ("fc1_fwd", lambda: sge.grouped_linear_fwd_fp8(qx["q"], sinv(qx), qw1["q"].view(G, N1, H), sinv(qw1), base,
-                                                       y, epilogue=sge.EPI_SCALED_SWIGLU, probs=P, preact=h,
+                                                       y, epilogue=fwd_epi, probs=P, preact=h,
                                                        out_amax=amax_y)),
         ("quant_y", quant(y, qy, lay, amax_y)),
         ("fc2_fwd", lambda: sge.grouped_linear_fwd_fp8(qy["q"], sinv(qy), qw2["q"].view(G, H, F), sinv(qw2), base,
                                                        out)),
         ("quant_dout", quant(DOUT, qd, lay)),
-        ("fc2_dgrad_dswiglu", lambda: sge.grouped_linear_dgrad_fp8(
-            qd["q"], sinv(qd), qw2["q_t"], sinv(qw2), base, epilogue=sge.EPI_DSCALED_SWIGLU, preact=h, probs=P,
+        (dact, lambda: sge.grouped_linear_dgrad_fp8(
+            qd["q"], sinv(qd), qw2["q_t"], sinv(qw2), base, epilogue=bwd_epi, preact=h, probs=P,
             dact=dh, dprobs=dp, dact_amax=amax_dh, workspace=ws)),
         ("fc2_wgrad", lambda: sge.grouped_linear_wgrad_fp8(qd["q_t"], sinv(qd), qy["q_t"], sinv(qy), lay, dw2)),
         ("quant_dh", quant(dh, qdh, lay, amax_dh)),
@@ -413,41 +421,44 @@ def cpu_baseline(wl, inp, target_s):
     elif wl["fmt"] == "fp8":
         T = inp["x"].shape[0]
         tok = 256
+        act = wl.get("act", "swiglu")
         while True:
             t0 = time.perf_counter()
             # first `tok` tokens, all routed to expert 0 (its weights only are quantized)
             b1 = np.array([0, tok], np.int64)
-            f = grouped.grouped_mlp_fwd_fp8(inp["x"][:tok], inp["w1"][:1], inp["w2"][:1], inp["p"][:tok], b1)
+            f = grouped.grouped_mlp_fwd_fp8(inp["x"][:tok], inp["w1"][:1], inp["w2"][:1], inp["p"][:tok], b1, act)
             grouped.grouped_mlp_bwd_fp8(inp["x"][:tok], inp["w1"][:1], inp["w2"][:1], inp["p"][:tok], b1,
-                                        inp["dout"][:tok], fwd=f)
+                                        inp["dout"][:tok], fwd=f, act=act)
             dt = time.perf_counter() - t0
             if dt >= target_s / 4 or tok >= T:
                 break
             tok = min(T, tok * 4)
         H = inp["x"].shape[1]
         N1 = inp["w1"].shape[1]
-        flops = 3 * (2 * tok * N1 * H + 2 * tok * H * (N1 // 2))
+        flops = 3 * (2 * tok * N1 * H + 2 * tok * H * (N1 // 2 if act == "swiglu" else N1))
         sample = (f"first {tok} of {T} tokens through the FP8 (per-group current scaling) grouped MLP forward + "
                   "backward with one expert (quantization of that expert's weights included)")
     elif wl["fmt"] == "mxfp8":
         T = inp["x"].shape[0]
         tok = 256
         bwd = "bwd" in wl["passes"]
+        act = wl.get("act", "swiglu")
         while True:
             t0 = time.perf_counter()
             # first `tok` tokens, all routed to expert 0 (its weights only are quantized)
             b1 = np.array([0, tok], np.int64)
-            f = grouped.grouped_mlp_fwd_mxfp8(inp["x"][:tok], inp["w1"][:1], inp["w2"][:1], inp["p"][:tok], b1)
+            f = grouped.grouped_mlp_fwd_mxfp8(inp["x"][:tok], inp["w1"][:1], inp["w2"][:1], inp["p"][:tok], b1,
+                                              act)
             if bwd:
                 grouped.grouped_mlp_bwd_mxfp8(inp["x"][:tok], inp["w1"][:1], inp["w2"][:1], inp["p"][:tok], b1,
-                                              inp["dout"][:tok], fwd=f)
+                                              inp["dout"][:tok], fwd=f, act=act)
             dt = time.perf_counter() - t0
             if dt >= target_s / 4 or tok >= T:
                 break
             tok = min(T, tok * 4)
         H = inp["x"].shape[1]
         N1 = inp["w1"].shape[1]
-        flops = (3 if bwd else 1) * (2 * tok * N1 * H + 2 * tok * H * (N1 // 2))
+        flops = (3 if bwd else 1) * (2 * tok * N1 * H + 2 * tok * H * (N1 // 2 if act == "swiglu" else N1))
         sample = (f"first {tok} of {T} tokens through the MXFP8 grouped MLP {'forward + backward' if bwd else 'forward'}"
                   " with one expert (quantization of that expert's weights included)")
     else:

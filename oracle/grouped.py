@@ -144,7 +144,7 @@ def grouped_mlp_bwd(dout, x, w1, w2, p, base, h=None, y=None, act="swiglu"):
     return {"gy": gy, "dh": dh, "dp": dp, "dw2": dw2, "dx": dx, "dw1": dw1}
 
 
-def grouped_mlp_fwd_mxfp8(x_bits, w1_bits, w2_bits, p, base):
+def grouped_mlp_fwd_mxfp8(x_bits, w1_bits, w2_bits, p, base, act="swiglu"):
     """Grouped MLP forward on MXFP8 operands, with the activation quantized for fc2.
 
     "Activation + GroupedLinear Fusion for MOE and other MOE optimizations" (Description:
@@ -170,7 +170,7 @@ def grouped_mlp_fwd_mxfp8(x_bits, w1_bits, w2_bits, p, base):
     w1_hat = mx_dequantize(*mxfp8_rowwise(w1_bits.reshape(G * N1, H))).reshape(G, N1, H)
     w2_hat = mx_dequantize(*mxfp8_rowwise(w2_bits.reshape(G * H, F))).reshape(G, H, F)
     h = grouped_linear_fwd(x_hat, w1_hat, base)
-    y = scaled_swiglu_fwd(h, p)
+    y = _ACTS[act][0](h, p)
     y_bits = f64_to_bf16(y)
     y_q, y_s = mxfp8_rowwise(y_bits)
     out = grouped_linear_fwd(mx_dequantize(y_q, y_s), w2_hat, base)
@@ -215,7 +215,7 @@ def grouped_linear_wgrad_mxfp8(dy_bits, x_bits, base, alpha=1.0, align=MX_TOKEN_
     return out
 
 
-def grouped_mlp_bwd_mxfp8(x_bits, w1_bits, w2_bits, p, base, dout_bits, fwd=None):
+def grouped_mlp_bwd_mxfp8(x_bits, w1_bits, w2_bits, p, base, dout_bits, fwd=None, act="swiglu"):
     """Backward of ``grouped_mlp_fwd_mxfp8`` on MXFP8 operands, given dL/dout (bf16 bits).
 
     "Activation + GroupedLinear Fusion for MOE and other MOE optimizations" (Sequence
@@ -233,10 +233,10 @@ def grouped_mlp_bwd_mxfp8(x_bits, w1_bits, w2_bits, p, base, dout_bits, fwd=None
     Returns gy, dh (fp64), dh_bits, dh_q, dh_s (the rowwise MXFP8 of dh_bits), dp, dw2, dx, dw1.
     """
     if fwd is None:
-        fwd = grouped_mlp_fwd_mxfp8(x_bits, w1_bits, w2_bits, p, base)
+        fwd = grouped_mlp_fwd_mxfp8(x_bits, w1_bits, w2_bits, p, base, act)
     h_saved = bf16_to_f64(f64_to_bf16(fwd["h"]))
     gy = grouped_linear_dgrad_mxfp8(dout_bits, w2_bits, base)
-    dh, dp = scaled_swiglu_bwd(gy, h_saved, p)
+    dh, dp = _ACTS[act][1](gy, h_saved, p)
     dh_bits = f64_to_bf16(dh)
     dh_q, dh_s = mxfp8_rowwise(dh_bits)
     dw2 = grouped_linear_wgrad_mxfp8(dout_bits, fwd["y_bits"], base)
@@ -265,7 +265,7 @@ def _fp8_experts_hat(w_bits):
     return _fp8_groups_hat(w_bits.reshape(G * N, K), c).reshape(G, N, K)
 
 
-def grouped_mlp_fwd_fp8(x_bits, w1_bits, w2_bits, p, base):
+def grouped_mlp_fwd_fp8(x_bits, w1_bits, w2_bits, p, base, act="swiglu"):
     """Grouped MLP forward on FP8 operands with per-group current scaling.
 
     Every GEMM operand is E4M3 with one scale per group ("Activation + GroupedLinear Fusion for
@@ -278,24 +278,24 @@ def grouped_mlp_fwd_fp8(x_bits, w1_bits, w2_bits, p, base):
     T = np.asarray(x_bits).shape[0]
     c, _ = mx_group_layout(base, T)
     h = grouped_linear_fwd(_fp8_groups_hat(x_bits, c), _fp8_experts_hat(w1_bits), base)
-    y = scaled_swiglu_fwd(h, p)
+    y = _ACTS[act][0](h, p)
     y_bits = f64_to_bf16(y)
     out = grouped_linear_fwd(_fp8_groups_hat(y_bits, c), _fp8_experts_hat(w2_bits), base)
     return {"h": h, "y": y, "y_bits": y_bits, "out": out}
 
 
-def grouped_mlp_bwd_fp8(x_bits, w1_bits, w2_bits, p, base, dout_bits, fwd=None):
+def grouped_mlp_bwd_fp8(x_bits, w1_bits, w2_bits, p, base, dout_bits, fwd=None, act="swiglu"):
     """Backward of ``grouped_mlp_fwd_fp8``: dout, dh, x, y and every W_g are E4M3 with one
     current-scaling scale per group; h is the forward's bf16 pre-activation and dh is rounded
     to bf16 before it is quantized. Returns gy, dh (fp64), dh_bits, dp, dw2, dx, dw1."""
     if fwd is None:
-        fwd = grouped_mlp_fwd_fp8(x_bits, w1_bits, w2_bits, p, base)
+        fwd = grouped_mlp_fwd_fp8(x_bits, w1_bits, w2_bits, p, base, act)
     T = np.asarray(x_bits).shape[0]
     c, _ = mx_group_layout(base, T)
     dout_hat = _fp8_groups_hat(dout_bits, c)
     w1_hat, w2_hat = _fp8_experts_hat(w1_bits), _fp8_experts_hat(w2_bits)
     gy = grouped_linear_dgrad(dout_hat, w2_hat, base)
-    dh, dp = scaled_swiglu_bwd(gy, bf16_to_f64(f64_to_bf16(fwd["h"])), p)
+    dh, dp = _ACTS[act][1](gy, bf16_to_f64(f64_to_bf16(fwd["h"])), p)
     dh_bits = f64_to_bf16(dh)
     dh_hat = _fp8_groups_hat(dh_bits, c)
     dw2 = grouped_linear_wgrad(dout_hat, _fp8_groups_hat(fwd["y_bits"], c), base)

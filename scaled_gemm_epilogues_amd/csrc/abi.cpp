@@ -345,15 +345,17 @@ sge_status sge_grouped_linear_fwd_mxfp8(const void* x_q, const void* x_s, const 
                                         int32_t epilogue, const float* probs, void* out, void* preact, void* out_q,
                                         void* out_s, hipStream_t stream) {
   if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_mxfp8: bad sizes");
-  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_SCALED_SWIGLU)
+  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_SCALED_SWIGLU && epilogue != SGE_EPI_SCALED_SRELU)
     return fail(SGE_ERR_ARG, "grouped_linear_fwd_mxfp8: epilogue %d not allowed", epilogue);
   const bool swiglu = epilogue == SGE_EPI_SCALED_SWIGLU;
+  const bool act = epilogue != SGE_EPI_NONE;                      // a scaled activation in the epilogue
   if (!x_q || !x_s || !w_q || !w_s || !offsets) return fail(SGE_ERR_NULL, "grouped_linear_fwd_mxfp8: NULL pointer");
   if ((out_q == nullptr) != (out_s == nullptr))
     return fail(SGE_ERR_NULL, "grouped_linear_fwd_mxfp8: out_q and out_s go together");
-  if (out_q && !swiglu) return fail(SGE_ERR_ARG, "grouped_linear_fwd_mxfp8: a quantized output needs the SwiGLU epilogue");
+  if (out_q && !act) return fail(SGE_ERR_ARG, "grouped_linear_fwd_mxfp8: a quantized output needs an activation epilogue");
   if (!out && !out_q) return fail(SGE_ERR_NULL, "grouped_linear_fwd_mxfp8: no output");
-  if (swiglu && !probs) return fail(SGE_ERR_NULL, "grouped_linear_fwd_mxfp8: probs is NULL");
+  if (act && !probs) return fail(SGE_ERR_NULL, "grouped_linear_fwd_mxfp8: probs is NULL");
+  if (out_q && N % 32) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_mxfp8: an MXFP8 output needs N %% 32 == 0");
   if (K % 128) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_mxfp8: K must be a multiple of 128 (got %lld)", (long long)K);
   if (N % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_mxfp8: N must be a multiple of 8");
   if (swiglu && N % 256) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_mxfp8: SwiGLU needs N %% 256 == 0");
@@ -556,33 +558,34 @@ sge_status sge_grouped_linear_dgrad_mxfp8(const void* dy_q, const void* dy_s, co
                                           void* dx, void* dact, float* dprobs, void* dact_q, void* dact_s,
                                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_mxfp8: bad sizes");
-  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_DSCALED_SWIGLU)
+  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_DSCALED_SWIGLU && epilogue != SGE_EPI_DSCALED_SRELU)
     return fail(SGE_ERR_ARG, "grouped_linear_dgrad_mxfp8: epilogue %d not allowed", epilogue);
-  const bool swiglu = epilogue == SGE_EPI_DSCALED_SWIGLU;
+  const bool swiglu = epilogue != SGE_EPI_NONE;                  // an activation backward in the epilogue
+  const int64_t hw = epilogue == SGE_EPI_DSCALED_SWIGLU ? 2 * K : K;   // pre-activation / dact width
   if (!dy_q || !dy_s || !w_q || !w_s || !offsets) return fail(SGE_ERR_NULL, "grouped_linear_dgrad_mxfp8: NULL pointer");
   if ((dact_q == nullptr) != (dact_s == nullptr))
     return fail(SGE_ERR_NULL, "grouped_linear_dgrad_mxfp8: dact_q and dact_s go together");
   if (swiglu) {
-    if (!preact || !probs || !dprobs) return fail(SGE_ERR_NULL, "grouped_linear_dgrad_mxfp8: SwiGLU backward needs preact, probs and dprobs");
+    if (!preact || !probs || !dprobs) return fail(SGE_ERR_NULL, "grouped_linear_dgrad_mxfp8: an activation backward needs preact, probs and dprobs");
     if (!dact && !dact_q) return fail(SGE_ERR_NULL, "grouped_linear_dgrad_mxfp8: no output");
   } else {
     if (!dx) return fail(SGE_ERR_NULL, "grouped_linear_dgrad_mxfp8: dx is NULL");
-    if (dact_q) return fail(SGE_ERR_ARG, "grouped_linear_dgrad_mxfp8: a quantized output needs the SwiGLU backward");
+    if (dact_q) return fail(SGE_ERR_ARG, "grouped_linear_dgrad_mxfp8: a quantized output needs an activation backward");
   }
   if (N % 128) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_mxfp8: N must be a multiple of 128 (got %lld)", (long long)N);
   if (K % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_mxfp8: K must be a multiple of 8");
-  if (swiglu && K % 32) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_mxfp8: SwiGLU backward needs K %% 32 == 0");
+  if (swiglu && K % 32) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_mxfp8: an activation backward needs K %% 32 == 0");
   if (!aligned16(dy_q) || !aligned16(dy_s) || !aligned16(w_q) || !aligned16(w_s) || (dx && !aligned16(dx)) ||
       (preact && !aligned16(preact)) || (dact && !aligned16(dact)) || (dact_q && !aligned16(dact_q)))
     return fail(SGE_ERR_ALIGN, "grouped_linear_dgrad_mxfp8: pointers must be 16-byte aligned");
   const int64_t GN = (int64_t)G * N;
   const Range in[5] = {range_of(dy_q, T, N, N, 1), range_of(dy_s, T, N / 32, N / 32, 1), range_of(w_q, K, GN, GN, 1),
                        range_of(w_s, K, GN / 32, GN / 32, 1),
-                       swiglu ? range_of(preact, T, 2 * K, 2 * K, 2) : Range{0, 0}};
+                       swiglu ? range_of(preact, T, hw, hw, 2) : Range{0, 0}};
   const Range outs[4] = {(dx && !swiglu) ? range_of(dx, T, K, K, 2) : Range{0, 0},
-                         (swiglu && dact) ? range_of(dact, T, 2 * K, 2 * K, 2) : Range{0, 0},
-                         dact_q ? range_of(dact_q, T, 2 * K, 2 * K, 1) : Range{0, 0},
-                         dact_s ? range_of(dact_s, T, 2 * K / 32, 2 * K / 32, 1) : Range{0, 0}};
+                         (swiglu && dact) ? range_of(dact, T, hw, hw, 2) : Range{0, 0},
+                         dact_q ? range_of(dact_q, T, hw, hw, 1) : Range{0, 0},
+                         dact_s ? range_of(dact_s, T, hw / 32, hw / 32, 1) : Range{0, 0}};
   for (int a = 0; a < 4; ++a) {
     for (const Range& i : in)
       if (overlap(outs[a], i)) return fail(SGE_ERR_ALIAS, "grouped_linear_dgrad_mxfp8: outputs overlap inputs");
@@ -619,14 +622,14 @@ sge_status sge_grouped_linear_dgrad_mxfp8(const void* dy_q, const void* dy_s, co
   if (swiglu) {
     p.probs = probs;
     p.aux = const_cast<uint16_t*>(static_cast<const uint16_t*>(preact));
-    p.ld_aux = 2 * K;
+    p.ld_aux = hw;
     p.aux_out = static_cast<uint16_t*>(dact);
-    p.ld_aux_out = 2 * K;
+    p.ld_aux_out = hw;
     p.dp_part = static_cast<float*>(workspace);
     p.F = K;
     p.q_out = static_cast<uint8_t*>(dact_q);
     p.s_out = static_cast<uint8_t*>(dact_s);
-    p.ld_q = 2 * K;
+    p.ld_q = hw;
   }
   hipError_t e = sge::launch_grouped_dgrad_mx(p, epilogue, stream);
   if (e != hipSuccess) return hip_status(e, "grouped dgrad mxfp8 launch");
@@ -733,12 +736,13 @@ sge_status sge_grouped_linear_fwd_fp8(const void* x_q, const float* x_sinv, cons
                                       int32_t epilogue, const float* probs, void* out, void* preact, float* out_amax,
                                       hipStream_t stream) {
   if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_fp8: bad sizes");
-  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_SCALED_SWIGLU)
+  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_SCALED_SWIGLU && epilogue != SGE_EPI_SCALED_SRELU)
     return fail(SGE_ERR_ARG, "grouped_linear_fwd_fp8: epilogue %d not allowed", epilogue);
   const bool swiglu = epilogue == SGE_EPI_SCALED_SWIGLU;
+  const bool act = epilogue != SGE_EPI_NONE;
   if (!x_q || !x_sinv || !w_q || !w_sinv || !offsets || !out) return fail(SGE_ERR_NULL, "grouped_linear_fwd_fp8: NULL pointer");
-  if (swiglu && !probs) return fail(SGE_ERR_NULL, "grouped_linear_fwd_fp8: probs is NULL");
-  if (out_amax && !swiglu) return fail(SGE_ERR_ARG, "grouped_linear_fwd_fp8: out_amax needs the SwiGLU epilogue");
+  if (act && !probs) return fail(SGE_ERR_NULL, "grouped_linear_fwd_fp8: probs is NULL");
+  if (out_amax && !act) return fail(SGE_ERR_ARG, "grouped_linear_fwd_fp8: out_amax needs an activation epilogue");
   if (K % 16) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_fp8: K must be a multiple of 16");
   if (N % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_fp8: N must be a multiple of 8");
   if (swiglu && N % 256) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_fp8: SwiGLU needs N %% 256 == 0");
@@ -791,14 +795,15 @@ sge_status sge_grouped_linear_dgrad_fp8(const void* dy_q, const float* dy_sinv, 
                                         void* dx, void* dact, float* dprobs, float* dact_amax, void* workspace,
                                         size_t workspace_bytes, hipStream_t stream) {
   if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_fp8: bad sizes");
-  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_DSCALED_SWIGLU)
+  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_DSCALED_SWIGLU && epilogue != SGE_EPI_DSCALED_SRELU)
     return fail(SGE_ERR_ARG, "grouped_linear_dgrad_fp8: epilogue %d not allowed", epilogue);
-  const bool swiglu = epilogue == SGE_EPI_DSCALED_SWIGLU;
+  const bool swiglu = epilogue != SGE_EPI_NONE;                  // an activation backward in the epilogue
+  const int64_t hw = epilogue == SGE_EPI_DSCALED_SWIGLU ? 2 * K : K;   // pre-activation / dact width
   if (!dy_q || !dy_sinv || !w_qT || !w_sinv || !offsets) return fail(SGE_ERR_NULL, "grouped_linear_dgrad_fp8: NULL pointer");
   if (swiglu && (!preact || !probs || !dact || !dprobs))
-    return fail(SGE_ERR_NULL, "grouped_linear_dgrad_fp8: SwiGLU backward needs preact, probs, dact and dprobs");
+    return fail(SGE_ERR_NULL, "grouped_linear_dgrad_fp8: an activation backward needs preact, probs, dact and dprobs");
   if (!swiglu && !dx) return fail(SGE_ERR_NULL, "grouped_linear_dgrad_fp8: dx is NULL");
-  if (dact_amax && !swiglu) return fail(SGE_ERR_ARG, "grouped_linear_dgrad_fp8: dact_amax needs the SwiGLU backward");
+  if (dact_amax && !swiglu) return fail(SGE_ERR_ARG, "grouped_linear_dgrad_fp8: dact_amax needs an activation backward");
   if (N % 16) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_fp8: N must be a multiple of 16");
   if (K % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_fp8: K must be a multiple of 8");
   if (!aligned16(dy_q) || !aligned16(w_qT) || (dx && !aligned16(dx)) || (preact && !aligned16(preact)) ||
@@ -806,8 +811,8 @@ sge_status sge_grouped_linear_dgrad_fp8(const void* dy_q, const float* dy_sinv, 
     return fail(SGE_ERR_ALIGN, "grouped_linear_dgrad_fp8: pointers must be 16-byte aligned");
   const int64_t GN = (int64_t)G * N;
   const Range in[3] = {range_of(dy_q, T, N, N, 1), range_of(w_qT, K, GN, GN, 1),
-                       swiglu ? range_of(preact, T, 2 * K, 2 * K, 2) : Range{0, 0}};
-  const Range out = swiglu ? range_of(dact, T, 2 * K, 2 * K, 2) : range_of(dx, T, K, K, 2);
+                       swiglu ? range_of(preact, T, hw, hw, 2) : Range{0, 0}};
+  const Range out = swiglu ? range_of(dact, T, hw, hw, 2) : range_of(dx, T, K, K, 2);
   const Range ram = dact_amax ? range_of(dact_amax, 1, G, G, 4) : Range{0, 0};
   for (const Range& i : in)
     if (overlap(out, i) || overlap(ram, i)) return fail(SGE_ERR_ALIAS, "grouped_linear_dgrad_fp8: output overlaps an input");
@@ -842,9 +847,9 @@ sge_status sge_grouped_linear_dgrad_fp8(const void* dy_q, const float* dy_sinv, 
   if (swiglu) {
     p.probs = probs;
     p.aux = const_cast<uint16_t*>(static_cast<const uint16_t*>(preact));
-    p.ld_aux = 2 * K;
+    p.ld_aux = hw;
     p.aux_out = static_cast<uint16_t*>(dact);
-    p.ld_aux_out = 2 * K;
+    p.ld_aux_out = hw;
     p.dp_part = static_cast<float*>(workspace);
     p.F = K;
     p.amax_out = dact_amax;

@@ -626,7 +626,16 @@ void gemm_kernel(const GemmParams p) {
     // pre-activation v (bf16) to aux, at the same offsets (ld_aux == ldc).
     constexpr bool kSR = EPI == E_SRELU;
     static_assert(BM == 2 * WM && A_BYTES + B_BYTES == 64 * BN * 4, "epilogue staging assumes 2 wave rows");
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(cptr + m0 * p.ldc, rows_left * p.ldc * 2);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(cptr ? cptr + m0 * p.ldc : cptr, cptr ? rows_left * p.ldc * 2 : 0);
+    // E_SRELU with q_out: y also as MXFP8 rowwise (ld_q == ldc, so byte offsets are offs / 2; four
+    // adjacent lanes hold a 32-column block); E4M3: the group's amax of y (as in E_SWIGLU).
+    const bool mxq = kSR && p.q_out != nullptr;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(mxq ? p.q_out + m0 * p.ld_q : p.q_out, mxq ? rows_left * p.ld_q : 0);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(mxq ? p.s_out + m0 * (p.ld_q / 32) : p.s_out,
+                                                mxq ? rows_left * (p.ld_q / 32) : 0);
+    constexpr bool kAmax = kSR && FMT == F_E4M3;
+    float amax_acc = 0.0f;
+    if (kAmax && threadIdx.x == 0) amax_slot = 0;
     constexpr int kChunks = BN / 8;                        // 8-column chunks per row
     constexpr int kIters = 128 * kChunks / (NWAVES * 64);  // chunks per thread per pass
     float* stage = reinterpret_cast<float*>(wm ? lds1 : lds0);
@@ -697,8 +706,29 @@ void gemm_kernel(const GemmParams p) {
         const v4i w = {(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3]), (int)pack_bf16x2(v[4], v[5]),
                        (int)pack_bf16x2(v[6], v[7])};
         __builtin_amdgcn_raw_buffer_store_b128(w, rc, offs[pass][it], 0, 0);
+        if constexpr (kSR) {
+          if constexpr (kAmax) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax_acc = fmaxf(amax_acc, fabsf(v[e]));
+          }
+          if (mxq) {
+            const int id = it * NWAVES * 64 + threadIdx.x;
+            const int c = id % kChunks;
+            int e8;
+            const v2i qv = mx_quant_lane8(w, e8);          // every lane takes part
+            const int o = offs[pass][it];
+            __builtin_amdgcn_raw_buffer_store_b64(qv, rq, o == (int)kOOB ? (int)kOOB : o >> 1, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b8((char)e8, rs, (o == (int)kOOB || (c & 3)) ? (int)kOOB : o >> 6, 0, 0);
+          }
+        }
       }
       if (pass == 0) __syncthreads();                      // stage reused by the second pass
+    }
+    if constexpr (kAmax) {
+      if (p.amax_out) {
+        amax_to_slot(&amax_slot, amax_acc);
+        slot_to_group(&amax_slot, p.amax_out, grp);
+      }
     }
   } else if constexpr (EPI == E_SWIGLU) {
     // Staged like E_STORE: alpha*acc (each wave column holds WN/2 gate columns a, then the
@@ -927,19 +957,23 @@ void gemm_kernel(const GemmParams p) {
           if (want_amax) {                                 // per item: no register lives across items
             float mi = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) mi = fmaxf(mi, fmaxf(fabsf(da[e]), fabsf(db[e])));
+            for (int e = 0; e < 8; ++e) mi = fmaxf(mi, fmaxf(fabsf(da[e]), fabsf(db[e])));   // db = 0 for SReLU
             amax_to_slot(&amax_slot, mi);
           }
         }
         if (mxq) {
-          int ea, eb;
-          const v2i qa = mx_quant_lane8(va, ea), qb = mx_quant_lane8(vb, eb);
+          int ea;
+          const v2i qa = mx_quant_lane8(va, ea);
           const int oq = od[ib] == (int)kOOB ? (int)kOOB : od[ib] >> 1;
           const int os = (od[ib] == (int)kOOB || (c & 3)) ? (int)kOOB : od[ib] >> 6;
           __builtin_amdgcn_raw_buffer_store_b64(qa, rq, oq, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b64(qb, rq, oq + fb / 2, 0, 0);
           __builtin_amdgcn_raw_buffer_store_b8((char)ea, rs, os, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b8((char)eb, rs, os + fb / 64, 0, 0);
+          if constexpr (!kSR) {
+            int eb;
+            const v2i qb = mx_quant_lane8(vb, eb);
+            __builtin_amdgcn_raw_buffer_store_b64(qb, rq, oq + fb / 2, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b8((char)eb, rs, os + fb / 64, 0, 0);
+          }
         }
         // the row's 32 chunks are lanes c = 0..31 of one half-wave: fixed-order tree sum
 #pragma unroll
@@ -1009,6 +1043,7 @@ hipError_t launch_grouped_fwd(const GemmParams& p, int epilogue, hipStream_t s) 
 
 hipError_t launch_grouped_fwd_mx(const GemmParams& p, int epilogue, hipStream_t s) {
   if (epilogue == E_SWIGLU) return launch_tile<F_MX, true, true, E_SWIGLU, S_GROUP_M>(p, s);
+  if (epilogue == E_SRELU) return launch_tile<F_MX, true, true, E_SRELU, S_GROUP_M>(p, s);
   return launch_tile<F_MX, true, true, E_STORE, S_GROUP_M>(p, s);
 }
 
@@ -1024,11 +1059,13 @@ hipError_t launch_grouped_wgrad(const GemmParams& p, hipStream_t s) {
 
 hipError_t launch_grouped_fwd_fp8(const GemmParams& p, int epilogue, hipStream_t s) {
   if (epilogue == E_SWIGLU) return launch_tile<F_E4M3, true, true, E_SWIGLU, S_GROUP_M>(p, s);
+  if (epilogue == E_SRELU) return launch_tile<F_E4M3, true, true, E_SRELU, S_GROUP_M>(p, s);
   return launch_tile<F_E4M3, true, true, E_STORE, S_GROUP_M>(p, s);
 }
 
 hipError_t launch_grouped_dgrad_fp8(const GemmParams& p, int epilogue, hipStream_t s) {
   if (epilogue == E_DSWIGLU) return launch_tile<F_E4M3, true, true, E_DSWIGLU, S_GROUP_M>(p, s);
+  if (epilogue == E_DSRELU) return launch_tile<F_E4M3, true, true, E_DSRELU, S_GROUP_M>(p, s);
   return launch_tile<F_E4M3, true, true, E_STORE, S_GROUP_M>(p, s);
 }
 
@@ -1038,6 +1075,7 @@ hipError_t launch_grouped_wgrad_fp8(const GemmParams& p, hipStream_t s) {
 
 hipError_t launch_grouped_dgrad_mx(const GemmParams& p, int epilogue, hipStream_t s) {
   if (epilogue == E_DSWIGLU) return launch_tile<F_MX, true, true, E_DSWIGLU, S_GROUP_M>(p, s);
+  if (epilogue == E_DSRELU) return launch_tile<F_MX, true, true, E_DSRELU, S_GROUP_M>(p, s);
   return launch_tile<F_MX, true, true, E_STORE, S_GROUP_M>(p, s);
 }
 

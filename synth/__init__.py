@@ -125,6 +125,11 @@ WORKLOADS = {
     # the bf16 grouped MLP with the scaled squared-ReLU activation (fc1 has ffn outputs, no gate)
     "grouped_srelu_mlp_T65536_G8": dict(kind="grouped", fmt="bf16", T=65536, G=8, hidden=2048, ffn=2048,
                                         alpha=1.0, act="srelu"),
+    # and on MXFP8 / FP8 (per-group current scaling) operands (forward + backward)
+    "mxfp8_grouped_srelu_mlp_T65536_G8": dict(kind="grouped", fmt="mxfp8", T=65536, G=8, hidden=2048, ffn=2048,
+                                              alpha=1.0, act="srelu", passes=("fwd", "bwd")),
+    "fp8_grouped_srelu_mlp_T65536_G8": dict(kind="grouped", fmt="fp8", T=65536, G=8, hidden=2048, ffn=2048,
+                                            alpha=1.0, act="srelu", passes=("fwd", "bwd")),
     # the MXFP8 linear fed by an RMSNorm whose kernel writes the MXFP8 operand (forward + backward,
     # the norm's backward included); x, W, dy as in the MXFP8 linear above, gamma = 1 + 0.1 N(0,1)
     "rmsnorm_mxfp8_linear_fwdbwd_16384x8192x8192": dict(kind="dense", fmt="mxfp8", M=16384, N=8192, K=8192,

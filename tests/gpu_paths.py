@@ -130,14 +130,24 @@ def run_grouped_mlp(inp, with_backward=True, act="swiglu"):
     return res
 
 
-def run_grouped_mlp_fwd_mx(inp):
-    """MXFP8 grouped MLP forward: quantize x, W1, W2 rowwise; fc1 + scaled SwiGLU emitting y as
-    bf16 and as MXFP8 rowwise; fc2 on the MXFP8 y."""
+def _act_epilogues(act):
+    """(fc1 width from W1's rows, forward epilogue, backward epilogue) of an activation."""
+    if act == "swiglu":
+        return (lambda n1: n1 // 2), sge.EPI_SCALED_SWIGLU, sge.EPI_DSCALED_SWIGLU
+    if act == "srelu":
+        return (lambda n1: n1), sge.EPI_SCALED_SRELU, sge.EPI_DSCALED_SRELU
+    raise ValueError(act)
+
+
+def run_grouped_mlp_fwd_mx(inp, act="swiglu"):
+    """MXFP8 grouped MLP forward: quantize x, W1, W2 rowwise; fc1 + the scaled activation
+    emitting y as bf16 and as MXFP8 rowwise; fc2 on the MXFP8 y."""
     X, W1, W2 = dev_bf16(inp["x"]), dev_bf16(inp["w1"]), dev_bf16(inp["w2"])
     P = torch.from_numpy(inp["p"]).cuda()
     T, H = X.shape
     G, N1, _ = W1.shape
-    F = N1 // 2
+    width, fwd_epi, _ = _act_epilogues(act)
+    F = width(N1)
     offs = torch.empty(1, G + 1, dtype=torch.int64, device="cuda")
     err = torch.empty(1, dtype=torch.int32, device="cuda")
     sge.splits_to_offsets(torch.from_numpy(inp["splits"]).cuda(), [1], offs, expected_total=T, err_flag=err)
@@ -151,14 +161,14 @@ def run_grouped_mlp_fwd_mx(inp):
     ys = torch.empty(T, F // 32, dtype=torch.uint8, device="cuda")
     out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
     sge.grouped_linear_fwd_mxfp8(qx["q_row"], qx["s_row"], qw1["q_row"].reshape(G, N1, H),
-                                 qw1["s_row"].reshape(G, N1, H // 32), base, out=y, epilogue=sge.EPI_SCALED_SWIGLU,
+                                 qw1["s_row"].reshape(G, N1, H // 32), base, out=y, epilogue=fwd_epi,
                                  probs=P, preact=h, out_q=yq, out_s=ys)
     sge.grouped_linear_fwd_mxfp8(yq, ys, qw2["q_row"].reshape(G, H, F), qw2["s_row"].reshape(G, H, F // 32), base,
                                  out=out)
     y_unfused = quant_mx(y, col=False)                    # the standalone quantizer on the bf16 y
     torch.cuda.synchronize()
     return {"err": err, "qx": qx, "qw1": qw1, "qw2": qw2, "h": h, "y": y, "yq": yq, "ys": ys, "out": out,
-            "y_unfused": y_unfused, "base": base}
+            "y_unfused": y_unfused, "base": base, "act": act}
 
 
 # ------------------------------------------------------- MXFP8 grouped backward
@@ -187,10 +197,10 @@ def quant_mx_grouped(t, lay, row=False, fill=None):
     return out
 
 
-def grouped_dgrad_mx(q_dy, w_colT, base, alpha=1.0, preact=None, probs=None, want_q=False):
+def grouped_dgrad_mx(q_dy, w_colT, base, alpha=1.0, preact=None, probs=None, want_q=False, act="swiglu"):
     """MXFP8 grouped dgrad from a rowwise-quantized dy and W's columnwise copy [K, G*N].
-    With ``preact`` the scaled-SwiGLU backward runs in the epilogue (dact, dprobs, and the
-    MXFP8 dact when ``want_q``); otherwise dx [T, K] is returned."""
+    With ``preact`` the scaled activation's backward runs in the epilogue (dact, dprobs, and
+    the MXFP8 dact when ``want_q``); otherwise dx [T, K] is returned."""
     T, N = q_dy["q_row"].shape
     K = w_colT["q_colT"].shape[0]
     G = base.numel() - 1
@@ -200,15 +210,16 @@ def grouped_dgrad_mx(q_dy, w_colT, base, alpha=1.0, preact=None, probs=None, wan
         sge.grouped_linear_dgrad_mxfp8(q_dy["q_row"], q_dy["s_row"], w_colT["q_colT"], w_colT["s_colT"], base,
                                        alpha=alpha, dx=out["dx"])
         return out
-    ws = torch.empty(max(1, sge.grouped_linear_bwd_workspace_size(T, K, G, sge.EPI_DSCALED_SWIGLU)),
-                     dtype=torch.uint8, device="cuda")
-    out["dact"] = torch.empty(T, 2 * K, dtype=torch.bfloat16, device="cuda")
+    _, _, epi = _act_epilogues(act)
+    hw = 2 * K if act == "swiglu" else K
+    ws = torch.empty(max(1, sge.grouped_linear_bwd_workspace_size(T, K, G, epi)), dtype=torch.uint8, device="cuda")
+    out["dact"] = torch.empty(T, hw, dtype=torch.bfloat16, device="cuda")
     out["dprobs"] = torch.empty(T, dtype=torch.float32, device="cuda")
     if want_q:
-        out["dact_q"] = torch.empty(T, 2 * K, dtype=torch.uint8, device="cuda")
-        out["dact_s"] = torch.empty(T, 2 * K // 32, dtype=torch.uint8, device="cuda")
+        out["dact_q"] = torch.empty(T, hw, dtype=torch.uint8, device="cuda")
+        out["dact_s"] = torch.empty(T, hw // 32, dtype=torch.uint8, device="cuda")
     sge.grouped_linear_dgrad_mxfp8(q_dy["q_row"], q_dy["s_row"], w_colT["q_colT"], w_colT["s_colT"], base,
-                                   alpha=alpha, epilogue=sge.EPI_DSCALED_SWIGLU, preact=preact, probs=probs,
+                                   alpha=alpha, epilogue=epi, preact=preact, probs=probs,
                                    dact=out["dact"], dprobs=out["dprobs"], dact_q=out.get("dact_q"),
                                    dact_s=out.get("dact_s"), workspace=ws)
     return out
@@ -224,20 +235,21 @@ def grouped_wgrad_mx(qa, qb, lay, G, alpha=1.0):
 
 def run_grouped_mlp_bwd_mx(inp, fwd):
     """MXFP8 grouped MLP backward after ``run_grouped_mlp_fwd_mx``: fc2 dgrad with the fused
-    scaled-SwiGLU backward and group quantize of dh, fc2 wgrad, fc1 dgrad on the MXFP8 dh,
-    fc1 wgrad; every wgrad operand token-blocked per group."""
+    backward of the scaled activation and group quantize of dh, fc2 wgrad, fc1 dgrad on the
+    MXFP8 dh, fc1 wgrad; every wgrad operand token-blocked per group."""
     X, W1, W2 = dev_bf16(inp["x"]), dev_bf16(inp["w1"]), dev_bf16(inp["w2"])
     DOUT = dev_bf16(inp["dout"])
     P = torch.from_numpy(inp["p"]).cuda()
     T, H = X.shape
     G, N1, _ = W1.shape
-    F = N1 // 2
+    act = fwd["act"]
+    F = _act_epilogues(act)[0](N1)
     base = fwd["base"]
     lay = mx_layout(base, T)
     q_dout = quant_mx_grouped(DOUT, lay, row=True)
     w2c = quant_mx(W2.reshape(G * H, F), row=False, col=True)        # [F, G*H]
-    w1c = quant_mx(W1.reshape(G * N1, H), row=False, col=True)       # [H, G*2F]
-    d2 = grouped_dgrad_mx(q_dout, w2c, base, preact=fwd["h"], probs=P, want_q=True)
+    w1c = quant_mx(W1.reshape(G * N1, H), row=False, col=True)       # [H, G*N1]
+    d2 = grouped_dgrad_mx(q_dout, w2c, base, preact=fwd["h"], probs=P, want_q=True, act=act)
     q_y = quant_mx_grouped(fwd["y"], lay)
     dw2 = grouped_wgrad_mx(q_dout, q_y, lay, G)
     d1 = grouped_dgrad_mx({"q_row": d2["dact_q"], "s_row": d2["dact_s"]}, w1c, base)
@@ -271,7 +283,7 @@ def quant_fp8_grouped(t, G, lay=None, row=True, col=True, fill=None, amax_in=Non
     return out
 
 
-def run_grouped_mlp_fp8(inp):
+def run_grouped_mlp_fp8(inp, act="swiglu"):
     """Grouped MLP forward + backward on E4M3 operands with current scaling per group: every
     operand quantized per group (x, y, dout, dh per token group; W1, W2 per expert), rowwise for
     the forward and the dgrads, transposed for the dgrads' weights and the wgrads' operands."""
@@ -279,7 +291,8 @@ def run_grouped_mlp_fp8(inp):
     P = torch.from_numpy(inp["p"]).cuda()
     T, H = X.shape
     G, N1, _ = W1.shape
-    F = N1 // 2
+    width, fwd_epi, bwd_epi = _act_epilogues(act)
+    F = width(N1)
     offs = torch.empty(1, G + 1, dtype=torch.int64, device="cuda")
     sge.splits_to_offsets(torch.from_numpy(inp["splits"]).cuda(), [1], offs)
     base = offs[0]
@@ -291,16 +304,16 @@ def run_grouped_mlp_fp8(inp):
     h, y, out = torch.empty(T, N1, **bf), torch.empty(T, F, **bf), torch.empty(T, H, **bf)
     amax_y = torch.empty(G, dtype=torch.float32, device="cuda")
     sge.grouped_linear_fwd_fp8(qx["q"], qx["scale_inv"], qw1["q"].view(G, N1, H), qw1["scale_inv"], base, y,
-                               epilogue=sge.EPI_SCALED_SWIGLU, probs=P, preact=h, out_amax=amax_y)
+                               epilogue=fwd_epi, probs=P, preact=h, out_amax=amax_y)
     qy = quant_fp8_grouped(y, G, lay, amax_in=amax_y)            # the amax fused into fc1's epilogue
     sge.grouped_linear_fwd_fp8(qy["q"], qy["scale_inv"], qw2["q"].view(G, H, F), qw2["scale_inv"], base, out)
     qd = quant_fp8_grouped(DOUT, G, lay)
     dh, dp = torch.empty(T, N1, **bf), torch.empty(T, dtype=torch.float32, device="cuda")
     amax_dh = torch.empty(G, dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(1, sge.grouped_linear_bwd_workspace_size(T, F, G, sge.EPI_DSCALED_SWIGLU)),
+    ws = torch.empty(max(1, sge.grouped_linear_bwd_workspace_size(T, F, G, bwd_epi)),
                      dtype=torch.uint8, device="cuda")
     sge.grouped_linear_dgrad_fp8(qd["q"], qd["scale_inv"], qw2["q_t"], qw2["scale_inv"], base,
-                                 epilogue=sge.EPI_DSCALED_SWIGLU, preact=h, probs=P, dact=dh, dprobs=dp,
+                                 epilogue=bwd_epi, preact=h, probs=P, dact=dh, dprobs=dp,
                                  dact_amax=amax_dh, workspace=ws)
     dw2 = torch.empty(G, H, F, **bf)
     sge.grouped_linear_wgrad_fp8(qd["q_t"], qd["scale_inv"], qy["q_t"], qy["scale_inv"], lay, dw2)

@@ -387,8 +387,21 @@ def test_srelu_epilogue_validation(sge):
     # bf16 grouped forward: SReLU needs probs
     assert f(B(1), B(2), 4, 100, 264, 256, B(3), 1.0, sge.EPI_SCALED_SRELU, None, B(4), B(5), None) == sge.ERR_NULL
     fm = sge._lib.sge_grouped_linear_fwd_mxfp8
-    assert fm(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, sge.EPI_SCALED_SRELU, B(6), B(7), B(8),
-              None, None, None) == sge.ERR_ARG                             # the MXFP8 path has no SReLU
+    assert fm(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, sge.EPI_SCALED_SRELU, None, B(7), B(8),
+              None, None, None) == sge.ERR_NULL                            # MXFP8 SReLU needs probs
+    assert fm(B(1), B(2), B(3), B(4), 4, 100, 264, 256, B(5), 1.0, sge.EPI_SCALED_SRELU, B(6), B(7), B(8),
+              B(9), B(10), None) == sge.ERR_SHAPE                          # MXFP8 output: N % 32
+    assert fm(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, sge.EPI_NONE, None, B(7), None,
+              B(9), B(10), None) == sge.ERR_ARG                            # MXFP8 output needs an activation
+    dm = sge._lib.sge_grouped_linear_dgrad_mxfp8
+    assert dm(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, sge.EPI_DSCALED_SRELU, None, B(6), None, B(7),
+              B(8), None, None, B(9), 1 << 20, None) == sge.ERR_NULL        # the backward needs preact
+    ff = sge._lib.sge_grouped_linear_fwd_fp8
+    assert ff(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, sge.EPI_NONE, None, B(7), None, B(8),
+              None) == sge.ERR_ARG                                         # a fused amax needs an activation
+    df = sge._lib.sge_grouped_linear_dgrad_fp8
+    assert df(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, sge.EPI_DSCALED_SRELU, B(6), B(7), None, None,
+              B(8), None, B(9), 1 << 20, None) == sge.ERR_NULL              # the backward needs dact
     b = sge._lib.sge_grouped_linear_bwd
     assert b(B(1), None, B(2), 4, 100, 256, 264, B(3), 1.0, sge.EPI_DSCALED_SRELU, B(4), B(5), None, B(6), None,
               None, B(7), 0, None) == sge.ERR_NULL                        # SReLU backward needs dact

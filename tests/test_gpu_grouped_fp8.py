@@ -11,7 +11,7 @@ import synth
 from oracle import grouped, offsets, quant
 
 from .gpu_paths import mx_layout, quant_fp8_grouped, run_grouped_mlp_fp8
-from .helpers import TAU_FP8, assert_close, dev, dev_bf16, host_f64, host_u8
+from .helpers import TAU_FP8, assert_close, assert_close_requantized, dev, dev_bf16, host_f64, host_u8
 
 pytestmark = pytest.mark.gpu
 
@@ -115,17 +115,18 @@ MLP_CASES = {
 }
 
 
+@pytest.mark.parametrize("act", ["swiglu", "srelu"])
 @pytest.mark.parametrize("case", list(MLP_CASES))
-def test_fp8_grouped_mlp_fwd_bwd(case):
+def test_fp8_grouped_mlp_fwd_bwd(case, act):
     splits, hidden, ffn = MLP_CASES[case]
     T = 700 if splits is None else sum(splits)
     G = 5 if splits is None else len(splits)
-    print(f"case fp8 grouped mlp {case} T={T} G={G} hidden={hidden} ffn={ffn}", flush=True)
-    inp = synth.grouped(T, G, hidden, ffn, seed=33, splits=splits)
-    got = run_grouped_mlp_fp8(inp)
+    print(f"case fp8 grouped mlp {case} {act} T={T} G={G} hidden={hidden} ffn={ffn}", flush=True)
+    inp = synth.grouped(T, G, hidden, ffn, seed=33, splits=splits, gated=act == "swiglu")
+    got = run_grouped_mlp_fp8(inp, act)
     base = offsets.base_offsets(inp["splits"])
-    fwd = grouped.grouped_mlp_fwd_fp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base)
-    bwd = grouped.grouped_mlp_bwd_fp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base, inp["dout"], fwd=fwd)
+    fwd = grouped.grouped_mlp_fwd_fp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base, act)
+    bwd = grouped.grouped_mlp_bwd_fp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base, inp["dout"], fwd=fwd, act=act)
     # the amax fused into the epilogues == the quantizer's own amax pass: identical bytes
     for fused, alone in (("qy", "qy_alone"), ("qdh", "qdh_alone")):
         for k in ("amax", "scale", "scale_inv"):
@@ -135,9 +136,10 @@ def test_fp8_grouped_mlp_fwd_bwd(case):
         assert np.array_equal(host_u8(got[fused]["q_t"])[:, :P], host_u8(got[alone]["q_t"])[:, :P]), fused
     assert_close(host_f64(got["h"]), fwd["h"], TAU_FP8, what="h", **KW)
     assert_close(host_f64(got["y"]), fwd["y"], TAU_FP8, what="y", **KW)
-    assert_close(host_f64(got["out"]), fwd["out"], TAU_FP8, what="out", **KW)
+    # out, dx and the weight gradients consume y or dh, quantized per group on each side
+    assert_close_requantized(host_f64(got["out"]), fwd["out"], TAU_FP8, what="out", **KW)
     assert_close(host_f64(got["dh"]), bwd["dh"], TAU_FP8, what="dh", **KW)
     assert_close(host_f64(got["dp"]), bwd["dp"], TAU_FP8, what="dprobs", **KW)
-    assert_close(host_f64(got["dx"]), bwd["dx"], TAU_FP8, what="dx", **KW)
-    assert_close(host_f64(got["dw2"]), bwd["dw2"], TAU_FP8, what="dw2", **KW)
-    assert_close(host_f64(got["dw1"]), bwd["dw1"], TAU_FP8, what="dw1", **KW)
+    assert_close_requantized(host_f64(got["dx"]), bwd["dx"], TAU_FP8, what="dx", **KW)
+    assert_close_requantized(host_f64(got["dw2"]), bwd["dw2"], TAU_FP8, what="dw2", **KW)
+    assert_close_requantized(host_f64(got["dw1"]), bwd["dw1"], TAU_FP8, what="dw1", **KW)

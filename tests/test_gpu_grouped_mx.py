@@ -25,20 +25,21 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("act", ["swiglu", "srelu"])
 @pytest.mark.parametrize("case", list(CASES))
-def test_mxfp8_grouped_mlp_forward(case):
+def test_mxfp8_grouped_mlp_forward(case, act):
     splits, hidden, ffn = CASES[case]
     T = 700 if splits is None else sum(splits)
     G = 5 if splits is None else len(splits)
-    print(f"case mxfp8 grouped fwd {case} T={T} G={G} hidden={hidden} ffn={ffn}", flush=True)
-    inp = synth.grouped(T, G, hidden, ffn, seed=31, splits=splits)
-    got = run_grouped_mlp_fwd_mx(inp)
+    print(f"case mxfp8 grouped fwd {case} {act} T={T} G={G} hidden={hidden} ffn={ffn}", flush=True)
+    inp = synth.grouped(T, G, hidden, ffn, seed=31, splits=splits, gated=act == "swiglu")
+    got = run_grouped_mlp_fwd_mx(inp, act)
     assert int(got["err"].item()) == 0
     base = offsets.base_offsets(inp["splits"])
-    ref = grouped.grouped_mlp_fwd_mxfp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base)
+    ref = grouped.grouped_mlp_fwd_mxfp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base, act)
 
     # quantized operands: bit-exact against the oracle's MXFP8
-    for key, src in (("qx", inp["x"]), ("qw1", inp["w1"].reshape(G * 2 * ffn, hidden)),
+    for key, src in (("qx", inp["x"]), ("qw1", inp["w1"].reshape(-1, hidden)),
                      ("qw2", inp["w2"].reshape(G * hidden, ffn))):
         q, s = quant.mxfp8_rowwise(src)
         assert np.array_equal(host_u8(got[key]["q_row"]), q), key

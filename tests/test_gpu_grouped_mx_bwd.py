@@ -1,6 +1,7 @@
 """MXFP8 grouped backward against the oracle: the token-blocked group layout and quantizer
-(bit-exact), the grouped dgrad with the fused scaled-SwiGLU backward and group quantize, the
-grouped wgrad on token-blocked operands, and the whole MLP backward (FP8 bar)."""
+(bit-exact), the grouped dgrad with the fused backward of the scaled activation (SwiGLU or
+SReLU) and group quantize, the grouped wgrad on token-blocked operands, and the whole MLP
+backward (FP8 bar)."""
 
 import numpy as np
 import pytest
@@ -184,17 +185,18 @@ MLP_CASES = {
 }
 
 
+@pytest.mark.parametrize("act", ["swiglu", "srelu"])
 @pytest.mark.parametrize("case", list(MLP_CASES))
-def test_mxfp8_grouped_mlp_backward(case):
+def test_mxfp8_grouped_mlp_backward(case, act):
     splits, hidden, ffn = MLP_CASES[case]
     T = 700 if splits is None else sum(splits)
     G = 5 if splits is None else len(splits)
-    print(f"case mxfp8 grouped mlp bwd {case} T={T} G={G} hidden={hidden} ffn={ffn}", flush=True)
-    inp = synth.grouped(T, G, hidden, ffn, seed=32, splits=splits)
-    fwd = run_grouped_mlp_fwd_mx(inp)
+    print(f"case mxfp8 grouped mlp bwd {case} {act} T={T} G={G} hidden={hidden} ffn={ffn}", flush=True)
+    inp = synth.grouped(T, G, hidden, ffn, seed=32, splits=splits, gated=act == "swiglu")
+    fwd = run_grouped_mlp_fwd_mx(inp, act)
     got = run_grouped_mlp_bwd_mx(inp, fwd)
     base = offsets.base_offsets(inp["splits"])
-    ref = grouped.grouped_mlp_bwd_mxfp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base, inp["dout"])
+    ref = grouped.grouped_mlp_bwd_mxfp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base, inp["dout"], act=act)
     # fused activation backward + group quantize == standalone quantizer on the same bf16 dh
     assert np.array_equal(host_u8(got["dhq"]), host_u8(got["dh_unfused"]["q_row"]))
     assert np.array_equal(host_u8(got["dhs"]), host_u8(got["dh_unfused"]["s_row"]))

@@ -422,3 +422,31 @@ def test_fp8_grouped_mlp_fwd_bwd_match_brute_force():
         dw1 = [[math.fsum(dhd[t][n] * xd[t][k] for t in ts) for k in range(H)] for n in range(2 * F)]
         np.testing.assert_allclose(got["dw2"][g], dw2, rtol=1e-12, atol=1e-15)
         np.testing.assert_allclose(got["dw1"][g], dw1, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("act", ["swiglu", "srelu"])
+def test_requantized_bar_covers_fp32_accumulation(act):
+    """The bar that the FP8 grouped MLP's GPU test puts on outputs fed by a requantized bf16
+    intermediate, exercised on the CPU: fc1 accumulated in fp32 (as a GPU kernel does) instead
+    of fp64 moves some bf16 activations by one step, and per-group E4M3 quantization can turn
+    such a step into a neighbouring code; fc2's wgrad on those codes stays inside the bar."""
+    from oracle import offsets
+    from oracle.grouped import _ACTS, _fp8_experts_hat, _fp8_groups_hat, grouped_linear_wgrad
+    from .helpers import TAU_FP8, assert_close_requantized
+
+    splits = [300, 0, 211, 9, 0, 40]
+    T, G = sum(splits), len(splits)
+    inp = synth.grouped(T, G, 256, 256, seed=33, splits=splits, gated=act == "swiglu")
+    base = offsets.base_offsets(inp["splits"])
+    fwd = grouped.grouped_mlp_fwd_fp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base, act)
+    bwd = grouped.grouped_mlp_bwd_fp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base, inp["dout"], fwd=fwd, act=act)
+    c, _ = quant.mx_group_layout(base, T)
+    xh = _fp8_groups_hat(inp["x"], c).astype(np.float32)
+    w1h = _fp8_experts_hat(inp["w1"]).astype(np.float32)
+    h32 = np.zeros((T, w1h.shape[1]), np.float32)
+    for g in range(G):
+        h32[base[g]:base[g + 1]] = xh[base[g]:base[g + 1]] @ w1h[g].T
+    y_bits = f64_to_bf16(_ACTS[act][0](h32.astype(np.float64), inp["p"]).astype(np.float32).astype(np.float64))
+    assert np.count_nonzero(y_bits != fwd["y_bits"]) > 0               # the case exercises the rounding
+    dw2 = grouped_linear_wgrad(_fp8_groups_hat(inp["dout"], c), _fp8_groups_hat(y_bits, c), base)
+    assert_close_requantized(dw2, bwd["dw2"], TAU_FP8, what="dw2")
