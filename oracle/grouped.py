@@ -115,13 +115,64 @@ def scaled_srelu_bwd(gy, h, p):
     return gy * p * 2.0 * r, np.sum(gy * r * r, axis=1)
 
 
+def scaled_clamped_swiglu_fwd(h, p, limit, alpha):
+    """Clamped SwiGLU scaled per token: with a, b the two halves of h [T, 2F],
+    a_c = min(a, limit), b_c = clamp(b, -limit, limit),
+    y = p * a_c * sigmoid(alpha * a_c) * (b_c + 1).
+
+    The PR page ("Activation + GroupedLinear Fusion for MOE ...", Description; Important Files
+    Changed: ScaledClampedQGeGLU) names the clamped SwiGLU without its formula. Read as the
+    published clamped form: the gate is clamped from above and passed through the quick-GELU
+    shape a * sigmoid(alpha * a) (the "QGeGLU"), the linear half is clamped both ways and
+    offset by one; limit and alpha are parameters.
+    """
+    h = np.asarray(h, np.float64)
+    F = h.shape[1] // 2
+    a = np.minimum(h[:, :F], limit)
+    b = np.clip(h[:, F:], -limit, limit)
+    return np.asarray(p, np.float64)[:, None] * (a * _sigmoid(alpha * a)) * (b + 1.0)
+
+
+def scaled_clamped_swiglu_bwd(gy, h, p, limit, alpha):
+    """Gradients of ``scaled_clamped_swiglu_fwd`` given dL/dy. A clamp passes the gradient
+    where its input lies inside the closed interval (as torch.clamp does) and stops it
+    outside: da = gy * p * (b_c + 1) * q'(a_c) where a <= limit, with
+    q'(u) = s * (1 + alpha * u * (1 - s)), s = sigmoid(alpha * u); db = gy * p * q(a_c) where
+    |b| <= limit; dp = sum_j gy_j * q(a_c,j) * (b_c,j + 1). Returns (dh [T, 2F], dp [T])."""
+    gy = np.asarray(gy, np.float64)
+    h = np.asarray(h, np.float64)
+    p = np.asarray(p, np.float64)[:, None]
+    F = h.shape[1] // 2
+    a_raw, b_raw = h[:, :F], h[:, F:]
+    a = np.minimum(a_raw, limit)
+    b = np.clip(b_raw, -limit, limit)
+    s = _sigmoid(alpha * a)
+    q = a * s
+    dq = s * (1.0 + alpha * a * (1.0 - s))
+    da = np.where(a_raw <= limit, gy * p * (b + 1.0) * dq, 0.0)
+    db = np.where(np.abs(b_raw) <= limit, gy * p * q, 0.0)
+    dp = np.sum(gy * q * (b + 1.0), axis=1)
+    return np.concatenate([da, db], axis=1), dp
+
+
 _ACTS = {"swiglu": (scaled_swiglu_fwd, scaled_swiglu_bwd), "srelu": (scaled_srelu_fwd, scaled_srelu_bwd)}
 
 
+def _act(act):
+    """(forward, backward) of an activation: "swiglu", "srelu", or ("clamped_swiglu", limit, alpha)."""
+    if isinstance(act, tuple):
+        name, limit, alpha = act
+        assert name == "clamped_swiglu", name
+        return (lambda h, p: scaled_clamped_swiglu_fwd(h, p, limit, alpha),
+                lambda gy, h, p: scaled_clamped_swiglu_bwd(gy, h, p, limit, alpha))
+    return _ACTS[act]
+
+
 def grouped_mlp_fwd(x, w1, w2, p, base, act="swiglu"):
-    """fc1 -> scaled activation (SwiGLU, or SReLU) -> fc2. Returns dict(h, y, out)."""
+    """fc1 -> scaled activation (SwiGLU, SReLU, or clamped SwiGLU as ("clamped_swiglu", limit,
+    alpha)) -> fc2. Returns dict(h, y, out)."""
     h = grouped_linear_fwd(x, w1, base)
-    y = _ACTS[act][0](h, p)
+    y = _act(act)[0](h, p)
     out = grouped_linear_fwd(y, w2, base)
     return {"h": h, "y": y, "out": out}
 
@@ -135,9 +186,9 @@ def grouped_mlp_bwd(dout, x, w1, w2, p, base, h=None, y=None, act="swiglu"):
     if h is None:
         h = grouped_linear_fwd(x, w1, base)
     if y is None:
-        y = _ACTS[act][0](h, p)
+        y = _act(act)[0](h, p)
     gy = grouped_linear_dgrad(dout, w2, base)
-    dh, dp = _ACTS[act][1](gy, h, p)
+    dh, dp = _act(act)[1](gy, h, p)
     dw2 = grouped_linear_wgrad(dout, y, base)
     dx = grouped_linear_dgrad(dh, w1, base)
     dw1 = grouped_linear_wgrad(dh, x, base)
@@ -170,7 +221,7 @@ def grouped_mlp_fwd_mxfp8(x_bits, w1_bits, w2_bits, p, base, act="swiglu"):
     w1_hat = mx_dequantize(*mxfp8_rowwise(w1_bits.reshape(G * N1, H))).reshape(G, N1, H)
     w2_hat = mx_dequantize(*mxfp8_rowwise(w2_bits.reshape(G * H, F))).reshape(G, H, F)
     h = grouped_linear_fwd(x_hat, w1_hat, base)
-    y = _ACTS[act][0](h, p)
+    y = _act(act)[0](h, p)
     y_bits = f64_to_bf16(y)
     y_q, y_s = mxfp8_rowwise(y_bits)
     out = grouped_linear_fwd(mx_dequantize(y_q, y_s), w2_hat, base)
@@ -236,7 +287,7 @@ def grouped_mlp_bwd_mxfp8(x_bits, w1_bits, w2_bits, p, base, dout_bits, fwd=None
         fwd = grouped_mlp_fwd_mxfp8(x_bits, w1_bits, w2_bits, p, base, act)
     h_saved = bf16_to_f64(f64_to_bf16(fwd["h"]))
     gy = grouped_linear_dgrad_mxfp8(dout_bits, w2_bits, base)
-    dh, dp = _ACTS[act][1](gy, h_saved, p)
+    dh, dp = _act(act)[1](gy, h_saved, p)
     dh_bits = f64_to_bf16(dh)
     dh_q, dh_s = mxfp8_rowwise(dh_bits)
     dw2 = grouped_linear_wgrad_mxfp8(dout_bits, fwd["y_bits"], base)
@@ -278,7 +329,7 @@ def grouped_mlp_fwd_fp8(x_bits, w1_bits, w2_bits, p, base, act="swiglu"):
     T = np.asarray(x_bits).shape[0]
     c, _ = mx_group_layout(base, T)
     h = grouped_linear_fwd(_fp8_groups_hat(x_bits, c), _fp8_experts_hat(w1_bits), base)
-    y = _ACTS[act][0](h, p)
+    y = _act(act)[0](h, p)
     y_bits = f64_to_bf16(y)
     out = grouped_linear_fwd(_fp8_groups_hat(y_bits, c), _fp8_experts_hat(w2_bits), base)
     return {"h": h, "y": y, "y_bits": y_bits, "out": out}
@@ -295,7 +346,7 @@ def grouped_mlp_bwd_fp8(x_bits, w1_bits, w2_bits, p, base, dout_bits, fwd=None, 
     dout_hat = _fp8_groups_hat(dout_bits, c)
     w1_hat, w2_hat = _fp8_experts_hat(w1_bits), _fp8_experts_hat(w2_bits)
     gy = grouped_linear_dgrad(dout_hat, w2_hat, base)
-    dh, dp = _ACTS[act][1](gy, bf16_to_f64(f64_to_bf16(fwd["h"])), p)
+    dh, dp = _act(act)[1](gy, bf16_to_f64(f64_to_bf16(fwd["h"])), p)
     dh_bits = f64_to_bf16(dh)
     dh_hat = _fp8_groups_hat(dh_bits, c)
     dw2 = grouped_linear_wgrad(dout_hat, _fp8_groups_hat(fwd["y_bits"], c), base)

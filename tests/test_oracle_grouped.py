@@ -184,3 +184,90 @@ def test_grouped_srelu_mlp_backward_vs_torch_autograd():
     assert np.allclose(ours_f["out"], out.detach().numpy(), rtol=1e-12, atol=1e-13)
     for k, t in (("dx", tx), ("dw1", tw1), ("dw2", tw2), ("dp", tp)):
         assert np.allclose(ours_b[k], t.grad.numpy(), rtol=1e-12, atol=1e-13), k
+
+
+def test_clamped_swiglu_closed_forms():
+    L = math.log(3.0)                                   # sigmoid(ln 3) = 3/4
+    # gate: below, at and above the limit; linear half: inside, at +-limit, beyond both sides
+    h = np.array([[0.0, L, 5.0, -1.0, 0.5, L, -L, 9.0, -9.0, 0.0]])
+    p = np.array([0.5])
+    y = grouped.scaled_clamped_swiglu_fwd(h, p, L, 1.0)
+    s1 = 1.0 / (1.0 + math.exp(1.0))                      # sigmoid(-1)
+    q = [0.0, 0.75 * L, 0.75 * L, -s1, 0.5 / (1.0 + math.exp(-0.5))]
+    bp = [1.0 + L, 1.0 - L, 1.0 + L, 1.0 - L, 1.0]
+    assert np.allclose(y[0], [0.5 * qi * bi for qi, bi in zip(q, bp)], rtol=1e-15, atol=0)
+    dh, dp = grouped.scaled_clamped_swiglu_bwd(np.ones((1, 5)), h, p, L, 1.0)
+    da, db = dh[0, :5], dh[0, 5:]
+    assert da[2] == 0.0 and da[1] != 0.0                  # gate above the limit: no gradient; at it: passes
+    assert db[2] == 0.0 and db[3] == 0.0 and db[1] != 0.0 and db[4] != 0.0   # beyond +-limit: none; at -limit: passes
+    assert np.isclose(dp[0], sum(qi * bi for qi, bi in zip(q, bp)), rtol=1e-15)
+
+
+def test_clamped_swiglu_reductions():
+    rng = np.random.default_rng(3)
+    h = rng.standard_normal((5, 16)) * 3
+    p = rng.random(5)
+    F = 8
+    # no clamp (infinite limit) and alpha = 1: SwiGLU of (a, b + 1)
+    shifted = h.copy()
+    shifted[:, F:] += 1.0
+    assert np.allclose(grouped.scaled_clamped_swiglu_fwd(h, p, np.inf, 1.0),
+                       grouped.scaled_swiglu_fwd(shifted, p), rtol=1e-14, atol=0)
+    # alpha = 2: a * sigmoid(2 a) = a * (1 + tanh a) / 2
+    a = np.minimum(h[:, :F], 1.5)
+    b = np.clip(h[:, F:], -1.5, 1.5)
+    ref = p[:, None] * a * (1.0 + np.tanh(a)) / 2.0 * (b + 1.0)
+    assert np.allclose(grouped.scaled_clamped_swiglu_fwd(h, p, 1.5, 2.0), ref, rtol=1e-13, atol=1e-15)
+
+
+def test_clamped_swiglu_backward_central_differences():
+    rng = np.random.default_rng(4)
+    T, F, L, alpha = 3, 6, 1.25, 1.702
+    h = rng.standard_normal((T, 2 * F)) * 1.5
+    h[np.abs(np.abs(h) - L) < 1e-3] += 0.01             # keep every point off the clamps' kinks
+    p = rng.random(T)
+    gy = rng.standard_normal((T, F))
+    dh, dp = grouped.scaled_clamped_swiglu_bwd(gy, h, p, L, alpha)
+    loss = lambda hh, pp: float(np.sum(gy * grouped.scaled_clamped_swiglu_fwd(hh, pp, L, alpha)))  # noqa: E731
+    eps = 1e-6
+    for t in range(T):
+        for j in range(2 * F):
+            e = np.zeros_like(h)
+            e[t, j] = eps
+            num = (loss(h + e, p) - loss(h - e, p)) / (2 * eps)
+            assert abs(num - dh[t, j]) <= 1e-7 * (1 + abs(num)), (t, j)
+        e = np.zeros_like(p)
+        e[t] = eps
+        assert abs((loss(h, p + e) - loss(h, p - e)) / (2 * eps) - dp[t]) <= 1e-7 * (1 + abs(dp[t]))
+
+
+def test_grouped_clamped_swiglu_mlp_backward_vs_torch_autograd():
+    splits = [2, 0, 3, 1]
+    T, H, F, G = 6, 4, 3, 4
+    L, alpha = 0.75, 1.702
+    base = offsets.base_offsets(splits)
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((T, H))
+    w1 = rng.standard_normal((G, 2 * F, H)) * 0.7
+    w2 = rng.standard_normal((G, H, F)) * 0.5
+    p = rng.random(T)
+    dout = rng.standard_normal((T, H))
+    act = ("clamped_swiglu", L, alpha)
+    ours_f = grouped.grouped_mlp_fwd(x, w1, w2, p, base, act=act)
+    ours_b = grouped.grouped_mlp_bwd(dout, x, w1, w2, p, base, act=act)
+    h = ours_f["h"]
+    assert np.any(h[:, :F] > L) and np.any(np.abs(h[:, F:]) > L)    # both clamps engage
+    tx, tw1, tw2, tp = (torch.tensor(a, requires_grad=True) for a in (x, w1, w2, p))
+    outs = []
+    for g in range(G):
+        lo, hi = base[g], base[g + 1]
+        hh = tx[lo:hi] @ tw1[g].T
+        a = torch.clamp(hh[:, :F], max=L)
+        b = torch.clamp(hh[:, F:], min=-L, max=L)
+        y = tp[lo:hi, None] * a * torch.sigmoid(alpha * a) * (b + 1.0)
+        outs.append(y @ tw2[g].T)
+    out = torch.cat(outs)
+    out.backward(torch.tensor(dout))
+    assert np.allclose(ours_f["out"], out.detach().numpy(), rtol=1e-12, atol=1e-13)
+    for k, t in (("dx", tx), ("dw1", tw1), ("dw2", tw2), ("dp", tp)):
+        assert np.allclose(ours_b[k], t.grad.numpy(), rtol=1e-12, atol=1e-13), k
