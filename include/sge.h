@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define SGE_ABI_VERSION 5
+#define SGE_ABI_VERSION 6
 
 /* Alignment, in tokens, of each group's start in a token-blocked MXFP8 operand. */
 #define SGE_MX_TOKEN_ALIGN 128
@@ -87,8 +87,31 @@ typedef enum {
   SGE_EPI_SCALED_SWIGLU = 1,   /* forward: h = alpha*acc, y = p * silu(h[:, :F]) * h[:, F:] */
   SGE_EPI_DSCALED_SWIGLU = 2,  /* backward: dgrad g of the next layer -> dh = [da, db], dp */
   SGE_EPI_SCALED_SRELU = 3,    /* forward: h = alpha*acc, y = p * max(h, 0)^2 (elementwise, no gate half) */
-  SGE_EPI_DSCALED_SRELU = 4    /* backward: dh = g * p * 2 max(h, 0), dp = sum_j g * max(h, 0)^2 */
+  SGE_EPI_DSCALED_SRELU = 4,   /* backward: dh = g * p * 2 max(h, 0), dp = sum_j g * max(h, 0)^2 */
+  SGE_EPI_SCALED_CLAMPED_SWIGLU = 5,   /* forward: gated like SWIGLU, clamped (sge_act_params) */
+  SGE_EPI_DSCALED_CLAMPED_SWIGLU = 6   /* backward of SCALED_CLAMPED_SWIGLU */
 } sge_epilogue;
+
+/*
+ * Parameters of the clamped SwiGLU epilogues (host struct, read during the call; NULL for
+ * every other epilogue). ("Activation + GroupedLinear Fusion for MOE and other MOE
+ * optimizations", Description: scaled SReLU, SwiGLU and clamped SwiGLU activations;
+ * Important Files Changed: ScaledClampedQGeGLU. The page names the activation without its
+ * formula; this is the published clamped form with the gate through u * sigmoid(alpha * u).)
+ * With a, b the two halves of h [T, 2F] and p the per-token scale:
+ *   a_c = min(a, limit),  b_c = clamp(b, -limit, limit),
+ *   y   = p * a_c * sigmoid(alpha * a_c) * (b_c + 1).
+ * Backward (from the saved bf16 h): with s = sigmoid(alpha * a_c), q = a_c * s,
+ *   da = g * p * (b_c + 1) * s * (1 + alpha * a_c * (1 - s))  where a <= limit, else 0;
+ *   db = g * p * q                                            where |b| <= limit, else 0;
+ *   dp = sum_j g_j * q_j * (b_c,j + 1).
+ * limit must be finite and > 0 and alpha finite (SGE_ERR_ARG); NULL with a clamped
+ * epilogue is SGE_ERR_NULL.
+ */
+typedef struct {
+  float limit;
+  float alpha;
+} sge_act_params;
 
 int sge_abi_version(void);
 const char* sge_status_string(sge_status s);
@@ -206,6 +229,9 @@ sge_status sge_splits_to_offsets(const int64_t* splits, int32_t G, const int64_t
  *                        preact [T, N] bf16 = h (saved for the backward; may be NULL).
  * SGE_EPI_SCALED_SRELU:  out [T, N] bf16 = p[t] * max(h, 0)^2 (scaled squared ReLU; the page
  *                        names scaled SReLU beside scaled SwiGLU), preact [T, N] = h (or NULL).
+ * SGE_EPI_SCALED_CLAMPED_SWIGLU: as SWIGLU with the clamped form of sge_act_params
+ *                        (act_params required); preact holds the unclamped h.
+ * act_params: host, read during the call; NULL unless the epilogue is clamped.
  * offsets: device int64 [G+1] (row 0 of sge_splits_to_offsets with multiplier 1);
  * values are clamped into [0, T] and made non-decreasing before use.
  * probs: device fp32 [T] (SWIGLU only). Shapes: K % 8 == 0, N % 8 == 0
@@ -213,6 +239,7 @@ sge_status sge_splits_to_offsets(const int64_t* splits, int32_t G, const int64_t
  */
 sge_status sge_grouped_linear_fwd(const void* x, const void* w, int32_t G, int64_t T, int64_t N,
                                   int64_t K, const int64_t* offsets, float alpha, int32_t epilogue,
+                                  const sge_act_params* act_params,
                                   const float* probs, void* out, void* preact, hipStream_t stream);
 
 /*
@@ -231,13 +258,16 @@ sge_status sge_grouped_linear_fwd(const void* x, const void* w, int32_t G, int64
  *   MXFP8 rowwise quantization of the bf16 output, i.e. the bytes sge_quantize_mxfp8 would
  *   write for `out` (the operand layout of the next grouped GEMM's forward). out_q and
  *   out_s are given together or not at all.
+ * SGE_EPI_SCALED_SRELU and SGE_EPI_SCALED_CLAMPED_SWIGLU (with act_params) as in
+ *   sge_grouped_linear_fwd, with the same optional MXFP8 output.
  * Shapes: K % 128 == 0; N % 8 == 0 (SWIGLU: N % 256 == 0). All pointers 16-byte aligned;
  * outputs must not overlap the inputs or each other (SGE_ERR_ALIAS). offsets and probs
  * as in sge_grouped_linear_fwd.
  */
 sge_status sge_grouped_linear_fwd_mxfp8(const void* x_q, const void* x_s, const void* w_q, const void* w_s,
                                         int32_t G, int64_t T, int64_t N, int64_t K, const int64_t* offsets,
-                                        float alpha, int32_t epilogue, const float* probs, void* out,
+                                        float alpha, int32_t epilogue,
+                                        const sge_act_params* act_params, const float* probs, void* out,
                                         void* preact, void* out_q, void* out_s, hipStream_t stream);
 
 /*
@@ -257,6 +287,9 @@ sge_status sge_grouped_linear_fwd_mxfp8(const void* x_q, const void* x_s, const 
  *                         dx is not used.
  * SGE_EPI_DSCALED_SRELU:  x was y = p * max(h, 0)^2 with preact h [T, K] bf16; writes
  *                         dact [T, K] = g*p*2*max(h, 0) and dprobs [T] = sum_j g*max(h, 0)^2.
+ * SGE_EPI_DSCALED_CLAMPED_SWIGLU: x was the clamped SwiGLU given by act_params (required)
+ *                         with preact h = [a, b] [T, 2K] bf16 (unclamped); writes dact [T, 2K]
+ *                         and dprobs [T] by the backward given with sge_act_params.
  * dw: device bf16 [G, N, K] or NULL to skip the weight gradient.
  * workspace: device, >= sge_grouped_linear_bwd_workspace_size(T, K, G, epilogue) bytes
  * (0 is valid for SGE_EPI_NONE).
@@ -264,7 +297,8 @@ sge_status sge_grouped_linear_fwd_mxfp8(const void* x_q, const void* x_s, const 
 size_t sge_grouped_linear_bwd_workspace_size(int64_t T, int64_t K, int32_t G, int32_t epilogue);
 sge_status sge_grouped_linear_bwd(const void* dy, const void* x, const void* w, int32_t G,
                                   int64_t T, int64_t N, int64_t K, const int64_t* offsets,
-                                  float alpha, int32_t epilogue, const void* preact,
+                                  float alpha, int32_t epilogue,
+                                  const sge_act_params* act_params, const void* preact,
                                   const float* probs, void* dact, float* dprobs, void* dx,
                                   void* dw, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream);
@@ -324,6 +358,8 @@ sge_status sge_quantize_mxfp8_grouped(const void* src, int64_t T, int64_t cols, 
  *     dact_q [T, 2K] u8 + dact_s [T, 2K/32] u8: the rowwise MXFP8 of the bf16 dact, the bytes
  *     sge_quantize_mxfp8 writes for it (the operand of the next layer's dgrad).
  *     workspace: >= sge_grouped_linear_bwd_workspace_size(T, K, G, epilogue) bytes.
+ *   SGE_EPI_DSCALED_SRELU and SGE_EPI_DSCALED_CLAMPED_SWIGLU (with act_params) as in
+ *   sge_grouped_linear_bwd, with the same optional MXFP8 dact.
  *   Shapes: N % 128 == 0, K % 8 == 0 (SwiGLU: K % 32 == 0). offsets as in
  *   sge_grouped_linear_fwd. Outputs may not overlap inputs or each other.
  *
@@ -336,6 +372,7 @@ sge_status sge_quantize_mxfp8_grouped(const void* src, int64_t T, int64_t cols, 
 sge_status sge_grouped_linear_dgrad_mxfp8(const void* dy_q, const void* dy_s, const void* w_q,
                                           const void* w_s, int32_t G, int64_t T, int64_t N, int64_t K,
                                           const int64_t* offsets, float alpha, int32_t epilogue,
+                                          const sge_act_params* act_params,
                                           const void* preact, const float* probs, void* dx, void* dact,
                                           float* dprobs, void* dact_q, void* dact_s, void* workspace,
                                           size_t workspace_bytes, hipStream_t stream);
@@ -369,13 +406,15 @@ sge_status sge_grouped_linear_wgrad_mxfp8(const void* dyT_q, const void* dyT_s, 
  * sge_grouped_linear_fwd_fp8: as sge_grouped_linear_fwd with x_q [T, K] u8 (x_sinv [G]: the
  *   scale_inv of each group's tokens) and w_q [G, N, K] u8 (w_sinv [G]: each expert's);
  *   h = fp32(x_sinv[g] * w_sinv[g]) * alpha * acc. K % 16 == 0, N % 8 == 0 (SwiGLU N % 256).
- *   out_amax (SwiGLU only; device fp32 [G] or NULL): each group's amax of the bf16 output,
- *   reduced in the epilogue (the amax a current-scaling quantize of it needs).
+ *   out_amax (an activation epilogue only; device fp32 [G] or NULL): each group's amax of the
+ *   bf16 output, reduced in the epilogue (the amax a current-scaling quantize of it needs).
+ *   Every activation epilogue of sge_grouped_linear_fwd is taken (clamped: with act_params).
  * sge_grouped_linear_dgrad_fp8: as sge_grouped_linear_dgrad_mxfp8 with dy_q [T, N] u8
  *   (dy_sinv [G]) and w_qT [K][G*N] u8, the transpose of W viewed [G*N, K] (the q_t of
  *   sge_quantize_fp8_grouped without a layout; w_sinv [G]). N % 16 == 0, K % 8 == 0; the
  *   SwiGLU backward writes dact [T, 2K] and dprobs [T] (workspace as for sge_grouped_linear_bwd),
- *   and, given dact_amax (device fp32 [G]), each group's amax of the bf16 dact.
+ *   and, given dact_amax (device fp32 [G]), each group's amax of the bf16 dact. Every
+ *   activation backward of sge_grouped_linear_bwd is taken (clamped: with act_params).
  * sge_grouped_linear_wgrad_fp8: dW_g = fp32(dy_sinv[g] * x_sinv[g]) * alpha * sum_{t in g}
  *   dy[t]^T x[t] from dyT_q [N][ld] and xT_q [K][ld] (q_t with the layout), dw [G, N, K] bf16.
  */
@@ -387,11 +426,13 @@ sge_status sge_quantize_fp8_grouped(const void* src, int64_t rows, int64_t cols,
 sge_status sge_grouped_linear_fwd_fp8(const void* x_q, const float* x_sinv, const void* w_q,
                                       const float* w_sinv, int32_t G, int64_t T, int64_t N, int64_t K,
                                       const int64_t* offsets, float alpha, int32_t epilogue,
+                                      const sge_act_params* act_params,
                                       const float* probs, void* out, void* preact, float* out_amax,
                                       hipStream_t stream);
 sge_status sge_grouped_linear_dgrad_fp8(const void* dy_q, const float* dy_sinv, const void* w_qT,
                                         const float* w_sinv, int32_t G, int64_t T, int64_t N, int64_t K,
                                         const int64_t* offsets, float alpha, int32_t epilogue,
+                                        const sge_act_params* act_params,
                                         const void* preact, const float* probs, void* dx, void* dact,
                                         float* dprobs, float* dact_amax, void* workspace,
                                         size_t workspace_bytes, hipStream_t stream);

@@ -27,6 +27,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_FORMAT, ERR_ALIGN, ERR_ALIAS, ERR_WORKSPACE, ERR_AR
 FMT_BF16, FMT_E4M3, FMT_MXFP8 = 0, 1, 2
 # grouped epilogues
 EPI_NONE, EPI_SCALED_SWIGLU, EPI_DSCALED_SWIGLU, EPI_SCALED_SRELU, EPI_DSCALED_SRELU = 0, 1, 2, 3, 4
+EPI_SCALED_CLAMPED_SWIGLU, EPI_DSCALED_CLAMPED_SWIGLU = 5, 6
 # normalizations
 NORM_RMS, NORM_LAYER = 0, 1
 
@@ -53,6 +54,19 @@ class SgeOperand(ctypes.Structure):
     ]
 
 
+class SgeActParams(ctypes.Structure):
+    """Clamped SwiGLU parameters: limit (the clamp bound) and alpha (the gate's sigmoid slope)."""
+    _fields_ = [("limit", ctypes.c_float), ("alpha", ctypes.c_float)]
+
+
+def _act(act):
+    """(limit, alpha) -> a pointer to SgeActParams (None -> NULL)."""
+    if act is None:
+        return None
+    limit, alpha = act
+    return ctypes.pointer(SgeActParams(float(limit), float(alpha)))
+
+
 class SgeError(RuntimeError):
     def __init__(self, status, message):
         super().__init__(f"{_lib.sge_status_string(status).decode()}: {message}")
@@ -61,6 +75,7 @@ class SgeError(RuntimeError):
 
 _vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 _OP = ctypes.POINTER(SgeOperand)
+_ACT = ctypes.POINTER(SgeActParams)
 _SIGS = {
     "sge_abi_version": ([], ctypes.c_int),
     "sge_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -71,28 +86,28 @@ _SIGS = {
     "sge_quantize_fp8_amax": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "sge_quantize_mxfp8": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "sge_splits_to_offsets": ([_vp, _i32, ctypes.POINTER(_i64), _i32, _i64, _vp, _vp, _vp], ctypes.c_int),
-    "sge_grouped_linear_fwd": ([_vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _vp, _vp, _vp, _vp],
+    "sge_grouped_linear_fwd": ([_vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _ACT, _vp, _vp, _vp, _vp],
                                ctypes.c_int),
-    "sge_grouped_linear_fwd_mxfp8": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _vp, _vp, _vp,
+    "sge_grouped_linear_fwd_mxfp8": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _ACT, _vp, _vp, _vp,
                                       _vp, _vp, _vp], ctypes.c_int),
     "sge_grouped_linear_bwd_workspace_size": ([_i64, _i64, _i32, _i32], _sz),
-    "sge_grouped_linear_bwd": ([_vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _vp, _vp, _vp, _vp,
+    "sge_grouped_linear_bwd": ([_vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _ACT, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "sge_scaled_swiglu_fwd": ([_vp, _vp, _vp, _i64, _i64, _vp], ctypes.c_int),
     "sge_scaled_swiglu_bwd": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp], ctypes.c_int),
     "sge_mx_token_capacity": ([_i64, _i32], _i64),
     "sge_mx_group_layout": ([_vp, _i32, _i64, _vp, _vp], ctypes.c_int),
     "sge_quantize_mxfp8_grouped": ([_vp, _i64, _i64, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
-    "sge_grouped_linear_dgrad_mxfp8": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _vp, _vp,
+    "sge_grouped_linear_dgrad_mxfp8": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _ACT, _vp, _vp,
                                         _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "sge_grouped_linear_wgrad_mxfp8": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _f32, _vp, _vp],
                                        ctypes.c_int),
     "sge_quantize_fp8_grouped_workspace_size": ([_i32], _sz),
     "sge_quantize_fp8_grouped": ([_vp, _i64, _i64, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                                  ctypes.c_int),
-    "sge_grouped_linear_fwd_fp8": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _vp, _vp, _vp,
+    "sge_grouped_linear_fwd_fp8": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _ACT, _vp, _vp, _vp,
                                     _vp, _vp], ctypes.c_int),
-    "sge_grouped_linear_dgrad_fp8": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _vp, _vp, _vp,
+    "sge_grouped_linear_dgrad_fp8": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _ACT, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "sge_grouped_linear_wgrad_fp8": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _f32, _vp, _vp],
                                      ctypes.c_int),
@@ -214,22 +229,24 @@ def splits_to_offsets(splits, multipliers, offsets, expected_total=-1, err_flag=
                                       _ptr(offsets), _ptr(err_flag), _stream(stream)))
 
 
-def grouped_linear_fwd(x, w, offsets, out, alpha=1.0, epilogue=EPI_NONE, probs=None, preact=None, stream=None):
-    """Grouped forward: x [T, K], w [G, N, K], offsets [G+1] (device) -> out (and preact for SwiGLU)."""
+def grouped_linear_fwd(x, w, offsets, out, alpha=1.0, epilogue=EPI_NONE, probs=None, preact=None, act=None,
+                       stream=None):
+    """Grouped forward: x [T, K], w [G, N, K], offsets [G+1] (device) -> out (and preact for SwiGLU).
+    ``act``: (limit, alpha) of the clamped SwiGLU epilogues."""
     G, N, K = w.shape
     T = x.shape[0]
     _check(_lib.sge_grouped_linear_fwd(_ptr(x), _ptr(w), G, T, N, K, _ptr(offsets), float(alpha), epilogue,
-                                       _ptr(probs), _ptr(out), _ptr(preact), _stream(stream)))
+                                       _act(act), _ptr(probs), _ptr(out), _ptr(preact), _stream(stream)))
 
 
 def grouped_linear_fwd_mxfp8(x_q, x_s, w_q, w_s, offsets, out=None, alpha=1.0, epilogue=EPI_NONE, probs=None,
-                             preact=None, out_q=None, out_s=None, stream=None):
+                             preact=None, out_q=None, out_s=None, act=None, stream=None):
     """Grouped forward with MXFP8 operands: x_q [T, K] u8 + x_s [T, K/32] u8, w_q [G, N, K] u8 +
     w_s [G, N, K/32] u8 (rowwise). SwiGLU may also emit out_q [T, N/2] + out_s [T, N/64]."""
     G, N, K = w_q.shape
     T = x_q.shape[0]
     _check(_lib.sge_grouped_linear_fwd_mxfp8(_ptr(x_q), _ptr(x_s), _ptr(w_q), _ptr(w_s), G, T, N, K, _ptr(offsets),
-                                             float(alpha), epilogue, _ptr(probs), _ptr(out), _ptr(preact),
+                                             float(alpha), epilogue, _act(act), _ptr(probs), _ptr(out), _ptr(preact),
                                              _ptr(out_q), _ptr(out_s), _stream(stream)))
 
 
@@ -238,14 +255,14 @@ def grouped_linear_bwd_workspace_size(T, K, G, epilogue):
 
 
 def grouped_linear_bwd(dy, x, w, offsets, alpha=1.0, epilogue=EPI_NONE, preact=None, probs=None, dact=None,
-                       dprobs=None, dx=None, dw=None, workspace=None, stream=None):
+                       dprobs=None, dx=None, dw=None, workspace=None, act=None, stream=None):
     """Grouped backward of one layer (see sge.h): dgrad (optionally through dSwiGLU) and wgrad."""
     G, N, K = w.shape
     T = dy.shape[0]
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.sge_grouped_linear_bwd(_ptr(dy), _ptr(x), _ptr(w), G, T, N, K, _ptr(offsets), float(alpha),
-                                       epilogue, _ptr(preact), _ptr(probs), _ptr(dact), _ptr(dprobs), _ptr(dx),
-                                       _ptr(dw), _ptr(workspace), ws_bytes, _stream(stream)))
+                                       epilogue, _act(act), _ptr(preact), _ptr(probs), _ptr(dact), _ptr(dprobs),
+                                       _ptr(dx), _ptr(dw), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 # ------------------------------------------------ MXFP8 grouped backward
@@ -274,7 +291,7 @@ def quantize_mxfp8_grouped(src, layout, q_colT, s_colT, q_row=None, s_row=None, 
 
 def grouped_linear_dgrad_mxfp8(dy_q, dy_s, w_q, w_s, offsets, alpha=1.0, epilogue=EPI_NONE, preact=None,
                                probs=None, dx=None, dact=None, dprobs=None, dact_q=None, dact_s=None,
-                               workspace=None, stream=None):
+                               workspace=None, act=None, stream=None):
     """MXFP8 grouped dgrad: dy_q [T, N] + dy_s [T, N/32] (rowwise), w_q [K, G*N] + w_s [K, G*N/32]
     (W viewed [G*N, K], quantized columnwise). SwiGLU backward writes dact / dact_q+dact_s and dprobs."""
     T, N = dy_q.shape
@@ -282,9 +299,9 @@ def grouped_linear_dgrad_mxfp8(dy_q, dy_s, w_q, w_s, offsets, alpha=1.0, epilogu
     G = offsets.numel() - 1
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.sge_grouped_linear_dgrad_mxfp8(_ptr(dy_q), _ptr(dy_s), _ptr(w_q), _ptr(w_s), G, T, N, K,
-                                               _ptr(offsets), float(alpha), epilogue, _ptr(preact), _ptr(probs),
-                                               _ptr(dx), _ptr(dact), _ptr(dprobs), _ptr(dact_q), _ptr(dact_s),
-                                               _ptr(workspace), ws_bytes, _stream(stream)))
+                                               _ptr(offsets), float(alpha), epilogue, _act(act), _ptr(preact),
+                                               _ptr(probs), _ptr(dx), _ptr(dact), _ptr(dprobs), _ptr(dact_q),
+                                               _ptr(dact_s), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def grouped_linear_wgrad_mxfp8(dyT_q, dyT_s, xT_q, xT_s, layout, dw, alpha=1.0, stream=None):
@@ -315,27 +332,27 @@ def quantize_fp8_grouped(src, G, amax, scale, scale_inv, workspace=None, layout=
 
 
 def grouped_linear_fwd_fp8(x_q, x_sinv, w_q, w_sinv, offsets, out, alpha=1.0, epilogue=EPI_NONE, probs=None,
-                           preact=None, out_amax=None, stream=None):
+                           preact=None, out_amax=None, act=None, stream=None):
     """Grouped forward on E4M3 operands with one scale_inv per group: x_q [T, K], w_q [G, N, K]."""
     G, N, K = w_q.shape
     T = x_q.shape[0]
     _check(_lib.sge_grouped_linear_fwd_fp8(_ptr(x_q), _ptr(x_sinv), _ptr(w_q), _ptr(w_sinv), G, T, N, K,
-                                           _ptr(offsets), float(alpha), epilogue, _ptr(probs), _ptr(out),
+                                           _ptr(offsets), float(alpha), epilogue, _act(act), _ptr(probs), _ptr(out),
                                            _ptr(preact), _ptr(out_amax), _stream(stream)))
 
 
 def grouped_linear_dgrad_fp8(dy_q, dy_sinv, w_qT, w_sinv, offsets, alpha=1.0, epilogue=EPI_NONE, preact=None,
                              probs=None, dx=None, dact=None, dprobs=None, dact_amax=None, workspace=None,
-                             stream=None):
+                             act=None, stream=None):
     """E4M3 grouped dgrad: dy_q [T, N], w_qT [K, G*N] (transpose of W viewed [G*N, K])."""
     T, N = dy_q.shape
     K = w_qT.shape[0]
     G = offsets.numel() - 1
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.sge_grouped_linear_dgrad_fp8(_ptr(dy_q), _ptr(dy_sinv), _ptr(w_qT), _ptr(w_sinv), G, T, N, K,
-                                             _ptr(offsets), float(alpha), epilogue, _ptr(preact), _ptr(probs),
-                                             _ptr(dx), _ptr(dact), _ptr(dprobs), _ptr(dact_amax), _ptr(workspace),
-                                             ws_bytes, _stream(stream)))
+                                             _ptr(offsets), float(alpha), epilogue, _act(act), _ptr(preact),
+                                             _ptr(probs), _ptr(dx), _ptr(dact), _ptr(dprobs), _ptr(dact_amax),
+                                             _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def grouped_linear_wgrad_fp8(dyT_q, dy_sinv, xT_q, x_sinv, layout, dw, alpha=1.0, stream=None):

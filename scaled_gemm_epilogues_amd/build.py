@@ -21,6 +21,10 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # Keep the compiler from forming packed fp32 (v_pk_*_f32) instructions.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Every `#pragma unroll` loop here is meant to unroll fully (the accumulator tiles are indexed
+    # by its counters); the default size cap left the clamped dSwiGLU epilogue's pass loop rolled,
+    # which put the MXFP8 tile's accumulators in scratch.
+    "-mllvm", "-pragma-unroll-threshold=65536",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -1,4 +1,5 @@
 // C ABI of libsge: argument validation (host only, before any HIP call) and dispatch.
+#include <cmath>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -139,6 +140,35 @@ sge_status check_gemm(const sge_operand* a, const sge_operand* b, const void* c,
 }
 
 }  // namespace
+
+// Epilogues the grouped calls take. Gated ones split the pre-activation into two halves.
+bool fwd_epilogue_ok(int32_t e) {
+  return e == SGE_EPI_NONE || e == SGE_EPI_SCALED_SWIGLU || e == SGE_EPI_SCALED_SRELU ||
+         e == SGE_EPI_SCALED_CLAMPED_SWIGLU;
+}
+bool bwd_epilogue_ok(int32_t e) {
+  return e == SGE_EPI_NONE || e == SGE_EPI_DSCALED_SWIGLU || e == SGE_EPI_DSCALED_SRELU ||
+         e == SGE_EPI_DSCALED_CLAMPED_SWIGLU;
+}
+bool gated_fwd(int32_t e) { return e == SGE_EPI_SCALED_SWIGLU || e == SGE_EPI_SCALED_CLAMPED_SWIGLU; }
+bool gated_bwd(int32_t e) { return e == SGE_EPI_DSCALED_SWIGLU || e == SGE_EPI_DSCALED_CLAMPED_SWIGLU; }
+bool clamped(int32_t e) { return e == SGE_EPI_SCALED_CLAMPED_SWIGLU || e == SGE_EPI_DSCALED_CLAMPED_SWIGLU; }
+
+// The clamped SwiGLU needs its parameters: limit > 0 and finite, alpha finite.
+sge_status check_act(int32_t e, const sge_act_params* act, const char* what) {
+  if (!clamped(e)) return SGE_OK;
+  if (!act) return fail(SGE_ERR_NULL, "%s: the clamped SwiGLU needs act (limit, alpha)", what);
+  if (!(act->limit > 0.0f) || !std::isfinite(act->limit) || !std::isfinite(act->alpha))
+    return fail(SGE_ERR_ARG, "%s: clamped SwiGLU limit must be finite and > 0, alpha finite", what);
+  return SGE_OK;
+}
+
+void set_act(sge::GemmParams& p, int32_t e, const sge_act_params* act) {
+  if (clamped(e)) {
+    p.act_limit = act->limit;
+    p.act_alpha = act->alpha;
+  }
+}
 
 extern "C" {
 
@@ -299,19 +329,21 @@ sge_status sge_splits_to_offsets(const int64_t* splits, int32_t G, const int64_t
 }
 
 sge_status sge_grouped_linear_fwd(const void* x, const void* w, int32_t G, int64_t T, int64_t N, int64_t K,
-                                  const int64_t* offsets, float alpha, int32_t epilogue, const float* probs, void* out,
-                                  void* preact, hipStream_t stream) {
+                                  const int64_t* offsets, float alpha, int32_t epilogue,
+                                  const sge_act_params* act_params, const float* probs, void* out, void* preact,
+                                  hipStream_t stream) {
   if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd: bad sizes");
-  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_SCALED_SWIGLU && epilogue != SGE_EPI_SCALED_SRELU)
+  if (!fwd_epilogue_ok(epilogue))
     return fail(SGE_ERR_ARG, "grouped_linear_fwd: epilogue %d not allowed", epilogue);
   if (!x || !w || !offsets || !out) return fail(SGE_ERR_NULL, "grouped_linear_fwd: NULL pointer");
   if (epilogue != SGE_EPI_NONE && !probs) return fail(SGE_ERR_NULL, "grouped_linear_fwd: probs is NULL");
+  if (sge_status st = check_act(epilogue, act_params, "grouped_linear_fwd")) return st;
   if (K % 8 || N % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd: N and K must be multiples of 8");
-  if (epilogue == SGE_EPI_SCALED_SWIGLU && N % 256)
+  if (gated_fwd(epilogue) && N % 256)
     return fail(SGE_ERR_SHAPE, "grouped_linear_fwd: SwiGLU needs N %% 256 == 0");
   if (!aligned16(x) || !aligned16(w) || !aligned16(out) || (preact && !aligned16(preact)))
     return fail(SGE_ERR_ALIGN, "grouped_linear_fwd: pointers must be 16-byte aligned");
-  const int64_t out_cols = epilogue == SGE_EPI_SCALED_SWIGLU ? N / 2 : N;
+  const int64_t out_cols = gated_fwd(epilogue) ? N / 2 : N;
   const Range ro = range_of(out, T, out_cols, out_cols, 2);
   if (overlap(ro, range_of(x, T, K, K, 2)) || overlap(ro, range_of(w, (int64_t)G * N, K, K, 2)) ||
       (preact && overlap(range_of(preact, T, N, N, 2), ro)))
@@ -337,17 +369,19 @@ sge_status sge_grouped_linear_fwd(const void* x, const void* w, int32_t G, int64
   p.aux = static_cast<uint16_t*>(preact);
   p.ld_aux = N;
   p.F = N / 2;
+  set_act(p, epilogue, act_params);
   return hip_status(sge::launch_grouped_fwd(p, epilogue, stream), "grouped fwd launch");
 }
 
 sge_status sge_grouped_linear_fwd_mxfp8(const void* x_q, const void* x_s, const void* w_q, const void* w_s, int32_t G,
                                         int64_t T, int64_t N, int64_t K, const int64_t* offsets, float alpha,
-                                        int32_t epilogue, const float* probs, void* out, void* preact, void* out_q,
-                                        void* out_s, hipStream_t stream) {
+                                        int32_t epilogue, const sge_act_params* act_params, const float* probs,
+                                        void* out, void* preact, void* out_q, void* out_s, hipStream_t stream) {
   if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_mxfp8: bad sizes");
-  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_SCALED_SWIGLU && epilogue != SGE_EPI_SCALED_SRELU)
+  if (!fwd_epilogue_ok(epilogue))
     return fail(SGE_ERR_ARG, "grouped_linear_fwd_mxfp8: epilogue %d not allowed", epilogue);
-  const bool swiglu = epilogue == SGE_EPI_SCALED_SWIGLU;
+  if (sge_status st = check_act(epilogue, act_params, "grouped_linear_fwd_mxfp8")) return st;
+  const bool swiglu = gated_fwd(epilogue);
   const bool act = epilogue != SGE_EPI_NONE;                      // a scaled activation in the epilogue
   if (!x_q || !x_s || !w_q || !w_s || !offsets) return fail(SGE_ERR_NULL, "grouped_linear_fwd_mxfp8: NULL pointer");
   if ((out_q == nullptr) != (out_s == nullptr))
@@ -406,25 +440,28 @@ sge_status sge_grouped_linear_fwd_mxfp8(const void* x_q, const void* x_s, const 
   p.q_out = static_cast<uint8_t*>(out_q);
   p.s_out = static_cast<uint8_t*>(out_s);
   p.ld_q = out_cols;
+  set_act(p, epilogue, act_params);
   return hip_status(sge::launch_grouped_fwd_mx(p, epilogue, stream), "grouped fwd mxfp8 launch");
 }
 
 size_t sge_grouped_linear_bwd_workspace_size(int64_t T, int64_t K, int32_t G, int32_t epilogue) {
   (void)G;
-  if ((epilogue != SGE_EPI_DSCALED_SWIGLU && epilogue != SGE_EPI_DSCALED_SRELU) || T <= 0 || K <= 0) return 0;
+  if (epilogue == SGE_EPI_NONE || !bwd_epilogue_ok(epilogue) || T <= 0 || K <= 0) return 0;
   const int64_t parts = sge::gemm_dp_parts_per_tile() * ((K + sge::gemm_tile_n() - 1) / sge::gemm_tile_n());
   return (size_t)(parts * T) * sizeof(float);
 }
 
 sge_status sge_grouped_linear_bwd(const void* dy, const void* x, const void* w, int32_t G, int64_t T, int64_t N,
-                                  int64_t K, const int64_t* offsets, float alpha, int32_t epilogue, const void* preact,
-                                  const float* probs, void* dact, float* dprobs, void* dx, void* dw, void* workspace,
+                                  int64_t K, const int64_t* offsets, float alpha, int32_t epilogue,
+                                  const sge_act_params* act_params, const void* preact, const float* probs,
+                                  void* dact, float* dprobs, void* dx, void* dw, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream) {
   if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_bwd: bad sizes");
-  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_DSCALED_SWIGLU && epilogue != SGE_EPI_DSCALED_SRELU)
+  if (!bwd_epilogue_ok(epilogue))
     return fail(SGE_ERR_ARG, "grouped_linear_bwd: epilogue %d not allowed", epilogue);
+  if (sge_status st = check_act(epilogue, act_params, "grouped_linear_bwd")) return st;
   const bool swiglu = epilogue != SGE_EPI_NONE;                  // an activation backward in the epilogue
-  const int64_t hw = epilogue == SGE_EPI_DSCALED_SWIGLU ? 2 * K : K;   // pre-activation / dact width
+  const int64_t hw = gated_bwd(epilogue) ? 2 * K : K;   // pre-activation / dact width
   if (!dy || !w || !offsets) return fail(SGE_ERR_NULL, "grouped_linear_bwd: NULL pointer");
   if (dw && !x) return fail(SGE_ERR_NULL, "grouped_linear_bwd: x is NULL");
   if (swiglu && (!preact || !probs || !dact || !dprobs))
@@ -474,6 +511,7 @@ sge_status sge_grouped_linear_bwd(const void* dy, const void* x, const void* w, 
       p.dp_part = static_cast<float*>(workspace);
       p.F = K;
     }
+    set_act(p, epilogue, act_params);
     e = sge::launch_grouped_dgrad(p, epilogue, stream);
     if (e != hipSuccess) return hip_status(e, "grouped dgrad launch");
     if (swiglu) {
@@ -554,14 +592,16 @@ sge_status sge_quantize_mxfp8_grouped(const void* src, int64_t T, int64_t cols, 
 
 sge_status sge_grouped_linear_dgrad_mxfp8(const void* dy_q, const void* dy_s, const void* w_q, const void* w_s,
                                           int32_t G, int64_t T, int64_t N, int64_t K, const int64_t* offsets,
-                                          float alpha, int32_t epilogue, const void* preact, const float* probs,
+                                          float alpha, int32_t epilogue, const sge_act_params* act_params,
+                                          const void* preact, const float* probs,
                                           void* dx, void* dact, float* dprobs, void* dact_q, void* dact_s,
                                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_mxfp8: bad sizes");
-  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_DSCALED_SWIGLU && epilogue != SGE_EPI_DSCALED_SRELU)
+  if (!bwd_epilogue_ok(epilogue))
     return fail(SGE_ERR_ARG, "grouped_linear_dgrad_mxfp8: epilogue %d not allowed", epilogue);
+  if (sge_status st = check_act(epilogue, act_params, "grouped_linear_dgrad_mxfp8")) return st;
   const bool swiglu = epilogue != SGE_EPI_NONE;                  // an activation backward in the epilogue
-  const int64_t hw = epilogue == SGE_EPI_DSCALED_SWIGLU ? 2 * K : K;   // pre-activation / dact width
+  const int64_t hw = gated_bwd(epilogue) ? 2 * K : K;   // pre-activation / dact width
   if (!dy_q || !dy_s || !w_q || !w_s || !offsets) return fail(SGE_ERR_NULL, "grouped_linear_dgrad_mxfp8: NULL pointer");
   if ((dact_q == nullptr) != (dact_s == nullptr))
     return fail(SGE_ERR_NULL, "grouped_linear_dgrad_mxfp8: dact_q and dact_s go together");
@@ -631,6 +671,7 @@ sge_status sge_grouped_linear_dgrad_mxfp8(const void* dy_q, const void* dy_s, co
     p.s_out = static_cast<uint8_t*>(dact_s);
     p.ld_q = hw;
   }
+  set_act(p, epilogue, act_params);
   hipError_t e = sge::launch_grouped_dgrad_mx(p, epilogue, stream);
   if (e != hipSuccess) return hip_status(e, "grouped dgrad mxfp8 launch");
   if (swiglu) {
@@ -733,12 +774,13 @@ sge_status sge_quantize_fp8_grouped(const void* src, int64_t rows, int64_t cols,
 
 sge_status sge_grouped_linear_fwd_fp8(const void* x_q, const float* x_sinv, const void* w_q, const float* w_sinv,
                                       int32_t G, int64_t T, int64_t N, int64_t K, const int64_t* offsets, float alpha,
-                                      int32_t epilogue, const float* probs, void* out, void* preact, float* out_amax,
-                                      hipStream_t stream) {
+                                      int32_t epilogue, const sge_act_params* act_params, const float* probs,
+                                      void* out, void* preact, float* out_amax, hipStream_t stream) {
   if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_fp8: bad sizes");
-  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_SCALED_SWIGLU && epilogue != SGE_EPI_SCALED_SRELU)
+  if (!fwd_epilogue_ok(epilogue))
     return fail(SGE_ERR_ARG, "grouped_linear_fwd_fp8: epilogue %d not allowed", epilogue);
-  const bool swiglu = epilogue == SGE_EPI_SCALED_SWIGLU;
+  if (sge_status st = check_act(epilogue, act_params, "grouped_linear_fwd_fp8")) return st;
+  const bool swiglu = gated_fwd(epilogue);
   const bool act = epilogue != SGE_EPI_NONE;
   if (!x_q || !x_sinv || !w_q || !w_sinv || !offsets || !out) return fail(SGE_ERR_NULL, "grouped_linear_fwd_fp8: NULL pointer");
   if (act && !probs) return fail(SGE_ERR_NULL, "grouped_linear_fwd_fp8: probs is NULL");
@@ -786,19 +828,22 @@ sge_status sge_grouped_linear_fwd_fp8(const void* x_q, const float* x_sinv, cons
   p.ld_aux = N;
   p.F = N / 2;
   p.amax_out = out_amax;
+  set_act(p, epilogue, act_params);
   return hip_status(sge::launch_grouped_fwd_fp8(p, epilogue, stream), "grouped fwd fp8 launch");
 }
 
 sge_status sge_grouped_linear_dgrad_fp8(const void* dy_q, const float* dy_sinv, const void* w_qT, const float* w_sinv,
                                         int32_t G, int64_t T, int64_t N, int64_t K, const int64_t* offsets,
-                                        float alpha, int32_t epilogue, const void* preact, const float* probs,
+                                        float alpha, int32_t epilogue, const sge_act_params* act_params,
+                                        const void* preact, const float* probs,
                                         void* dx, void* dact, float* dprobs, float* dact_amax, void* workspace,
                                         size_t workspace_bytes, hipStream_t stream) {
   if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_fp8: bad sizes");
-  if (epilogue != SGE_EPI_NONE && epilogue != SGE_EPI_DSCALED_SWIGLU && epilogue != SGE_EPI_DSCALED_SRELU)
+  if (!bwd_epilogue_ok(epilogue))
     return fail(SGE_ERR_ARG, "grouped_linear_dgrad_fp8: epilogue %d not allowed", epilogue);
+  if (sge_status st = check_act(epilogue, act_params, "grouped_linear_dgrad_fp8")) return st;
   const bool swiglu = epilogue != SGE_EPI_NONE;                  // an activation backward in the epilogue
-  const int64_t hw = epilogue == SGE_EPI_DSCALED_SWIGLU ? 2 * K : K;   // pre-activation / dact width
+  const int64_t hw = gated_bwd(epilogue) ? 2 * K : K;   // pre-activation / dact width
   if (!dy_q || !dy_sinv || !w_qT || !w_sinv || !offsets) return fail(SGE_ERR_NULL, "grouped_linear_dgrad_fp8: NULL pointer");
   if (swiglu && (!preact || !probs || !dact || !dprobs))
     return fail(SGE_ERR_NULL, "grouped_linear_dgrad_fp8: an activation backward needs preact, probs, dact and dprobs");
@@ -854,6 +899,7 @@ sge_status sge_grouped_linear_dgrad_fp8(const void* dy_q, const float* dy_sinv, 
     p.F = K;
     p.amax_out = dact_amax;
   }
+  set_act(p, epilogue, act_params);
   hipError_t e = sge::launch_grouped_dgrad_fp8(p, epilogue, stream);
   if (e != hipSuccess) return hip_status(e, "grouped dgrad fp8 launch");
   if (swiglu) {

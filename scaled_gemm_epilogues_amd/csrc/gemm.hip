@@ -37,7 +37,9 @@
 namespace sge {
 
 enum { F_BF16 = 0, F_E4M3 = 1, F_MX = 2, F_MXU = 3 };   // F_MXU: MXFP8 with unaligned scale rows
-enum { E_STORE = 0, E_SWIGLU = 1, E_DSWIGLU = 2, E_SRELU = 3, E_DSRELU = 4 };
+enum { E_STORE = 0, E_SWIGLU = 1, E_DSWIGLU = 2, E_SRELU = 3, E_DSRELU = 4, E_CSWIGLU = 5, E_DCSWIGLU = 6 };
+// Gated forward epilogues: B's rows are the gate / up halves interleaved per tile, output F wide.
+constexpr bool glu_fwd(int e) { return e == E_SWIGLU || e == E_CSWIGLU; }
 enum { S_DENSE = 0, S_GROUP_M = 1, S_GROUP_K = 2 };
 
 constexpr int kRowBytes = 128;   // contraction bytes per LDS row and per k-tile
@@ -316,7 +318,7 @@ void gemm_kernel(const GemmParams p) {
     grp = g;
     m0 = lo + (int64_t)lin * BM;
     row_end = hi;
-    n0 = (int64_t)nt * (EPI == E_SWIGLU ? BN / 2 : BN);
+    n0 = (int64_t)nt * (glu_fwd(EPI) ? BN / 2 : BN);
     bptr += (int64_t)g * p.b_group_stride * ES;
     if constexpr (FMT == F_MX || FMT == F_MXU) bmx += (int64_t)g * p.b_mx_group_stride;
   } else {
@@ -349,7 +351,7 @@ void gemm_kernel(const GemmParams p) {
     row_end = p.M;
     cptr += (int64_t)g * p.c_group_stride;
   }
-  const int64_t n_end = EPI == E_SWIGLU ? p.F : p.N;
+  const int64_t n_end = glu_fwd(EPI) ? p.F : p.N;
 
   // ---------------------------------------------------------------- main loop
   f32x16 acc[WMF][WNF];
@@ -363,7 +365,7 @@ void gemm_kernel(const GemmParams p) {
   IdentityRows idrows;
   SwigluRows<WN> swrows{p.F};
   // Rows of B: N (dense / group M, 2F for SwiGLU), or the N_out rows of group K.
-  const int64_t b_rows = EPI == E_SWIGLU ? 2 * p.F : p.N;
+  const int64_t b_rows = glu_fwd(EPI) ? 2 * p.F : p.N;
 
   // Tile copies. Inner-contiguous operands are addressed from their first tile row,
   // outer-contiguous ones from the tile's first outer column of contraction row 0.
@@ -374,7 +376,7 @@ void gemm_kernel(const GemmParams p) {
   const uint8_t* b_base = BK ? bptr + n0 * p.ldb * ES : bptr + n0 * 2;
   const int64_t b_bytes = BK ? (b_rows - n0) * p.ldb * ES : p.K * p.ldb * 2 - n0 * 2;
   ca.init(p.lda, m0, row_end, idrows);
-  if constexpr (EPI == E_SWIGLU) cb.init(p.ldb, n0, b_rows, swrows);
+  if constexpr (glu_fwd(EPI)) cb.init(p.ldb, n0, b_rows, swrows);
   else cb.init(p.ldb, n0, b_rows, idrows);
 
   auto issue_tile = [&](uint8_t* buf, int64_t k0) {
@@ -401,7 +403,7 @@ void gemm_kernel(const GemmParams p) {
         const bool is_a = piece < BM / 64;
         const int r = (is_a ? piece : piece - BM / 64) * 64 + lane;
         // B rows follow the tile's row map (the SwiGLU gate/up interleave)
-        const int64_t row = is_a ? m0 + r : (EPI == E_SWIGLU ? swrows(n0, r) : n0 + r);
+        const int64_t row = is_a ? m0 + r : (glu_fwd(EPI) ? swrows(n0, r) : n0 + r);
         const bool ok = row < (is_a ? row_end : b_rows) && blk0 < nblk;
         const uint8_t* base = is_a ? p.a_mx : bmx;
         const int64_t ld = is_a ? p.a_mx_ld : p.b_mx_ld;
@@ -446,7 +448,7 @@ void gemm_kernel(const GemmParams p) {
 #pragma unroll
       for (int j = 0; j < WNF; ++j) {
         const int rr = wn * WN + j * 32 + (lane & 31);
-        const int64_t row = EPI == E_SWIGLU ? swrows(n0, rr) : n0 + rr;
+        const int64_t row = glu_fwd(EPI) ? swrows(n0, rr) : n0 + rr;
         uint32_t v = 0x7F7F7F7Fu;
         if (row < b_rows) {
           const uint8_t* s = bmx + row * p.b_mx_ld + blk0;
@@ -730,7 +732,7 @@ void gemm_kernel(const GemmParams p) {
         slot_to_group(&amax_slot, p.amax_out, grp);
       }
     }
-  } else if constexpr (EPI == E_SWIGLU) {
+  } else if constexpr (glu_fwd(EPI)) {
     // Staged like E_STORE: alpha*acc (each wave column holds WN/2 gate columns a, then the
     // matching WN/2 up columns b) goes to LDS, then each thread takes 8 consecutive output
     // columns of one row: y = p * silu(a) * b, and 16-byte stores of bf16 y and of the two
@@ -810,7 +812,16 @@ void gemm_kernel(const GemmParams p) {
         const float pm = pr[it];
         float y[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = pm * (a[e] * fast_sigmoid(a[e])) * b[e];
+        for (int e = 0; e < 8; ++e) {
+          if constexpr (EPI == E_CSWIGLU) {
+            // clamped: gate min(a, limit) through u * sigmoid(act_alpha * u), up clamp(b) + 1
+            const float ac = fminf(a[e], p.act_limit);
+            const float bc = __builtin_amdgcn_fmed3f(b[e], -p.act_limit, p.act_limit) + 1.0f;
+            y[e] = pm * (ac * fast_sigmoid(p.act_alpha * ac)) * bc;
+          } else {
+            y[e] = pm * (a[e] * fast_sigmoid(a[e])) * b[e];
+          }
+        }
         const v4i va = {(int)pack_bf16x2(a[0], a[1]), (int)pack_bf16x2(a[2], a[3]), (int)pack_bf16x2(a[4], a[5]),
                         (int)pack_bf16x2(a[6], a[7])};
         const v4i vb = {(int)pack_bf16x2(b[0], b[1]), (int)pack_bf16x2(b[2], b[3]), (int)pack_bf16x2(b[4], b[5]),
@@ -839,7 +850,7 @@ void gemm_kernel(const GemmParams p) {
         slot_to_group(&amax_slot, p.amax_out, grp);
       }
     }
-  } else {  // E_DSWIGLU, E_DSRELU
+  } else {  // E_DSWIGLU, E_DSRELU, E_DCSWIGLU
     // Staged like E_STORE: g = alpha*acc for half of each wave's rows goes to LDS, then each
     // thread takes 8 consecutive columns of one row: 16-byte loads of a and b (the two halves
     // of the saved pre-activation), 16-byte stores of da and db. A row's BN/8 chunks are 32
@@ -850,6 +861,9 @@ void gemm_kernel(const GemmParams p) {
     // E_DSRELU (scaled squared ReLU): one pre-activation h [T, F]; dh = g * p * 2 max(h, 0),
     // dprobs partial sum of g * max(h, 0)^2.
     constexpr bool kSR = EPI == E_DSRELU;
+    // E_DCSWIGLU (clamped SwiGLU): the gate's gradient passes where a <= limit, the up half's
+    // where |b| <= limit (a clamp passes it inside its closed interval), from the clamped values.
+    constexpr bool kCl = EPI == E_DCSWIGLU;
     const int64_t hbytes = rows_left * p.ld_aux * 2;
     const int64_t dbytes = p.aux_out ? rows_left * p.ld_aux_out * 2 : 0;
     // One resource per tensor; the b half sits F columns further (an out-of-range offset
@@ -936,6 +950,18 @@ void gemm_kernel(const GemmParams p) {
             da[e] = g[e] * pm * 2.0f * rl;
             db[e] = 0.0f;
             part += g[e] * rl * rl;
+          } else if constexpr (kCl) {
+            const uint32_t wb = (uint32_t)hb[ib][e >> 1];
+            const float b = (e & 1) ? bf16_hi(wb) : bf16_lo(wb);
+            const float lim = p.act_limit, al = p.act_alpha;
+            const float ac = fminf(a, lim);
+            const float bc = __builtin_amdgcn_fmed3f(b, -lim, lim) + 1.0f;
+            const float sg = fast_sigmoid(al * ac);
+            const float q = ac * sg;
+            const float dq = sg * (1.0f + al * ac * (1.0f - sg));
+            da[e] = a <= lim ? g[e] * pm * bc * dq : 0.0f;
+            db[e] = fabsf(b) <= lim ? g[e] * pm * q : 0.0f;
+            part += g[e] * q * bc;
           } else {
             const uint32_t wb = (uint32_t)hb[ib][e >> 1];
             const float b = (e & 1) ? bf16_hi(wb) : bf16_lo(wb);
@@ -1010,8 +1036,8 @@ static hipError_t launch_tile(GemmParams p, hipStream_t s) {
     p.nt_count = (int)((p.N + BN - 1) / BN);
     grid = p.mt_count * p.nt_count;
   } else if constexpr (SCHED == S_GROUP_M) {
-    const int64_t ncols = EPI == E_SWIGLU ? p.F : p.N;
-    const int64_t ntile = EPI == E_SWIGLU ? BN / 2 : BN;
+    const int64_t ncols = glu_fwd(EPI) ? p.F : p.N;
+    const int64_t ntile = glu_fwd(EPI) ? BN / 2 : BN;
     p.nt_count = (int)((ncols + ntile - 1) / ntile);
     const int64_t mtiles = (p.T + BM - 1) / BM + p.G;     // upper bound over any split
     grid = (int)(mtiles * p.nt_count);
@@ -1038,18 +1064,21 @@ hipError_t launch_gemm(const GemmParams& p, int fmt, bool a_kmaj, bool b_kmaj, h
 hipError_t launch_grouped_fwd(const GemmParams& p, int epilogue, hipStream_t s) {
   if (epilogue == E_SWIGLU) return launch_tile<F_BF16, true, true, E_SWIGLU, S_GROUP_M>(p, s);
   if (epilogue == E_SRELU) return launch_tile<F_BF16, true, true, E_SRELU, S_GROUP_M>(p, s);
+  if (epilogue == E_CSWIGLU) return launch_tile<F_BF16, true, true, E_CSWIGLU, S_GROUP_M>(p, s);
   return launch_tile<F_BF16, true, true, E_STORE, S_GROUP_M>(p, s);
 }
 
 hipError_t launch_grouped_fwd_mx(const GemmParams& p, int epilogue, hipStream_t s) {
   if (epilogue == E_SWIGLU) return launch_tile<F_MX, true, true, E_SWIGLU, S_GROUP_M>(p, s);
   if (epilogue == E_SRELU) return launch_tile<F_MX, true, true, E_SRELU, S_GROUP_M>(p, s);
+  if (epilogue == E_CSWIGLU) return launch_tile<F_MX, true, true, E_CSWIGLU, S_GROUP_M>(p, s);
   return launch_tile<F_MX, true, true, E_STORE, S_GROUP_M>(p, s);
 }
 
 hipError_t launch_grouped_dgrad(const GemmParams& p, int epilogue, hipStream_t s) {
   if (epilogue == E_DSWIGLU) return launch_tile<F_BF16, true, false, E_DSWIGLU, S_GROUP_M>(p, s);
   if (epilogue == E_DSRELU) return launch_tile<F_BF16, true, false, E_DSRELU, S_GROUP_M>(p, s);
+  if (epilogue == E_DCSWIGLU) return launch_tile<F_BF16, true, false, E_DCSWIGLU, S_GROUP_M>(p, s);
   return launch_tile<F_BF16, true, false, E_STORE, S_GROUP_M>(p, s);
 }
 
@@ -1060,12 +1089,14 @@ hipError_t launch_grouped_wgrad(const GemmParams& p, hipStream_t s) {
 hipError_t launch_grouped_fwd_fp8(const GemmParams& p, int epilogue, hipStream_t s) {
   if (epilogue == E_SWIGLU) return launch_tile<F_E4M3, true, true, E_SWIGLU, S_GROUP_M>(p, s);
   if (epilogue == E_SRELU) return launch_tile<F_E4M3, true, true, E_SRELU, S_GROUP_M>(p, s);
+  if (epilogue == E_CSWIGLU) return launch_tile<F_E4M3, true, true, E_CSWIGLU, S_GROUP_M>(p, s);
   return launch_tile<F_E4M3, true, true, E_STORE, S_GROUP_M>(p, s);
 }
 
 hipError_t launch_grouped_dgrad_fp8(const GemmParams& p, int epilogue, hipStream_t s) {
   if (epilogue == E_DSWIGLU) return launch_tile<F_E4M3, true, true, E_DSWIGLU, S_GROUP_M>(p, s);
   if (epilogue == E_DSRELU) return launch_tile<F_E4M3, true, true, E_DSRELU, S_GROUP_M>(p, s);
+  if (epilogue == E_DCSWIGLU) return launch_tile<F_E4M3, true, true, E_DCSWIGLU, S_GROUP_M>(p, s);
   return launch_tile<F_E4M3, true, true, E_STORE, S_GROUP_M>(p, s);
 }
 
@@ -1076,6 +1107,7 @@ hipError_t launch_grouped_wgrad_fp8(const GemmParams& p, hipStream_t s) {
 hipError_t launch_grouped_dgrad_mx(const GemmParams& p, int epilogue, hipStream_t s) {
   if (epilogue == E_DSWIGLU) return launch_tile<F_MX, true, true, E_DSWIGLU, S_GROUP_M>(p, s);
   if (epilogue == E_DSRELU) return launch_tile<F_MX, true, true, E_DSRELU, S_GROUP_M>(p, s);
+  if (epilogue == E_DCSWIGLU) return launch_tile<F_MX, true, true, E_DCSWIGLU, S_GROUP_M>(p, s);
   return launch_tile<F_MX, true, true, E_STORE, S_GROUP_M>(p, s);
 }
 

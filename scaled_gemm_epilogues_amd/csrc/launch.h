@@ -46,6 +46,8 @@ struct GemmParams {
   int64_t b_mx_bytes;         // MXFP8: bytes of B's whole scale array from b_mx (0: rows x ld)
   int sinv_per_group;         // E4M3 grouped: a_sinv / b_sinv are [G], indexed by the group
   float* amax_out;            // (d)SwiGLU: per-group amax of the bf16 output, atomic max (zeroed by the caller)
+  float act_limit;            // clamped SwiGLU: the clamp bound (gate above, up half both ways)
+  float act_alpha;            //   and the gate's sigmoid slope
 };
 
 hipError_t launch_gemm(const GemmParams& p, int fmt, bool a_kmaj, bool b_kmaj, hipStream_t s);

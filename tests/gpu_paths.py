@@ -100,9 +100,9 @@ def run_grouped_mlp(inp, with_backward=True, act="swiglu"):
     splits = torch.from_numpy(inp["splits"]).cuda()
     T, H = X.shape
     G, N1, _ = W1.shape
-    F = N1 // 2 if act == "swiglu" else N1
-    fwd_epi = sge.EPI_SCALED_SWIGLU if act == "swiglu" else sge.EPI_SCALED_SRELU
-    bwd_epi = sge.EPI_DSCALED_SWIGLU if act == "swiglu" else sge.EPI_DSCALED_SRELU
+    width, fwd_epi, bwd_epi = _act_epilogues(act)
+    F = width(N1)
+    ap = _act_params(act)
     offs = torch.empty(1, G + 1, dtype=torch.int64, device="cuda")
     err = torch.empty(1, dtype=torch.int32, device="cuda")
     sge.splits_to_offsets(splits, [1], offs, expected_total=T, err_flag=err)
@@ -110,7 +110,7 @@ def run_grouped_mlp(inp, with_backward=True, act="swiglu"):
     h = torch.empty(T, N1, dtype=torch.bfloat16, device="cuda")
     y = torch.empty(T, F, dtype=torch.bfloat16, device="cuda")
     out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
-    sge.grouped_linear_fwd(X, W1, base, y, epilogue=fwd_epi, probs=P, preact=h)
+    sge.grouped_linear_fwd(X, W1, base, y, epilogue=fwd_epi, probs=P, preact=h, act=ap)
     sge.grouped_linear_fwd(y, W2, base, out)
     res = {"offsets": offs, "err": err, "h": h, "y": y, "out": out}
     if with_backward:
@@ -121,7 +121,7 @@ def run_grouped_mlp(inp, with_backward=True, act="swiglu"):
         ws = torch.empty(max(1, sge.grouped_linear_bwd_workspace_size(T, F, G, bwd_epi)),
                          dtype=torch.uint8, device="cuda")
         sge.grouped_linear_bwd(DOUT, y, W2, base, epilogue=bwd_epi, preact=h, probs=P, dact=dh,
-                               dprobs=dp, dw=dw2, workspace=ws)
+                               dprobs=dp, dw=dw2, workspace=ws, act=ap)
         dx = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
         dw1 = torch.empty(G, N1, H, dtype=torch.bfloat16, device="cuda")
         sge.grouped_linear_bwd(dh, X, W1, base, dx=dx, dw=dw1)
@@ -131,12 +131,20 @@ def run_grouped_mlp(inp, with_backward=True, act="swiglu"):
 
 
 def _act_epilogues(act):
-    """(fc1 width from W1's rows, forward epilogue, backward epilogue) of an activation."""
+    """(fc1 width from W1's rows, forward epilogue, backward epilogue) of an activation:
+    "swiglu", "srelu", or ("clamped_swiglu", limit, alpha) as the oracle names them."""
     if act == "swiglu":
         return (lambda n1: n1 // 2), sge.EPI_SCALED_SWIGLU, sge.EPI_DSCALED_SWIGLU
     if act == "srelu":
         return (lambda n1: n1), sge.EPI_SCALED_SRELU, sge.EPI_DSCALED_SRELU
+    if isinstance(act, tuple) and act[0] == "clamped_swiglu":
+        return (lambda n1: n1 // 2), sge.EPI_SCALED_CLAMPED_SWIGLU, sge.EPI_DSCALED_CLAMPED_SWIGLU
     raise ValueError(act)
+
+
+def _act_params(act):
+    """(limit, alpha) of a clamped activation, else None."""
+    return tuple(act[1:]) if isinstance(act, tuple) else None
 
 
 def run_grouped_mlp_fwd_mx(inp, act="swiglu"):
@@ -162,7 +170,7 @@ def run_grouped_mlp_fwd_mx(inp, act="swiglu"):
     out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
     sge.grouped_linear_fwd_mxfp8(qx["q_row"], qx["s_row"], qw1["q_row"].reshape(G, N1, H),
                                  qw1["s_row"].reshape(G, N1, H // 32), base, out=y, epilogue=fwd_epi,
-                                 probs=P, preact=h, out_q=yq, out_s=ys)
+                                 probs=P, preact=h, out_q=yq, out_s=ys, act=_act_params(act))
     sge.grouped_linear_fwd_mxfp8(yq, ys, qw2["q_row"].reshape(G, H, F), qw2["s_row"].reshape(G, H, F // 32), base,
                                  out=out)
     y_unfused = quant_mx(y, col=False)                    # the standalone quantizer on the bf16 y
@@ -211,7 +219,7 @@ def grouped_dgrad_mx(q_dy, w_colT, base, alpha=1.0, preact=None, probs=None, wan
                                        alpha=alpha, dx=out["dx"])
         return out
     _, _, epi = _act_epilogues(act)
-    hw = 2 * K if act == "swiglu" else K
+    hw = K if act == "srelu" else 2 * K                  # gated activations: two halves
     ws = torch.empty(max(1, sge.grouped_linear_bwd_workspace_size(T, K, G, epi)), dtype=torch.uint8, device="cuda")
     out["dact"] = torch.empty(T, hw, dtype=torch.bfloat16, device="cuda")
     out["dprobs"] = torch.empty(T, dtype=torch.float32, device="cuda")
@@ -221,7 +229,7 @@ def grouped_dgrad_mx(q_dy, w_colT, base, alpha=1.0, preact=None, probs=None, wan
     sge.grouped_linear_dgrad_mxfp8(q_dy["q_row"], q_dy["s_row"], w_colT["q_colT"], w_colT["s_colT"], base,
                                    alpha=alpha, epilogue=epi, preact=preact, probs=probs,
                                    dact=out["dact"], dprobs=out["dprobs"], dact_q=out.get("dact_q"),
-                                   dact_s=out.get("dact_s"), workspace=ws)
+                                   dact_s=out.get("dact_s"), workspace=ws, act=_act_params(act))
     return out
 
 
@@ -304,7 +312,7 @@ def run_grouped_mlp_fp8(inp, act="swiglu"):
     h, y, out = torch.empty(T, N1, **bf), torch.empty(T, F, **bf), torch.empty(T, H, **bf)
     amax_y = torch.empty(G, dtype=torch.float32, device="cuda")
     sge.grouped_linear_fwd_fp8(qx["q"], qx["scale_inv"], qw1["q"].view(G, N1, H), qw1["scale_inv"], base, y,
-                               epilogue=fwd_epi, probs=P, preact=h, out_amax=amax_y)
+                               epilogue=fwd_epi, probs=P, preact=h, out_amax=amax_y, act=_act_params(act))
     qy = quant_fp8_grouped(y, G, lay, amax_in=amax_y)            # the amax fused into fc1's epilogue
     sge.grouped_linear_fwd_fp8(qy["q"], qy["scale_inv"], qw2["q"].view(G, H, F), qw2["scale_inv"], base, out)
     qd = quant_fp8_grouped(DOUT, G, lay)
@@ -314,7 +322,7 @@ def run_grouped_mlp_fp8(inp, act="swiglu"):
                      dtype=torch.uint8, device="cuda")
     sge.grouped_linear_dgrad_fp8(qd["q"], qd["scale_inv"], qw2["q_t"], qw2["scale_inv"], base,
                                  epilogue=bwd_epi, preact=h, probs=P, dact=dh, dprobs=dp,
-                                 dact_amax=amax_dh, workspace=ws)
+                                 dact_amax=amax_dh, workspace=ws, act=_act_params(act))
     dw2 = torch.empty(G, H, F, **bf)
     sge.grouped_linear_wgrad_fp8(qd["q_t"], qd["scale_inv"], qy["q_t"], qy["scale_inv"], lay, dw2)
     qdh = quant_fp8_grouped(dh, G, lay, amax_in=amax_dh)        # the amax fused into fc2's dgrad epilogue

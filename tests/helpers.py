@@ -95,3 +95,31 @@ def assert_mx_dequant_close(gpu, ref, what=""):
     assert bad.mean() <= 1e-3, f"{what}: {bad.sum()} of {bad.size} outside the FP8 bar"
     assert np.all(err[bad] <= 0.25 * np.abs(ref[bad]) + 0.05), f"{what}: beyond one shared-exponent step"
 
+
+
+def clamp_settled_h(gpu_dh, dh, gy, h, p, act, delta=2.0 ** -16):
+    """The oracle's pre-activation for a clamped SwiGLU backward, with its ambiguous pass-through
+    decisions settled the way the kernel took them.
+
+    Both sides decide on the saved bf16 pre-activation (the oracle on its fp64 h rounded to
+    bf16, the kernel on its fp32 h rounded to bf16). Where the fp64 h lies within ``delta`` of
+    the bf16 rounding midpoint just above the limit (the gate, a) or its magnitude does (the up
+    half, b), an fp32 accumulation may round to the other side, and both decisions are correct.
+    For those elements only, h moves to the bf16 value on the other side of the decision when
+    the oracle's gradient from there (``dh`` is the oracle's from ``h``, ``gy`` its incoming
+    gradient) is the closer one to the kernel's ``gpu_dh``; the clamped values, and so the
+    forward and dprobs, are the same on both sides. Returns (h, number of ambiguous elements);
+    the caller reruns the oracle's backward from that h."""
+    from oracle.codecs import bf16_to_f64, f64_to_bf16
+    from oracle.grouped import scaled_clamped_swiglu_bwd
+    _, limit, alpha = act
+    u = 2.0 ** (np.floor(np.log2(limit)) - 7)                 # bf16 spacing at the limit
+    mid = limit + u / 2
+    F = h.shape[1] // 2
+    hb = bf16_to_f64(f64_to_bf16(h))
+    amb = np.concatenate([np.abs(h[:, :F] - mid) <= delta, np.abs(np.abs(h[:, F:]) - mid) <= delta], axis=1)
+    other = np.where(np.abs(hb) <= limit, limit + u, limit) * np.where(h < 0, -1.0, 1.0)
+    alt, _ = scaled_clamped_swiglu_bwd(gy, np.where(amb, other, hb), p, limit, alpha)
+    gpu_dh = np.asarray(gpu_dh, np.float64)
+    take = amb & (np.abs(gpu_dh - alt) < np.abs(gpu_dh - dh))
+    return np.where(take, other, h), int(amb.sum())

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol(sge):
     lib = ctypes.CDLL(sge.library_path())
     for name in _declared():
         assert hasattr(lib, name), name
-    assert sge.abi_version() == 5
+    assert sge.abi_version() == 6
 
 
 def test_status_strings(sge):
@@ -41,6 +41,13 @@ def test_status_strings(sge):
 
 
 FAKE = 0x10000            # never dereferenced: every call below fails validation first
+
+
+def _act_after(fn, epi_index, act=None):
+    """Calls ``fn`` with the activation-parameter pointer (``act``, default NULL) inserted right
+    after its epilogue argument at ``epi_index``; the remaining arguments keep their positions."""
+    return lambda *a: fn(*a[:epi_index + 1], act, *a[epi_index + 1:])
+
 
 
 def _op(sge, outer, inner, ld=None, contig=1, fmt=0, data=FAKE, sinv=None, mx=None, mx_ld=0):
@@ -130,24 +137,22 @@ def test_grouped_validation_errors(sge):
     assert lib.sge_splits_to_offsets(FAKE, 0, m, 1, -1, FAKE * 2, None, None) == sge.ERR_ARG
     assert lib.sge_splits_to_offsets(FAKE, 8, m, 9, -1, FAKE * 2, None, None) == sge.ERR_ARG
     assert lib.sge_splits_to_offsets(None, 8, m, 1, -1, FAKE * 2, None, None) == sge.ERR_NULL
-    st = lib.sge_grouped_linear_fwd(FAKE, FAKE * 64, 8, 100, 136, 64, FAKE * 1024, 1.0, 1, FAKE * 4096, FAKE * 8192,
-                                    None, None)
+    fwd, bwd = _act_after(lib.sge_grouped_linear_fwd, 8), _act_after(lib.sge_grouped_linear_bwd, 9)
+    st = fwd(FAKE, FAKE * 64, 8, 100, 136, 64, FAKE * 1024, 1.0, 1, FAKE * 4096, FAKE * 8192, None, None)
     assert st == sge.ERR_SHAPE                       # SwiGLU needs N % 256
-    st = lib.sge_grouped_linear_fwd(FAKE, FAKE * 64, 8, 100, 256, 64, FAKE * 1024, 1.0, 1, None, FAKE * 8192, None,
-                                    None)
+    st = fwd(FAKE, FAKE * 64, 8, 100, 256, 64, FAKE * 1024, 1.0, 1, None, FAKE * 8192, None, None)
     assert st == sge.ERR_NULL                        # SwiGLU needs probs
-    st = lib.sge_grouped_linear_fwd(FAKE, FAKE * 64, 8, 100, 256, 64, FAKE * 1024, 1.0, 7, None, FAKE * 8192, None,
-                                    None)
+    st = fwd(FAKE, FAKE * 64, 8, 100, 256, 64, FAKE * 1024, 1.0, 7, None, FAKE * 8192, None, None)
     assert st == sge.ERR_ARG
     ws = lib.sge_grouped_linear_bwd_workspace_size(1000, 2048, 8, 2)
     assert ws > 0 and ws % (1000 * 4) == 0
-    st = lib.sge_grouped_linear_bwd(FAKE, FAKE * 8, FAKE * 64, 8, 1000, 256, 2048, FAKE * 1024, 1.0, 2,
-                                    FAKE * 2048, FAKE * 4096, FAKE * 8192, FAKE * 9000, None, None, None, 0, None)
+    st = bwd(FAKE, FAKE * 8, FAKE * 64, 8, 1000, 256, 2048, FAKE * 1024, 1.0, 2,
+             FAKE * 2048, FAKE * 4096, FAKE * 8192, FAKE * 9000, None, None, None, 0, None)
     assert st == sge.ERR_WORKSPACE
 
 
 def test_grouped_mxfp8_validation_errors(sge):
-    f = sge._lib.sge_grouped_linear_fwd_mxfp8
+    f = _act_after(sge._lib.sge_grouped_linear_fwd_mxfp8, 10)
     G, T, N, K = 4, 100, 512, 256
     x_q, x_s, w_q, w_s, offs, probs = FAKE, FAKE * 64, FAKE * 128, FAKE * 4096, FAKE * 8192, FAKE * 8300
     y, h, yq, ys = FAKE * 10000, FAKE * 20000, FAKE * 30000, FAKE * 40000
@@ -214,7 +219,7 @@ def test_mxfp8_grouped_backward_validation_errors(sge):
     a = list(ok); a[9] = B(3)
     assert q(*a) == sge.ERR_ALIAS                                         # s_colT over layout
 
-    d = sge._lib.sge_grouped_linear_dgrad_mxfp8
+    d = _act_after(sge._lib.sge_grouped_linear_dgrad_mxfp8, 10)
     G, T, N, K = 4, 100, 256, 512
     sw = sge.EPI_DSCALED_SWIGLU
     ws = sge.grouped_linear_bwd_workspace_size(T, K, G, sw)
@@ -290,7 +295,7 @@ def test_fp8_grouped_validation_errors(sge):
     a = list(ok); a[11] = B(9); a[8] = B(9)
     assert q(*a) == sge.ERR_ALIAS                                         # amax output over amax_in
 
-    f = sge._lib.sge_grouped_linear_fwd_fp8
+    f = _act_after(sge._lib.sge_grouped_linear_fwd_fp8, 10)
     G, T, N, K = 4, 100, 512, 256
     ok = [B(1), B(2), B(3), B(4), G, T, N, K, B(5), 1.0, sge.EPI_SCALED_SWIGLU, B(6), B(7), B(8), None, None]
     a = list(ok); a[1] = None
@@ -308,7 +313,7 @@ def test_fp8_grouped_validation_errors(sge):
     a = list(ok); a[14] = B(7)
     assert f(*a) == sge.ERR_ALIAS                                         # out_amax over out
 
-    d = sge._lib.sge_grouped_linear_dgrad_fp8
+    d = _act_after(sge._lib.sge_grouped_linear_dgrad_fp8, 10)
     sw = sge.EPI_DSCALED_SWIGLU
     wsb = sge.grouped_linear_bwd_workspace_size(T, K, G, sw)
     ok = [B(1), B(2), B(3), B(4), G, T, N, K, B(5), 1.0, sw, B(6), B(7), None, B(8), B(9), None, B(10), wsb, None]
@@ -383,26 +388,66 @@ def test_srelu_epilogue_validation(sge):
     def B(k):
         return FAKE * 8 * k
 
-    f = sge._lib.sge_grouped_linear_fwd
+    f = _act_after(sge._lib.sge_grouped_linear_fwd, 8)
     # bf16 grouped forward: SReLU needs probs
     assert f(B(1), B(2), 4, 100, 264, 256, B(3), 1.0, sge.EPI_SCALED_SRELU, None, B(4), B(5), None) == sge.ERR_NULL
-    fm = sge._lib.sge_grouped_linear_fwd_mxfp8
+    fm = _act_after(sge._lib.sge_grouped_linear_fwd_mxfp8, 10)
     assert fm(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, sge.EPI_SCALED_SRELU, None, B(7), B(8),
               None, None, None) == sge.ERR_NULL                            # MXFP8 SReLU needs probs
     assert fm(B(1), B(2), B(3), B(4), 4, 100, 264, 256, B(5), 1.0, sge.EPI_SCALED_SRELU, B(6), B(7), B(8),
               B(9), B(10), None) == sge.ERR_SHAPE                          # MXFP8 output: N % 32
     assert fm(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, sge.EPI_NONE, None, B(7), None,
               B(9), B(10), None) == sge.ERR_ARG                            # MXFP8 output needs an activation
-    dm = sge._lib.sge_grouped_linear_dgrad_mxfp8
+    dm = _act_after(sge._lib.sge_grouped_linear_dgrad_mxfp8, 10)
     assert dm(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, sge.EPI_DSCALED_SRELU, None, B(6), None, B(7),
               B(8), None, None, B(9), 1 << 20, None) == sge.ERR_NULL        # the backward needs preact
-    ff = sge._lib.sge_grouped_linear_fwd_fp8
+    ff = _act_after(sge._lib.sge_grouped_linear_fwd_fp8, 10)
     assert ff(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, sge.EPI_NONE, None, B(7), None, B(8),
               None) == sge.ERR_ARG                                         # a fused amax needs an activation
-    df = sge._lib.sge_grouped_linear_dgrad_fp8
+    df = _act_after(sge._lib.sge_grouped_linear_dgrad_fp8, 10)
     assert df(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, sge.EPI_DSCALED_SRELU, B(6), B(7), None, None,
               B(8), None, B(9), 1 << 20, None) == sge.ERR_NULL              # the backward needs dact
-    b = sge._lib.sge_grouped_linear_bwd
+    b = _act_after(sge._lib.sge_grouped_linear_bwd, 9)
     assert b(B(1), None, B(2), 4, 100, 256, 264, B(3), 1.0, sge.EPI_DSCALED_SRELU, B(4), B(5), None, B(6), None,
               None, B(7), 0, None) == sge.ERR_NULL                        # SReLU backward needs dact
     assert sge.grouped_linear_bwd_workspace_size(100, 264, 4, sge.EPI_DSCALED_SRELU) == 2 * 100 * 4
+
+
+def test_clamped_swiglu_epilogue_validation(sge):
+    """The clamped SwiGLU epilogues need their (limit, alpha): NULL is ERR_NULL, a limit that is
+    not finite and positive or a non-finite alpha is ERR_ARG; the workspace query and the shape
+    rules are those of the SwiGLU epilogues."""
+    def B(k):
+        return FAKE * 8 * k
+
+    cf, cb = sge.EPI_SCALED_CLAMPED_SWIGLU, sge.EPI_DSCALED_CLAMPED_SWIGLU
+    good = sge._act((7.0, 1.702))
+    fwd = sge._lib.sge_grouped_linear_fwd
+
+    def f(act, n=256):
+        return _act_after(fwd, 8, act)(B(1), B(2), 4, 100, n, 256, B(3), 1.0, cf, B(4), B(5), B(6), None)
+
+    assert f(None) == sge.ERR_NULL
+    for bad in ((0.0, 1.0), (-1.0, 1.0), (float("inf"), 1.0), (float("nan"), 1.0), (7.0, float("nan"))):
+        assert f(sge._act(bad)) == sge.ERR_ARG, bad
+    assert f(good, n=264) == sge.ERR_SHAPE                                # gated: N % 256
+    assert sge.grouped_linear_bwd_workspace_size(100, 264, 4, cb) == sge.grouped_linear_bwd_workspace_size(
+        100, 264, 4, sge.EPI_DSCALED_SWIGLU) > 0
+    b = _act_after(sge._lib.sge_grouped_linear_bwd, 9)
+    assert b(B(1), None, B(2), 4, 100, 256, 264, B(3), 1.0, cb, B(4), B(5), B(6), B(7), None,
+             None, B(8), 1 << 20, None) == sge.ERR_NULL                  # act missing
+    b = _act_after(sge._lib.sge_grouped_linear_bwd, 9, good)
+    assert b(B(1), None, B(2), 4, 100, 256, 264, B(3), 1.0, cb, B(4), B(5), B(6), B(7), None,
+             None, B(8), 16, None) == sge.ERR_WORKSPACE
+    fm = _act_after(sge._lib.sge_grouped_linear_fwd_mxfp8, 10)
+    assert fm(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, cf, B(6), B(7), B(8),
+              None, None, None) == sge.ERR_NULL                            # MXFP8: act missing
+    dm = _act_after(sge._lib.sge_grouped_linear_dgrad_mxfp8, 10, sge._act((0.0, 1.0)))
+    assert dm(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, cb, B(6), B(7), None, B(8),
+              B(9), None, None, B(10), 1 << 20, None) == sge.ERR_ARG       # MXFP8 dgrad: bad limit
+    ff = _act_after(sge._lib.sge_grouped_linear_fwd_fp8, 10)
+    assert ff(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, cf, B(6), B(7), B(8), None,
+              None) == sge.ERR_NULL                                        # FP8: act missing
+    df = _act_after(sge._lib.sge_grouped_linear_dgrad_fp8, 10)
+    assert df(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, cb, B(6), B(7), None, B(8),
+              B(9), None, B(10), 1 << 20, None) == sge.ERR_NULL            # FP8 dgrad: act missing

@@ -7,10 +7,10 @@ import torch
 import scaled_gemm_epilogues_amd as sge
 import synth
 from oracle import grouped, offsets
-from oracle.codecs import bf16_to_f64
+from oracle.codecs import bf16_to_f64, f64_to_bf16
 
 from .gpu_paths import run_grouped_mlp
-from .helpers import TAU_BF16, assert_close, dev_bf16, host_f64
+from .helpers import TAU_BF16, assert_close, clamp_settled_h, dev_bf16, host_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -154,6 +154,46 @@ def test_grouped_srelu_mlp_parity(case):
     f = grouped.grouped_mlp_fwd(x, w1, w2, p, base, act="srelu")
     b = grouped.grouped_mlp_bwd(bf16_to_f64(inp["dout"]), x, w1, w2, p, base, h=f["h"], y=f["y"], act="srelu")
     kw = dict(rel_tight=2.0 ** -7, abs_tight=5e-2)
+    assert_close(host_f64(got["h"]), f["h"], TAU_BF16, what="h")
+    for k, ref in (("y", f["y"]), ("out", f["out"]), ("dh", b["dh"]), ("dp", b["dp"]), ("dw2", b["dw2"]),
+                   ("dx", b["dx"]), ("dw1", b["dw1"])):
+        assert_close(host_f64(got[k]), ref, TAU_BF16, what=k, **kw)
+
+
+CLAMPED_CASES = {
+    # limit well inside the pre-activations' spread: both clamps engage on many elements
+    "engaged_empty_and_single": ([0, 1, 300, 0, 211, 8], 256, 256, 0.25, 1.702),
+    # a limit no pre-activation reaches, alpha 1: only the up half's offset of one remains
+    "not_engaged": (None, 256, 256, 64.0, 1.0),
+}
+
+
+@pytest.mark.parametrize("case", list(CLAMPED_CASES))
+def test_grouped_clamped_swiglu_mlp_parity(case):
+    """Grouped MLP with the clamped SwiGLU in fc1's epilogue and its backward in fc2's dgrad
+    epilogue. The oracle's backward reads the pre-activation rounded to bf16, as the saved
+    pre-activation the kernel reads (the clamps' pass-through decisions are taken on it)."""
+    splits, hidden, ffn, limit, alpha = CLAMPED_CASES[case]
+    act = ("clamped_swiglu", limit, alpha)
+    T = 520 if splits is None else sum(splits)
+    G = 5 if splits is None else len(splits)
+    print(f"case grouped clamped swiglu mlp {case} T={T} G={G} hidden={hidden} ffn={ffn}", flush=True)
+    inp = synth.grouped(T, G, hidden, ffn, seed=25, splits=splits)
+    got = run_grouped_mlp(inp, act=act)
+    base = offsets.base_offsets(inp["splits"])
+    x, w1, w2 = bf16_to_f64(inp["x"]), bf16_to_f64(inp["w1"]), bf16_to_f64(inp["w2"])
+    p = inp["p"].astype(np.float64)
+    f = grouped.grouped_mlp_fwd(x, w1, w2, p, base, act=act)
+    h_saved = bf16_to_f64(f64_to_bf16(f["h"]))
+    b = grouped.grouped_mlp_bwd(bf16_to_f64(inp["dout"]), x, w1, w2, p, base, h=h_saved, y=f["y"], act=act)
+    if limit < 1.0:                                        # the clamps engage on both halves
+        F = ffn
+        assert np.mean(f["h"][:, :F] > limit) > 0.05 and np.mean(np.abs(f["h"][:, F:]) > limit) > 0.05
+    kw = dict(rel_tight=2.0 ** -7, abs_tight=5e-2)
+    h_set, n_amb = clamp_settled_h(host_f64(got["dh"]), b["dh"], b["gy"], f["h"], p, act)
+    assert n_amb <= 1e-3 * h_set.size
+    b = grouped.grouped_mlp_bwd(bf16_to_f64(inp["dout"]), x, w1, w2, p, base, h=bf16_to_f64(f64_to_bf16(h_set)),
+                                y=f["y"], act=act)
     assert_close(host_f64(got["h"]), f["h"], TAU_BF16, what="h")
     for k, ref in (("y", f["y"]), ("out", f["out"]), ("dh", b["dh"]), ("dp", b["dp"]), ("dw2", b["dw2"]),
                    ("dx", b["dx"]), ("dw1", b["dw1"])):

@@ -11,9 +11,13 @@ import synth
 from oracle import grouped, offsets, quant
 
 from .gpu_paths import mx_layout, quant_fp8_grouped, run_grouped_mlp_fp8
-from .helpers import TAU_FP8, assert_close, assert_close_requantized, dev, dev_bf16, host_f64, host_u8
+from .helpers import (TAU_FP8, assert_close, assert_close_requantized, clamp_settled_h, dev, dev_bf16, host_f64,
+                      host_u8)
 
 pytestmark = pytest.mark.gpu
+
+# Clamped SwiGLU with a limit well inside the pre-activations' spread (both clamps engage)
+CLAMPED = ("clamped_swiglu", 0.25, 1.702)
 
 KW = dict(rel_tight=2.0 ** -3, abs_tight=0.1)
 
@@ -115,14 +119,14 @@ MLP_CASES = {
 }
 
 
-@pytest.mark.parametrize("act", ["swiglu", "srelu"])
+@pytest.mark.parametrize("act", ["swiglu", "srelu", CLAMPED], ids=["swiglu", "srelu", "clamped_swiglu"])
 @pytest.mark.parametrize("case", list(MLP_CASES))
 def test_fp8_grouped_mlp_fwd_bwd(case, act):
     splits, hidden, ffn = MLP_CASES[case]
     T = 700 if splits is None else sum(splits)
     G = 5 if splits is None else len(splits)
     print(f"case fp8 grouped mlp {case} {act} T={T} G={G} hidden={hidden} ffn={ffn}", flush=True)
-    inp = synth.grouped(T, G, hidden, ffn, seed=33, splits=splits, gated=act == "swiglu")
+    inp = synth.grouped(T, G, hidden, ffn, seed=33, splits=splits, gated=act != "srelu")
     got = run_grouped_mlp_fp8(inp, act)
     base = offsets.base_offsets(inp["splits"])
     fwd = grouped.grouped_mlp_fwd_fp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base, act)
@@ -138,6 +142,11 @@ def test_fp8_grouped_mlp_fwd_bwd(case, act):
     assert_close(host_f64(got["y"]), fwd["y"], TAU_FP8, what="y", **KW)
     # out, dx and the weight gradients consume y or dh, quantized per group on each side
     assert_close_requantized(host_f64(got["out"]), fwd["out"], TAU_FP8, what="out", **KW)
+    if isinstance(act, tuple):                             # clamps: settle the ambiguous decisions
+        h_set, n_amb = clamp_settled_h(host_f64(got["dh"]), bwd["dh"], bwd["gy"], fwd["h"], inp["p"], act)
+        assert n_amb <= 1e-3 * h_set.size
+        bwd = grouped.grouped_mlp_bwd_fp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base, inp["dout"],
+                                          fwd=dict(fwd, h=h_set), act=act)
     assert_close(host_f64(got["dh"]), bwd["dh"], TAU_FP8, what="dh", **KW)
     assert_close(host_f64(got["dp"]), bwd["dp"], TAU_FP8, what="dprobs", **KW)
     assert_close_requantized(host_f64(got["dx"]), bwd["dx"], TAU_FP8, what="dx", **KW)

@@ -17,6 +17,9 @@ from .helpers import TAU_FP8, assert_close, assert_mx_dequant_close, host_f64, h
 
 pytestmark = pytest.mark.gpu
 
+# Clamped SwiGLU with a limit well inside the pre-activations' spread (both clamps engage)
+CLAMPED = ("clamped_swiglu", 0.25, 1.702)
+
 KW = dict(rel_tight=2.0 ** -3, abs_tight=0.1)
 
 CASES = {
@@ -25,14 +28,14 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("act", ["swiglu", "srelu"])
+@pytest.mark.parametrize("act", ["swiglu", "srelu", CLAMPED], ids=["swiglu", "srelu", "clamped_swiglu"])
 @pytest.mark.parametrize("case", list(CASES))
 def test_mxfp8_grouped_mlp_forward(case, act):
     splits, hidden, ffn = CASES[case]
     T = 700 if splits is None else sum(splits)
     G = 5 if splits is None else len(splits)
     print(f"case mxfp8 grouped fwd {case} {act} T={T} G={G} hidden={hidden} ffn={ffn}", flush=True)
-    inp = synth.grouped(T, G, hidden, ffn, seed=31, splits=splits, gated=act == "swiglu")
+    inp = synth.grouped(T, G, hidden, ffn, seed=31, splits=splits, gated=act != "srelu")
     got = run_grouped_mlp_fwd_mx(inp, act)
     assert int(got["err"].item()) == 0
     base = offsets.base_offsets(inp["splits"])

@@ -14,9 +14,13 @@ from oracle.quant import mx_dequantize
 
 from .gpu_paths import (grouped_dgrad_mx, grouped_wgrad_mx, mx_layout, quant_mx, quant_mx_grouped,
                         run_grouped_mlp_bwd_mx, run_grouped_mlp_fwd_mx)
-from .helpers import TAU_FP8, assert_close, assert_mx_dequant_close, dev, dev_bf16, host_f64, host_u8
+from .helpers import (TAU_FP8, assert_close, assert_mx_dequant_close, clamp_settled_h, dev, dev_bf16, host_f64,
+                      host_u8)
 
 pytestmark = pytest.mark.gpu
+
+# Clamped SwiGLU with a limit well inside the pre-activations' spread (both clamps engage)
+CLAMPED = ("clamped_swiglu", 0.25, 1.702)
 
 KW = dict(rel_tight=2.0 ** -3, abs_tight=0.1)
 
@@ -185,21 +189,28 @@ MLP_CASES = {
 }
 
 
-@pytest.mark.parametrize("act", ["swiglu", "srelu"])
+@pytest.mark.parametrize("act", ["swiglu", "srelu", CLAMPED], ids=["swiglu", "srelu", "clamped_swiglu"])
 @pytest.mark.parametrize("case", list(MLP_CASES))
 def test_mxfp8_grouped_mlp_backward(case, act):
     splits, hidden, ffn = MLP_CASES[case]
     T = 700 if splits is None else sum(splits)
     G = 5 if splits is None else len(splits)
     print(f"case mxfp8 grouped mlp bwd {case} {act} T={T} G={G} hidden={hidden} ffn={ffn}", flush=True)
-    inp = synth.grouped(T, G, hidden, ffn, seed=32, splits=splits, gated=act == "swiglu")
+    inp = synth.grouped(T, G, hidden, ffn, seed=32, splits=splits, gated=act != "srelu")
     fwd = run_grouped_mlp_fwd_mx(inp, act)
     got = run_grouped_mlp_bwd_mx(inp, fwd)
     base = offsets.base_offsets(inp["splits"])
-    ref = grouped.grouped_mlp_bwd_mxfp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base, inp["dout"], act=act)
+    rf = grouped.grouped_mlp_fwd_mxfp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base, act)
+    ref = grouped.grouped_mlp_bwd_mxfp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base, inp["dout"], fwd=rf,
+                                        act=act)
     # fused activation backward + group quantize == standalone quantizer on the same bf16 dh
     assert np.array_equal(host_u8(got["dhq"]), host_u8(got["dh_unfused"]["q_row"]))
     assert np.array_equal(host_u8(got["dhs"]), host_u8(got["dh_unfused"]["s_row"]))
+    if isinstance(act, tuple):                             # clamps: settle the ambiguous decisions
+        h_set, n_amb = clamp_settled_h(host_f64(got["dh"]), ref["dh"], ref["gy"], rf["h"], inp["p"], act)
+        assert n_amb <= 1e-3 * h_set.size
+        ref = grouped.grouped_mlp_bwd_mxfp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base, inp["dout"],
+                                            fwd=dict(rf, h=h_set), act=act)
     assert_close(host_f64(got["dh"]), ref["dh"], TAU_FP8, what="dh", **KW)
     assert_close(host_f64(got["dp"]), ref["dp"], TAU_FP8, what="dprobs", **KW)
     assert_close(host_f64(got["dx"]), ref["dx"], TAU_FP8, what="dx", **KW)
