@@ -184,6 +184,18 @@ def build_dense(torch, sge, wl, inp):
     return launches, flops, hbm
 
 
+def act_config(sge, wl):
+    """(gated, forward epilogue, backward epilogue, name of the fc2 dgrad launch, clamp parameters)
+    of a grouped workload's activation: "swiglu", "srelu" or ("clamped_swiglu", limit, alpha)."""
+    act = wl.get("act", "swiglu")
+    if act == "srelu":
+        return False, sge.EPI_SCALED_SRELU, sge.EPI_DSCALED_SRELU, "fc2_dgrad_dsrelu", None
+    if act == "swiglu":
+        return True, sge.EPI_SCALED_SWIGLU, sge.EPI_DSCALED_SWIGLU, "fc2_dgrad_dswiglu", None
+    return (True, sge.EPI_SCALED_CLAMPED_SWIGLU, sge.EPI_DSCALED_CLAMPED_SWIGLU, "fc2_dgrad_dclamped_swiglu",
+            tuple(act[1:]))
+
+
 def build_grouped(torch, sge, wl, inp):
     import numpy as np
 
@@ -195,10 +207,8 @@ def build_grouped(torch, sge, wl, inp):
     splits = torch.from_numpy(inp["splits"]).cuda()
     T, H = X.shape
     G, N1, _ = W1.shape
-    act = wl.get("act", "swiglu")
-    F = N1 // 2 if act == "swiglu" else N1
-    fwd_epi = sge.EPI_SCALED_SWIGLU if act == "swiglu" else sge.EPI_SCALED_SRELU
-    bwd_epi = sge.EPI_DSCALED_SWIGLU if act == "swiglu" else sge.EPI_DSCALED_SRELU
+    gated, fwd_epi, bwd_epi, dact, ap = act_config(sge, wl)
+    F = N1 // 2 if gated else N1
     bf = dict(dtype=torch.bfloat16, device="cuda")
     offs = torch.empty(2, G + 1, dtype=torch.int64, device="cuda")
     h, y, out = torch.empty(T, N1, **bf), torch.empty(T, F, **bf), torch.empty(T, H, **bf)
@@ -206,7 +216,6 @@ def build_grouped(torch, sge, wl, inp):
     dw2, dx, dw1 = torch.empty(G, H, F, **bf), torch.empty(T, H, **bf), torch.empty(G, N1, H, **bf)
     ws = torch.empty(max(1, sge.grouped_linear_bwd_workspace_size(T, F, G, bwd_epi)),
                      dtype=torch.uint8, device="cuda")
-    dact = "fc2_dgrad_dswiglu" if act == "swiglu" else "fc2_dgrad_dsrelu"
     flops = {"fc1_fwd": 2 * T * N1 * H, "fc2_fwd": 2 * T * H * F, dact: 2 * T * H * F,
              "fc2_wgrad": 2 * T * H * F, "fc1_dgrad": 2 * T * N1 * H, "fc1_wgrad": 2 * T * N1 * H}
 
@@ -218,10 +227,11 @@ def build_grouped(torch, sge, wl, inp):
                                  ws, flops)
     launches = [
         ("offsets", lambda: sge.splits_to_offsets(splits, [1, H], offs)),
-        ("fc1_fwd", lambda: sge.grouped_linear_fwd(X, W1, base, y, epilogue=fwd_epi, probs=P, preact=h)),
+        ("fc1_fwd", lambda: sge.grouped_linear_fwd(X, W1, base, y, epilogue=fwd_epi, probs=P, preact=h,
+                                                   act=ap)),
         ("fc2_fwd", lambda: sge.grouped_linear_fwd(y, W2, base, out)),
         (dact, lambda: sge.grouped_linear_bwd(DOUT, None, W2, base, epilogue=bwd_epi,
-                                                             preact=h, probs=P, dact=dh, dprobs=dp, workspace=ws)),
+                                              preact=h, probs=P, dact=dh, dprobs=dp, workspace=ws, act=ap)),
         ("fc2_wgrad", lambda: sge.grouped_linear_bwd(DOUT, y, W2, base, dw=dw2)),
         ("fc1_dgrad", lambda: sge.grouped_linear_bwd(dh, None, W1, base, dx=dx)),
         ("fc1_wgrad", lambda: sge.grouped_linear_bwd(dh, X, W1, base, dw=dw1)),
@@ -236,11 +246,8 @@ def build_grouped_mx(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, d
     as MXFP8 for fc2, and fc2's dgrad emits dh as MXFP8 for fc1's dgrad."""
     T, H = X.shape
     G, N1, _ = W1.shape
-    swiglu = wl.get("act", "swiglu") == "swiglu"
+    swiglu, fwd_epi, bwd_epi, dact, ap = act_config(sge, wl)   # swiglu: a gated activation
     F = N1 // 2 if swiglu else N1
-    fwd_epi = sge.EPI_SCALED_SWIGLU if swiglu else sge.EPI_SCALED_SRELU
-    bwd_epi = sge.EPI_DSCALED_SWIGLU if swiglu else sge.EPI_DSCALED_SRELU
-    dact = "fc2_dgrad_dswiglu" if swiglu else "fc2_dgrad_dsrelu"
     bwd = "bwd" in wl["passes"]
     u8 = dict(dtype=torch.uint8, device="cuda")
     base = offs[0]
@@ -260,7 +267,7 @@ def build_grouped_mx(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, d
             ("quant_w2", lambda: sge.quantize_mxfp8(W2f, q_row=qw2, s_row=sw2)),
             ("fc1_fwd", lambda: sge.grouped_linear_fwd_mxfp8(
                 qx, sx, qw1.view(G, N1, H), sw1.view(G, N1, H // 32), base, out=None,
-                epilogue=fwd_epi, probs=P, preact=h, out_q=qy, out_s=sy)),
+                epilogue=fwd_epi, probs=P, preact=h, out_q=qy, out_s=sy, act=ap)),
             ("fc2_fwd", lambda: sge.grouped_linear_fwd_mxfp8(qy, sy, qw2.view(G, H, F), sw2.view(G, H, F // 32),
                                                              base, out=out)),
         ], flops, hbm
@@ -290,13 +297,13 @@ def build_grouped_mx(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, d
         ("quant_w2", lambda: sge.quantize_mxfp8(W2f, q_row=qw2, s_row=sw2, q_colT=qw2T, s_colT=sw2T)),
         ("fc1_fwd", lambda: sge.grouped_linear_fwd_mxfp8(
             qx, sx, qw1.view(G, N1, H), sw1.view(G, N1, H // 32), base, out=y,
-            epilogue=fwd_epi, probs=P, preact=h, out_q=qy, out_s=sy)),
+            epilogue=fwd_epi, probs=P, preact=h, out_q=qy, out_s=sy, act=ap)),
         ("quant_y", lambda: sge.quantize_mxfp8_grouped(y, lay, qyT, syT)),
         ("fc2_fwd", lambda: sge.grouped_linear_fwd_mxfp8(qy, sy, qw2.view(G, H, F), sw2.view(G, H, F // 32),
                                                          base, out=out)),
         ("quant_dout", lambda: sge.quantize_mxfp8_grouped(DOUT, lay, qdT, sdT, q_row=qd, s_row=sd)),
         (dact, lambda: sge.grouped_linear_dgrad_mxfp8(
-            qd, sd, qw2T, sw2T, base, epilogue=bwd_epi, preact=h, probs=P, dact=dh, dprobs=dp,
+            qd, sd, qw2T, sw2T, base, epilogue=bwd_epi, preact=h, probs=P, dact=dh, dprobs=dp, act=ap,
             dact_q=qdh, dact_s=sdh, workspace=ws)),
         ("fc2_wgrad", lambda: sge.grouped_linear_wgrad_mxfp8(qdT, sdT, qyT, syT, lay, dw2)),
         ("quant_dh", lambda: sge.quantize_mxfp8_grouped(dh, lay, qdhT, sdhT)),
@@ -313,11 +320,8 @@ def build_grouped_fp8(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, 
     scales."""
     T, H = X.shape
     G, N1, _ = W1.shape
-    swiglu = wl.get("act", "swiglu") == "swiglu"
+    swiglu, fwd_epi, bwd_epi, dact, ap = act_config(sge, wl)   # swiglu: a gated activation
     F = N1 // 2 if swiglu else N1
-    fwd_epi = sge.EPI_SCALED_SWIGLU if swiglu else sge.EPI_SCALED_SRELU
-    bwd_epi = sge.EPI_DSCALED_SWIGLU if swiglu else sge.EPI_DSCALED_SRELU
-    dact = "fc2_dgrad_dswiglu" if swiglu else "fc2_dgrad_dsrelu"
     base = offs[0]
     u8 = dict(dtype=torch.uint8, device="cuda")
     ld = sge.mx_token_capacity(T, G)
@@ -352,14 +356,14 @@ def build_grouped_fp8(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, 
         ("quant_w1", quant(W1f, qw1, None)),
         ("quant_w2", quant(W2f, qw2, None)),
         ("fc1_fwd", lambda: sge.grouped_linear_fwd_fp8(qx["q"], sinv(qx), qw1["q"].view(G, N1, H), sinv(qw1), base,
-                                                       y, epilogue=fwd_epi, probs=P, preact=h,
+                                                       y, epilogue=fwd_epi, probs=P, preact=h, act=ap,
                                                        out_amax=amax_y)),
         ("quant_y", quant(y, qy, lay, amax_y)),
         ("fc2_fwd", lambda: sge.grouped_linear_fwd_fp8(qy["q"], sinv(qy), qw2["q"].view(G, H, F), sinv(qw2), base,
                                                        out)),
         ("quant_dout", quant(DOUT, qd, lay)),
         (dact, lambda: sge.grouped_linear_dgrad_fp8(
-            qd["q"], sinv(qd), qw2["q_t"], sinv(qw2), base, epilogue=bwd_epi, preact=h, probs=P,
+            qd["q"], sinv(qd), qw2["q_t"], sinv(qw2), base, epilogue=bwd_epi, preact=h, probs=P, act=ap,
             dact=dh, dprobs=dp, dact_amax=amax_dh, workspace=ws)),
         ("fc2_wgrad", lambda: sge.grouped_linear_wgrad_fp8(qd["q_t"], sinv(qd), qy["q_t"], sinv(qy), lay, dw2)),
         ("quant_dh", quant(dh, qdh, lay, amax_dh)),
@@ -435,7 +439,7 @@ def cpu_baseline(wl, inp, target_s):
             tok = min(T, tok * 4)
         H = inp["x"].shape[1]
         N1 = inp["w1"].shape[1]
-        flops = 3 * (2 * tok * N1 * H + 2 * tok * H * (N1 // 2 if act == "swiglu" else N1))
+        flops = 3 * (2 * tok * N1 * H + 2 * tok * H * (N1 if act == "srelu" else N1 // 2))
         sample = (f"first {tok} of {T} tokens through the FP8 (per-group current scaling) grouped MLP forward + "
                   "backward with one expert (quantization of that expert's weights included)")
     elif wl["fmt"] == "mxfp8":
@@ -458,7 +462,7 @@ def cpu_baseline(wl, inp, target_s):
             tok = min(T, tok * 4)
         H = inp["x"].shape[1]
         N1 = inp["w1"].shape[1]
-        flops = (3 if bwd else 1) * (2 * tok * N1 * H + 2 * tok * H * (N1 // 2 if act == "swiglu" else N1))
+        flops = (3 if bwd else 1) * (2 * tok * N1 * H + 2 * tok * H * (N1 if act == "srelu" else N1 // 2))
         sample = (f"first {tok} of {T} tokens through the MXFP8 grouped MLP {'forward + backward' if bwd else 'forward'}"
                   " with one expert (quantization of that expert's weights included)")
     else:
@@ -482,7 +486,7 @@ def cpu_baseline(wl, inp, target_s):
             tok = min(T, tok * 4)
         H = inp["x"].shape[1]
         N1 = inp["w1"].shape[1]
-        F = N1 // 2 if wl.get("act", "swiglu") == "swiglu" else N1
+        F = N1 if wl.get("act", "swiglu") == "srelu" else N1 // 2
         flops = 3 * (2 * tok * N1 * H + 2 * tok * H * F)
         sample = f"first {tok} of {T} tokens through the grouped MLP forward and backward"
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",

@@ -130,6 +130,10 @@ WORKLOADS = {
                                               alpha=1.0, act="srelu", passes=("fwd", "bwd")),
     "fp8_grouped_srelu_mlp_T65536_G8": dict(kind="grouped", fmt="fp8", T=65536, G=8, hidden=2048, ffn=2048,
                                             alpha=1.0, act="srelu", passes=("fwd", "bwd")),
+    # the bf16 grouped MLP with the clamped SwiGLU (gate clamped above at 7 through u * sigmoid(1.702 u), up
+    # half clamped to [-7, 7] and offset by one)
+    "grouped_clamped_swiglu_mlp_T65536_G8": dict(kind="grouped", fmt="bf16", T=65536, G=8, hidden=2048,
+                                                 ffn=2048, alpha=1.0, act=("clamped_swiglu", 7.0, 1.702)),
     # the MXFP8 linear fed by an RMSNorm whose kernel writes the MXFP8 operand (forward + backward,
     # the norm's backward included); x, W, dy as in the MXFP8 linear above, gamma = 1 + 0.1 N(0,1)
     "rmsnorm_mxfp8_linear_fwdbwd_16384x8192x8192": dict(kind="dense", fmt="mxfp8", M=16384, N=8192, K=8192,
@@ -148,4 +152,4 @@ def workload_inputs(name, seed=0):
         if w.get("norm"):
             d["gamma"] = norm_gamma(w["K"], seed=seed)
         return d
-    return grouped(w["T"], w["G"], w["hidden"], w["ffn"], seed=seed, gated=w.get("act", "swiglu") == "swiglu")
+    return grouped(w["T"], w["G"], w["hidden"], w["ffn"], seed=seed, gated=w.get("act", "swiglu") != "srelu")

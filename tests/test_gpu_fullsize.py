@@ -96,12 +96,23 @@ def test_dense_workload_full_size_sampled(name):
                  what=f"{name} wgrad")
 
 
-def test_grouped_workload_full_size_sampled():
-    name = "grouped_swiglu_mlp_T65536_G8"
+def _gated_act(act):
+    """(forward, backward) of a gated activation of the oracle: SwiGLU or the clamped SwiGLU."""
+    if act == "swiglu":
+        return grouped.scaled_swiglu_fwd, grouped.scaled_swiglu_bwd
+    _, limit, alpha = act
+    return (lambda h, p: grouped.scaled_clamped_swiglu_fwd(h, p, limit, alpha),
+            lambda gy, h, p: grouped.scaled_clamped_swiglu_bwd(gy, h, p, limit, alpha))
+
+
+@pytest.mark.parametrize("name", ["grouped_swiglu_mlp_T65536_G8", "grouped_clamped_swiglu_mlp_T65536_G8"])
+def test_grouped_workload_full_size_sampled(name):
     w = synth.WORKLOADS[name]
+    act = w.get("act", "swiglu")
+    act_fwd, act_bwd = _gated_act(act)
     print(f"case full-size {name}", flush=True)
     inp = synth.workload_inputs(name, seed=0)
-    got = run_grouped_mlp(inp)
+    got = run_grouped_mlp(inp, act=act)
     assert int(got["err"].item()) == 0
     base = offsets.base_offsets(inp["splits"])
     assert np.array_equal(got["offsets"][0].cpu().numpy(), base)
@@ -119,9 +130,9 @@ def test_grouped_workload_full_size_sampled():
         toks = np.array(sorted({lo, hi - 1} | set(rng.integers(lo, hi, size=min(6, hi - lo)).tolist())))
         one = np.array([0, len(toks)])
         xs = bf16_to_f64(x[toks])
-        f = grouped.grouped_mlp_fwd(xs, W1[g:g + 1], W2[g:g + 1], p[toks], one)
+        f = grouped.grouped_mlp_fwd(xs, W1[g:g + 1], W2[g:g + 1], p[toks], one, act=act)
         b = grouped.grouped_mlp_bwd(bf16_to_f64(dout[toks]), xs, W1[g:g + 1], W2[g:g + 1], p[toks], one,
-                                    h=f["h"], y=f["y"])
+                                    h=f["h"], y=f["y"], act=act)
         tt = torch.from_numpy(toks).cuda()
         kw = dict(rel_tight=2.0 ** -7, abs_tight=5e-2)
         assert_close(host_f64(got["out"][tt]), f["out"], TAU_BF16, what=f"out g{g}", **kw)
@@ -132,13 +143,13 @@ def test_grouped_workload_full_size_sampled():
         # weight gradients at sampled columns: every token of the group, column-local quantities
         xg = bf16_to_f64(x[lo:hi])
         hk = xg @ W1[g][np.concatenate([cols, F + cols])].T          # h[:, k] and h[:, F+k]
-        yk = grouped.scaled_swiglu_fwd(hk, p[lo:hi])                  # y[:, cols]
+        yk = act_fwd(hk, p[lo:hi])                                    # y[:, cols]
         dg = bf16_to_f64(dout[lo:hi])
         ref_dw2 = dg.T @ yk                                           # dW2_g[:, cols]
         assert_close(host_f64(got["dw2"][g][:, torch.from_numpy(cols).cuda()]), ref_dw2, TAU_BF16,
                      what=f"dw2 g{g}", **kw)
         gk = dg @ W2[g][:, cols]                                      # g[:, cols]
-        dhk, _ = grouped.scaled_swiglu_bwd(gk, hk, p[lo:hi])          # dh[:, cols] and dh[:, F+cols]
+        dhk, _ = act_bwd(gk, hk, p[lo:hi])                            # dh[:, cols] and dh[:, F+cols]
         rows1 = np.concatenate([cols, F + cols])
         ref_dw1 = dhk.T @ xg                                          # dW1_g[rows1, :]
         assert_close(host_f64(got["dw1"][g][torch.from_numpy(rows1).cuda()]), ref_dw1, TAU_BF16,
