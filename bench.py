@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--profile-reps", type=int, default=5, help="keep the default for --summarize-traffic")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="one 1 GiB device-to-device copy (calibrates FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
+                    help="write profiles/mfma_util.md from rocprofv3 --pmc runs of the MFMA counters")
     ap.add_argument("--summarize-traffic", metavar="PMC_DIR",
                     help="write profiles/traffic.json and its summary from rocprofv3 --pmc CSV output")
     ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "BENCH_JSON", "OUT_MD", "COMMAND"),
@@ -414,7 +416,7 @@ def cpu_baseline(wl, inp, target_s):
             rows = min(M, rows * 4)
         reps = 1
         if dt < target_s / 4:                                   # the whole workload is quick: repeat it
-            reps = max(1, int(target_s / 4 / max(dt, 1e-3)))
+            reps = max(1, int(target_s / max(dt, 1e-3)))        # for about target_s of CPU time
             t0 = time.perf_counter()
             for _ in range(reps):
                 run(rows)
@@ -595,6 +597,67 @@ def summarize_traffic(pmc_dir):
     print("\n".join(md))
 
 
+MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F8"
+
+
+def summarize_mfma(pmc_dir):
+    """profiles/mfma_util.md and .json: MFMA utilisation of each profiled GEMM launch.
+
+    Expects one rocprofv3 --pmc run of MFMA_COUNTERS per launch, named
+    ``<workload>__<key>_MFMA`` (of ``bench.py --workload <workload> --profile-launch <key>``).
+    Per launch, over its last profile-reps GEMM dispatches: the MFMA pipe's busy fraction
+    (SQ_VALU_MFMA_BUSY_CYCLES summed over the SIMDs / (GRBM_GUI_ACTIVE of one XCD x SIMDs));
+    the clock the GPU ran at (GRBM_GUI_ACTIVE of one XCD / dispatch duration); the MFMA FLOPs
+    the counters saw (MOPS x 512); and the rate against the dense peak at 2.4 GHz, which is
+    the busy fraction times the clock's share of 2.4 GHz."""
+    import csv
+    import glob
+    agent = None
+    out = {}
+    md = ["# MFMA utilisation per GEMM launch", "",
+          "One rocprofv3 counter run per launch, from /tmp:", "", "```",
+          f"rocprofv3 --pmc {MFMA_COUNTERS} --output-format csv -d <dir> -o <workload>__<key>_MFMA -- \\",
+          "    python3 bench.py --workload <workload> --profile-launch <key> --no-cpu-baseline",
+          "then: python3 bench.py --summarize-mfma <dir>", "```", "",
+          "busy = SQ_VALU_MFMA_BUSY_CYCLES (all SIMDs) / (GRBM_GUI_ACTIVE of one XCD x SIMDs); clock =",
+          "GRBM_GUI_ACTIVE of one XCD / dispatch time; MFMA TFLOP = (MOPS_BF16 + MOPS_F8) x 512 per",
+          "dispatch; of peak = busy x clock / 2.4 GHz (the fraction of the dense MFMA peak, 2.5 PFLOP/s",
+          "bf16 or 5.0 PFLOP/s FP8, reached inside the counted dispatch).", "",
+          "| workload | launch | kernel | MFMA busy | clock GHz | MFMA TFLOP / dispatch | dispatch us | of peak |",
+          "|---|---|---|---|---|---|---|---|"]
+    for f in sorted(glob.glob(os.path.join(pmc_dir, "*__*_MFMA_counter_collection.csv"))):
+        tag = os.path.basename(f)[: -len("_MFMA_counter_collection.csv")]
+        wl, key = tag.split("__", 1)
+        if agent is None:
+            for a in csv.DictReader(open(f.replace("_counter_collection.csv", "_agent_info.csv"))):
+                if a.get("Name", "").startswith("gfx"):
+                    agent = {"xcc": int(a["Num_Xcc"]), "simd": int(a["Simd_Count"])}
+        disp = {}
+        for r in csv.DictReader(open(f)):
+            if "gemm_kernel" not in r["Kernel_Name"]:
+                continue
+            d = disp.setdefault(int(r["Dispatch_Id"]), {"kernel": r["Kernel_Name"], "ns": int(r["End_Timestamp"]) -
+                                                         int(r["Start_Timestamp"])})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        last = [disp[k] for k in sorted(disp)][-PROFILE_REPS:]
+        n = len(last)
+        gui = sum(d["GRBM_GUI_ACTIVE"] for d in last) / n / agent["xcc"]
+        busy = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in last) / n / (gui * agent["simd"])
+        ns = sum(d["ns"] for d in last) / n
+        clk = gui / ns
+        tflop = sum(d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] + d["SQ_INSTS_VALU_MFMA_MOPS_F8"] for d in last) / n * 512 / 1e12
+        out[f"{wl}:{key}"] = {"mfma_busy": busy, "clock_ghz": clk, "mfma_tflop_per_dispatch": tflop,
+                              "dispatch_us": ns / 1e3, "frac_of_peak": busy * clk / 2.4}
+        kern = last[0]["kernel"].split("(")[0].replace("void ", "")
+        md.append(f"| {wl} | {key} | `{kern}` | {busy:.3f} | {clk:.2f} | {tflop:.3f} | {ns / 1e3:.1f} | "
+                  f"{busy * clk / 2.4:.3f} |")
+    with open(os.path.join(ROOT, "profiles", "mfma_util.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+    with open(os.path.join(ROOT, "profiles", "mfma_util.md"), "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
 def summarize_trace(trace_dir, bench_json, out_md, command):
     """Markdown summary of a rocprofv3 --kernel-trace --stats CSV run of bench.py."""
     import csv
@@ -629,6 +692,9 @@ def main():
     args = parse()
     if args.summarize_traffic:
         summarize_traffic(args.summarize_traffic)
+        return 0
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
         return 0
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
