@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define SGE_ABI_VERSION 6
+#define SGE_ABI_VERSION 7
 
 /* Alignment, in tokens, of each group's start in a token-blocked MXFP8 operand. */
 #define SGE_MX_TOKEN_ALIGN 128
@@ -241,6 +241,40 @@ sge_status sge_grouped_linear_fwd(const void* x, const void* w, int32_t G, int64
                                   int64_t K, const int64_t* offsets, float alpha, int32_t epilogue,
                                   const sge_act_params* act_params,
                                   const float* probs, void* out, void* preact, hipStream_t stream);
+
+/*
+ * The whole grouped MLP, fc1 -> scaled activation -> fc2, as one call each way.
+ * ("Activation + GroupedLinear Fusion for MOE and other MOE optimizations", Description:
+ * the offsets are computed once in the forward and reused by the backward; review discussion:
+ * the FC1 - ACT - FC2 fused module beside the FC1 - ACT fusion.)
+ *
+ * A chain of the grouped-linear calls with alpha 1, every argument checked before the first
+ * launch (a rejected call enqueues nothing). activation: SGE_EPI_SCALED_SWIGLU,
+ * SGE_EPI_SCALED_SRELU or SGE_EPI_SCALED_CLAMPED_SWIGLU (with act_params); N1 = 2F for the
+ * gated ones (F % 128 == 0), F for SReLU; H % 8 == 0, F % 8 == 0.
+ *
+ * sge_grouped_mlp_fwd: splits device int64 [G] -> offsets device int64 [G+1] (exclusive prefix
+ *   sum; err_flag, optional device int32, set to 1 when they do not sum to T or one is
+ *   negative, else 0), then with x [T, H], W1 [G, N1, H], W2 [G, H, F] (bf16), probs [T] fp32:
+ *   preact [T, N1] = h, act_out [T, F] = the scaled activation of h, out [T, H] = fc2 of act_out.
+ * sge_grouped_mlp_bwd: from dout [T, H] and the forward's offsets, preact and act_out:
+ *   dpreact [T, N1] and dprobs [T] (the activation's backward in fc2's dgrad), dw2 [G, H, F],
+ *   dx [T, H], dw1 [G, N1, H] (bf16; dx, dw1, dw2 may each be NULL to skip). workspace: device,
+ *   >= sge_grouped_mlp_bwd_workspace_size(T, F, G, activation) bytes.
+ * All bf16 tensors 16-byte aligned; outputs may not overlap inputs or each other.
+ */
+sge_status sge_grouped_mlp_fwd(const void* x, const void* w1, const void* w2, int32_t G, int64_t T,
+                               int64_t H, int64_t F, const int64_t* splits, int64_t* offsets,
+                               int32_t* err_flag, int32_t activation, const sge_act_params* act_params,
+                               const float* probs, void* preact, void* act_out, void* out,
+                               hipStream_t stream);
+size_t sge_grouped_mlp_bwd_workspace_size(int64_t T, int64_t F, int32_t G, int32_t activation);
+sge_status sge_grouped_mlp_bwd(const void* dout, const void* x, const void* w1, const void* w2,
+                               int32_t G, int64_t T, int64_t H, int64_t F, const int64_t* offsets,
+                               int32_t activation, const sge_act_params* act_params, const float* probs,
+                               const void* preact, const void* act_out, void* dpreact, float* dprobs,
+                               void* dx, void* dw1, void* dw2, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
 
 /*
  * Grouped linear forward with MXFP8 operands, and the fused activation + group quantize.

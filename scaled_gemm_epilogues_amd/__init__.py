@@ -43,6 +43,7 @@ EXPORTED = (
     "sge_quantize_fp8_grouped_workspace_size", "sge_quantize_fp8_grouped", "sge_grouped_linear_fwd_fp8",
     "sge_grouped_linear_dgrad_fp8", "sge_grouped_linear_wgrad_fp8",
     "sge_norm_fwd_workspace_size", "sge_norm_fwd", "sge_norm_bwd_workspace_size", "sge_norm_bwd",
+    "sge_grouped_mlp_fwd", "sge_grouped_mlp_bwd_workspace_size", "sge_grouped_mlp_bwd",
 )
 
 
@@ -115,6 +116,11 @@ _SIGS = {
     "sge_norm_fwd": ([_i32, _vp, _vp, _vp, _i64, _i64, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                       _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "sge_norm_bwd_workspace_size": ([_i64, _i64], _sz),
+    "sge_grouped_mlp_fwd": ([_vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _ACT, _vp, _vp, _vp, _vp, _vp],
+                            ctypes.c_int),
+    "sge_grouped_mlp_bwd_workspace_size": ([_i64, _i64, _i32, _i32], _sz),
+    "sge_grouped_mlp_bwd": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _ACT, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "sge_norm_bwd": ([_i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
@@ -263,6 +269,33 @@ def grouped_linear_bwd(dy, x, w, offsets, alpha=1.0, epilogue=EPI_NONE, preact=N
     _check(_lib.sge_grouped_linear_bwd(_ptr(dy), _ptr(x), _ptr(w), G, T, N, K, _ptr(offsets), float(alpha),
                                        epilogue, _act(act), _ptr(preact), _ptr(probs), _ptr(dact), _ptr(dprobs),
                                        _ptr(dx), _ptr(dw), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+# ------------------------------------------------ the whole grouped MLP
+def grouped_mlp_fwd(x, w1, w2, splits, offsets, probs, preact, act_out, out, activation=EPI_SCALED_SWIGLU,
+                    act=None, err_flag=None, stream=None):
+    """fc1 -> scaled activation -> fc2 in one call: x [T, H], w1 [G, N1, H], w2 [G, H, F], splits [G]
+    (device int64) -> offsets [G+1], preact [T, N1], act_out [T, F], out [T, H]."""
+    G, H, F = w2.shape
+    T = x.shape[0]
+    _check(_lib.sge_grouped_mlp_fwd(_ptr(x), _ptr(w1), _ptr(w2), G, T, H, F, _ptr(splits), _ptr(offsets),
+                                    _ptr(err_flag), activation, _act(act), _ptr(probs), _ptr(preact), _ptr(act_out),
+                                    _ptr(out), _stream(stream)))
+
+
+def grouped_mlp_bwd_workspace_size(T, F, G, activation):
+    return int(_lib.sge_grouped_mlp_bwd_workspace_size(T, F, G, activation))
+
+
+def grouped_mlp_bwd(dout, x, w1, w2, offsets, probs, preact, act_out, dpreact, dprobs, dx=None, dw1=None, dw2=None,
+                    workspace=None, activation=EPI_SCALED_SWIGLU, act=None, stream=None):
+    """Backward of ``grouped_mlp_fwd`` from dout [T, H] with the forward's offsets, preact and act_out."""
+    G, H, F = w2.shape
+    T = dout.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.sge_grouped_mlp_bwd(_ptr(dout), _ptr(x), _ptr(w1), _ptr(w2), G, T, H, F, _ptr(offsets), activation,
+                                    _act(act), _ptr(probs), _ptr(preact), _ptr(act_out), _ptr(dpreact), _ptr(dprobs),
+                                    _ptr(dx), _ptr(dw1), _ptr(dw2), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 # ------------------------------------------------ MXFP8 grouped backward

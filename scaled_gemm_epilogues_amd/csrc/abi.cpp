@@ -1078,4 +1078,104 @@ sge_status sge_scaled_swiglu_bwd(const void* gy, const void* h, const float* pro
                     "swiglu bwd launch");
 }
 
+// ------------------------------------------------------------------ grouped MLP
+// fc1 -> scaled activation -> fc2 as one call each way, chaining the grouped-linear calls above.
+// Every argument is checked here, before the first launch, so a rejected call enqueues nothing.
+struct Arg {
+  Range r;
+  unsigned align;   // required alignment of the base pointer in bytes
+};
+
+static sge_status check_mlp(const char* what, int32_t G, int64_t T, int64_t H, int64_t F, int32_t activation,
+                            const sge_act_params* act_params, const void* const* need, int n_need, const Arg* ins,
+                            int n_in, const Arg* outs, int n_out) {
+  if (G < 1 || T < 0 || H <= 0 || F <= 0) return fail(SGE_ERR_SHAPE, "%s: bad sizes", what);
+  if (activation != SGE_EPI_SCALED_SWIGLU && activation != SGE_EPI_SCALED_SRELU &&
+      activation != SGE_EPI_SCALED_CLAMPED_SWIGLU)
+    return fail(SGE_ERR_ARG, "%s: activation %d not allowed", what, activation);
+  if (sge_status st = check_act(activation, act_params, what)) return st;
+  for (int i = 0; i < n_need; ++i)
+    if (!need[i]) return fail(SGE_ERR_NULL, "%s: a required pointer is NULL (required argument %d)", what, i);
+  if (H % 8 || F % 8) return fail(SGE_ERR_SHAPE, "%s: H and F must be multiples of 8", what);
+  if (gated_fwd(activation) && F % 128) return fail(SGE_ERR_SHAPE, "%s: a gated activation needs F %% 128 == 0", what);
+  for (int i = 0; i < n_in + n_out; ++i) {
+    const Arg& a = i < n_in ? ins[i] : outs[i - n_in];
+    if (a.r.lo % a.align) return fail(SGE_ERR_ALIGN, "%s: argument not %u-byte aligned", what, a.align);
+  }
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlap(outs[i].r, ins[j].r)) return fail(SGE_ERR_ALIAS, "%s: an output overlaps an input", what);
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(outs[i].r, outs[j].r)) return fail(SGE_ERR_ALIAS, "%s: outputs overlap", what);
+  }
+  return SGE_OK;
+}
+
+sge_status sge_grouped_mlp_fwd(const void* x, const void* w1, const void* w2, int32_t G, int64_t T, int64_t H,
+                               int64_t F, const int64_t* splits, int64_t* offsets, int32_t* err_flag,
+                               int32_t activation, const sge_act_params* act_params, const float* probs,
+                               void* preact, void* act_out, void* out, hipStream_t stream) {
+  const int64_t N1 = gated_fwd(activation) ? 2 * F : F;
+  const void* need[9] = {x, w1, w2, splits, offsets, probs, preact, act_out, out};
+  const Arg ins[5] = {{range_of(x, T, H, H, 2), 16}, {range_of(w1, (int64_t)G * N1, H, H, 2), 16},
+                      {range_of(w2, (int64_t)G * H, F, F, 2), 16}, {range_of(splits, 1, G, G, 8), 8},
+                      {range_of(probs, 1, T, T, 4), 4}};
+  const Arg outs[5] = {{range_of(offsets, 1, G + 1, G + 1, 8), 8}, {range_of(preact, T, N1, N1, 2), 16},
+                       {range_of(act_out, T, F, F, 2), 16}, {range_of(out, T, H, H, 2), 16},
+                       {err_flag ? range_of(err_flag, 1, 1, 1, 4) : Range{0, 0}, 4}};
+  if (sge_status st = check_mlp("grouped_mlp_fwd", G, T, H, F, activation, act_params, need, 9, ins, 5, outs, 5))
+    return st;
+  const int64_t one = 1;
+  if (sge_status st = sge_splits_to_offsets(splits, G, &one, 1, T, offsets, err_flag, stream)) return st;
+  if (T == 0) return ok();
+  if (sge_status st = sge_grouped_linear_fwd(x, w1, G, T, N1, H, offsets, 1.0f, activation, act_params, probs,
+                                             act_out, preact, stream))
+    return st;
+  return sge_grouped_linear_fwd(act_out, w2, G, T, H, F, offsets, 1.0f, SGE_EPI_NONE, nullptr, nullptr, out,
+                                nullptr, stream);
+}
+
+size_t sge_grouped_mlp_bwd_workspace_size(int64_t T, int64_t F, int32_t G, int32_t activation) {
+  const int32_t d = activation == SGE_EPI_SCALED_SWIGLU           ? SGE_EPI_DSCALED_SWIGLU
+                    : activation == SGE_EPI_SCALED_SRELU          ? SGE_EPI_DSCALED_SRELU
+                    : activation == SGE_EPI_SCALED_CLAMPED_SWIGLU ? SGE_EPI_DSCALED_CLAMPED_SWIGLU
+                                                                  : SGE_EPI_NONE;
+  return d == SGE_EPI_NONE ? 0 : sge_grouped_linear_bwd_workspace_size(T, F, G, d);
+}
+
+sge_status sge_grouped_mlp_bwd(const void* dout, const void* x, const void* w1, const void* w2, int32_t G,
+                               int64_t T, int64_t H, int64_t F, const int64_t* offsets, int32_t activation,
+                               const sge_act_params* act_params, const float* probs, const void* preact,
+                               const void* act_out, void* dpreact, float* dprobs, void* dx, void* dw1, void* dw2,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int64_t N1 = gated_fwd(activation) ? 2 * F : F;
+  const void* need[10] = {dout, x, w1, w2, offsets, probs, preact, act_out, dpreact, dprobs};
+  const Arg ins[8] = {{range_of(dout, T, H, H, 2), 16}, {range_of(x, T, H, H, 2), 16},
+                      {range_of(w1, (int64_t)G * N1, H, H, 2), 16}, {range_of(w2, (int64_t)G * H, F, F, 2), 16},
+                      {range_of(offsets, 1, G + 1, G + 1, 8), 8}, {range_of(probs, 1, T, T, 4), 4},
+                      {range_of(preact, T, N1, N1, 2), 16}, {range_of(act_out, T, F, F, 2), 16}};
+  const size_t ws_need = sge_grouped_mlp_bwd_workspace_size(T, F, G, activation);
+  const Arg outs[6] = {{range_of(dpreact, T, N1, N1, 2), 16}, {range_of(dprobs, 1, T, T, 4), 4},
+                       {dx ? range_of(dx, T, H, H, 2) : Range{0, 0}, 16},
+                       {dw1 ? range_of(dw1, (int64_t)G * N1, H, H, 2) : Range{0, 0}, 16},
+                       {dw2 ? range_of(dw2, (int64_t)G * H, F, F, 2) : Range{0, 0}, 16},
+                       {workspace ? range_of(workspace, 1, (int64_t)ws_need, (int64_t)ws_need, 1) : Range{0, 0}, 4}};
+  if (sge_status st = check_mlp("grouped_mlp_bwd", G, T, H, F, activation, act_params, need, 10, ins, 8, outs, 6))
+    return st;
+  if (workspace_bytes < ws_need || (ws_need && !workspace))
+    return fail(SGE_ERR_WORKSPACE, "grouped_mlp_bwd: workspace %zu bytes, need %zu", workspace_bytes, ws_need);
+  const int32_t dact = activation == SGE_EPI_SCALED_SWIGLU  ? SGE_EPI_DSCALED_SWIGLU
+                       : activation == SGE_EPI_SCALED_SRELU ? SGE_EPI_DSCALED_SRELU
+                                                            : SGE_EPI_DSCALED_CLAMPED_SWIGLU;
+  // fc2: dgrad through the activation's backward (dpreact, dprobs), and its weight gradient
+  if (sge_status st = sge_grouped_linear_bwd(dout, act_out, w2, G, T, H, F, offsets, 1.0f, dact, act_params, preact,
+                                             probs, dpreact, dprobs, nullptr, dw2, workspace, workspace_bytes,
+                                             stream))
+    return st;
+  if (!dx && !dw1) return ok();
+  // fc1: dgrad and weight gradient from dpreact
+  return sge_grouped_linear_bwd(dpreact, x, w1, G, T, N1, H, offsets, 1.0f, SGE_EPI_NONE, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, dx, dw1, nullptr, 0, stream);
+}
+
 }  // extern "C"

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol(sge):
     lib = ctypes.CDLL(sge.library_path())
     for name in _declared():
         assert hasattr(lib, name), name
-    assert sge.abi_version() == 6
+    assert sge.abi_version() == 7
 
 
 def test_status_strings(sge):
@@ -451,3 +451,52 @@ def test_clamped_swiglu_epilogue_validation(sge):
     df = _act_after(sge._lib.sge_grouped_linear_dgrad_fp8, 10)
     assert df(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, cb, B(6), B(7), None, B(8),
               B(9), None, B(10), 1 << 20, None) == sge.ERR_NULL            # FP8 dgrad: act missing
+
+
+def test_grouped_mlp_validation(sge):
+    """The whole grouped MLP checks every argument before its first launch."""
+    def B(k):
+        return FAKE * 8 * k
+
+    G, T, H, F = 4, 100, 256, 256
+    sw = sge.EPI_SCALED_SWIGLU
+    f = sge._lib.sge_grouped_mlp_fwd
+    # x, w1, w2, G, T, H, F, splits, offsets, err, act, params, probs, preact, y, out, stream
+    ok = [B(1), B(1000), B(3000), G, T, H, F, B(5000), B(5100), None, sw, None, B(5200), B(6000), B(20000),
+          B(30000), None]
+    a = list(ok); a[0] = None
+    assert f(*a) == sge.ERR_NULL
+    a = list(ok); a[10] = sge.EPI_DSCALED_SWIGLU
+    assert f(*a) == sge.ERR_ARG                                           # a backward epilogue
+    a = list(ok); a[10] = sge.EPI_SCALED_CLAMPED_SWIGLU
+    assert f(*a) == sge.ERR_NULL                                          # clamped without its parameters
+    a = list(ok); a[6] = 200
+    assert f(*a) == sge.ERR_SHAPE                                         # gated: F % 128
+    a = list(ok); a[6] = 200; a[10] = sge.EPI_SCALED_SRELU; a[15] = B(1)
+    assert f(*a) == sge.ERR_ALIAS                                         # SReLU: F % 8 passes the shape check
+    a = list(ok); a[13] = B(6000) + 8
+    assert f(*a) == sge.ERR_ALIGN
+    a = list(ok); a[8] = B(5000) + 4
+    assert f(*a) == sge.ERR_ALIGN                                         # offsets: 8-byte aligned
+    a = list(ok); a[15] = B(1)
+    assert f(*a) == sge.ERR_ALIAS                                         # out over x
+    a = list(ok); a[14] = B(6000)
+    assert f(*a) == sge.ERR_ALIAS                                         # act_out over preact
+    a = list(ok); a[9] = B(5100)
+    assert f(*a) == sge.ERR_ALIAS                                         # err_flag over offsets
+    b = sge._lib.sge_grouped_mlp_bwd
+    ws = sge.grouped_mlp_bwd_workspace_size(T, F, G, sw)
+    assert ws == sge.grouped_linear_bwd_workspace_size(T, F, G, sge.EPI_DSCALED_SWIGLU) > 0
+    assert sge.grouped_mlp_bwd_workspace_size(T, F, G, sge.EPI_NONE) == 0
+    # dout, x, w1, w2, G, T, H, F, offsets, act, params, probs, preact, y, dpreact, dprobs, dx, dw1, dw2, ws, bytes
+    okb = [B(1), B(1000), B(2000), B(4000), G, T, H, F, B(5000), sw, None, B(5100), B(6000), B(20000), B(30000),
+           B(40000), B(50000), B(60000), B(80000), B(90000), ws, None]
+    assert b(*okb[:14], None, *okb[15:]) == sge.ERR_NULL                  # dpreact required
+    a = list(okb); a[19] = None
+    assert b(*a) == sge.ERR_WORKSPACE
+    a = list(okb); a[20] = ws - 4
+    assert b(*a) == sge.ERR_WORKSPACE
+    a = list(okb); a[19] = B(1000)
+    assert b(*a) == sge.ERR_ALIAS                                         # workspace over x
+    a = list(okb); a[16] = B(30000)
+    assert b(*a) == sge.ERR_ALIAS                                         # dx over dpreact
