@@ -209,3 +209,42 @@ def test_norm_steps_graph_replays_match_eager(kind):
 
     _replays_match(step, [Y, RS, f8["q"], f8["q_t"], f8["scale_inv"], mr[0], mr[1], mc[0], mc[1], DX, DG] +
                    ([MU, DB] if ln else []))
+
+
+@pytest.mark.parametrize("act", ["swiglu", "clamped_swiglu"])
+def test_grouped_mlp_module_graph_replays_match_eager(act):
+    """The whole grouped MLP calls (offsets, fc1 + activation, fc2, and the backward) captured
+    together in one graph."""
+    epi, params = ((sge.EPI_SCALED_SWIGLU, None) if act == "swiglu"
+                   else (sge.EPI_SCALED_CLAMPED_SWIGLU, (0.25, 1.702)))
+    inp = synth.grouped(700, 5, 256, 256, seed=34, splits=[0, 300, 1, 390, 9])
+    X, W1, W2, DOUT = dev_bf16(inp["x"]), dev_bf16(inp["w1"]), dev_bf16(inp["w2"]), dev_bf16(inp["dout"])
+    P = torch.from_numpy(inp["p"]).cuda()
+    splits = torch.from_numpy(inp["splits"]).cuda()
+    T, G, H, F = 700, 5, 256, 256
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    offs = torch.empty(G + 1, dtype=torch.int64, device="cuda")
+    err = torch.empty(1, dtype=torch.int32, device="cuda")
+    h, y, out = torch.empty(T, 2 * F, **bf), torch.empty(T, F, **bf), torch.empty(T, H, **bf)
+    dh, dp = torch.empty(T, 2 * F, **bf), torch.empty(T, dtype=torch.float32, device="cuda")
+    dx, dw1, dw2 = torch.empty(T, H, **bf), torch.empty(G, 2 * F, H, **bf), torch.empty(G, H, F, **bf)
+    ws = torch.empty(sge.grouped_mlp_bwd_workspace_size(T, F, G, epi), dtype=torch.uint8, device="cuda")
+    outs = [offs, err, h, y, out, dh, dp, dx, dw1, dw2]
+
+    def step():
+        sge.grouped_mlp_fwd(X, W1, W2, splits, offs, P, h, y, out, activation=epi, act=params, err_flag=err)
+        sge.grouped_mlp_bwd(DOUT, X, W1, W2, offs, P, h, y, dh, dp, dx=dx, dw1=dw1, dw2=dw2, workspace=ws,
+                            activation=epi, act=params)
+    step()
+    torch.cuda.synchronize()
+    want = [_bits(t) for t in outs]
+    g = _capture(step)
+    for _ in range(3):
+        for t in outs:
+            t.zero_()
+        torch.cuda.synchronize()
+        _ = torch.randn(64, 64, device="cuda") @ torch.randn(64, 64, device="cuda")   # eager work between
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip([_bits(t) for t in outs], want):
+            assert np.array_equal(a, b)
