@@ -752,6 +752,26 @@ def main():
         g.replay()
         per[name] = time_ms(torch, g.replay, 3) / reps
         del g
+    # HBM-bound launches (quantizers, norms) are timed cold as well: before each timed launch a
+    # 512 MiB write evicts the 256 MB Infinity Cache, so their inputs come from HBM; the median
+    # of 10 such launches is their duration (the warm graph figure is kept as ms_warm).
+    cold = {}
+    if any(k in hbm for k in per):
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for name, f in launches:
+            if name not in hbm:
+                continue
+            ts = []
+            for _ in range(10):
+                flush.zero_()
+                ev[0].record()
+                f()
+                ev[1].record()
+                torch.cuda.synchronize()
+                ts.append(ev[0].elapsed_time(ev[1]))
+            cold[name] = sorted(ts)[len(ts) // 2]
+        del flush
 
     fmt = wl["fmt"]
     peak = PEAK_TFLOPS[fmt]
@@ -761,8 +781,9 @@ def main():
             kernels[k] = {"ms": round(ms, 4), "tflops": round(flops[k] / ms / 1e9, 1),
                           "frac_peak": round(flops[k] / ms / 1e9 / peak, 4)}
         elif k in hbm:
-            kernels[k] = {"ms": round(ms, 4), "gbs": round(hbm[k] / ms / 1e6, 1),
-                          "frac_hbm": round(hbm[k] / ms / 1e6 / PEAK_HBM_GBS, 4)}
+            c = cold[k]
+            kernels[k] = {"ms": round(c, 4), "gbs": round(hbm[k] / c / 1e6, 1),
+                          "frac_hbm": round(hbm[k] / c / 1e6 / PEAK_HBM_GBS, 4), "ms_warm": round(ms, 4)}
         else:
             kernels[k] = {"ms": round(ms, 4)}
     dom = max((k for k in per if k in flops), key=lambda k: per[k])

@@ -130,6 +130,17 @@ __device__ __forceinline__ bool group_tile(const int64_t* __restrict__ layout, i
 // transposed copy is written through LDS so each column's 128 rows leave as one 128-byte
 // line. Tiles are visited in the reverse order of the amax pass, which left the most
 // recently read part of the tensor in the last-level cache.
+// The dispatcher hands workgroups to the 8 XCDs round-robin (workgroup b runs on XCD b % 8),
+// each with its own L2. Renumbering tiles so that XCD x takes one contiguous range makes the
+// tiles an XCD runs together neighbours (a tile's 64-byte rowwise output rows are half a
+// 128-byte line whose other half the next column tile writes). Bijective on [0, total).
+// Used by the grouped quantizers, where it measured 3-13% faster.
+__device__ __forceinline__ int64_t xcd_tile(int64_t bid, int64_t total) {
+  const int64_t x = bid & 7, i = bid >> 3;
+  const int64_t q = total >> 3, r = total & 7;
+  return x * q + (x < r ? x : r) + i;
+}
+
 constexpr int kQR = 128, kQC = 64;
 
 __global__ __launch_bounds__(256) void quantize_fp8_kernel(
@@ -229,8 +240,11 @@ __global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const uint16_t* __r
                                                             const int64_t* __restrict__ layout, int64_t ld_t) {
   __shared__ __attribute__((aligned(16))) uint16_t xt[kMC][kMR + 8];    // [column][row] bf16 bits
   const int64_t tc = (cols + kMC - 1) / kMC;
-  const int64_t p0 = (int64_t)(blockIdx.x / tc) * kMR;     // first row (dense) or stored position
-  const int64_t c0 = (int64_t)(blockIdx.x % tc) * kMC;
+  // Grouped (token-blocked) tiles in XCD-contiguous ranges: measured 5% faster there, while
+  // the dense order suits the dense layout better (7-10% faster on a 16384 x 8192 tensor).
+  const int64_t tile = GROUPED ? xcd_tile(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
+  const int64_t p0 = (tile / tc) * kMR;                   // first row (dense) or stored position
+  const int64_t c0 = (tile % tc) * kMC;
   int64_t r0 = p0;               // first source row of the tile
   int64_t nrows = rows - p0;     // source rows of the tile that exist
   int64_t npos = rows - p0;      // columnwise positions the tile writes
@@ -402,8 +416,9 @@ __global__ __launch_bounds__(256) void quantize_fp8_grouped_kernel(
     }
   }
   const int64_t tc = (cols + kQC - 1) / kQC;
-  const int64_t p0 = (int64_t)(blockIdx.x / tc) * kQR;
-  const int64_t c0 = (int64_t)(blockIdx.x % tc) * kQC;
+  const int64_t tid = xcd_tile(blockIdx.x, gridDim.x);
+  const int64_t p0 = (tid / tc) * kQR;
+  const int64_t c0 = (tid % tc) * kQC;
   int g;
   int64_t r0, nrows;
   if (!group_tile(layout, G, rows, p0, g, r0, nrows)) return;   // block-uniform
