@@ -126,10 +126,6 @@ __device__ __forceinline__ bool group_tile(const int64_t* __restrict__ layout, i
   return true;
 }
 
-// Tiles of 128 rows x 64 columns; 256 threads, 8 bf16 (16 B) per thread per pass. The
-// transposed copy is written through LDS so each column's 128 rows leave as one 128-byte
-// line. Tiles are visited in the reverse order of the amax pass, which left the most
-// recently read part of the tensor in the last-level cache.
 // The dispatcher hands workgroups to the 8 XCDs round-robin (workgroup b runs on XCD b % 8),
 // each with its own L2. Renumbering tiles so that XCD x takes one contiguous range makes the
 // tiles an XCD runs together neighbours (a tile's 64-byte rowwise output rows are half a
@@ -141,6 +137,10 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t bid, int64_t total) {
   return x * q + (x < r ? x : r) + i;
 }
 
+// Tiles of 128 rows x 64 columns; 256 threads, 8 bf16 (16 B) per thread per pass. The
+// transposed copy is written through LDS so each column's 128 rows leave as one 128-byte
+// line. Tiles are visited in the reverse order of the amax pass, which left the most
+// recently read part of the tensor in the last-level cache.
 constexpr int kQR = 128, kQC = 64;
 
 __global__ __launch_bounds__(256) void quantize_fp8_kernel(
