@@ -10,7 +10,9 @@ inputs already resident in HBM:
   of both layers.
 
 Prints ONE JSON line on stdout. The default workload is the bf16 forward +
-backward at M = N = K = 4096 (alpha 0.125). The timed region is ``--steps``
+backward at M = N = K = 4096 (alpha 0.125). Before the ``--warmup`` steps the
+step runs untimed for ``--ramp-seconds`` (the GPU raises its clocks over the
+first ~100 ms of load). The timed region is ``--steps``
 eager steps between HIP events; ``ms_per_step_graph`` replays the same step
 captured as one HIP graph (every libsge call is capture-safe), for
 comparison. Per-kernel durations come from a graph of repeated
@@ -43,6 +45,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--ramp-seconds", type=float, default=0.3,
+                    help="untimed steps run for this long before the warm-up steps (the GPU's clock ramp)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -734,27 +738,42 @@ def main():
         print(json.dumps({"profile_launch": args.profile_launch, PROFILE_REPS_KEY: args.profile_reps}), flush=True)
         return 0
 
+    # Clock ramp: under sustained load MI355X raises its clocks over the first ~50-100 ms (the
+    # 4096^3 bf16 step falls from 0.50 to 0.33 ms over its first ~150 steps, and is back near
+    # 0.40 ms after 2 s idle), so the step runs untimed for ramp_seconds before the `warmup`
+    # steps, and the timed steps measure the steady state a training loop runs at.
+    t_end = time.perf_counter() + args.ramp_seconds
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            eager_step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         eager_step()
     torch.cuda.synchronize()
     # The timed region: exactly `steps` eager steps between HIP events, synchronized on both sides.
     ms_per_step = time_ms(torch, eager_step, args.steps)
-    # The same step as one HIP graph (reported for comparison; not the timed value).
-    graph = capture(torch, [f for _, f in launches])
-    ms_graph = time_ms(torch, graph.replay, max(1, min(args.steps, 10)))
-    del graph
-    # Per-kernel durations: a graph of `reps` back-to-back launches of one call, timed with
-    # HIP events around its replays (the kernels run on the replay stream the events mark).
-    per = {}
+    # The same step as one HIP graph (reported for comparison; not the timed value), and per
+    # kernel a graph of `reps` back-to-back launches of one call. Capturing leaves the GPU idle
+    # for milliseconds, long enough for its clocks to drop, so every graph is captured first,
+    # the step runs untimed again for half the ramp time, and only then are the graphs timed
+    # with HIP events around their replays (on the replay stream the events mark).
     reps = 8
-    for name, f in launches:
-        g = capture(torch, [f] * reps)
+    step_graph = capture(torch, [f for _, f in launches])
+    graphs = {name: capture(torch, [f] * reps) for name, f in launches}
+    t_end = time.perf_counter() + args.ramp_seconds / 2
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            eager_step()
+        torch.cuda.synchronize()
+    ms_graph = time_ms(torch, step_graph.replay, max(1, min(args.steps, 10)))
+    per = {}
+    for name, g in graphs.items():
         g.replay()
         per[name] = time_ms(torch, g.replay, 3) / reps
-        del g
+    del step_graph, graphs
     # HBM-bound launches (quantizers, norms) are timed cold as well: before each timed launch a
     # 512 MiB write evicts the 256 MB Infinity Cache, so their inputs come from HBM; the median
-    # of 10 such launches is their duration (the warm graph figure is kept as ms_warm).
+    # of 10 such launches is their duration (the in-step figure is kept as ms_warm).
     cold = {}
     if any(k in hbm for k in per):
         flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
@@ -797,7 +816,8 @@ def main():
     cfg.update({k: wl[k] for k in ("M", "N", "K", "T", "G", "hidden", "ffn", "alpha") if k in wl})
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "ms_per_step_graph": round(ms_graph, 4),
+        "warmup": args.warmup, "warmup_ramp_s": args.ramp_seconds, "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_graph": round(ms_graph, 4),
         "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": fmt, "data": "synthetic (seeded; see synth/)",
         "config": cfg, "frac_of_peak": round(value / peak, 4), "kernels": kernels, "roofline": roofline,
