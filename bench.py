@@ -732,6 +732,11 @@ def main():
             return 2
         eager_step()
         torch.cuda.synchronize()
+        t_end = time.perf_counter() + args.ramp_seconds      # the clock ramp, as for the timed steps
+        while time.perf_counter() < t_end:
+            for _ in range(8):
+                eager_step()
+            torch.cuda.synchronize()
         for _ in range(args.profile_reps):
             fns[args.profile_launch]()
         torch.cuda.synchronize()
