@@ -261,7 +261,9 @@ sge_status sge_grouped_linear_fwd(const void* x, const void* w, int32_t G, int64
  *   dpreact [T, N1] and dprobs [T] (the activation's backward in fc2's dgrad), dw2 [G, H, F],
  *   dx [T, H], dw1 [G, N1, H] (bf16; dx, dw1, dw2 may each be NULL to skip). workspace: device,
  *   >= sge_grouped_mlp_bwd_workspace_size(T, F, G, activation) bytes.
- * All bf16 tensors 16-byte aligned; outputs may not overlap inputs or each other.
+ * All bf16 tensors 16-byte aligned; outputs may not overlap inputs or each other. With T == 0
+ * the T-sized tensors may be NULL: the forward writes the offsets only, the backward zeros
+ * dw1 and dw2 (empty sums).
  */
 sge_status sge_grouped_mlp_fwd(const void* x, const void* w1, const void* w2, int32_t G, int64_t T,
                                int64_t H, int64_t F, const int64_t* splits, int64_t* offsets,

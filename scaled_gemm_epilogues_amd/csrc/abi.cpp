@@ -1095,7 +1095,8 @@ static sge_status check_mlp(const char* what, int32_t G, int64_t T, int64_t H, i
     return fail(SGE_ERR_ARG, "%s: activation %d not allowed", what, activation);
   if (sge_status st = check_act(activation, act_params, what)) return st;
   for (int i = 0; i < n_need; ++i)
-    if (!need[i]) return fail(SGE_ERR_NULL, "%s: a required pointer is NULL (required argument %d)", what, i);
+    if (!need[i])
+      return fail(SGE_ERR_NULL, "%s: a required pointer is NULL (W1, W2, offsets, or a T-sized tensor)", what);
   if (H % 8 || F % 8) return fail(SGE_ERR_SHAPE, "%s: H and F must be multiples of 8", what);
   if (gated_fwd(activation) && F % 128) return fail(SGE_ERR_SHAPE, "%s: a gated activation needs F %% 128 == 0", what);
   for (int i = 0; i < n_in + n_out; ++i) {
@@ -1116,7 +1117,9 @@ sge_status sge_grouped_mlp_fwd(const void* x, const void* w1, const void* w2, in
                                int32_t activation, const sge_act_params* act_params, const float* probs,
                                void* preact, void* act_out, void* out, hipStream_t stream) {
   const int64_t N1 = gated_fwd(activation) ? 2 * F : F;
-  const void* need[9] = {x, w1, w2, splits, offsets, probs, preact, act_out, out};
+  // the T-sized tensors may be NULL (empty) when T == 0
+  const void* need[9] = {w1, w2, splits, offsets, T ? x : w1, T ? probs : w1, T ? preact : w1, T ? act_out : w1,
+                         T ? out : w1};
   const Arg ins[5] = {{range_of(x, T, H, H, 2), 16}, {range_of(w1, (int64_t)G * N1, H, H, 2), 16},
                       {range_of(w2, (int64_t)G * H, F, F, 2), 16}, {range_of(splits, 1, G, G, 8), 8},
                       {range_of(probs, 1, T, T, 4), 4}};
@@ -1149,7 +1152,9 @@ sge_status sge_grouped_mlp_bwd(const void* dout, const void* x, const void* w1, 
                                const void* act_out, void* dpreact, float* dprobs, void* dx, void* dw1, void* dw2,
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const int64_t N1 = gated_fwd(activation) ? 2 * F : F;
-  const void* need[10] = {dout, x, w1, w2, offsets, probs, preact, act_out, dpreact, dprobs};
+  // the T-sized tensors may be NULL (empty) when T == 0
+  const void* need[10] = {w1, w2, offsets, T ? dout : w1, T ? x : w1, T ? probs : w1, T ? preact : w1,
+                          T ? act_out : w1, T ? dpreact : w1, T ? dprobs : w1};
   const Arg ins[8] = {{range_of(dout, T, H, H, 2), 16}, {range_of(x, T, H, H, 2), 16},
                       {range_of(w1, (int64_t)G * N1, H, H, 2), 16}, {range_of(w2, (int64_t)G * H, F, F, 2), 16},
                       {range_of(offsets, 1, G + 1, G + 1, 8), 8}, {range_of(probs, 1, T, T, 4), 4},
@@ -1164,6 +1169,13 @@ sge_status sge_grouped_mlp_bwd(const void* dout, const void* x, const void* w1, 
     return st;
   if (workspace_bytes < ws_need || (ws_need && !workspace))
     return fail(SGE_ERR_WORKSPACE, "grouped_mlp_bwd: workspace %zu bytes, need %zu", workspace_bytes, ws_need);
+  if (T == 0) {                                          // empty groups: zero weight gradients
+    hipError_t e = hipSuccess;
+    if (dw2) e = sge::launch_fill_bf16_zero(static_cast<uint16_t*>(dw2), (int64_t)G * H, F, F, stream);
+    if (e == hipSuccess && dw1)
+      e = sge::launch_fill_bf16_zero(static_cast<uint16_t*>(dw1), (int64_t)G * N1, H, H, stream);
+    return hip_status(e, "grouped_mlp_bwd fill");
+  }
   const int32_t dact = activation == SGE_EPI_SCALED_SWIGLU  ? SGE_EPI_DSCALED_SWIGLU
                        : activation == SGE_EPI_SCALED_SRELU ? SGE_EPI_DSCALED_SRELU
                                                             : SGE_EPI_DSCALED_CLAMPED_SWIGLU;

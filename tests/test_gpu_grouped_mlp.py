@@ -93,3 +93,37 @@ def test_grouped_mlp_module_flags_bad_splits():
     inp = synth.grouped(300, 3, 256, 256, seed=43, splits=[100, 100, 99])    # sums to 299, not T = 300
     got = _module(inp, sge.EPI_SCALED_SWIGLU, None)
     assert int(got["err"].item()) == 1
+
+
+def test_grouped_mlp_module_edge_cases():
+    """No tokens (offsets still written, nothing else launched), one group, every token in one
+    group of several."""
+    # T = 0
+    G, H, F = 3, 256, 128
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    W1 = torch.zeros(G, 2 * F, H, **bf)
+    W2 = torch.zeros(G, H, F, **bf)
+    X = torch.zeros(0, H, **bf)
+    S = torch.zeros(G, dtype=torch.int64, device="cuda")
+    offs = torch.full((G + 1,), -1, dtype=torch.int64, device="cuda")
+    err = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    empty = torch.zeros(0, 2 * F, **bf)
+    sge.grouped_mlp_fwd(X, W1, W2, S, offs, torch.zeros(0, device="cuda"), empty, torch.zeros(0, F, **bf),
+                        torch.zeros(0, H, **bf), err_flag=err)
+    torch.cuda.synchronize()
+    assert torch.equal(offs.cpu(), torch.zeros(G + 1, dtype=torch.int64)) and int(err.item()) == 0
+    dw1, dw2 = torch.ones(G, 2 * F, H, **bf), torch.ones(G, H, F, **bf)
+    sge.grouped_mlp_bwd(torch.zeros(0, H, **bf), X, W1, W2, offs, torch.zeros(0, device="cuda"), empty,
+                        torch.zeros(0, F, **bf), torch.zeros(0, 2 * F, **bf), torch.zeros(0, device="cuda"),
+                        dx=torch.zeros(0, H, **bf), dw1=dw1, dw2=dw2)
+    torch.cuda.synchronize()
+    assert torch.all(dw1 == 0) and torch.all(dw2 == 0)                 # empty sums
+    # one group, and all tokens in the middle group of three
+    for splits, G in (([300], 1), ([0, 300, 0], 3)):
+        inp = synth.grouped(300, G, 256, 128, seed=44, splits=splits)
+        got = _module(inp, sge.EPI_SCALED_SWIGLU, None)
+        ref = run_grouped_mlp(inp)
+        for k in ("h", "y", "out", "dh", "dx", "dw1", "dw2"):
+            assert torch.equal(got[k].view(torch.int16), ref[k].view(torch.int16)), (splits, k)
+        if G == 3:
+            assert torch.all(got["dw1"][0] == 0) and torch.all(got["dw2"][2] == 0)
