@@ -58,7 +58,10 @@ constexpr int kWavesM = SGE_WAVES_M, kWavesN = SGE_WAVES_N, kFragsM = SGE_FRAGS_
 #define SGE_XCD_GROUP_M 4
 #endif
 #ifndef SGE_RD_PER_MFMA
-#define SGE_RD_PER_MFMA 2
+#define SGE_RD_PER_MFMA 2        // fragment reads issued after each MFMA (bf16, E4M3)
+#endif
+#ifndef SGE_RD_PER_MFMA_MX
+#define SGE_RD_PER_MFMA_MX 1     // the same for MXFP8 (one read per MFMA: 7% faster step than two)
 #endif
 #ifndef SGE_DSWIGLU_BATCH
 #define SGE_DSWIGLU_BATCH 8      // dSwiGLU epilogue chunks whose loads are in flight together
@@ -530,7 +533,7 @@ void gemm_kernel(const GemmParams p) {
 
   // Issue order inside a scheduling region: the next step's fragment reads go out early,
   // kRdPer after each of the first MFMAs, and the remaining MFMAs cover their latency.
-  constexpr int kRdPer0 = SGE_RD_PER_MFMA;
+  constexpr int kRdPer0 = kMX ? SGE_RD_PER_MFMA_MX : SGE_RD_PER_MFMA;
   constexpr int kRdPer = kRdPer0 * kMfma >= kReads ? kRdPer0 : (kReads + kMfma - 1) / kMfma;
   constexpr int kRdFull = kReads / kRdPer, kRdRem = kReads % kRdPer;
   constexpr int kRdUsed = kRdFull + (kRdRem ? 1 : 0);
