@@ -281,7 +281,7 @@ void gemm_kernel(const GemmParams p) {
   if constexpr (SCHED == S_DENSE) {
     const int MT = p.mt_count, NT = p.nt_count;
     const int bid = xcd_tile(blockIdx.x, MT * NT);                      // grid is exactly MT * NT
-    const int GM = SGE_XCD_GROUP_M;
+    const int GM = FMT == F_E4M3 ? 8 : SGE_XCD_GROUP_M;   // E4M3: 8 measured 1.2% faster (FP8 step)
     const int group = bid / (GM * NT);
     const int first_m = group * GM;
     const int gsz = min(MT - first_m, GM);
