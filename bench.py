@@ -540,7 +540,7 @@ def _pmc_rows(path):
     return out
 
 
-def summarize_traffic(pmc_dir):
+def summarize_traffic(pmc_dir, out_dir=None):
     """profiles/traffic.json: HBM bytes per launch of each profiled kernel.
 
     Expects rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs named ``copy_<COUNTER>`` (of
@@ -594,9 +594,10 @@ def summarize_traffic(pmc_dir):
         out["raw_kib_per_launch"][f"{wl}:{key}"] = {"FETCH_SIZE": fetch / 1024.0, "WRITE_SIZE": write / 1024.0}
         kern = " + ".join(f"`{k.split('(')[0].replace('void ', '')[:60]}`" for k in per_kernel)
         md.append(f"| {wl} | {key} | {kern} | {fetch / 2**20:.1f} | {write / 2**20:.1f} | {t / 1e6:.1f} |")
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    with open(os.path.join(out_dir, "traffic.json"), "w") as fh:
         json.dump(out, fh, indent=1)
-    with open(os.path.join(ROOT, "profiles", "traffic_per_launch.md"), "w") as fh:
+    with open(os.path.join(out_dir, "traffic_per_launch.md"), "w") as fh:
         fh.write("\n".join(md) + "\n")
     print("\n".join(md))
 
@@ -604,7 +605,7 @@ def summarize_traffic(pmc_dir):
 MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F8"
 
 
-def summarize_mfma(pmc_dir):
+def summarize_mfma(pmc_dir, out_dir=None):
     """profiles/mfma_util.md and .json: MFMA utilisation of each profiled GEMM launch.
 
     Expects one rocprofv3 --pmc run of MFMA_COUNTERS per launch, named
@@ -655,9 +656,10 @@ def summarize_mfma(pmc_dir):
         kern = last[0]["kernel"].split("(")[0].replace("void ", "")
         md.append(f"| {wl} | {key} | `{kern}` | {busy:.3f} | {clk:.2f} | {tflop:.3f} | {ns / 1e3:.1f} | "
                   f"{busy * clk / 2.4:.3f} |")
-    with open(os.path.join(ROOT, "profiles", "mfma_util.json"), "w") as fh:
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    with open(os.path.join(out_dir, "mfma_util.json"), "w") as fh:
         json.dump(out, fh, indent=1)
-    with open(os.path.join(ROOT, "profiles", "mfma_util.md"), "w") as fh:
+    with open(os.path.join(out_dir, "mfma_util.md"), "w") as fh:
         fh.write("\n".join(md) + "\n")
     print("\n".join(md))
 
