@@ -57,6 +57,12 @@ constexpr int kWavesM = SGE_WAVES_M, kWavesN = SGE_WAVES_N, kFragsM = SGE_FRAGS_
 #ifndef SGE_XCD_GROUP_M
 #define SGE_XCD_GROUP_M 4
 #endif
+#ifndef SGE_GROUPED_GM
+#define SGE_GROUPED_GM 4         // row tiles per band in a group's tile order (grouped rows)
+#endif
+#ifndef SGE_GROUPED_GM_STORE
+#define SGE_GROUPED_GM_STORE 8   // the same for plain-store launches with a K-major weight
+#endif
 #ifndef SGE_RD_PER_MFMA
 #define SGE_RD_PER_MFMA 2        // fragment reads issued after each MFMA (bf16, E4M3)
 #endif
@@ -306,10 +312,12 @@ void gemm_kernel(const GemmParams p) {
     }
     total *= p.nt_count;
     if ((int)blockIdx.x >= total) return;                // beyond the last real tile
-    const int t = xcd_tile(blockIdx.x, total);
-    nt = t % p.nt_count;
-    int lin = t / p.nt_count;
-    int g = -1;
+    // Each group's row tiles x column tiles are contiguous in t; inside a group they go in
+    // bands of SGE_GROUPED_GM row tiles, row tile fastest, so the tiles an XCD runs together
+    // share a few panels of both operands (a 16-column-tile gated fc1 otherwise spans 2 row
+    // bands x 16 weight panels per 32 tiles).
+    int w = xcd_tile(blockIdx.x, total);
+    int g = -1, mtg = 0;
     int64_t lo = 0, hi = 0, prev = 0;
     for (int gg = 0; gg < p.G; ++gg) {
       int64_t a = p.offsets[gg], b = p.offsets[gg + 1];
@@ -317,10 +325,19 @@ void gemm_kernel(const GemmParams p) {
       b = b < a ? a : (b > p.T ? p.T : b);
       prev = b;
       const int tiles = (int)((b - a + BM - 1) / BM);
-      if (lin < tiles) { g = gg; lo = a; hi = b; break; }
-      lin -= tiles;
+      if (w < tiles * p.nt_count) { g = gg; lo = a; hi = b; mtg = tiles; break; }
+      w -= tiles * p.nt_count;
     }
     if (g < 0) return;                                   // beyond the last real tile
+    // Bands of 8 for plain stores with a K-major weight (4-10% faster fc2 forward and FP8 /
+    // MXFP8 fc1 dgrad than 4), 4 elsewhere (8 is 4-6% slower on the gated fc1 forward and
+    // the bf16 dgrad, whose weight is read N-major).
+    constexpr int GMG = (EPI == E_STORE && BK) ? SGE_GROUPED_GM_STORE : SGE_GROUPED_GM;
+    const int first = w / (GMG * p.nt_count) * GMG;
+    const int gsz = min(mtg - first, GMG);
+    const int in_band = w % (GMG * p.nt_count);
+    const int lin = first + in_band % gsz;
+    nt = in_band / gsz;
     grp = g;
     m0 = lo + (int64_t)lin * BM;
     row_end = hi;
