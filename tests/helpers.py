@@ -123,3 +123,36 @@ def clamp_settled_h(gpu_dh, dh, gy, h, p, act, delta=2.0 ** -16):
     gpu_dh = np.asarray(gpu_dh, np.float64)
     take = amb & (np.abs(gpu_dh - alt) < np.abs(gpu_dh - dh))
     return np.where(take, other, h), int(amb.sum())
+
+
+def assert_oracle_mx_rowwise(bits, q, s, what=""):
+    """MXFP8 bytes written by a fused epilogue equal the oracle's rowwise MXFP8 of the GPU's own
+    bf16 tensor (``bits``, uint16): the quantization is a function of the bf16 values alone, so
+    the codes and E8M0 scales must agree bit for bit."""
+    from oracle import quant
+    rq, rs = quant.mxfp8_rowwise(np.asarray(bits, np.uint16))
+    q, s = np.asarray(q), np.asarray(s)
+    assert q.shape == rq.shape and s.shape == rs.shape, (what, q.shape, rq.shape, s.shape, rs.shape)
+    if not np.array_equal(s, rs):
+        i = np.argwhere(s != rs)[0]
+        raise AssertionError(f"{what}: E8M0 scale {tuple(i)} = {s[tuple(i)]}, oracle {rs[tuple(i)]}")
+    if not np.array_equal(q, rq):
+        i = np.argwhere(q != rq)[0]
+        raise AssertionError(f"{what}: code {tuple(i)} = {q[tuple(i)]:#04x}, oracle {rq[tuple(i)]:#04x}")
+
+
+def assert_oracle_fp8_grouped(bits, got, c, pad, what=""):
+    """Per-group FP8 current scaling written by the GPU (``got``: amax, scale, scale_inv, q and,
+    if present, q_t in the aligned token layout) equals the oracle's applied to the GPU's own
+    bf16 tensor ``bits``: amax, scale and scale_inv as fp32 bit patterns, every code."""
+    from oracle import quant
+    ld = None if got.get("q_t") is None else got["q_t"].shape[1]
+    ref = quant.fp8_current_scaling_grouped(np.asarray(bits, np.uint16), c, pad, ld)
+    for k in ("amax", "scale", "scale_inv"):
+        g = got[k].detach().cpu().numpy().astype(np.float32)
+        assert np.array_equal(g.view(np.uint32), ref[k].astype(np.float32).view(np.uint32)), (what, k, g, ref[k])
+    lo, hi = int(c[0]), int(c[-1])
+    assert np.array_equal(host_u8(got["q"])[lo:hi], ref["q"][lo:hi]), f"{what}: codes differ from the oracle's"
+    if ld is not None:
+        P = int(pad[-1])
+        assert np.array_equal(host_u8(got["q_t"])[:, :P], ref["q_t"][:, :P]), f"{what}: transposed codes differ"

@@ -13,7 +13,8 @@ from oracle import grouped, linear, offsets, quant
 from oracle.codecs import bf16_to_f64, f64_to_bf16
 
 from .gpu_paths import run_dense, run_grouped_mlp, run_grouped_mlp_bwd_mx, run_grouped_mlp_fp8, run_grouped_mlp_fwd_mx
-from .helpers import TAU_BF16, TAU_FP8, assert_close, assert_mx_dequant_close, host_f64, host_u8
+from .helpers import (TAU_BF16, TAU_FP8, assert_close, assert_mx_dequant_close, assert_oracle_mx_rowwise, host_bits,
+                      host_f64, host_u8)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -21,6 +22,29 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 def _pick(n, k, rng):
     idx = set(rng.choice(n, size=min(k, n), replace=False).tolist()) | {0, n - 1}
     return np.array(sorted(idx))
+
+
+def _small_and_largest(sizes):
+    """The two smallest non-empty groups and the largest one."""
+    small = [int(v) for v in np.argsort(np.where(sizes > 0, sizes, 1 << 62))[:2]]
+    return sorted(set(small) | {int(np.argmax(sizes))})
+
+
+def _boundary_and_sampled_rows(base, rng, k):
+    """k sampled token rows plus every non-empty group's first and last row."""
+    T = int(base[-1])
+    rows = set(rng.choice(T, size=min(k, T), replace=False).tolist())
+    for g in range(len(base) - 1):
+        if base[g + 1] > base[g]:
+            rows |= {int(base[g]), int(base[g + 1]) - 1}
+    return np.array(sorted(rows))
+
+
+def _assert_fused_mx_rows(y, yq, ys, base, rng, what):
+    """Fused MXFP8 rows of a bf16 tensor == the oracle's rowwise MXFP8 of those bf16 rows."""
+    rows = _boundary_and_sampled_rows(base, rng, 2048)
+    rr = torch.from_numpy(rows).cuda()
+    assert_oracle_mx_rowwise(host_bits(y[rr]), host_u8(yq[rr]), host_u8(ys[rr]), what=what)
 
 
 def _fp8_rows(bits, rows, scale):
@@ -166,6 +190,9 @@ def test_grouped_mxfp8_forward_full_size_sampled():
     assert np.array_equal(host_u8(got["yq"]), host_u8(got["y_unfused"]["q_row"]))
     assert np.array_equal(host_u8(got["ys"]), host_u8(got["y_unfused"]["s_row"]))
     base = offsets.base_offsets(inp["splits"])
+    # and the oracle's MXFP8 of the launch's bf16 y (rowwise blocks are row-local): sampled rows
+    # and every group's first and last row
+    _assert_fused_mx_rows(got["y"], got["yq"], got["ys"], base, np.random.default_rng(21), "y (fused MXFP8)")
     sizes = np.diff(base)
     nonempty = [g for g in range(len(sizes)) if sizes[g] > 0]
     rng = np.random.default_rng(11)
@@ -196,12 +223,15 @@ def test_grouped_mxfp8_backward_full_size_sampled():
     assert np.array_equal(host_u8(got["dhq"]), host_u8(got["dh_unfused"]["q_row"]))
     assert np.array_equal(host_u8(got["dhs"]), host_u8(got["dh_unfused"]["s_row"]))
     base = offsets.base_offsets(inp["splits"])
+    # and the oracle's MXFP8 of the launch's bf16 dh, on sampled rows and the group boundaries
+    _assert_fused_mx_rows(got["dh"], got["dhq"], got["dhs"], base, np.random.default_rng(22), "dh (fused MXFP8)")
     sizes = np.diff(base)
     F = inp["w2"].shape[2]
     rng = np.random.default_rng(12)
     kw = dict(rel_tight=2.0 ** -3, abs_tight=0.1)
-    # the two smallest non-empty groups: the wgrad samples need the oracle over a whole group
-    for g in [int(v) for v in np.argsort(np.where(sizes > 0, sizes, 1 << 62))[:2]]:
+    # the two smallest non-empty groups and the largest one (its wgrad tiles have the longest
+    # contraction); the wgrad samples take sampled columns over all of a group's tokens
+    for g in _small_and_largest(sizes):
         lo, hi = int(base[g]), int(base[g + 1])
         Tg = hi - lo
         # per-token outputs at sampled tokens (the per-token oracle on those tokens alone)
@@ -243,8 +273,26 @@ def test_grouped_fp8_full_size_sampled():
     sizes = np.diff(base)
     rng = np.random.default_rng(13)
     kw = dict(rel_tight=2.0 ** -3, abs_tight=0.1)
-    # per-group scales depend on a whole group: the oracle reruns the two smallest groups whole
-    for g in [int(v) for v in np.argsort(np.where(sizes > 0, sizes, 1 << 62))[:2]]:
+    # the fused amax of y and dh, and the codes quantized with it: the oracle's per-group current
+    # scaling of the launch's bf16 tensors (amax and scales over each whole group; codes of
+    # sampled rows and the group boundaries)
+    for key, q in (("y", "qy"), ("dh", "qdh")):
+        bits = host_bits(got[key])
+        rows = _boundary_and_sampled_rows(base, np.random.default_rng(23), 2048)
+        rr = torch.from_numpy(rows).cuda()
+        qrows = host_u8(got[q]["q"][rr])
+        for g in range(len(sizes)):
+            lo, hi = int(base[g]), int(base[g + 1])
+            a = quant.amax(bits[lo:hi])
+            s_ = quant.fp8_scale(a)
+            for k, ref in (("amax", a), ("scale", s_), ("scale_inv", quant.fp8_scale_inv(s_))):
+                gv = np.float32(got[q][k][g].item())
+                assert gv.view(np.uint32) == np.float32(ref).view(np.uint32), (key, g, k, gv, ref)
+            sel = (rows >= lo) & (rows < hi)
+            assert np.array_equal(qrows[sel], quant.fp8_quantize_with_scale(bits[rows[sel]], s_)), (key, g)
+    # per-group scales depend on a whole group: the oracle reruns the two smallest groups and the
+    # largest one whole
+    for g in _small_and_largest(sizes):
         lo, hi = int(base[g]), int(base[g + 1])
         one = np.array([0, hi - lo])
         args = (inp["x"][lo:hi], inp["w1"][g:g + 1], inp["w2"][g:g + 1], inp["p"][lo:hi], one)
@@ -285,7 +333,17 @@ def test_rmsnorm_full_size_sampled():
     torch.cuda.synchronize()
     # the fused MXFP8 copies equal the standalone quantizer on the same bf16 output, whole tensor
     assert np.array_equal(host_u8(mx_row[0]), host_u8(alone["q_row"]))
+    assert np.array_equal(host_u8(mx_row[1]), host_u8(alone["s_row"]))
+    assert np.array_equal(host_u8(mx_col[0]), host_u8(alone["q_colT"]))
     assert np.array_equal(host_u8(mx_col[1]), host_u8(alone["s_colT"]))
+    # and the oracle's MXFP8 of the launch's bf16 output: sampled rows (rowwise copy) and sampled
+    # columns (columnwise copy, blocks down a column)
+    rs_ = _pick(M, 256, np.random.default_rng(16))
+    cs_ = _pick(K, 128, np.random.default_rng(17))
+    rr, cc = torch.from_numpy(rs_).cuda(), torch.from_numpy(cs_).cuda()
+    assert_oracle_mx_rowwise(host_bits(Y[rr]), host_u8(mx_row[0][rr]), host_u8(mx_row[1][rr]), what="norm MXFP8 row")
+    assert_oracle_mx_rowwise(host_bits(Y[:, cc].t()), host_u8(mx_col[0][cc]), host_u8(mx_col[1][cc]),
+                             what="norm MXFP8 col")
     rows = _pick(M, 8, np.random.default_rng(14))
     ref = norm.norm_fwd("rms", d["x"][rows], d["gamma"], None, w["eps"])
     tt = torch.from_numpy(rows).cuda()

@@ -11,8 +11,8 @@ import synth
 from oracle import grouped, offsets, quant
 
 from .gpu_paths import mx_layout, quant_fp8_grouped, run_grouped_mlp_fp8
-from .helpers import (TAU_FP8, assert_close, assert_close_requantized, clamp_settled_h, dev, dev_bf16, host_f64,
-                      host_u8)
+from .helpers import (TAU_FP8, assert_close, assert_close_requantized, assert_oracle_fp8_grouped, clamp_settled_h,
+                      dev, dev_bf16, host_bits, host_f64, host_u8)
 
 pytestmark = pytest.mark.gpu
 
@@ -131,7 +131,12 @@ def test_fp8_grouped_mlp_fwd_bwd(case, act):
     base = offsets.base_offsets(inp["splits"])
     fwd = grouped.grouped_mlp_fwd_fp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base, act)
     bwd = grouped.grouped_mlp_bwd_fp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base, inp["dout"], fwd=fwd, act=act)
-    # the amax fused into the epilogues == the quantizer's own amax pass: identical bytes
+    # the amax fused into the epilogues, and the bytes quantized with it, == the oracle's per-group
+    # current scaling of the same launch's bf16 y and dh
+    c, pad = quant.mx_group_layout(base, T)
+    assert_oracle_fp8_grouped(host_bits(got["y"]), got["qy"], c, pad, what="y (fused amax)")
+    assert_oracle_fp8_grouped(host_bits(got["dh"]), got["qdh"], c, pad, what="dh (fused amax)")
+    # and == the quantizer's own amax pass: identical bytes
     for fused, alone in (("qy", "qy_alone"), ("qdh", "qdh_alone")):
         for k in ("amax", "scale", "scale_inv"):
             assert np.array_equal(_host_f32(got[fused][k]), _host_f32(got[alone][k])), (fused, k)

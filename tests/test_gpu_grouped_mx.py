@@ -1,7 +1,8 @@
 """MXFP8 grouped MLP forward with the fused activation + group quantize, against the oracle.
 
-The fused MXFP8 output of fc1 must equal, byte for byte, the standalone MXFP8 quantizer run on
-the same launch's bf16 output (the fusion of the activation and the group quantize); every
+The fused MXFP8 output of fc1 must equal, byte for byte, the oracle's MXFP8 quantization of the
+same launch's bf16 output (the fusion of the activation and the group quantize; the standalone
+quantizer on that output writes the same bytes); every
 value is compared with the oracle's own pipeline from the same seeded inputs within the FP8 bar.
 """
 
@@ -13,7 +14,8 @@ from oracle import grouped, offsets, quant
 from oracle.quant import mx_dequantize
 
 from .gpu_paths import run_grouped_mlp_fwd_mx
-from .helpers import TAU_FP8, assert_close, assert_mx_dequant_close, host_f64, host_u8
+from .helpers import (TAU_FP8, assert_close, assert_mx_dequant_close, assert_oracle_mx_rowwise, host_bits, host_f64,
+                      host_u8)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,7 +50,9 @@ def test_mxfp8_grouped_mlp_forward(case, act):
         assert np.array_equal(host_u8(got[key]["q_row"]), q), key
         assert np.array_equal(host_u8(got[key]["s_row"]), s), key
 
-    # fused activation + group quantize == standalone quantizer on the same bf16 activation
+    # fused activation + group quantize == the oracle's MXFP8 of the same launch's bf16 activation
+    assert_oracle_mx_rowwise(host_bits(got["y"]), host_u8(got["yq"]), host_u8(got["ys"]), what="y (fused MXFP8)")
+    # and == the standalone quantizer on it
     assert np.array_equal(host_u8(got["yq"]), host_u8(got["y_unfused"]["q_row"]))
     assert np.array_equal(host_u8(got["ys"]), host_u8(got["y_unfused"]["s_row"]))
 

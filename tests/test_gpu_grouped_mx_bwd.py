@@ -14,8 +14,8 @@ from oracle.quant import mx_dequantize
 
 from .gpu_paths import (grouped_dgrad_mx, grouped_wgrad_mx, mx_layout, quant_mx, quant_mx_grouped,
                         run_grouped_mlp_bwd_mx, run_grouped_mlp_fwd_mx)
-from .helpers import (TAU_FP8, assert_close, assert_mx_dequant_close, clamp_settled_h, dev, dev_bf16, host_f64,
-                      host_u8)
+from .helpers import (TAU_FP8, assert_close, assert_mx_dequant_close, assert_oracle_mx_rowwise, clamp_settled_h, dev,
+                      dev_bf16, host_bits, host_f64, host_u8)
 
 pytestmark = pytest.mark.gpu
 
@@ -136,7 +136,10 @@ def test_grouped_dgrad_mxfp8_dswiglu_fused_quantize(case):
     out = grouped_dgrad_mx(q_dy, w_col, dev(base), preact=dev_bf16(h), probs=dev(p), want_q=True)
     unfused = quant_mx(out["dact"], col=False)
     torch.cuda.synchronize()
-    # fused group quantize == the standalone quantizer on the same bf16 dact
+    # fused group quantize == the oracle's MXFP8 of the same launch's bf16 dact, and the standalone
+    # quantizer on it
+    assert_oracle_mx_rowwise(host_bits(out["dact"]), host_u8(out["dact_q"]), host_u8(out["dact_s"]),
+                             what="dact (fused MXFP8)")
     assert np.array_equal(host_u8(out["dact_q"]), host_u8(unfused["q_row"]))
     assert np.array_equal(host_u8(out["dact_s"]), host_u8(unfused["s_row"]))
     gy = grouped.grouped_linear_dgrad_mxfp8(dy, w, base)
@@ -203,9 +206,18 @@ def test_mxfp8_grouped_mlp_backward(case, act):
     rf = grouped.grouped_mlp_fwd_mxfp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base, act)
     ref = grouped.grouped_mlp_bwd_mxfp8(inp["x"], inp["w1"], inp["w2"], inp["p"], base, inp["dout"], fwd=rf,
                                         act=act)
-    # fused activation backward + group quantize == standalone quantizer on the same bf16 dh
+    # fused activation backward + group quantize == the oracle's MXFP8 of the same launch's bf16
+    # dh, and the standalone quantizer on it
+    assert_oracle_mx_rowwise(host_bits(got["dh"]), host_u8(got["dhq"]), host_u8(got["dhs"]), what="dh (fused MXFP8)")
     assert np.array_equal(host_u8(got["dhq"]), host_u8(got["dh_unfused"]["q_row"]))
     assert np.array_equal(host_u8(got["dhs"]), host_u8(got["dh_unfused"]["s_row"]))
+    # the token-blocked wgrad operands of y and dh: the oracle's blocking of the GPU's bf16 tensors
+    c, pad = quant.mx_group_layout(base, T)
+    P = int(pad[-1])
+    for key, src in (("q_y", fwd["y"]), ("q_dh", got["dh"])):
+        q, s = quant.mxfp8_colwise_grouped(host_bits(src), c, pad, got[key]["ld"])
+        assert np.array_equal(host_u8(got[key]["q_colT"])[:, :P], q[:, :P]), key
+        assert np.array_equal(host_u8(got[key]["s_colT"])[:, :P // 32], s[:, :P // 32]), key
     if isinstance(act, tuple):                             # clamps: settle the ambiguous decisions
         h_set, n_amb = clamp_settled_h(host_f64(got["dh"]), ref["dh"], ref["gy"], rf["h"], inp["p"], act)
         assert n_amb <= 1e-3 * h_set.size

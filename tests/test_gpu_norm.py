@@ -1,6 +1,7 @@
 """RMSNorm / LayerNorm on the GPU against the oracle: the bf16 output and saved statistics,
-the fused quantized outputs (byte-identical to the standalone quantizers on the same bf16
-output, and close to the oracle's quantization of its own output), and the backward."""
+the fused quantized outputs (byte-identical to the oracle's quantizers applied to the same
+launch's bf16 output and to the standalone quantizers on it, and close to the oracle's
+quantization of its own output), and the backward."""
 
 import numpy as np
 import pytest
@@ -11,7 +12,8 @@ import synth
 from oracle import norm, quant
 
 from .gpu_paths import quant_fp8, quant_mx
-from .helpers import TAU_BF16, TAU_FP8, assert_close, assert_mx_dequant_close, dev_bf16, host_f64, host_u8
+from .helpers import (TAU_BF16, TAU_FP8, assert_close, assert_mx_dequant_close, assert_oracle_mx_rowwise, dev_bf16,
+                      host_bits, host_f64, host_u8)
 
 pytestmark = pytest.mark.gpu
 
@@ -87,6 +89,18 @@ def test_norm_forward_fused_quantized_outputs(kind, shape):
     assert np.array_equal(host_u8(got["mx_row"][1]), host_u8(mxs["s_row"]))
     assert np.array_equal(host_u8(got["mx_col"][0]), host_u8(mxs["q_colT"]))
     assert np.array_equal(host_u8(got["mx_col"][1]), host_u8(mxs["s_colT"]))
+    # == the oracle's quantizers on the same launch's bf16 output (bit-exact: amax, scale,
+    # scale_inv, codes, both MXFP8 copies)
+    yb = host_bits(got["y"])
+    rf = quant.fp8_current_scaling(yb)
+    for k in ("amax", "scale", "scale_inv"):
+        g = np.float32(got["fp8"][k].item())
+        assert g.view(np.uint32) == np.float32(rf[k]).view(np.uint32), (k, g, rf[k])
+    assert np.array_equal(host_u8(got["fp8"]["q"]), rf["q"])
+    assert np.array_equal(host_u8(got["fp8"]["q_t"]), rf["q_t"])
+    assert_oracle_mx_rowwise(yb, host_u8(got["mx_row"][0]), host_u8(got["mx_row"][1]), what="norm MXFP8 row")
+    assert_oracle_mx_rowwise(np.ascontiguousarray(yb.T), host_u8(got["mx_col"][0]), host_u8(got["mx_col"][1]),
+                             what="norm MXFP8 col")
     # and close to the oracle's quantization of its own output
     ref = norm.norm_fwd_quantized(kind, d["x"], d["gamma"], d["beta"], 1e-5)
     assert_close(got["fp8"]["amax"].item(), ref["fp8"]["amax"], TAU_BF16, what="amax", rel_tight=2.0 ** -7)
