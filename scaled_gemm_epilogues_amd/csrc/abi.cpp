@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <initializer_list>
 #include <string>
 
 #include "../../include/sge.h"
@@ -93,6 +94,30 @@ sge_status check_operand(const sge_operand* o, const char* name) {
   return SGE_OK;
 }
 
+// The GEMM kernels address each operand, output and scale array through buffer resources with
+// 32-bit byte offsets, counted from a tile's first row (from a k-tile's first contraction row for
+// the transposed bf16 operands); a resource spans at most kMaxSpan bytes. A row stride is
+// accepted when 256 rows of it (plus the tile's contraction bytes) fit, and the arrays a kernel
+// addresses from one base (MXFP8 scale arrays, a gated weight's two halves) must fit whole.
+// Larger shapes are refused (SGE_ERR_SHAPE) rather than read as zeros.
+constexpr int64_t kMaxSpan = 0x7FFFFF00;
+constexpr int64_t kMaxRowBytes = (kMaxSpan - 4096) / 257;
+
+sge_status check_strides(const char* what, std::initializer_list<int64_t> row_bytes) {
+  for (int64_t b : row_bytes)
+    if (b > kMaxRowBytes)
+      return fail(SGE_ERR_SHAPE, "%s: a row stride of %lld bytes exceeds the kernels' 32-bit tile addressing (%lld)",
+                  what, (long long)b, (long long)kMaxRowBytes);
+  return SGE_OK;
+}
+
+sge_status check_span(const char* what, int64_t bytes) {
+  if (bytes > kMaxSpan)
+    return fail(SGE_ERR_SHAPE, "%s: an array of %lld bytes exceeds the kernels' 32-bit addressing (%lld)", what,
+                (long long)bytes, (long long)kMaxSpan);
+  return SGE_OK;
+}
+
 sge::GemmParams gemm_params(const sge_operand& a, const sge_operand& b, void* c, int64_t ldc, float alpha,
                             int accumulate) {
   sge::GemmParams p;
@@ -133,6 +158,11 @@ sge_status check_gemm(const sge_operand* a, const sge_operand* b, const void* c,
   if (b->outer % 8) return fail(SGE_ERR_SHAPE, "%s: output columns %lld not a multiple of 8", what,
                                 (long long)b->outer);
   if (ldc < b->outer) return fail(SGE_ERR_SHAPE, "%s: output ld too small", what);
+  if ((s = check_strides(what, {a->ld * elem_size(a->format), b->ld * elem_size(b->format), ldc * 2})) != SGE_OK)
+    return s;
+  if (a->format == SGE_FMT_MXFP8 &&
+      ((s = check_span(what, a->outer * a->mx_ld)) != SGE_OK || (s = check_span(what, b->outer * b->mx_ld)) != SGE_OK))
+    return s;
   if (c && (!aligned16(c) || (ldc * 2) % 16)) return fail(SGE_ERR_ALIGN, "%s: output not 16-byte aligned", what);
   const int64_t tiles = ((a->outer + 255) / 256) * ((b->outer + 255) / 256);
   if (tiles > 0x7FFFFFFF) return fail(SGE_ERR_SHAPE, "%s: too many tiles", what);
@@ -341,6 +371,9 @@ sge_status sge_grouped_linear_fwd(const void* x, const void* w, int32_t G, int64
   if (K % 8 || N % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd: N and K must be multiples of 8");
   if (gated_fwd(epilogue) && N % 256)
     return fail(SGE_ERR_SHAPE, "grouped_linear_fwd: SwiGLU needs N %% 256 == 0");
+  if (sge_status st = check_strides("grouped_linear_fwd", {K * 2, N * 2})) return st;
+  if (gated_fwd(epilogue))
+    if (sge_status st = check_span("grouped_linear_fwd", (N / 2 + 256) * K * 2)) return st;
   if (!aligned16(x) || !aligned16(w) || !aligned16(out) || (preact && !aligned16(preact)))
     return fail(SGE_ERR_ALIGN, "grouped_linear_fwd: pointers must be 16-byte aligned");
   const int64_t out_cols = gated_fwd(epilogue) ? N / 2 : N;
@@ -393,6 +426,11 @@ sge_status sge_grouped_linear_fwd_mxfp8(const void* x_q, const void* x_s, const 
   if (K % 128) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_mxfp8: K must be a multiple of 128 (got %lld)", (long long)K);
   if (N % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_mxfp8: N must be a multiple of 8");
   if (swiglu && N % 256) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_mxfp8: SwiGLU needs N %% 256 == 0");
+  if (sge_status st = check_strides("grouped_linear_fwd_mxfp8", {K, N * 2})) return st;
+  if (swiglu)
+    if (sge_status st = check_span("grouped_linear_fwd_mxfp8", (N / 2 + 256) * K)) return st;
+  if (sge_status st = check_span("grouped_linear_fwd_mxfp8", T * (K / 32))) return st;
+  if (sge_status st = check_span("grouped_linear_fwd_mxfp8", (int64_t)G * N * (K / 32))) return st;
   if (!aligned16(x_q) || !aligned16(x_s) || !aligned16(w_q) || !aligned16(w_s) || (out && !aligned16(out)) ||
       (preact && !aligned16(preact)) || (out_q && !aligned16(out_q)))
     return fail(SGE_ERR_ALIGN, "grouped_linear_fwd_mxfp8: pointers must be 16-byte aligned");
@@ -467,6 +505,7 @@ sge_status sge_grouped_linear_bwd(const void* dy, const void* x, const void* w, 
   if (swiglu && (!preact || !probs || !dact || !dprobs))
     return fail(SGE_ERR_NULL, "grouped_linear_bwd: the activation backward needs preact, probs, dact and dprobs");
   if (K % 8 || N % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_bwd: N and K must be multiples of 8");
+  if (sge_status st = check_strides("grouped_linear_bwd", {N * 2, K * 2, hw * 2})) return st;
   if (!aligned16(dy) || (x && !aligned16(x)) || !aligned16(w) || (dx && !aligned16(dx)) || (dw && !aligned16(dw)) ||
       (preact && !aligned16(preact)) || (dact && !aligned16(dact)))
     return fail(SGE_ERR_ALIGN, "grouped_linear_bwd: pointers must be 16-byte aligned");
@@ -615,6 +654,9 @@ sge_status sge_grouped_linear_dgrad_mxfp8(const void* dy_q, const void* dy_s, co
   if (N % 128) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_mxfp8: N must be a multiple of 128 (got %lld)", (long long)N);
   if (K % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_mxfp8: K must be a multiple of 8");
   if (swiglu && K % 32) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_mxfp8: an activation backward needs K %% 32 == 0");
+  if (sge_status st = check_strides("grouped_linear_dgrad_mxfp8", {N, (int64_t)G * N, hw * 2})) return st;
+  if (sge_status st = check_span("grouped_linear_dgrad_mxfp8", T * (N / 32))) return st;
+  if (sge_status st = check_span("grouped_linear_dgrad_mxfp8", K * ((int64_t)G * N / 32))) return st;
   if (!aligned16(dy_q) || !aligned16(dy_s) || !aligned16(w_q) || !aligned16(w_s) || (dx && !aligned16(dx)) ||
       (preact && !aligned16(preact)) || (dact && !aligned16(dact)) || (dact_q && !aligned16(dact_q)))
     return fail(SGE_ERR_ALIGN, "grouped_linear_dgrad_mxfp8: pointers must be 16-byte aligned");
@@ -689,6 +731,8 @@ sge_status sge_grouped_linear_wgrad_mxfp8(const void* dyT_q, const void* dyT_s, 
   if (!dyT_q || !dyT_s || !xT_q || !xT_s || !layout || !dw) return fail(SGE_ERR_NULL, "grouped_linear_wgrad_mxfp8: NULL pointer");
   if (ld % SGE_MX_TOKEN_ALIGN) return fail(SGE_ERR_SHAPE, "grouped_linear_wgrad_mxfp8: ld must be a multiple of %d", SGE_MX_TOKEN_ALIGN);
   if (K % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_wgrad_mxfp8: K must be a multiple of 8");
+  if (sge_status st = check_strides("grouped_linear_wgrad_mxfp8", {ld, K * 2})) return st;
+  if (sge_status st = check_span("grouped_linear_wgrad_mxfp8", (N > K ? N : K) * (ld / 32))) return st;
   if (!aligned16(dyT_q) || !aligned16(dyT_s) || !aligned16(xT_q) || !aligned16(xT_s) || !aligned16(dw))
     return fail(SGE_ERR_ALIGN, "grouped_linear_wgrad_mxfp8: pointers must be 16-byte aligned");
   const Range rdw = range_of(dw, (int64_t)G * N, K, K, 2);
@@ -788,6 +832,9 @@ sge_status sge_grouped_linear_fwd_fp8(const void* x_q, const float* x_sinv, cons
   if (K % 16) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_fp8: K must be a multiple of 16");
   if (N % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_fp8: N must be a multiple of 8");
   if (swiglu && N % 256) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_fp8: SwiGLU needs N %% 256 == 0");
+  if (sge_status st = check_strides("grouped_linear_fwd_fp8", {K, N * 2})) return st;
+  if (swiglu)
+    if (sge_status st = check_span("grouped_linear_fwd_fp8", (N / 2 + 256) * K)) return st;
   if (!aligned16(x_q) || !aligned16(w_q) || !aligned16(out) || (preact && !aligned16(preact)))
     return fail(SGE_ERR_ALIGN, "grouped_linear_fwd_fp8: pointers must be 16-byte aligned");
   const int64_t out_cols = swiglu ? N / 2 : N;
@@ -851,6 +898,7 @@ sge_status sge_grouped_linear_dgrad_fp8(const void* dy_q, const float* dy_sinv, 
   if (dact_amax && !swiglu) return fail(SGE_ERR_ARG, "grouped_linear_dgrad_fp8: dact_amax needs an activation backward");
   if (N % 16) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_fp8: N must be a multiple of 16");
   if (K % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_fp8: K must be a multiple of 8");
+  if (sge_status st = check_strides("grouped_linear_dgrad_fp8", {N, (int64_t)G * N, hw * 2})) return st;
   if (!aligned16(dy_q) || !aligned16(w_qT) || (dx && !aligned16(dx)) || (preact && !aligned16(preact)) ||
       (dact && !aligned16(dact)))
     return fail(SGE_ERR_ALIGN, "grouped_linear_dgrad_fp8: pointers must be 16-byte aligned");
@@ -917,6 +965,7 @@ sge_status sge_grouped_linear_wgrad_fp8(const void* dyT_q, const float* dy_sinv,
   if (!dyT_q || !dy_sinv || !xT_q || !x_sinv || !layout || !dw) return fail(SGE_ERR_NULL, "grouped_linear_wgrad_fp8: NULL pointer");
   if (ld % SGE_MX_TOKEN_ALIGN) return fail(SGE_ERR_SHAPE, "grouped_linear_wgrad_fp8: ld must be a multiple of %d", SGE_MX_TOKEN_ALIGN);
   if (K % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_wgrad_fp8: K must be a multiple of 8");
+  if (sge_status st = check_strides("grouped_linear_wgrad_fp8", {ld, K * 2})) return st;
   if (!aligned16(dyT_q) || !aligned16(xT_q) || !aligned16(dw))
     return fail(SGE_ERR_ALIGN, "grouped_linear_wgrad_fp8: pointers must be 16-byte aligned");
   const Range rdw = range_of(dw, (int64_t)G * N, K, K, 2);
@@ -1099,6 +1148,10 @@ static sge_status check_mlp(const char* what, int32_t G, int64_t T, int64_t H, i
       return fail(SGE_ERR_NULL, "%s: a required pointer is NULL (W1, W2, offsets, or a T-sized tensor)", what);
   if (H % 8 || F % 8) return fail(SGE_ERR_SHAPE, "%s: H and F must be multiples of 8", what);
   if (gated_fwd(activation) && F % 128) return fail(SGE_ERR_SHAPE, "%s: a gated activation needs F %% 128 == 0", what);
+  const int64_t N1 = gated_fwd(activation) ? 2 * F : F;
+  if (sge_status st = check_strides(what, {H * 2, N1 * 2})) return st;
+  if (gated_fwd(activation))
+    if (sge_status st = check_span(what, (F + 256) * H * 2)) return st;
   for (int i = 0; i < n_in + n_out; ++i) {
     const Arg& a = i < n_in ? ins[i] : outs[i - n_in];
     if (a.r.lo % a.align) return fail(SGE_ERR_ALIGN, "%s: argument not %u-byte aligned", what, a.align);

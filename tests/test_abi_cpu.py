@@ -500,3 +500,32 @@ def test_grouped_mlp_validation(sge):
     assert b(*a) == sge.ERR_ALIAS                                         # workspace over x
     a = list(okb); a[16] = B(30000)
     assert b(*a) == sge.ERR_ALIAS                                         # dx over dpreact
+
+
+def test_shapes_beyond_32bit_tile_addressing_are_refused(sge):
+    """Row strides whose 256-row tile span (or arrays addressed whole, such as MXFP8 scales and a
+    gated weight's two halves) would not fit the kernels' 32-bit buffer offsets give
+    SGE_ERR_SHAPE instead of reading zeros."""
+    big = 1 << 23                                         # bf16 elements: 16 MiB per row
+    st, msg = _fwd(sge, _op(sge, 64, 128, ld=big), _op(sge, 64, 128, data=FAKE * 2))
+    assert st == sge.ERR_SHAPE and "32-bit" in msg, msg
+    st, msg = _fwd(sge, _op(sge, 64, 128), _op(sge, 64, 128, data=FAKE * 2), ld_res=big)
+    assert st == sge.ERR_SHAPE and "32-bit" in msg, msg
+    # an MXFP8 scale array of 2^31 bytes (rows x mx_ld)
+    st, msg = _fwd(sge, _op(sge, 1 << 21, 128, fmt=2, mx=FAKE, mx_ld=1 << 10),
+                   _op(sge, 64, 128, fmt=2, data=FAKE * 2, mx=FAKE, mx_ld=4))
+    assert st == sge.ERR_SHAPE and "32-bit" in msg, msg
+    # one stride below the limit passes the check (and then fails later on the fake aliasing)
+    st, msg = _fwd(sge, _op(sge, 64, 128, ld=1 << 21), _op(sge, 64, 128, data=FAKE * 2))
+    assert "32-bit" not in msg, msg
+    lib = sge._lib
+    fwd = _act_after(lib.sge_grouped_linear_fwd, 8)
+    # grouped: a contraction of 2^23 bf16 per row
+    st = fwd(FAKE, FAKE * 64, 8, 100, 256, big, FAKE * 1024, 1.0, 0, None, FAKE * 8192, None, None)
+    assert st == sge.ERR_SHAPE and "32-bit" in lib.sge_last_error_message().decode()
+    # gated fc1: both halves of one expert's weight are addressed from one base (2^31 bytes here)
+    st = fwd(FAKE, FAKE * 64, 8, 100, 1 << 20, 2048, FAKE * 1024, 1.0, 1, FAKE * 4096, FAKE * 8192, None, None)
+    assert st == sge.ERR_SHAPE and "32-bit" in lib.sge_last_error_message().decode()
+    # the same weight without the gate is only addressed tile by tile
+    st = fwd(FAKE, FAKE * 64, 8, 100, 1 << 20, 2048, FAKE * 1024, 1.0, 0, None, FAKE * 8192, None, None)
+    assert "32-bit" not in lib.sge_last_error_message().decode()
