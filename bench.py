@@ -10,7 +10,10 @@ inputs already resident in HBM:
   of both layers.
 
 Prints ONE JSON line on stdout. The default workload is the bf16 forward +
-backward at M = N = K = 4096 (alpha 0.125). Before the ``--warmup`` steps the
+backward at M = N = K = 4096 (alpha 0.125); the FP8 (8192 x 14336 x 4096), MXFP8
+(16384 x 8192 x 8192) and grouped SwiGLU MLP (65,536 tokens, 8 experts) workloads
+are timed the same way in the same run and reported under ``configs``, each
+with its own oracle sample. Before the ``--warmup`` steps the
 step runs untimed for ``--ramp-seconds`` (the GPU raises its clocks over the
 first ~100 ms of load). The timed region is ``--steps``
 eager steps between HIP events; ``ms_per_step_graph`` replays the same step
@@ -38,6 +41,10 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0}
 PEAK_HBM_GBS = 8000.0
 METRIC = "scaled-linear fwd+bwd TFLOP/s & % of MFMA peak (bf16/FP8/MXFP8), 1 MI355X"
 DEFAULT_WORKLOAD = "bf16_fwdbwd_4096"
+# timed in the same run as the default workload: the FP8 and MXFP8 dense configurations the metric
+# names, and the grouped MLP
+DEFAULT_CONFIGS = ("fp8_tensor_fwdbwd_8192x14336x4096", "mxfp8_fwdbwd_16384x8192x8192",
+                   "grouped_swiglu_mlp_T65536_G8")
 
 
 def parse():
@@ -48,8 +55,14 @@ def parse():
     ap.add_argument("--ramp-seconds", type=float, default=0.3,
                     help="untimed steps run for this long before the warm-up steps (the GPU's clock ramp)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--configs", default="auto",
+                    help="comma-separated workloads timed in the same run after --workload and reported under "
+                         "'configs' (auto: the FP8, MXFP8 and grouped workloads when --workload is the default; "
+                         "none: no others)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds-configs", type=float, default=4.0,
+                    help="target CPU time of the oracle sample of each of the other --configs workloads")
     # measurement helpers (rocprofv3 targets and summaries); none of them prints the bench line
     ap.add_argument("--profile-launch", metavar="KEY",
                     help="one warm-up step, then --profile-reps launches of this call only (a --pmc target)")
@@ -383,11 +396,11 @@ def build_grouped_fp8(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, 
 def cpu_baseline(wl, inp, target_s):
     """The oracle, as it stands, on a bounded sample of the same workload (rows of the token dim)."""
     import numpy as np
-    try:
+    try:                                                       # the threads the BLAS pool runs with
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:                                          # pragma: no cover
-        cores = os.cpu_count() or 1
+        cores = cpu_threads()
     from oracle import grouped, linear, norm, offsets
     from oracle.codecs import bf16_to_f64, f64_to_bf16
 
@@ -694,6 +707,142 @@ def summarize_trace(trace_dir, bench_json, out_md, command):
         fh.write("\n".join(L) + "\n")
 
 
+def host_info():
+    """Host CPUs visible to this process, their model and the BLAS library numpy calls."""
+    info = {"host_cpus": len(os.sched_getaffinity(0)), "cpu_model": None, "blas": None}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:                                            # pragma: no cover
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+    except Exception:                                          # pragma: no cover
+        pass
+    return info
+
+
+def cpu_threads():
+    """Threads the oracle's BLAS runs with: every CPU this process may use, capped by
+    OMP_NUM_THREADS when the host sets it (the share of the machine this job holds)."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return n
+
+
+def ramp(torch, step, seconds):
+    """Untimed steps for ``seconds`` (the GPU raises its clocks over ~100 ms of load)."""
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+
+
+def measure(torch, sge, synth, args, name, cpu_seconds):
+    """Times one workload: ``args.steps`` eager steps after the clock ramp and ``args.warmup``
+    steps, per-kernel graph timings, cold HBM-bound launches, the roofline of the kernel with the
+    largest share of the step, and (cpu_seconds > 0) the oracle on a bounded sample of it."""
+    wl = synth.WORKLOADS[name]
+    inp = synth.workload_inputs(name, seed=0)
+    builder = build_dense if wl["kind"] == "dense" else build_grouped
+    launches, flops, hbm = builder(torch, sge, wl, inp)
+    step_flops = sum(flops.values())
+
+    def eager_step():
+        for _, f in launches:
+            f()
+
+    # Clock ramp: under sustained load MI355X raises its clocks over the first ~50-100 ms (the
+    # 4096^3 bf16 step falls from 0.50 to 0.33 ms over its first ~150 steps, and is back near
+    # 0.40 ms after 2 s idle), so the step runs untimed for ramp_seconds before the `warmup`
+    # steps, and the timed steps measure the steady state a training loop runs at.
+    ramp(torch, eager_step, args.ramp_seconds)
+    for _ in range(args.warmup):
+        eager_step()
+    torch.cuda.synchronize()
+    # The timed region: exactly `steps` eager steps between HIP events, synchronized on both sides.
+    ms_per_step = time_ms(torch, eager_step, args.steps)
+    # The same step as one HIP graph (reported for comparison; not the timed value), and per
+    # kernel a graph of `reps` back-to-back launches of one call. Capturing leaves the GPU idle
+    # for milliseconds, long enough for its clocks to drop, so every graph is captured first,
+    # the step runs untimed again for half the ramp time, and only then are the graphs timed
+    # with HIP events around their replays (on the replay stream the events mark).
+    reps = 8
+    step_graph = capture(torch, [f for _, f in launches])
+    graphs = {k: capture(torch, [f] * reps) for k, f in launches}
+    ramp(torch, eager_step, args.ramp_seconds / 2)
+    ms_graph = time_ms(torch, step_graph.replay, max(1, min(args.steps, 10)))
+    per = {}
+    for k, g in graphs.items():
+        g.replay()
+        per[k] = time_ms(torch, g.replay, 3) / reps
+    del step_graph, graphs
+    # HBM-bound launches (quantizers, norms) are timed cold as well: before each timed launch a
+    # 512 MiB write evicts the 256 MB Infinity Cache, so their inputs come from HBM; the median
+    # of 10 such launches is their duration (the in-step figure is kept as ms_warm).
+    cold = {}
+    if any(k in hbm for k in per):
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for k, f in launches:
+            if k not in hbm:
+                continue
+            ts = []
+            for _ in range(10):
+                flush.zero_()
+                ev[0].record()
+                f()
+                ev[1].record()
+                torch.cuda.synchronize()
+                ts.append(ev[0].elapsed_time(ev[1]))
+            cold[k] = sorted(ts)[len(ts) // 2]
+        del flush
+
+    fmt = wl["fmt"]
+    peak = PEAK_TFLOPS[fmt]
+    kernels = {}
+    for k, ms in per.items():
+        if k in flops:
+            kernels[k] = {"ms": round(ms, 4), "tflops": round(flops[k] / ms / 1e9, 1),
+                          "frac_peak": round(flops[k] / ms / 1e9 / peak, 4)}
+        elif k in hbm:
+            c = cold[k]
+            kernels[k] = {"ms": round(c, 4), "gbs": round(hbm[k] / c / 1e6, 1),
+                          "frac_hbm": round(hbm[k] / c / 1e6 / PEAK_HBM_GBS, 4), "ms_warm": round(ms, 4)}
+        else:
+            kernels[k] = {"ms": round(ms, 4)}
+    dom = max((k for k in per if k in flops), key=lambda k: per[k])
+    achieved = flops[dom] / per[dom] / 1e9
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic_for(f"{name}:{dom}"),
+                "kernel": dom, "flops_per_launch": flops[dom], "avg_launch_ms": round(per[dom], 4)}
+    gemm_ms = sum(per[k] for k in per if k in flops)
+    value = step_flops / (ms_per_step * 1e9)
+    cfg = {"workload": name}
+    cfg.update({k: wl[k] for k in ("M", "N", "K", "T", "G", "hidden", "ffn", "alpha") if k in wl})
+    res = {"value": round(value, 2), "unit": "TFLOP/s", "ms_per_step": round(ms_per_step, 4),
+           "ms_per_step_graph": round(ms_graph, 4), "dtype": fmt, "config": cfg,
+           "frac_of_peak": round(value / peak, 4),
+           "gemm_tflops": round(step_flops / (gemm_ms * 1e9), 1),
+           "gemm_frac_of_peak": round(step_flops / (gemm_ms * 1e9) / peak, 4),
+           "kernels": kernels, "roofline": roofline}
+    del launches
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(wl, inp, cpu_seconds)
+    return res
+
+
 def main():
     args = parse()
     if args.summarize_traffic:
@@ -717,120 +866,70 @@ def main():
     import scaled_gemm_epilogues_amd as sge
     import synth
 
-    wl = synth.WORKLOADS[args.workload]
-    inp = synth.workload_inputs(args.workload, seed=0)
-    builder = build_dense if wl["kind"] == "dense" else build_grouped
-    launches, flops, hbm = builder(torch, sge, wl, inp)
-    step_flops = sum(flops.values())
-
-    def eager_step():
-        for _, f in launches:
-            f()
-
     if args.profile_launch:
+        wl = synth.WORKLOADS[args.workload]
+        inp = synth.workload_inputs(args.workload, seed=0)
+        builder = build_dense if wl["kind"] == "dense" else build_grouped
+        launches, _, _ = builder(torch, sge, wl, inp)
         fns = dict(launches)
         if args.profile_launch not in fns:
             print(f"unknown launch {args.profile_launch}; this workload has {list(fns)}", file=sys.stderr)
             return 2
+
+        def eager_step():
+            for _, f in launches:
+                f()
+
         eager_step()
         torch.cuda.synchronize()
-        t_end = time.perf_counter() + args.ramp_seconds      # the clock ramp, as for the timed steps
-        while time.perf_counter() < t_end:
-            for _ in range(8):
-                eager_step()
-            torch.cuda.synchronize()
+        ramp(torch, eager_step, args.ramp_seconds)             # the clock ramp, as for the timed steps
         for _ in range(args.profile_reps):
             fns[args.profile_launch]()
         torch.cuda.synchronize()
         print(json.dumps({"profile_launch": args.profile_launch, PROFILE_REPS_KEY: args.profile_reps}), flush=True)
         return 0
 
-    # Clock ramp: under sustained load MI355X raises its clocks over the first ~50-100 ms (the
-    # 4096^3 bf16 step falls from 0.50 to 0.33 ms over its first ~150 steps, and is back near
-    # 0.40 ms after 2 s idle), so the step runs untimed for ramp_seconds before the `warmup`
-    # steps, and the timed steps measure the steady state a training loop runs at.
-    t_end = time.perf_counter() + args.ramp_seconds
-    while time.perf_counter() < t_end:
-        for _ in range(8):
-            eager_step()
-        torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        eager_step()
-    torch.cuda.synchronize()
-    # The timed region: exactly `steps` eager steps between HIP events, synchronized on both sides.
-    ms_per_step = time_ms(torch, eager_step, args.steps)
-    # The same step as one HIP graph (reported for comparison; not the timed value), and per
-    # kernel a graph of `reps` back-to-back launches of one call. Capturing leaves the GPU idle
-    # for milliseconds, long enough for its clocks to drop, so every graph is captured first,
-    # the step runs untimed again for half the ramp time, and only then are the graphs timed
-    # with HIP events around their replays (on the replay stream the events mark).
-    reps = 8
-    step_graph = capture(torch, [f for _, f in launches])
-    graphs = {name: capture(torch, [f] * reps) for name, f in launches}
-    t_end = time.perf_counter() + args.ramp_seconds / 2
-    while time.perf_counter() < t_end:
-        for _ in range(8):
-            eager_step()
-        torch.cuda.synchronize()
-    ms_graph = time_ms(torch, step_graph.replay, max(1, min(args.steps, 10)))
-    per = {}
-    for name, g in graphs.items():
-        g.replay()
-        per[name] = time_ms(torch, g.replay, 3) / reps
-    del step_graph, graphs
-    # HBM-bound launches (quantizers, norms) are timed cold as well: before each timed launch a
-    # 512 MiB write evicts the 256 MB Infinity Cache, so their inputs come from HBM; the median
-    # of 10 such launches is their duration (the in-step figure is kept as ms_warm).
-    cold = {}
-    if any(k in hbm for k in per):
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        for name, f in launches:
-            if name not in hbm:
-                continue
-            ts = []
-            for _ in range(10):
-                flush.zero_()
-                ev[0].record()
-                f()
-                ev[1].record()
-                torch.cuda.synchronize()
-                ts.append(ev[0].elapsed_time(ev[1]))
-            cold[name] = sorted(ts)[len(ts) // 2]
-        del flush
+    if args.configs == "auto":
+        extra = list(DEFAULT_CONFIGS) if args.workload == DEFAULT_WORKLOAD else []
+    elif args.configs in ("", "none"):
+        extra = []
+    else:
+        extra = [c for c in args.configs.split(",") if c and c != args.workload]
+    for c in [args.workload] + extra:
+        if c not in synth.WORKLOADS:
+            print(f"unknown workload {c}", file=sys.stderr)
+            return 2
+    want_cpu = not args.no_cpu_baseline
+    if want_cpu:
+        # the oracle's BLAS threads, fixed before its first call
+        try:
+            from threadpoolctl import threadpool_limits
+            threadpool_limits(limits=cpu_threads(), user_api="blas")
+        except Exception:                                      # pragma: no cover
+            pass
+    head = measure(torch, sge, synth, args, args.workload, args.cpu_seconds if want_cpu else 0)
+    print(f"# {args.workload}: {head['value']} TFLOP/s, {head['ms_per_step']} ms/step", file=sys.stderr, flush=True)
+    configs = {}
+    for c in extra:
+        r = measure(torch, sge, synth, args, c, args.cpu_seconds_configs if want_cpu else 0)
+        configs[c] = r
+        print(f"# {c}: {r['value']} TFLOP/s, {r['ms_per_step']} ms/step", file=sys.stderr, flush=True)
 
-    fmt = wl["fmt"]
-    peak = PEAK_TFLOPS[fmt]
-    kernels = {}
-    for k, ms in per.items():
-        if k in flops:
-            kernels[k] = {"ms": round(ms, 4), "tflops": round(flops[k] / ms / 1e9, 1),
-                          "frac_peak": round(flops[k] / ms / 1e9 / peak, 4)}
-        elif k in hbm:
-            c = cold[k]
-            kernels[k] = {"ms": round(c, 4), "gbs": round(hbm[k] / c / 1e6, 1),
-                          "frac_hbm": round(hbm[k] / c / 1e6 / PEAK_HBM_GBS, 4), "ms_warm": round(ms, 4)}
-        else:
-            kernels[k] = {"ms": round(ms, 4)}
-    dom = max((k for k in per if k in flops), key=lambda k: per[k])
-    achieved = flops[dom] / per[dom] / 1e9
-    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": traffic_for(f"{args.workload}:{dom}"),
-                "kernel": dom, "flops_per_launch": flops[dom], "avg_launch_ms": round(per[dom], 4)}
-
-    value = step_flops / (ms_per_step * 1e9)
-    cfg = {"workload": args.workload}
-    cfg.update({k: wl[k] for k in ("M", "N", "K", "T", "G", "hidden", "ffn", "alpha") if k in wl})
     line = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "warmup_ramp_s": args.ramp_seconds, "ms_per_step": round(ms_per_step, 4),
-        "ms_per_step_graph": round(ms_graph, 4),
+        "metric": METRIC, "value": head["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "warmup_ramp_s": args.ramp_seconds, "ms_per_step": head["ms_per_step"],
+        "ms_per_step_graph": head["ms_per_step_graph"],
         "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": fmt, "data": "synthetic (seeded; see synth/)",
-        "config": cfg, "frac_of_peak": round(value / peak, 4), "kernels": kernels, "roofline": roofline,
+        "scaling": "weak", "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic (seeded; see synth/)",
+        "config": head["config"], "frac_of_peak": head["frac_of_peak"], "gemm_tflops": head["gemm_tflops"],
+        "gemm_frac_of_peak": head["gemm_frac_of_peak"], "kernels": head["kernels"], "roofline": head["roofline"],
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+    if "cpu_baseline" in head:
+        line["cpu_baseline"] = head["cpu_baseline"]
+    if configs:
+        line["configs"] = configs
+    if want_cpu:
+        line["host"] = host_info()
     print(json.dumps(line), flush=True)
     return 0
 
