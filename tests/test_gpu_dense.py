@@ -136,7 +136,7 @@ def test_outputs_respect_leading_dimension():
     assert_close(host_f64(view), ref, TAU_BF16, what="ld view")
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp8"])
 def test_bitwise_repeatable(fmt):
     d = synth.dense(512, 512, 256, seed=9)
     a = run_dense(fmt, d, 0.5)
