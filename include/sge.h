@@ -183,6 +183,21 @@ sge_status sge_quantize_fp8_amax(const void* src, int64_t rows, int64_t cols, ui
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * sge_quantize_fp8_amax without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * The amax partials go to a scratch array the library holds on each GPU (4 KiB, the most
+ * partials the amax pass writes for any tensor size; a size needing more would be refused with
+ * SGE_ERR_WORKSPACE). The call allocates nothing. Every call on a GPU shares that GPU's array:
+ * calls that overlap on one GPU (concurrent streams, or host threads) race on it and must be
+ * serialized by the caller. Each amax pass writes every partial it later reads, so nothing
+ * carries over from an earlier call. Arguments, results and errors are those of
+ * sge_quantize_fp8_amax; SGE_ERR_HIP if the array's device address cannot be obtained.
+ */
+sge_status sge_quantize_fp8_amax_noalloc(const void* src, int64_t rows, int64_t cols, uint8_t* q,
+                                         uint8_t* q_t, float* amax, float* scale, float* scale_inv,
+                                         hipStream_t stream);
+
+/*
  * MXFP8 quantization of a bf16 matrix [rows, cols], rowwise and/or columnwise.
  * (MXFP8 operands: "core.tensor_parallel.inference_layers", _apply_linear with an
  * MXFP8Tensor; the shared exponent follows OCP MX v1.0 section 6.3.)

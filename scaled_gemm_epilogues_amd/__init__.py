@@ -34,7 +34,8 @@ NORM_RMS, NORM_LAYER = 0, 1
 EXPORTED = (
     "sge_abi_version", "sge_status_string", "sge_last_error_message",
     "sge_linear_scale_add_fwd", "sge_linear_scale_bwd",
-    "sge_quantize_fp8_amax_workspace_size", "sge_quantize_fp8_amax", "sge_quantize_mxfp8",
+    "sge_quantize_fp8_amax_workspace_size", "sge_quantize_fp8_amax", "sge_quantize_fp8_amax_noalloc",
+    "sge_quantize_mxfp8",
     "sge_splits_to_offsets", "sge_grouped_linear_fwd", "sge_grouped_linear_fwd_mxfp8",
     "sge_grouped_linear_bwd_workspace_size", "sge_grouped_linear_bwd",
     "sge_scaled_swiglu_fwd", "sge_scaled_swiglu_bwd",
@@ -85,6 +86,7 @@ _SIGS = {
     "sge_linear_scale_bwd": ([_OP, _OP, _OP, _OP, _vp, _i64, _vp, _i64, _f32, _f32, _vp], ctypes.c_int),
     "sge_quantize_fp8_amax_workspace_size": ([_i64, _i64], _sz),
     "sge_quantize_fp8_amax": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "sge_quantize_fp8_amax_noalloc": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "sge_quantize_mxfp8": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "sge_splits_to_offsets": ([_vp, _i32, ctypes.POINTER(_i64), _i32, _i64, _vp, _vp, _vp], ctypes.c_int),
     "sge_grouped_linear_fwd": ([_vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _ACT, _vp, _vp, _vp, _vp],
@@ -218,6 +220,14 @@ def quantize_fp8_amax(src, q, q_t, amax, scale, scale_inv, workspace, stream=Non
     _check(_lib.sge_quantize_fp8_amax(_ptr(src), rows, cols, _ptr(q), _ptr(q_t), _ptr(amax), _ptr(scale),
                                       _ptr(scale_inv), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def quantize_fp8_amax_noalloc(src, q, q_t, amax, scale, scale_inv, stream=None):
+    """``quantize_fp8_amax`` with the amax partials in the library's per-GPU scratch array (no
+    workspace; calls overlapping on one GPU race on that array)."""
+    rows, cols = src.shape
+    _check(_lib.sge_quantize_fp8_amax_noalloc(_ptr(src), rows, cols, _ptr(q), _ptr(q_t), _ptr(amax), _ptr(scale),
+                                              _ptr(scale_inv), _stream(stream)))
 
 
 def quantize_mxfp8(src, q_row=None, s_row=None, q_colT=None, s_colT=None, stream=None):

@@ -302,21 +302,32 @@ size_t sge_quantize_fp8_amax_workspace_size(int64_t rows, int64_t cols) {
   return (size_t)sge::amax_partial_blocks(rows * cols) * sizeof(uint32_t);
 }
 
-sge_status sge_quantize_fp8_amax(const void* src, int64_t rows, int64_t cols, uint8_t* q, uint8_t* q_t, float* amax,
-                                 float* scale, float* scale_inv, void* workspace, size_t workspace_bytes,
-                                 hipStream_t stream) {
-  if (rows < 0 || cols < 0) return fail(SGE_ERR_SHAPE, "quantize_fp8_amax: negative size");
-  if ((rows * cols > 0 && !src) || !amax || !scale || !scale_inv || !workspace)
-    return fail(SGE_ERR_NULL, "quantize_fp8_amax: NULL pointer");
-  if (rows % 16 || cols % 16) return fail(SGE_ERR_SHAPE, "quantize_fp8_amax: rows and cols must be multiples of 16");
+// Validation (NULL, shape, alignment, alias), then the two launches; the partials go to
+// `workspace`, or, with workspace == NULL, to this GPU's scratch array.
+static sge_status quantize_fp8_amax_impl(const char* what, const void* src, int64_t rows, int64_t cols, uint8_t* q,
+                                         uint8_t* q_t, float* amax, float* scale, float* scale_inv, void* workspace,
+                                         size_t workspace_bytes, bool scratch, hipStream_t stream) {
+  if (rows < 0 || cols < 0) return fail(SGE_ERR_SHAPE, "%s: negative size", what);
+  if ((rows * cols > 0 && !src) || !amax || !scale || !scale_inv || (!scratch && !workspace))
+    return fail(SGE_ERR_NULL, "%s: NULL pointer", what);
+  if (rows % 16 || cols % 16) return fail(SGE_ERR_SHAPE, "%s: rows and cols must be multiples of 16", what);
   if (!aligned16(src) || (q && !aligned16(q)) || (q_t && !aligned16(q_t)))
-    return fail(SGE_ERR_ALIGN, "quantize_fp8_amax: pointers must be 16-byte aligned");
+    return fail(SGE_ERR_ALIGN, "%s: pointers must be 16-byte aligned", what);
   const Range in = range_of(src, rows, cols, cols, 2);
   if ((q && overlap(in, range_of(q, rows, cols, cols, 1))) || (q_t && overlap(in, range_of(q_t, cols, rows, rows, 1))))
-    return fail(SGE_ERR_ALIAS, "quantize_fp8_amax: output overlaps the input");
+    return fail(SGE_ERR_ALIAS, "%s: output overlaps the input", what);
   const size_t need = sge_quantize_fp8_amax_workspace_size(rows, cols);
-  if (workspace_bytes < need)
-    return fail(SGE_ERR_WORKSPACE, "quantize_fp8_amax: workspace %zu < %zu bytes", workspace_bytes, need);
+  if (scratch) {
+    uint32_t* ws = nullptr;
+    hipError_t e = sge::amax_scratch(&ws, &workspace_bytes);
+    if (e != hipSuccess) return hip_status(e, "scratch array address");
+    if (workspace_bytes < need)
+      return fail(SGE_ERR_WORKSPACE, "%s: %zu bytes of amax partials exceed the %zu-byte scratch array", what, need,
+                  workspace_bytes);
+    workspace = ws;
+  } else if (workspace_bytes < need) {
+    return fail(SGE_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", what, workspace_bytes, need);
+  }
   const int nb = sge::amax_partial_blocks(rows * cols);
   hipError_t e = sge::launch_amax_partial(static_cast<const uint16_t*>(src), rows * cols,
                                           static_cast<uint32_t*>(workspace), nb, stream);
@@ -324,6 +335,19 @@ sge_status sge_quantize_fp8_amax(const void* src, int64_t rows, int64_t cols, ui
   e = sge::launch_quantize_fp8(static_cast<const uint16_t*>(src), rows, cols, static_cast<const uint32_t*>(workspace),
                                nb, q, q_t, amax, scale, scale_inv, stream);
   return hip_status(e, "quantize launch");
+}
+
+sge_status sge_quantize_fp8_amax(const void* src, int64_t rows, int64_t cols, uint8_t* q, uint8_t* q_t, float* amax,
+                                 float* scale, float* scale_inv, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  return quantize_fp8_amax_impl("quantize_fp8_amax", src, rows, cols, q, q_t, amax, scale, scale_inv, workspace,
+                                workspace_bytes, false, stream);
+}
+
+sge_status sge_quantize_fp8_amax_noalloc(const void* src, int64_t rows, int64_t cols, uint8_t* q, uint8_t* q_t,
+                                         float* amax, float* scale, float* scale_inv, hipStream_t stream) {
+  return quantize_fp8_amax_impl("quantize_fp8_amax_noalloc", src, rows, cols, q, q_t, amax, scale, scale_inv,
+                                nullptr, 0, true, stream);
 }
 
 sge_status sge_quantize_mxfp8(const void* src, int64_t rows, int64_t cols, uint8_t* q_row, uint8_t* s_row,

@@ -72,6 +72,9 @@ hipError_t launch_fill_f32_zero(float* c, int64_t n, hipStream_t s);
 hipError_t launch_amax_partial(const uint16_t* src, int64_t n, uint32_t* partial, int nblocks,
                                hipStream_t s);
 int amax_partial_blocks(int64_t n);
+// Device address and size of this GPU's amax partial scratch array (no allocation; the address is
+// looked up once per device, with that device current).
+hipError_t amax_scratch(uint32_t** partial, size_t* bytes);
 hipError_t launch_quantize_fp8(const uint16_t* src, int64_t rows, int64_t cols, const uint32_t* partial,
                                int nparts, uint8_t* q, uint8_t* q_t, float* amax, float* scale,
                                float* scale_inv, hipStream_t s);

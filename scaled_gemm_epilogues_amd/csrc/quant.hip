@@ -12,6 +12,8 @@
 // element once and writes both the rowwise and the columnwise (transposed)
 // copy. The per-block amax is an integer max over bf16 bit patterns with the
 // sign cleared, which orders like the magnitudes.
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -74,6 +76,34 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const uint16
 int amax_partial_blocks(int64_t n) {
   const int64_t want = (n / 8 + kAmaxThreads * 8 - 1) / (kAmaxThreads * 8);
   return (int)(want < 1 ? 1 : (want > 1024 ? 1024 : want));
+}
+
+// Partials of the per-tensor amax for callers that cannot allocate (the no-allocation variant of
+// the FP8 current-scaling quantizer): one array per GPU, held until the process ends, as large as
+// the most partials amax_partial_blocks() asks for. Host code never passes the array's name to a
+// kernel (on the host it only stands for the symbol); it takes the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+constexpr int kScratchPartials = 1024;
+static __device__ __align__(256) uint32_t scratch[kScratchPartials];
+
+hipError_t amax_scratch(uint32_t** partial, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static uint32_t* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<uint32_t*>(p);
+  }
+  *partial = addr[dev];
+  *bytes = sizeof(scratch);
+  return hipSuccess;
 }
 
 hipError_t launch_amax_partial(const uint16_t* src, int64_t n, uint32_t* partial, int nblocks,

@@ -529,3 +529,13 @@ def test_shapes_beyond_32bit_tile_addressing_are_refused(sge):
     # the same weight without the gate is only addressed tile by tile
     st = fwd(FAKE, FAKE * 64, 8, 100, 1 << 20, 2048, FAKE * 1024, 1.0, 0, None, FAKE * 8192, None, None)
     assert "32-bit" not in lib.sge_last_error_message().decode()
+
+
+def test_quantize_fp8_amax_noalloc_validation_errors(sge):
+    """The no-allocation quantizer validates like the workspace call, before any HIP call."""
+    lib = sge._lib
+    f = lib.sge_quantize_fp8_amax_noalloc
+    assert f(FAKE, 60, 64, FAKE * 8, None, FAKE * 16, FAKE * 17, FAKE * 18, None) == sge.ERR_SHAPE
+    assert f(FAKE, 64, 64, FAKE * 8, None, None, FAKE * 17, FAKE * 18, None) == sge.ERR_NULL
+    assert f(FAKE + 8, 64, 64, FAKE * 8, None, FAKE * 16, FAKE * 17, FAKE * 18, None) == sge.ERR_ALIGN
+    assert f(FAKE, 64, 64, FAKE + 1024, None, FAKE * 16, FAKE * 17, FAKE * 18, None) == sge.ERR_ALIAS
