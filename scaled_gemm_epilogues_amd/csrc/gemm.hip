@@ -76,17 +76,25 @@ constexpr int kWavesM = SGE_WAVES_M, kWavesN = SGE_WAVES_N, kFragsM = SGE_FRAGS_
 #define SGE_DSWIGLU_BATCH 4      // dSwiGLU epilogue chunks whose loads are in flight together
 #endif
 
-template <int FMT>
+#ifndef SGE_DEEP_8BIT
+#define SGE_DEEP_8BIT 1          // 8-bit dense GEMMs: 64-byte k-tiles in four LDS stages
+#endif
+
+// Deep pipeline: with one wave per SIMD nothing covers a wave's wait for its tile copies, so the
+// 8-bit dense GEMMs keep three k-tiles in flight ahead of the one being multiplied (four LDS
+// stages of 64 contraction bytes, 128 KB in all) instead of one (two stages of 128 bytes).
+constexpr bool deep_pipe(int fmt, int sched) {
+  return SGE_DEEP_8BIT && (fmt == F_MX || fmt == F_E4M3) && sched == S_DENSE;
+}
+
+// Waves and fragments of a tile: MXFP8 (more live registers for the E8M0 scales) and the
+// deep-pipelined 8-bit tiles take 2x2 waves of 4x4 accumulators (one wave per SIMD; a third
+// fewer LDS fragment bytes per MFMA); the rest 2x4 waves of 4x2.
+template <int FMT, int SCHED>
 struct TileShape {
-  static constexpr int WGM = kWavesM, WGN = kWavesN, WMF = kFragsM, WNF = kFragsN;
-};
-template <>
-struct TileShape<2> {
-  static constexpr int WGM = 2, WGN = 2, WMF = 4, WNF = 4;
-};
-template <>
-struct TileShape<3> {
-  static constexpr int WGM = 2, WGN = 2, WMF = 4, WNF = 4;
+  static constexpr bool k4 = FMT == F_MX || FMT == F_MXU || deep_pipe(FMT, SCHED);
+  static constexpr int WGM = k4 ? 2 : kWavesM, WGN = k4 ? 2 : kWavesN;
+  static constexpr int WMF = k4 ? 4 : kFragsM, WNF = k4 ? 4 : kFragsN;
 };
 
 // The dispatcher hands workgroups to the 8 XCDs round-robin (workgroup b runs on XCD b % 8),
@@ -153,6 +161,15 @@ __device__ __forceinline__ void lds_copy16(const i32x4& rsrc, const void* lds, u
 }
 #pragma clang diagnostic pop
 
+// XOR swizzle of the 16-byte chunks of an LDS row: 128-byte rows use swz(); 64-byte rows (four
+// chunks) flip by (row / 4) % 4, so 16 consecutive rows reading one logical chunk (a phase of a
+// ds_read_b128) cover all 64 banks.
+template <int RB>
+__device__ __forceinline__ int swz_rows(int row) {
+  if constexpr (RB == 128) return swz(row);
+  else return (row >> 2) & 3;
+}
+
 // Global -> LDS copy of one operand tile with buffer_load ... lds (16 B per lane, the wave's
 // 64 lanes filling 1 KB of LDS contiguously); no staging registers. Lanes fetch permuted
 // sources so that the LDS image is swizzled:
@@ -163,11 +180,12 @@ __device__ __forceinline__ void lds_copy16(const i32x4& rsrc, const void* lds, u
 //   ds_read_b64_tr_b16 (4 consecutive rows x 64 bytes) hit distinct banks.
 // Chunks outside the operand (rows >= row_end, contraction >= k_end) are fetched from an
 // out-of-range offset and land as zeros.
-template <int ROWS, bool KMAJ, int ES, int NWAVES>
+template <int ROWS, bool KMAJ, int ES, int NWAVES, int RB = kRowBytes>
 struct TileCopy {
-  static constexpr int kInstr = ROWS * kRowBytes / 1024 / NWAVES;   // 1-KB pieces per wave
-  static constexpr int kRowsPerInstr = KMAJ ? 8 : 1024 / (ROWS * 2);
-  static constexpr int kChunksPerRow = KMAJ ? 8 : ROWS / 8;
+  static_assert(KMAJ || RB == kRowBytes, "outer-contiguous tiles take 128-byte k-tiles");
+  static constexpr int kInstr = ROWS * RB / 1024 / NWAVES;          // 1-KB pieces per wave
+  static constexpr int kRowsPerInstr = KMAJ ? 1024 / RB : 1024 / (ROWS * 2);
+  static constexpr int kChunksPerRow = KMAJ ? RB / 16 : ROWS / 8;
   uint32_t off[kInstr];      // byte offset of the lane's source at contraction 0 (or kOOB)
   int32_t kk[kInstr];        // contraction index of the lane's source relative to the tile start
 
@@ -180,7 +198,7 @@ struct TileCopy {
       const int r = piece * kRowsPerInstr + lane / kChunksPerRow;   // LDS row
       const int p = lane % kChunksPerRow;                           // physical chunk
       if constexpr (KMAJ) {
-        const int c = p ^ swz(r);
+        const int c = p ^ swz_rows<RB>(r);
         const int64_t row = rowmap(row0, r);
         kk[i] = c * (16 / ES);
         off[i] = row < row_end ? (uint32_t)((row - row0) * ld * ES + c * 16) : kOOB;
@@ -261,15 +279,20 @@ void gemm_kernel(const GemmParams p) {
   constexpr int ES = FMT == F_BF16 ? 2 : 1;
   constexpr int WM = 32 * WMF, WN = 32 * WNF;
   constexpr int BM = WGM * WM, BN = WGN * WN;
-  constexpr int KT_ELEMS = kRowBytes / ES;               // contraction elements per k-tile
-  constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
-  // Two LDS stages as distinct objects, so the compiler can tell the tile being
-  // multiplied from the one the direct-to-LDS loads are filling.
-  __shared__ __attribute__((aligned(16))) uint8_t lds0[A_BYTES + B_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds1[A_BYTES + B_BYTES];
-  // MXFP8: E8M0 scales of 4 k-tiles (16 blocks of 32) per operand row, double-buffered.
-  constexpr int kScaleTiles = 4;
-  constexpr int SC_BYTES = FMT == F_MX ? (BM + BN) * 4 * kScaleTiles : 16;
+  constexpr bool kDeep = deep_pipe(FMT, SCHED);
+  constexpr int RB = kDeep ? 64 : kRowBytes;             // contraction bytes per LDS row and k-tile
+  constexpr int NST = kDeep ? 4 : 2;                     // LDS stages
+  constexpr int KT_ELEMS = RB / ES;                      // contraction elements per k-tile
+  constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB, STAGE = A_BYTES + B_BYTES;
+  static_assert(NST * STAGE == 131072, "the stages fill the 128 KB the epilogue stages its tile through");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE];
+  // The epilogue stages fp32 rows through the two 64 KB halves of the same memory.
+  uint8_t* const half0 = lds;
+  uint8_t* const half1 = lds + NST * STAGE / 2;
+  // MXFP8: E8M0 scales of 16 blocks of 32 per operand row (4 k-tiles of 128 bytes or 8 of 64),
+  // double-buffered.
+  constexpr int kScaleTiles = 512 / RB;
+  constexpr int SC_BYTES = (FMT == F_MX && !kDeep) ? (BM + BN) * 4 * kScaleTiles : 16;
   __shared__ __attribute__((aligned(16))) uint8_t sc_lds[2][SC_BYTES];
   __shared__ uint32_t amax_slot;                         // FP8 (d)SwiGLU epilogues: the tile's amax
 
@@ -392,8 +415,8 @@ void gemm_kernel(const GemmParams p) {
 
   // Tile copies. Inner-contiguous operands are addressed from their first tile row,
   // outer-contiguous ones from the tile's first outer column of contraction row 0.
-  TileCopy<BM, AK, ES, NWAVES> ca;
-  TileCopy<BN, BK, ES, NWAVES> cb;
+  TileCopy<BM, AK, ES, NWAVES, RB> ca;
+  TileCopy<BN, BK, ES, NWAVES, RB> cb;
   const uint8_t* a_base = AK ? p.a + m0 * p.lda * ES : p.a + m0 * 2;
   const int64_t a_bytes = AK ? ((SCHED == S_GROUP_M ? p.T : p.M) - m0) * p.lda * ES : p.K * p.lda * 2 - m0 * 2;
   const uint8_t* b_base = BK ? bptr + n0 * p.ldb * ES : bptr + n0 * 2;
@@ -417,7 +440,7 @@ void gemm_kernel(const GemmParams p) {
     if constexpr (FMT == F_MX) {
       // 1-KB pieces: 64 rows x 16 bytes; A rows then B rows.
       constexpr int kPieces = (BM + BN) / 64;
-      const int64_t blk0 = (k_begin >> 5) + (int64_t)group * 4 * kScaleTiles;
+      const int64_t blk0 = (k_begin >> 5) + (int64_t)group * 16;
       const int64_t nblk = (k_end + 31) >> 5;
 #pragma unroll
       for (int it = 0; it < (kPieces + NWAVES - 1) / NWAVES; ++it) {
@@ -445,13 +468,17 @@ void gemm_kernel(const GemmParams p) {
       const int sh = 8 * (lane >> 5);
       if constexpr (mx_lds) {
         const int t = (int)((k0 - k_begin) / KT_ELEMS);
-        const uint8_t* sl = sc_lds[(t / kScaleTiles) & 1] + (t % kScaleTiles) * 4;
+        // a k-tile's RB/32 bytes start at byte (t % kScaleTiles) * RB/32 of the row's 16; 64-byte
+        // tiles take the aligned dword holding their 2 bytes and shift the odd tile's down
+        const int byte0 = (t % kScaleTiles) * (RB / 32);
+        const uint8_t* sl = sc_lds[(t / kScaleTiles) & 1] + (byte0 & ~3);
+        const int sh2 = sh + 8 * (byte0 & 3);
 #pragma unroll
         for (int i = 0; i < WMF; ++i)
-          da[i] = *reinterpret_cast<const uint32_t*>(sl + (wm * WM + i * 32 + (lane & 31)) * 16) >> sh;
+          da[i] = *reinterpret_cast<const uint32_t*>(sl + (wm * WM + i * 32 + (lane & 31)) * 16) >> sh2;
 #pragma unroll
         for (int j = 0; j < WNF; ++j)
-          db[j] = *reinterpret_cast<const uint32_t*>(sl + (BM + wn * WN + j * 32 + (lane & 31)) * 16) >> sh;
+          db[j] = *reinterpret_cast<const uint32_t*>(sl + (BM + wn * WN + j * 32 + (lane & 31)) * 16) >> sh2;
         return;
       }
       const int64_t blk0 = k0 >> 5;
@@ -491,7 +518,7 @@ void gemm_kernel(const GemmParams p) {
 
   // Fragments: 8 bf16 (32x32x16) or 32 fp8 (32x32x64) contraction values per lane.
   using Frag = typename std::conditional<FMT == F_BF16, bf16x8, i32x8>::type;
-  constexpr int KS = FMT == F_BF16 ? 4 : 2;                         // MFMA k-steps per tile
+  constexpr int KS = FMT == F_BF16 ? RB / 32 : RB / 64;             // MFMA k-steps per tile
   constexpr int kReads = FMT == F_BF16 ? (AK ? WMF : 2 * WMF) + (BK ? WNF : 2 * WNF) : 2 * (WMF + WNF);
   constexpr int kMfma = WMF * WNF;
 
@@ -516,9 +543,9 @@ void gemm_kernel(const GemmParams p) {
       // bytes 16-31 hold k = 32 + 16*half .. +15 of the 64-wide step.
       auto rd8 = [&](const uint8_t* base, int r) {
         const int c0 = ks * 4 + lhalf, c1 = c0 + 2;
-        const uint8_t* row = base + r * kRowBytes;
-        const int4 lo = *reinterpret_cast<const int4*>(row + ((c0 ^ swz(r)) << 4));
-        const int4 hi = *reinterpret_cast<const int4*>(row + ((c1 ^ swz(r)) << 4));
+        const uint8_t* row = base + r * RB;
+        const int4 lo = *reinterpret_cast<const int4*>(row + ((c0 ^ swz_rows<RB>(r)) << 4));
+        const int4 hi = *reinterpret_cast<const int4*>(row + ((c1 ^ swz_rows<RB>(r)) << 4));
         return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       };
       fa[0] = rd8(a_lds, wm * WM + lrow);
@@ -572,6 +599,185 @@ void gemm_kernel(const GemmParams p) {
     }
   };
 
+  Frag fa[2][WMF], fb[2][WNF];
+  if constexpr (kDeep) {
+    // Four k-tiles of copies are in flight: the fragments of a tile (one MFMA k-step) are all in
+    // registers before its MFMAs run, so once every wave has passed the barrier that follows
+    // those reads, the tile's stage is refilled with the tile four ahead. Each tile's barrier
+    // is preceded by the wave's wait for its own copies of the next tile (vector loads complete
+    // in the order issued, so the copies of later tiles stay in flight) and for its own LDS
+    // reads; after it, that next tile's stage is visible to every wave.
+    // MXFP8 scales: the 16 E8M0 bytes of 8 k-tiles per operand row (one 16-byte piece of the row,
+    // as whole lines are fetched) go to one of two LDS buffers while the 8 tiles before them are
+    // multiplied. Every tile issues that copy (so each tile has the same count of copies to wait
+    // for); on the 7 tiles of 8 that are not due, its lanes take an out-of-range offset, which
+    // reads nothing from memory, and it lands in a dummy LDS area.
+    // A steady-state tile is one basic block with an explicit order: two MFMAs, the wait and
+    // the barrier, then each remaining MFMA followed by one copy of the tile four ahead and one
+    // fragment (with its scale) of the next tile. Fragments and scales are double-buffered by
+    // tile parity (the loop body is written out twice so every register index is a constant).
+    static_assert(NST == 4 && KS == 1 && WMF == 4 && WNF == 4, "deep pipeline: 4x4 fragments, one k-step");
+    constexpr int kGrpTiles = 8;                        // k-tiles per scale group (16 blocks of 32)
+    constexpr int SC_GROUP = kMX ? (BM + BN) * 16 : 0;  // scale bytes per group
+    constexpr int kScPer = SC_GROUP / 1024 / NWAVES;    // 1-KB pieces (64 rows) per wave
+    static_assert(!kMX || kScPer * 1024 * NWAVES == SC_GROUP, "scale pieces split evenly over the waves");
+    constexpr int kCa = decltype(ca)::kInstr, kCb = decltype(cb)::kInstr;
+    constexpr int CPT = kCa + kCb + kScPer;             // copies per tile per wave
+    constexpr int kHead = 2;                            // MFMAs issued before the wait and the barrier
+    static_assert(CPT <= kMfma - kHead, "one copy after each MFMA that follows the barrier");
+    // two group buffers, then the dummy area the off-cycle copies land in
+    __shared__ __attribute__((aligned(16))) uint8_t sc_st[kMX ? 2 * SC_GROUP + 1024 : 16];
+    uint32_t sa2[2][WMF], sb2[2][WNF];
+    auto stage = [&](int t) { return lds + (t % NST) * STAGE; };
+    uint32_t sc_off[kMX ? kScPer : 1];
+    bool sc_isa[kMX ? kScPer : 1];
+    if constexpr (kMX) {
+#pragma unroll
+      for (int it = 0; it < kScPer; ++it) {
+        const int piece = it * NWAVES + wave;
+        const bool is_a = piece < BM / 64;
+        const int r = (is_a ? piece : piece - BM / 64) * 64 + lane;
+        const int64_t row = is_a ? m0 + r : n0 + r;
+        const bool ok = row < (is_a ? row_end : b_rows);
+        sc_isa[it] = is_a;
+        sc_off[it] = ok ? (uint32_t)(row * (is_a ? p.a_mx_ld : p.b_mx_ld)) : kOOB;
+      }
+    }
+    const i32x4 rs_a = make_rsrc4(p.a_mx, kMX ? p.M * p.a_mx_ld : 0);
+    const i32x4 rs_b = make_rsrc4(bmx, kMX ? b_rows * p.b_mx_ld : 0);
+    // Copy number c (0 .. CPT-1) made while tile t - NST is multiplied: the A and B pieces of tile
+    // t, then, when t % 8 == 4, the scale pieces of group g = t / 8 + 1. That group is first
+    // read at tile t + 4 (whose copies follow these); its buffer held group g - 2, last read at
+    // tile t - 5, before the barrier of the tile being multiplied.
+    auto copy = [&](int t, int c) {
+      const int64_t k0 = k_begin + (int64_t)t * KT_ELEMS;
+      uint8_t* buf = stage(t);
+      if (c < kCa) {
+        const i32x4 rsrc = make_rsrc4(a_base + k0, a_bytes - k0);
+        lds_copy16(rsrc, buf + (NWAVES * c + wave) * 1024, (k0 + ca.kk[c] < k_end) ? ca.off[c] : kOOB);
+      } else if (c < kCa + kCb) {
+        const int i = c - kCa;
+        const i32x4 rsrc = make_rsrc4(b_base + k0, b_bytes - k0);
+        lds_copy16(rsrc, buf + A_BYTES + (NWAVES * i + wave) * 1024, (k0 + cb.kk[i] < k_end) ? cb.off[i] : kOOB);
+      } else if constexpr (kMX) {
+        const int it = c - kCa - kCb;
+        const int piece = it * NWAVES + wave;
+        const int g = t / kGrpTiles + 1;
+        const bool due = t % kGrpTiles == kGrpTiles / 2 && g * kGrpTiles < KT;
+        const uint8_t* dst = due ? sc_st + (g & 1) * SC_GROUP + piece * 1024 : sc_st + 2 * SC_GROUP;
+        const uint32_t o = (due && sc_off[it] != kOOB) ? sc_off[it] + (uint32_t)(g * 16) : kOOB;
+        lds_copy16(sc_isa[it] ? rs_a : rs_b, dst, o);
+      }
+    };
+    // Fragment f of tile t (f = 0: A0, 1..4: B0..B3, 5..7: A1..A3, the order the MFMAs use them)
+    // and the dword of its row's E8M0 bytes that holds tile t's two blocks (the two lane halves
+    // read the same dword: a broadcast, not a bank conflict). The tile that uses it shifts it by
+    // 8 bits in the upper lane half and selects byte 2 * (t % 2) in the MFMA.
+    auto frag = [&](int t, int f, Frag (&fa_)[WMF], Frag (&fb_)[WNF], uint32_t (&sa_)[WMF], uint32_t (&sb_)[WNF]) {
+      const uint8_t* buf = stage(t);
+      const bool is_a = f == 0 || f >= 5;
+      const int idx = f == 0 ? 0 : (f >= 5 ? f - 4 : f - 1);
+      const int r = is_a ? wm * WM + idx * 32 + lrow : wn * WN + idx * 32 + lrow;
+      const uint8_t* row = buf + (is_a ? 0 : A_BYTES) + r * RB;
+      const int4 lo = *reinterpret_cast<const int4*>(row + ((lhalf ^ swz_rows<RB>(r)) << 4));
+      const int4 hi = *reinterpret_cast<const int4*>(row + (((2 + lhalf) ^ swz_rows<RB>(r)) << 4));
+      const i32x8 v = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      if (is_a) fa_[idx] = v;
+      else fb_[idx] = v;
+      if constexpr (kMX) {
+        const uint8_t* sl = sc_st + ((t / kGrpTiles) & 1) * SC_GROUP;
+        const uint32_t e = *reinterpret_cast<const uint32_t*>(sl + ((is_a ? 0 : BM) + r) * 16 + 4 * ((t % kGrpTiles) >> 1));
+        if (is_a) sa_[idx] = e;
+        else sb_[idx] = e;
+      }
+    };
+    auto mma1 = [&](const Frag (&fa_)[WMF], const Frag (&fb_)[WNF], const uint32_t (&sa_)[WMF],
+                    const uint32_t (&sb_)[WNF], int q, auto odd_c) {
+      const int i = q / WNF, j = q % WNF;
+      constexpr int sel = 2 * decltype(odd_c)::value;   // byte of the tile's first block
+      if constexpr (kMX)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb_[j], fa_[i], acc[i][j], 0, 0, sel,
+                                                                    (int)sb_[j], sel, (int)sa_[i]);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb_[j], fa_[i], acc[i][j], 0, 0, 0,
+                                                                    0x7F7F7F7F, 0, 0x7F7F7F7F);
+    };
+    auto barrier_after = [&](auto n_c) {               // own copies down to n outstanding, then barrier
+      constexpr int n = decltype(n_c)::value;
+      if constexpr (n == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+    };
+    auto wait_tile = [&](int t, int issued_after) {     // tile t landed; issued_after: later tiles issued
+      if (issued_after >= 3) barrier_after(std::integral_constant<int, 3 * CPT>{});
+      else if (issued_after == 2) barrier_after(std::integral_constant<int, 2 * CPT>{});
+      else if (issued_after == 1) barrier_after(std::integral_constant<int, CPT>{});
+      else barrier_after(std::integral_constant<int, 0>{});
+    };
+    if (KT > 0) {
+      if constexpr (kMX) {                              // group 0's scales, before every tile copy
+#pragma unroll
+        for (int it = 0; it < kScPer; ++it) {
+          const int piece = it * NWAVES + wave;
+          lds_copy16(sc_isa[it] ? rs_a : rs_b, sc_st + piece * 1024, sc_off[it]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NST; ++t)
+        if (t < KT)
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) copy(t, c);
+      wait_tile(0, KT - 1 < NST - 1 ? KT - 1 : NST - 1);
+#pragma unroll
+      for (int f = 0; f < 8; ++f) frag(0, f, fa[0], fb[0], sa2[0], sb2[0]);
+    }
+    // Tile kt (parity P): tile kt + NST exists (steady) or not (tail).
+    auto tile = [&](int kt, auto par, auto steady_c) {
+      constexpr int P = decltype(par)::value, Q = P ^ 1;
+      constexpr bool steady = decltype(steady_c)::value;
+      const std::integral_constant<int, P> odd{};        // tile kt is odd exactly when P == 1
+      if constexpr (kMX) {                               // the upper lane half's block is the next byte
+#pragma unroll
+        for (int i = 0; i < WMF; ++i) sa2[P][i] >>= 8 * lhalf;
+#pragma unroll
+        for (int j = 0; j < WNF; ++j) sb2[P][j] >>= 8 * lhalf;
+      }
+#pragma unroll
+      for (int q = 0; q < kHead; ++q) mma1(fa[P], fb[P], sa2[P], sb2[P], q, odd);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (steady) {
+        barrier_after(std::integral_constant<int, 2 * CPT>{});   // tiles kt+2, kt+3 stay in flight
+      } else {
+        if (kt + 1 < KT) wait_tile(kt + 1, KT - 2 - kt < NST - 2 ? KT - 2 - kt : NST - 2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = kHead; q < kMfma; ++q) {
+        mma1(fa[P], fb[P], sa2[P], sb2[P], q, odd);
+        const int s_ = q - kHead;
+        if constexpr (steady) {
+          if (s_ < CPT) copy(kt + NST, s_);
+          if (s_ < 8) frag(kt + 1, s_, fa[Q], fb[Q], sa2[Q], sb2[Q]);
+        } else {
+          if (s_ < CPT && kt + NST < KT) copy(kt + NST, s_);
+          if (s_ < 8 && kt + 1 < KT) frag(kt + 1, s_, fa[Q], fb[Q], sa2[Q], sb2[Q]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    using S1 = std::integral_constant<bool, true>;
+    using S0 = std::integral_constant<bool, false>;
+    int kt = 0;
+    for (; kt + 1 + NST < KT; kt += 2) {                // tiles kt + NST and kt + 1 + NST exist
+      tile(kt, std::integral_constant<int, 0>{}, S1{});
+      tile(kt + 1, std::integral_constant<int, 1>{}, S1{});
+    }
+    for (; kt < KT; kt += 2) {                          // at most NST + 1 tiles
+      tile(kt, std::integral_constant<int, 0>{}, S0{});
+      if (kt + 1 < KT) tile(kt + 1, std::integral_constant<int, 1>{}, S0{});
+    }
+  } else {
   // Each wave waits for its own direct-to-LDS copies, then the barrier makes the
   // whole stage visible (and frees the other stage for the next copies).
   auto stage_done = [&]() {
@@ -583,17 +789,18 @@ void gemm_kernel(const GemmParams p) {
   // run; the barrier sits before the tile's last k-step, whose MFMAs cover the
   // reads of the next tile's first fragments (the fragments of that last step
   // are already in registers, so the other stage may be refilled).
-  Frag fa[2][WMF], fb[2][WNF];
+  uint8_t* const st0 = lds;
+  uint8_t* const st1 = lds + STAGE;
   if (KT > 0) {
-    issue_tile(lds0, k_begin);
+    issue_tile(st0, k_begin);
     if constexpr (mx_lds) issue_scales(0, 0);
     stage_done();
     load_scales(k_begin, sa, sb);
-    rd(lds0, 0, fa[0], fb[0]);
+    rd(st0, 0, fa[0], fb[0]);
   }
   for (int kt = 0; kt < KT; ++kt) {
-    const uint8_t* cur = (kt & 1) ? lds1 : lds0;
-    uint8_t* nxt = (kt & 1) ? lds0 : lds1;
+    const uint8_t* cur = (kt & 1) ? st1 : st0;
+    uint8_t* nxt = (kt & 1) ? st0 : st1;
     if (kt + 1 < KT) {
       issue_tile(nxt, k_begin + (int64_t)(kt + 1) * KT_ELEMS);
       if constexpr (kMX && !mx_lds) load_scales(k_begin + (int64_t)(kt + 1) * KT_ELEMS, san, sbn);
@@ -627,6 +834,7 @@ void gemm_kernel(const GemmParams p) {
       }
     }
   }
+  }
 
   // ---------------------------------------------------------------- epilogue
   // Branch-free: every global access is a buffer op over the output tile whose
@@ -650,7 +858,7 @@ void gemm_kernel(const GemmParams p) {
     // E_SRELU (scaled squared ReLU, elementwise): y = p * max(v, 0)^2 goes to c and the
     // pre-activation v (bf16) to aux, at the same offsets (ld_aux == ldc).
     constexpr bool kSR = EPI == E_SRELU;
-    static_assert(BM == 2 * WM && A_BYTES + B_BYTES == 64 * BN * 4, "epilogue staging assumes 2 wave rows");
+    static_assert(BM == 2 * WM && NST * STAGE == 2 * 64 * BN * 4, "epilogue staging assumes 2 wave rows");
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(cptr ? cptr + m0 * p.ldc : cptr, cptr ? rows_left * p.ldc * 2 : 0);
     // E_SRELU with q_out: y also as MXFP8 rowwise (ld_q == ldc, so byte offsets are offs / 2; four
     // adjacent lanes hold a 32-column block); E4M3: the group's amax of y (as in E_SWIGLU).
@@ -663,7 +871,7 @@ void gemm_kernel(const GemmParams p) {
     if (kAmax && threadIdx.x == 0) amax_slot = 0;
     constexpr int kChunks = BN / 8;                        // 8-column chunks per row
     constexpr int kIters = 128 * kChunks / (NWAVES * 64);  // chunks per thread per pass
-    float* stage = reinterpret_cast<float*>(wm ? lds1 : lds0);
+    float* stage = reinterpret_cast<float*>(wm ? half1 : half0);
     // The residual of both passes is requested first: its HBM latency overlaps the staging.
     v4i res[2][kIters];
     int offs[2][kIters];
@@ -703,7 +911,7 @@ void gemm_kernel(const GemmParams p) {
       for (int it = 0; it < kIters; ++it) {
         const int id = it * NWAVES * 64 + threadIdx.x;
         const int rp = id / kChunks, c = id % kChunks;
-        const float* row = reinterpret_cast<const float*>(rp >= 64 ? lds1 : lds0) + (rp & 63) * BN;
+        const float* row = reinterpret_cast<const float*>(rp >= 64 ? half1 : half0) + (rp & 63) * BN;
         const int sw = (rp & 63) & 15;
         const float4 lo = *reinterpret_cast<const float4*>(row + (((2 * c) ^ sw) << 2));
         const float4 hi = *reinterpret_cast<const float4*>(row + (((2 * c + 1) ^ sw) << 2));
@@ -764,7 +972,7 @@ void gemm_kernel(const GemmParams p) {
     // With q_out, y is also emitted as MXFP8 rowwise (E4M3 bytes plus one E8M0 exponent per
     // 32 columns): the MX quantization of bf16(y), exactly as the standalone quantizer would
     // produce it from the bf16 output (four adjacent lanes hold one 32-column block).
-    static_assert(BM == 2 * WM && A_BYTES + B_BYTES == 64 * BN * 4, "epilogue staging assumes 2 wave rows");
+    static_assert(BM == 2 * WM && NST * STAGE == 2 * 64 * BN * 4, "epilogue staging assumes 2 wave rows");
     static_assert(WNF % 2 == 0 && BN / 16 == 16, "gate and up fragments per wave column; 16 chunks per row");
     const int64_t ybytes = cptr ? rows_left * p.ldc * 2 : 0;
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(cptr ? cptr + m0 * p.ldc : cptr, ybytes);
@@ -780,7 +988,7 @@ void gemm_kernel(const GemmParams p) {
     constexpr int kCpw = WN / 16, kGpw = WN / 4;           // chunks, granules per wave column
     constexpr int kIters = 128 * kChunks / (NWAVES * 64);
     auto wsw = [](int w) { return (w & 1) | ((w & 2) << 2); };
-    float* stage = reinterpret_cast<float*>(wm ? lds1 : lds0);
+    float* stage = reinterpret_cast<float*>(wm ? half1 : half0);
     constexpr bool kAmax = FMT == F_E4M3;                  // per-group amax of y (FP8 current scaling)
     float amax_acc = 0.0f;                                 // max |y| (masked lanes hold 0)
     if (kAmax && threadIdx.x == 0) amax_slot = 0;
@@ -823,7 +1031,7 @@ void gemm_kernel(const GemmParams p) {
         const int id = it * NWAVES * 64 + threadIdx.x;
         const int rp_ = id / kChunks, c = id % kChunks;
         const int rr = rp_ & 63, wc = c / kCpw, cc = c % kCpw;
-        const float* row = reinterpret_cast<const float*>(rp_ >= 64 ? lds1 : lds0) + rr * BN;
+        const float* row = reinterpret_cast<const float*>(rp_ >= 64 ? half1 : half0) + rr * BN;
         const int x = (rr & 15) ^ wsw(wc);
         const int ga = wc * kGpw + 2 * cc, gb = ga + kGpw / 2;   // gate and up granules of this chunk
         const float4 a0 = *reinterpret_cast<const float4*>(row + ((ga ^ x) << 2));
@@ -879,7 +1087,7 @@ void gemm_kernel(const GemmParams p) {
     // of the saved pre-activation), 16-byte stores of da and db. A row's BN/8 chunks are 32
     // consecutive lanes, which reduce the row's dprobs partial in a fixed order; one partial
     // per row and column tile goes to the workspace.
-    static_assert(BM == 2 * WM && A_BYTES + B_BYTES == 64 * BN * 4, "epilogue staging assumes 2 wave rows");
+    static_assert(BM == 2 * WM && NST * STAGE == 2 * 64 * BN * 4, "epilogue staging assumes 2 wave rows");
     static_assert(BN / 8 == 32, "a row's chunks fill half a wave");
     // E_DSRELU (scaled squared ReLU): one pre-activation h [T, F]; dh = g * p * 2 max(h, 0),
     // dprobs partial sum of g * max(h, 0)^2.
@@ -908,7 +1116,7 @@ void gemm_kernel(const GemmParams p) {
     const __amdgpu_buffer_rsrc_t rpart = make_rsrc(p.dp_part + (int64_t)nt * p.T + m0, rows_left * 4);
     constexpr int kChunks = BN / 8;
     constexpr int kIters = 128 * kChunks / (NWAVES * 64);
-    float* stage = reinterpret_cast<float*>(wm ? lds1 : lds0);
+    float* stage = reinterpret_cast<float*>(wm ? half1 : half0);
     __syncthreads();                                       // every wave is done with the LDS stages
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
@@ -958,7 +1166,7 @@ void gemm_kernel(const GemmParams p) {
         const int it = it0 + ib;
         const int id = it * NWAVES * 64 + threadIdx.x;
         const int rp_ = id / kChunks, c = id % kChunks;
-        const float* row = reinterpret_cast<const float*>(rp_ >= 64 ? lds1 : lds0) + (rp_ & 63) * BN;
+        const float* row = reinterpret_cast<const float*>(rp_ >= 64 ? half1 : half0) + (rp_ & 63) * BN;
         const int sw = (rp_ & 63) & 15;
         const float4 lo = *reinterpret_cast<const float4*>(row + (((2 * c) ^ sw) << 2));
         const float4 hi = *reinterpret_cast<const float4*>(row + (((2 * c + 1) ^ sw) << 2));
@@ -1051,8 +1259,8 @@ static hipError_t launch_cfg(GemmParams p, int grid, hipStream_t s) {
 
 template <int FMT, bool AK, bool BK, int EPI, int SCHED>
 static hipError_t launch_tile(GemmParams p, hipStream_t s) {
-  constexpr int WGM = TileShape<FMT>::WGM, WGN = TileShape<FMT>::WGN;
-  constexpr int WMF = TileShape<FMT>::WMF, WNF = TileShape<FMT>::WNF;
+  constexpr int WGM = TileShape<FMT, SCHED>::WGM, WGN = TileShape<FMT, SCHED>::WGN;
+  constexpr int WMF = TileShape<FMT, SCHED>::WMF, WNF = TileShape<FMT, SCHED>::WNF;
   constexpr int BM = WGM * 32 * WMF, BN = WGN * 32 * WNF;
   int grid = 0;
   if constexpr (SCHED == S_DENSE) {
