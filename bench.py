@@ -239,6 +239,11 @@ def build_grouped(torch, sge, wl, inp):
              "fc2_wgrad": 2 * T * H * F, "fc1_dgrad": 2 * T * N1 * H, "fc1_wgrad": 2 * T * N1 * H}
 
     base = offs[0]
+    if wl["fmt"] == "bf16":
+        # each layer's backward is one call: its dgrad (with the activation's backward for fc2)
+        # and its weight gradient share one launch
+        flops = {"fc1_fwd": 2 * T * N1 * H, "fc2_fwd": 2 * T * H * F, "fc2_bwd": 4 * T * H * F,
+                 "fc1_bwd": 4 * T * N1 * H}
     if wl["fmt"] == "mxfp8":
         return build_grouped_mx(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, dh, dp, dw2, dx, dw1, ws)
     if wl["fmt"] == "fp8":
@@ -249,11 +254,9 @@ def build_grouped(torch, sge, wl, inp):
         ("fc1_fwd", lambda: sge.grouped_linear_fwd(X, W1, base, y, epilogue=fwd_epi, probs=P, preact=h,
                                                    act=ap)),
         ("fc2_fwd", lambda: sge.grouped_linear_fwd(y, W2, base, out)),
-        (dact, lambda: sge.grouped_linear_bwd(DOUT, None, W2, base, epilogue=bwd_epi,
-                                              preact=h, probs=P, dact=dh, dprobs=dp, workspace=ws, act=ap)),
-        ("fc2_wgrad", lambda: sge.grouped_linear_bwd(DOUT, y, W2, base, dw=dw2)),
-        ("fc1_dgrad", lambda: sge.grouped_linear_bwd(dh, None, W1, base, dx=dx)),
-        ("fc1_wgrad", lambda: sge.grouped_linear_bwd(dh, X, W1, base, dw=dw1)),
+        ("fc2_bwd", lambda: sge.grouped_linear_bwd(DOUT, y, W2, base, epilogue=bwd_epi, preact=h, probs=P,
+                                                   dact=dh, dprobs=dp, dw=dw2, workspace=ws, act=ap)),
+        ("fc1_bwd", lambda: sge.grouped_linear_bwd(dh, X, W1, base, dx=dx, dw=dw1)),
     ]
     return launches, flops, {}
 

@@ -342,6 +342,9 @@ sge_status sge_grouped_linear_fwd_mxfp8(const void* x_q, const void* x_s, const 
  *                         with preact h = [a, b] [T, 2K] bf16 (unclamped); writes dact [T, 2K]
  *                         and dprobs [T] by the backward given with sge_act_params.
  * dw: device bf16 [G, N, K] or NULL to skip the weight gradient.
+ * When both the dgrad (dx or the activation backward) and dw are asked for, the two GEMMs run
+ * in one launch (the dgrad's tiles, then the weight gradient's); the results are the same
+ * bits as from two calls.
  * workspace: device, >= sge_grouped_linear_bwd_workspace_size(T, K, G, epilogue) bytes
  * (0 is valid for SGE_EPI_NONE).
  */

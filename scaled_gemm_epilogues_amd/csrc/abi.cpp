@@ -547,62 +547,62 @@ sge_status sge_grouped_linear_bwd(const void* dy, const void* x, const void* w, 
     if (dw) return hip_status(sge::launch_fill_bf16_zero(static_cast<uint16_t*>(dw), (int64_t)G * N, K, K, stream), "fill");
     return ok();
   }
-  hipError_t e = hipSuccess;
-  if (swiglu || dx) {
-    sge::GemmParams p;
-    memset(&p, 0, sizeof(p));
-    p.a = static_cast<const uint8_t*>(dy);
-    p.lda = N;
-    p.b = static_cast<const uint8_t*>(w);
-    p.ldb = K;
-    p.M = T;
-    p.N = K;
-    p.K = N;
-    p.b_group_stride = N * K;
-    p.alpha = alpha;
-    p.c = static_cast<uint16_t*>(dx);
-    p.ldc = K;
-    p.offsets = offsets;
-    p.G = G;
-    p.T = T;
+  const bool want_dg = swiglu || dx;
+  sge::GemmParams pd, pw;
+  memset(&pd, 0, sizeof(pd));
+  memset(&pw, 0, sizeof(pw));
+  if (want_dg) {
+    pd.a = static_cast<const uint8_t*>(dy);
+    pd.lda = N;
+    pd.b = static_cast<const uint8_t*>(w);
+    pd.ldb = K;
+    pd.M = T;
+    pd.N = K;
+    pd.K = N;
+    pd.b_group_stride = N * K;
+    pd.alpha = alpha;
+    pd.c = static_cast<uint16_t*>(dx);
+    pd.ldc = K;
+    pd.offsets = offsets;
+    pd.G = G;
+    pd.T = T;
     if (swiglu) {
-      p.probs = probs;
-      p.aux = const_cast<uint16_t*>(static_cast<const uint16_t*>(preact));
-      p.ld_aux = hw;
-      p.aux_out = static_cast<uint16_t*>(dact);
-      p.ld_aux_out = hw;
-      p.dp_part = static_cast<float*>(workspace);
-      p.F = K;
+      pd.probs = probs;
+      pd.aux = const_cast<uint16_t*>(static_cast<const uint16_t*>(preact));
+      pd.ld_aux = hw;
+      pd.aux_out = static_cast<uint16_t*>(dact);
+      pd.ld_aux_out = hw;
+      pd.dp_part = static_cast<float*>(workspace);
+      pd.F = K;
     }
-    set_act(p, epilogue, act_params);
-    e = sge::launch_grouped_dgrad(p, epilogue, stream);
-    if (e != hipSuccess) return hip_status(e, "grouped dgrad launch");
-    if (swiglu) {
-      const int parts =
-          (int)(sge::gemm_dp_parts_per_tile() * ((K + sge::gemm_tile_n() - 1) / sge::gemm_tile_n()));
-      e = sge::launch_rowsum_parts(static_cast<const float*>(workspace), parts, offsets, G, T, dprobs, stream);
-      if (e != hipSuccess) return hip_status(e, "dprobs reduction launch");
-    }
+    set_act(pd, epilogue, act_params);
   }
   if (dw) {
-    sge::GemmParams p;
-    memset(&p, 0, sizeof(p));
-    p.a = static_cast<const uint8_t*>(dy);
-    p.lda = N;
-    p.b = static_cast<const uint8_t*>(x);
-    p.ldb = K;
-    p.M = N;
-    p.N = K;
-    p.K = T;
-    p.alpha = alpha;
-    p.c = static_cast<uint16_t*>(dw);
-    p.ldc = K;
-    p.c_group_stride = N * K;
-    p.offsets = offsets;
-    p.G = G;
-    p.T = T;
-    e = sge::launch_grouped_wgrad(p, stream);
-    if (e != hipSuccess) return hip_status(e, "grouped wgrad launch");
+    pw.a = static_cast<const uint8_t*>(dy);
+    pw.lda = N;
+    pw.b = static_cast<const uint8_t*>(x);
+    pw.ldb = K;
+    pw.M = N;
+    pw.N = K;
+    pw.K = T;
+    pw.alpha = alpha;
+    pw.c = static_cast<uint16_t*>(dw);
+    pw.ldc = K;
+    pw.c_group_stride = N * K;
+    pw.offsets = offsets;
+    pw.G = G;
+    pw.T = T;
+  }
+  // Both GEMMs read only the call's inputs, so they share one launch when both are asked for.
+  hipError_t e = hipSuccess;
+  if (want_dg && dw) e = sge::launch_grouped_dgrad_wgrad(pd, epilogue, pw, stream);
+  else if (want_dg) e = sge::launch_grouped_dgrad(pd, epilogue, stream);
+  else if (dw) e = sge::launch_grouped_wgrad(pw, stream);
+  if (e != hipSuccess) return hip_status(e, "grouped dgrad / wgrad launch");
+  if (swiglu) {
+    const int parts = (int)(sge::gemm_dp_parts_per_tile() * ((K + sge::gemm_tile_n() - 1) / sge::gemm_tile_n()));
+    e = sge::launch_rowsum_parts(static_cast<const float*>(workspace), parts, offsets, G, T, dprobs, stream);
+    if (e != hipSuccess) return hip_status(e, "dprobs reduction launch");
   }
   return ok();
 }

@@ -56,6 +56,9 @@ hipError_t launch_grouped_fwd(const GemmParams& p, int epilogue, hipStream_t s);
 hipError_t launch_grouped_fwd_mx(const GemmParams& p, int epilogue, hipStream_t s);
 hipError_t launch_grouped_dgrad(const GemmParams& p, int epilogue, hipStream_t s);
 hipError_t launch_grouped_wgrad(const GemmParams& p, hipStream_t s);
+// The grouped dgrad (epilogue as in launch_grouped_dgrad) and the grouped wgrad of one layer, in
+// one launch (the two GEMMs are independent).
+hipError_t launch_grouped_dgrad_wgrad(const GemmParams& dg, int epilogue, const GemmParams& wg, hipStream_t s);
 // MXFP8 operands, both inner-contiguous (scale rows dword-aligned: contraction % 128 == 0).
 hipError_t launch_grouped_dgrad_mx(const GemmParams& p, int epilogue, hipStream_t s);
 // E4M3 operands with one scale per group (sinv_per_group), both inner-contiguous.
