@@ -77,7 +77,7 @@ constexpr int kWavesM = SGE_WAVES_M, kWavesN = SGE_WAVES_N, kFragsM = SGE_FRAGS_
 #endif
 
 #ifndef SGE_DEEP_8BIT
-#define SGE_DEEP_8BIT 1          // 8-bit dense GEMMs: 64-byte k-tiles in four LDS stages
+#define SGE_DEEP_8BIT 1          // 8-bit dense / weight-gradient GEMMs: 64-byte k-tiles, four LDS stages
 #endif
 
 // Deep pipeline: with one wave per SIMD nothing covers a wave's wait for its tile copies, so the
@@ -85,16 +85,21 @@ constexpr int kWavesM = SGE_WAVES_M, kWavesN = SGE_WAVES_N, kFragsM = SGE_FRAGS_
 // bytes, one MFMA k-step each, 128 KB in all) instead of one (two stages of 128 bytes). The bf16
 // tiles keep two stages and two waves per SIMD: on 2x2 waves with four 64-byte stages, and on
 // 2x4 waves with eight 32-byte stages (a barrier every 8 MFMAs), they measured 4-30% slower.
-constexpr bool deep_pipe(int fmt, int sched) {
-  return SGE_DEEP_8BIT && (fmt == F_MX || fmt == F_E4M3) && sched == S_DENSE;
+// Among the grouped GEMMs only the weight gradients (contraction over a group's tokens: few,
+// long tiles) take it: measured on the FP8 / MXFP8 grouped MLP they ran 2.5-4.6% faster, while
+// the row-partitioned ones ran from 2% faster to 29% slower (the FP8 activation-backward
+// epilogue on four waves instead of eight).
+constexpr bool deep_pipe(int fmt, int sched, int epi) {
+  return SGE_DEEP_8BIT && (fmt == F_MX || fmt == F_E4M3) && (sched == S_DENSE || sched == S_GROUP_K) &&
+         epi == E_STORE;
 }
 
 // Waves and fragments of a tile: MXFP8 (more live registers for the E8M0 scales) and the
 // deep-pipelined 8-bit tiles take 2x2 waves of 4x4 accumulators (one wave per SIMD; a third
 // fewer LDS fragment bytes per MFMA); the rest 2x4 waves of 4x2.
-template <int FMT, int SCHED>
+template <int FMT, int SCHED, int EPI>
 struct TileShape {
-  static constexpr bool k4 = FMT == F_MX || FMT == F_MXU || deep_pipe(FMT, SCHED);
+  static constexpr bool k4 = FMT == F_MX || FMT == F_MXU || deep_pipe(FMT, SCHED, EPI);
   static constexpr int WGM = k4 ? 2 : kWavesM, WGN = k4 ? 2 : kWavesN;
   static constexpr int WMF = k4 ? 4 : kFragsM, WNF = k4 ? 4 : kFragsN;
 };
@@ -272,8 +277,8 @@ struct SwigluRows {
 };
 
 // LDS a tile needs beside its 128 KB of stages: the MXFP8 scale buffers.
-constexpr int tile_sc_bytes(int fmt, int sched) {
-  return fmt == F_MX ? (deep_pipe(fmt, sched) ? 2 * 512 * 16 + 1024 : 2 * 512 * 16) : 32;
+constexpr int tile_sc_bytes(int fmt, int sched, int epi) {
+  return fmt == F_MX ? (deep_pipe(fmt, sched, epi) ? 2 * 512 * 16 + 1024 : 2 * 512 * 16) : 32;
 }
 
 // One output tile of one GEMM: tile number blk of the launch's tiles of this GEMM (a workgroup
@@ -287,7 +292,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
   constexpr int ES = FMT == F_BF16 ? 2 : 1;
   constexpr int WM = 32 * WMF, WN = 32 * WNF;
   constexpr int BM = WGM * WM, BN = WGN * WN;
-  constexpr bool kDeep = deep_pipe(FMT, SCHED);
+  constexpr bool kDeep = deep_pipe(FMT, SCHED, EPI);
   constexpr int RB = kDeep ? 64 : kRowBytes;             // contraction bytes per LDS row and k-tile
   constexpr int NST = kDeep ? 4 : 2;                     // LDS stages
   constexpr int KT_ELEMS = RB / ES;                      // contraction elements per k-tile
@@ -301,7 +306,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
   // double-buffered.
   constexpr int kScaleTiles = 512 / RB;
   constexpr int SC_BYTES = (FMT == F_MX && !kDeep) ? (BM + BN) * 4 * kScaleTiles : 16;
-  static_assert(2 * SC_BYTES <= tile_sc_bytes(FMT, SCHED), "scale buffers");
+  static_assert(2 * SC_BYTES <= tile_sc_bytes(FMT, SCHED, EPI), "scale buffers");
   uint8_t (*const sc_lds)[SC_BYTES] = reinterpret_cast<uint8_t (*)[SC_BYTES]>(sc_);
   uint32_t& amax_slot = *amax_slot_;                     // FP8 (d)SwiGLU epilogues: the tile's amax
 
@@ -641,7 +646,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
     constexpr int kHead = 2;                            // MFMAs issued before the wait and the barrier
     static_assert(CPT <= kMT - kHead && kFT <= kMT - kHead, "one copy and one fragment after each MFMA");
     // two group buffers, then the dummy area the off-cycle copies land in
-    static_assert(!kMX || 2 * SC_GROUP + 1024 <= tile_sc_bytes(FMT, SCHED), "scale buffers");
+    static_assert(!kMX || 2 * SC_GROUP + 1024 <= tile_sc_bytes(FMT, SCHED, EPI), "scale buffers");
     uint8_t* const sc_st = sc_;
     uint32_t sa2[2][WMF], sb2[2][WNF];
     Frag fa2[2][KS][WMF], fb2[2][KS][WNF];              // [tile parity][k-step][fragment]
@@ -654,14 +659,20 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
         const int piece = it * NWAVES + wave;
         const bool is_a = piece < BM / 64;
         const int r = (is_a ? piece : piece - BM / 64) * 64 + lane;
-        const int64_t row = is_a ? m0 + r : n0 + r;
+        // B rows follow the tile's row map (the gate / up interleave of a gated fc1)
+        const int64_t row = is_a ? m0 + r : (glu_fwd(EPI) ? swrows(n0, r) : n0 + r);
         const bool ok = row < (is_a ? row_end : b_rows);
         sc_isa[it] = is_a;
-        sc_off[it] = ok ? (uint32_t)(row * (is_a ? p.a_mx_ld : p.b_mx_ld)) : kOOB;
+        // the row's scale bytes from the first block of this tile run's contraction range
+        sc_off[it] = ok ? (uint32_t)(row * (is_a ? p.a_mx_ld : p.b_mx_ld) + (k_begin >> 5)) : kOOB;
       }
     }
-    const i32x4 rs_a = make_rsrc4(p.a_mx, kMX ? p.M * p.a_mx_ld : 0);
-    const i32x4 rs_b = make_rsrc4(bmx, kMX ? b_rows * p.b_mx_ld : 0);
+    // A's scales: rows of the whole operand; B's: to the end of the scale array (one expert's
+    // rows can sit inside wider rows holding every expert's)
+    const int64_t a_rows_total = SCHED == S_GROUP_M ? p.T : p.M;
+    const i32x4 rs_a = make_rsrc4(p.a_mx, kMX ? a_rows_total * p.a_mx_ld : 0);
+    const i32x4 rs_b = make_rsrc4(bmx, !kMX ? 0 : (p.b_mx_bytes ? (int64_t)((p.b_mx + p.b_mx_bytes) - bmx)
+                                                                 : b_rows * p.b_mx_ld));
     // Copy number c (0 .. CPT-1) made while tile t - NST is multiplied: the A and B pieces of tile
     // t, then, when t % 8 == 4, the scale pieces of group g = t / 8 + 1. That group is first
     // read at tile t + 4 (whose copies follow these); its buffer held group g - 2, last read at
@@ -1280,7 +1291,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM *
                           amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
 void gemm_kernel(const GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[131072];
-  __shared__ __attribute__((aligned(16))) uint8_t sc[tile_sc_bytes(FMT, SCHED)];
+  __shared__ __attribute__((aligned(16))) uint8_t sc[tile_sc_bytes(FMT, SCHED, EPI)];
   __shared__ uint32_t amax_slot;
   gemm_tile<FMT, AK, BK, EPI, SCHED, WGM, WGN, WMF, WNF>(p, blockIdx.x, lds, sc, &amax_slot);
 }
@@ -1297,11 +1308,11 @@ static hipError_t launch_cfg(GemmParams p, int grid, hipStream_t s) {
 // A GEMM's tile kind: its tile shape, the tile body, and the launch size.
 template <int FMT, bool AK, bool BK, int EPI, int SCHED>
 struct Kind {
-  using TS = TileShape<FMT, SCHED>;
+  using TS = TileShape<FMT, SCHED, EPI>;
   static constexpr int WGM = TS::WGM, WGN = TS::WGN, WMF = TS::WMF, WNF = TS::WNF;
   static constexpr int BM = WGM * 32 * WMF, BN = WGN * 32 * WNF;
   static constexpr int kThreads = 64 * WGM * WGN;
-  static constexpr int kScBytes = tile_sc_bytes(FMT, SCHED);
+  static constexpr int kScBytes = tile_sc_bytes(FMT, SCHED, EPI);
   __device__ __forceinline__ static void run(const GemmParams& p, int blk, uint8_t* lds, uint8_t* sc,
                                              uint32_t* slot) {
     gemm_tile<FMT, AK, BK, EPI, SCHED, WGM, WGN, WMF, WNF>(p, blk, lds, sc, slot);
