@@ -536,11 +536,16 @@ PROFILE_REPS = 5
 
 
 def copy_calibration():
+    """Two plain copies of COPY_BYTES: the runtime's device-to-device copy (its blit kernel), then
+    an elementwise kernel (out = in * 1, 16-byte vector loads and stores per thread, the access
+    size of the GEMM tile copies), each reading and writing COPY_BYTES once."""
     import torch
     a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
     torch.cuda.synchronize()
     b.copy_(a)
+    torch.cuda.synchronize()
+    torch.mul(a, 1.0, out=b)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": COPY_BYTES}), flush=True)
 
@@ -565,28 +570,39 @@ def summarize_traffic(pmc_dir, out_dir=None):
     last profile-reps dispatches (all of one kernel), each counter scaled by the bytes a plain
     copy moves per unit of that counter."""
     import glob
-    cal = {}
+    cal, blit = {}, {}
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         rows = _pmc_rows(os.path.join(pmc_dir, f"copy_{c}_counter_collection.csv"))
-        copies = [v for k, v in rows.values() if "copyBuffer" in k]
-        cal[c] = COPY_BYTES / (copies[-1] * 1024.0)            # counters count KiB
+        blits = [v for k, v in rows.values() if "copyBuffer" in k]
+        elem = [v for k, v in rows.values() if "elementwise" in k]
+        if blits:
+            blit[c] = COPY_BYTES / (blits[-1] * 1024.0)        # counters count KiB
+        # the scale factor comes from the elementwise copy (16-byte accesses, like the GEMMs'
+        # tile copies) when it was profiled, else from the blit
+        cal[c] = COPY_BYTES / ((elem or blits)[-1] * 1024.0)
+    kind = "elementwise copy" if cal != blit else "device-to-device copy (blit kernel)"
     src = os.path.join(ROOT, "scaled_gemm_epilogues_amd", "csrc", "gemm.hip")
     out = {"source": "gemm.hip", "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
-           "calibration": {"copy_bytes": COPY_BYTES, "fetch_factor": cal["FETCH_SIZE"],
-                           "write_factor": cal["WRITE_SIZE"]},
+           "calibration": {"copy_bytes": COPY_BYTES, "kernel": kind, "fetch_factor": cal["FETCH_SIZE"],
+                           "write_factor": cal["WRITE_SIZE"], "blit_fetch_factor": blit.get("FETCH_SIZE"),
+                           "blit_write_factor": blit.get("WRITE_SIZE")},
            "bytes_per_launch": {}, "raw_kib_per_launch": {}}
-    md = ["# HBM-side traffic per launch (GEMMs and quantizers)", "",
+    blit_note = (f" (the runtime's device-to-device blit of the same size reads as fetch factor "
+                 f"{blit['FETCH_SIZE']:.3f}, write factor {blit['WRITE_SIZE']:.3f})") if blit and cal != blit else ""
+    md = ["# Traffic between the L2s and the fabric per launch (GEMMs and quantizers)", "",
           "Two rocprofv3 counter runs per launch (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each",
-          "scaled by what the same counter reads for a 1 GiB device-to-device copy",
-          f"(fetch factor {cal['FETCH_SIZE']:.3f}, write factor {cal['WRITE_SIZE']:.3f}). Commands, from /tmp:", "",
+          f"scaled by what the same counter reads for a 1 GiB {kind}",
+          f"(fetch factor {cal['FETCH_SIZE']:.3f}, write factor {cal['WRITE_SIZE']:.3f}){blit_note}.",
+          "Commands, from /tmp:", "",
           "```",
           "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o copy_FETCH_SIZE -- python3 bench.py --copy-calibration",
           "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o <workload>__<key>_FETCH_SIZE -- \\",
           "    python3 bench.py --workload <workload> --profile-launch <key> --no-cpu-baseline",
           "(the same with WRITE_SIZE), then: python3 bench.py --summarize-traffic <dir>",
           "```", "",
-          "FETCH_SIZE counts L2 misses, so operand panels that several XCDs' L2s each fetch count once",
-          "per XCD (the repeats are served by the Infinity Cache).", "",
+          "FETCH_SIZE counts the bytes each XCD's L2 fetches on a miss, from HBM or from the Infinity",
+          "Cache: operand panels that several XCDs' L2s each need count once per XCD, and only the",
+          "first of them comes from HBM. So these are L2 fill bytes, an upper bound of the HBM bytes.", "",
           "| workload | launch | kernels | FETCH_SIZE MiB | WRITE_SIZE MiB | traffic MB (scaled) |", "|---|---|---|---|---|---|"]
     for f in sorted(glob.glob(os.path.join(pmc_dir, "*__*_FETCH_SIZE_counter_collection.csv"))):
         tag = os.path.basename(f)[: -len("_FETCH_SIZE_counter_collection.csv")]

@@ -63,10 +63,13 @@ def test_summarize_traffic(tmp_path):
     b = _bench()
     d = tmp_path / "pmc"
     d.mkdir()
-    # calibration: a 1 GiB copy reads as 2^19 KiB fetched (factor 2) and 2^20 KiB written (factor 1)
-    for c, kib in (("FETCH_SIZE", 2 ** 19), ("WRITE_SIZE", 2 ** 20)):
+    # calibration: the 1 GiB blit reads as 2^19 KiB fetched, the elementwise copy as 2^18 KiB (factor
+    # 4, the one used) and both as 2^20 KiB written (factor 1)
+    for c, blit_kib, elem_kib in (("FETCH_SIZE", 2 ** 19, 2 ** 18), ("WRITE_SIZE", 2 ** 20, 2 ** 20)):
         _write(d / f"copy_{c}_counter_collection.csv",
-               [dict(Dispatch_Id=1, Kernel_Name="__amd_rocclr_copyBuffer", Counter_Name=c, Counter_Value=kib)])
+               [dict(Dispatch_Id=1, Kernel_Name="__amd_rocclr_copyBuffer", Counter_Name=c, Counter_Value=blit_kib),
+                dict(Dispatch_Id=2, Kernel_Name="void at::native::vectorized_elementwise_kernel<4>", Counter_Name=c,
+                     Counter_Value=elem_kib)])
     # a launch of two kernels repeated PROFILE_REPS times after a warm-up step
     for c, per_kernel in (("FETCH_SIZE", (100.0, 50.0)), ("WRITE_SIZE", (10.0, 20.0))):
         rows = [dict(Dispatch_Id=1, Kernel_Name="warm", Counter_Name=c, Counter_Value=999.0)]
@@ -79,5 +82,6 @@ def test_summarize_traffic(tmp_path):
     out.mkdir()
     b.summarize_traffic(str(d), str(out))
     t = json.load(open(out / "traffic.json"))
-    assert t["calibration"]["fetch_factor"] == 2.0 and t["calibration"]["write_factor"] == 1.0
-    assert t["bytes_per_launch"]["wl:quant_x"] == int((150.0 * 2.0 + 30.0 * 1.0) * 1024)
+    assert t["calibration"]["fetch_factor"] == 4.0 and t["calibration"]["write_factor"] == 1.0
+    assert t["calibration"]["blit_fetch_factor"] == 2.0
+    assert t["bytes_per_launch"]["wl:quant_x"] == int((150.0 * 4.0 + 30.0 * 1.0) * 1024)
