@@ -574,7 +574,7 @@ def summarize_traffic(pmc_dir, out_dir=None):
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         rows = _pmc_rows(os.path.join(pmc_dir, f"copy_{c}_counter_collection.csv"))
         blits = [v for k, v in rows.values() if "copyBuffer" in k]
-        elem = [v for k, v in rows.values() if "elementwise" in k]
+        elem = [v for k, v in rows.values() if "elementwise" in k and "Fill" not in k]   # not the inputs' fill
         if blits:
             blit[c] = COPY_BYTES / (blits[-1] * 1024.0)        # counters count KiB
         # the scale factor comes from the elementwise copy (16-byte accesses, like the GEMMs'
@@ -671,7 +671,7 @@ def summarize_mfma(pmc_dir, out_dir=None):
                     agent = {"xcc": int(a["Num_Xcc"]), "simd": int(a["Simd_Count"])}
         disp = {}
         for r in csv.DictReader(open(f)):
-            if "gemm_kernel" not in r["Kernel_Name"]:
+            if "gemm_kernel" not in r["Kernel_Name"] and "gemm_pair_kernel" not in r["Kernel_Name"]:
                 continue
             d = disp.setdefault(int(r["Dispatch_Id"]), {"kernel": r["Kernel_Name"], "ns": int(r["End_Timestamp"]) -
                                                          int(r["Start_Timestamp"])})
