@@ -311,6 +311,7 @@ static sge_status quantize_fp8_amax_impl(const char* what, const void* src, int6
   if ((rows * cols > 0 && !src) || !amax || !scale || !scale_inv || (!scratch && !workspace))
     return fail(SGE_ERR_NULL, "%s: NULL pointer", what);
   if (rows % 16 || cols % 16) return fail(SGE_ERR_SHAPE, "%s: rows and cols must be multiples of 16", what);
+  if (sge_status st = check_strides(what, {cols * 2})) return st;   // 128-row tiles, 32-bit offsets
   if (!aligned16(src) || (q && !aligned16(q)) || (q_t && !aligned16(q_t)))
     return fail(SGE_ERR_ALIGN, "%s: pointers must be 16-byte aligned", what);
   const Range in = range_of(src, rows, cols, cols, 2);
@@ -360,6 +361,7 @@ sge_status sge_quantize_mxfp8(const void* src, int64_t rows, int64_t cols, uint8
   if (rows * cols > 0 && !src) return fail(SGE_ERR_NULL, "quantize_mxfp8: src is NULL");
   if (cols % 32 || (want_col && rows % 32))
     return fail(SGE_ERR_SHAPE, "quantize_mxfp8: cols (and rows, for the columnwise copy) must be multiples of 32");
+  if (sge_status st = check_strides("quantize_mxfp8", {cols * 2})) return st;   // 128-row tiles, 32-bit offsets
   if (!aligned16(src) || (q_row && !aligned16(q_row)) || (q_colT && !aligned16(q_colT)))
     return fail(SGE_ERR_ALIGN, "quantize_mxfp8: pointers must be 16-byte aligned");
   const Range in = range_of(src, rows, cols, cols, 2);
@@ -632,6 +634,7 @@ sge_status sge_quantize_mxfp8_grouped(const void* src, int64_t T, int64_t cols, 
     return fail(SGE_ERR_NULL, "quantize_mxfp8_grouped: q_row and s_row go together");
   if (T * cols > 0 && !src) return fail(SGE_ERR_NULL, "quantize_mxfp8_grouped: src is NULL");
   if (cols % 32) return fail(SGE_ERR_SHAPE, "quantize_mxfp8_grouped: cols must be a multiple of 32");
+  if (sge_status st = check_strides("quantize_mxfp8_grouped", {cols * 2})) return st;   // 128-row tiles, 32-bit offsets
   if (ld % SGE_MX_TOKEN_ALIGN || ld < sge_mx_token_capacity(T, G))
     return fail(SGE_ERR_SHAPE, "quantize_mxfp8_grouped: ld=%lld must be a multiple of %d and >= sge_mx_token_capacity(T, G)=%lld",
                 (long long)ld, SGE_MX_TOKEN_ALIGN, (long long)sge_mx_token_capacity(T, G));
@@ -804,6 +807,7 @@ sge_status sge_quantize_fp8_grouped(const void* src, int64_t rows, int64_t cols,
   if (!q && !q_t) return fail(SGE_ERR_NULL, "quantize_fp8_grouped: no output requested");
   if (rows * cols > 0 && !src) return fail(SGE_ERR_NULL, "quantize_fp8_grouped: src is NULL");
   if (cols % 16) return fail(SGE_ERR_SHAPE, "quantize_fp8_grouped: cols must be a multiple of 16");
+  if (sge_status st = check_strides("quantize_fp8_grouped", {cols * 2})) return st;   // 128-row tiles, 32-bit offsets
   if (!layout && (rows % G || (rows / G) % 128))
     return fail(SGE_ERR_SHAPE, "quantize_fp8_grouped: without a layout, rows / G must be a whole multiple of 128");
   int64_t npos = rows;

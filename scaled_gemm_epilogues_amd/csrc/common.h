@@ -12,6 +12,15 @@ typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 
 constexpr int kWave = 64;
 
+constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past num_records: the load returns zeros
+
+// Buffer resource over [base, base + bytes); loads beyond it read as zero, stores beyond it are
+// dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7FFFFF00 ? 0x7FFFFF00 : (bytes < 0 ? 0 : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
 // bf16 bit pattern -> fp32 (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t two) { return __builtin_bit_cast(float, two << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t two) { return __builtin_bit_cast(float, two & 0xFFFF0000u); }

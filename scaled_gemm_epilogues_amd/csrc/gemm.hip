@@ -135,13 +135,6 @@ __device__ __forceinline__ void slot_to_group(uint32_t* slot, float* amax, int g
 
 typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 
-constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past num_records: the load returns zeros
-
-// Buffer resource over [base, base + bytes); loads beyond it read as zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = bytes > 0x7FFFFF00 ? 0x7FFFFF00 : (bytes < 0 ? 0 : (int)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
-}
 
 // The same resource as four dwords, for the direct-to-LDS copies issued from inline asm.
 typedef int i32x4 __attribute__((ext_vector_type(4)));

@@ -73,6 +73,22 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const uint16
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
 
+// The 16-byte chunks at column c of rows lr0 + 32k (k = 0..3) of a 128-row tile whose first row
+// is r0 and which has nrows rows (rows past them, and columns past cols, read as zeros): branch-
+// free buffer loads, so all four are in flight together. Offsets fit in 31 bits (the callers
+// refuse rows longer than 2^22 elements).
+__device__ __forceinline__ void load_rows4(const uint16_t* src, int64_t r0, int64_t nrows, int64_t cols, int64_t c,
+                                          int lr0, uint4 (&v)[4]) {
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + r0 * cols, (nrows < 128 ? nrows : 128) * cols * 2);
+  const uint32_t cb = c < cols ? (uint32_t)(c * 2) : kOOB;
+  const uint32_t rb = (uint32_t)(cols * 2);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const v4i x = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(cb + (uint32_t)(lr0 + 32 * k) * rb), 0, 0);
+    v[k] = make_uint4((uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]);
+  }
+}
+
 int amax_partial_blocks(int64_t n) {
   const int64_t want = (n / 8 + kAmaxThreads * 8 - 1) / (kAmaxThreads * 8);
   return (int)(want < 1 ? 1 : (want > 1024 ? 1024 : want));
@@ -202,13 +218,15 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(
   for (int64_t it = blockIdx.x; it < ntiles; it += gridDim.x) {
     const int64_t tile_id = ntiles - 1 - it;
     const int64_t r0 = (tile_id / tc) * kQR, c0 = (tile_id % tc) * kQC;
+    uint4 vv[4];
+    load_rows4(src, r0, rows - r0, cols, c0 + cchunk * 8, rsub, vv);
 #pragma unroll
     for (int pass = 0; pass < kQR / 32; ++pass) {
       const int lr = rsub + 32 * pass;
       const int64_t r = r0 + lr, c = c0 + cchunk * 8;
       uint32_t b[4] = {0, 0, 0, 0};
       if (r < rows && c < cols) {
-        const uint4 v = *reinterpret_cast<const uint4*>(src + r * cols + c);
+        const uint4 v = vv[pass];
         b[0] = e4m3x2(bf16_lo(v.x) * scale, bf16_hi(v.x) * scale);
         b[1] = e4m3x2(bf16_lo(v.y) * scale, bf16_hi(v.y) * scale);
         b[2] = e4m3x2(bf16_lo(v.z) * scale, bf16_hi(v.z) * scale);
@@ -299,12 +317,12 @@ __global__ __launch_bounds__(MxTile<WIDE>::kThreads) void quantize_mxfp8_kernel(
   uint32_t ab[4][8];
   uint32_t x_sign[4];    // bit e: sign of element e
   bool ok[4];
+  uint4 vv[4];
+  load_rows4(src, r0, nrows, cols, c, lr, vv);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int64_t r = r0 + lr + 32 * k;
     ok[k] = lr + 32 * k < nrows && c < cols;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (ok[k]) v = *reinterpret_cast<const uint4*>(src + r * cols + c);
+    const uint4 v = vv[k];
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     x_sign[k] = 0;
 #pragma unroll
@@ -432,15 +450,18 @@ __global__ __launch_bounds__(256) void amax_grouped_kernel(const uint16_t* __res
   if (!group_tile(layout, G, rows, p0, g, r0, nrows)) return;   // block-uniform
   const int t = threadIdx.x;
   const int64_t c = c0 + (t & 63) * 8;
+  // Branch-free buffer loads over the tile's existing rows (the rest, and columns past the end,
+  // read as zeros, which leave a magnitude maximum unchanged), so a thread's loads are all in
+  // flight together. Offsets fit in 31 bits: 128 rows of a row at most 2^22 bf16 long.
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + r0 * cols, (nrows < kQR ? nrows : kQR) * cols * 2);
+  const uint32_t cb = c < cols ? (uint32_t)(c * 2) : kOOB;
+  const uint32_t rb = (uint32_t)(cols * 2);
   uint32_t m = 0;
-  if (c < cols) {
 #pragma unroll 8
-    for (int lr = t >> 6; lr < kQR; lr += 4) {
-      if (lr < nrows) {
-        const uint32_t x = absmax_bits8(*reinterpret_cast<const uint4*>(src + (r0 + lr) * cols + c));
-        m = m > x ? m : x;
-      }
-    }
+  for (int lr = t >> 6; lr < kQR; lr += 4) {
+    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(cb + (uint32_t)lr * rb), 0, 0);
+    const uint32_t x = absmax_bits8(make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]));
+    m = m > x ? m : x;
   }
   m = block_max_u32(m, red);
   // non-negative floats order like their bit patterns: an integer max of (bf16 bits << 16)
@@ -464,7 +485,9 @@ __global__ __launch_bounds__(256) void quantize_fp8_grouped_kernel(
     }
   }
   const int64_t tc = (cols + kQC - 1) / kQC;
-  const int64_t tid = xcd_tile(blockIdx.x, gridDim.x);
+  // XCD-contiguous ranges, each walked from its end: the amax pass went the other way, so the
+  // tiles it read last (still in the last-level cache) come first
+  const int64_t tid = gridDim.x - 1 - xcd_tile(blockIdx.x, gridDim.x);
   const int64_t p0 = (tid / tc) * kQR;
   const int64_t c0 = (tid % tc) * kQC;
   int g;
@@ -474,13 +497,15 @@ __global__ __launch_bounds__(256) void quantize_fp8_grouped_kernel(
   fp8_scales(amax_g[g], scale, scale_inv);
   const int cchunk = t & 7;
   const int rsub = t >> 3;
+  uint4 vv[4];
+  load_rows4(src, r0, nrows, cols, c0 + cchunk * 8, rsub, vv);
 #pragma unroll
   for (int pass = 0; pass < kQR / 32; ++pass) {
     const int lr = rsub + 32 * pass;
     const int64_t r = r0 + lr, c = c0 + cchunk * 8;
     uint32_t b[4] = {0, 0, 0, 0};
     if (lr < nrows && c < cols) {
-      const uint4 v = *reinterpret_cast<const uint4*>(src + r * cols + c);
+      const uint4 v = vv[pass];
       b[0] = e4m3x2(bf16_lo(v.x) * scale, bf16_hi(v.x) * scale);
       b[1] = e4m3x2(bf16_lo(v.y) * scale, bf16_hi(v.y) * scale);
       b[2] = e4m3x2(bf16_lo(v.z) * scale, bf16_hi(v.z) * scale);

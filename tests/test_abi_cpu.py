@@ -531,6 +531,32 @@ def test_shapes_beyond_32bit_tile_addressing_are_refused(sge):
     assert "32-bit" not in lib.sge_last_error_message().decode()
 
 
+def test_quantizers_refuse_rows_beyond_32bit_tile_addressing(sge):
+    """The quantizers address a tile of 128 rows through one buffer resource with 32-bit byte
+    offsets: a row longer than that allows gives SGE_ERR_SHAPE (before any HIP call); one within
+    it passes that check and fails a later one (the fake pointers overlap), so nothing launches."""
+    lib = sge._lib
+    big, fits = 1 << 23, 1 << 21                          # bf16 elements per row
+    ld = sge.mx_token_capacity(100, 4)
+    for cols, refused in ((big, True), (fits, False)):
+        calls = (
+            lambda: lib.sge_quantize_fp8_amax(FAKE, 16, cols, FAKE * 8, None, FAKE * 16, FAKE * 17, FAKE * 18,
+                                              FAKE * 32, 1 << 20, None),
+            lambda: lib.sge_quantize_fp8_amax_noalloc(FAKE, 16, cols, FAKE * 8, None, FAKE * 16, FAKE * 17,
+                                                      FAKE * 18, None),
+            lambda: lib.sge_quantize_mxfp8(FAKE, 32, cols, FAKE * 8, FAKE * 9, None, None, None),
+            lambda: lib.sge_quantize_mxfp8_grouped(FAKE, 100, cols, 4, FAKE * 64, ld, None, None, FAKE * 80,
+                                                   FAKE * 96, None),
+            lambda: lib.sge_quantize_fp8_grouped(FAKE, 100, cols, 4, FAKE * 64, ld, FAKE * 72, None, FAKE * 88,
+                                                 FAKE * 89, FAKE * 90, None, FAKE * 91, 64, None),
+        )
+        for call in calls:
+            st = call()
+            msg = lib.sge_last_error_message().decode()
+            assert st != sge.OK, msg
+            assert (st == sge.ERR_SHAPE and "32-bit" in msg) == refused, (st, msg)
+
+
 def test_quantize_fp8_amax_noalloc_validation_errors(sge):
     """The no-allocation quantizer validates like the workspace call, before any HIP call."""
     lib = sge._lib
