@@ -6,8 +6,9 @@
 //
 // Forward: one row per block iteration (grid-stride over rows, at most kNormBlocks blocks),
 // 256 threads, thread t owning the 8-column chunks 8t + 2048i. Statistics in fp32 with a
-// fixed-order block reduction (LayerNorm's variance in a second pass around the mean); the
-// output is rounded once to bf16. With AMAX each block also reduces the bf16 output's
+// fixed-order block reduction (LayerNorm's variance in a second pass around the mean, over the
+// row held in registers; the block's next row is loaded meanwhile); the output is rounded
+// once to bf16. With AMAX each block also reduces the bf16 output's
 // magnitude into one partial (the current-scaling quantize pass finishes it); with MXROW the
 // rowwise MXFP8 copy of the bf16 output is written from registers (four adjacent lanes hold a
 // 32-column block), the bytes the standalone quantizer writes for the same bf16 output.
@@ -16,7 +17,10 @@
 // per row the two means (of d*xhat, and of d for LayerNorm) are block-reduced, dx is written
 // in bf16, and each block keeps its own column sums of dz*xhat and dz in registers, stored
 // once as fp32 partials; a second kernel adds the partials of all blocks in a fixed order
-// (deterministic dgamma / dbeta).
+// (deterministic dgamma / dbeta). Rows stay in registers between passes, and a block loads its
+// next row while working the current one.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -39,17 +43,37 @@ __device__ __forceinline__ float block_sum_f32(float v, float* red) {
   return s;
 }
 
-__device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+__device__ __forceinline__ float bf16_at(const uint4& u, int e) {
+  const uint32_t w = e < 2 ? u.x : (e < 4 ? u.y : (e < 6 ? u.z : u.w));
+  return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+// One row's NCH 16-byte chunks per thread (columns 8t + 2048i) as branch-free buffer loads:
+// chunks past the row, and every chunk of a row past the end (nbytes 0), read as zeros, so all
+// of them are in flight together. A resource per row keeps the offsets 32-bit.
+template <int NCH>
+__device__ __forceinline__ void load_row(const uint16_t* base, int64_t cols, bool exists, uint4 (&u)[NCH]) {
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, exists ? cols * 2 : 0);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    v[2 * e] = bf16_lo(w[e]);
-    v[2 * e + 1] = bf16_hi(w[e]);
+  for (int i = 0; i < NCH; ++i) {
+    const int64_t c = 8 * (int64_t)threadIdx.x + 2048 * (int64_t)i;
+    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rs, c < cols ? (int)(c * 2) : (int)kOOB, 0, 0);
+    u[i] = make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
   }
 }
 
-template <bool LN, bool AMAX, bool MXROW>
+template <int NCH>
+__device__ __forceinline__ void load_vec(const uint16_t* p, int64_t cols, uint4 (&u)[NCH]) {
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int64_t c = 8 * (int64_t)threadIdx.x + 2048 * (int64_t)i;
+    u[i] = c < cols ? *reinterpret_cast<const uint4*>(p + c) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// NCH: chunks of 8 columns per thread (cols <= 2048 * NCH). The row stays in registers between
+// the statistics and the output, and the block's next row is loaded while this one is worked.
+template <bool LN, bool AMAX, bool MXROW, int NCH>
 __global__ __launch_bounds__(kNormThreads) void norm_fwd_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, const uint16_t* __restrict__ beta,
     int64_t rows, int64_t cols, float eps, int zero_centered, uint16_t* __restrict__ y, float* __restrict__ mu_out,
@@ -57,54 +81,47 @@ __global__ __launch_bounds__(kNormThreads) void norm_fwd_kernel(
     uint8_t* __restrict__ s_row) {
   __shared__ float red[kNormThreads / 64];
   const int t = threadIdx.x;
-  const int nch = (int)((cols / 8 + kNormThreads - 1) / kNormThreads);   // uniform over the block
   const float gofs = zero_centered ? 1.0f : 0.0f;
   const float inv_cols = 1.0f / (float)cols;
+  uint4 gq[NCH], bq[NCH];
+  load_vec<NCH>(gamma, cols, gq);
+  if constexpr (LN) load_vec<NCH>(beta, cols, bq);
   uint32_t amax = 0;
-  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-    const uint16_t* xr = x + r * cols;
+  auto work = [&](int64_t r, const uint4 (&ux)[NCH]) {
     float mu = 0.0f;
     if constexpr (LN) {
       float s = 0.0f;
-      for (int i = 0; i < nch; ++i) {
-        const int64_t c = 8 * (int64_t)t + 2048 * (int64_t)i;
-        if (c < cols) {
-          float v[8];
-          load8(xr + c, v);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) s += v[e];
-        }
-      }
+      for (int i = 0; i < NCH; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += bf16_at(ux[i], e);   // zeros past the row
       mu = block_sum_f32(s, red) * inv_cols;
     }
     float ss = 0.0f;
-    for (int i = 0; i < nch; ++i) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
       const int64_t c = 8 * (int64_t)t + 2048 * (int64_t)i;
       if (c < cols) {
-        float v[8];
-        load8(xr + c, v);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float d = v[e] - mu;
+          const float d = bf16_at(ux[i], e) - mu;
           ss += d * d;
         }
       }
     }
     const float rs = 1.0f / sqrtf(block_sum_f32(ss, red) * inv_cols + eps);
-    for (int i = 0; i < nch; ++i) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
       const int64_t c = 8 * (int64_t)t + 2048 * (int64_t)i;
+      if (c >= cols && !MXROW) continue;
       const bool ok = c < cols;
       v4i vy = {0, 0, 0, 0};
       if (ok) {
-        float v[8], g[8], b[8];
-        load8(xr + c, v);
-        load8(gamma + c, g);
-        if constexpr (LN) load8(beta + c, b);
         float o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          o[e] = (v[e] - mu) * rs * (g[e] + gofs);
-          if constexpr (LN) o[e] += b[e];
+          o[e] = (bf16_at(ux[i], e) - mu) * rs * (bf16_at(gq[i], e) + gofs);
+          if constexpr (LN) o[e] += bf16_at(bq[i], e);
         }
         vy = v4i{(int)pack_bf16x2(o[0], o[1]), (int)pack_bf16x2(o[2], o[3]), (int)pack_bf16x2(o[4], o[5]),
                  (int)pack_bf16x2(o[6], o[7])};
@@ -131,6 +148,17 @@ __global__ __launch_bounds__(kNormThreads) void norm_fwd_kernel(
       if (mu_out) mu_out[r] = mu;
       rsigma_out[r] = rs;
     }
+  };
+  const int64_t G = gridDim.x;
+  uint4 ua[NCH], ub[NCH];
+  int64_t r = blockIdx.x;
+  load_row<NCH>(x + r * cols, cols, r < rows, ua);
+  for (; r < rows; r += 2 * G) {
+    load_row<NCH>(x + (r + G) * cols, cols, r + G < rows, ub);
+    work(r, ua);
+    if (r + G >= rows) break;
+    load_row<NCH>(x + (r + 2 * G) * cols, cols, r + 2 * G < rows, ua);
+    work(r + G, ub);
   }
   if constexpr (AMAX) {
     amax = wave_max(amax);
@@ -152,51 +180,44 @@ __global__ __launch_bounds__(kNormThreads) void norm_bwd_kernel(
     const float* __restrict__ rsigma_in, const uint16_t* __restrict__ gamma, int64_t rows, int64_t cols,
     int zero_centered, uint16_t* __restrict__ dx, float* __restrict__ dg_part, float* __restrict__ db_part) {
   // NCH: chunks of 8 columns per thread (cols <= 2048 * NCH); the row's dz and x stay in
-  // registers (as loaded bf16) between the reduction pass and the dx pass.
+  // registers (as loaded bf16) between the reduction pass and the dx pass, and the block's next
+  // row (with its statistics) is loaded while this one is worked.
   __shared__ float red[kNormThreads / 64];
   const int t = threadIdx.x;
   const float gofs = zero_centered ? 1.0f : 0.0f;
   const float inv_cols = 1.0f / (float)cols;
-  float pg[NCH][8], pb[NCH][8], g[NCH][8];
+  float pg[NCH][8], pb[NCH][8];
+  uint4 gq[NCH];
+  load_vec<NCH>(gamma, cols, gq);
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int64_t c = 8 * (int64_t)t + 2048 * (int64_t)i;
+  for (int i = 0; i < NCH; ++i)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pg[i][e] = pb[i][e] = g[i][e] = 0.0f;
-    if (c < cols) {
-      load8(gamma + c, g[i]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) g[i][e] += gofs;
-    }
-  }
-  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-    const float rs = rsigma_in[r];
-    const float m = LN ? mu_in[r] : 0.0f;
-    const uint16_t* dzr = dz + r * cols;
-    const uint16_t* xr = x + r * cols;
-    uint4 ud[NCH], ux[NCH];
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int64_t c = 8 * (int64_t)t + 2048 * (int64_t)i;
-      ud[i] = ux[i] = make_uint4(0, 0, 0, 0);
-      if (c < cols) {
-        ud[i] = *reinterpret_cast<const uint4*>(dzr + c);
-        ux[i] = *reinterpret_cast<const uint4*>(xr + c);
-      }
-    }
+    for (int e = 0; e < 8; ++e) pg[i][e] = pb[i][e] = 0.0f;
+  struct Row {
+    uint4 d[NCH], x[NCH];
+    float rs, m;
+  };
+  auto load = [&](int64_t r, Row& w) {
+    const bool ex = r < rows;
+    load_row<NCH>(dz + r * cols, cols, ex, w.d);
+    load_row<NCH>(x + r * cols, cols, ex, w.x);
+    const int64_t rr = ex ? r : 0;                      // a row that exists (rows > 0 here)
+    w.rs = rsigma_in[rr];
+    w.m = LN ? mu_in[rr] : 0.0f;
+  };
+  auto work = [&](int64_t r, const Row& w) {
+    const float rs = w.rs, m = w.m;
     float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const uint32_t wd[4] = {ud[i].x, ud[i].y, ud[i].z, ud[i].w}, wx[4] = {ux[i].x, ux[i].y, ux[i].z, ux[i].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float d = (e & 1) ? bf16_hi(wd[e >> 1]) : bf16_lo(wd[e >> 1]);
-        const float v = (e & 1) ? bf16_hi(wx[e >> 1]) : bf16_lo(wx[e >> 1]);
-        const float xh = (v - m) * rs;
-        const float dg = d * g[i][e];
+        const float d = bf16_at(w.d[i], e);             // zero past the row
+        const float xh = (bf16_at(w.x[i], e) - m) * rs;
+        const float dg = d * (bf16_at(gq[i], e) + gofs);
         s1 += dg * xh;
         if constexpr (LN) s2 += dg;
-        pg[i][e] += d * xh;                              // zero for columns past the row (d = 0)
+        pg[i][e] += d * xh;
         if constexpr (LN) pb[i][e] += d;
       }
     }
@@ -206,20 +227,28 @@ __global__ __launch_bounds__(kNormThreads) void norm_bwd_kernel(
     for (int i = 0; i < NCH; ++i) {
       const int64_t c = 8 * (int64_t)t + 2048 * (int64_t)i;
       if (c < cols) {
-        const uint32_t wd[4] = {ud[i].x, ud[i].y, ud[i].z, ud[i].w}, wx[4] = {ux[i].x, ux[i].y, ux[i].z, ux[i].w};
         float o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float d = (e & 1) ? bf16_hi(wd[e >> 1]) : bf16_lo(wd[e >> 1]);
-          const float v = (e & 1) ? bf16_hi(wx[e >> 1]) : bf16_lo(wx[e >> 1]);
-          const float xh = (v - m) * rs;
-          o[e] = rs * (d * g[i][e] - m2 - xh * m1);
+          const float xh = (bf16_at(w.x[i], e) - m) * rs;
+          o[e] = rs * (bf16_at(w.d[i], e) * (bf16_at(gq[i], e) + gofs) - m2 - xh * m1);
         }
         *reinterpret_cast<v4i*>(dx + r * cols + c) =
             v4i{(int)pack_bf16x2(o[0], o[1]), (int)pack_bf16x2(o[2], o[3]), (int)pack_bf16x2(o[4], o[5]),
                 (int)pack_bf16x2(o[6], o[7])};
       }
     }
+  };
+  const int64_t G = gridDim.x;
+  Row ra, rb;
+  int64_t r = blockIdx.x;
+  load(r, ra);
+  for (; r < rows; r += 2 * G) {
+    load(r + G, rb);
+    work(r, ra);
+    if (r + G >= rows) break;
+    load(r + 2 * G, ra);
+    work(r + G, rb);
   }
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
@@ -237,14 +266,28 @@ __global__ __launch_bounds__(kNormThreads) void norm_bwd_kernel(
   }
 }
 
-// out[c] = bf16(sum over parts b, in order, of part[b][c]).
-__global__ __launch_bounds__(256) void colsum_parts_kernel(const float* __restrict__ part, int nparts, int64_t cols,
-                                                          uint16_t* __restrict__ out) {
-  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= cols) return;
+// out[c] = bf16 of the sum over parts b of part[b][c] in a fixed order: eight groups of threads
+// per column each add the parts b = g, g + 8, g + 16, ... in turn (loads in flight together),
+// then the eight group sums are added in group order.
+constexpr int kCsCols = 32, kCsGroups = 8;
+__global__ __launch_bounds__(kCsCols * kCsGroups) void colsum_parts_kernel(const float* __restrict__ part, int nparts,
+                                                                         int64_t cols, uint16_t* __restrict__ out) {
+  __shared__ float red[kCsGroups][kCsCols];
+  const int tx = threadIdx.x % kCsCols, ty = threadIdx.x / kCsCols;
+  const int64_t c = (int64_t)blockIdx.x * kCsCols + tx;
   float s = 0.0f;
-  for (int b = 0; b < nparts; ++b) s += part[(int64_t)b * cols + c];
-  out[c] = f32_to_bf16(s);
+  if (c < cols) {
+#pragma unroll 8
+    for (int b = ty; b < nparts; b += kCsGroups) s += part[(int64_t)b * cols + c];
+  }
+  red[ty][tx] = s;
+  __syncthreads();
+  if (ty == 0 && c < cols) {
+    float t = red[0][tx];
+#pragma unroll
+    for (int g = 1; g < kCsGroups; ++g) t += red[g][tx];
+    out[c] = f32_to_bf16(t);
+  }
 }
 
 int norm_blocks(int64_t rows) { return (int)(rows < kNormBlocks ? (rows < 1 ? 1 : rows) : kNormBlocks); }
@@ -256,21 +299,31 @@ hipError_t launch_norm_fwd(bool ln, const uint16_t* x, const uint16_t* gamma, co
   if (rows == 0) return hipSuccess;
   const dim3 grid(norm_blocks(rows)), block(kNormThreads);
   const bool am = amax_part != nullptr, mx = q_row != nullptr;
-#define SGE_NORM_FWD(L, A, M)                                                                            \
-  hipLaunchKernelGGL((norm_fwd_kernel<L, A, M>), grid, block, 0, s, x, gamma, beta, rows, cols, eps, zc, y, mu, \
+  const int64_t nch = (cols / 8 + kNormThreads - 1) / kNormThreads;
+  auto go = [&](auto lnc, auto amc, auto mxc) {
+    constexpr bool L = decltype(lnc)::value, A = decltype(amc)::value, M = decltype(mxc)::value;
+#define SGE_NORM_FWD(C)                                                                                          \
+  hipLaunchKernelGGL((norm_fwd_kernel<L, A, M, C>), grid, block, 0, s, x, gamma, beta, rows, cols, eps, zc, y, mu, \
                      rsigma, amax_part, q_row, s_row)
-  if (ln) {
-    if (am && mx) SGE_NORM_FWD(true, true, true);
-    else if (am) SGE_NORM_FWD(true, true, false);
-    else if (mx) SGE_NORM_FWD(true, false, true);
-    else SGE_NORM_FWD(true, false, false);
-  } else {
-    if (am && mx) SGE_NORM_FWD(false, true, true);
-    else if (am) SGE_NORM_FWD(false, true, false);
-    else if (mx) SGE_NORM_FWD(false, false, true);
-    else SGE_NORM_FWD(false, false, false);
-  }
+    if (nch <= 1) SGE_NORM_FWD(1);
+    else if (nch <= 2) SGE_NORM_FWD(2);
+    else if (nch <= 4) SGE_NORM_FWD(4);
+    else SGE_NORM_FWD(8);
 #undef SGE_NORM_FWD
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  if (ln) {
+    if (am && mx) go(T{}, T{}, T{});
+    else if (am) go(T{}, T{}, F{});
+    else if (mx) go(T{}, F{}, T{});
+    else go(T{}, F{}, F{});
+  } else {
+    if (am && mx) go(F{}, T{}, T{});
+    else if (am) go(F{}, T{}, F{});
+    else if (mx) go(F{}, F{}, T{});
+    else go(F{}, F{}, F{});
+  }
   return hipGetLastError();
 }
 
@@ -296,9 +349,9 @@ hipError_t launch_norm_bwd(bool ln, const uint16_t* dz, const uint16_t* x, const
     hipError_t e = launch_fill_f32_zero(part, (int64_t)nb * cols * 2, s);   // no rows: zero gradients
     if (e != hipSuccess) return e;
   }
-  const dim3 g((unsigned)((cols + 255) / 256));
-  hipLaunchKernelGGL(colsum_parts_kernel, g, dim3(256), 0, s, dg_part, nb, cols, dgamma);
-  if (ln) hipLaunchKernelGGL(colsum_parts_kernel, g, dim3(256), 0, s, db_part, nb, cols, dbeta);
+  const dim3 g((unsigned)((cols + kCsCols - 1) / kCsCols));
+  hipLaunchKernelGGL(colsum_parts_kernel, g, dim3(kCsCols * kCsGroups), 0, s, dg_part, nb, cols, dgamma);
+  if (ln) hipLaunchKernelGGL(colsum_parts_kernel, g, dim3(kCsCols * kCsGroups), 0, s, db_part, nb, cols, dbeta);
   return hipGetLastError();
 }
 
