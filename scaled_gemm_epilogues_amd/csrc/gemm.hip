@@ -694,11 +694,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
       }
     };
     // Fragment f of tile t: A0, B0.., A1.. (the order the MFMAs use them): 32 bytes from two
-    // 16-byte chunks of a 64-byte row. MXFP8: also the dword of the row's E8M0 bytes that holds tile t's two blocks (the two lane
-    // halves read the same dword: a broadcast, not a bank conflict); the tile that uses it
-    // shifts it by 8 bits in the upper lane half and selects byte 2 * (t % 2) in the MFMA.
+    // 16-byte chunks of a 64-byte row. MXFP8: also the dword of the row's E8M0 bytes that holds
+    // the blocks of tiles t and t + 1 for even t (the two lane halves read the same dword: a
+    // broadcast, not a bank conflict); the even tile shifts it by 8 bits in the upper lane half,
+    // the odd tile after it takes that shifted copy, and each selects byte 2 * (t % 2) in the MFMA.
     auto frag = [&](int t, int f, Frag (&fa_)[KS][WMF], Frag (&fb_)[KS][WNF], uint32_t (&sa_)[WMF],
-                    uint32_t (&sb_)[WNF]) {
+                    uint32_t (&sb_)[WNF], auto odd_t) {
       const uint8_t* buf = stage(t);
       const int ks = f / kFPS, g = f % kFPS;
       const bool is_a = g == 0 || g > WNF;
@@ -713,10 +714,17 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
       if (is_a) fa_[ks][idx] = v;
       else fb_[ks][idx] = v;
       if constexpr (kMX) {
-        const uint8_t* sl = sc_st + ((t / kGrpTiles) & 1) * SC_GROUP;
-        const uint32_t e = *reinterpret_cast<const uint32_t*>(sl + ((is_a ? 0 : BM) + r) * 16 + 4 * ((t % kGrpTiles) >> 1));
-        if (is_a) sa_[idx] = e;
-        else sb_[idx] = e;
+        if constexpr (decltype(odd_t)::value) {
+          // an odd tile's two blocks sit in the dword its even predecessor read (and shifted)
+          if (is_a) sa_[idx] = sa2[0][idx];
+          else sb_[idx] = sb2[0][idx];
+        } else {
+          const uint8_t* sl = sc_st + ((t / kGrpTiles) & 1) * SC_GROUP;
+          const uint32_t e =
+              *reinterpret_cast<const uint32_t*>(sl + ((is_a ? 0 : BM) + r) * 16 + 4 * ((t % kGrpTiles) >> 1));
+          if (is_a) sa_[idx] = e;
+          else sb_[idx] = e;
+        }
       }
     };
     auto mma1 = [&](const Frag (&fa_)[KS][WMF], const Frag (&fb_)[KS][WNF], const uint32_t (&sa_)[WMF],
@@ -761,15 +769,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
           for (int c = 0; c < CPT; ++c) copy(t, c);
       wait_tile(0, KT - 1 < NST - 1 ? KT - 1 : NST - 1);
 #pragma unroll
-      for (int f = 0; f < kFT; ++f) frag(0, f, fa2[0], fb2[0], sa2[0], sb2[0]);
+      for (int f = 0; f < kFT; ++f) frag(0, f, fa2[0], fb2[0], sa2[0], sb2[0], std::false_type{});
     }
     // Tile kt (parity P): tile kt + NST exists (steady) or not (tail).
     auto tile = [&](int kt, auto par, auto steady_c) {
       constexpr int P = decltype(par)::value, Q = P ^ 1;
       constexpr bool steady = decltype(steady_c)::value;
       const std::integral_constant<int, P> odd{};        // tile kt is odd exactly when P == 1
-      if constexpr (kMX) {                               // the upper lane half's block is the next byte
-#pragma unroll
+      if constexpr (kMX && P == 0) {                     // the upper lane half's block is the next byte
+#pragma unroll                                           // (odd tiles copy the shifted dword)
         for (int i = 0; i < WMF; ++i) sa2[P][i] >>= 8 * lhalf;
 #pragma unroll
         for (int j = 0; j < WNF; ++j) sb2[P][j] >>= 8 * lhalf;
@@ -789,10 +797,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
         const int s_ = q - kHead;
         if constexpr (steady) {
           if (s_ < CPT) copy(kt + NST, s_);
-          if (s_ < kFT) frag(kt + 1, s_, fa2[Q], fb2[Q], sa2[Q], sb2[Q]);
+          if (s_ < kFT) frag(kt + 1, s_, fa2[Q], fb2[Q], sa2[Q], sb2[Q], std::integral_constant<bool, Q == 1>{});
         } else {
           if (s_ < CPT && kt + NST < KT) copy(kt + NST, s_);
-          if (s_ < kFT && kt + 1 < KT) frag(kt + 1, s_, fa2[Q], fb2[Q], sa2[Q], sb2[Q]);
+          if (s_ < kFT && kt + 1 < KT) frag(kt + 1, s_, fa2[Q], fb2[Q], sa2[Q], sb2[Q], std::integral_constant<bool, Q == 1>{});
         }
         __builtin_amdgcn_sched_barrier(0);
       }
