@@ -137,3 +137,31 @@ def test_norm_backward(kind, shape):
     assert_close(host_f64(dg), ref["dgamma"], TAU_BF16, what="dgamma", **KW)
     if kind == "ln":
         assert_close(host_f64(db), ref["dbeta"], TAU_BF16, what="dbeta", **KW)
+
+
+@pytest.mark.parametrize("kind", ["rms", "ln"])
+def test_norm_backward_bitwise_repeatable(kind):
+    """dgamma / dbeta are sums of per-block partials in a fixed order (and dx a per-row block
+    reduction in a fixed order): two runs on the same inputs give the same bits. 3000 rows give
+    every one of the 512 blocks several rows (the next-row loads alternate buffers)."""
+    R, C = 3000, 4096
+    print(f"case norm bwd repeatable {kind} {R}x{C}", flush=True)
+    d = _inputs(R, C, 23)
+    k = sge.NORM_LAYER if kind == "ln" else sge.NORM_RMS
+    f = _run_fwd(kind, d, False, 1e-5)
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    X, DZ, gam = dev_bf16(d["x"]), dev_bf16(d["dz"]), dev_bf16(d["gamma"])
+    ws = torch.empty(sge.norm_bwd_workspace_size(R, C), dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(2):
+        dx, dg, db = torch.empty(R, C, **bf), torch.empty(C, **bf), torch.empty(C, **bf)
+        ws.fill_(0xFF)                                   # partials rewritten on every run
+        sge.norm_bwd(k, DZ, X, f["rsigma"], gam, dx, dg, ws, mu=f["mu"] if kind == "ln" else None,
+                     dbeta=db if kind == "ln" else None, zero_centered=False)
+        torch.cuda.synchronize()
+        outs.append([host_bits(t) for t in ((dx, dg, db) if kind == "ln" else (dx, dg))])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    ref_f = norm.norm_fwd(kind, d["x"], d["gamma"], d["beta"], 1e-5, False)
+    ref = norm.norm_bwd(kind, d["dz"], d["x"], ref_f["mu"], ref_f["rsigma"], d["gamma"], False)
+    assert_close(host_f64(dg), ref["dgamma"], TAU_BF16, what="dgamma", **KW)
