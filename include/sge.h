@@ -21,6 +21,12 @@
  * matrix as bytes (OCP OFP8 E4M3, max 448); an E8M0 scale array as bytes
  * (2^(s-127)). Leading dimensions are in elements. Base pointers must be
  * 16-byte aligned and leading dimensions a multiple of 16 bytes.
+ *
+ * Size limits: the kernels address a tile (256 rows of a GEMM operand or output, 128 rows of a
+ * quantizer's input) through 32-bit byte offsets from the tile's first row, and a few arrays
+ * (MXFP8 scale arrays, a gated weight's two halves) from one base. A row stride of more than
+ * about 8.3 MB (0x7FFFFF00 / 257 bytes), or such an array of 2^31 bytes or more, gives
+ * SGE_ERR_SHAPE rather than being read as zeros.
  */
 #ifndef SGE_H
 #define SGE_H
