@@ -8,6 +8,7 @@ namespace sge {
 
 typedef __attribute__((__ext_vector_type__(8))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 
 constexpr int kWave = 64;

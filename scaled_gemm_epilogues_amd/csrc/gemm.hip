@@ -14,19 +14,20 @@
 //
 // Design (CDNA4):
 // * 256x256 macro tiles: 8 waves in a 2x4 grid (bf16, E4M3) or 4 waves in a 2x2 grid
-//   (MXFP8); each wave owns WMF x WNF fragments of 32x32 fp32 accumulators
-//   (v_mfma_f32_32x32x16_bf16, or the MX-scaled v_mfma_scale_f32_32x32x64_f8f6f4 for
-//   E4M3 / MXFP8 with E8M0 scales).
+//   (MXFP8); each wave owns WMF x WNF blocks of 32x32 fp32 accumulators, multiplied with
+//   v_mfma_f32_16x16x32_bf16 (four per block and k-step) for bf16, or with the MX-scaled
+//   v_mfma_scale_f32_32x32x64_f8f6f4 for E4M3 / MXFP8 with E8M0 scales.
 // * Tiles are renumbered so each XCD runs a contiguous block of them (its own L2).
 // * Tiles of 128 contraction bytes per operand row (64 bf16 or 128 fp8) move
 //   from HBM straight into LDS with buffer_load ... lds (no staging registers;
-//   out-of-range lanes read zeros), in two LDS stages: the copy of tile k+1 is
-//   in flight while tile k is multiplied. LDS images are XOR-swizzled per 16-B
-//   chunk so fragment reads are free of bank conflicts.
+//   out-of-range lanes read zeros), in two LDS stages (8-bit dense and weight-gradient
+//   GEMMs: four stages of 64 bytes): the copy of a later tile is in flight while a
+//   tile is multiplied. LDS images are laid out (XOR-swizzled 16-B chunks, 16-row
+//   blocks for bf16) so fragment reads are free of bank conflicts.
 // * bf16 operands stored with the contraction dimension outermost (dgrad's W,
 //   wgrad's dy and x) are copied as they are and read with the transposing
 //   ds_read_b64_tr_b16, so dgrad and wgrad read the untransposed tensors.
-// * Fragments of k-step s+1 are read from LDS while the MFMAs of step s run.
+// * Fragments of the next k-step are read from LDS while the MFMAs of the current one run.
 // * The MFMA is issued with B as its first operand, so each lane ends with 4
 //   consecutive output columns per group and stores 8 bytes of bf16 at a time.
 #include <type_traits>
@@ -45,7 +46,7 @@ enum { S_DENSE = 0, S_GROUP_M = 1, S_GROUP_K = 2 };
 constexpr int kRowBytes = 128;   // contraction bytes per LDS row and per k-tile
 
 // Macro tile 256x256. bf16 and E4M3: 2x4 waves (two per SIMD), each owning 4x2 32x32
-// accumulators, so one wave's LDS and barrier waits are covered by the other's MFMAs.
+// accumulator blocks, so one wave's LDS and barrier waits are covered by the other's MFMAs.
 // MXFP8 (more live registers for the E8M0 scales): 2x2 waves, each 4x4 accumulators.
 #ifndef SGE_WAVES_M
 #define SGE_WAVES_M 2
@@ -74,6 +75,14 @@ constexpr int kWavesM = SGE_WAVES_M, kWavesN = SGE_WAVES_N, kFragsM = SGE_FRAGS_
 #endif
 #ifndef SGE_DSWIGLU_BATCH
 #define SGE_DSWIGLU_BATCH 4      // dSwiGLU epilogue chunks whose loads are in flight together
+#endif
+
+#ifndef SGE_BF16_M16
+#define SGE_BF16_M16 1           // bf16 tiles multiply with 16x16x32 MFMAs (else 32x32x16)
+#endif
+
+#ifndef SGE_M16_CPG
+#define SGE_M16_CPG 2            // bf16 16x16x32 loop: tile copies issued after each MFMA group (1, 4 and 8 measured slower)
 #endif
 
 #ifndef SGE_DEEP_8BIT
@@ -159,7 +168,20 @@ __device__ __forceinline__ void lds_copy16(const i32x4& rsrc, const void* lds, u
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
                : "memory", "m0");
 }
+// The same with the LDS byte address given as a wave-uniform 32-bit value (kept in SGPRs).
+__device__ __forceinline__ void lds_copy16_at(const i32x4& rsrc, uint32_t lds_addr, uint32_t voff) {
+  const i32x4 r = {__builtin_amdgcn_readfirstlane(rsrc.x), __builtin_amdgcn_readfirstlane(rsrc.y),
+                   __builtin_amdgcn_readfirstlane(rsrc.z), __builtin_amdgcn_readfirstlane(rsrc.w)};
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(__builtin_amdgcn_readfirstlane(lds_addr)),
+               "v"(voff), "s"(r)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 
 // XOR swizzle of the 16-byte chunks of an LDS row: 128-byte rows use swz(); 64-byte rows (four
 // chunks) flip by (row / 4) % 4, so 16 consecutive rows reading one logical chunk (a phase of a
@@ -170,14 +192,31 @@ __device__ __forceinline__ int swz_rows(int row) {
   else return (row >> 2) & 3;
 }
 
+// 16-byte chunk swizzle of contraction row k of an outer-contiguous bf16 tile (512-byte rows): bits
+// 2-3 from k % 4 spread the four rows one transposing read covers; with 16x16x32 MFMAs the four
+// 16-lane groups read rows k, k + 8, k + 16 and k + 24 (32 bytes each), which bits 1 and 4 (from
+// k / 8 and k / 16) also spread. The weight-gradient GEMM, whose fragments all come from such
+// reads, shows no LDS bank conflicts on MI355X (SQ_LDS_BANK_CONFLICT) beyond its epilogue's.
+__device__ __forceinline__ int tr_swz(int k) {
+  return 4 * (k & 3) ^ (SGE_BF16_M16 ? 2 * ((k >> 3) & 1) ^ 16 * ((k >> 4) & 1) : 0);
+}
+// Inner-contiguous bf16 tiles under 16x16x32 MFMAs are stored in 1-KB blocks: block b holds rows
+// 16 (b / 2) .. + 15 at contraction bytes 64 (b % 2) .. + 63 (one k-step), row i of the block at
+// byte 64 i, its 16-byte chunk c at slot c ^ ((i / 2) % 4). A fragment read (lane l: row l % 16,
+// chunk l / 16) then takes one block; measured on MI355X (LDS timing and SQ_LDS_BANK_CONFLICT) it
+// runs conflict-free, as fast as the 32x32x16 reads of 128-byte rows, while reading 128-byte rows
+// at chunks l / 16 costs 4 extra cycles per read under every XOR swizzle of the chunks tried. The
+// copy of a block stays coalesced: lanes 4i .. 4i + 3 fetch the 64 contiguous bytes of row i.
+__device__ __forceinline__ int blk16_slot(int i, int c) { return c ^ ((i >> 1) & 3); }
+
 // Global -> LDS copy of one operand tile with buffer_load ... lds (16 B per lane, the wave's
 // 64 lanes filling 1 KB of LDS contiguously); no staging registers. Lanes fetch permuted
 // sources so that the LDS image is swizzled:
 // * inner-contiguous tile: ROWS rows of 128 contraction bytes; chunk c of row r sits at
-//   chunk c ^ swz(r);
+//   chunk c ^ swz(r) (8-bit), or in the 16-row blocks of blk16_slot (bf16);
 // * outer-contiguous tile (bf16): 64 contraction rows of ROWS*2 bytes; chunk c of row k sits
-//   at chunk c ^ (4*(k & 3)), so the 32 lanes the LDS serves per cycle for a transposing
-//   ds_read_b64_tr_b16 (4 consecutive rows x 64 bytes) hit distinct banks.
+//   at chunk c ^ tr_swz(k), so the 32 lanes the LDS serves per cycle for a transposing
+//   ds_read_b64_tr_b16 hit distinct banks.
 // Chunks outside the operand (rows >= row_end, contraction >= k_end) are fetched from an
 // out-of-range offset and land as zeros.
 template <int ROWS, bool KMAJ, int ES, int NWAVES, int RB = kRowBytes>
@@ -197,12 +236,21 @@ struct TileCopy {
       const int r = piece * kRowsPerInstr + lane / kChunksPerRow;   // LDS row
       const int p = lane % kChunksPerRow;                           // physical chunk
       if constexpr (KMAJ) {
+        if constexpr (ES == 2 && SGE_BF16_M16) {
+          static_assert(RB == 128 && ROWS % 16 == 0, "16-row blocks of two 64-byte halves");
+          const int rb = (piece >> 1) * 16 + (lane >> 2);                 // row of this lane's chunk
+          const int cb = 4 * (piece & 1) + blk16_slot(lane >> 2, lane & 3);
+          const int64_t row = rowmap(row0, rb);
+          kk[i] = cb * 8;
+          off[i] = row < row_end ? (uint32_t)((row - row0) * ld * 2 + cb * 16) : kOOB;
+        } else {
         const int c = p ^ swz_rows<RB>(r);
         const int64_t row = rowmap(row0, r);
         kk[i] = c * (16 / ES);
         off[i] = row < row_end ? (uint32_t)((row - row0) * ld * ES + c * 16) : kOOB;
+        }
       } else {
-        const int c = p ^ (4 * (r & 3));
+        const int c = p ^ tr_swz(r);
         const int64_t outer = row0 + c * 8;
         kk[i] = r;
         off[i] = outer < row_end ? (uint32_t)(r * ld * 2 + c * 16) : kOOB;
@@ -230,6 +278,13 @@ struct TileCopy {
 __device__ __forceinline__ bf16x8 frag_k_bf16(const uint8_t* lds, int r, int ch) {
   return *reinterpret_cast<const bf16x8*>(lds + r * kRowBytes + ((ch ^ swz(r)) << 4));
 }
+// The 16x16x32 fragment (lane l: row rbase + l % 16, contraction 32 ks + 8 (l / 16) .. + 7) from
+// an inner-contiguous tile in 16-row blocks (rbase % 16 == 0).
+__device__ __forceinline__ bf16x8 frag_k16_bf16(const uint8_t* lds, int rbase, int ks, int lane) {
+  const int i = lane & 15;
+  return *reinterpret_cast<const bf16x8*>(lds + (rbase >> 4) * 2048 + ks * 1024 + i * 64 +
+                                          (blk16_slot(i, lane >> 4) << 4));
+}
 
 // The same fragment from an outer-contiguous tile with two transposing reads. Within each
 // 16-lane group, ds_read_b64_tr_b16 hands output lane 4g+c element c of the 8-byte rows
@@ -241,8 +296,26 @@ __device__ __forceinline__ bf16x8 frag_t_bf16(const uint8_t* lds, int mbase, int
   const int m = mbase + 16 * (q & 1) + 4 * (s & 3);
   const int k = ks * 16 + 8 * (q >> 1) + (s >> 2);
   const int k2 = k + 4;
-  const uint8_t* p0 = lds + k * (ROWS * 2) + ((((m >> 3) ^ (4 * (k & 3)))) << 4) + (m & 7) * 2;
-  const uint8_t* p1 = lds + k2 * (ROWS * 2) + ((((m >> 3) ^ (4 * (k2 & 3)))) << 4) + (m & 7) * 2;
+  const uint8_t* p0 = lds + k * (ROWS * 2) + (((m >> 3) ^ tr_swz(k)) << 4) + (m & 7) * 2;
+  const uint8_t* p1 = lds + k2 * (ROWS * 2) + (((m >> 3) ^ tr_swz(k2)) << 4) + (m & 7) * 2;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p1);
+  typedef short i16x8 __attribute__((__vector_size__(8 * sizeof(short))));
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// The 16x16x32 operand fragment (lane l: outer mbase + l % 16, contraction 32 ks + 8 (l / 16) ..
+// + 7) from an outer-contiguous tile: 16-lane group q reads contraction rows 32 ks + 8 q .. + 7,
+// four at a time, lane s at row offset s / 4 and outer offset 4 (s % 4), as in frag_t_bf16.
+template <int ROWS>
+__device__ __forceinline__ bf16x8 frag_t16_bf16(const uint8_t* lds, int mbase, int ks, int lane) {
+  const int q = lane >> 4, s = lane & 15;
+  const int m = mbase + 4 * (s & 3);
+  const int k = ks * 32 + 8 * q + (s >> 2);
+  const int k2 = k + 4;
+  const uint8_t* p0 = lds + k * (ROWS * 2) + (((m >> 3) ^ tr_swz(k)) << 4) + (m & 7) * 2;
+  const uint8_t* p1 = lds + k2 * (ROWS * 2) + (((m >> 3) ^ tr_swz(k2)) << 4) + (m & 7) * 2;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p1);
   typedef short i16x8 __attribute__((__vector_size__(8 * sizeof(short))));
@@ -409,13 +482,23 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
   const int64_t n_end = glu_fwd(EPI) ? p.F : p.N;
 
   // ---------------------------------------------------------------- main loop
+  // bf16 (kM16): each 32x32 block (i, j) of the wave's output is four 16x16x32 MFMA tiles
+  // acc4[i][j][2 ii + jj] (rows 16 ii.., columns 16 jj..); under the power limit that holds the
+  // clock down under MFMA load, register-only 16x16x32 loops sustain ~13% more bf16 FLOP/s
+  // than 32x32x16 ones on MI355X. 8-bit formats: one 32x32 accumulator per block.
+  constexpr bool kM16 = FMT == F_BF16 && SGE_BF16_M16;
   f32x16 acc[WMF][WNF];
+  f32x4 acc4[WMF][WNF][4];
 #pragma unroll
   for (int i = 0; i < WMF; ++i)
 #pragma unroll
-    for (int j = 0; j < WNF; ++j)
+    for (int j = 0; j < WNF; ++j) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+      for (int e = 0; e < 16; ++e) {
+        if constexpr (kM16) acc4[i][j][e >> 2][e & 3] = 0.0f;
+        else acc[i][j][e] = 0.0f;
+      }
+    }
 
   IdentityRows idrows;
   SwigluRows<WN> swrows{p.F};
@@ -816,6 +899,127 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
       tile(kt, std::integral_constant<int, 0>{}, S0{});
       if (kt + 1 < KT) tile(kt + 1, std::integral_constant<int, 1>{}, S0{});
     }
+  } else if constexpr (kM16) {
+    // bf16 on 16x16x32 MFMAs, two LDS stages of 64-element k-tiles (two MFMA k-steps each).
+    // Fragments: the wave's 2 WMF A pieces of 16 rows and 2 WNF B pieces. A pieces are read in
+    // place (piece f of the next step goes into fa16[f] right after the last MFMA that used it),
+    // except the last one, which is double-buffered by step parity so that the step's last
+    // fragment read is not the last instruction before the next step's first MFMAs; B pieces are
+    // double-buffered. The barrier of tile kt sits after the first MFMAs of its second step,
+    // behind each wave's wait for its copies of tile kt + 1; after it the copies of tile kt + 2
+    // go into tile kt's stage (every wave has its fragments of that stage in registers), one per
+    // group of MFMAs, so a copy has a whole tile of MFMAs to land.
+    constexpr int FA = 2 * WMF, FB = 2 * WNF;
+    constexpr int CPT = decltype(ca)::kInstr + decltype(cb)::kInstr;   // copies per tile per wave
+    static_assert(CPT <= FA && FB < FA - 1, "one copy per group; B reads before the last A read");
+    bf16x8 fa16[FA - 1], fa16l[2], fb16[2][FB];
+    auto rd_a = [&](const uint8_t* buf, int ks, int f, bf16x8& dst) {
+      const int mb = wm * WM + f * 16;
+      dst = AK ? frag_k16_bf16(buf, mb, ks, lane) : frag_t16_bf16<BM>(buf, mb, ks, lane);
+    };
+    auto rd_b = [&](const uint8_t* buf, int ks, int f, bf16x8 (&fb)[FB]) {
+      const int nb = wn * WN + f * 16;
+      const uint8_t* b_lds = buf + A_BYTES;
+      fb[f] = BK ? frag_k16_bf16(b_lds, nb, ks, lane) : frag_t16_bf16<BN>(b_lds, nb, ks, lane);
+    };
+    // The copies of one tile: buffer resources based at its first contraction element (32-bit
+    // offsets), its LDS stage, and its contraction extent (chunks at or past it read zeros).
+    struct TileSrc {
+      i32x4 ra, rb;
+      uint32_t dst;
+      int klim;
+    };
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lds0 = lds_addr_of(lds);
+    auto tile_src = [&](int t) {
+      const int64_t k0 = k_begin + (int64_t)t * KT_ELEMS;
+      const int64_t sa = AK ? k0 * 2 : k0 * p.lda * 2, sb = BK ? k0 * 2 : k0 * p.ldb * 2;
+      const int64_t kl = k_end - k0;
+      return TileSrc{make_rsrc4(a_base + sa, a_bytes - sa), make_rsrc4(b_base + sb, b_bytes - sb),
+                     lds0 + (uint32_t)((t & 1) * STAGE), (int)(kl < KT_ELEMS ? kl : KT_ELEMS)};
+    };
+    // Copy c (0 .. CPT-1) of a tile: A's pieces, then B's.
+    auto copy1 = [&](const TileSrc& ts, int c) {
+      if (c < decltype(ca)::kInstr) {
+        lds_copy16_at(ts.ra, ts.dst + (uint32_t)((NWAVES * c + wave_s) * 1024), ca.kk[c] < ts.klim ? ca.off[c] : kOOB);
+      } else {
+        const int i = c - decltype(ca)::kInstr;
+        lds_copy16_at(ts.rb, ts.dst + (uint32_t)(A_BYTES + (NWAVES * i + wave_s) * 1024),
+                      cb.kk[i] < ts.klim ? cb.off[i] : kOOB);
+      }
+    };
+    // One k-step of parity P on (fa16, fa16l[P], fbc): for each A piece f its 2 WNF MFMAs, then
+    // its read for the step (nbuf, nks), the last piece's into fa16l[P ^ 1] with piece FB's; B
+    // reads into fbn over the first FB groups. A tile's second step (P == 1) puts the wait for
+    // the next tile's copies and the barrier after its first group, and with COPY (and do_copy)
+    // issues SGE_M16_CPG copies of the tile ts after each group.
+    auto step = [&](auto par, auto copy_c, const bf16x8 (&fbc)[FB], bf16x8 (&fbn)[FB], const uint8_t* nbuf, int nks,
+                    const TileSrc& ts, bool do_copy) {
+      constexpr int P = decltype(par)::value;
+      constexpr bool COPY = decltype(copy_c)::value;
+      auto group = [&](int f, const bf16x8& a) {
+        const int i = f >> 1, ii = f & 1;
+#pragma unroll
+        for (int j = 0; j < WNF; ++j)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+            acc4[i][j][2 * ii + jj] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(fbc[2 * j + jj], a, acc4[i][j][2 * ii + jj], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (P == 1 && f == 0) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");             // the next tile landed
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");           // this wave's reads of its stage done
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      auto after = [&](int f) {                          // B read and copy of group f
+        if (f < FB) rd_b(nbuf, nks, f, fbn);
+        if constexpr (COPY) {
+#pragma unroll
+          for (int u = 0; u < SGE_M16_CPG; ++u)
+            if (f * SGE_M16_CPG + u < CPT && do_copy) copy1(ts, f * SGE_M16_CPG + u);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      };
+#pragma unroll
+      for (int f = 0; f < FA - 1; ++f) {
+        group(f, fa16[f]);
+        rd_a(nbuf, nks, f, fa16[f]);
+        if (f == FB) rd_a(nbuf, nks, FA - 1, fa16l[P ^ 1]);
+        after(f);
+      }
+      group(FA - 1, fa16l[P]);
+      after(FA - 1);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using C0 = std::false_type;
+    using C1 = std::true_type;
+    if (KT > 0) {
+      issue_tile(lds, k_begin);
+      if (KT > 1) {
+        issue_tile(lds + STAGE, k_begin + KT_ELEMS);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPT) : "memory");   // tile 0 landed, tile 1 in flight
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      __syncthreads();
+#pragma unroll
+      for (int f = 0; f < FA - 1; ++f) {
+        rd_a(lds, 0, f, fa16[f]);
+        if (f < FB) rd_b(lds, 0, f, fb16[0]);
+      }
+      rd_a(lds, 0, FA - 1, fa16l[0]);
+    }
+    for (int kt = 0; kt < KT; ++kt) {
+      uint8_t* const cur = (kt & 1) ? lds + STAGE : lds;
+      const uint8_t* const nxt = (kt & 1) ? lds : lds + STAGE;
+      const TileSrc ts = tile_src(kt + 2);                            // into stage kt % 2
+      step(I0{}, C0{}, fb16[0], fb16[1], cur, 1, ts, false);
+      // On the last tile the second step reads a stale stage: in bounds, never used.
+      step(I1{}, C1{}, fb16[1], fb16[0], nxt, 0, ts, kt + 2 < KT);
+    }
   } else {
   // Each wave waits for its own direct-to-LDS copies, then the barrier makes the
   // whole stage visible (and frees the other stage for the next copies).
@@ -886,8 +1090,17 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
   }
   const int64_t c_rows = SCHED == S_GROUP_M ? p.T : p.M;
   const int64_t rows_left = c_rows - m0;
-  auto row_in_tile = [&](int i) { return wm * WM + i * 32 + lrow; };
-  auto row_ok = [&](int i) { return m0 + row_in_tile(i) < row_end; };
+  // Group q (0..3) of 4 consecutive output columns that a lane holds in 32x32 block (i, j):
+  // its row and first column within the block, and its 4 values times alpha.
+  auto acc_row = [&](int q) { return kM16 ? 16 * (q >> 1) + (lane & 15) : lrow; };
+  auto acc_col = [&](int q) { return kM16 ? 16 * (q & 1) + 4 * (lane >> 4) : 8 * q + 4 * lhalf; };
+  auto acc_get = [&](int i, int j, int q, float a) {
+    if constexpr (kM16)
+      return make_float4(a * acc4[i][j][q][0], a * acc4[i][j][q][1], a * acc4[i][j][q][2], a * acc4[i][j][q][3]);
+    else
+      return make_float4(a * acc[i][j][4 * q + 0], a * acc[i][j][4 * q + 1], a * acc[i][j][4 * q + 2],
+                         a * acc[i][j][4 * q + 3]);
+  };
 
   if constexpr (EPI == E_STORE || EPI == E_SRELU) {
     // Two passes over half of each wave's rows: alpha*acc (fp32) goes to LDS in row-major
@@ -934,14 +1147,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
 #pragma unroll
       for (int il = 0; il < WMF / 2; ++il) {
         const int i = pass * (WMF / 2) + il;
-        const int r = il * 32 + lrow;                      // row within this wave row's half
 #pragma unroll
         for (int j = 0; j < WNF; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int g = (wn * WN + j * 32 + 8 * q + 4 * lhalf) >> 2;
-            const float4 v = make_float4(alpha * acc[i][j][4 * q + 0], alpha * acc[i][j][4 * q + 1],
-                                         alpha * acc[i][j][4 * q + 2], alpha * acc[i][j][4 * q + 3]);
+            const int r = il * 32 + acc_row(q);            // row within this wave row's half
+            const int g = (wn * WN + j * 32 + acc_col(q)) >> 2;
+            const float4 v = acc_get(i, j, q, alpha);
             *reinterpret_cast<float4*>(stage + r * BN + ((g ^ (r & 15)) << 2)) = v;
           }
       }
@@ -1037,14 +1249,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
 #pragma unroll
       for (int il = 0; il < WMF / 2; ++il) {
         const int i = pass * (WMF / 2) + il;
-        const int r = il * 32 + lrow;
 #pragma unroll
         for (int j = 0; j < WNF; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int g = (wn * WN + j * 32 + 8 * q + 4 * lhalf) >> 2;
-            const float4 v = make_float4(alpha * acc[i][j][4 * q + 0], alpha * acc[i][j][4 * q + 1],
-                                         alpha * acc[i][j][4 * q + 2], alpha * acc[i][j][4 * q + 3]);
+            const int r = il * 32 + acc_row(q);
+            const int g = (wn * WN + j * 32 + acc_col(q)) >> 2;
+            const float4 v = acc_get(i, j, q, alpha);
             *reinterpret_cast<float4*>(stage + r * BN + ((g ^ (r & 15) ^ wsw(wn)) << 2)) = v;
           }
       }
@@ -1162,14 +1373,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
 #pragma unroll
       for (int il = 0; il < WMF / 2; ++il) {
         const int i = pass * (WMF / 2) + il;
-        const int r = il * 32 + lrow;
 #pragma unroll
         for (int j = 0; j < WNF; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int g = (wn * WN + j * 32 + 8 * q + 4 * lhalf) >> 2;
-            const float4 v = make_float4(alpha * acc[i][j][4 * q + 0], alpha * acc[i][j][4 * q + 1],
-                                         alpha * acc[i][j][4 * q + 2], alpha * acc[i][j][4 * q + 3]);
+            const int r = il * 32 + acc_row(q);
+            const int g = (wn * WN + j * 32 + acc_col(q)) >> 2;
+            const float4 v = acc_get(i, j, q, alpha);
             *reinterpret_cast<float4*>(stage + r * BN + ((g ^ (r & 15)) << 2)) = v;
           }
       }
