@@ -911,7 +911,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
     // group of MFMAs, so a copy has a whole tile of MFMAs to land.
     constexpr int FA = 2 * WMF, FB = 2 * WNF;
     constexpr int CPT = decltype(ca)::kInstr + decltype(cb)::kInstr;   // copies per tile per wave
-    static_assert(CPT <= FA && FB < FA - 1, "one copy per group; B reads before the last A read");
+    static_assert(CPT <= FA * SGE_M16_CPG, "copies fit the groups");
+    static_assert(FB < FA - 1, "B reads before the last A read");
     bf16x8 fa16[FA - 1], fa16l[2], fb16[2][FB];
     auto rd_a = [&](const uint8_t* buf, int ks, int f, bf16x8& dst) {
       const int mb = wm * WM + f * 16;
