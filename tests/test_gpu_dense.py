@@ -57,6 +57,19 @@ def test_dense_parity_aligned_tiles(fmt):
         assert_close(host_f64(got[k]), ref[k], tau, what=f"{fmt} {k}")
 
 
+# bf16 contraction lengths at the k-step (32) and k-tile (64) edges: shorter than a step, one step,
+# one tile, a tile and a ragged step; the last case also gives dgrad (over N = 24) and wgrad (over
+# M = 40) a single partial k-tile.
+@pytest.mark.parametrize("M,N,K", [(264, 264, 8), (264, 264, 32), (264, 264, 64), (264, 264, 72), (40, 24, 96)])
+def test_bf16_contraction_edges(M, N, K):
+    print(f"case dense bf16 M={M} N={N} K={K}", flush=True)
+    d = synth.dense(M, N, K, seed=5)
+    got = run_dense("bf16", d, 0.75)
+    ref = _oracle_dense("bf16", d, 0.75)
+    for k in ("fwd", "dgrad", "wgrad"):
+        assert_close(host_f64(got[k]), ref[k], TAU_BF16, what=f"bf16 {k} M={M} N={N} K={K}")
+
+
 def test_forward_256x512x512_full_parity():
     """The small forward workload at its own size: every element against the oracle."""
     w = synth.WORKLOADS["bf16_fwd_256x512x512"]
