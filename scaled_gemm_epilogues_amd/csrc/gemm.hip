@@ -262,15 +262,15 @@ struct TileCopy {
   // base_row0: address of operand row row0 (inner-contiguous) or of contraction row 0 (outer).
   __device__ __forceinline__ void issue(uint8_t* lds, const uint8_t* base, int64_t ld, int64_t bytes_from_base,
                                         int64_t k0, int64_t k_end) const {
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // Resource based at the tile's first contraction element keeps offsets 32-bit.
     const int64_t shift = KMAJ ? k0 * ES : k0 * ld * 2;
     const i32x4 rsrc = make_rsrc4(base + shift, bytes_from_base - shift);
+    const int64_t kl = k_end - k0;                       // chunks at or past it read zeros
+    const int klim = kl < (1 << 30) ? (int)kl : (1 << 30);
+    const uint32_t dst = lds_addr_of(lds);
 #pragma unroll
-    for (int i = 0; i < kInstr; ++i) {
-      const uint32_t o = (k0 + kk[i] < k_end) ? off[i] : kOOB;
-      lds_copy16(rsrc, lds + (NWAVES * i + wave) * 1024, o);
-    }
+    for (int i = 0; i < kInstr; ++i) lds_copy16_at(rsrc, dst + (uint32_t)((NWAVES * i + wave) * 1024), kk[i] < klim ? off[i] : kOOB);
   }
 };
 
