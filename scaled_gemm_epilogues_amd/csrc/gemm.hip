@@ -92,8 +92,8 @@ constexpr int kWavesM = SGE_WAVES_M, kWavesN = SGE_WAVES_N, kFragsM = SGE_FRAGS_
 // Deep pipeline: with one wave per SIMD nothing covers a wave's wait for its tile copies, so the
 // 8-bit dense GEMMs keep four k-tiles of copies in flight (four LDS stages of 64 contraction
 // bytes, one MFMA k-step each, 128 KB in all) instead of one (two stages of 128 bytes). The bf16
-// tiles keep two stages and two waves per SIMD: on 2x2 waves with four 64-byte stages, and on
-// 2x4 waves with eight 32-byte stages (a barrier every 8 MFMAs), they measured 4-30% slower.
+// tiles keep two stages and two waves per SIMD: four 32- or 64-byte stages (a barrier every k-step)
+// and 2x2-wave tiles measured 4-30% slower on 32x32x16 MFMAs and 12-15% slower on 16x16x32 ones.
 // Among the grouped GEMMs only the weight gradients (contraction over a group's tokens: few,
 // long tiles) take it: measured on the FP8 / MXFP8 grouped MLP they ran 2.5-4.6% faster, while
 // the row-partitioned ones ran from 2% faster to 29% slower (the FP8 activation-backward
@@ -907,8 +907,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
     // fragment read is not the last instruction before the next step's first MFMAs; B pieces are
     // double-buffered. The barrier of tile kt sits after the first MFMAs of its second step,
     // behind each wave's wait for its copies of tile kt + 1; after it the copies of tile kt + 2
-    // go into tile kt's stage (every wave has its fragments of that stage in registers), one per
-    // group of MFMAs, so a copy has a whole tile of MFMAs to land.
+    // go into tile kt's stage (every wave has its fragments of that stage in registers),
+    // SGE_M16_CPG after each group of MFMAs from the first on, so a copy has nearly a whole tile
+    // of MFMAs to land.
     constexpr int FA = 2 * WMF, FB = 2 * WNF;
     constexpr int CPT = decltype(ca)::kInstr + decltype(cb)::kInstr;   // copies per tile per wave
     static_assert(CPT <= FA * SGE_M16_CPG, "copies fit the groups");
