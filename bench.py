@@ -265,7 +265,8 @@ def build_grouped_mx(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, d
     """The grouped MLP on MXFP8 operands: every GEMM operand quantized each step, blocked along
     that GEMM's contraction (rowwise for the forward and the dgrads, W's columnwise copy for
     the dgrads, per-group token blocks for the wgrads). fc1's scaled activation emits its output
-    as MXFP8 for fc2, and fc2's dgrad emits dh as MXFP8 for fc1's dgrad."""
+    as MXFP8 for fc2's forward and token-blocked for fc2's wgrad, and fc2's dgrad emits dh the
+    same two ways for fc1's dgrad and wgrad (neither is written in bf16)."""
     T, H = X.shape
     G, N1, _ = W1.shape
     swiglu, fwd_epi, bwd_epi, dact, ap = act_config(sge, wl)   # swiglu: a gated activation
@@ -293,10 +294,8 @@ def build_grouped_mx(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, d
             ("fc2_fwd", lambda: sge.grouped_linear_fwd_mxfp8(qy, sy, qw2.view(G, H, F), sw2.view(G, H, F // 32),
                                                              base, out=out)),
         ], flops, hbm
-    bf = dict(dtype=torch.bfloat16, device="cuda")
     ld = sge.mx_token_capacity(T, G)
     lay = torch.empty(2, G + 1, dtype=torch.int64, device="cuda")
-    y = torch.empty(T, F, **bf)
     qxT, sxT = torch.empty(H, ld, **u8), torch.empty(H, ld // 32, **u8)
     qw1T, sw1T = torch.empty(H, G * N1, **u8), torch.empty(H, G * N1 // 32, **u8)
     qw2T, sw2T = torch.empty(F, G * H, **u8), torch.empty(F, G * H // 32, **u8)
@@ -309,8 +308,7 @@ def build_grouped_mx(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, d
                   "fc1_wgrad": 2 * T * N1 * H})
     # algorithmic bytes: bf16 read, E4M3 written per copy, one E8M0 byte per 32 (padding not counted)
     hbm = {"quant_x": T * H * 4 + T * H // 16, "quant_w1": G * N1 * H * 4 + G * N1 * H // 16,
-           "quant_w2": G * H * F * 4 + G * H * F // 16, "quant_y": T * F * 3 + T * F // 32,
-           "quant_dout": T * H * 4 + T * H // 16, "quant_dh": T * N1 * 3 + T * N1 // 32}
+           "quant_w2": G * H * F * 4 + G * H * F // 16, "quant_dout": T * H * 4 + T * H // 16}
     launches = [
         ("offsets", lambda: sge.splits_to_offsets(splits, [1, H], offs)),
         ("mx_layout", lambda: sge.mx_group_layout(base, T, lay)),
@@ -318,17 +316,16 @@ def build_grouped_mx(torch, sge, wl, X, W1, W2, DOUT, P, splits, offs, h, out, d
         ("quant_w1", lambda: sge.quantize_mxfp8(W1f, q_row=qw1, s_row=sw1, q_colT=qw1T, s_colT=sw1T)),
         ("quant_w2", lambda: sge.quantize_mxfp8(W2f, q_row=qw2, s_row=sw2, q_colT=qw2T, s_colT=sw2T)),
         ("fc1_fwd", lambda: sge.grouped_linear_fwd_mxfp8(
-            qx, sx, qw1.view(G, N1, H), sw1.view(G, N1, H // 32), base, out=y,
-            epilogue=fwd_epi, probs=P, preact=h, out_q=qy, out_s=sy, act=ap)),
-        ("quant_y", lambda: sge.quantize_mxfp8_grouped(y, lay, qyT, syT)),
+            qx, sx, qw1.view(G, N1, H), sw1.view(G, N1, H // 32), base, out=None,
+            epilogue=fwd_epi, probs=P, preact=h, out_q=qy, out_s=sy, act=ap, layout=lay,
+            out_colT_q=qyT, out_colT_s=syT)),
         ("fc2_fwd", lambda: sge.grouped_linear_fwd_mxfp8(qy, sy, qw2.view(G, H, F), sw2.view(G, H, F // 32),
                                                          base, out=out)),
         ("quant_dout", lambda: sge.quantize_mxfp8_grouped(DOUT, lay, qdT, sdT, q_row=qd, s_row=sd)),
         (dact, lambda: sge.grouped_linear_dgrad_mxfp8(
-            qd, sd, qw2T, sw2T, base, epilogue=bwd_epi, preact=h, probs=P, dact=dh, dprobs=dp, act=ap,
-            dact_q=qdh, dact_s=sdh, workspace=ws)),
+            qd, sd, qw2T, sw2T, base, epilogue=bwd_epi, preact=h, probs=P, dact=None, dprobs=dp, act=ap,
+            dact_q=qdh, dact_s=sdh, workspace=ws, layout=lay, dact_colT_q=qdhT, dact_colT_s=sdhT)),
         ("fc2_wgrad", lambda: sge.grouped_linear_wgrad_mxfp8(qdT, sdT, qyT, syT, lay, dw2)),
-        ("quant_dh", lambda: sge.quantize_mxfp8_grouped(dh, lay, qdhT, sdhT)),
         ("fc1_dgrad", lambda: sge.grouped_linear_dgrad_mxfp8(qdh, sdh, qw1T, sw1T, base, dx=dx)),
         ("fc1_wgrad", lambda: sge.grouped_linear_wgrad_mxfp8(qdhT, sdhT, qxT, sxT, lay, dw1)),
     ]

@@ -310,22 +310,31 @@ sge_status sge_grouped_mlp_bwd(const void* dout, const void* x, const void* w1, 
  *   x_q [T, K] u8, x_s [T, K/32] u8;  w_q [G, N, K] u8, w_s [G, N, K/32] u8
  *   (exactly what sge_quantize_mxfp8 writes as q_row / s_row).
  * SGE_EPI_NONE: out [T, N] bf16.
- * SGE_EPI_SCALED_SWIGLU: out [T, N/2] bf16 (may be NULL when out_q is given), preact
+ * SGE_EPI_SCALED_SWIGLU: out [T, N/2] bf16 (may be NULL when out_q or out_colT_q is given), preact
  *   [T, N] bf16 (may be NULL), and optionally out_q [T, N/2] u8 + out_s [T, N/64] u8: the
  *   MXFP8 rowwise quantization of the bf16 output, i.e. the bytes sge_quantize_mxfp8 would
  *   write for `out` (the operand layout of the next grouped GEMM's forward). out_q and
  *   out_s are given together or not at all.
  * SGE_EPI_SCALED_SRELU and SGE_EPI_SCALED_CLAMPED_SWIGLU (with act_params) as in
  *   sge_grouped_linear_fwd, with the same optional MXFP8 output.
+ * Every activation epilogue may also write the activation output token-blocked (the operand
+ *   the next layer's weight gradient contracts over tokens): out_colT_q [C][ld_t] u8 and
+ *   out_colT_s [C][ld_t/32] u8 (C = the output's columns; given together, or both NULL),
+ *   exactly the q_colT / s_colT that sge_quantize_mxfp8_grouped writes for the bf16 output
+ *   with `layout` and ld = ld_t (padding up to each group's aligned end included, columns
+ *   from pad[G] on untouched). layout: [2][G+1] from sge_mx_group_layout of the same offsets,
+ *   T and G; ld_t % 128 == 0 and ld_t >= sge_mx_token_capacity(T, G). Unused (may be NULL / 0)
+ *   without out_colT_q. out may then be NULL.
  * Shapes: K % 128 == 0; N % 8 == 0 (SWIGLU: N % 256 == 0). All pointers 16-byte aligned;
- * outputs must not overlap the inputs or each other (SGE_ERR_ALIAS). offsets and probs
- * as in sge_grouped_linear_fwd.
+ * outputs must not overlap the inputs or each other (SGE_ERR_ALIAS).
+ * offsets and probs as in sge_grouped_linear_fwd.
  */
 sge_status sge_grouped_linear_fwd_mxfp8(const void* x_q, const void* x_s, const void* w_q, const void* w_s,
                                         int32_t G, int64_t T, int64_t N, int64_t K, const int64_t* offsets,
                                         float alpha, int32_t epilogue,
                                         const sge_act_params* act_params, const float* probs, void* out,
-                                        void* preact, void* out_q, void* out_s, hipStream_t stream);
+                                        void* preact, void* out_q, void* out_s, const int64_t* layout,
+                                        int64_t ld_t, void* out_colT_q, void* out_colT_s, hipStream_t stream);
 
 /*
  * Grouped linear backward for one layer with the precomputed offsets.
@@ -413,13 +422,18 @@ sge_status sge_quantize_mxfp8_grouped(const void* src, int64_t T, int64_t cols, 
  *     (sge_quantize_mxfp8 q_colT/s_colT); blocks never cross experts as N % 32 == 0.
  *   SGE_EPI_NONE: dx [T, K] bf16 = g.
  *   SGE_EPI_DSCALED_SWIGLU (x was y = p * silu(a) * b, preact h = [a, b] [T, 2K] bf16):
- *     dact [T, 2K] bf16 = [g*p*b*silu'(a), g*p*silu(a)] (may be NULL when dact_q is given),
+ *     dact [T, 2K] bf16 = [g*p*b*silu'(a), g*p*silu(a)] (may be NULL when dact_q or dact_colT_q is given),
  *     dprobs [T] fp32 = sum_j g*silu(a)*b (deterministic order), and optionally
  *     dact_q [T, 2K] u8 + dact_s [T, 2K/32] u8: the rowwise MXFP8 of the bf16 dact, the bytes
  *     sge_quantize_mxfp8 writes for it (the operand of the next layer's dgrad).
  *     workspace: >= sge_grouped_linear_bwd_workspace_size(T, K, G, epilogue) bytes.
  *   SGE_EPI_DSCALED_SRELU and SGE_EPI_DSCALED_CLAMPED_SWIGLU (with act_params) as in
  *   sge_grouped_linear_bwd, with the same optional MXFP8 dact.
+ *   With an activation backward, dact may also be written token-blocked (the operand of the
+ *   next layer's weight gradient): dact_colT_q [W][ld_t] u8 + dact_colT_s [W][ld_t/32] u8
+ *   (W = dact's width; given together), exactly what sge_quantize_mxfp8_grouped writes as
+ *   q_colT / s_colT for the bf16 dact with `layout` and ld = ld_t; layout and ld_t as for
+ *   sge_grouped_linear_fwd_mxfp8's out_colT_q (unused without dact_colT_q).
  *   Shapes: N % 128 == 0, K % 8 == 0 (SwiGLU: K % 32 == 0). offsets as in
  *   sge_grouped_linear_fwd. Outputs may not overlap inputs or each other.
  *
@@ -434,7 +448,8 @@ sge_status sge_grouped_linear_dgrad_mxfp8(const void* dy_q, const void* dy_s, co
                                           const int64_t* offsets, float alpha, int32_t epilogue,
                                           const sge_act_params* act_params,
                                           const void* preact, const float* probs, void* dx, void* dact,
-                                          float* dprobs, void* dact_q, void* dact_s, void* workspace,
+                                          float* dprobs, void* dact_q, void* dact_s, const int64_t* layout,
+                                          int64_t ld_t, void* dact_colT_q, void* dact_colT_s, void* workspace,
                                           size_t workspace_bytes, hipStream_t stream);
 sge_status sge_grouped_linear_wgrad_mxfp8(const void* dyT_q, const void* dyT_s, const void* xT_q,
                                           const void* xT_s, int32_t G, int64_t N, int64_t K,

@@ -92,7 +92,7 @@ _SIGS = {
     "sge_grouped_linear_fwd": ([_vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _ACT, _vp, _vp, _vp, _vp],
                                ctypes.c_int),
     "sge_grouped_linear_fwd_mxfp8": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _ACT, _vp, _vp, _vp,
-                                      _vp, _vp, _vp], ctypes.c_int),
+                                      _vp, _vp, _vp, _i64, _vp, _vp, _vp], ctypes.c_int),
     "sge_grouped_linear_bwd_workspace_size": ([_i64, _i64, _i32, _i32], _sz),
     "sge_grouped_linear_bwd": ([_vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _ACT, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
@@ -102,7 +102,7 @@ _SIGS = {
     "sge_mx_group_layout": ([_vp, _i32, _i64, _vp, _vp], ctypes.c_int),
     "sge_quantize_mxfp8_grouped": ([_vp, _i64, _i64, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "sge_grouped_linear_dgrad_mxfp8": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _f32, _i32, _ACT, _vp, _vp,
-                                        _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+                                        _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "sge_grouped_linear_wgrad_mxfp8": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _f32, _vp, _vp],
                                        ctypes.c_int),
     "sge_quantize_fp8_grouped_workspace_size": ([_i32], _sz),
@@ -256,14 +256,18 @@ def grouped_linear_fwd(x, w, offsets, out, alpha=1.0, epilogue=EPI_NONE, probs=N
 
 
 def grouped_linear_fwd_mxfp8(x_q, x_s, w_q, w_s, offsets, out=None, alpha=1.0, epilogue=EPI_NONE, probs=None,
-                             preact=None, out_q=None, out_s=None, act=None, stream=None):
+                             preact=None, out_q=None, out_s=None, act=None, layout=None, out_colT_q=None,
+                             out_colT_s=None, stream=None):
     """Grouped forward with MXFP8 operands: x_q [T, K] u8 + x_s [T, K/32] u8, w_q [G, N, K] u8 +
-    w_s [G, N, K/32] u8 (rowwise). SwiGLU may also emit out_q [T, N/2] + out_s [T, N/64]."""
+    w_s [G, N, K/32] u8 (rowwise). SwiGLU may also emit out_q [T, N/2] + out_s [T, N/64], and
+    the token-blocked out_colT_q [N/2, ld] + out_colT_s [N/2, ld/32] with ``layout``."""
     G, N, K = w_q.shape
     T = x_q.shape[0]
+    ld_t = 0 if out_colT_q is None else out_colT_q.shape[1]
     _check(_lib.sge_grouped_linear_fwd_mxfp8(_ptr(x_q), _ptr(x_s), _ptr(w_q), _ptr(w_s), G, T, N, K, _ptr(offsets),
                                              float(alpha), epilogue, _act(act), _ptr(probs), _ptr(out), _ptr(preact),
-                                             _ptr(out_q), _ptr(out_s), _stream(stream)))
+                                             _ptr(out_q), _ptr(out_s), _ptr(layout), ld_t, _ptr(out_colT_q),
+                                             _ptr(out_colT_s), _stream(stream)))
 
 
 def grouped_linear_bwd_workspace_size(T, K, G, epilogue):
@@ -334,17 +338,21 @@ def quantize_mxfp8_grouped(src, layout, q_colT, s_colT, q_row=None, s_row=None, 
 
 def grouped_linear_dgrad_mxfp8(dy_q, dy_s, w_q, w_s, offsets, alpha=1.0, epilogue=EPI_NONE, preact=None,
                                probs=None, dx=None, dact=None, dprobs=None, dact_q=None, dact_s=None,
-                               workspace=None, act=None, stream=None):
+                               workspace=None, act=None, layout=None, dact_colT_q=None, dact_colT_s=None,
+                               stream=None):
     """MXFP8 grouped dgrad: dy_q [T, N] + dy_s [T, N/32] (rowwise), w_q [K, G*N] + w_s [K, G*N/32]
-    (W viewed [G*N, K], quantized columnwise). SwiGLU backward writes dact / dact_q+dact_s and dprobs."""
+    (W viewed [G*N, K], quantized columnwise). SwiGLU backward writes dact / dact_q+dact_s and dprobs,
+    and the token-blocked dact_colT_q [2K, ld] + dact_colT_s [2K, ld/32] with ``layout``."""
     T, N = dy_q.shape
     K = w_q.shape[0]
     G = offsets.numel() - 1
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ld_t = 0 if dact_colT_q is None else dact_colT_q.shape[1]
     _check(_lib.sge_grouped_linear_dgrad_mxfp8(_ptr(dy_q), _ptr(dy_s), _ptr(w_q), _ptr(w_s), G, T, N, K,
                                                _ptr(offsets), float(alpha), epilogue, _act(act), _ptr(preact),
                                                _ptr(probs), _ptr(dx), _ptr(dact), _ptr(dprobs), _ptr(dact_q),
-                                               _ptr(dact_s), _ptr(workspace), ws_bytes, _stream(stream)))
+                                               _ptr(dact_s), _ptr(layout), ld_t, _ptr(dact_colT_q),
+                                               _ptr(dact_colT_s), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def grouped_linear_wgrad_mxfp8(dyT_q, dyT_s, xT_q, xT_s, layout, dw, alpha=1.0, stream=None):

@@ -118,6 +118,19 @@ sge_status check_span(const char* what, int64_t bytes) {
   return SGE_OK;
 }
 
+// A token-blocked output written by a grouped epilogue: the layout, and ld as the token-blocked
+// quantizer takes it (every group's range fits below ld). Addressed with 64-bit pointers.
+sge_status check_colT(const char* what, int64_t T, int32_t G, const int64_t* layout, int64_t ld, const void* q,
+                      const void* sc) {
+  if (!layout) return fail(SGE_ERR_NULL, "%s: a token-blocked output needs the group layout", what);
+  if (G > 4096) return fail(SGE_ERR_ARG, "%s: G=%d outside [1, 4096]", what, G);
+  if (ld % SGE_MX_TOKEN_ALIGN || ld < sge_mx_token_capacity(T, G))
+    return fail(SGE_ERR_SHAPE, "%s: ld_t=%lld must be a multiple of %d and >= sge_mx_token_capacity(T, G)=%lld", what,
+                (long long)ld, SGE_MX_TOKEN_ALIGN, (long long)sge_mx_token_capacity(T, G));
+  if (!aligned16(q) || !aligned16(sc)) return fail(SGE_ERR_ALIGN, "%s: pointers must be 16-byte aligned", what);
+  return SGE_OK;
+}
+
 sge::GemmParams gemm_params(const sge_operand& a, const sge_operand& b, void* c, int64_t ldc, float alpha,
                             int accumulate) {
   sge::GemmParams p;
@@ -435,7 +448,8 @@ sge_status sge_grouped_linear_fwd(const void* x, const void* w, int32_t G, int64
 sge_status sge_grouped_linear_fwd_mxfp8(const void* x_q, const void* x_s, const void* w_q, const void* w_s, int32_t G,
                                         int64_t T, int64_t N, int64_t K, const int64_t* offsets, float alpha,
                                         int32_t epilogue, const sge_act_params* act_params, const float* probs,
-                                        void* out, void* preact, void* out_q, void* out_s, hipStream_t stream) {
+                                        void* out, void* preact, void* out_q, void* out_s, const int64_t* layout,
+                                        int64_t ld_t, void* out_colT_q, void* out_colT_s, hipStream_t stream) {
   if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_mxfp8: bad sizes");
   if (!fwd_epilogue_ok(epilogue))
     return fail(SGE_ERR_ARG, "grouped_linear_fwd_mxfp8: epilogue %d not allowed", epilogue);
@@ -446,7 +460,11 @@ sge_status sge_grouped_linear_fwd_mxfp8(const void* x_q, const void* x_s, const 
   if ((out_q == nullptr) != (out_s == nullptr))
     return fail(SGE_ERR_NULL, "grouped_linear_fwd_mxfp8: out_q and out_s go together");
   if (out_q && !act) return fail(SGE_ERR_ARG, "grouped_linear_fwd_mxfp8: a quantized output needs an activation epilogue");
-  if (!out && !out_q) return fail(SGE_ERR_NULL, "grouped_linear_fwd_mxfp8: no output");
+  if ((out_colT_q == nullptr) != (out_colT_s == nullptr))
+    return fail(SGE_ERR_NULL, "grouped_linear_fwd_mxfp8: out_colT_q and out_colT_s go together");
+  if (out_colT_q && !act)
+    return fail(SGE_ERR_ARG, "grouped_linear_fwd_mxfp8: a token-blocked output needs an activation epilogue");
+  if (!out && !out_q && !out_colT_q) return fail(SGE_ERR_NULL, "grouped_linear_fwd_mxfp8: no output");
   if (act && !probs) return fail(SGE_ERR_NULL, "grouped_linear_fwd_mxfp8: probs is NULL");
   if (out_q && N % 32) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_mxfp8: an MXFP8 output needs N %% 32 == 0");
   if (K % 128) return fail(SGE_ERR_SHAPE, "grouped_linear_fwd_mxfp8: K must be a multiple of 128 (got %lld)", (long long)K);
@@ -461,18 +479,23 @@ sge_status sge_grouped_linear_fwd_mxfp8(const void* x_q, const void* x_s, const 
       (preact && !aligned16(preact)) || (out_q && !aligned16(out_q)))
     return fail(SGE_ERR_ALIGN, "grouped_linear_fwd_mxfp8: pointers must be 16-byte aligned");
   const int64_t out_cols = swiglu ? N / 2 : N;
-  const Range in[4] = {range_of(x_q, T, K, K, 1), range_of(x_s, T, K / 32, K / 32, 1),
-                       range_of(w_q, (int64_t)G * N, K, K, 1), range_of(w_s, (int64_t)G * N, K / 32, K / 32, 1)};
-  const Range outs[4] = {out ? range_of(out, T, out_cols, out_cols, 2) : Range{0, 0},
+  if (out_colT_q)
+    if (sge_status st = check_colT("grouped_linear_fwd_mxfp8", T, G, layout, ld_t, out_colT_q, out_colT_s)) return st;
+  const Range in[5] = {range_of(x_q, T, K, K, 1), range_of(x_s, T, K / 32, K / 32, 1),
+                       range_of(w_q, (int64_t)G * N, K, K, 1), range_of(w_s, (int64_t)G * N, K / 32, K / 32, 1),
+                       out_colT_q ? range_of(layout, 2, G + 1, G + 1, 8) : Range{0, 0}};
+  const Range outs[6] = {out ? range_of(out, T, out_cols, out_cols, 2) : Range{0, 0},
                          preact ? range_of(preact, T, N, N, 2) : Range{0, 0},
                          out_q ? range_of(out_q, T, out_cols, out_cols, 1) : Range{0, 0},
-                         out_s ? range_of(out_s, T, out_cols / 32, out_cols / 32, 1) : Range{0, 0}};
+                         out_s ? range_of(out_s, T, out_cols / 32, out_cols / 32, 1) : Range{0, 0},
+                         out_colT_q ? range_of(out_colT_q, out_cols, ld_t, ld_t, 1) : Range{0, 0},
+                         out_colT_s ? range_of(out_colT_s, out_cols, ld_t / 32, ld_t / 32, 1) : Range{0, 0}};
   for (const Range& o : outs) {
     for (const Range& i : in)
       if (overlap(o, i)) return fail(SGE_ERR_ALIAS, "grouped_linear_fwd_mxfp8: outputs overlap inputs");
   }
-  for (int a = 0; a < 4; ++a)
-    for (int b = a + 1; b < 4; ++b)
+  for (int a = 0; a < 6; ++a)
+    for (int b = a + 1; b < 6; ++b)
       if (overlap(outs[a], outs[b])) return fail(SGE_ERR_ALIAS, "grouped_linear_fwd_mxfp8: outputs overlap");
   if (T == 0 || N == 0) return ok();
   sge::GemmParams p;
@@ -504,6 +527,10 @@ sge_status sge_grouped_linear_fwd_mxfp8(const void* x_q, const void* x_s, const 
   p.q_out = static_cast<uint8_t*>(out_q);
   p.s_out = static_cast<uint8_t*>(out_s);
   p.ld_q = out_cols;
+  p.qt_out = static_cast<uint8_t*>(out_colT_q);
+  p.st_out = static_cast<uint8_t*>(out_colT_s);
+  p.ld_t = ld_t;
+  p.mx_layout = layout;
   set_act(p, epilogue, act_params);
   return hip_status(sge::launch_grouped_fwd_mx(p, epilogue, stream), "grouped fwd mxfp8 launch");
 }
@@ -661,7 +688,9 @@ sge_status sge_grouped_linear_dgrad_mxfp8(const void* dy_q, const void* dy_s, co
                                           float alpha, int32_t epilogue, const sge_act_params* act_params,
                                           const void* preact, const float* probs,
                                           void* dx, void* dact, float* dprobs, void* dact_q, void* dact_s,
-                                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                                          const int64_t* layout, int64_t ld_t, void* dact_colT_q,
+                                          void* dact_colT_s, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream) {
   if (G < 1 || T < 0 || N < 0 || K < 0) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_mxfp8: bad sizes");
   if (!bwd_epilogue_ok(epilogue))
     return fail(SGE_ERR_ARG, "grouped_linear_dgrad_mxfp8: epilogue %d not allowed", epilogue);
@@ -671,12 +700,15 @@ sge_status sge_grouped_linear_dgrad_mxfp8(const void* dy_q, const void* dy_s, co
   if (!dy_q || !dy_s || !w_q || !w_s || !offsets) return fail(SGE_ERR_NULL, "grouped_linear_dgrad_mxfp8: NULL pointer");
   if ((dact_q == nullptr) != (dact_s == nullptr))
     return fail(SGE_ERR_NULL, "grouped_linear_dgrad_mxfp8: dact_q and dact_s go together");
+  if ((dact_colT_q == nullptr) != (dact_colT_s == nullptr))
+    return fail(SGE_ERR_NULL, "grouped_linear_dgrad_mxfp8: dact_colT_q and dact_colT_s go together");
   if (swiglu) {
     if (!preact || !probs || !dprobs) return fail(SGE_ERR_NULL, "grouped_linear_dgrad_mxfp8: an activation backward needs preact, probs and dprobs");
-    if (!dact && !dact_q) return fail(SGE_ERR_NULL, "grouped_linear_dgrad_mxfp8: no output");
+    if (!dact && !dact_q && !dact_colT_q) return fail(SGE_ERR_NULL, "grouped_linear_dgrad_mxfp8: no output");
   } else {
     if (!dx) return fail(SGE_ERR_NULL, "grouped_linear_dgrad_mxfp8: dx is NULL");
-    if (dact_q) return fail(SGE_ERR_ARG, "grouped_linear_dgrad_mxfp8: a quantized output needs an activation backward");
+    if (dact_q || dact_colT_q)
+      return fail(SGE_ERR_ARG, "grouped_linear_dgrad_mxfp8: a quantized output needs an activation backward");
   }
   if (N % 128) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_mxfp8: N must be a multiple of 128 (got %lld)", (long long)N);
   if (K % 8) return fail(SGE_ERR_SHAPE, "grouped_linear_dgrad_mxfp8: K must be a multiple of 8");
@@ -688,17 +720,22 @@ sge_status sge_grouped_linear_dgrad_mxfp8(const void* dy_q, const void* dy_s, co
       (preact && !aligned16(preact)) || (dact && !aligned16(dact)) || (dact_q && !aligned16(dact_q)))
     return fail(SGE_ERR_ALIGN, "grouped_linear_dgrad_mxfp8: pointers must be 16-byte aligned");
   const int64_t GN = (int64_t)G * N;
-  const Range in[5] = {range_of(dy_q, T, N, N, 1), range_of(dy_s, T, N / 32, N / 32, 1), range_of(w_q, K, GN, GN, 1),
+  if (dact_colT_q)
+    if (sge_status st = check_colT("grouped_linear_dgrad_mxfp8", T, G, layout, ld_t, dact_colT_q, dact_colT_s)) return st;
+  const Range in[6] = {range_of(dy_q, T, N, N, 1), range_of(dy_s, T, N / 32, N / 32, 1), range_of(w_q, K, GN, GN, 1),
                        range_of(w_s, K, GN / 32, GN / 32, 1),
-                       swiglu ? range_of(preact, T, hw, hw, 2) : Range{0, 0}};
-  const Range outs[4] = {(dx && !swiglu) ? range_of(dx, T, K, K, 2) : Range{0, 0},
+                       swiglu ? range_of(preact, T, hw, hw, 2) : Range{0, 0},
+                       dact_colT_q ? range_of(layout, 2, G + 1, G + 1, 8) : Range{0, 0}};
+  const Range outs[6] = {(dx && !swiglu) ? range_of(dx, T, K, K, 2) : Range{0, 0},
                          (swiglu && dact) ? range_of(dact, T, hw, hw, 2) : Range{0, 0},
                          dact_q ? range_of(dact_q, T, hw, hw, 1) : Range{0, 0},
-                         dact_s ? range_of(dact_s, T, hw / 32, hw / 32, 1) : Range{0, 0}};
-  for (int a = 0; a < 4; ++a) {
+                         dact_s ? range_of(dact_s, T, hw / 32, hw / 32, 1) : Range{0, 0},
+                         dact_colT_q ? range_of(dact_colT_q, hw, ld_t, ld_t, 1) : Range{0, 0},
+                         dact_colT_s ? range_of(dact_colT_s, hw, ld_t / 32, ld_t / 32, 1) : Range{0, 0}};
+  for (int a = 0; a < 6; ++a) {
     for (const Range& i : in)
       if (overlap(outs[a], i)) return fail(SGE_ERR_ALIAS, "grouped_linear_dgrad_mxfp8: outputs overlap inputs");
-    for (int b = a + 1; b < 4; ++b)
+    for (int b = a + 1; b < 6; ++b)
       if (overlap(outs[a], outs[b])) return fail(SGE_ERR_ALIAS, "grouped_linear_dgrad_mxfp8: outputs overlap");
   }
   const size_t need = sge_grouped_linear_bwd_workspace_size(T, K, G, epilogue);
@@ -739,6 +776,10 @@ sge_status sge_grouped_linear_dgrad_mxfp8(const void* dy_q, const void* dy_s, co
     p.q_out = static_cast<uint8_t*>(dact_q);
     p.s_out = static_cast<uint8_t*>(dact_s);
     p.ld_q = hw;
+    p.qt_out = static_cast<uint8_t*>(dact_colT_q);
+    p.st_out = static_cast<uint8_t*>(dact_colT_s);
+    p.ld_t = ld_t;
+    p.mx_layout = layout;
   }
   set_act(p, epilogue, act_params);
   hipError_t e = sge::launch_grouped_dgrad_mx(p, epilogue, stream);

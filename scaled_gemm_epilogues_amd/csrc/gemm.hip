@@ -347,6 +347,79 @@ constexpr int tile_sc_bytes(int fmt, int sched, int epi) {
   return fmt == F_MX ? (deep_pipe(fmt, sched, epi) ? 2 * 512 * 16 + 1024 : 2 * 512 * 16) : 32;
 }
 
+// Token-blocked MXFP8 of one 32-row block of two adjacent columns of an epilogue's bf16 output,
+// read back from the staged tile: `rows` is the tile's fp32 staging (BN floats per row) whose
+// slot(rl) float of row rl now holds the two bf16 values as one packed pair (low half: the first
+// column). Each column gets the E8M0 exponent of its block's bf16 magnitude maximum and 32 E4M3
+// codes, exactly as the token-blocked quantizer makes them from the bf16 tensor; when ok, the
+// codes go to q (first column) and q + ld_t (second), 32 contiguous bytes each. Returns the two
+// E8M0 bytes (first column's in bits 0-7, second's in bits 8-15).
+template <int BN, class Slot>
+__device__ __forceinline__ uint32_t mx_colT_block(const float* rows, int rl0, const Slot& slot, uint8_t* q,
+                                                  int64_t ld_t, bool ok) {
+  uint32_t v[32];
+#pragma unroll
+  for (int r = 0; r < 32; ++r) v[r] = __builtin_bit_cast(uint32_t, rows[(rl0 + r) * BN + slot(rl0 + r)]);
+  uint32_t mlo = 0, mhi = 0;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    const uint32_t lo = v[r] & 0x7FFFu, hi = (v[r] >> 16) & 0x7FFFu;
+    mlo = lo > mlo ? lo : mlo;
+    mhi = hi > mhi ? hi : mhi;
+  }
+  const int xlo = mx_exponent(mlo), xhi = mx_exponent(mhi);
+  const float slo = pow2_neg(xlo), shi = pow2_neg(xhi);
+  v4i qlo[2], qhi[2];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t* w = v + 4 * k;
+    qlo[k >> 2][k & 3] = (int)(e4m3x2(bf16_lo(w[0]) * slo, bf16_lo(w[1]) * slo) |
+                               (e4m3x2(bf16_lo(w[2]) * slo, bf16_lo(w[3]) * slo) << 16));
+    qhi[k >> 2][k & 3] = (int)(e4m3x2(bf16_hi(w[0]) * shi, bf16_hi(w[1]) * shi) |
+                               (e4m3x2(bf16_hi(w[2]) * shi, bf16_hi(w[3]) * shi) << 16));
+  }
+  if (ok) {
+    reinterpret_cast<v4i*>(q)[0] = qlo[0];
+    reinterpret_cast<v4i*>(q)[1] = qlo[1];
+    reinterpret_cast<v4i*>(q + ld_t)[0] = qhi[0];
+    reinterpret_cast<v4i*>(q + ld_t)[1] = qhi[1];
+  }
+  return (uint32_t)(xlo + 127) | ((uint32_t)(xhi + 127) << 8);
+}
+
+// The token-blocked output of one pass for a thread: two adjacent output columns whose bf16
+// pairs overwrote float dw of the staged granule that sits at slot gran ^ (rl % 16) of each row
+// rl, blocks k0 .. k0 + NB - 1 of the pass's four (rows 32 k .. + 31; rows 64+ in half1). feat
+// is the first column's index in the token-blocked arrays, pos the pass's first position.
+template <int BN, int NB>
+__device__ __forceinline__ void mx_colT_run(const uint8_t* half0, const uint8_t* half1, int gran, int dw, int k0,
+                                            uint8_t* qt, uint8_t* st, int64_t ld_t, int64_t feat, int64_t pos, bool ok) {
+  auto slot = [&](int rl) { return ((gran ^ (rl & 15)) << 2) | dw; };
+  uint32_t elo = 0, ehi = 0;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int k = k0 + b;
+    const uint32_t e = mx_colT_block<BN>(reinterpret_cast<const float*>(k >= 2 ? half1 : half0), 32 * (k & 1), slot,
+                                         qt + feat * ld_t + pos + 32 * k, ld_t, ok);
+    elo |= (e & 0xFFu) << (8 * b);
+    ehi |= (e >> 8) << (8 * b);
+  }
+  if (ok) {
+    uint8_t* s = st + feat * (ld_t / 32) + (pos >> 5) + k0;
+    if constexpr (NB == 4) {
+      *reinterpret_cast<uint32_t*>(s) = elo;
+      *reinterpret_cast<uint32_t*>(s + ld_t / 32) = ehi;
+    } else if constexpr (NB == 2) {
+      *reinterpret_cast<uint16_t*>(s) = (uint16_t)elo;
+      *reinterpret_cast<uint16_t*>(s + ld_t / 32) = (uint16_t)ehi;
+    } else {
+      static_assert(NB == 1, "one, two or four blocks");
+      s[0] = (uint8_t)elo;
+      s[ld_t / 32] = (uint8_t)ehi;
+    }
+  }
+}
+
 // One output tile of one GEMM: tile number blk of the launch's tiles of this GEMM (a workgroup
 // with blk % 8 == x runs on XCD x). lds_ (128 KB), sc_ (tile_sc_bytes) and amax_slot_ are the
 // workgroup's LDS, which tiles of different GEMMs in one launch share.
@@ -387,6 +460,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
   uint16_t* cptr = p.c;
   int nt;
   int grp = 0;                                           // the group (E4M3 per-group scales)
+  int64_t grp_lo = 0;                                    // row-partitioned: the group's first row
   if constexpr (SCHED == S_DENSE) {
     const int MT = p.mt_count, NT = p.nt_count;
     if (blk >= MT * NT) return;
@@ -443,6 +517,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
     const int lin = first + in_band % gsz;
     nt = in_band / gsz;
     grp = g;
+    grp_lo = lo;
     m0 = lo + (int64_t)lin * BM;
     row_end = hi;
     n0 = (int64_t)nt * (glu_fwd(EPI) ? BN / 2 : BN);
@@ -1103,6 +1178,38 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
       return make_float4(a * acc[i][j][4 * q + 0], a * acc[i][j][4 * q + 1], a * acc[i][j][4 * q + 2],
                          a * acc[i][j][4 * q + 3]);
   };
+  // Row-partitioned MXFP8 activation epilogues with qt_out also write their bf16 output
+  // token-blocked (the grouped wgrad operand): after a pass's items, each bf16 result sits in
+  // the staged tile over the fp32 values it came from (every thread overwrites only what it
+  // read), and threads then quantize it down the columns, 32 rows per block. A tile starts on
+  // its group's first row or BM rows later, so its rows are positions colt_pos0 + row of the
+  // group's 128-aligned range; a pass at or past colt_rows (the group's rows in the tile
+  // rounded up to 128) belongs to the next group and is not written, the rest of the range is
+  // padding quantized from zeros.
+  constexpr bool kColT = FMT == F_MX && SCHED == S_GROUP_M && EPI != E_STORE;
+  const bool colq = kColT && p.qt_out != nullptr;
+  int64_t colt_pos0 = 0;
+  int colt_rows = 0;
+  if (colq) {
+    colt_pos0 = p.mx_layout[p.G + 1 + grp] + (m0 - grp_lo);
+    const int64_t rem = row_end - m0;
+    colt_rows = rem >= BM ? BM : (int)((rem + 127) & ~(int64_t)127);
+  }
+  // The staged epilogues run two passes of 128 rows (rows 0-63 of a pass in LDS half0, 64-127
+  // in half1). These kernels take 128 consecutive rows per pass (wave row `pass` stages all its
+  // fragments), so each column's 128 codes of a pass fill one whole 128-byte line within the
+  // pass: measured, lines completed a pass apart cost far more than the codes themselves. The
+  // others take half of each wave row's rows per pass. Row of the tile of pass row rp:
+  constexpr bool kContig = kColT;
+  auto pass_row = [&](int pass, int rp) {
+    return kContig ? pass * WM + rp : (rp >> 6) * WM + pass * (WM / 2) + (rp & 63);
+  };
+  // A pass's run of codes for output column col is written: inside the tile's part of the
+  // group's range and of the ld_t columns.
+  auto colt_ok = [&](int64_t col, int pass) {
+    const int64_t pos = colt_pos0 + pass * WM;
+    return col < n_end && pass * WM < colt_rows && pos >= 0 && pos + WM <= p.ld_t;
+  };
 
   if constexpr (EPI == E_STORE || EPI == E_SRELU) {
     // Two passes over half of each wave's rows: alpha*acc (fp32) goes to LDS in row-major
@@ -1127,6 +1234,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
     constexpr int kIters = 128 * kChunks / (NWAVES * 64);  // chunks per thread per pass
     float* stage = reinterpret_cast<float*>(wm ? half1 : half0);
     // The residual of both passes is requested first: its HBM latency overlaps the staging.
+    // Output offset of a thread's item it of a pass (kOOB out of range); held across the
+    // epilogue except with the token-blocked output, whose kernels keep every accumulator
+    // live longer and recompute it instead.
+    auto out_off = [&](int pass, int it) {
+      const int id = it * NWAVES * 64 + threadIdx.x;
+      const int brow = pass_row(pass, id / kChunks);
+      const int64_t n = n0 + (id % kChunks) * 8;
+      return (m0 + brow < row_end && n < n_end) ? (int)(((int64_t)brow * p.ldc + n) * 2) : (int)kOOB;
+    };
     v4i res[2][kIters];
     int offs[2][kIters];
 #pragma unroll
@@ -1134,10 +1250,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
 #pragma unroll
       for (int it = 0; it < kIters; ++it) {
         const int id = it * NWAVES * 64 + threadIdx.x;
-        const int rp = id / kChunks, c = id % kChunks;     // row of the pass (0..127), chunk
-        const int brow = (rp >> 6) * WM + pass * (WM / 2) + (rp & 63);
-        const int64_t n = n0 + c * 8;
-        offs[pass][it] = (m0 + brow < row_end && n < n_end) ? (int)(((int64_t)brow * p.ldc + n) * 2) : (int)kOOB;
+        const int rp = id / kChunks;                       // row of the pass (0..127)
+        const int brow = pass_row(pass, rp);
+        if constexpr (!kContig) offs[pass][it] = out_off(pass, it);
         if (!kSR && p.accumulate) res[pass][it] = __builtin_amdgcn_raw_buffer_load_b128(rc, offs[pass][it], 0, 0);
         if constexpr (kSR)                                 // the row's scale p (res[.][.][0] carries it)
           res[pass][it][0] = __builtin_amdgcn_raw_buffer_load_b32(
@@ -1147,17 +1262,21 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-      for (int il = 0; il < WMF / 2; ++il) {
-        const int i = pass * (WMF / 2) + il;
+      for (int il = 0; il < (kContig ? WMF : WMF / 2); ++il) {
+        const int i = kContig ? il : pass * (WMF / 2) + il;
+        float* const st = kContig ? reinterpret_cast<float*>(il >= WMF / 2 ? half1 : half0) : stage;
+        const int rb = (kContig ? il % (WMF / 2) : il) * 32;
+        if (!kContig || wm == pass) {
 #pragma unroll
         for (int j = 0; j < WNF; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int r = il * 32 + acc_row(q);            // row within this wave row's half
+            const int r = rb + acc_row(q);            // row within its LDS half
             const int g = (wn * WN + j * 32 + acc_col(q)) >> 2;
             const float4 v = acc_get(i, j, q, alpha);
-            *reinterpret_cast<float4*>(stage + r * BN + ((g ^ (r & 15)) << 2)) = v;
+            *reinterpret_cast<float4*>(st + r * BN + ((g ^ (r & 15)) << 2)) = v;
           }
+        }
       }
       __syncthreads();
 #pragma unroll
@@ -1166,6 +1285,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
         const int rp = id / kChunks, c = id % kChunks;
         const float* row = reinterpret_cast<const float*>(rp >= 64 ? half1 : half0) + (rp & 63) * BN;
         const int sw = (rp & 63) & 15;
+        const int off = kContig ? out_off(pass, it) : offs[pass][it];
         const float4 lo = *reinterpret_cast<const float4*>(row + (((2 * c) ^ sw) << 2));
         const float4 hi = *reinterpret_cast<const float4*>(row + (((2 * c + 1) ^ sw) << 2));
         float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -1175,7 +1295,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
                           (int)pack_bf16x2(v[6], v[7])};
           __builtin_amdgcn_raw_buffer_store_b128(       // no pre-activation buffer: a zero-size resource
               vh, make_rsrc(p.aux ? p.aux + m0 * p.ld_aux : p.aux, p.aux ? rows_left * p.ld_aux * 2 : 0),
-              offs[pass][it], 0, 0);
+              off, 0, 0);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float rl = fmaxf(v[e], 0.0f);
@@ -1191,7 +1311,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
         }
         const v4i w = {(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3]), (int)pack_bf16x2(v[4], v[5]),
                        (int)pack_bf16x2(v[6], v[7])};
-        __builtin_amdgcn_raw_buffer_store_b128(w, rc, offs[pass][it], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(w, rc, off, 0, 0);
         if constexpr (kSR) {
           if constexpr (kAmax) {
 #pragma unroll
@@ -1202,10 +1322,24 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
             const int c = id % kChunks;
             int e8;
             const v2i qv = mx_quant_lane8(w, e8);          // every lane takes part
-            const int o = offs[pass][it];
+            const int o = off;
             __builtin_amdgcn_raw_buffer_store_b64(qv, rq, o == (int)kOOB ? (int)kOOB : o >> 1, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b8((char)e8, rs, (o == (int)kOOB || (c & 3)) ? (int)kOOB : o >> 6, 0, 0);
           }
+          if constexpr (kColT) {
+            if (colq)                                      // y over its first fp32 granule (zero outside)
+              *reinterpret_cast<float4*>(const_cast<float*>(row) + (((2 * c) ^ sw) << 2)) =
+                  __builtin_bit_cast(float4, off != (int)kOOB ? w : v4i{0, 0, 0, 0});
+          }
+        }
+      }
+      if constexpr (kSR && kColT) {
+        if (colq) {
+          __syncthreads();                                 // the pass's y is in the staged tile
+          // columns nl, nl + 1; lanes 0-31 take blocks 0-1 of the pass, lanes 32-63 blocks 2-3
+          const int nl = 64 * wave + 2 * (lane & 31);
+          mx_colT_run<BN, 2>(half0, half1, 2 * (nl >> 3), (nl & 7) >> 1, 2 * (lane >> 5), p.qt_out, p.st_out, p.ld_t,
+                             n0 + nl, colt_pos0 + pass * WM, colt_ok(n0 + nl, pass));
         }
       }
       if (pass == 0) __syncthreads();                      // stage reused by the second pass
@@ -1249,39 +1383,43 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-      for (int il = 0; il < WMF / 2; ++il) {
-        const int i = pass * (WMF / 2) + il;
+      for (int il = 0; il < (kContig ? WMF : WMF / 2); ++il) {
+        const int i = kContig ? il : pass * (WMF / 2) + il;
+        float* const st = kContig ? reinterpret_cast<float*>(il >= WMF / 2 ? half1 : half0) : stage;
+        const int rb = (kContig ? il % (WMF / 2) : il) * 32;
+        if (!kContig || wm == pass) {
 #pragma unroll
         for (int j = 0; j < WNF; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int r = il * 32 + acc_row(q);
+            const int r = rb + acc_row(q);
             const int g = (wn * WN + j * 32 + acc_col(q)) >> 2;
             const float4 v = acc_get(i, j, q, alpha);
-            *reinterpret_cast<float4*>(stage + r * BN + ((g ^ (r & 15) ^ wsw(wn)) << 2)) = v;
+            *reinterpret_cast<float4*>(st + r * BN + ((g ^ (r & 15) ^ wsw(wn)) << 2)) = v;
           }
+        }
       }
       __syncthreads();
       float pr[kIters];
-      int oy[kIters], oh[kIters], oq[kIters], os[kIters];
 #pragma unroll
       for (int it = 0; it < kIters; ++it) {
         const int id = it * NWAVES * 64 + threadIdx.x;
-        const int rp_ = id / kChunks, c = id % kChunks;
-        const int brow = (rp_ >> 6) * WM + pass * (WM / 2) + (rp_ & 63);
-        const int64_t n = n0 + c * 8;
-        const bool rok = m0 + brow < row_end;
-        const bool ok = rok && n < n_end;
-        oy[it] = ok ? (int)(((int64_t)brow * p.ldc + n) * 2) : (int)kOOB;
-        oh[it] = ok ? (int)(((int64_t)brow * p.ld_aux + n) * 2) : (int)kOOB;
-        oq[it] = ok ? (int)((int64_t)brow * p.ld_q + n) : (int)kOOB;
-        os[it] = (ok && (c & 3) == 0) ? (int)((int64_t)brow * (p.ld_q / 32) + (n >> 5)) : (int)kOOB;
-        pr[it] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, rok ? brow * 4 : (int)kOOB, 0, 0));
+        const int brow = pass_row(pass, id / kChunks);
+        pr[it] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                               rp, m0 + brow < row_end ? brow * 4 : (int)kOOB, 0, 0));
       }
 #pragma unroll
       for (int it = 0; it < kIters; ++it) {
         const int id = it * NWAVES * 64 + threadIdx.x;
         const int rp_ = id / kChunks, c = id % kChunks;
+        // output offsets (out-of-range: kOOB), computed here rather than held across the loop
+        const int brow = pass_row(pass, rp_);
+        const int64_t n = n0 + c * 8;
+        const bool ok = m0 + brow < row_end && n < n_end;
+        const int oy = ok ? (int)(((int64_t)brow * p.ldc + n) * 2) : (int)kOOB;
+        const int oh = ok ? (int)(((int64_t)brow * p.ld_aux + n) * 2) : (int)kOOB;
+        const int oq = ok ? (int)((int64_t)brow * p.ld_q + n) : (int)kOOB;
+        const int os = (ok && (c & 3) == 0) ? (int)((int64_t)brow * (p.ld_q / 32) + (n >> 5)) : (int)kOOB;
         const int rr = rp_ & 63, wc = c / kCpw, cc = c % kCpw;
         const float* row = reinterpret_cast<const float*>(rp_ >= 64 ? half1 : half0) + rr * BN;
         const int x = (rr & 15) ^ wsw(wc);
@@ -1311,9 +1449,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
                         (int)pack_bf16x2(b[6], b[7])};
         const v4i vy = {(int)pack_bf16x2(y[0], y[1]), (int)pack_bf16x2(y[2], y[3]), (int)pack_bf16x2(y[4], y[5]),
                         (int)pack_bf16x2(y[6], y[7])};
-        __builtin_amdgcn_raw_buffer_store_b128(va, rha, oh[it], 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(vb, rhb, oh[it], 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(vy, ry, oy[it], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(va, rha, oh, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(vb, rhb, oh, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(vy, ry, oy, 0, 0);
         if constexpr (kAmax) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) amax_acc = fmaxf(amax_acc, fabsf(y[e]));
@@ -1321,8 +1459,25 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
         if (mxq) {
           int e8;
           const v2i qv = mx_quant_lane8(vy, e8);
-          __builtin_amdgcn_raw_buffer_store_b64(qv, rq, oq[it], 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b8((char)e8, rs, os[it], 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(qv, rq, oq, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b8((char)e8, rs, os, 0, 0);
+        }
+        if constexpr (kColT) {
+          if (colq)                                        // y over the gate's first granule (zero outside)
+            *reinterpret_cast<float4*>(const_cast<float*>(row) + ((ga ^ x) << 2)) =
+                __builtin_bit_cast(float4, ok ? vy : v4i{0, 0, 0, 0});
+        }
+      }
+      if constexpr (kColT) {
+        if (colq) {
+          static_assert(WGN == 2 && kCpw == 8, "two wave columns of 8 output chunks");
+          __syncthreads();                                 // the pass's y is in the staged tile
+          // Wave w: block w of the pass; lane l: output columns 2l, 2l + 1. Per row the 64 lanes
+          // read 16 distinct granules (the wave columns' XORs differ in bit 0).
+          const int yc = 2 * lane, wc = yc / (8 * kCpw);
+          const int gran = (wc * kGpw + 2 * ((yc >> 3) % kCpw)) ^ wsw(wc);
+          mx_colT_run<BN, 1>(half0, half1, gran, (yc & 7) >> 1, wave, p.qt_out, p.st_out, p.ld_t, n0 + yc,
+                             colt_pos0 + pass * WM, colt_ok(n0 + yc, pass));
         }
       }
       if (pass == 0) __syncthreads();                      // stage reused by the second pass
@@ -1373,17 +1528,21 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-      for (int il = 0; il < WMF / 2; ++il) {
-        const int i = pass * (WMF / 2) + il;
+      for (int il = 0; il < (kContig ? WMF : WMF / 2); ++il) {
+        const int i = kContig ? il : pass * (WMF / 2) + il;
+        float* const st = kContig ? reinterpret_cast<float*>(il >= WMF / 2 ? half1 : half0) : stage;
+        const int rb = (kContig ? il % (WMF / 2) : il) * 32;
+        if (!kContig || wm == pass) {
 #pragma unroll
         for (int j = 0; j < WNF; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int r = il * 32 + acc_row(q);
+            const int r = rb + acc_row(q);
             const int g = (wn * WN + j * 32 + acc_col(q)) >> 2;
             const float4 v = acc_get(i, j, q, alpha);
-            *reinterpret_cast<float4*>(stage + r * BN + ((g ^ (r & 15)) << 2)) = v;
+            *reinterpret_cast<float4*>(st + r * BN + ((g ^ (r & 15)) << 2)) = v;
           }
+        }
       }
       __syncthreads();
       // Chunks go in batches of SGE_DSWIGLU_BATCH (all loads of a batch in flight together),
@@ -1401,7 +1560,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
         const int it = it0 + ib;
         const int id = it * NWAVES * 64 + threadIdx.x;
         const int rp_ = id / kChunks, c = id % kChunks;
-        const int brow = (rp_ >> 6) * WM + pass * (WM / 2) + (rp_ & 63);
+        const int brow = pass_row(pass, rp_);
         const int64_t n = n0 + c * 8;
         const bool rok = m0 + brow < row_end;
         const bool ok = rok && n < n_end;
@@ -1484,12 +1643,41 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
             __builtin_amdgcn_raw_buffer_store_b8((char)eb, rs, os + fb / 64, 0, 0);
           }
         }
+        if constexpr (kColT) {
+          if (colq) {                                      // da, db over their fp32 granules (zero outside)
+            const bool okw = od[ib] != (int)kOOB;
+            float* wrow = const_cast<float*>(row);
+            *reinterpret_cast<float4*>(wrow + (((2 * c) ^ sw) << 2)) = __builtin_bit_cast(float4, okw ? va : v4i{0, 0, 0, 0});
+            if constexpr (!kSR)
+              *reinterpret_cast<float4*>(wrow + (((2 * c + 1) ^ sw) << 2)) =
+                  __builtin_bit_cast(float4, okw ? vb : v4i{0, 0, 0, 0});
+          }
+        }
         // the row's 32 chunks are lanes c = 0..31 of one half-wave: fixed-order tree sum
 #pragma unroll
         for (int d = 1; d < 32; d <<= 1) part += __shfl_xor(part, d, 64);
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, part), rpart, c == 0 ? orow[ib] : (int)kOOB,
                                               0, 0);
       }
+      }
+      if constexpr (kColT) {
+        if (colq) {
+          __syncthreads();                                 // the pass's da / db are in the staged tile
+          // Columns nl, nl + 1 of da (lanes 0-31) and of db (32-63, gated activations), all four
+          // blocks of the pass; per row a wave reads 16 distinct granules. SReLU (da only): lanes
+          // 32-63 take blocks 2-3 instead.
+          const int nl = 64 * wave + 2 * (lane & 31);
+          const int64_t pos = colt_pos0 + pass * WM;
+          const bool ok = colt_ok(n0 + nl, pass);
+          if constexpr (kSR) {
+            mx_colT_run<BN, 2>(half0, half1, 2 * (nl >> 3), (nl & 7) >> 1, 2 * (lane >> 5), p.qt_out, p.st_out,
+                               p.ld_t, n0 + nl, pos, ok);
+          } else {
+            const int side = lane >> 5;
+            mx_colT_run<BN, 4>(half0, half1, 2 * (nl >> 3) + side, (nl & 7) >> 1, 0, p.qt_out, p.st_out, p.ld_t,
+                               n0 + nl + (side ? p.F : 0), pos, ok);
+          }
+        }
       }
       if (pass == 0) __syncthreads();                      // stage reused by the second pass
     }

@@ -48,6 +48,12 @@ struct GemmParams {
   float* amax_out;            // (d)SwiGLU: per-group amax of the bf16 output, atomic max (zeroed by the caller)
   float act_limit;            // clamped SwiGLU: the clamp bound (gate above, up half both ways)
   float act_alpha;            //   and the gate's sigmoid slope
+  // Row-partitioned MXFP8 activation epilogues: the activation output also quantized with
+  // blocks of 32 along each group's tokens (the grouped wgrad operand), stored transposed.
+  uint8_t* qt_out;            // E4M3 [cols][ld_t], group g's token t at column pad[g] + t - c[g] (or NULL)
+  uint8_t* st_out;            //   and its E8M0 scales [cols][ld_t / 32]
+  int64_t ld_t;
+  const int64_t* mx_layout;   //   [2][G+1]: clamped offsets c, then the 128-aligned group starts pad
 };
 
 hipError_t launch_gemm(const GemmParams& p, int fmt, bool a_kmaj, bool b_kmaj, hipStream_t s);

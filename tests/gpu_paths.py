@@ -149,7 +149,8 @@ def _act_params(act):
 
 def run_grouped_mlp_fwd_mx(inp, act="swiglu"):
     """MXFP8 grouped MLP forward: quantize x, W1, W2 rowwise; fc1 + the scaled activation
-    emitting y as bf16 and as MXFP8 rowwise; fc2 on the MXFP8 y."""
+    emitting y as bf16, as MXFP8 rowwise and token-blocked (the fc2 wgrad operand); fc2 on the
+    MXFP8 y."""
     X, W1, W2 = dev_bf16(inp["x"]), dev_bf16(inp["w1"]), dev_bf16(inp["w2"])
     P = torch.from_numpy(inp["p"]).cuda()
     T, H = X.shape
@@ -168,15 +169,20 @@ def run_grouped_mlp_fwd_mx(inp, act="swiglu"):
     yq = torch.empty(T, F, dtype=torch.uint8, device="cuda")
     ys = torch.empty(T, F // 32, dtype=torch.uint8, device="cuda")
     out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    lay = mx_layout(base, T)
+    ld = sge.mx_token_capacity(T, G)
+    q_y = {"q_colT": torch.empty(F, ld, dtype=torch.uint8, device="cuda"),
+           "s_colT": torch.empty(F, ld // 32, dtype=torch.uint8, device="cuda"), "ld": ld}
     sge.grouped_linear_fwd_mxfp8(qx["q_row"], qx["s_row"], qw1["q_row"].reshape(G, N1, H),
                                  qw1["s_row"].reshape(G, N1, H // 32), base, out=y, epilogue=fwd_epi,
-                                 probs=P, preact=h, out_q=yq, out_s=ys, act=_act_params(act))
+                                 probs=P, preact=h, out_q=yq, out_s=ys, act=_act_params(act), layout=lay,
+                                 out_colT_q=q_y["q_colT"], out_colT_s=q_y["s_colT"])
     sge.grouped_linear_fwd_mxfp8(yq, ys, qw2["q_row"].reshape(G, H, F), qw2["s_row"].reshape(G, H, F // 32), base,
                                  out=out)
     y_unfused = quant_mx(y, col=False)                    # the standalone quantizer on the bf16 y
     torch.cuda.synchronize()
     return {"err": err, "qx": qx, "qw1": qw1, "qw2": qw2, "h": h, "y": y, "yq": yq, "ys": ys, "out": out,
-            "y_unfused": y_unfused, "base": base, "act": act}
+            "y_unfused": y_unfused, "base": base, "act": act, "lay": lay, "q_y": q_y}
 
 
 # ------------------------------------------------------- MXFP8 grouped backward
@@ -205,10 +211,13 @@ def quant_mx_grouped(t, lay, row=False, fill=None):
     return out
 
 
-def grouped_dgrad_mx(q_dy, w_colT, base, alpha=1.0, preact=None, probs=None, want_q=False, act="swiglu"):
+def grouped_dgrad_mx(q_dy, w_colT, base, alpha=1.0, preact=None, probs=None, want_q=False, act="swiglu",
+                     lay=None, want_bf16=True, fill=0xAB):
     """MXFP8 grouped dgrad from a rowwise-quantized dy and W's columnwise copy [K, G*N].
     With ``preact`` the scaled activation's backward runs in the epilogue (dact, dprobs, and
-    the MXFP8 dact when ``want_q``); otherwise dx [T, K] is returned."""
+    the MXFP8 dact when ``want_q``; with the layout ``lay`` also the token-blocked dact, whose
+    buffers start filled with ``fill``; ``want_bf16=False`` skips the bf16 dact); otherwise
+    dx [T, K] is returned."""
     T, N = q_dy["q_row"].shape
     K = w_colT["q_colT"].shape[0]
     G = base.numel() - 1
@@ -221,15 +230,22 @@ def grouped_dgrad_mx(q_dy, w_colT, base, alpha=1.0, preact=None, probs=None, wan
     _, _, epi = _act_epilogues(act)
     hw = K if act == "srelu" else 2 * K                  # gated activations: two halves
     ws = torch.empty(max(1, sge.grouped_linear_bwd_workspace_size(T, K, G, epi)), dtype=torch.uint8, device="cuda")
-    out["dact"] = torch.empty(T, hw, dtype=torch.bfloat16, device="cuda")
+    if want_bf16:
+        out["dact"] = torch.empty(T, hw, dtype=torch.bfloat16, device="cuda")
     out["dprobs"] = torch.empty(T, dtype=torch.float32, device="cuda")
     if want_q:
         out["dact_q"] = torch.empty(T, hw, dtype=torch.uint8, device="cuda")
         out["dact_s"] = torch.empty(T, hw // 32, dtype=torch.uint8, device="cuda")
+    if lay is not None:
+        ld = sge.mx_token_capacity(T, G)
+        out["ld"] = ld
+        out["q_colT"] = torch.full((hw, ld), fill, dtype=torch.uint8, device="cuda")
+        out["s_colT"] = torch.full((hw, ld // 32), fill, dtype=torch.uint8, device="cuda")
     sge.grouped_linear_dgrad_mxfp8(q_dy["q_row"], q_dy["s_row"], w_colT["q_colT"], w_colT["s_colT"], base,
                                    alpha=alpha, epilogue=epi, preact=preact, probs=probs,
-                                   dact=out["dact"], dprobs=out["dprobs"], dact_q=out.get("dact_q"),
-                                   dact_s=out.get("dact_s"), workspace=ws, act=_act_params(act))
+                                   dact=out.get("dact"), dprobs=out["dprobs"], dact_q=out.get("dact_q"),
+                                   dact_s=out.get("dact_s"), workspace=ws, act=_act_params(act), layout=lay,
+                                   dact_colT_q=out.get("q_colT"), dact_colT_s=out.get("s_colT"))
     return out
 
 
@@ -243,8 +259,9 @@ def grouped_wgrad_mx(qa, qb, lay, G, alpha=1.0):
 
 def run_grouped_mlp_bwd_mx(inp, fwd):
     """MXFP8 grouped MLP backward after ``run_grouped_mlp_fwd_mx``: fc2 dgrad with the fused
-    backward of the scaled activation and group quantize of dh, fc2 wgrad, fc1 dgrad on the
-    MXFP8 dh, fc1 wgrad; every wgrad operand token-blocked per group."""
+    backward of the scaled activation and group quantize of dh (rowwise and token-blocked),
+    fc2 wgrad, fc1 dgrad on the MXFP8 dh, fc1 wgrad; every wgrad operand token-blocked per
+    group (y's and dh's by the producing epilogues)."""
     X, W1, W2 = dev_bf16(inp["x"]), dev_bf16(inp["w1"]), dev_bf16(inp["w2"])
     DOUT = dev_bf16(inp["dout"])
     P = torch.from_numpy(inp["p"]).cuda()
@@ -253,15 +270,15 @@ def run_grouped_mlp_bwd_mx(inp, fwd):
     act = fwd["act"]
     F = _act_epilogues(act)[0](N1)
     base = fwd["base"]
-    lay = mx_layout(base, T)
+    lay = fwd["lay"]
     q_dout = quant_mx_grouped(DOUT, lay, row=True)
     w2c = quant_mx(W2.reshape(G * H, F), row=False, col=True)        # [F, G*H]
     w1c = quant_mx(W1.reshape(G * N1, H), row=False, col=True)       # [H, G*N1]
-    d2 = grouped_dgrad_mx(q_dout, w2c, base, preact=fwd["h"], probs=P, want_q=True, act=act)
-    q_y = quant_mx_grouped(fwd["y"], lay)
+    d2 = grouped_dgrad_mx(q_dout, w2c, base, preact=fwd["h"], probs=P, want_q=True, act=act, lay=lay)
+    q_y = fwd["q_y"]
     dw2 = grouped_wgrad_mx(q_dout, q_y, lay, G)
     d1 = grouped_dgrad_mx({"q_row": d2["dact_q"], "s_row": d2["dact_s"]}, w1c, base)
-    q_dh = quant_mx_grouped(d2["dact"], lay)
+    q_dh = {"q_colT": d2["q_colT"], "s_colT": d2["s_colT"], "ld": d2["ld"]}
     q_x = quant_mx_grouped(X, lay)
     dw1 = grouped_wgrad_mx(q_dh, q_x, lay, G)
     dh_unfused = quant_mx(d2["dact"], col=False)                     # the standalone quantizer on dh

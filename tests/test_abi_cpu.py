@@ -157,11 +157,13 @@ def test_grouped_mxfp8_validation_errors(sge):
     x_q, x_s, w_q, w_s, offs, probs = FAKE, FAKE * 64, FAKE * 128, FAKE * 4096, FAKE * 8192, FAKE * 8300
     y, h, yq, ys = FAKE * 10000, FAKE * 20000, FAKE * 30000, FAKE * 40000
     swiglu = sge.EPI_SCALED_SWIGLU
-    ok_args = (x_q, x_s, w_q, w_s, G, T, N, K, offs, 1.0, swiglu, probs, y, h, yq, ys, None)
+    lay, yT, yTs = FAKE * 50000, FAKE * 60000, FAKE * 70000
+    ld_t = sge.mx_token_capacity(T, G)
+    ok_args = (x_q, x_s, w_q, w_s, G, T, N, K, offs, 1.0, swiglu, probs, y, h, yq, ys, lay, ld_t, yT, yTs, None)
     assert f(*((None,) + ok_args[1:])) == sge.ERR_NULL                  # x_q
     args = list(ok_args); args[14] = None
     assert f(*args) == sge.ERR_NULL                                       # out_q without out_s
-    args = list(ok_args); args[12] = None; args[14] = None; args[15] = None
+    args = list(ok_args); args[12] = None; args[14] = None; args[15] = None; args[18] = None; args[19] = None
     assert f(*args) == sge.ERR_NULL                                       # no output at all
     args = list(ok_args); args[11] = None
     assert f(*args) == sge.ERR_NULL                                       # SwiGLU needs probs
@@ -177,6 +179,27 @@ def test_grouped_mxfp8_validation_errors(sge):
     assert f(*args) == sge.ERR_ALIAS                                      # out_q over x_q
     args = list(ok_args); args[15] = y
     assert f(*args) == sge.ERR_ALIAS                                      # out_s over out
+    # the token-blocked output
+    args = list(ok_args); args[19] = None
+    assert f(*args) == sge.ERR_NULL                                       # out_colT_q without out_colT_s
+    args = list(ok_args); args[16] = None
+    assert f(*args) == sge.ERR_NULL                                       # needs the layout
+    args = list(ok_args); args[17] = ld_t - 128
+    assert f(*args) == sge.ERR_SHAPE                                      # ld_t below capacity
+    args = list(ok_args); args[17] = ld_t + 64
+    assert f(*args) == sge.ERR_SHAPE                                      # ld_t % 128
+    args = list(ok_args); args[10] = sge.EPI_NONE; args[14] = None; args[15] = None
+    assert f(*args) == sge.ERR_ARG                                        # needs an activation epilogue
+    args = list(ok_args); args[18] = FAKE * 60000 + 8
+    assert f(*args) == sge.ERR_ALIGN
+    args = list(ok_args); args[19] = FAKE * 70000 + 4
+    assert f(*args) == sge.ERR_ALIGN                                      # out_colT_s too (word stores)
+    args = list(ok_args); args[18] = x_q
+    assert f(*args) == sge.ERR_ALIAS                                      # out_colT_q over x_q
+    args = list(ok_args); args[19] = lay
+    assert f(*args) == sge.ERR_ALIAS                                      # out_colT_s over the layout
+    args = list(ok_args); args[18] = y
+    assert f(*args) == sge.ERR_ALIAS                                      # out_colT_q over out
 
 
 
@@ -223,11 +246,12 @@ def test_mxfp8_grouped_backward_validation_errors(sge):
     G, T, N, K = 4, 100, 256, 512
     sw = sge.EPI_DSCALED_SWIGLU
     ws = sge.grouped_linear_bwd_workspace_size(T, K, G, sw)
+    ld_t = sge.mx_token_capacity(T, G)
     ok = [B(1), B(2), B(3), B(4), G, T, N, K, B(5), 1.0, sw, B(6), B(7), None,
-          B(8), B(9), B(10), B(11), B(12), ws, None]
+          B(8), B(9), B(10), B(11), B(16), ld_t, B(14), B(20), B(12), ws, None]
     a = list(ok); a[11] = None
     assert d(*a) == sge.ERR_NULL                                          # SwiGLU needs preact
-    a = list(ok); a[14] = None; a[16] = None; a[17] = None
+    a = list(ok); a[14] = None; a[16] = None; a[17] = None; a[20] = None; a[21] = None
     assert d(*a) == sge.ERR_NULL                                          # no output
     a = list(ok); a[17] = None
     assert d(*a) == sge.ERR_NULL                                          # dact_q without dact_s
@@ -243,8 +267,22 @@ def test_mxfp8_grouped_backward_validation_errors(sge):
     assert d(*a) == sge.ERR_ALIAS                                         # dact over preact
     a = list(ok); a[16] = B(8)
     assert d(*a) == sge.ERR_ALIAS                                         # dact_q over dact
-    a = list(ok); a[19] = ws - 4
+    a = list(ok); a[23] = ws - 4
     assert d(*a) == sge.ERR_WORKSPACE
+    a = list(ok); a[21] = None
+    assert d(*a) == sge.ERR_NULL                                          # dact_colT_q without dact_colT_s
+    a = list(ok); a[18] = None
+    assert d(*a) == sge.ERR_NULL                                          # needs the layout
+    a = list(ok); a[19] = ld_t - 128
+    assert d(*a) == sge.ERR_SHAPE                                         # ld_t below capacity
+    a = list(ok); a[10] = sge.EPI_NONE; a[13] = B(15); a[16] = None; a[17] = None
+    assert d(*a) == sge.ERR_ARG                                           # token-blocked output needs SwiGLU
+    a = list(ok); a[20] = B(14) + 8
+    assert d(*a) == sge.ERR_ALIGN
+    a = list(ok); a[20] = B(6)
+    assert d(*a) == sge.ERR_ALIAS                                         # dact_colT_q over preact
+    a = list(ok); a[21] = B(8)
+    assert d(*a) == sge.ERR_ALIAS                                         # dact_colT_s over dact
 
     w = sge._lib.sge_grouped_linear_wgrad_mxfp8
     ok = [B(1), B(2), B(3), B(4), G, N, K, B(5), 640, 1.0, B(6), None]
@@ -393,14 +431,14 @@ def test_srelu_epilogue_validation(sge):
     assert f(B(1), B(2), 4, 100, 264, 256, B(3), 1.0, sge.EPI_SCALED_SRELU, None, B(4), B(5), None) == sge.ERR_NULL
     fm = _act_after(sge._lib.sge_grouped_linear_fwd_mxfp8, 10)
     assert fm(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, sge.EPI_SCALED_SRELU, None, B(7), B(8),
-              None, None, None) == sge.ERR_NULL                            # MXFP8 SReLU needs probs
+              None, None, None, 0, None, None, None) == sge.ERR_NULL       # MXFP8 SReLU needs probs
     assert fm(B(1), B(2), B(3), B(4), 4, 100, 264, 256, B(5), 1.0, sge.EPI_SCALED_SRELU, B(6), B(7), B(8),
-              B(9), B(10), None) == sge.ERR_SHAPE                          # MXFP8 output: N % 32
+              B(9), B(10), None, 0, None, None, None) == sge.ERR_SHAPE     # MXFP8 output: N % 32
     assert fm(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, sge.EPI_NONE, None, B(7), None,
-              B(9), B(10), None) == sge.ERR_ARG                            # MXFP8 output needs an activation
+              B(9), B(10), None, 0, None, None, None) == sge.ERR_ARG       # MXFP8 output needs an activation
     dm = _act_after(sge._lib.sge_grouped_linear_dgrad_mxfp8, 10)
     assert dm(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, sge.EPI_DSCALED_SRELU, None, B(6), None, B(7),
-              B(8), None, None, B(9), 1 << 20, None) == sge.ERR_NULL        # the backward needs preact
+              B(8), None, None, None, 0, None, None, B(9), 1 << 20, None) == sge.ERR_NULL   # needs preact
     ff = _act_after(sge._lib.sge_grouped_linear_fwd_fp8, 10)
     assert ff(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, sge.EPI_NONE, None, B(7), None, B(8),
               None) == sge.ERR_ARG                                         # a fused amax needs an activation
@@ -441,10 +479,10 @@ def test_clamped_swiglu_epilogue_validation(sge):
              None, B(8), 16, None) == sge.ERR_WORKSPACE
     fm = _act_after(sge._lib.sge_grouped_linear_fwd_mxfp8, 10)
     assert fm(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, cf, B(6), B(7), B(8),
-              None, None, None) == sge.ERR_NULL                            # MXFP8: act missing
+              None, None, None, 0, None, None, None) == sge.ERR_NULL       # MXFP8: act missing
     dm = _act_after(sge._lib.sge_grouped_linear_dgrad_mxfp8, 10, sge._act((0.0, 1.0)))
     assert dm(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, cb, B(6), B(7), None, B(8),
-              B(9), None, None, B(10), 1 << 20, None) == sge.ERR_ARG       # MXFP8 dgrad: bad limit
+              B(9), None, None, None, 0, None, None, B(10), 1 << 20, None) == sge.ERR_ARG   # bad limit
     ff = _act_after(sge._lib.sge_grouped_linear_fwd_fp8, 10)
     assert ff(B(1), B(2), B(3), B(4), 4, 100, 256, 256, B(5), 1.0, cf, B(6), B(7), B(8), None,
               None) == sge.ERR_NULL                                        # FP8: act missing

@@ -151,6 +151,58 @@ def test_grouped_dgrad_mxfp8_dswiglu_fused_quantize(case):
                             what="dact (MXFP8)")
 
 
+COLT_CASES = {
+    "ragged_with_empty_groups": ([300, 0, 211, 9, 0, 40], 256, 384),
+    # whole tiles, a group ending 127 rows into its second tile's aligned range, an empty one
+    "tile_multiples": ([512, 256, 129, 0, 383], 128, 256),
+    "dirichlet_6": (None, 256, 128),
+}
+
+
+@pytest.mark.parametrize("act", ["swiglu", "srelu", CLAMPED], ids=["swiglu", "srelu", "clamped_swiglu"])
+@pytest.mark.parametrize("case", list(COLT_CASES))
+def test_grouped_dgrad_mxfp8_token_blocked_output(case, act):
+    """The dgrad epilogue's token-blocked dact: bit-exact against the oracle's token blocking of
+    the same launch's bf16 dact and against the standalone token-blocked quantizer, padding
+    included; nothing written past the last group's range; the same bytes (and the same
+    rowwise MXFP8) without the bf16 dact."""
+    splits, N, K = COLT_CASES[case]
+    if splits is None:
+        splits = synth.dirichlet_splits(np.random.default_rng(6), 6, 900)
+    T, G = int(sum(splits)), len(splits)
+    hw = K if act == "srelu" else 2 * K
+    print(f"case mx grouped dgrad token-blocked {case} {act} T={T} G={G} N={N} K={K}", flush=True)
+    r = synth.streams(16)
+    dy = synth.normal_bf16(r["dy"], (T, N), 1e-2)
+    w = synth.normal_bf16(r["w"], (G, N, K), 0.02)
+    h = synth.normal_bf16(r["x"], (T, hw), 1.0)
+    p = r["p"].random(size=T, dtype=np.float32)
+    base = offsets.base_offsets(splits)
+    W = dev_bf16(w)
+    q_dy = quant_mx(dev_bf16(dy), col=False)
+    w_col = quant_mx(W.reshape(G * N, K), row=False)
+    lay = mx_layout(dev(base), T)
+    kw = dict(preact=dev_bf16(h), probs=dev(p), act=act, lay=lay)
+    out = grouped_dgrad_mx(q_dy, w_col, dev(base), want_q=True, **kw)
+    alone = grouped_dgrad_mx(q_dy, w_col, dev(base), want_q=True, want_bf16=False, fill=0x5C, **kw)
+    std = quant_mx_grouped(out["dact"], lay)
+    torch.cuda.synchronize()
+    c, pad = quant.mx_group_layout(base, T)
+    P = int(pad[-1])
+    q, s = quant.mxfp8_colwise_grouped(host_bits(out["dact"]), c, pad, out["ld"])
+    gq, gs = host_u8(out["q_colT"]), host_u8(out["s_colT"])
+    assert np.array_equal(gq[:, :P], q[:, :P]) and np.array_equal(gs[:, :P // 32], s[:, :P // 32])
+    assert np.all(gq[:, P:] == 0xAB) and np.all(gs[:, P // 32:] == 0xAB)
+    assert np.array_equal(gq[:, :P], host_u8(std["q_colT"])[:, :P])
+    assert np.array_equal(gs[:, :P // 32], host_u8(std["s_colT"])[:, :P // 32])
+    aq, as_ = host_u8(alone["q_colT"]), host_u8(alone["s_colT"])
+    assert np.array_equal(aq[:, :P], gq[:, :P]) and np.array_equal(as_[:, :P // 32], gs[:, :P // 32])
+    assert np.all(aq[:, P:] == 0x5C) and np.all(as_[:, P // 32:] == 0x5C)
+    assert np.array_equal(host_u8(alone["dact_q"]), host_u8(out["dact_q"]))
+    assert np.array_equal(host_u8(alone["dact_s"]), host_u8(out["dact_s"]))
+    assert np.array_equal(host_u8(alone["dprobs"]), host_u8(out["dprobs"]))
+
+
 WGRAD_CASES = {
     "ragged_with_empty_groups": ([300, 0, 211, 9, 0, 40], 256, 192),
     "dirichlet_wide": (None, 512, 384),
@@ -211,7 +263,8 @@ def test_mxfp8_grouped_mlp_backward(case, act):
     assert_oracle_mx_rowwise(host_bits(got["dh"]), host_u8(got["dhq"]), host_u8(got["dhs"]), what="dh (fused MXFP8)")
     assert np.array_equal(host_u8(got["dhq"]), host_u8(got["dh_unfused"]["q_row"]))
     assert np.array_equal(host_u8(got["dhs"]), host_u8(got["dh_unfused"]["s_row"]))
-    # the token-blocked wgrad operands of y and dh: the oracle's blocking of the GPU's bf16 tensors
+    # the token-blocked wgrad operands of y and dh, written by the producing epilogues: the
+    # oracle's blocking of the same launches' bf16 tensors
     c, pad = quant.mx_group_layout(base, T)
     P = int(pad[-1])
     for key, src in (("q_y", fwd["y"]), ("q_dh", got["dh"])):
