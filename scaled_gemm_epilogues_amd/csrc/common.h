@@ -83,28 +83,59 @@ __device__ __forceinline__ T wave_max(T v) {
 typedef int v4i __attribute__((__vector_size__(4 * sizeof(int))));
 typedef int v2i __attribute__((__vector_size__(2 * sizeof(int))));
 
+// ---------------------------------------------- MXFP8 with gfx950's scaled conversion
+// v_cvt_scalef32_pk_fp8_bf16 converts two packed bf16 values to E4M3 divided by 2^E, where E is
+// taken from the exponent field of its fp32 scale operand alone (E8M0: field 0 is 2^-127), with
+// round-to-nearest-even, and turns magnitudes past 448 (after rounding) into 448 or NaN. Measured
+// on MI355X over every bf16 pattern at block exponents -127 .. 120: in range it matches the
+// fp32 route (scale by 2^-X, clamp to +-448, v_cvt_pk_fp8_f32) bit for bit, so clamping the
+// bf16 magnitudes to 448 * 2^X first makes the two routes agree on every finite input.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// The packed magnitude maximum of two bf16 lanes: per-half max of (v & 0x7FFF).
+__device__ __forceinline__ uint32_t pk_absmax_bits(uint32_t m, uint32_t v) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, m),
+                                                                __builtin_bit_cast(u16x2, v & 0x7FFF7FFFu)));
+}
+// bf16 bits of 448 * 2^X, the largest magnitude a block with exponent X encodes (X <= 119 for
+// a finite block; larger X come only from Inf / NaN maxima and are held at 119).
+__device__ __forceinline__ uint32_t mx_bound_bits(int X) { return ((uint32_t)((X > 119 ? 119 : X) + 135) << 7) | 0x60u; }
+// Two packed bf16 with each magnitude clamped to its half of bound2, signs kept.
+__device__ __forceinline__ uint32_t clamp_pair(uint32_t v, uint32_t bound2) {
+  const u16x2 m = __builtin_elementwise_min(__builtin_bit_cast(u16x2, v & 0x7FFF7FFFu), __builtin_bit_cast(u16x2, bound2));
+  return __builtin_bit_cast(uint32_t, m) | (v & 0x80008000u);
+}
+// The scale operand for block exponent X: E8M0 byte X + 127 in the fp32 exponent field.
+__device__ __forceinline__ float mx_scale_operand(int X) { return __builtin_bit_cast(float, (uint32_t)(X + 127) << 23); }
+// E4M3 codes of four values, packed bf16 pairs p01 (values 0, 1) and p23 (2, 3), already
+// clamped, at block exponent given by `scale`: bytes 0..3 of the result.
+__device__ __forceinline__ uint32_t e4m3x4_scaled(uint32_t p01, uint32_t p23, float scale) {
+  s16x2 q = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(s16x2{0, 0}, __builtin_bit_cast(bf16x2v, p01), scale, false);
+  q = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(q, __builtin_bit_cast(bf16x2v, p23), scale, true);
+  return __builtin_bit_cast(uint32_t, q);
+}
+
 // MXFP8 of 8 bf16 values (one lane's 16 bytes, packed pairs) inside a block of 32 that four
 // adjacent lanes (lane ^ 1, lane ^ 2) hold together: the block amax of the bf16 magnitudes,
-// the E8M0 exponent, and this lane's 8 E4M3 codes. Every lane of the wave must take part.
+// the E8M0 exponent, and this lane's 8 E4M3 codes (by the scaled conversion; the codes of
+// the fp32 route for finite values). Every lane of the wave must take part.
 __device__ __forceinline__ v2i mx_quant_lane8(const v4i& v, int& e8m0) {
-  uint32_t m = 0;
+  uint32_t m2 = 0;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t w = (uint32_t)v[e], lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
-    m = lo > m ? lo : m;
-    m = hi > m ? hi : m;
-  }
+  for (int e = 0; e < 4; ++e) m2 = pk_absmax_bits(m2, (uint32_t)v[e]);
+  uint32_t m = (m2 & 0xFFFFu) > (m2 >> 16) ? (m2 & 0xFFFFu) : (m2 >> 16);
   uint32_t o = __shfl_xor(m, 1, 64);
   m = o > m ? o : m;
   o = __shfl_xor(m, 2, 64);
   m = o > m ? o : m;
   const int X = mx_exponent(m);
-  const float sc = pow2_neg(X);
-  uint32_t qb[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) qb[e] = e4m3x2(bf16_lo((uint32_t)v[e]) * sc, bf16_hi((uint32_t)v[e]) * sc);
+  const uint32_t bound = mx_bound_bits(X) * 0x10001u;
+  const float sc = mx_scale_operand(X);
   e8m0 = X + 127;
-  return v2i{(int)(qb[0] | (qb[1] << 16)), (int)(qb[2] | (qb[3] << 16))};
+  return v2i{(int)e4m3x4_scaled(clamp_pair((uint32_t)v[0], bound), clamp_pair((uint32_t)v[1], bound), sc),
+             (int)e4m3x4_scaled(clamp_pair((uint32_t)v[2], bound), clamp_pair((uint32_t)v[3], bound), sc)};
 }
 
 }  // namespace sge

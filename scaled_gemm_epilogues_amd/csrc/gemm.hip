@@ -351,32 +351,32 @@ constexpr int tile_sc_bytes(int fmt, int sched, int epi) {
 // read back from the staged tile: `rows` is the tile's fp32 staging (BN floats per row) whose
 // slot(rl) float of row rl now holds the two bf16 values as one packed pair (low half: the first
 // column). Each column gets the E8M0 exponent of its block's bf16 magnitude maximum and 32 E4M3
-// codes, exactly as the token-blocked quantizer makes them from the bf16 tensor; when ok, the
-// codes go to q (first column) and q + ld_t (second), 32 contiguous bytes each. Returns the two
-// E8M0 bytes (first column's in bits 0-7, second's in bits 8-15).
+// codes (by the scaled conversion), exactly as the token-blocked quantizer makes them from the
+// bf16 tensor for finite values; when ok, the codes go to q (first column) and q + ld_t
+// (second), 32 contiguous bytes each. Returns the two E8M0 bytes (first column's in bits 0-7,
+// second's in bits 8-15).
 template <int BN, class Slot>
 __device__ __forceinline__ uint32_t mx_colT_block(const float* rows, int rl0, const Slot& slot, uint8_t* q,
                                                   int64_t ld_t, bool ok) {
   uint32_t v[32];
 #pragma unroll
   for (int r = 0; r < 32; ++r) v[r] = __builtin_bit_cast(uint32_t, rows[(rl0 + r) * BN + slot(rl0 + r)]);
-  uint32_t mlo = 0, mhi = 0;
+  uint32_t m = 0;                                        // both columns' magnitude maxima
 #pragma unroll
-  for (int r = 0; r < 32; ++r) {
-    const uint32_t lo = v[r] & 0x7FFFu, hi = (v[r] >> 16) & 0x7FFFu;
-    mlo = lo > mlo ? lo : mlo;
-    mhi = hi > mhi ? hi : mhi;
-  }
-  const int xlo = mx_exponent(mlo), xhi = mx_exponent(mhi);
-  const float slo = pow2_neg(xlo), shi = pow2_neg(xhi);
+  for (int r = 0; r < 32; ++r) m = pk_absmax_bits(m, v[r]);
+  const int xlo = mx_exponent(m & 0xFFFFu), xhi = mx_exponent(m >> 16);
+  const uint32_t bound = mx_bound_bits(xlo) | (mx_bound_bits(xhi) << 16);
+  const float slo = mx_scale_operand(xlo), shi = mx_scale_operand(xhi);
   v4i qlo[2], qhi[2];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint32_t* w = v + 4 * k;
-    qlo[k >> 2][k & 3] = (int)(e4m3x2(bf16_lo(w[0]) * slo, bf16_lo(w[1]) * slo) |
-                               (e4m3x2(bf16_lo(w[2]) * slo, bf16_lo(w[3]) * slo) << 16));
-    qhi[k >> 2][k & 3] = (int)(e4m3x2(bf16_hi(w[0]) * shi, bf16_hi(w[1]) * shi) |
-                               (e4m3x2(bf16_hi(w[2]) * shi, bf16_hi(w[3]) * shi) << 16));
+  for (int k = 0; k < 8; ++k) {                          // rows 4k .. 4k + 3
+    const uint32_t c0 = clamp_pair(v[4 * k], bound), c1 = clamp_pair(v[4 * k + 1], bound);
+    const uint32_t c2 = clamp_pair(v[4 * k + 2], bound), c3 = clamp_pair(v[4 * k + 3], bound);
+    // each column's two rows side by side: low halves, then high halves
+    qlo[k >> 2][k & 3] = (int)e4m3x4_scaled(__builtin_amdgcn_perm(c1, c0, 0x05040100u),
+                                            __builtin_amdgcn_perm(c3, c2, 0x05040100u), slo);
+    qhi[k >> 2][k & 3] = (int)e4m3x4_scaled(__builtin_amdgcn_perm(c1, c0, 0x07060302u),
+                                            __builtin_amdgcn_perm(c3, c2, 0x07060302u), shi);
   }
   if (ok) {
     reinterpret_cast<v4i*>(q)[0] = qlo[0];

@@ -313,47 +313,22 @@ __global__ __launch_bounds__(MxTile<WIDE>::kThreads) void quantize_mxfp8_kernel(
   const int lr = t / (kMC / 8);          // 0..31
   const int cc = t % (kMC / 8);          // column chunk of 8
   const int64_t c = c0 + cc * 8;
-  float x[4][8];
-  uint32_t ab[4][8];
-  uint32_t x_sign[4];    // bit e: sign of element e
   bool ok[4];
   uint4 vv[4];
   load_rows4(src, r0, nrows, cols, c, lr, vv);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    ok[k] = lr + 32 * k < nrows && c < cols;
-    const uint4 v = vv[k];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    x_sign[k] = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x_sign[k] |= ((w[e] >> 15) & 1u) << (2 * e) | ((w[e] >> 31) & 1u) << (2 * e + 1);
-      x[k][2 * e] = bf16_lo(w[e]);
-      x[k][2 * e + 1] = bf16_hi(w[e]);
-      ab[k][2 * e] = w[e] & 0x7FFFu;
-      ab[k][2 * e + 1] = (w[e] >> 16) & 0x7FFFu;
-    }
-  }
+  for (int k = 0; k < 4; ++k) ok[k] = lr + 32 * k < nrows && c < cols;
 
   if (q_row) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      // Rowwise: a 32-column block is 4 consecutive threads of one row.
-      uint32_t m = 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) m = ab[k][e] > m ? ab[k][e] : m;
-      uint32_t o = __shfl_xor(m, 1, 64);
-      m = o > m ? o : m;
-      o = __shfl_xor(m, 2, 64);
-      m = o > m ? o : m;
-      const int X = mx_exponent(m);
-      const float sc = pow2_neg(X);
+      // Rowwise: a 32-column block is 4 consecutive threads of one row (every lane takes part).
+      int e8;
+      const v2i qv = mx_quant_lane8(v4i{(int)vv[k].x, (int)vv[k].y, (int)vv[k].z, (int)vv[k].w}, e8);
       if (ok[k]) {
         const int64_t r = r0 + lr + 32 * k;
-        const uint32_t b01 = e4m3x2(x[k][0] * sc, x[k][1] * sc), b23 = e4m3x2(x[k][2] * sc, x[k][3] * sc);
-        const uint32_t b45 = e4m3x2(x[k][4] * sc, x[k][5] * sc), b67 = e4m3x2(x[k][6] * sc, x[k][7] * sc);
-        *reinterpret_cast<uint2*>(q_row + r * cols + c) = make_uint2(b01 | (b23 << 16), b45 | (b67 << 16));
-        if ((cc & 3) == 0) s_row[r * (cols / 32) + (c >> 5)] = (uint8_t)(X + 127);
+        *reinterpret_cast<v2i*>(q_row + r * cols + c) = qv;
+        if ((cc & 3) == 0) s_row[r * (cols / 32) + (c >> 5)] = (uint8_t)e8;
       }
     }
   }
@@ -363,9 +338,11 @@ __global__ __launch_bounds__(MxTile<WIDE>::kThreads) void quantize_mxfp8_kernel(
     // the block of rows 32k..32k+31 (k = t % 4) of column t / 4: local amax, 32 codes,
     // written as 32 contiguous bytes (each column's 128 rows leave as one line).
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t w[4] = {vv[k].x, vv[k].y, vv[k].z, vv[k].w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xt[cc * 8 + e][lr + 32 * k] = (uint16_t)(ab[k][e] | (x_sign[k] >> e & 1) << 15);
+      for (int e = 0; e < 8; ++e) xt[cc * 8 + e][lr + 32 * k] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    }
     __syncthreads();
     const int col = t >> 2, k = t & 3;
     const uint4* seg = reinterpret_cast<const uint4*>(&xt[col][32 * k]);
@@ -375,21 +352,15 @@ __global__ __launch_bounds__(MxTile<WIDE>::kThreads) void quantize_mxfp8_kernel(
       const uint4 v = seg[i];
       w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
     }
-    uint32_t m = 0;
+    uint32_t m2 = 0;                                     // rows of one column, two per word
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t v = absmax_bits2(w[i]);
-      m = v > m ? v : m;
-    }
-    const int X = mx_exponent(m);
-    const float sc = pow2_neg(X);
+    for (int i = 0; i < 16; ++i) m2 = pk_absmax_bits(m2, w[i]);
+    const int X = mx_exponent((m2 & 0xFFFFu) > (m2 >> 16) ? (m2 & 0xFFFFu) : (m2 >> 16));
+    const uint32_t bound = mx_bound_bits(X) * 0x10001u;
+    const float sc = mx_scale_operand(X);
     uint32_t o[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t lo = e4m3x2(bf16_lo(w[2 * i]) * sc, bf16_hi(w[2 * i]) * sc);
-      const uint32_t hi = e4m3x2(bf16_lo(w[2 * i + 1]) * sc, bf16_hi(w[2 * i + 1]) * sc);
-      o[i] = lo | (hi << 16);
-    }
+    for (int i = 0; i < 8; ++i) o[i] = e4m3x4_scaled(clamp_pair(w[2 * i], bound), clamp_pair(w[2 * i + 1], bound), sc);
     const int64_t ldc = GROUPED ? ld_t : rows;
     if (c0 + col < cols && 32 * k < npos) {
       uint8_t* dst = q_colT + (c0 + col) * ldc + p0 + 32 * k;
