@@ -87,9 +87,11 @@ typedef int v2i __attribute__((__vector_size__(2 * sizeof(int))));
 // v_cvt_scalef32_pk_fp8_bf16 converts two packed bf16 values to E4M3 divided by 2^E, where E is
 // taken from the exponent field of its fp32 scale operand alone (E8M0: field 0 is 2^-127), with
 // round-to-nearest-even, and turns magnitudes past 448 (after rounding) into 448 or NaN. Measured
-// on MI355X over every bf16 pattern at block exponents -127 .. 120: in range it matches the
-// fp32 route (scale by 2^-X, clamp to +-448, v_cvt_pk_fp8_f32) bit for bit, so clamping the
-// bf16 magnitudes to 448 * 2^X first makes the two routes agree on every finite input.
+// on MI355X over every bf16 pattern at 14 block exponents from -127 to 120 (the extremes, -126,
+// -100, -20, -8, -1, 0, 1, 7, 8, 20, 100, 119): in range it matches the fp32 route (scale by
+// 2^-X, clamp to +-448, v_cvt_pk_fp8_f32) bit for bit, so clamping the bf16 magnitudes to
+// 448 * 2^X first makes the two routes agree on finite inputs; the quantizer tests compare
+// every finite bf16 value against the oracle.
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
