@@ -3,7 +3,7 @@
 import numpy as np
 import torch
 
-# Spec bars: |gpu - ref| <= tau * (|ref| + 1) per element.
+# Parity bars: |gpu - ref| <= tau * (|ref| + 1) per element.
 TAU_BF16 = 2e-2
 TAU_FP8 = 6e-2
 
@@ -32,11 +32,11 @@ def host_bits(t):
 
 
 def assert_close(gpu, ref, tau, what="", rel_tight=2.0 ** -8, abs_tight=1e-2):
-    """Both the spec bar and a tighter bar scaled by the output's RMS.
+    """Both the parity bar and a tighter bar scaled by the output's RMS.
 
     The tight bar allows one bf16 rounding of the output (2^-8 relative) plus
     ``abs_tight`` of the RMS for accumulation-order and intermediate roundings;
-    it fails e.g. an all-zero output, which the spec bar alone would
+    it fails e.g. an all-zero output, which the parity bar alone would
     accept for outputs much smaller than 1.
     """
     gpu = np.asarray(gpu, np.float64)
@@ -47,7 +47,7 @@ def assert_close(gpu, ref, tau, what="", rel_tight=2.0 ** -8, abs_tight=1e-2):
     bound = tau * (np.abs(ref) + 1.0)
     if not np.all(err <= bound):
         i = np.unravel_index(np.argmax(err - bound), err.shape)
-        raise AssertionError(f"{what}: north-star bar broken at {i}: gpu={gpu[i]} ref={ref[i]}")
+        raise AssertionError(f"{what}: parity bar broken at {i}: gpu={gpu[i]} ref={ref[i]}")
     rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
     tight = rel_tight * np.abs(ref) + abs_tight * rms
     if not np.all(err <= tight):
@@ -63,7 +63,7 @@ def assert_close_requantized(gpu, ref, tau, what="", rel_tight=2.0 ** -3, abs_ti
     An element of the two intermediates one bf16 step apart may straddle an E4M3 rounding
     boundary; the two sides then take neighbouring codes (one step is 2^-3 of the element's
     binade), which moves every output that the element feeds by that step times the other
-    operand. So: the spec bar on every element, the tight bar of ``assert_close`` on all
+    operand. So: the parity bar on every element, the tight bar of ``assert_close`` on all
     but ``max_frac`` of them, and those within ``flip_rms`` of the output's RMS."""
     gpu = np.asarray(gpu, np.float64)
     ref = np.asarray(ref, np.float64)
@@ -73,7 +73,7 @@ def assert_close_requantized(gpu, ref, tau, what="", rel_tight=2.0 ** -3, abs_ti
     bound = tau * (np.abs(ref) + 1.0)
     if not np.all(err <= bound):
         i = np.unravel_index(np.argmax(err - bound), err.shape)
-        raise AssertionError(f"{what}: north-star bar broken at {i}: gpu={gpu[i]} ref={ref[i]}")
+        raise AssertionError(f"{what}: parity bar broken at {i}: gpu={gpu[i]} ref={ref[i]}")
     rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
     bad = err > rel_tight * np.abs(ref) + abs_tight * rms
     assert bad.sum() <= max_frac * bad.size, f"{what}: {bad.sum()} of {bad.size} outside the tight bar"
