@@ -12,7 +12,8 @@ import synth
 from oracle import grouped, linear, offsets, quant
 from oracle.codecs import bf16_to_f64, f64_to_bf16
 
-from .gpu_paths import run_dense, run_grouped_mlp, run_grouped_mlp_bwd_mx, run_grouped_mlp_fp8, run_grouped_mlp_fwd_mx
+from .gpu_paths import (quant_mx_grouped, run_dense, run_grouped_mlp, run_grouped_mlp_bwd_mx, run_grouped_mlp_fp8,
+                        run_grouped_mlp_fwd_mx)
 from .helpers import (TAU_BF16, TAU_FP8, assert_close, assert_mx_dequant_close, assert_oracle_mx_rowwise, host_bits,
                       host_f64, host_u8)
 
@@ -45,6 +46,23 @@ def _assert_fused_mx_rows(y, yq, ys, base, rng, what):
     rows = _boundary_and_sampled_rows(base, rng, 2048)
     rr = torch.from_numpy(rows).cuda()
     assert_oracle_mx_rowwise(host_bits(y[rr]), host_u8(yq[rr]), host_u8(ys[rr]), what=what)
+
+
+def _assert_fused_token_blocked(out, qT, lay, base, rng, what, ncols=6):
+    """An epilogue's token-blocked MXFP8 copy of its bf16 output: the whole tensor against the
+    standalone token-blocked quantizer on the same launch's bf16 output (compared on the GPU), and
+    sampled columns over all tokens against the oracle's token blocking of those bf16 columns."""
+    T = out.shape[0]
+    c, pad = quant.mx_group_layout(base, T)
+    P = int(pad[-1])
+    std = quant_mx_grouped(out, lay)
+    assert torch.equal(qT["q_colT"][:, :P], std["q_colT"][:, :P]), what
+    assert torch.equal(qT["s_colT"][:, :P // 32], std["s_colT"][:, :P // 32]), what
+    cols = _pick(out.shape[1], ncols, rng)
+    cc = torch.from_numpy(cols).cuda()
+    q, s = quant.mxfp8_colwise_grouped(host_bits(out[:, cc]), c, pad, qT["ld"])
+    assert np.array_equal(host_u8(qT["q_colT"][cc])[:, :P], q[:, :P]), what
+    assert np.array_equal(host_u8(qT["s_colT"][cc])[:, :P // 32], s[:, :P // 32]), what
 
 
 def _fp8_rows(bits, rows, scale):
@@ -193,6 +211,9 @@ def test_grouped_mxfp8_forward_full_size_sampled():
     # and the oracle's MXFP8 of the launch's bf16 y (rowwise blocks are row-local): sampled rows
     # and every group's first and last row
     _assert_fused_mx_rows(got["y"], got["yq"], got["ys"], base, np.random.default_rng(21), "y (fused MXFP8)")
+    # the token-blocked y written by the same epilogue
+    _assert_fused_token_blocked(got["y"], got["q_y"], got["lay"], base, np.random.default_rng(23),
+                                "y (fused token-blocked MXFP8)")
     sizes = np.diff(base)
     nonempty = [g for g in range(len(sizes)) if sizes[g] > 0]
     rng = np.random.default_rng(11)
@@ -225,6 +246,9 @@ def test_grouped_mxfp8_backward_full_size_sampled():
     base = offsets.base_offsets(inp["splits"])
     # and the oracle's MXFP8 of the launch's bf16 dh, on sampled rows and the group boundaries
     _assert_fused_mx_rows(got["dh"], got["dhq"], got["dhs"], base, np.random.default_rng(22), "dh (fused MXFP8)")
+    # the token-blocked dh written by the dgrad epilogue
+    _assert_fused_token_blocked(got["dh"], got["q_dh"], got["lay"], base, np.random.default_rng(24),
+                                "dh (fused token-blocked MXFP8)")
     sizes = np.diff(base)
     F = inp["w2"].shape[2]
     rng = np.random.default_rng(12)
