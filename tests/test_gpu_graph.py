@@ -163,6 +163,13 @@ def test_quantized_grouped_steps_graph_replays_match_eager():
     dhq, dhs = torch.empty(T, N1, **u8), torch.empty(T, N1 // 32, **u8)
     dw2 = torch.empty(G, H, F, **bf)
     ws = torch.empty(max(1, sge.grouped_linear_bwd_workspace_size(T, F, G, sge.EPI_DSCALED_SWIGLU)), **u8)
+    # MXFP8 fc1 forward whose epilogue writes y rowwise and token-blocked (no bf16 y), and the
+    # dgrad's token-blocked dh
+    mx, mxs = torch.empty(T, H, **u8), torch.empty(T, H // 32, **u8)
+    w1q, w1s = torch.empty(G * N1, H, **u8), torch.empty(G * N1, H // 32, **u8)
+    h2, yq2, ys2 = torch.empty(T, N1, **bf), torch.empty(T, F, **u8), torch.empty(T, F // 32, **u8)
+    yT2, ysT2 = torch.empty(F, ld, **u8), torch.empty(F, ld // 32, **u8)
+    dhT, dhsT = torch.empty(N1, ld, **u8), torch.empty(N1, ld // 32, **u8)
 
     def step():
         sge.splits_to_offsets(splits, [1], offs)
@@ -177,11 +184,17 @@ def test_quantized_grouped_steps_graph_replays_match_eager():
         sge.quantize_mxfp8(W2.reshape(G * H, F), q_colT=w2c, s_colT=w2s)
         sge.quantize_mxfp8_grouped(y, lay, myT, mysT)
         sge.grouped_linear_dgrad_mxfp8(md, ms, w2c, w2s, base, epilogue=sge.EPI_DSCALED_SWIGLU, preact=h, probs=P,
-                                       dact=dh, dprobs=dp, dact_q=dhq, dact_s=dhs, workspace=ws)
+                                       dact=dh, dprobs=dp, dact_q=dhq, dact_s=dhs, workspace=ws, layout=lay,
+                                       dact_colT_q=dhT, dact_colT_s=dhsT)
         sge.grouped_linear_wgrad_mxfp8(mdT, msT, myT, mysT, lay, dw2)
+        sge.quantize_mxfp8(X, q_row=mx, s_row=mxs)
+        sge.quantize_mxfp8(W1.reshape(G * N1, H), q_row=w1q, s_row=w1s)
+        sge.grouped_linear_fwd_mxfp8(mx, mxs, w1q.view(G, N1, H), w1s.view(G, N1, H // 32), base, out=None,
+                                     epilogue=sge.EPI_SCALED_SWIGLU, probs=P, preact=h2, out_q=yq2, out_s=ys2,
+                                     layout=lay, out_colT_q=yT2, out_colT_s=ysT2)
 
     _replays_match(step, [lay, fx[0], fx[1], fx[4], fw[1], y, amax_y, fy[0], fy[4], md, mdT, w2c, dh, dp, dhq,
-                          dhs, dw2])
+                          dhs, dw2, dhT, dhsT, mx, w1q, h2, yq2, ys2, yT2, ysT2])
 
 
 @pytest.mark.parametrize("kind", [sge.NORM_RMS, sge.NORM_LAYER])
