@@ -1182,10 +1182,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
   // token-blocked (the grouped wgrad operand): after a pass's items, each bf16 result sits in
   // the staged tile over the fp32 values it came from (every thread overwrites only what it
   // read), and threads then quantize it down the columns, 32 rows per block. A tile starts on
-  // its group's first row or BM rows later, so its rows are positions colt_pos0 + row of the
-  // group's 128-aligned range; a pass at or past colt_rows (the group's rows in the tile
-  // rounded up to 128) belongs to the next group and is not written, the rest of the range is
-  // padding quantized from zeros.
+  // its group's first row or a multiple of BM rows later, so its rows are positions
+  // colt_pos0 + row of the group's 128-aligned range; a pass at or past colt_rows (the group's
+  // rows in the tile rounded up to 128) belongs to the next group and is not written, the rest
+  // of the range is padding quantized from zeros.
   constexpr bool kColT = FMT == F_MX && SCHED == S_GROUP_M && EPI != E_STORE;
   const bool colq = kColT && p.qt_out != nullptr;
   int64_t colt_pos0 = 0;
@@ -1233,7 +1233,6 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
     constexpr int kChunks = BN / 8;                        // 8-column chunks per row
     constexpr int kIters = 128 * kChunks / (NWAVES * 64);  // chunks per thread per pass
     float* stage = reinterpret_cast<float*>(wm ? half1 : half0);
-    // The residual of both passes is requested first: its HBM latency overlaps the staging.
     // Output offset of a thread's item it of a pass (kOOB out of range); held across the
     // epilogue except with the token-blocked output, whose kernels keep every accumulator
     // live longer and recompute it instead.
@@ -1243,6 +1242,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
       const int64_t n = n0 + (id % kChunks) * 8;
       return (m0 + brow < row_end && n < n_end) ? (int)(((int64_t)brow * p.ldc + n) * 2) : (int)kOOB;
     };
+    // The residual of both passes is requested first: its HBM latency overlaps the staging.
     v4i res[2][kIters];
     int offs[2][kIters];
 #pragma unroll
@@ -1271,7 +1271,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
         for (int j = 0; j < WNF; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int r = rb + acc_row(q);            // row within its LDS half
+            const int r = rb + acc_row(q);                 // row within its LDS half
             const int g = (wn * WN + j * 32 + acc_col(q)) >> 2;
             const float4 v = acc_get(i, j, q, alpha);
             *reinterpret_cast<float4*>(st + r * BN + ((g ^ (r & 15)) << 2)) = v;
@@ -1647,7 +1647,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int blk, uint8_t*
           if (colq) {                                      // da, db over their fp32 granules (zero outside)
             const bool okw = od[ib] != (int)kOOB;
             float* wrow = const_cast<float*>(row);
-            *reinterpret_cast<float4*>(wrow + (((2 * c) ^ sw) << 2)) = __builtin_bit_cast(float4, okw ? va : v4i{0, 0, 0, 0});
+            *reinterpret_cast<float4*>(wrow + (((2 * c) ^ sw) << 2)) =
+                __builtin_bit_cast(float4, okw ? va : v4i{0, 0, 0, 0});
             if constexpr (!kSR)
               *reinterpret_cast<float4*>(wrow + (((2 * c + 1) ^ sw) << 2)) =
                   __builtin_bit_cast(float4, okw ? vb : v4i{0, 0, 0, 0});
