@@ -79,6 +79,7 @@ COLT_CASES = {
     # second tile), an empty one, and one ending 128 rows into an aligned 256
     "tile_multiples": ([512, 256, 129, 0, 383], 128, 384),
     "ragged_with_empty_groups": ([300, 0, 211, 9, 0, 40], 256, 128),
+    "many_small_groups": ([7, 0, 128, 33, 1, 256, 0, 90, 12, 5, 64, 31, 2, 0, 19, 40], 128, 128),
 }
 
 

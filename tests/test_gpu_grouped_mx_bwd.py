@@ -156,6 +156,8 @@ COLT_CASES = {
     # whole tiles, a group ending 127 rows into its second tile's aligned range, an empty one
     "tile_multiples": ([512, 256, 129, 0, 383], 128, 256),
     "dirichlet_6": (None, 256, 128),
+    # many small groups (every tile a single partial pass), one exactly 128 and one exactly 256
+    "many_small_groups": ([7, 0, 128, 33, 1, 256, 0, 90, 12, 5, 64, 31, 2, 0, 19, 40], 128, 128),
 }
 
 
